@@ -1,0 +1,330 @@
+"""Plain CPU oracle for the Sparse-BitLinear (W1.58A8, N:M) forward path.
+
+TEST INFRASTRUCTURE ONLY.  This is the slow, obviously-correct definition the
+HIP kernels are checked against.  Only the test-suite, the package smoke check
+and the benchmark's CPU-baseline leg may import it; the library never does,
+and it shares no code, tables or constants with the GPU path.  Inputs come
+from the seeded generators in `synth.py`, which hold none of this arithmetic.
+
+Sources (the method pages; sections, equations and items named per page):
+  [SB-es]  "Sparse-BitNet: 1.58-bit LLMs are Naturally Friendly to
+           Semi-Structured Sparsity", gist.science Spanish summary,
+           "Resumen tecnico", sections 1 (Problema) and 2 (Metodologia).
+  [SB-ar]  the same paper, gist.science Arabic summary, section 2
+           (Methodology): items "Ternary Quantization", "Dynamic N:M
+           Masking", "Mask Generation", "Quant-Then-Mask Order".
+  [BN-cpp] "Marco de inferencia de Microsoft lleva modelos de lenguaje
+           grande de 1 bit a dispositivos locales" (unite.ai), section
+           "Fundamento matematico": activation quantization (item 2) and the
+           BitLinear operation (item 3).
+  [BN-spec] "Introduccion Detallada al Proyecto BitNet" (aibars.net),
+           "Especificaciones Tecnicas": W1.58A8, absmean weights, 8-bit
+           activations, no bias.
+
+Readings taken where the pages are silent or garbled (each one is also
+listed with its reason in the design notes):
+  * beta is ONE scale per weight matrix: the exact mean of |w| over all
+    n_out*k BF16 master values (pruned ones included, because quantization
+    comes before the mask), rounded once to fp32, nearest-even.  The value
+    used for scaling is beta_eff = max(beta, 1e-5f).
+  * codes: c = RoundClip(w / beta_eff, -1, 1), round half to even.
+  * the N:M groups are m consecutive positions along k inside one output row;
+    the mask keeps exactly n per group, the n largest |w| of the BF16 master,
+    ties to the lower index; +0 and -0 tie.
+  * activations: per token, gamma = max_k |x|, gamma_eff = max(gamma, 1e-5f),
+    q = clamp(rint(RN_fp32(Qb * x / gamma_eff)), -127, 127) with Qb = 128 and
+    rint rounding half to even.  RN_fp32(Qb*x/gamma) is evaluated as the
+    single correctly-rounded fp32 quotient x / (gamma_eff / 128), where the
+    divisor is exact.
+  * rescale: y = RN_fp32(fp32(acc) * RN_fp32(RN_fp32(beta_eff * gamma_eff) * 2^-7)).
+  * byte formats (the pages only speak of "metadata" for the kernel) are
+    defined in `pack_dense2`, `pack_bitmap` and `pack_nm` below.
+
+Non-finite inputs are a precondition violation: the functions raise.
+
+Pinned by tests/test_oracle_*.py (exact-rational brute force, enumeration of
+all C(m, n) subsets, Python-int contraction, closed-form statistics, the
+hand-derived 16-weight worked example and format round trips).
+"""
+
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+QB = 128                # 2^(b-1) for b = 8 bit activations  [BN-cpp] item 2
+Q_CLIP = 127            # symmetric int8 clip  [BN-spec]
+EPS_SCALE = np.float32(1e-5)
+
+
+# --------------------------------------------------------------------------
+# BF16 helpers
+# --------------------------------------------------------------------------
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """BF16 bit patterns -> fp32 values (exact: BF16 is the top half of fp32)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _check_finite_bf16(bits: np.ndarray) -> None:
+    if np.any((np.asarray(bits, dtype=np.uint16) & 0x7F80) == 0x7F80):
+        raise ValueError("non-finite BF16 master weight")
+
+
+# --------------------------------------------------------------------------
+# exact rounding of a non-negative rational to fp32
+# --------------------------------------------------------------------------
+
+def rational_to_f32(num: int, den: int) -> np.float32:
+    """Round num/den (num >= 0, den > 0) to the nearest fp32, ties to even.
+
+    Integer arithmetic only: find the binade, take 24 significant bits (or the
+    fixed 2^-149 grid for subnormals), and round on the exact remainder.
+    """
+    if num < 0 or den <= 0:
+        raise ValueError("rational_to_f32 needs num >= 0 and den > 0")
+    if num == 0:
+        return np.float32(0.0)
+    # e = floor(log2(num/den))
+    e = num.bit_length() - den.bit_length()
+    if (num << max(0, -e)) < (den << max(0, e)):
+        e -= 1
+    lsb = max(e - 23, -149)          # exponent of the last kept bit
+    if lsb >= 0:
+        n2, d2 = num, den << lsb
+    else:
+        n2, d2 = num << (-lsb), den
+    q, r = divmod(n2, d2)
+    if 2 * r > d2 or (2 * r == d2 and (q & 1)):
+        q += 1
+    val = float(q) * 2.0 ** lsb     # exact in fp64 (q <= 2^24)
+    if val >= 2.0 ** 128:
+        return np.float32(np.inf)
+    return np.float32(val)
+
+
+# --------------------------------------------------------------------------
+# a1: beta, the absmean weight scale  [SB-ar] "Ternary Quantization";
+#     [BN-spec] absmean weights
+# --------------------------------------------------------------------------
+
+def absmean_exact(bits: np.ndarray) -> Fraction:
+    """Exact mean of |w| over every BF16 value of the matrix.
+
+    A finite BF16 magnitude is sig * 2^(max(e,1) - 134) with e the biased
+    exponent and sig = mantissa | (e != 0) << 7, i.e. an integer number of
+    2^-133 units.  Per-exponent sums of sig are exact in float64 (each sum is
+    an integer below 2^53), so the total is an exact Python integer.
+    """
+    b = np.asarray(bits, dtype=np.uint16).ravel()
+    if b.size == 0:
+        raise ValueError("empty weight matrix")
+    _check_finite_bf16(b)
+    mag = (b & 0x7FFF).astype(np.int64)
+    e = mag >> 7
+    sig = (mag & 0x7F) | ((e != 0).astype(np.int64) << 7)
+    per_e = np.bincount(e, weights=sig.astype(np.float64), minlength=256)
+    total = 0
+    for ei in range(256):
+        s = int(per_e[ei])
+        if s:
+            total += s << (max(ei, 1) - 1)   # units of 2^-133
+    return Fraction(total, b.size << 133)
+
+
+def absmean_beta(bits: np.ndarray) -> np.float32:
+    """beta = RN_fp32(mean |w|): one scale per weight matrix."""
+    f = absmean_exact(bits)
+    return rational_to_f32(f.numerator, f.denominator)
+
+
+def beta_eff(beta) -> np.float32:
+    return np.maximum(np.float32(beta), EPS_SCALE)
+
+
+# --------------------------------------------------------------------------
+# a3: ternarization  c = RoundClip(w / beta_eff, -1, 1)
+# --------------------------------------------------------------------------
+
+def ternarize(bits: np.ndarray, beta) -> np.ndarray:
+    """Ternary codes in {-1, 0, +1} (int8), same shape as `bits`.
+
+    w / beta_eff is formed in float64.  It cannot land on the wrong side of
+    +-1/2: when |w| != beta_eff/2 the exact ratio differs from 1/2 by at
+    least 2^-25 (both are fp32 grid values), far beyond float64 rounding, and
+    when |w| == beta_eff/2 the quotient 1/2 is exact; rint then rounds that
+    tie to even (to 0).
+    """
+    _check_finite_bf16(bits)
+    w = bf16_to_f32(bits).astype(np.float64)
+    r = np.rint(w / np.float64(beta_eff(beta)))
+    return np.clip(r, -1, 1).astype(np.int8)
+
+
+# --------------------------------------------------------------------------
+# a2: N:M mask from the BF16 master magnitudes  [SB-es] section 2 (mask
+#     generation from master weights); [SB-ar] "Dynamic N:M Masking",
+#     "Mask Generation"
+# --------------------------------------------------------------------------
+
+def nm_keep(bits: np.ndarray, n: int, m: int) -> np.ndarray:
+    """Boolean keep-mask [n_out][k]: exactly n kept in each group of m along k.
+
+    rank_j = #{i : |w_i| > |w_j|} + #{i < j : |w_i| == |w_j|}; keep_j = rank_j < n.
+    """
+    b = np.asarray(bits, dtype=np.uint16)
+    n_out, k = b.shape
+    if m < 1 or n < 1 or n > m or k % m:
+        raise ValueError("bad N:M pattern for this shape")
+    _check_finite_bf16(b)
+    mag = np.abs(bf16_to_f32(b)).reshape(n_out, k // m, m)
+    keep = np.empty((n_out, k // m, m), dtype=bool)
+    idx = np.arange(m)
+    lower = idx[None, :] < idx[:, None]          # lower[j, i] = i < j
+    step = max(1, (1 << 22) // max(1, k * m))
+    for r0 in range(0, n_out, step):
+        a = mag[r0:r0 + step]                     # [R, G, m]
+        wj = a[..., :, None]                      # j along axis -2
+        wi = a[..., None, :]                      # i along axis -1
+        rank = (wi > wj).sum(-1) + ((wi == wj) & lower).sum(-1)
+        keep[r0:r0 + step] = rank < n
+    return keep.reshape(n_out, k)
+
+
+# --------------------------------------------------------------------------
+# a1-a4 together: quant, then mask  [SB-es] section 2 (quant-then-mask);
+# [SB-ar] "Quant-Then-Mask Order"
+# --------------------------------------------------------------------------
+
+def quant_weights(bits: np.ndarray, n: int, m: int):
+    """(beta, keep, codes) with codes = RoundClip(w/beta_eff, -1, 1) * keep."""
+    beta = absmean_beta(bits)
+    keep = nm_keep(bits, n, m)
+    codes = ternarize(bits, beta) * keep.astype(np.int8)
+    return beta, keep, codes.astype(np.int8)
+
+
+# --------------------------------------------------------------------------
+# a5: byte formats
+# --------------------------------------------------------------------------
+
+def pack_dense2(codes: np.ndarray) -> np.ndarray:
+    """DENSE2: byte n*(k/4) + k/4, bits 2*(k%4)..+1 hold u = c + 1 in {0,1,2}."""
+    c = np.asarray(codes, dtype=np.int8)
+    n_out, k = c.shape
+    if k % 4:
+        raise ValueError("k must be a multiple of 4")
+    u = (c.astype(np.int16) + 1).astype(np.uint8).reshape(n_out, k // 4, 4)
+    out = np.zeros((n_out, k // 4), dtype=np.uint8)
+    for s in range(4):
+        out |= (u[..., s] << (2 * s)).astype(np.uint8)
+    return out
+
+
+def unpack_dense2(packed: np.ndarray, k: int) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    n_out = p.shape[0]
+    u = np.stack([(p >> (2 * s)) & 3 for s in range(4)], axis=-1).reshape(n_out, k)
+    return (u.astype(np.int16) - 1).astype(np.int8)
+
+
+def pack_bitmap(keep: np.ndarray) -> np.ndarray:
+    """Bitmap (mask bits / N:M metadata): byte n*(k/8) + k/8, bit k%8 = kept."""
+    kp = np.asarray(keep, dtype=bool)
+    n_out, k = kp.shape
+    if k % 8:
+        raise ValueError("k must be a multiple of 8")
+    return np.packbits(kp.reshape(n_out, k // 8, 8), axis=-1, bitorder="little").reshape(n_out, k // 8)
+
+
+def unpack_bitmap(bitmap: np.ndarray, k: int) -> np.ndarray:
+    bm = np.asarray(bitmap, dtype=np.uint8)
+    return np.unpackbits(bm, axis=-1, bitorder="little")[:, :k].astype(bool)
+
+
+def pack_nm(codes: np.ndarray, keep: np.ndarray, n: int, m: int) -> np.ndarray:
+    """N:M codes: the kept positions of row r, in ascending k, are numbered
+    i = 0 .. k*n/m - 1; byte r*(k*n/(4m)) + i/4, bits 2*(i%4)..+1 hold u = c+1.
+    Requires exactly n kept per group (k*n/m must be a multiple of 4)."""
+    c = np.asarray(codes, dtype=np.int8)
+    kp = np.asarray(keep, dtype=bool)
+    n_out, k = c.shape
+    per_row = k * n // m
+    if k % m or per_row % 4:
+        raise ValueError("k*n/m must be a multiple of 4")
+    if np.any(kp.reshape(n_out, k // m, m).sum(-1) != n):
+        raise ValueError("mask must keep exactly n per group")
+    kept_u = (c[kp].astype(np.int16) + 1).astype(np.uint8).reshape(n_out, per_row // 4, 4)
+    out = np.zeros((n_out, per_row // 4), dtype=np.uint8)
+    for s in range(4):
+        out |= (kept_u[..., s] << (2 * s)).astype(np.uint8)
+    return out
+
+
+def unpack_nm(packed: np.ndarray, bitmap: np.ndarray, n: int, m: int, k: int) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    n_out = p.shape[0]
+    kept_u = np.stack([(p >> (2 * s)) & 3 for s in range(4)], axis=-1).reshape(n_out, -1)
+    keep = unpack_bitmap(bitmap, k)
+    codes = np.zeros((n_out, k), dtype=np.int8)
+    codes[keep] = (kept_u.astype(np.int16) - 1).astype(np.int8).ravel()
+    return codes
+
+
+# --------------------------------------------------------------------------
+# a6: per-token absmax int8 activation quantization  [BN-cpp] item 2;
+#     [BN-spec] 8-bit activations
+# --------------------------------------------------------------------------
+
+def quant_acts(x: np.ndarray):
+    """(q int8 [m_tok][k], gamma fp32 [m_tok]) with gamma = max_k |x|."""
+    x = np.asarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("non-finite activation")
+    gamma = np.abs(x).max(axis=1).astype(np.float32)
+    g_eff = np.maximum(gamma, EPS_SCALE)
+    s = (g_eff / np.float32(QB)).astype(np.float32)        # exact power-of-two scaling
+    t = (x / s[:, None]).astype(np.float32)                 # one IEEE fp32 division
+    q = np.clip(np.rint(t), -Q_CLIP, Q_CLIP).astype(np.int8)
+    return q, gamma
+
+
+# --------------------------------------------------------------------------
+# a7-a8: ternary x int8 contraction and rescale  [BN-cpp] item 3
+#        y = W~ x~ (beta gamma / Qb); no bias [BN-spec]
+# --------------------------------------------------------------------------
+
+def contract(codes: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """acc[t, r] = sum_k codes[r, k] * q[t, k] (int32).
+
+    The float64 matmul is exact: every partial sum is an integer of magnitude
+    at most 127*k < 2^53.
+    """
+    c = np.asarray(codes, dtype=np.int8)
+    qq = np.asarray(q, dtype=np.int8)
+    if c.shape[1] != qq.shape[1]:
+        raise ValueError("k mismatch")
+    acc = qq.astype(np.float64) @ c.astype(np.float64).T
+    return np.rint(acc).astype(np.int32)
+
+
+def rescale(acc: np.ndarray, beta, gamma: np.ndarray) -> np.ndarray:
+    """y[t, r] = RN(fp32(acc) * RN(RN(beta_eff * gamma_eff[t]) * 2^-7))."""
+    b = beta_eff(beta)
+    g = np.maximum(np.asarray(gamma, dtype=np.float32), EPS_SCALE)
+    s = ((b * g).astype(np.float32) * np.float32(1.0 / QB)).astype(np.float32)
+    return (np.asarray(acc).astype(np.float32) * s[:, None]).astype(np.float32)
+
+
+def linear(codes: np.ndarray, q: np.ndarray, beta, gamma: np.ndarray):
+    acc = contract(codes, q)
+    return acc, rescale(acc, beta, gamma)
+
+
+def forward(bits: np.ndarray, x: np.ndarray, n: int, m: int):
+    """The whole path for one matrix: returns a dict of every intermediate."""
+    beta, keep, codes = quant_weights(bits, n, m)
+    q, gamma = quant_acts(x)
+    acc, y = linear(codes, q, beta, gamma)
+    return dict(beta=beta, keep=keep, codes=codes, q=q, gamma=gamma, acc=acc, y=y)
