@@ -1,0 +1,166 @@
+/*
+ * sbl.h -- C ABI of the Sparse-BitLinear (W1.58A8, N:M) forward path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (BitNet b1.58 with N:M semi-structured sparsity, "Sparse-BitNet"):
+ *   beta  = mean |w| over the BF16 master matrix            (absmean scale)
+ *   c     = RoundClip(w / max(beta, 1e-5), -1, 1)           (ternary codes)
+ *   keep  = top-n of every m consecutive |w| along k, from the BF16 master,
+ *           ties to the lower index; codes are masked after quantization
+ *   q     = clamp(rint(128 x / max(gamma, 1e-5)), -127, 127),
+ *           gamma = max_k |x| per token                    (int8 activations)
+ *   acc   = sum_k c[n,k] q[t,k]                             (int32, exact)
+ *   y     = acc * (max(beta,1e-5) * max(gamma,1e-5) / 128)  (fp32, no bias)
+ * Sources: the Sparse-BitNet paper summaries (gist.science, Spanish and
+ * Arabic), section 2 "Methodology" (Sparse-BitLinear: ternary quantization
+ * with an absmean scale, dynamic N:M masking from the BF16 master weights,
+ * quant-then-mask order, metadata for the hardware kernel); the bitnet.cpp
+ * article (unite.ai), "Fundamento matematico" items 2 (activation
+ * quantization) and 3 (BitLinear operation); the BitNet project page
+ * (aibars.net), "Especificaciones Tecnicas" (W1.58A8, no bias).
+ *
+ * Conventions for every call:
+ *  - Every array pointer is a DEVICE pointer owned by the caller (for example
+ *    a PyTorch tensor's data_ptr()).  The library never allocates, frees or
+ *    retains caller memory and keeps no mutable global state, so concurrent
+ *    calls on different streams are safe.
+ *  - Arrays are dense, row-major, 16-byte aligned (scalars: 4-byte aligned).
+ *  - Outputs must not alias inputs.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work and return; nothing is read back to the host.
+ *  - Arguments are validated on the host before anything is enqueued; on an
+ *    error nothing is enqueued and the status is returned.  A failed launch
+ *    returns SBL_ERR_LAUNCH and sbl_last_hip_error() (per thread) gives the
+ *    HIP error code.  No exception, abort or exit crosses this boundary.
+ *  - Non-finite inputs (Inf/NaN) are a precondition violation: results are
+ *    unspecified but every kernel still terminates and stays in bounds.
+ *  - Shape limits: 64 <= k <= 131072 and k % 64 == 0 (so 127*k < 2^24 and
+ *    fp32(acc) is exact); m in {4, 8}; 1 <= n <= m; n_out*k <= 2^34.
+ *
+ * Byte formats (our own; the pages only say the kernel receives N:M
+ * "metadata"):
+ *  DENSE2  [n_out][k/4] bytes: byte r*(k/4) + k/4, bits 2*(k%4)..+1 hold
+ *          u = c + 1 in {0,1,2} (3 is never written).  2 bits per weight.
+ *  BITMAP  [n_out][k/8] bytes: byte r*(k/8) + k/8, bit k%8 = 1 when kept.
+ *          Serves as the mask output and as the N:M metadata.
+ *  NM      [n_out][k*n/(4m)] bytes: the kept positions of row r, in
+ *          ascending k, are numbered i = 0 .. k*n/m - 1; byte
+ *          r*(k*n/(4m)) + i/4, bits 2*(i%4)..+1 hold u = c + 1.  Always used
+ *          together with its BITMAP metadata.
+ */
+#ifndef SBL_H
+#define SBL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SBL_ABI_VERSION 1
+
+typedef enum {
+  SBL_OK = 0,
+  SBL_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  SBL_ERR_SHAPE = 2,       /* a size is out of range or inconsistent          */
+  SBL_ERR_ALIGN = 3,       /* a pointer is not aligned as required            */
+  SBL_ERR_UNSUPPORTED = 4, /* unsupported n:m pattern or format               */
+  SBL_ERR_LAUNCH = 5,      /* a HIP launch failed; see sbl_last_hip_error()   */
+  SBL_ERR_WORKSPACE = 6    /* workspace missing or smaller than required      */
+} sbl_status;
+
+typedef enum {
+  SBL_FMT_DENSE2 = 0,      /* 2-bit dense codes, no metadata                  */
+  SBL_FMT_NM = 1           /* kept codes only (2 bits each) + BITMAP metadata */
+} sbl_format;
+
+typedef void* sbl_stream;  /* a hipStream_t */
+
+/* ABI version of the loaded library (SBL_ABI_VERSION). */
+int sbl_abi_version(void);
+
+/* Static text for a status code. */
+const char* sbl_status_string(int status);
+
+/* HIP error code of this thread's last SBL_ERR_LAUNCH (0 if none). */
+int sbl_last_hip_error(void);
+
+/* Bytes of packed codes for an n_out x k matrix in `fmt` (DENSE2 ignores n, m).
+ * Returns -1 for invalid arguments. */
+int64_t sbl_packed_bytes(int64_t n_out, int64_t k, int32_t n, int32_t m, int32_t fmt);
+
+/* Bytes of metadata: 0 for DENSE2, n_out*k/8 (the BITMAP) for NM; -1 if invalid. */
+int64_t sbl_meta_bytes(int64_t n_out, int64_t k, int32_t fmt);
+
+/* Bytes of device workspace sbl_quant_weights needs (the exact beta
+ * reduction); the same for every shape.  Contents need no initialisation. */
+int64_t sbl_workspace_bytes(int64_t n_out, int64_t k);
+
+/* Weight preparation: beta, N:M mask, ternary codes, packing -- one pass of
+ * the per-training-step recompute (mask recomputed from the current BF16
+ * masters; Sparse-BitNet "dynamic mask recomputation").
+ *   w_bf16     [n_out][k] BF16 bit patterns (input).
+ *   n, m       the N:M pattern: keep n of every m along k (n == m: no mask).
+ *   beta       [1] fp32 output: RN_fp32 of the exact mean of |w| over all
+ *              n_out*k values (pruned ones included).  The codes use
+ *              max(beta, 1e-5).
+ *   mask_bits  [n_out][k/8] BITMAP output, or NULL.
+ *   codes      [n_out][k] int8 output in {-1,0,1} (already masked), or NULL.
+ *   fmt        format of `packed`.
+ *   packed     packed codes output (sbl_packed_bytes), or NULL.
+ *   meta       [n_out][k/8] BITMAP output for fmt == SBL_FMT_NM (required
+ *              there when packed != NULL); ignored for DENSE2.
+ *   workspace  device scratch of sbl_workspace_bytes() bytes, 16-byte
+ *              aligned; overwritten.  Calls sharing one workspace must be
+ *              ordered on one stream.
+ */
+int sbl_quant_weights(const uint16_t* w_bf16, int64_t n_out, int64_t k, int32_t n, int32_t m,
+                      float* beta, uint8_t* mask_bits, int8_t* codes,
+                      int32_t fmt, uint8_t* packed, uint8_t* meta,
+                      void* workspace, int64_t workspace_bytes, sbl_stream stream);
+
+/* Packing alone: ternary codes (+ mask) -> packed bytes.
+ *   codes      [n_out][k] int8 in {-1,0,1} (other values: unspecified bytes).
+ *   mask_bits  [n_out][k/8] BITMAP; required for NM, ignored for DENSE2.
+ *              NM takes, per group, the codes of the first n kept positions
+ *              in ascending k; a group with fewer than n kept bits is padded
+ *              with code 0.
+ *   packed     output (sbl_packed_bytes).
+ *   meta       NM only: receives a copy of mask_bits, or NULL to skip.
+ */
+int sbl_pack(const int8_t* codes, const uint8_t* mask_bits, int64_t n_out, int64_t k,
+             int32_t n, int32_t m, int32_t fmt, uint8_t* packed, uint8_t* meta,
+             sbl_stream stream);
+
+/* Per-token absmax int8 activation quantization.
+ *   x      [m_tok][k] fp32 input.
+ *   xq     [m_tok][k] int8 output: clamp(rint(x / (max(gamma,1e-5)/128)), -127, 127),
+ *          one correctly rounded fp32 division, rint half to even.
+ *   gamma  [m_tok] fp32 output: max_k |x[t,k]| (exact).
+ * m_tok == 0 is a no-op.
+ */
+int sbl_quant_acts(const float* x, int64_t m_tok, int64_t k, int8_t* xq, float* gamma,
+                   sbl_stream stream);
+
+/* Ternary x int8 product with fp32 rescale; no bias.
+ *   packed, meta  weights in `fmt` (meta: BITMAP for NM, NULL for DENSE2);
+ *                 n, m must be those the weights were packed with.
+ *   beta          [1] fp32 (as produced by sbl_quant_weights).
+ *   xq, gamma     [m_tok][k] int8 and [m_tok] fp32 (as produced by sbl_quant_acts).
+ *   y             [m_tok][n_out] fp32 output:
+ *                 RN(fp32(acc) * RN(RN(max(beta,1e-5) * max(gamma,1e-5)) * 2^-7)).
+ *   acc           [m_tok][n_out] int32 output (exact sum), or NULL.
+ * Decode sizes (m_tok <= 16) run a bandwidth-bound GEMV, larger ones an
+ * int8-MFMA GEMM; both give identical bits.  m_tok == 0 is a no-op.
+ */
+int sbl_linear(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
+               const float* beta, const int8_t* xq, const float* gamma,
+               int64_t m_tok, int64_t n_out, int64_t k, float* y, int32_t* acc,
+               sbl_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SBL_H */

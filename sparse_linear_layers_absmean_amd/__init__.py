@@ -1,0 +1,16 @@
+"""Sparse-BitLinear (W1.58A8, N:M) for AMD MI355X.
+
+The compute path lives in libsbl.so (HIP kernels for gfx950 behind the C ABI
+declared in include/sbl.h); `sbl` is its thin Python binding.  Importing the
+package does not load the library: `sbl.load()` (or the first call) does.
+"""
+
+from .sbl import (SBL_FMT_DENSE2, SBL_FMT_NM, SblError, linear, load, new_workspace, quant_acts,
+                  quant_weights, sbl_abi_version, sbl_linear, sbl_meta_bytes, sbl_pack,
+                  sbl_packed_bytes, sbl_quant_acts, sbl_quant_weights, sbl_workspace_bytes)
+
+__all__ = [
+    "SBL_FMT_DENSE2", "SBL_FMT_NM", "SblError", "linear", "load", "new_workspace", "quant_acts",
+    "quant_weights", "sbl_abi_version", "sbl_linear", "sbl_meta_bytes", "sbl_pack",
+    "sbl_packed_bytes", "sbl_quant_acts", "sbl_quant_weights", "sbl_workspace_bytes",
+]

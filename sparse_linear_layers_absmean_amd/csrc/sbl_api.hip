@@ -1,0 +1,131 @@
+// C ABI of libsbl: host-side validation and kernel dispatch.  See include/sbl.h.
+#include "../../include/sbl.h"
+#include "sbl_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxK = 131072;            // 127*k < 2^24: fp32(acc) exact
+constexpr int64_t kMaxElems = int64_t(1) << 34;
+constexpr int64_t kMaxTokens = int64_t(1) << 24;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool nm_ok(int32_t n, int32_t m) { return (m == 4 || m == 8) && n >= 1 && n <= m; }
+
+bool k_ok(int64_t k) { return k >= 64 && k <= kMaxK && k % 64 == 0; }
+
+int launch_status(hipError_t e) {
+  if (e == hipSuccess) return SBL_OK;
+  g_last_hip_error = (int)e;
+  return SBL_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sbl_abi_version(void) { return SBL_ABI_VERSION; }
+
+const char* sbl_status_string(int status) {
+  switch (status) {
+    case SBL_OK: return "ok";
+    case SBL_ERR_NULL: return "required pointer is NULL";
+    case SBL_ERR_SHAPE: return "size out of range or inconsistent";
+    case SBL_ERR_ALIGN: return "pointer misaligned";
+    case SBL_ERR_UNSUPPORTED: return "unsupported n:m pattern or format";
+    case SBL_ERR_LAUNCH: return "HIP launch failed";
+    case SBL_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int sbl_last_hip_error(void) { return g_last_hip_error; }
+
+int64_t sbl_packed_bytes(int64_t n_out, int64_t k, int32_t n, int32_t m, int32_t fmt) {
+  if (n_out < 1 || !k_ok(k) || n_out * k > kMaxElems) return -1;
+  if (fmt == SBL_FMT_DENSE2) return n_out * (k / 4);
+  if (fmt == SBL_FMT_NM && nm_ok(n, m)) return n_out * (k / m) * n / 4;
+  return -1;
+}
+
+int64_t sbl_meta_bytes(int64_t n_out, int64_t k, int32_t fmt) {
+  if (n_out < 1 || !k_ok(k) || n_out * k > kMaxElems) return -1;
+  if (fmt == SBL_FMT_DENSE2) return 0;
+  if (fmt == SBL_FMT_NM) return n_out * (k / 8);
+  return -1;
+}
+
+int64_t sbl_workspace_bytes(int64_t n_out, int64_t k) {
+  (void)n_out;
+  (void)k;
+  return sbl::kWorkspaceBytes;
+}
+
+int sbl_quant_weights(const uint16_t* w_bf16, int64_t n_out, int64_t k, int32_t n, int32_t m,
+                      float* beta, uint8_t* mask_bits, int8_t* codes, int32_t fmt,
+                      uint8_t* packed, uint8_t* meta, void* workspace, int64_t workspace_bytes,
+                      sbl_stream stream) {
+  if (!w_bf16 || !beta) return SBL_ERR_NULL;
+  if (packed && fmt == SBL_FMT_NM && !meta) return SBL_ERR_NULL;
+  if (!workspace || workspace_bytes < sbl::kWorkspaceBytes) return SBL_ERR_WORKSPACE;
+  if (n_out < 1 || !k_ok(k) || n_out * k > kMaxElems) return SBL_ERR_SHAPE;
+  if (!nm_ok(n, m)) return SBL_ERR_UNSUPPORTED;
+  if (packed && fmt != SBL_FMT_DENSE2 && fmt != SBL_FMT_NM) return SBL_ERR_UNSUPPORTED;
+  if (!aligned(w_bf16, 16) || !aligned(beta, 4) || !aligned(workspace, 16) ||
+      (mask_bits && !aligned(mask_bits, 16)) || (codes && !aligned(codes, 16)) ||
+      (packed && !aligned(packed, 16)) || (meta && !aligned(meta, 16)))
+    return SBL_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t total = n_out * k;
+  int st = launch_status(sbl::launch_beta(w_bf16, total, reinterpret_cast<uint64_t*>(workspace), beta, s));
+  if (st != SBL_OK) return st;
+  return launch_status(sbl::launch_mask_pack(w_bf16, total, n, m, beta, mask_bits, codes,
+                                             packed ? fmt : SBL_FMT_DENSE2, packed,
+                                             fmt == SBL_FMT_NM ? meta : nullptr, s));
+}
+
+int sbl_pack(const int8_t* codes, const uint8_t* mask_bits, int64_t n_out, int64_t k, int32_t n,
+             int32_t m, int32_t fmt, uint8_t* packed, uint8_t* meta, sbl_stream stream) {
+  if (!codes || !packed) return SBL_ERR_NULL;
+  if (fmt == SBL_FMT_NM && !mask_bits) return SBL_ERR_NULL;
+  if (n_out < 1 || !k_ok(k) || n_out * k > kMaxElems) return SBL_ERR_SHAPE;
+  if (fmt != SBL_FMT_DENSE2 && fmt != SBL_FMT_NM) return SBL_ERR_UNSUPPORTED;
+  if (!nm_ok(n, m)) return SBL_ERR_UNSUPPORTED;
+  if (!aligned(codes, 16) || !aligned(packed, 16) || (mask_bits && !aligned(mask_bits, 16)) ||
+      (meta && !aligned(meta, 16)))
+    return SBL_ERR_ALIGN;
+  return launch_status(sbl::launch_pack(codes, mask_bits, n_out * k, n, m, fmt, packed,
+                                        fmt == SBL_FMT_NM ? meta : nullptr,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+int sbl_quant_acts(const float* x, int64_t m_tok, int64_t k, int8_t* xq, float* gamma,
+                   sbl_stream stream) {
+  if (m_tok < 0 || m_tok > kMaxTokens || !k_ok(k)) return SBL_ERR_SHAPE;
+  if (m_tok == 0) return SBL_OK;
+  if (!x || !xq || !gamma) return SBL_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(gamma, 4)) return SBL_ERR_ALIGN;
+  return launch_status(sbl::launch_quant_acts(x, m_tok, k, xq, gamma,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+int sbl_linear(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
+               const float* beta, const int8_t* xq, const float* gamma, int64_t m_tok,
+               int64_t n_out, int64_t k, float* y, int32_t* acc, sbl_stream stream) {
+  if (m_tok < 0 || m_tok > kMaxTokens || n_out < 0 || !k_ok(k) || n_out * k > kMaxElems)
+    return SBL_ERR_SHAPE;
+  if (fmt != SBL_FMT_DENSE2 && fmt != SBL_FMT_NM) return SBL_ERR_UNSUPPORTED;
+  if (fmt == SBL_FMT_NM && !nm_ok(n, m)) return SBL_ERR_UNSUPPORTED;
+  if (m_tok == 0 || n_out == 0) return SBL_OK;
+  if (!packed || !beta || !xq || !gamma || !y) return SBL_ERR_NULL;
+  if (fmt == SBL_FMT_NM && !meta) return SBL_ERR_NULL;
+  if (!aligned(packed, 16) || !aligned(xq, 16) || !aligned(y, 4) || !aligned(beta, 4) ||
+      !aligned(gamma, 4) || (acc && !aligned(acc, 4)) || (meta && !aligned(meta, 16)))
+    return SBL_ERR_ALIGN;
+  return launch_status(sbl::launch_linear(packed, meta, fmt, n, m, beta, xq, gamma, m_tok, n_out,
+                                          k, y, acc, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

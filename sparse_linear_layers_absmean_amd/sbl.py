@@ -1,0 +1,226 @@
+"""Thin Python binding of libsbl (include/sbl.h) over PyTorch device tensors.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libsbl.so.  PyTorch supplies device memory and the current HIP stream.  The
+binding checks that each tensor is on the GPU, contiguous, of the right dtype
+and large enough for the sizes passed, so a kernel can never be handed a
+buffer smaller than it will touch.  There is no CPU fallback: if the library
+is missing, loading fails loudly.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first so libsbl binds to the same HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsbl.so")
+
+SBL_OK = 0
+SBL_FMT_DENSE2 = 0
+SBL_FMT_NM = 1
+ABI_VERSION = 1
+
+_c_i64 = ctypes.c_int64
+_c_i32 = ctypes.c_int32
+_c_p = ctypes.c_void_p
+
+_lib = None
+
+
+class SblError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        lib = load()
+        msg = lib.sbl_status_string(status).decode()
+        if status == 5:
+            msg += f" (hip error {lib.sbl_last_hip_error()})"
+        super().__init__(f"{func}: status {status}: {msg}")
+        self.status = status
+
+
+def load():
+    """Load libsbl.so (built in-tree by build.py / __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.sbl_abi_version.restype = ctypes.c_int
+    lib.sbl_status_string.restype = ctypes.c_char_p
+    lib.sbl_status_string.argtypes = [ctypes.c_int]
+    lib.sbl_last_hip_error.restype = ctypes.c_int
+    lib.sbl_packed_bytes.restype = _c_i64
+    lib.sbl_packed_bytes.argtypes = [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32]
+    lib.sbl_meta_bytes.restype = _c_i64
+    lib.sbl_meta_bytes.argtypes = [_c_i64, _c_i64, _c_i32]
+    lib.sbl_workspace_bytes.restype = _c_i64
+    lib.sbl_workspace_bytes.argtypes = [_c_i64, _c_i64]
+    lib.sbl_quant_weights.restype = ctypes.c_int
+    lib.sbl_quant_weights.argtypes = [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p,
+                                      _c_i32, _c_p, _c_p, _c_p, _c_i64, _c_p]
+    lib.sbl_pack.restype = ctypes.c_int
+    lib.sbl_pack.argtypes = [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p]
+    lib.sbl_quant_acts.restype = ctypes.c_int
+    lib.sbl_quant_acts.argtypes = [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]
+    lib.sbl_linear.restype = ctypes.c_int
+    lib.sbl_linear.argtypes = [_c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p,
+                               _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]
+    if lib.sbl_abi_version() != ABI_VERSION:
+        raise RuntimeError("libsbl.so ABI version mismatch: rebuild it")
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------- helpers
+
+def _ptr(t, dtype, nbytes: int, name: str):
+    """Device pointer of a contiguous tensor holding at least nbytes, or None."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(func: str, status: int):
+    if status != SBL_OK:
+        raise SblError(func, status)
+
+
+# ---------------------------------------------------------------- the C ABI, by name
+
+def sbl_abi_version() -> int:
+    return load().sbl_abi_version()
+
+
+def sbl_packed_bytes(n_out: int, k: int, n: int, m: int, fmt: int) -> int:
+    return load().sbl_packed_bytes(n_out, k, n, m, fmt)
+
+
+def sbl_meta_bytes(n_out: int, k: int, fmt: int) -> int:
+    return load().sbl_meta_bytes(n_out, k, fmt)
+
+
+def sbl_workspace_bytes(n_out: int = 1, k: int = 64) -> int:
+    return load().sbl_workspace_bytes(n_out, k)
+
+
+_W16 = (torch.int16, torch.uint16, torch.bfloat16)
+
+
+def sbl_quant_weights(w_bf16, n: int, m: int, beta, workspace, mask_bits=None, codes=None,
+                      fmt: int = SBL_FMT_DENSE2, packed=None, meta=None, stream=None):
+    """w_bf16: [n_out][k] BF16 (or its 16-bit patterns as int16/uint16)."""
+    lib = load()
+    n_out, k = w_bf16.shape
+    pb = lib.sbl_packed_bytes(n_out, k, n, m, fmt) if packed is not None else 0
+    mb = n_out * k // 8
+    st = lib.sbl_quant_weights(
+        _ptr(w_bf16, _W16, n_out * k * 2, "w_bf16"), n_out, k, n, m,
+        _ptr(beta, torch.float32, 4, "beta"),
+        _ptr(mask_bits, torch.uint8, mb, "mask_bits"),
+        _ptr(codes, torch.int8, n_out * k, "codes"),
+        fmt, _ptr(packed, torch.uint8, max(pb, 0), "packed"),
+        _ptr(meta, torch.uint8, mb, "meta") if fmt == SBL_FMT_NM else None,
+        _ptr(workspace, None, lib.sbl_workspace_bytes(n_out, k), "workspace"),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream))
+    _check("sbl_quant_weights", st)
+
+
+def sbl_pack(codes, mask_bits, n: int, m: int, fmt: int, packed, meta=None, stream=None):
+    lib = load()
+    n_out, k = codes.shape
+    pb = lib.sbl_packed_bytes(n_out, k, n, m, fmt)
+    mb = n_out * k // 8
+    st = lib.sbl_pack(_ptr(codes, torch.int8, n_out * k, "codes"),
+                      _ptr(mask_bits, torch.uint8, mb, "mask_bits") if fmt == SBL_FMT_NM else None,
+                      n_out, k, n, m, fmt, _ptr(packed, torch.uint8, max(pb, 0), "packed"),
+                      _ptr(meta, torch.uint8, mb, "meta") if fmt == SBL_FMT_NM else None,
+                      _stream(stream))
+    _check("sbl_pack", st)
+
+
+def sbl_quant_acts(x, xq, gamma, stream=None):
+    lib = load()
+    m_tok, k = x.shape
+    st = lib.sbl_quant_acts(_ptr(x, torch.float32, m_tok * k * 4, "x"), m_tok, k,
+                            _ptr(xq, torch.int8, m_tok * k, "xq"),
+                            _ptr(gamma, torch.float32, m_tok * 4, "gamma"), _stream(stream))
+    _check("sbl_quant_acts", st)
+
+
+def sbl_linear(packed, meta, fmt: int, n: int, m: int, beta, xq, gamma, n_out: int, y, acc=None,
+               stream=None):
+    lib = load()
+    m_tok, k = xq.shape
+    pb = lib.sbl_packed_bytes(n_out, k, n, m, fmt) if n_out > 0 else 0
+    mb = n_out * k // 8
+    st = lib.sbl_linear(_ptr(packed, torch.uint8, max(pb, 0), "packed"),
+                        _ptr(meta, torch.uint8, mb, "meta") if fmt == SBL_FMT_NM else None,
+                        fmt, n, m, _ptr(beta, torch.float32, 4, "beta"),
+                        _ptr(xq, torch.int8, m_tok * k, "xq"),
+                        _ptr(gamma, torch.float32, m_tok * 4, "gamma"), m_tok, n_out, k,
+                        _ptr(y, torch.float32, m_tok * n_out * 4, "y"),
+                        _ptr(acc, torch.int32, m_tok * n_out * 4, "acc"), _stream(stream))
+    _check("sbl_linear", st)
+
+
+# ---------------------------------------------------------------- allocating conveniences
+
+def new_workspace(device="cuda"):
+    return torch.empty(sbl_workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+def quant_weights(w_bf16, n: int, m: int, fmt: int = SBL_FMT_DENSE2, want_codes: bool = False,
+                  workspace=None, stream=None):
+    """Allocate outputs and run sbl_quant_weights; returns a dict of device tensors."""
+    n_out, k = w_bf16.shape
+    dev = w_bf16.device
+    out = {"beta": torch.empty(1, dtype=torch.float32, device=dev),
+           "mask": torch.empty((n_out, k // 8), dtype=torch.uint8, device=dev)}
+    pb = sbl_packed_bytes(n_out, k, n, m, fmt)
+    if pb < 0:
+        raise ValueError("unsupported shape or pattern")
+    out["packed"] = torch.empty(pb, dtype=torch.uint8, device=dev)
+    out["meta"] = out["mask"] if fmt == SBL_FMT_NM else None
+    out["codes"] = torch.empty((n_out, k), dtype=torch.int8, device=dev) if want_codes else None
+    ws = workspace if workspace is not None else new_workspace(dev)
+    sbl_quant_weights(w_bf16, n, m, out["beta"], ws, mask_bits=out["mask"], codes=out["codes"],
+                      fmt=fmt, packed=out["packed"], meta=out["meta"], stream=stream)
+    return out
+
+
+def quant_acts(x, stream=None):
+    m_tok, k = x.shape
+    xq = torch.empty((m_tok, k), dtype=torch.int8, device=x.device)
+    gamma = torch.empty(m_tok, dtype=torch.float32, device=x.device)
+    sbl_quant_acts(x, xq, gamma, stream=stream)
+    return xq, gamma
+
+
+def linear(packed, meta, fmt, n, m, beta, xq, gamma, n_out, want_acc=False, stream=None):
+    m_tok = xq.shape[0]
+    y = torch.empty((m_tok, n_out), dtype=torch.float32, device=xq.device)
+    acc = torch.empty((m_tok, n_out), dtype=torch.int32, device=xq.device) if want_acc else None
+    sbl_linear(packed, meta, fmt, n, m, beta, xq, gamma, n_out, y, acc, stream=stream)
+    return y, acc

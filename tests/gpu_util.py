@@ -1,0 +1,91 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+(via the thin binding) and the CPU oracle on the same seeded inputs."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from oracle import sbl_oracle as O
+
+FMT_DENSE2, FMT_NM = 0, 1
+Y_RTOL = 1e-6          # fp32 outputs: relative error bound (exact zeros where acc == 0)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray):
+    import torch
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+def gpu_quant_weights(bits: np.ndarray, n: int, m: int, fmt: int):
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    n_out, k = bits.shape
+    w = to_dev(bits)
+    beta = torch.empty(1, dtype=torch.float32, device="cuda")
+    mask = torch.empty((n_out, k // 8), dtype=torch.uint8, device="cuda")
+    codes = torch.empty((n_out, k), dtype=torch.int8, device="cuda")
+    packed = torch.empty(sbl.sbl_packed_bytes(n_out, k, n, m, fmt), dtype=torch.uint8, device="cuda")
+    meta = torch.empty((n_out, k // 8), dtype=torch.uint8, device="cuda") if fmt == FMT_NM else None
+    ws = sbl.new_workspace()
+    sbl.sbl_quant_weights(w, n, m, beta, ws, mask_bits=mask, codes=codes, fmt=fmt, packed=packed,
+                          meta=meta)
+    return dict(beta=beta, mask=mask, codes=codes, packed=packed, meta=meta)
+
+
+def gpu_forward(bits: np.ndarray, x: np.ndarray, n: int, m: int, fmt: int):
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    n_out, k = bits.shape
+    out = gpu_quant_weights(bits, n, m, fmt)
+    xd = to_dev(x.astype(np.float32))
+    xq, gamma = sbl.quant_acts(xd)
+    y, acc = sbl.linear(out["packed"], out["meta"], fmt, n, m, out["beta"], xq, gamma, n_out,
+                        want_acc=True)
+    torch.cuda.synchronize()
+    res = {key: (to_np(v) if v is not None else None) for key, v in out.items()}
+    res.update(xq=to_np(xq), gamma=to_np(gamma), y=to_np(y), acc=to_np(acc))
+    return res
+
+
+def oracle_forward(bits: np.ndarray, x: np.ndarray, n: int, m: int):
+    r = O.forward(bits, x, n, m)
+    r["bitmap"] = O.pack_bitmap(r["keep"])
+    r["dense2"] = O.pack_dense2(r["codes"])
+    r["nm"] = O.pack_nm(r["codes"], r["keep"], n, m) if (bits.shape[1] * n // m) % 4 == 0 else None
+    return r
+
+
+def check_y(y_gpu, y_ref, acc_ref):
+    nz = acc_ref != 0
+    assert np.all(y_gpu[~nz] == 0)
+    if nz.any():
+        rel = np.abs(y_gpu[nz].astype(np.float64) / y_ref[nz].astype(np.float64) - 1.0)
+        assert rel.max() <= Y_RTOL, rel.max()
+
+
+def compare_all(g, r, fmt: int, n_out: int):
+    assert g["beta"][0] == r["beta"], (g["beta"][0], r["beta"])
+    assert np.array_equal(g["mask"], r["bitmap"])
+    assert np.array_equal(g["codes"], r["codes"])
+    if fmt == FMT_DENSE2:
+        assert np.array_equal(g["packed"].reshape(n_out, -1), r["dense2"])
+    else:
+        assert np.array_equal(g["packed"].reshape(n_out, -1), r["nm"])
+        assert np.array_equal(g["meta"], r["bitmap"])
+    assert np.array_equal(g["gamma"], r["gamma"])
+    assert np.array_equal(g["xq"], r["q"])
+    assert np.array_equal(g["acc"], r["acc"])
+    check_y(g["y"], r["y"], r["acc"])

@@ -1,0 +1,180 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, sizes its buffers correctly and rejects bad arguments on the host
+(before any HIP call) with the documented status codes."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sbl.h")
+LIB = os.path.join(ROOT, "sparse_linear_layers_absmean_amd", "libsbl.so")
+
+# Validation calls below pass fake (never dereferenced) device addresses.  They
+# must be rejected on the host; as a belt-and-braces guard they are not run
+# on a machine that has a GPU, where a validation bug could reach a kernel.
+HAS_GPU_NODE = os.path.exists("/dev/kfd")
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sbl_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libsbl.so is not built (run __graft_entry__.build())")
+    import torch  # noqa: F401  (same HIP runtime as the tests that use the GPU)
+    from sparse_linear_layers_absmean_amd import sbl
+    return sbl.load()
+
+
+def test_header_declares_the_four_calls():
+    fns = _header_functions()
+    for f in ["sbl_quant_weights", "sbl_pack", "sbl_quant_acts", "sbl_linear"]:
+        assert f in fns
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (sbl_[a-z0-9_]+)", out))
+    for f in _header_functions():
+        assert f in exported, f
+        assert hasattr(lib, f)
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.sbl_abi_version() == 1
+    for st in range(7):
+        assert len(lib.sbl_status_string(st)) > 0
+    assert lib.sbl_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("n_out,k", [(1, 64), (256, 256), (1536, 4096), (8640, 3200), (3, 131072)])
+def test_packed_and_meta_bytes(lib, n_out, k):
+    assert lib.sbl_packed_bytes(n_out, k, 6, 8, 0) == n_out * k // 4
+    assert lib.sbl_packed_bytes(n_out, k, 6, 8, 1) == n_out * k * 6 // 32
+    assert lib.sbl_packed_bytes(n_out, k, 2, 4, 1) == n_out * k * 2 // 16
+    assert lib.sbl_packed_bytes(n_out, k, 5, 8, 1) == n_out * k * 5 // 32
+    assert lib.sbl_meta_bytes(n_out, k, 0) == 0
+    assert lib.sbl_meta_bytes(n_out, k, 1) == n_out * k // 8
+    assert lib.sbl_workspace_bytes(n_out, k) >= 2080
+
+
+def test_packed_bytes_closed_form_bits_per_weight(lib):
+    # DENSE2 holds 2 bits/weight; N:M 6:8 holds 2.5 (codes 1.5 + bitmap 1); 2:4 holds 2 (1 + 1)
+    n_out, k = 1024, 4096
+    w = n_out * k
+    assert lib.sbl_packed_bytes(n_out, k, 6, 8, 0) * 8 == 2 * w
+    assert (lib.sbl_packed_bytes(n_out, k, 6, 8, 1) + lib.sbl_meta_bytes(n_out, k, 1)) * 8 == 2.5 * w
+    assert (lib.sbl_packed_bytes(n_out, k, 2, 4, 1) + lib.sbl_meta_bytes(n_out, k, 1)) * 8 == 2 * w
+
+
+@pytest.mark.parametrize("args", [(0, 64, 6, 8, 0), (4, 0, 6, 8, 0), (4, 96, 6, 8, 0),
+                                  (4, 262144, 6, 8, 0), (4, 64, 0, 8, 1), (4, 64, 9, 8, 1),
+                                  (4, 64, 2, 3, 1), (4, 64, 6, 8, 7)])
+def test_packed_bytes_rejects(lib, args):
+    assert lib.sbl_packed_bytes(*args) == -1
+
+
+A = 1 << 20          # a 16-byte aligned fake address (never dereferenced)
+S = ctypes.c_void_p
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation runs only on GPU-less hosts")
+def test_quant_weights_validation(lib):
+    f = lib.sbl_quant_weights
+    ws = lib.sbl_workspace_bytes(4, 64)
+    ok = dict(w=A, n_out=4, k=64, n=6, m=8, beta=A, mask=A, codes=A, fmt=0, packed=A, meta=A,
+              ws=A, wsb=ws, s=None)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["w"], a["n_out"], a["k"], a["n"], a["m"], a["beta"], a["mask"], a["codes"],
+                 a["fmt"], a["packed"], a["meta"], a["ws"], a["wsb"], a["s"])
+
+    assert call(w=None) == 1
+    assert call(beta=None) == 1
+    assert call(fmt=1, meta=None) == 1
+    assert call(ws=None) == 6
+    assert call(wsb=ws - 1) == 6
+    assert call(n_out=0) == 2
+    assert call(k=96) == 2
+    assert call(k=0) == 2
+    assert call(k=262144) == 2
+    assert call(n_out=1 << 30, k=131072) == 2
+    assert call(n=7, m=6) == 4
+    assert call(n=0) == 4
+    assert call(n=9) == 4
+    assert call(fmt=3) == 4
+    assert call(w=A + 2) == 3
+    assert call(beta=A + 2) == 3
+    assert call(packed=A + 8) == 3
+    assert call(mask=A + 1) == 3
+    assert call(codes=A + 4) == 3
+    assert call(ws=A + 8) == 3
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation runs only on GPU-less hosts")
+def test_pack_validation(lib):
+    f = lib.sbl_pack
+    assert f(None, A, 4, 64, 6, 8, 1, A, A, None) == 1
+    assert f(A, None, 4, 64, 6, 8, 1, A, A, None) == 1
+    assert f(A, A, 4, 64, 6, 8, 0, None, None, None) == 1
+    assert f(A, A, 4, 80, 6, 8, 0, A, None, None) == 2
+    assert f(A, A, 0, 64, 6, 8, 0, A, None, None) == 2
+    assert f(A, A, 4, 64, 6, 8, 2, A, None, None) == 4
+    assert f(A, A, 4, 64, 5, 4, 1, A, A, None) == 4
+    assert f(A + 4, A, 4, 64, 6, 8, 0, A, None, None) == 3
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation runs only on GPU-less hosts")
+def test_quant_acts_validation(lib):
+    f = lib.sbl_quant_acts
+    assert f(A, 0, 64, A, A, None) == 0                 # empty batch: no-op
+    assert f(None, 0, 64, None, None, None) == 0
+    assert f(A, -1, 64, A, A, None) == 2
+    assert f(A, 1, 63, A, A, None) == 2
+    assert f(A, 1, 0, A, A, None) == 2
+    assert f(A, (1 << 24) + 1, 64, A, A, None) == 2
+    assert f(None, 1, 64, A, A, None) == 1
+    assert f(A, 1, 64, None, A, None) == 1
+    assert f(A, 1, 64, A, None, None) == 1
+    assert f(A + 4, 1, 64, A, A, None) == 3
+    assert f(A, 1, 64, A + 2, A, None) == 3
+    assert f(A, 1, 64, A, A + 1, None) == 3
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation runs only on GPU-less hosts")
+def test_linear_validation(lib):
+    f = lib.sbl_linear
+    base = [A, A, 0, 6, 8, A, A, A, 4, 16, 64, A, A, None]
+
+    def call(i_val):
+        a = list(base)
+        for i, v in i_val:
+            a[i] = v
+        return f(*a)
+
+    assert call([(8, 0)]) == 0                       # m_tok = 0: no-op
+    assert call([(9, 0)]) == 0                       # n_out = 0: no-op
+    assert call([(8, -1)]) == 2
+    assert call([(10, 100)]) == 2
+    assert call([(10, 0)]) == 2
+    assert call([(2, 5)]) == 4
+    assert call([(2, 1), (3, 3), (4, 2)]) == 4       # NM with 3:2
+    assert call([(0, None)]) == 1
+    assert call([(5, None)]) == 1
+    assert call([(6, None)]) == 1
+    assert call([(7, None)]) == 1
+    assert call([(11, None)]) == 1
+    assert call([(2, 1), (1, None)]) == 1            # NM needs meta
+    assert call([(0, A + 8)]) == 3
+    assert call([(6, A + 4)]) == 3
+    assert call([(11, A + 2)]) == 3
+    assert call([(12, A + 1)]) == 3
