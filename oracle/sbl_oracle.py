@@ -38,7 +38,8 @@ listed with its reason in the design notes):
     divisor is exact.
   * rescale: y = RN_fp32(fp32(acc) * RN_fp32(RN_fp32(beta_eff * gamma_eff) * 2^-7)).
   * byte formats (the pages only speak of "metadata" for the kernel) are
-    defined in `pack_dense2`, `pack_bitmap` and `pack_nm` below.
+    defined in `pack_dense2`, `pack_bitmap` and `pack_nm` below; they are
+    this implementation's choice, not the pages'.
 
 Non-finite inputs are a precondition violation: the functions raise.
 
@@ -210,23 +211,35 @@ def quant_weights(bits: np.ndarray, n: int, m: int):
 # --------------------------------------------------------------------------
 
 def pack_dense2(codes: np.ndarray) -> np.ndarray:
-    """DENSE2: byte n*(k/4) + k/4, bits 2*(k%4)..+1 hold u = c + 1 in {0,1,2}."""
+    """DENSE2: 2 bits per weight, u = c + 1 in {0,1,2} (3 is never written).
+
+    Row r occupies bytes r*(k/4) .. r*(k/4) + k/4 - 1.  Within it, each run of
+    16 weights k = 16b .. 16b+15 fills the 4 bytes 4b .. 4b+3: weight k lives
+    in byte 4*(k // 16) + (k % 4), at bit offset 2*((k // 4) % 4).  (So byte
+    4b + j holds weights 16b + j + 4s at bit pairs s = 0..3: shifting the
+    little-endian word right by 2s and masking 0x03030303 yields the u of
+    weights 16b+4s .. 16b+4s+3 in byte order.)
+    """
     c = np.asarray(codes, dtype=np.int8)
     n_out, k = c.shape
-    if k % 4:
-        raise ValueError("k must be a multiple of 4")
-    u = (c.astype(np.int16) + 1).astype(np.uint8).reshape(n_out, k // 4, 4)
+    if k % 16:
+        raise ValueError("k must be a multiple of 16")
+    u = (c.astype(np.int16) + 1).astype(np.uint8)
     out = np.zeros((n_out, k // 4), dtype=np.uint8)
-    for s in range(4):
-        out |= (u[..., s] << (2 * s)).astype(np.uint8)
+    for kk in range(16):
+        byte = 4 * np.arange(k // 16) + (kk % 4)
+        out[:, byte] |= (u[:, kk::16] << (2 * (kk // 4))).astype(np.uint8)
     return out
 
 
 def unpack_dense2(packed: np.ndarray, k: int) -> np.ndarray:
     p = np.asarray(packed, dtype=np.uint8)
     n_out = p.shape[0]
-    u = np.stack([(p >> (2 * s)) & 3 for s in range(4)], axis=-1).reshape(n_out, k)
-    return (u.astype(np.int16) - 1).astype(np.int8)
+    codes = np.empty((n_out, k), dtype=np.int8)
+    for kk in range(16):
+        byte = 4 * np.arange(k // 16) + (kk % 4)
+        codes[:, kk::16] = ((p[:, byte] >> (2 * (kk // 4))) & 3).astype(np.int16) - 1
+    return codes
 
 
 def pack_bitmap(keep: np.ndarray) -> np.ndarray:

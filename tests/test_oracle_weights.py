@@ -171,3 +171,21 @@ def test_pack_round_trips():
             assert nm.shape == (8, 128 * n // m // 4)
             assert np.array_equal(O.unpack_nm(nm, bm, n, m, 128), codes)
         assert not np.any(((d2[..., None] >> np.array([0, 2, 4, 6], np.uint8)) & 3) == 3)
+
+
+def test_dense2_layout_per_element_and_word_decode():
+    # per-element statement of the layout, and the property it is chosen for:
+    # (word >> 2s) & 0x03030303 gives u of weights 16b+4s .. 16b+4s+3 in byte order
+    rng = np.random.default_rng(67)
+    codes = rng.integers(-1, 2, (3, 64)).astype(np.int8)
+    p = O.pack_dense2(codes)
+    for r in range(3):
+        for kk in range(64):
+            byte = p[r, 4 * (kk // 16) + kk % 4]
+            assert ((int(byte) >> (2 * ((kk // 4) % 4))) & 3) - 1 == codes[r, kk]
+        words = p[r].view("<u4")
+        for b in range(4):
+            for s in range(4):
+                d = (int(words[b]) >> (2 * s)) & 0x03030303
+                got = [((d >> (8 * j)) & 3) - 1 for j in range(4)]
+                assert got == codes[r, 16 * b + 4 * s: 16 * b + 4 * s + 4].tolist()
