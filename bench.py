@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Benchmark of the Sparse-BitLinear hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input: for
+each of the 7 matrices of a transformer block (q, k, v, o, gate, up, down)
+  sbl_quant_weights  exact absmean beta + N:M mask from the BF16 masters +
+                     ternary codes + packing (the per-training-step recompute)
+  sbl_quant_acts     per-token absmax int8 activations
+  sbl_linear         ternary x int8 product + fp32 rescale (GEMV at decode)
+Default workload: decode of a 0.7B-class block (hidden 1536, FFN 4096), one
+token, 6:8 N:M format.  Inputs are seeded synthetic data resident in HBM; the
+steps rotate over enough distinct copies (>= 512 MB) that the 256 MB
+Infinity Cache cannot serve a step from the previous one.
+
+Printed: one JSON line.  `value` is the step's algorithmic bytes (BF16
+masters read once, packed codes written and read, activations, outputs) per
+second; the `roofline*` objects give per-kernel rates from HIP-event timing of
+back-to-back launches; `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Sparse-BitLinear GEMV weight GB/s + prefill int8 TOPS, as % of MI355X peak"
+HBM_PEAK_GBPS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+
+FORMATS = {"dense2": (0, 6, 8), "nm68": (1, 6, 8), "nm24": (1, 2, 4)}
+
+WORKLOADS = {
+    # name: (synth workload, hidden, ffn, m_tok, description)
+    "decode_0p7b": ("b0p7", 1536, 4096, 1,
+                    "Decode GEMV, M=1 token, 0.7B-class block: hidden 1536, FFN 4096"),
+    "decode_3b": ("b3", 3200, 8640, 1, "Decode GEMV, 3B-class block: hidden 3200, FFN 8640"),
+    "prefill_3b": ("b3_prefill", 3200, 8640, 2048,
+                   "Prefill GEMM, M=2048 tokens, 3B-class block: hidden 3200, FFN 8640"),
+    "train_13b": ("b13", 5120, 13824, 4096,
+                  "Training-step path, 13B-class block: hidden 5120, FFN 13824, M=4096"),
+    "decode_70b": ("b70", 8192, 28672, 1, "Decode GEMV, M=1, 70B-class block: hidden 8192, FFN 28672"),
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="decode_0p7b", choices=sorted(WORKLOADS))
+    p.add_argument("--fmt", default="nm68", choices=sorted(FORMATS))
+    p.add_argument("--m-tok", type=int, default=None)
+    p.add_argument("--pool-mb", type=float, default=560.0,
+                   help="minimum bytes of distinct BF16 master copies the steps rotate over")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM measurement")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def block(h, f):
+    import synth
+    return synth.block_shapes(h, f)
+
+
+class Timer:
+    """HIP events on torch's current stream (every libsbl launch goes there)."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.a.record()
+
+    def stop_ms(self):
+        self.b.record()
+        self.b.synchronize()
+        return self.a.elapsed_time(self.b)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding is a design note, not a measured path", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    from sparse_linear_layers_absmean_amd import sbl
+
+    sbl.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wname, h, f, m_tok, desc = WORKLOADS[args.workload]
+    if args.m_tok:
+        m_tok = args.m_tok
+    fmt, n, m = FORMATS[args.fmt]
+    mats = block(h, f)
+    block_w = sum(no * k for _, no, k in mats)
+    copies = max(2, int(np.ceil(args.pool_mb * 1e6 / (2 * block_w))))
+    copies = min(copies, 64)
+
+    # ---------------- inputs: seeded synthetic, resident in HBM
+    t0 = time.time()
+    masters = [[torch.from_numpy(synth.workload_masters(wname, i, no, k, copy=c).view(np.int16)).to(dev)
+                for i, (_, no, k) in enumerate(mats)] for c in range(copies)]
+    # a block's matrices read 4 inputs: q/k/v share one, o one, gate/up one, down one
+    groups = [[0, 1, 2], [3], [4, 5], [6]]
+    xs = [[torch.from_numpy(synth.workload_acts(wname, grp[0], m_tok, mats[grp[0]][2], copy=c)).to(dev)
+           for grp in groups] for c in range(copies)]
+    gen_s = time.time() - t0
+
+    def alloc_out(no, k):
+        pb = sbl.sbl_packed_bytes(no, k, n, m, fmt)
+        return dict(beta=torch.empty(1, dtype=torch.float32, device=dev),
+                    packed=torch.empty(pb, dtype=torch.uint8, device=dev),
+                    meta=torch.empty((no, k // 8), dtype=torch.uint8, device=dev) if fmt == 1 else None,
+                    y=torch.empty((m_tok, no), dtype=torch.float32, device=dev), n_out=no)
+
+    outs = [[alloc_out(no, k) for (_, no, k) in mats] for _ in range(copies)]
+    acts = [[dict(xq=torch.empty((m_tok, mats[grp[0]][2]), dtype=torch.int8, device=dev),
+                  gamma=torch.empty(m_tok, dtype=torch.float32, device=dev)) for grp in groups]
+            for _ in range(copies)]
+    ws = torch.zeros(sbl.sbl_workspace_bytes(), dtype=torch.uint8, device=dev)
+
+    def items_of(c, gi, pool=None):
+        src = outs[c] if pool is None else pool
+        return [dict(src[i], xq=acts[c][gi]["xq"], gamma=acts[c][gi]["gamma"]) for i in groups[gi]]
+
+    def qw_all(c):
+        for i, (_, no, k) in enumerate(mats):
+            o = outs[c][i]
+            sbl.sbl_quant_weights(masters[c][i], n, m, o["beta"], ws, fmt=fmt, packed=o["packed"],
+                                  meta=o["meta"])
+
+    def qa_all(c):
+        for gi in range(len(groups)):
+            sbl.sbl_quant_acts(xs[c][gi], acts[c][gi]["xq"], acts[c][gi]["gamma"])
+
+    def step(c):
+        qw_all(c)
+        for gi in range(len(groups)):
+            sbl.sbl_quant_acts(xs[c][gi], acts[c][gi]["xq"], acts[c][gi]["gamma"])
+            sbl.sbl_linear_batch(items_of(c, gi), fmt, n, m)
+
+    # ---------------- algorithmic bytes
+    def packed_b(no, k):
+        return sbl.sbl_packed_bytes(no, k, n, m, fmt) + max(0, sbl.sbl_meta_bytes(no, k, fmt))
+
+    qw_bytes = sum(2 * no * k + packed_b(no, k) for _, no, k in mats)
+    qa_bytes = sum(m_tok * mats[grp[0]][2] * 5 + 4 * m_tok for grp in groups)
+    lin_bytes = sum(packed_b(no, k) + m_tok * k + 4 * m_tok + 4 * m_tok * no + 4 for _, no, k in mats)
+    step_bytes = qw_bytes + qa_bytes + lin_bytes
+    weight_bytes = sum(packed_b(no, k) for _, no, k in mats)
+
+    # ---------------- whole-step timing
+    for s in range(args.warmup):
+        step(s % copies)
+    torch.cuda.synchronize()
+    tm = Timer()
+    tm.start()
+    for s in range(args.steps):
+        step(s % copies)
+    step_ms = tm.stop_ms() / args.steps
+    torch.cuda.synchronize()
+
+    # ---------------- per-call rates (back-to-back launches, rotating copies)
+    def time_calls(fn, reps):
+        for r in range(min(reps, copies)):
+            fn(r % copies)
+        torch.cuda.synchronize()
+        tm.start()
+        for r in range(reps):
+            fn(r % copies)
+        return tm.stop_ms() / reps
+
+    # GEMV pool: distinct packed buffers totalling >= 512 MB (cold Infinity Cache)
+    gemv_copies = max(copies, int(np.ceil(560e6 / weight_bytes)))
+    gemv_pool = []
+    for c in range(gemv_copies):
+        gemv_pool.append([dict(o, packed=o["packed"].clone(),
+                               meta=o["meta"].clone() if o["meta"] is not None else None)
+                          for o in outs[c % copies]])
+
+    def lin_all(c):
+        for gi in range(len(groups)):
+            sbl.sbl_linear_batch(items_of(c % copies, gi, gemv_pool[c % gemv_copies]), fmt, n, m)
+
+    reps = max(20, args.steps)
+    qw_ms = time_calls(qw_all, reps)
+    qa_ms = time_calls(qa_all, reps)
+    lin_ms = time_calls(lin_all, max(reps, 2 * gemv_copies))
+
+    def roof(bytes_per, ms, kernel, launches, traffic=None):
+        gbps = bytes_per / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernel,
+                "launches_per_step": launches, "avg_launch_us": round(ms * 1e3 / launches, 3)}
+
+    per_call = {
+        "sbl_quant_weights": roof(qw_bytes, qw_ms, "beta_kernel + mask_pack_kernel", 7),
+        "sbl_quant_acts": roof(qa_bytes, qa_ms, "quant_acts_kernel", len(groups)),
+        "sbl_linear": roof(lin_bytes, lin_ms, "gemv_kernel (grouped: qkv, o, gate+up, down)",
+                           len(groups)),
+    }
+    dominant = max(per_call, key=lambda kk: {"sbl_quant_weights": qw_ms, "sbl_quant_acts": qa_ms,
+                                              "sbl_linear": lin_ms}[kk])
+    gemv_gbps = weight_bytes / (lin_ms * 1e-3) / 1e9
+
+    # ---------------- prefill GEMM (3B block, M = 2048 tokens), int8 ops
+    prefill = None
+    if not args.no_prefill:
+        prefill = bench_prefill(torch, np, synth, sbl, dev, tm)
+
+    # ---------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(np, synth, wname, mats, m_tok, n, m, fmt, args.cpu_seconds, step_bytes)
+
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded N(0,0.02) BF16 masters, N(0,1) fp32 activations)",
+        "config": {"workload": desc, "format": args.fmt, "m_tok": m_tok, "matrices": len(mats),
+                   "block_weights": block_w, "rotation_copies": copies,
+                   "step_algorithmic_bytes": step_bytes},
+        "roofline": dict(per_call[dominant], call=dominant),
+        "roofline_gemv": {"bound": "hbm", "achieved": round(gemv_gbps, 1), "peak": HBM_PEAK_GBPS,
+                          "unit": "GB/s", "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4),
+                          "traffic": None, "weight_bytes_per_step": weight_bytes,
+                          "note": "packed weight bytes / sbl_linear_batch time, 4 grouped launches per block"},
+        "per_call": per_call,
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+        "input_gen_s": round(gen_s, 1),
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_prefill(torch, np, synth, sbl, dev, tm):
+    """3B-class block at M = 2048 tokens, 6:8 N:M weights: sbl_linear (GEMM) TOPS."""
+    wname, h, f, m_tok = "b3_prefill", 3200, 8640, 2048
+    fmt, n, m = 1, 6, 8
+    mats = synth.block_shapes(h, f)
+    ws = torch.zeros(sbl.sbl_workspace_bytes(), dtype=torch.uint8, device=dev)
+    items = []
+    for i, (_, no, k) in enumerate(mats):
+        w = torch.from_numpy(synth.workload_masters(wname, i, no, k).view(np.int16)).to(dev)
+        o = sbl.quant_weights(w, n, m, fmt=fmt, workspace=ws)
+        x = torch.from_numpy(synth.workload_acts(wname, i, m_tok, k)).to(dev)
+        xq, gamma = sbl.quant_acts(x)
+        y = torch.empty((m_tok, no), dtype=torch.float32, device=dev)
+        items.append((o, xq, gamma, y, no, k))
+        del w, x
+
+    groups = [[0, 1, 2], [3], [4, 5], [6]]          # q/k/v, o, gate/up, down
+
+    def run():
+        for grp in groups:
+            sbl.sbl_linear_batch([dict(packed=items[i][0]["packed"], meta=items[i][0]["meta"],
+                                       beta=items[i][0]["beta"], xq=items[i][1], gamma=items[i][2],
+                                       n_out=items[i][4], y=items[i][3]) for i in grp], fmt, n, m)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    reps = 5
+    tm.start()
+    for _ in range(reps):
+        run()
+    ms = tm.stop_ms() / reps
+    ops = sum(2 * m_tok * no * k for *_, no, k in items)
+    tops = ops / (ms * 1e-3) / 1e12
+    return {"workload": "Prefill GEMM, M=2048 tokens, 3B-class block (hidden 3200, FFN 8640), 6:8 N:M",
+            "ms_per_block": round(ms, 4), "int8_TOPS": round(tops, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS,
+                         "unit": "TOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": None}}
+
+
+def cpu_baseline(np, synth, wname, mats, m_tok, n, m, fmt, budget_s, step_bytes):
+    """The CPU oracle, untuned, on the same workload: whole blocks until the budget is spent."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import sbl_oracle as O
+    done_bytes, blocks, t_total = 0, 0, 0.0
+    with threadpool_limits(1):
+        while t_total < budget_s and blocks < 3:
+            for i, (_, no, k) in enumerate(mats):
+                bits = synth.workload_masters(wname, i, no, k)
+                first = {0: 0, 1: 0, 2: 0, 3: 3, 4: 4, 5: 4, 6: 6}[i]    # shared block inputs
+                x = synth.workload_acts(wname, first, m_tok, k)
+                t = time.perf_counter()
+                beta, keep, codes = O.quant_weights(bits, n, m)
+                if fmt == 1:
+                    O.pack_nm(codes, keep, n, m)
+                    O.pack_bitmap(keep)
+                else:
+                    O.pack_dense2(codes)
+                q, gamma = O.quant_acts(x)
+                O.linear(codes, q, beta, gamma)
+                t_total += time.perf_counter() - t
+            blocks += 1
+            done_bytes += step_bytes
+    gbps = done_bytes / t_total / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{blocks} full block step(s) of the same workload ({len(mats)} matrices), "
+                      f"{t_total:.1f} s single-threaded NumPy",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

@@ -39,8 +39,12 @@
  *
  * Byte formats (our own; the pages only say the kernel receives N:M
  * "metadata"):
- *  DENSE2  [n_out][k/4] bytes: byte r*(k/4) + k/4, bits 2*(k%4)..+1 hold
- *          u = c + 1 in {0,1,2} (3 is never written).  2 bits per weight.
+ *  DENSE2  [n_out][k/4] bytes, 2 bits per weight holding u = c + 1 in
+ *          {0,1,2} (3 is never written).  Weight kk of row r lives in byte
+ *          r*(k/4) + 4*(kk/16) + kk%4, at bit offset 2*((kk/4)%4): in every
+ *          16-weight little-endian word, (word >> 2s) & 0x03030303 gives the
+ *          u of weights 4s..4s+3 in byte order, i.e. an int8 MFMA operand in
+ *          natural k order after 7 VALU ops per 16 weights.
  *  BITMAP  [n_out][k/8] bytes: byte r*(k/8) + k/8, bit k%8 = 1 when kept.
  *          Serves as the mask output and as the N:M metadata.
  *  NM      [n_out][k*n/(4m)] bytes: the kept positions of row r, in
@@ -94,8 +98,13 @@ int64_t sbl_packed_bytes(int64_t n_out, int64_t k, int32_t n, int32_t m, int32_t
 int64_t sbl_meta_bytes(int64_t n_out, int64_t k, int32_t fmt);
 
 /* Bytes of device workspace sbl_quant_weights needs (the exact beta
- * reduction); the same for every shape.  Contents need no initialisation. */
+ * reduction); the same for every shape. */
 int64_t sbl_workspace_bytes(int64_t n_out, int64_t k);
+
+/* Zero-fill a workspace (enqueued on `stream`).  A workspace must be
+ * zero-filled once before its first use -- by this call or by allocating it
+ * zero-filled; every sbl_quant_weights call leaves it zero-filled again. */
+int sbl_workspace_init(void* workspace, int64_t workspace_bytes, sbl_stream stream);
 
 /* Weight preparation: beta, N:M mask, ternary codes, packing -- one pass of
  * the per-training-step recompute (mask recomputed from the current BF16
@@ -112,8 +121,9 @@ int64_t sbl_workspace_bytes(int64_t n_out, int64_t k);
  *   meta       [n_out][k/8] BITMAP output for fmt == SBL_FMT_NM (required
  *              there when packed != NULL); ignored for DENSE2.
  *   workspace  device scratch of sbl_workspace_bytes() bytes, 16-byte
- *              aligned; overwritten.  Calls sharing one workspace must be
- *              ordered on one stream.
+ *              aligned, zero-filled before its first use (see
+ *              sbl_workspace_init) and left zero-filled by every call.
+ *              Calls sharing one workspace must be ordered on one stream.
  */
 int sbl_quant_weights(const uint16_t* w_bf16, int64_t n_out, int64_t k, int32_t n, int32_t m,
                       float* beta, uint8_t* mask_bits, int8_t* codes,
@@ -158,6 +168,28 @@ int sbl_linear(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t 
                const float* beta, const int8_t* xq, const float* gamma,
                int64_t m_tok, int64_t n_out, int64_t k, float* y, int32_t* acc,
                sbl_stream stream);
+
+/* One product of a batch (the arguments of one sbl_linear call). */
+typedef struct {
+  const uint8_t* packed;
+  const uint8_t* meta;     /* NM: BITMAP metadata; DENSE2: NULL              */
+  const float* beta;
+  const int8_t* xq;
+  const float* gamma;
+  int64_t m_tok, n_out, k;
+  float* y;
+  int32_t* acc;            /* nullable                                       */
+} sbl_linear_item;
+
+/* Several independent products (e.g. the q, k, v projections of one block)
+ * in as few launches as possible: decode-sized items (m_tok <= 16) share one
+ * bandwidth-bound GEMV launch per 8 items; larger ones each run the GEMM.
+ * `items` is a HOST array of `count` (1..256) descriptors, all in format
+ * `fmt` with pattern n:m; every item is validated as sbl_linear validates
+ * its arguments before anything is enqueued.  Results are bit-identical to
+ * calling sbl_linear on each item. */
+int sbl_linear_batch(const sbl_linear_item* items, int32_t count, int32_t fmt, int32_t n,
+                     int32_t m, sbl_stream stream);
 
 #ifdef __cplusplus
 }

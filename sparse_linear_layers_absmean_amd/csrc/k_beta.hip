@@ -17,6 +17,8 @@
 //  * The last workgroup to finish rebuilds the exact sum as a multi-word
 //    integer, divides it by n_out*k with a bit-serial long division and
 //    rounds once to fp32 (nearest, ties to even), subnormals included.
+//    It then zero-fills the accumulators, so the workspace is ready for the
+//    next call (it must be zero-filled once before its first use).
 #include "sbl_internal.h"
 
 namespace sbl {
@@ -56,46 +58,56 @@ __device__ void add_shifted(uint32_t* L, uint64_t v, int s) {
   }
 }
 
-__device__ __forceinline__ uint32_t get_bit(const uint32_t* L, int pos) {
-  return pos < 0 ? 0u : (L[pos >> 5] >> (pos & 31)) & 1u;
-}
-
-// exact RN_fp32(S * 2^-133 / n); S in limbs
+// exact RN_fp32(S * 2^-133 / n) for the integer S held in limbs (shared memory)
 __device__ float round_quotient(const uint32_t* L, uint64_t n) {
   int top = -1;
   for (int i = kLimbs - 1; i >= 0 && top < 0; --i)
     if (L[i]) top = i * 32 + 31 - __clz(L[i]);
   if (top < 0) return 0.0f;
+  // 64-bit window of S whose bit 63 is S's bit `top`; bits of S below the
+  // window only matter as a sticky flag.  The division below consumes at most
+  // log2(n) + 26 <= 61 bits (n <= 2^34), so the window always suffices.
+  const int lo = top - 63;
+  uint64_t win;
+  bool below = false;
+  if (lo >= 0) {
+    const int li = lo >> 5, sh = lo & 31;
+    const uint64_t a = (uint64_t)L[li] | ((uint64_t)L[li + 1] << 32);
+    const uint64_t c = (li + 2 < kLimbs) ? L[li + 2] : 0u;
+    win = (a >> sh) | (sh ? (c << (64 - sh)) : 0u);
+    for (int i = 0; i < li && !below; ++i) below = L[i] != 0;
+    below = below || (L[li] & ((1u << sh) - 1u)) != 0;
+  } else {
+    win = ((uint64_t)L[0] | ((uint64_t)L[1] << 32)) << (-lo);
+  }
   uint64_t rem = 0, q = 0;
-  int lead = 1 << 30, lsb = 0, last = -18;
+  bool found = false;
+  int lsb = 0;
   for (int pos = top; pos >= -17; --pos) {
-    rem = (rem << 1) | get_bit(L, pos);
+    rem = (rem << 1) | (win >> 63);
+    win <<= 1;
     const uint32_t qb = rem >= n;
     if (qb) rem -= n;
-    if (lead == (1 << 30)) {
+    if (!found) {
       if (qb) {
-        lead = pos;
+        found = true;
         q = 1;
-        lsb = max(pos - 23, -16);       // 2^-149 = position -16 in 2^-133 units
+        lsb = max(pos - 23, -16);                   // 2^-149 is position -16 in 2^-133 units
       }
     } else {
       q = (q << 1) | qb;
     }
-    if (lead != (1 << 30) && pos == lsb - 1) {  // guard bit collected
-      last = pos;
-      break;
-    }
+    if (found && pos == lsb - 1) break;             // guard bit collected
   }
-  if (lead == (1 << 30)) return 0.0f;          // below 2^-150: rounds to zero
-  bool sticky = rem != 0;
-  for (int pos = last - 1; pos >= 0 && !sticky; --pos) sticky = get_bit(L, pos) != 0;
+  if (!found) return 0.0f;                          // below 2^-150: rounds to zero
+  const bool sticky = rem != 0 || win != 0 || below;
   const uint64_t guard = q & 1u;
   uint64_t mant = q >> 1;
   if (guard && (sticky || (mant & 1u))) ++mant;
   return ldexpf((float)mant, lsb - 133);
 }
 
-__global__ __launch_bounds__(kBetaThreads) void beta_kernel(const uint4* __restrict__ w, int64_t nvec,
+__global__ __launch_bounds__(kBetaThreads) void beta_kernel(const u32x4* __restrict__ w, int64_t nvec,
                                                            uint64_t* __restrict__ ws,
                                                            float* __restrict__ beta_out,
                                                            uint64_t n_total) {
@@ -130,6 +142,8 @@ __global__ __launch_bounds__(kBetaThreads) void beta_kernel(const uint4* __restr
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) units += __shfl_xor(units, off, 64);
   __shared__ unsigned long long wave_sum[kBetaThreads / 64];
+  __shared__ unsigned long long nz_bins[kBetaThreads / 64];
+  __shared__ uint64_t bins[256];
   __shared__ bool is_last;
   __shared__ uint32_t limbs[kLimbs];
   if ((threadIdx.x & 63) == 0) wave_sum[threadIdx.x >> 6] = units;
@@ -147,15 +161,34 @@ __global__ __launch_bounds__(kBetaThreads) void beta_kernel(const uint4* __restr
     is_last = ticket == (unsigned long long)gridDim.x - 1;
   }
   __syncthreads();
-  if (!is_last || threadIdx.x != 0) return;
+  if (!is_last) return;
+  // Last workgroup: every other one has finished its atomics.  Read the
+  // per-exponent bins in parallel, then leave the workspace zero-filled for
+  // the next call.
   __threadfence();
+  const uint64_t b = ld_agent(&ws[kWsBins + threadIdx.x]);
+  bins[threadIdx.x] = b;
+  ws[kWsBins + threadIdx.x] = 0;
+  const unsigned long long nz = __ballot(b != 0);
+  if ((threadIdx.x & 63) == 0) nz_bins[threadIdx.x >> 6] = nz;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  const uint64_t fast_lo = ld_agent(&ws[kWsFastLo]);
+  const uint64_t fast_hi = ld_agent(&ws[kWsFastHi]);
+  ws[kWsFastLo] = 0;
+  ws[kWsFastHi] = 0;
+  ws[kWsCount] = 0;
   for (int i = 0; i < kLimbs; ++i) limbs[i] = 0;
-  for (int e = 0; e < 256; ++e) {
-    const uint64_t b = ld_agent(&ws[kWsBins + e]);
-    add_shifted(limbs, b, max(e, 1) - 1);
+  for (int wv = 0; wv < kBetaThreads / 64; ++wv) {
+    unsigned long long m = nz_bins[wv];
+    while (m) {
+      const int e = wv * 64 + __ffsll(m) - 1;
+      m &= m - 1;
+      add_shifted(limbs, bins[e], max(e, 1) - 1);
+    }
   }
-  add_shifted(limbs, ld_agent(&ws[kWsFastLo]), 95);        // 2^-38 = 2^95 * 2^-133
-  add_shifted(limbs, ld_agent(&ws[kWsFastHi]), 95 + 64);
+  add_shifted(limbs, fast_lo, 95);        // 2^-38 = 2^95 * 2^-133
+  add_shifted(limbs, fast_hi, 95 + 64);
   beta_out[0] = round_quotient(limbs, n_total);
 }
 
@@ -165,9 +198,13 @@ __global__ void zero_ws_kernel(uint64_t* ws) {
 
 }  // namespace
 
+hipError_t launch_workspace_init(uint64_t* ws, hipStream_t s) {
+  hipLaunchKernelGGL(zero_ws_kernel, dim3(1), dim3(256), 0, s, ws);
+  return hipGetLastError();
+}
+
 hipError_t launch_beta(const uint16_t* w, int64_t total, uint64_t* ws, float* beta,
                        hipStream_t s) {
-  hipLaunchKernelGGL(zero_ws_kernel, dim3(1), dim3(256), 0, s, ws);
   const int64_t nvec = total / 8;
   int64_t blocks = (nvec + kBetaThreads * 8 - 1) / (kBetaThreads * 8);
   blocks = blocks < 1 ? 1 : (blocks > 4096 ? 4096 : blocks);
@@ -175,7 +212,7 @@ hipError_t launch_beta(const uint16_t* w, int64_t total, uint64_t* ws, float* be
       (nvec + kBetaThreads * kMaxIterPerThread - 1) / (kBetaThreads * kMaxIterPerThread);
   if (blocks < min_blocks) blocks = min_blocks;
   hipLaunchKernelGGL(beta_kernel, dim3((unsigned)blocks), dim3(kBetaThreads), 0, s,
-                     reinterpret_cast<const uint4*>(w), nvec, ws, beta, (uint64_t)total);
+                     reinterpret_cast<const u32x4*>(w), nvec, ws, beta, (uint64_t)total);
   return hipGetLastError();
 }
 

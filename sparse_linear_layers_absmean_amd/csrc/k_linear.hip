@@ -1,84 +1,183 @@
 // Ternary x int8 product with fp32 rescale (BitLinear operation, bitnet.cpp
 // article "Fundamento matematico" item 3: y = W~ x~ beta gamma / Qb; no bias
-// per the BitNet spec).
+// per the BitNet spec), decode-sized token counts (m_tok <= 16).
 //
 // int8 MFMA formulation (gfx950 v_mfma_i32_16x16x64_i8): weights are the A
 // operand (16 output rows x 64 k), activations the B operand (64 k x 16
-// tokens).  A DENSE2 dword holds 16 weights as u = c + 1 in 2-bit fields;
-// (dword >> 2s) & 0x03030303 yields four int8 lanes u(k0+4j+s), j = 0..3, so
-// the 16 weights decode with 7 VALU ops into the A operand in a permuted
-// k-order.  The activations are permuted the same way (a 4x4 byte transpose
-// with v_perm), so the contraction over the 64 k-slots is unchanged:
-//   sum_k u q = sum_k c q + sum_k q,   hence acc = MFMA result - sum_k q.
-// The per-token sum of q comes from v_dot4 with 0x01010101 on the B operand.
-// All integer steps are exact; int32 cannot overflow since |acc| <= 127 k < 2^24.
-#include "sbl_internal.h"
+// tokens).  A lane holds 16 consecutive k of one row (A) or one token (B).
+//  * DENSE2: one 16-weight word decodes with 7 VALU ops into four dwords of
+//    u = c + 1 bytes in natural k order; then sum_k u q = sum_k c q + sum_k q,
+//    so acc = MFMA result - sum_k q, with sum_k q from v_dot4 against 0x01010101.
+//  * N:M 6:8 and 2:4: per group, a 256-entry LDS table spreads the 2-bit kept
+//    codes into int8 c bytes, a second table (indexed by the metadata bitmap
+//    byte) gives v_perm selectors that scatter them to their k positions and
+//    zero the pruned ones: 2 table reads + 2 v_perm per 8 weights.
+// Work split: a workgroup owns 32 output rows (two 16-row tiles per wave) and
+// its 8 waves split k; a 64-lane load brings 16 rows x 64 weights per tile.
+// Partial int32 tiles are summed through LDS, then rescaled.  Up to 8
+// independent matrices share one launch (grouped GEMV).  Everything integer
+// is exact: |acc| <= 127 k < 2^24.
+#include "sbl_decode.h"
 
 namespace sbl {
 
 namespace {
 
-typedef int32_t v4i __attribute__((ext_vector_type(4)));
+using namespace dec;
 
-__device__ __forceinline__ v4i transpose4x4(uint32_t n0, uint32_t n1, uint32_t n2, uint32_t n3) {
-  // out_s byte j = byte s of n_j
-  const uint32_t x0 = __builtin_amdgcn_perm(n1, n0, 0x05010400u);
-  const uint32_t x1 = __builtin_amdgcn_perm(n1, n0, 0x07030602u);
-  const uint32_t y0 = __builtin_amdgcn_perm(n3, n2, 0x05010400u);
-  const uint32_t y1 = __builtin_amdgcn_perm(n3, n2, 0x07030602u);
-  v4i r;
-  r[0] = (int32_t)__builtin_amdgcn_perm(y0, x0, 0x05040100u);
-  r[1] = (int32_t)__builtin_amdgcn_perm(y0, x0, 0x07060302u);
-  r[2] = (int32_t)__builtin_amdgcn_perm(y1, x1, 0x05040100u);
-  r[3] = (int32_t)__builtin_amdgcn_perm(y1, x1, 0x07060302u);
-  return r;
+constexpr int kTW = 2;                 // 16-row tiles per wave
+constexpr int kKS = 8;                 // waves per workgroup (k split)
+constexpr int kGemvThreads = 64 * kKS;
+
+template <int KIND>
+struct Frag {
+  u32x4 b[4];
+  ARaw<KIND> a[kTW];
+};
+
+template <int KIND>
+__device__ __forceinline__ void load_frag(Frag<KIND>& f, const LinDesc& d, int64_t row0, int r, int t,
+                                          int sb, int nkb) {
+  const int g = (threadIdx.x & 63) >> 4;
+  const int kb = 4 * sb + g;
+  const bool kok = kb < nkb;
+  if (kok && t < d.m_tok) {
+    const int8_t* xp = d.xq + (int64_t)t * d.k + (int64_t)kb * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.b[i] = ld16(xp + 16 * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.b[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int ti = 0; ti < kTW; ++ti) {
+    const int64_t row = row0 + 16 * ti + r;
+    load_a<KIND>(f.a[ti], d, row, kb, kok && row < d.n_out);
+  }
 }
 
-__device__ __forceinline__ v4i decode_dense2(uint32_t wd) {
-  v4i a;
-  a[0] = (int32_t)(wd & 0x03030303u);
-  a[1] = (int32_t)((wd >> 2) & 0x03030303u);
-  a[2] = (int32_t)((wd >> 4) & 0x03030303u);
-  a[3] = (int32_t)((wd >> 6) & 0x03030303u);
-  return a;
+template <int KIND>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const LinBatch batch) {
+  __shared__ NmLut lut;
+  __shared__ int32_t red[kKS][kTW * 4][64];
+  __shared__ int32_t redq[kKS][64];
+  if (KIND != kDense2) build_lut<KIND>(lut);
+  int di = 0;
+  for (int i = 1; i < batch.count; ++i)
+    if ((int)blockIdx.x >= batch.start[i]) di = i;
+  const LinDesc& d = batch.d[di];
+  const int64_t row0 = (int64_t)((int)blockIdx.x - batch.start[di]) * (16 * kTW);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int nkb = d.k / 64;
+  const int nsb = (nkb + 3) / 4;
+  const int sb0 = wave * nsb / kKS, sb1 = (wave + 1) * nsb / kKS;
+  if (KIND != kDense2) __syncthreads();
+
+  v4i c[kTW];
+#pragma unroll
+  for (int ti = 0; ti < kTW; ++ti) c[ti] = v4i{0, 0, 0, 0};
+  int qs = 0;
+  if (sb0 < sb1) {
+    Frag<KIND> cur;
+    load_frag<KIND>(cur, d, row0, r, r, sb0, nkb);
+    for (int sb = sb0; sb < sb1; ++sb) {
+      Frag<KIND> nxt;
+      const bool more = sb + 1 < sb1;
+      if (more) load_frag<KIND>(nxt, d, row0, r, r, sb + 1, nkb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const v4i b = {(int32_t)cur.b[i][0], (int32_t)cur.b[i][1], (int32_t)cur.b[i][2],
+                       (int32_t)cur.b[i][3]};
+#pragma unroll
+        for (int ti = 0; ti < kTW; ++ti)
+          c[ti] = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_a<KIND>(cur.a[ti], i, lut), b, c[ti], 0, 0, 0);
+        if (KIND == kDense2) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) qs = __builtin_amdgcn_sdot4(b[j], 0x01010101, qs, false);
+        }
+      }
+      if (more) cur = nxt;
+    }
+  }
+  if (KIND == kDense2) {
+    qs += __shfl_xor(qs, 16, 64);
+    qs += __shfl_xor(qs, 32, 64);                    // sum of q over this wave's k for token lane%16
+  }
+#pragma unroll
+  for (int ti = 0; ti < kTW; ++ti)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][ti * 4 + v][lane] = c[ti][v];
+  redq[wave][lane] = qs;
+  __syncthreads();
+  if (wave >= kTW) return;
+  const int ti = wave;
+  int32_t sum[4] = {0, 0, 0, 0};
+  int32_t qsum = 0;
+#pragma unroll
+  for (int w = 0; w < kKS; ++w) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sum[v] += red[w][ti * 4 + v][lane];
+    qsum += redq[w][lane];
+  }
+  const int t = r;                                   // C[4*(lane/16)+v][lane%16]: column = token
+  if (t >= d.m_tok) return;
+  const float s = out_scale(d.beta, d.gamma, t);
+  const int64_t rbase = row0 + 16 * ti + 4 * g;
+  float* yrow = d.y + (int64_t)t * d.n_out;
+  int32_t* arow = d.acc ? d.acc + (int64_t)t * d.n_out : nullptr;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int64_t row = rbase + v;
+    if (row < d.n_out) {
+      const int32_t a = sum[v] - (KIND == kDense2 ? qsum : 0);
+      yrow[row] = (float)a * s;
+      if (arow) arow[row] = a;
+    }
+  }
 }
 
-// 16 weights of row r at k0 .. k0+15 from the N:M format, as a DENSE2 dword
+// ---------------------------------------------------------------------------
+// Generic path: any token count, any n:m.  One wave = 16 rows x 16 tokens over
+// the whole k; weights decoded to natural-order int8 bytes per 16 k.
+// ---------------------------------------------------------------------------
+
 template <int M>
-__device__ uint32_t nm_dword(const uint8_t* __restrict__ codes_row, const uint8_t* __restrict__ meta_row,
-                             int n, int64_t k0) {
-  uint32_t out = 0;
+__device__ v4i nm_bytes16(const uint8_t* __restrict__ codes_row, const uint8_t* __restrict__ meta_row,
+                          int n, int64_t k0) {
+  uint32_t out[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int gi = 0; gi < 16 / M; ++gi) {
-    const int64_t kg = k0 + gi * M;                 // first k of the group
-    const int64_t G = kg / M;                       // group index within the row
+    const int64_t kg = k0 + gi * M;
     uint32_t bits = meta_row[kg >> 3];
     if (M == 4) bits = (bits >> (kg & 4)) & 0xFu;
-    int64_t pos = 2 * G * n;                        // bit offset of the group's first code
+    int64_t pos = 2 * (kg / M) * n;
     int kept = 0;
 #pragma unroll
     for (int j = 0; j < M; ++j) {
-      uint32_t u = 1u;
+      uint32_t cb = 0;
       if (((bits >> j) & 1u) && kept < n) {
-        u = (codes_row[pos >> 3] >> (pos & 7)) & 3u;
+        const uint32_t u = (codes_row[pos >> 3] >> (pos & 7)) & 3u;
+        cb = (u - 1u) & 0xFFu;
         pos += 2;
         ++kept;
       }
-      out |= u << (2 * (gi * M + j));
+      const int p = gi * M + j;
+      out[p >> 2] |= cb << (8 * (p & 3));
     }
   }
-  return out;
+  return v4i{(int32_t)out[0], (int32_t)out[1], (int32_t)out[2], (int32_t)out[3]};
 }
 
 template <int FMT, int M>
-__global__ __launch_bounds__(256) void linear_mfma_kernel(const uint8_t* __restrict__ packed,
-                                                          const uint8_t* __restrict__ meta, int n,
-                                                          const float* __restrict__ beta,
-                                                          const int8_t* __restrict__ xq,
-                                                          const float* __restrict__ gamma,
-                                                          int64_t m_tok, int64_t n_out, int64_t k,
-                                                          float* __restrict__ y,
-                                                          int32_t* __restrict__ acc_out) {
+__global__ __launch_bounds__(256) void linear_generic_kernel(const uint8_t* __restrict__ packed,
+                                                             const uint8_t* __restrict__ meta, int n,
+                                                             const float* __restrict__ beta,
+                                                             const int8_t* __restrict__ xq,
+                                                             const float* __restrict__ gamma,
+                                                             int64_t m_tok, int64_t n_out, int64_t k,
+                                                             float* __restrict__ y,
+                                                             int32_t* __restrict__ acc_out) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row0 = (int64_t)blockIdx.x * 64 + wave * 16;
   const int64_t tok0 = (int64_t)blockIdx.y * 16;
@@ -88,57 +187,110 @@ __global__ __launch_bounds__(256) void linear_mfma_kernel(const uint8_t* __restr
   const bool row_ok = r < n_out, tok_ok = t < m_tok;
   const int64_t row_bytes = FMT == 0 ? k / 4 : k * n / (4 * M);
   const uint8_t* wrow = packed + (row_ok ? r : 0) * row_bytes;
-  const uint8_t* mrow = meta + (row_ok ? r : 0) * (k / 8);
+  const uint8_t* mrow = FMT == 0 ? nullptr : meta + (row_ok ? r : 0) * (k / 8);
   const int8_t* xrow = xq + (tok_ok ? t : 0) * k;
   v4i c = {0, 0, 0, 0};
   int qs = 0;
   for (int64_t kb = 0; kb < k; kb += 64) {
     const int64_t kk = kb + 16 * g;
-    uint32_t wd = 0x55555555u;                      // u = 1 everywhere: code 0
-    if (row_ok) {
-      if (FMT == 0) wd = reinterpret_cast<const uint32_t*>(wrow)[kk >> 4];
-      else wd = nm_dword<M>(wrow, mrow, n, kk);
-    }
-    uint4 nb = make_uint4(0, 0, 0, 0);
-    if (tok_ok) nb = *reinterpret_cast<const uint4*>(xrow + kk);
-    const v4i a = decode_dense2(wd);
-    const v4i b = transpose4x4(nb.x, nb.y, nb.z, nb.w);
+    v4i a = {0, 0, 0, 0};
+    if (FMT == 0) a = dense2_quad(row_ok ? reinterpret_cast<const uint32_t*>(wrow)[kk >> 4] : 0x55555555u);
+    else if (row_ok) a = nm_bytes16<M>(wrow, mrow, n, kk);
+    u32x4 nb = {0u, 0u, 0u, 0u};
+    if (tok_ok) nb = ld16(xrow + kk);
+    const v4i b = {(int32_t)nb[0], (int32_t)nb[1], (int32_t)nb[2], (int32_t)nb[3]};
     c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-    qs = __builtin_amdgcn_sdot4(b[0], 0x01010101, qs, false);
-    qs = __builtin_amdgcn_sdot4(b[1], 0x01010101, qs, false);
-    qs = __builtin_amdgcn_sdot4(b[2], 0x01010101, qs, false);
-    qs = __builtin_amdgcn_sdot4(b[3], 0x01010101, qs, false);
+    if (FMT == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qs = __builtin_amdgcn_sdot4(b[j], 0x01010101, qs, false);
+    }
   }
   qs += __shfl_xor(qs, 16, 64);
-  qs += __shfl_xor(qs, 32, 64);                     // sum of q over k for token t
+  qs += __shfl_xor(qs, 32, 64);
   if (!tok_ok) return;
-  const float bs = fmaxf(beta[0], 1e-5f);
-  const float gs = fmaxf(gamma[t], 1e-5f);
-  const float s = (bs * gs) * 0.0078125f;
+  const float s = out_scale(beta, gamma, t);
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int64_t row = row0 + 4 * g + v;            // C[4*(lane/16)+v][lane%16]
     if (row < n_out) {
-      const int32_t a = c[v] - qs;
+      const int32_t a = c[v] - (FMT == 0 ? qs : 0);
       y[t * n_out + row] = (float)a * s;
       if (acc_out) acc_out[t * n_out + row] = a;
     }
   }
 }
 
+int kind_of(int fmt, int n, int m) {
+  if (fmt == 0) return kDense2;
+  if (m == 8 && n == 6) return kNm68;
+  if (m == 4 && n == 2) return kNm24;
+  return -1;
+}
+
+hipError_t launch_gemv_group(int kind, const LinDesc* items, int count, hipStream_t s) {
+  LinBatch b = {};
+  int blocks = 0;
+  for (int i = 0; i < count; ++i) {
+    b.d[i] = items[i];
+    b.start[i] = blocks;
+    blocks += (int)((items[i].n_out + 16 * kTW - 1) / (16 * kTW));
+  }
+  b.start[count] = blocks;
+  b.count = count;
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks), block(kGemvThreads);
+  if (kind == kDense2) hipLaunchKernelGGL(gemv_kernel<kDense2>, grid, block, 0, s, b);
+  else if (kind == kNm68) hipLaunchKernelGGL(gemv_kernel<kNm68>, grid, block, 0, s, b);
+  else hipLaunchKernelGGL(gemv_kernel<kNm24>, grid, block, 0, s, b);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_linear(const uint8_t* packed, const uint8_t* meta, int fmt, int n, int m,
-                         const float* beta, const int8_t* xq, const float* gamma, int64_t m_tok,
-                         int64_t n_out, int64_t k, float* y, int32_t* acc, hipStream_t s) {
-  const dim3 grid((unsigned)((n_out + 63) / 64), (unsigned)((m_tok + 15) / 16)), block(256);
+hipError_t launch_linear_generic(const LinearArgs& a, int fmt, int n, int m, hipStream_t s) {
+  const dim3 grid((unsigned)((a.n_out + 63) / 64), (unsigned)((a.m_tok + 15) / 16)), block(256);
   if (fmt == 0)
-    hipLaunchKernelGGL((linear_mfma_kernel<0, 8>), grid, block, 0, s, packed, meta, n, beta, xq, gamma, m_tok, n_out, k, y, acc);
+    hipLaunchKernelGGL((linear_generic_kernel<0, 8>), grid, block, 0, s, a.packed, a.meta, n, a.beta, a.xq, a.gamma, a.m_tok, a.n_out, a.k, a.y, a.acc);
   else if (m == 8)
-    hipLaunchKernelGGL((linear_mfma_kernel<1, 8>), grid, block, 0, s, packed, meta, n, beta, xq, gamma, m_tok, n_out, k, y, acc);
+    hipLaunchKernelGGL((linear_generic_kernel<1, 8>), grid, block, 0, s, a.packed, a.meta, n, a.beta, a.xq, a.gamma, a.m_tok, a.n_out, a.k, a.y, a.acc);
   else
-    hipLaunchKernelGGL((linear_mfma_kernel<1, 4>), grid, block, 0, s, packed, meta, n, beta, xq, gamma, m_tok, n_out, k, y, acc);
+    hipLaunchKernelGGL((linear_generic_kernel<1, 4>), grid, block, 0, s, a.packed, a.meta, n, a.beta, a.xq, a.gamma, a.m_tok, a.n_out, a.k, a.y, a.acc);
   return hipGetLastError();
+}
+
+hipError_t launch_linear_batch(const LinearArgs* items, int count, int fmt, int n, int m,
+                               hipStream_t s) {
+  const int kind = kind_of(fmt, n, m);
+  LinDesc gemv[kMaxDesc];
+  LinearArgs gemm[kMaxDesc];
+  int nv = 0, nm = 0;
+  for (int i = 0; i < count; ++i) {
+    const LinearArgs& a = items[i];
+    if (a.m_tok == 0 || a.n_out == 0) continue;
+    hipError_t e = hipSuccess;
+    if (kind < 0) {
+      e = launch_linear_generic(a, fmt, n, m, s);
+    } else if (a.m_tok <= kGemvMaxTokens) {
+      gemv[nv++] = to_desc(a);
+      if (nv == kMaxDesc) {
+        e = launch_gemv_group(kind, gemv, nv, s);
+        nv = 0;
+      }
+    } else {
+      gemm[nm++] = a;
+      if (nm == kMaxDesc) {
+        e = launch_gemm_group(gemm, nm, kind, s);
+        nm = 0;
+      }
+    }
+    if (e != hipSuccess) return e;
+  }
+  if (nv) {
+    const hipError_t e = launch_gemv_group(kind, gemv, nv, s);
+    if (e != hipSuccess) return e;
+  }
+  if (nm) return launch_gemm_group(gemm, nm, kind, s);
+  return hipSuccess;
 }
 
 }  // namespace sbl

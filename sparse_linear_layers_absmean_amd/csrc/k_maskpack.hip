@@ -22,6 +22,7 @@
 // cross chunks (m divides 64) and chunks never cross rows (64 divides k), so
 // the matrix is processed as a flat array.  Per chunk it writes 16 bytes of
 // DENSE2, 8 bytes of bitmap, 64*n/m/4 bytes of N:M codes and 64 code bytes.
+// DENSE2 word layout: see d2_shift.
 #include "sbl_internal.h"
 
 namespace sbl {
@@ -29,6 +30,10 @@ namespace sbl {
 namespace {
 
 constexpr int kThreads = 256;
+
+// DENSE2 bit offset of weight p inside its 16-weight word: byte p%4, bit pair (p/4)%4,
+// so (word >> 2s) & 0x03030303 holds weights 4s .. 4s+3 in byte order.
+__device__ __forceinline__ int d2_shift(int p) { return 8 * (p & 3) + 2 * ((p >> 2) & 3); }
 
 struct ChunkOut {
   uint32_t d2[4];        // DENSE2: word q holds weights 16q .. 16q+15
@@ -146,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void mask_pack_kernel(const uint4* __rest
         const bool keep = key[j] > thr;
         const bool nz = keep && key[j] > thr_nz;
         const uint32_t u = nz ? (sgn[j] ? 0u : 2u) : 1u;
-        o.d2[idx >> 4] |= u << (2 * (idx & 15));
+        o.d2[idx >> 4] |= u << d2_shift(idx);
         o.keep |= (uint64_t)keep << idx;
         o.cb[idx >> 2] |= ((u - 1u) & 0xFFu) << (8 * (idx & 3));
         if (want_nm && keep) {
@@ -187,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const uint4* __restrict_
       for (int j = 0; j < M; ++j) {
         const int idx = g * M + j;
         const uint32_t u = ((cw[idx >> 2] >> (8 * (idx & 3))) + 1u) & 3u;
-        o.d2[idx >> 4] |= u << (2 * (idx & 15));
+        o.d2[idx >> 4] |= u << d2_shift(idx);
         if (fmt == 1 && ((keep >> idx) & 1) && kept < n) {
           nm_insert(o, u, 2 * (g * n + kept));
           ++kept;

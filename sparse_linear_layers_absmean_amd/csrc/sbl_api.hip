@@ -63,6 +63,14 @@ int64_t sbl_workspace_bytes(int64_t n_out, int64_t k) {
   return sbl::kWorkspaceBytes;
 }
 
+int sbl_workspace_init(void* workspace, int64_t workspace_bytes, sbl_stream stream) {
+  if (!workspace) return SBL_ERR_NULL;
+  if (workspace_bytes < sbl::kWorkspaceBytes) return SBL_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return SBL_ERR_ALIGN;
+  return launch_status(sbl::launch_workspace_init(reinterpret_cast<uint64_t*>(workspace),
+                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
 int sbl_quant_weights(const uint16_t* w_bf16, int64_t n_out, int64_t k, int32_t n, int32_t m,
                       float* beta, uint8_t* mask_bits, int8_t* codes, int32_t fmt,
                       uint8_t* packed, uint8_t* meta, void* workspace, int64_t workspace_bytes,
@@ -111,21 +119,62 @@ int sbl_quant_acts(const float* x, int64_t m_tok, int64_t k, int8_t* xq, float* 
                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
-int sbl_linear(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
-               const float* beta, const int8_t* xq, const float* gamma, int64_t m_tok,
-               int64_t n_out, int64_t k, float* y, int32_t* acc, sbl_stream stream) {
-  if (m_tok < 0 || m_tok > kMaxTokens || n_out < 0 || !k_ok(k) || n_out * k > kMaxElems)
+namespace {
+
+int check_linear(const sbl_linear_item& it, int32_t fmt, int32_t n, int32_t m) {
+  if (it.m_tok < 0 || it.m_tok > kMaxTokens || it.n_out < 0 || !k_ok(it.k) ||
+      it.n_out * it.k > kMaxElems)
     return SBL_ERR_SHAPE;
   if (fmt != SBL_FMT_DENSE2 && fmt != SBL_FMT_NM) return SBL_ERR_UNSUPPORTED;
   if (fmt == SBL_FMT_NM && !nm_ok(n, m)) return SBL_ERR_UNSUPPORTED;
-  if (m_tok == 0 || n_out == 0) return SBL_OK;
-  if (!packed || !beta || !xq || !gamma || !y) return SBL_ERR_NULL;
-  if (fmt == SBL_FMT_NM && !meta) return SBL_ERR_NULL;
-  if (!aligned(packed, 16) || !aligned(xq, 16) || !aligned(y, 4) || !aligned(beta, 4) ||
-      !aligned(gamma, 4) || (acc && !aligned(acc, 4)) || (meta && !aligned(meta, 16)))
+  if (it.m_tok == 0 || it.n_out == 0) return SBL_OK;
+  if (!it.packed || !it.beta || !it.xq || !it.gamma || !it.y) return SBL_ERR_NULL;
+  if (fmt == SBL_FMT_NM && !it.meta) return SBL_ERR_NULL;
+  if (!aligned(it.packed, 16) || !aligned(it.xq, 16) || !aligned(it.y, 4) ||
+      !aligned(it.beta, 4) || !aligned(it.gamma, 4) || (it.acc && !aligned(it.acc, 4)) ||
+      (it.meta && !aligned(it.meta, 16)))
     return SBL_ERR_ALIGN;
-  return launch_status(sbl::launch_linear(packed, meta, fmt, n, m, beta, xq, gamma, m_tok, n_out,
-                                          k, y, acc, reinterpret_cast<hipStream_t>(stream)));
+  return SBL_OK;
+}
+
+sbl::LinearArgs to_args(const sbl_linear_item& it, int32_t fmt) {
+  sbl::LinearArgs a;
+  a.packed = it.packed;
+  a.meta = fmt == SBL_FMT_NM ? it.meta : nullptr;
+  a.beta = it.beta;
+  a.xq = it.xq;
+  a.gamma = it.gamma;
+  a.m_tok = it.m_tok;
+  a.n_out = it.n_out;
+  a.k = it.k;
+  a.y = it.y;
+  a.acc = it.acc;
+  return a;
+}
+
+}  // namespace
+
+int sbl_linear(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
+               const float* beta, const int8_t* xq, const float* gamma, int64_t m_tok,
+               int64_t n_out, int64_t k, float* y, int32_t* acc, sbl_stream stream) {
+  const sbl_linear_item it = {packed, meta, beta, xq, gamma, m_tok, n_out, k, y, acc};
+  const int st = check_linear(it, fmt, n, m);
+  if (st != SBL_OK || m_tok == 0 || n_out == 0) return st;
+  const sbl::LinearArgs a = to_args(it, fmt);
+  return launch_status(sbl::launch_linear_batch(&a, 1, fmt, n, m, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int sbl_linear_batch(const sbl_linear_item* items, int32_t count, int32_t fmt, int32_t n,
+                     int32_t m, sbl_stream stream) {
+  if (!items) return SBL_ERR_NULL;
+  if (count < 1 || count > 256) return SBL_ERR_SHAPE;
+  sbl::LinearArgs args[256];
+  for (int i = 0; i < count; ++i) {
+    const int st = check_linear(items[i], fmt, n, m);
+    if (st != SBL_OK) return st;
+    args[i] = to_args(items[i], fmt);
+  }
+  return launch_status(sbl::launch_linear_batch(args, count, fmt, n, m, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -29,6 +29,8 @@ constexpr int64_t kWorkspaceBytes = 4096;
 // Weights handled by one thread of the mask/pack kernels (one 128-byte BF16 chunk).
 constexpr int kChunk = 64;
 
+hipError_t launch_workspace_init(uint64_t* ws, hipStream_t s);
+
 hipError_t launch_beta(const uint16_t* w, int64_t total, uint64_t* ws, float* beta,
                        hipStream_t s);
 
@@ -42,8 +44,28 @@ hipError_t launch_pack(const int8_t* codes, const uint8_t* mask, int64_t total, 
 hipError_t launch_quant_acts(const float* x, int64_t m_tok, int64_t k, int8_t* xq, float* gamma,
                              hipStream_t s);
 
-hipError_t launch_linear(const uint8_t* packed, const uint8_t* meta, int fmt, int n, int m,
-                         const float* beta, const int8_t* xq, const float* gamma, int64_t m_tok,
-                         int64_t n_out, int64_t k, float* y, int32_t* acc, hipStream_t s);
+struct LinearArgs {
+  const uint8_t* packed;
+  const uint8_t* meta;
+  const float* beta;
+  const int8_t* xq;
+  const float* gamma;
+  int64_t m_tok, n_out, k;
+  float* y;
+  int32_t* acc;
+};
+
+// token counts up to this run the grouped GEMV; larger ones the GEMM
+constexpr int64_t kGemvMaxTokens = 16;
+
+hipError_t launch_linear_batch(const LinearArgs* items, int count, int fmt, int n, int m,
+                               hipStream_t s);
+
+// any shape, any n:m (one wave per 16 rows x 16 tokens)
+hipError_t launch_linear_generic(const LinearArgs& a, int fmt, int n, int m, hipStream_t s);
+
+// up to 8 products with m_tok > kGemvMaxTokens in one launch, DENSE2 (kind 0),
+// N:M 6:8 (kind 1) or 2:4 (kind 2)
+hipError_t launch_gemm_group(const LinearArgs* items, int count, int kind, hipStream_t s);
 
 }  // namespace sbl

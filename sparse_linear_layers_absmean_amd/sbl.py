@@ -30,6 +30,12 @@ _c_p = ctypes.c_void_p
 _lib = None
 
 
+class LinearItem(ctypes.Structure):
+    """sbl_linear_item of include/sbl.h."""
+    _fields_ = [("packed", _c_p), ("meta", _c_p), ("beta", _c_p), ("xq", _c_p), ("gamma", _c_p),
+                ("m_tok", _c_i64), ("n_out", _c_i64), ("k", _c_i64), ("y", _c_p), ("acc", _c_p)]
+
+
 class SblError(RuntimeError):
     def __init__(self, func: str, status: int):
         lib = load()
@@ -58,6 +64,8 @@ def load():
     lib.sbl_meta_bytes.argtypes = [_c_i64, _c_i64, _c_i32]
     lib.sbl_workspace_bytes.restype = _c_i64
     lib.sbl_workspace_bytes.argtypes = [_c_i64, _c_i64]
+    lib.sbl_workspace_init.restype = ctypes.c_int
+    lib.sbl_workspace_init.argtypes = [_c_p, _c_i64, _c_p]
     lib.sbl_quant_weights.restype = ctypes.c_int
     lib.sbl_quant_weights.argtypes = [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p,
                                       _c_i32, _c_p, _c_p, _c_p, _c_i64, _c_p]
@@ -68,6 +76,8 @@ def load():
     lib.sbl_linear.restype = ctypes.c_int
     lib.sbl_linear.argtypes = [_c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p,
                                _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]
+    lib.sbl_linear_batch.restype = ctypes.c_int
+    lib.sbl_linear_batch.argtypes = [ctypes.POINTER(LinearItem), _c_i32, _c_i32, _c_i32, _c_i32, _c_p]
     if lib.sbl_abi_version() != ABI_VERSION:
         raise RuntimeError("libsbl.so ABI version mismatch: rebuild it")
     _lib = lib
@@ -122,6 +132,13 @@ def sbl_meta_bytes(n_out: int, k: int, fmt: int) -> int:
 
 def sbl_workspace_bytes(n_out: int = 1, k: int = 64) -> int:
     return load().sbl_workspace_bytes(n_out, k)
+
+
+def sbl_workspace_init(workspace, stream=None):
+    lib = load()
+    nbytes = lib.sbl_workspace_bytes(1, 64)
+    _check("sbl_workspace_init",
+           lib.sbl_workspace_init(_ptr(workspace, None, nbytes, "workspace"), nbytes, _stream(stream)))
 
 
 _W16 = (torch.int16, torch.uint16, torch.bfloat16)
@@ -185,10 +202,29 @@ def sbl_linear(packed, meta, fmt: int, n: int, m: int, beta, xq, gamma, n_out: i
     _check("sbl_linear", st)
 
 
+def sbl_linear_batch(items, fmt: int, n: int, m: int, stream=None):
+    """items: sequence of dicts with keys packed, meta, beta, xq, gamma, n_out, y[, acc]."""
+    lib = load()
+    arr = (LinearItem * len(items))()
+    for i, it in enumerate(items):
+        m_tok, k = it["xq"].shape
+        n_out = it["n_out"]
+        pb = lib.sbl_packed_bytes(n_out, k, n, m, fmt) if n_out > 0 else 0
+        arr[i] = LinearItem(
+            _ptr(it["packed"], torch.uint8, max(pb, 0), "packed"),
+            _ptr(it.get("meta"), torch.uint8, n_out * k // 8, "meta") if fmt == SBL_FMT_NM else None,
+            _ptr(it["beta"], torch.float32, 4, "beta"), _ptr(it["xq"], torch.int8, m_tok * k, "xq"),
+            _ptr(it["gamma"], torch.float32, m_tok * 4, "gamma"), m_tok, n_out, k,
+            _ptr(it["y"], torch.float32, m_tok * n_out * 4, "y"),
+            _ptr(it.get("acc"), torch.int32, m_tok * n_out * 4, "acc"))
+    _check("sbl_linear_batch", lib.sbl_linear_batch(arr, len(items), fmt, n, m, _stream(stream)))
+
+
 # ---------------------------------------------------------------- allocating conveniences
 
 def new_workspace(device="cuda"):
-    return torch.empty(sbl_workspace_bytes(), dtype=torch.uint8, device=device)
+    """A zero-filled workspace (sbl_quant_weights leaves it zero-filled again)."""
+    return torch.zeros(sbl_workspace_bytes(), dtype=torch.uint8, device=device)
 
 
 def quant_weights(w_bf16, n: int, m: int, fmt: int = SBL_FMT_DENSE2, want_codes: bool = False,

@@ -8,8 +8,8 @@ import pytest
 
 import synth
 from oracle import sbl_oracle as O
-from gpu_util import (FMT_DENSE2, FMT_NM, compare_all, gpu_forward, gpu_quant_weights,
-                            oracle_forward, say, to_dev, to_np)
+from gpu_util import (FMT_DENSE2, FMT_NM, check_y, compare_all, gpu_forward, gpu_quant_weights,
+                      oracle_forward, say, to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -176,3 +176,42 @@ def test_empty_batches_are_noops():
     y, acc = sbl.linear(w["packed"], None, FMT_DENSE2, 6, 8, w["beta"], xq, gamma, 16, want_acc=True)
     torch.cuda.synchronize()
     assert y.shape == (0, 16)
+
+
+@pytest.mark.parametrize("fmt,n,m", [(FMT_DENSE2, 6, 8), (FMT_NM, 6, 8), (FMT_NM, 2, 4), (FMT_NM, 5, 8)])
+def test_linear_batch_matches_single_calls(fmt, n, m):
+    """Grouped launches (decode items share one GEMV launch) give the oracle's results."""
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    rng = np.random.default_rng([21, fmt, n, m])
+    shapes = [(96, 128, 1), (200, 320, 3), (33, 64, 16), (130, 512, 2), (64, 192, 40), (17, 256, 1),
+              (300, 640, 5), (48, 128, 8), (80, 384, 1), (16, 64, 1)]
+    items, refs = [], []
+    for n_out, k, m_tok in shapes:
+        bits = synth.gaussian_masters(rng, n_out, k)
+        x = synth.gaussian_acts(rng, m_tok, k)
+        w = gpu_quant_weights(bits, n, m, fmt)
+        xq, gamma = sbl.quant_acts(to_dev(x))
+        y = torch.empty((m_tok, n_out), dtype=torch.float32, device="cuda")
+        acc = torch.empty((m_tok, n_out), dtype=torch.int32, device="cuda")
+        items.append(dict(packed=w["packed"], meta=w["meta"], beta=w["beta"], xq=xq, gamma=gamma,
+                          n_out=n_out, y=y, acc=acc))
+        refs.append(oracle_forward(bits, x, n, m))
+    say(f"linear_batch fmt={fmt} {n}:{m} items={len(items)}")
+    sbl.sbl_linear_batch(items, fmt, n, m)
+    torch.cuda.synchronize()
+    for it, r in zip(items, refs):
+        assert np.array_equal(to_np(it["acc"]), r["acc"])
+        check_y(to_np(it["y"]), r["y"], r["acc"])
+
+
+@pytest.mark.parametrize("fmt,n,m", [(FMT_DENSE2, 6, 8), (FMT_NM, 6, 8), (FMT_NM, 2, 4)])
+def test_gemm_multi_tile_ragged(fmt, n, m):
+    """Token counts above the decode range: several 256-row x 128-token tiles,
+    ragged in rows, tokens and k (a half 128-k step at the end)."""
+    rng = np.random.default_rng([31, fmt, n, m])
+    n_out, k, m_tok = 600, 704, 300
+    bits = synth.gaussian_masters(rng, n_out, k)
+    x = synth.gaussian_acts(rng, m_tok, k, t_row_frac=0.25)
+    say(f"gemm multi-tile fmt={fmt} {n}:{m}")
+    compare_all(gpu_forward(bits, x, n, m, fmt), oracle_forward(bits, x, n, m), fmt, n_out)
