@@ -4,19 +4,30 @@
 // is a dense contraction, so it runs on gfx950 int8 MFMA
 // (v_mfma_i32_32x32x32_i8, 32 rows x 32 tokens x 32 k per instruction).
 //
-// Tiling: a workgroup (4 waves) owns 256 weight rows x 128 tokens; wave
-// (wn, wt) owns rows 128*wn .. +128 (4 MFMA row tiles) x tokens 64*wt .. +64
-// (2 column tiles).  Per 128-k step:
-//  * activations: the workgroup stages a 128 token x 128 byte int8 tile in
-//    LDS (double-buffered, rows padded to 144 bytes so the 16-byte operand
-//    reads of 8 consecutive tokens hit distinct banks); each B operand read
-//    feeds 4 MFMAs (one per row tile);
-//  * weights: every lane loads its packed bytes straight from global memory
-//    (16 bytes of DENSE2 = 64 weights per row tile) and decodes them into A
-//    operands in registers (7 VALU ops per 16 weights; N:M via LDS tables +
-//    v_perm), one k-step ahead of use.
+// Tiling: a workgroup (4 waves) owns 256 weight rows x 256 tokens; wave w
+// owns rows 64w .. +64 (2 MFMA row tiles) x all 256 tokens (8 column
+// tiles): 16 accumulator tiles (256 AGPRs), one wave per SIMD.  Splitting
+// the rows (not the tokens) across waves means every weight operand is
+// decoded exactly once per workgroup; VALU work interleaved with MFMAs is
+// what limits a one-wave-per-SIMD int8 GEMM, so it is kept minimal.
+// The k loop advances 64 k per step (two MFMA sub-steps):
+//  * activations: each step's 256 token x 64 byte int8 tile is fetched into
+//    registers kDepth steps ahead with buffer loads, written to one of two
+//    LDS buffers one step ahead of use, and read back as B operands; 16-byte
+//    chunks are XOR-swizzled so consecutive tokens read distinct banks.
+//    Each B operand feeds 2 MFMAs (one per row tile).
+//  * weights: every lane fetches its packed words kDepth-1 steps ahead
+//    straight into registers and decodes them into A operands (7 VALU ops
+//    per 16 weights; N:M via LDS tables + v_perm); each A operand feeds 8
+//    MFMAs.
+//  * the per-step workgroup barrier waits only for LDS traffic, never for
+//    the global loads in flight.
+// The deep register pipeline keeps several steps of global loads in flight,
+// which one wave per SIMD needs to cover HBM / Infinity Cache latency.
 // DENSE2 feeds u = c + 1 to the MFMA and subtracts sum_k q per token at the
-// end (the sums come from v_dot4 on the B operands); N:M decodes to c.
+// end; the threads that stage activations into LDS accumulate those sums
+// with v_dot4 as they go (once per byte, not once per wave).  N:M decodes
+// to c directly.
 // All integer work is exact; results are bit-identical to the GEMV path.
 #include "sbl_decode.h"
 
@@ -28,24 +39,114 @@ using namespace dec;
 
 typedef int32_t v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 256;            // weight rows per workgroup
-constexpr int kBN = 128;            // tokens per workgroup
-constexpr int kBK = 128;            // k per step
-constexpr int kStride = kBK + 16;   // LDS bytes per token row
+constexpr int kBK = 64;             // k per step
 constexpr int kThreads = 256;
-constexpr int kRT = 4;              // 32-row tiles per wave
-constexpr int kCT = 2;              // 32-token tiles per wave
+constexpr int kDepth = 2;           // steps of loads in flight (registers)
+constexpr int kUnroll = 2;          // lcm(kDepth, 2 LDS buffers)
 
-__device__ __forceinline__ void lds_st16(uint8_t* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Raw weight bytes of one lane for one 64-k step of one row tile.  Lane
+// group g uses the 16-weight words 2h + g (h = 0, 1) of the row's 64-weight
+// block; raw data are kept untouched until decode so that no load result is
+// consumed early (which would force a wait on the whole prefetch pipeline).
+template <int KIND> struct WRaw;
+template <> struct WRaw<kDense2> { uint32_t w[2]; };                 // words g and 2 + g
+template <> struct WRaw<kNm68> { uint32_t c[3]; uint32_t m[2]; };    // whole block: 12 code bytes, 8 meta bytes
+template <> struct WRaw<kNm24> { uint32_t c[2]; uint32_t m[2]; };    // whole block: 8 code bytes, 8 meta bytes
+
 __device__ __forceinline__ v4i lds_ld16(const uint8_t* p) {
   const u32x4 v = *reinterpret_cast<const u32x4*>(p);
   return v4i{(int32_t)v[0], (int32_t)v[1], (int32_t)v[2], (int32_t)v[3]};
 }
 
+// byte offset of 16-byte chunk c of token row r in an LDS activation tile.
+// The XOR swizzle makes the 16-byte reads of 8 (and of 16) consecutive rows
+// at the same chunk land in distinct bank groups: rows are 64 bytes, so rows
+// r and r+2 (128-byte banking) or r and r+4 (256-byte banking) would
+// otherwise collide.
+template <int kBK_ = kBK>
+__device__ __forceinline__ int bt_off(int r, int c) {
+  return r * kBK + 16 * (c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1)));
+}
+
+// Buffer resources: loads past the end of a buffer return zeros, so rows past
+// n_out and tokens past m_tok need neither branches nor clamping (their
+// results are never stored).  32-bit offsets: the host keeps every buffer of
+// this path below 2 GiB.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int KIND>
+__device__ __forceinline__ void load_w(WRaw<KIND>& a, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rm,
+                                       int voff_w, int voff_m, int ks) {
+  if constexpr (KIND == kDense2) {
+    a.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, voff_w, 16 * ks, 0);
+    a.w[1] = __builtin_amdgcn_raw_buffer_load_b32(rw, voff_w + 8, 16 * ks, 0);
+  } else if constexpr (KIND == kNm68) {
+    const auto c = __builtin_amdgcn_raw_buffer_load_b96(rw, voff_w, 12 * ks, 0);
+    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rm, voff_m, 8 * ks, 0);
+    a.c[0] = c[0]; a.c[1] = c[1]; a.c[2] = c[2];
+    a.m[0] = m[0]; a.m[1] = m[1];
+  } else {
+    const auto c = __builtin_amdgcn_raw_buffer_load_b64(rw, voff_w, 8 * ks, 0);
+    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rm, voff_m, 8 * ks, 0);
+    a.c[0] = c[0]; a.c[1] = c[1];
+    a.m[0] = m[0]; a.m[1] = m[1];
+  }
+}
+
+// Workgroup barrier for LDS hand-off.  Unlike __syncthreads() it does not
+// drain outstanding global loads (vmcnt), so the prefetch pipeline stays in
+// flight across it; the "memory" clobber keeps LDS accesses on their side.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// A operand (16 weights, k order) of sub-step h (0: first 32 k, 1: second):
+// word w = 2h + g of the 64-weight block.
+template <int KIND>
+__device__ __forceinline__ v4i decode_w(const WRaw<KIND>& a, int h, int g, const NmLut& L) {
+  if constexpr (KIND == kDense2) {
+    return dense2_quad(a.w[h]);
+  } else if constexpr (KIND == kNm68) {
+    // word w: codes = bits 24w .. 24w+23 of the 96-bit block, meta = bytes 2w, 2w+1
+    const uint32_t c24 = h == 0 ? (g ? __builtin_amdgcn_alignbit(a.c[1], a.c[0], 24) : a.c[0])
+                                : (g ? (a.c[2] >> 8) : __builtin_amdgcn_alignbit(a.c[2], a.c[1], 16));
+    const uint32_t m16 = (g ? (a.m[h] >> 16) : a.m[h]);
+    v4i r;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t c12 = (c24 >> (12 * q)) & 0xFFFu;
+      const uint32_t mb = (m16 >> (8 * q)) & 0xFFu;
+      const uint32_t lo = L.spread[c12 & 0xFFu];
+      const uint32_t hi = L.spread[c12 >> 8];
+      r[2 * q] = (int32_t)__builtin_amdgcn_perm(hi, lo, L.sel[mb][0]);
+      r[2 * q + 1] = (int32_t)__builtin_amdgcn_perm(hi, lo, L.sel[mb][1]);
+    }
+    return r;
+  } else {
+    // word w: codes = bytes 2w, 2w+1, meta = bytes 2w, 2w+1
+    const uint32_t c16 = g ? (a.c[h] >> 16) : a.c[h];
+    const uint32_t m16 = g ? (a.m[h] >> 16) : a.m[h];
+    v4i r;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t v = L.spread[(c16 >> (8 * q)) & 0xFFu];
+      const uint32_t mb = (m16 >> (8 * q)) & 0xFFu;
+      r[2 * q] = (int32_t)__builtin_amdgcn_perm(v, v, L.sel[mb][0]);
+      r[2 * q + 1] = (int32_t)__builtin_amdgcn_perm(v, v, L.sel[mb][1]);
+    }
+    return r;
+  }
+}
+
+// KRT 32-row tiles and KCT 32-token tiles per wave; 4 waves along the rows.
+template <int KIND, int KRT, int KCT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const LinBatch batch) {
+  constexpr int kRT = KRT, kCT = KCT;
+  constexpr int kBM = 4 * 32 * kRT;                 // weight rows per workgroup
+  constexpr int kBN = 32 * kCT;                     // tokens per workgroup (every wave sees all)
+  constexpr int kStPasses = kBN * kBK / (16 * kThreads);   // 16-byte staging loads per thread
   __shared__ NmLut lut;
-  __shared__ __attribute__((aligned(16))) uint8_t btile[2][kBN * kStride];
+  __shared__ __attribute__((aligned(16))) uint8_t btile[2][kBN * kBK];
   if (KIND != kDense2) build_lut<KIND>(lut);
 
   int di = 0;
@@ -57,35 +158,50 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const LinBatch batch)
   const int64_t n0 = (int64_t)tile_n * kBM;
   const int64_t t0 = (int64_t)tile_t * kBN;
   const int64_t K = d.k;
-  const int nks = (int)((K + kBK - 1) / kBK);
+  const int nks = (int)(K / kBK);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wn = wave & 1, wt = wave >> 1;
   const int li = lane & 31, g = lane >> 5;
+  __shared__ int32_t qsum_lds[kBN];
 
-  // activation staging: thread -> token (tid >> 3) + 32p, 16-byte chunk tid & 7
-  const int st_tok = tid >> 3, st_chunk = tid & 7;
+  // activation staging: thread -> token (tid >> 2) + 64p, 16-byte chunk tid & 3
+  const int st_tok = tid >> 2, st_chunk = tid & 3;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(d.xq, (int64_t)d.m_tok * K);
+  int voff_b[kStPasses];
+#pragma unroll
+  for (int p = 0; p < kStPasses; ++p) voff_b[p] = (int)((t0 + st_tok + 64 * p) * K + 16 * st_chunk);
   auto load_b = [&](int ks, u32x4* r) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int64_t tok = t0 + st_tok + 32 * p;
-      const int64_t kk = (int64_t)ks * kBK + 16 * st_chunk;
-      r[p] = (tok < d.m_tok && kk < K) ? ld16(d.xq + tok * K + kk) : u32x4{0u, 0u, 0u, 0u};
+    for (int p = 0; p < kStPasses; ++p) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, voff_b[p], kBK * ks, 0);
+      r[p] = u32x4{v[0], v[1], v[2], v[3]};
     }
   };
+  int qpart[kStPasses] = {};                         // DENSE2: per staged token, sum of its q bytes
   auto store_b = [&](int buf, const u32x4* r) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) lds_st16(&btile[buf][(st_tok + 32 * p) * kStride + 16 * st_chunk], r[p]);
-  };
-  // weights: lane (li, g) of row tile rt covers k = ks*128 + 64g .. +64 of row n0 + 128wn + 32rt + li
-  auto load_w = [&](int ks, ARaw<KIND>* a) {
-    const int kb = 2 * ks + g;                       // 64-weight block index within the row
-    const bool kok = (int64_t)kb * 64 < K;
+    for (int p = 0; p < kStPasses; ++p) {
+      *reinterpret_cast<u32x4*>(&btile[buf][bt_off(st_tok + 64 * p, st_chunk)]) = r[p];
+      if (KIND == kDense2) {
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) {
-      const int64_t row = n0 + 128 * wn + 32 * rt + li;
-      load_a<KIND>(a[rt], d, row, kb, kok && row < d.n_out);
+        for (int j = 0; j < 4; ++j) qpart[p] = __builtin_amdgcn_sdot4((int)r[p][j], 0x01010101, qpart[p], false);
+      }
     }
+  };
+  // weights: row tile rt of this wave = rows n0 + 32*kRT*wn + 32rt + li
+  const int64_t wrow_bytes = KIND == kDense2 ? K / 4 : (KIND == kNm68 ? 3 * K / 16 : K / 8);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(d.packed, d.n_out * wrow_bytes);
+  const __amdgpu_buffer_rsrc_t rm = make_rsrc(KIND == kDense2 ? d.packed : d.meta, d.n_out * (K / 8));
+  int voff_w[kRT], voff_m[kRT];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    const int64_t row = n0 + 32 * kRT * wave + 32 * rt + li;
+    voff_w[rt] = (int)(row * wrow_bytes + (KIND == kDense2 ? 4 * g : 0));
+    voff_m[rt] = (int)(row * (K / 8));
+  }
+  auto load_wall = [&](int ks, WRaw<KIND>* a) {
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) load_w<KIND>(a[rt], rw, rm, voff_w[rt], voff_m[rt], ks);
   };
 
   v16i acc[kRT][kCT];
@@ -93,66 +209,81 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const LinBatch batch)
   for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) acc[rt][ct] = v16i{};
-  int qs[kCT] = {0, 0};
 
-  ARaw<KIND> wcur[kRT], wnxt[kRT];
-  u32x4 bst[4];
-  load_b(0, bst);
-  load_w(0, wcur);
-  store_b(0, bst);
-  __syncthreads();
-
-  for (int ks = 0; ks < nks; ++ks) {
-    const int buf = ks & 1;
-    const bool more = ks + 1 < nks;
-    if (more) {
-      load_b(ks + 1, bst);
-      load_w(ks + 1, wnxt);
-    }
-    const uint8_t* bt = &btile[buf][0];
+  u32x4 bst[kDepth][kStPasses];
+  WRaw<KIND> wr[kDepth][kRT];
+  // prologue: steps 0 .. kDepth-1 in flight, step 0 in LDS
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {               // 32-k MFMA sub-steps
+  for (int s = 0; s < kDepth; ++s) {
+    if (s < nks) {
+      load_b(s, bst[s]);
+      load_wall(s, wr[s]);
+    }
+  }
+  if (KIND != kDense2) __syncthreads();             // tables built
+  store_b(0, bst[0]);
+  lds_barrier();
+
+  // one 64-k step; u = ks mod kUnroll fixes the register slot and LDS buffer
+  auto step = [&](const int ks, const int u) {
+    const int slot = u % kDepth;                    // == ks % kDepth (kUnroll is a multiple of kDepth)
+    // activations of step ks + kDepth go to the slot step ks vacated (it is in LDS)
+    if (ks + kDepth < nks) load_b(ks + kDepth, bst[slot]);
+    const uint8_t* bt = &btile[u & 1][0];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {                   // 32-k MFMA sub-steps
       v4i b[kCT];
 #pragma unroll
-      for (int ct = 0; ct < kCT; ++ct)
-        b[ct] = lds_ld16(bt + (64 * wt + 32 * ct + li) * kStride + 64 * g + 16 * kk);
+      for (int ct = 0; ct < kCT; ++ct) b[ct] = lds_ld16(bt + bt_off(32 * ct + li, 2 * h + g));
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
-        const v4i a = decode_a<KIND>(wcur[rt], kk, lut);
+        const v4i a = decode_w<KIND>(wr[slot][rt], h, g, lut);
 #pragma unroll
         for (int ct = 0; ct < kCT; ++ct)
           acc[rt][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[ct], acc[rt][ct], 0, 0, 0);
       }
-      if (KIND == kDense2) {
-#pragma unroll
-        for (int ct = 0; ct < kCT; ++ct)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) qs[ct] = __builtin_amdgcn_sdot4(b[ct][j], 0x01010101, qs[ct], false);
-      }
     }
-    if (more) {
-      store_b(buf ^ 1, bst);
+    // weights of step ks + kDepth reuse the slot just consumed
+    if (ks + kDepth < nks) load_wall(ks + kDepth, wr[slot]);
+    if (ks + 1 < nks) store_b((u + 1) & 1, bst[(u + 1) % kDepth]);
+    lds_barrier();
+  };
+  // main loop without exits (keeps the accumulators resident in AGPRs),
+  // then the remaining nks % kUnroll steps
+  int ks0 = 0;
+  for (; ks0 + kUnroll <= nks; ks0 += kUnroll) {
 #pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) wcur[rt] = wnxt[rt];
+    for (int u = 0; u < kUnroll; ++u) step(ks0 + u, u);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll - 1; ++u)
+    if (ks0 + u < nks) step(ks0 + u, u);
+
+  // per-token sums of q (DENSE2): the 4 threads staging a token hold its 4 chunks
+  if (KIND == kDense2) {
+#pragma unroll
+    for (int p = 0; p < kStPasses; ++p) {
+      int v = qpart[p];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      if (st_chunk == 0) qsum_lds[st_tok + 64 * p] = v;
     }
     __syncthreads();
   }
-
   // epilogue: lane (li, g) holds C[8*(v/4) + 4g + v%4][li] of each 32x32 tile
 #pragma unroll
   for (int ct = 0; ct < kCT; ++ct) {
-    if (KIND == kDense2) qs[ct] += __shfl_xor(qs[ct], 32, 64);
-    const int64_t t = t0 + 64 * wt + 32 * ct + li;
+    const int64_t t = t0 + 32 * ct + li;
     if (t >= d.m_tok) continue;
     const float s = out_scale(d.beta, d.gamma, t);
     float* yrow = d.y + t * d.n_out;
     int32_t* arow = d.acc ? d.acc + t * d.n_out : nullptr;
-    const int32_t corr = KIND == kDense2 ? qs[ct] : 0;
+    const int32_t corr = KIND == kDense2 ? qsum_lds[32 * ct + li] : 0;
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t row = n0 + 128 * wn + 32 * rt + 8 * q + 4 * g;
+        const int64_t row = n0 + 32 * kRT * wave + 32 * rt + 8 * q + 4 * g;
         int32_t a4[4];
         float y4[4];
 #pragma unroll
@@ -177,9 +308,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const LinBatch batch)
   }
 }
 
+// Tile shapes (weight rows x tokens), workgroups that fit on one CU at once,
+// and the measured time of one such round relative to one 256 x 256 tile.
+// A launch costs whole rounds of 256 CUs: small tiles fill the chip when a
+// product has few large tiles (tile quantization), large tiles reuse operands.
+struct TileShape { int rows, toks, slots; double round_cost; };
+constexpr TileShape kShapes[] = {{256, 256, 1, 1.0}, {256, 128, 1, 0.59}, {128, 256, 1, 0.59},
+                                 {128, 128, 3, 0.75}};
+
+int pick_shape(const LinearArgs* items, int count) {
+  int best = 0;
+  double best_t = 1e300;
+  for (int si = 0; si < 4; ++si) {
+    const TileShape& sh = kShapes[si];
+    int64_t tiles = 0, ksteps = 0;
+    for (int i = 0; i < count; ++i) {
+      const int64_t t = ((items[i].n_out + sh.rows - 1) / sh.rows) * ((items[i].m_tok + sh.toks - 1) / sh.toks);
+      tiles += t;
+      ksteps += t * (items[i].k / kBK);
+    }
+    const int64_t per_round = 256 * (int64_t)sh.slots;
+    const double rounds = (double)((tiles + per_round - 1) / per_round);
+    const double t = rounds * sh.round_cost * ((double)ksteps / (double)tiles);
+    if (t < best_t * 0.999) { best_t = t; best = si; }
+  }
+  return best;
+}
+
 }  // namespace
 
-hipError_t launch_gemm_group(const LinearArgs* items, int count, int kind, hipStream_t s) {
+bool gemm_fits(const LinearArgs& a, int kind) {
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t row_bytes = kind == kDense2 ? a.k / 4 : (kind == kNm68 ? 3 * a.k / 16 : a.k / 8);
+  return (a.m_tok + 256) * a.k < lim && (a.n_out + 256) * row_bytes < lim &&
+         (a.n_out + 256) * (a.k / 8) < lim;
+}
+
+namespace {
+
+template <int KRT, int KCT>
+hipError_t launch_shape(const LinearArgs* items, int count, int kind, hipStream_t s) {
+  constexpr int kBM = 4 * 32 * KRT, kBN = 32 * KCT;
   LinBatch b = {};
   int blocks = 0;
   for (int i = 0; i < count; ++i) {
@@ -192,10 +361,25 @@ hipError_t launch_gemm_group(const LinearArgs* items, int count, int kind, hipSt
   b.count = count;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(kThreads);
-  if (kind == kDense2) hipLaunchKernelGGL(gemm_kernel<kDense2>, grid, block, 0, s, b);
-  else if (kind == kNm68) hipLaunchKernelGGL(gemm_kernel<kNm68>, grid, block, 0, s, b);
-  else hipLaunchKernelGGL(gemm_kernel<kNm24>, grid, block, 0, s, b);
+  if (kind == kDense2) hipLaunchKernelGGL((gemm_kernel<kDense2, KRT, KCT>), grid, block, 0, s, b);
+  else if (kind == kNm68) hipLaunchKernelGGL((gemm_kernel<kNm68, KRT, KCT>), grid, block, 0, s, b);
+  else hipLaunchKernelGGL((gemm_kernel<kNm24, KRT, KCT>), grid, block, 0, s, b);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_group(const LinearArgs* items, int count, int kind, hipStream_t s) {
+#ifdef SBL_GEMM_FORCE_SHAPE
+  switch (SBL_GEMM_FORCE_SHAPE) {
+#else
+  switch (pick_shape(items, count)) {
+#endif
+    case 0: return launch_shape<2, 8>(items, count, kind, s);
+    case 1: return launch_shape<2, 4>(items, count, kind, s);
+    case 2: return launch_shape<1, 8>(items, count, kind, s);
+    default: return launch_shape<1, 4>(items, count, kind, s);
+  }
 }
 
 }  // namespace sbl

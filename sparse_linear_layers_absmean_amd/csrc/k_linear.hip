@@ -268,7 +268,7 @@ hipError_t launch_linear_batch(const LinearArgs* items, int count, int fmt, int 
     const LinearArgs& a = items[i];
     if (a.m_tok == 0 || a.n_out == 0) continue;
     hipError_t e = hipSuccess;
-    if (kind < 0) {
+    if (kind < 0 || (a.m_tok > kGemvMaxTokens && !gemm_fits(a, kind))) {
       e = launch_linear_generic(a, fmt, n, m, s);
     } else if (a.m_tok <= kGemvMaxTokens) {
       gemv[nv++] = to_desc(a);

@@ -1,5 +1,5 @@
 // C ABI of libsbl: host-side validation and kernel dispatch.  See include/sbl.h.
-#include "../../include/sbl.h"
+#include "sbl.h"
 #include "sbl_internal.h"
 
 namespace {

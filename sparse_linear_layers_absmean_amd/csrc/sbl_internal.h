@@ -68,4 +68,7 @@ hipError_t launch_linear_generic(const LinearArgs& a, int fmt, int n, int m, hip
 // N:M 6:8 (kind 1) or 2:4 (kind 2)
 hipError_t launch_gemm_group(const LinearArgs* items, int count, int kind, hipStream_t s);
 
+// whether the GEMM's 32-bit buffer offsets cover this product
+bool gemm_fits(const LinearArgs& a, int kind);
+
 }  // namespace sbl
