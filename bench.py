@@ -134,17 +134,17 @@ def main():
     acts = [[dict(xq=torch.empty((m_tok, mats[grp[0]][2]), dtype=torch.int8, device=dev),
                   gamma=torch.empty(m_tok, dtype=torch.float32, device=dev)) for grp in groups]
             for _ in range(copies)]
-    ws = torch.zeros(sbl.sbl_workspace_bytes(), dtype=torch.uint8, device=dev)
+    wss = [[sbl.new_workspace(no, k, dev) for (_, no, k) in mats] for _ in range(copies)]
 
     def items_of(c, gi, pool=None):
         src = outs[c] if pool is None else pool
         return [dict(src[i], xq=acts[c][gi]["xq"], gamma=acts[c][gi]["gamma"]) for i in groups[gi]]
 
     def qw_all(c):
-        for i, (_, no, k) in enumerate(mats):
-            o = outs[c][i]
-            sbl.sbl_quant_weights(masters[c][i], n, m, o["beta"], ws, fmt=fmt, packed=o["packed"],
-                                  meta=o["meta"])
+        sbl.sbl_quant_weights_batch(
+            [dict(w=masters[c][i], beta=outs[c][i]["beta"], packed=outs[c][i]["packed"],
+                  meta=outs[c][i]["meta"], workspace=wss[c][i]) for i in range(len(mats))],
+            n, m, fmt)
 
     def qa_all(c):
         for gi in range(len(groups)):
@@ -166,25 +166,37 @@ def main():
     step_bytes = qw_bytes + qa_bytes + lin_bytes
     weight_bytes = sum(packed_b(no, k) for _, no, k in mats)
 
+    # ---------------- HIP graphs: one per rotation copy, so that host launch
+    # overhead stays out of the timed region (the step has no memset nodes)
+    def capture(fn):
+        fn()                                  # eager run first: every kernel loaded
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    step_graphs = [capture(lambda c=c: step(c)) for c in range(copies)]
+
     # ---------------- whole-step timing
     for s in range(args.warmup):
-        step(s % copies)
+        step_graphs[s % copies].replay()
     torch.cuda.synchronize()
     tm = Timer()
     tm.start()
     for s in range(args.steps):
-        step(s % copies)
+        step_graphs[s % copies].replay()
     step_ms = tm.stop_ms() / args.steps
     torch.cuda.synchronize()
 
-    # ---------------- per-call rates (back-to-back launches, rotating copies)
-    def time_calls(fn, reps):
-        for r in range(min(reps, copies)):
-            fn(r % copies)
+    # ---------------- per-call rates: graphs of one call kind, replayed back to back
+    def time_graphs(graphs, reps):
+        for r in range(min(reps, len(graphs))):
+            graphs[r % len(graphs)].replay()
         torch.cuda.synchronize()
         tm.start()
         for r in range(reps):
-            fn(r % copies)
+            graphs[r % len(graphs)].replay()
         return tm.stop_ms() / reps
 
     # GEMV pool: distinct packed buffers totalling >= 512 MB (cold Infinity Cache)
@@ -199,10 +211,14 @@ def main():
         for gi in range(len(groups)):
             sbl.sbl_linear_batch(items_of(c % copies, gi, gemv_pool[c % gemv_copies]), fmt, n, m)
 
+    qw_graphs = [capture(lambda c=c: qw_all(c)) for c in range(copies)]
+    qa_graphs = [capture(lambda c=c: qa_all(c)) for c in range(copies)]
+    lin_graphs = [capture(lambda c=c: lin_all(c)) for c in range(gemv_copies)]
+
     reps = max(20, args.steps)
-    qw_ms = time_calls(qw_all, reps)
-    qa_ms = time_calls(qa_all, reps)
-    lin_ms = time_calls(lin_all, max(reps, 2 * gemv_copies))
+    qw_ms = time_graphs(qw_graphs, reps)
+    qa_ms = time_graphs(qa_graphs, reps)
+    lin_ms = time_graphs(lin_graphs, max(reps, 2 * gemv_copies))
 
     def roof(bytes_per, ms, kernel, launches, traffic=None):
         gbps = bytes_per / (ms * 1e-3) / 1e9
@@ -211,7 +227,8 @@ def main():
                 "launches_per_step": launches, "avg_launch_us": round(ms * 1e3 / launches, 3)}
 
     per_call = {
-        "sbl_quant_weights": roof(qw_bytes, qw_ms, "beta_kernel + mask_pack_kernel", 7),
+        "sbl_quant_weights": roof(qw_bytes, qw_ms, "sbl_quant_weights_batch over the 7 matrices: "
+                                  "absmean_partial + absmean_final + mask_pack kernels", 1),
         "sbl_quant_acts": roof(qa_bytes, qa_ms, "quant_acts_kernel", len(groups)),
         "sbl_linear": roof(lin_bytes, lin_ms, "gemv_kernel (grouped: qkv, o, gate+up, down)",
                            len(groups)),
@@ -266,11 +283,10 @@ def bench_prefill(torch, np, synth, sbl, dev, tm):
     wname, h, f, m_tok = "b3_prefill", 3200, 8640, 2048
     fmt, n, m = 1, 6, 8
     mats = synth.block_shapes(h, f)
-    ws = torch.zeros(sbl.sbl_workspace_bytes(), dtype=torch.uint8, device=dev)
     items = []
     for i, (_, no, k) in enumerate(mats):
         w = torch.from_numpy(synth.workload_masters(wname, i, no, k).view(np.int16)).to(dev)
-        o = sbl.quant_weights(w, n, m, fmt=fmt, workspace=ws)
+        o = sbl.quant_weights(w, n, m, fmt=fmt)
         x = torch.from_numpy(synth.workload_acts(wname, i, m_tok, k)).to(dev)
         xq, gamma = sbl.quant_acts(x)
         y = torch.empty((m_tok, no), dtype=torch.float32, device=dev)

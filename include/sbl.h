@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define SBL_ABI_VERSION 1
+#define SBL_ABI_VERSION 2
 
 typedef enum {
   SBL_OK = 0,
@@ -97,13 +97,16 @@ int64_t sbl_packed_bytes(int64_t n_out, int64_t k, int32_t n, int32_t m, int32_t
 /* Bytes of metadata: 0 for DENSE2, n_out*k/8 (the BITMAP) for NM; -1 if invalid. */
 int64_t sbl_meta_bytes(int64_t n_out, int64_t k, int32_t fmt);
 
-/* Bytes of device workspace sbl_quant_weights needs (the exact beta
- * reduction); the same for every shape. */
+/* Bytes of device workspace sbl_quant_weights needs for an n_out x k matrix
+ * (the exact beta reduction: 2 KB of per-exponent bins plus one 8-byte
+ * partial sum per workgroup, rounded up to 4 KB; 12 KB or less up to 2^31
+ * values).  Returns -1 for invalid arguments. */
 int64_t sbl_workspace_bytes(int64_t n_out, int64_t k);
 
-/* Zero-fill a workspace (enqueued on `stream`).  A workspace must be
- * zero-filled once before its first use -- by this call or by allocating it
- * zero-filled; every sbl_quant_weights call leaves it zero-filled again. */
+/* Zero-fill a workspace of `workspace_bytes` bytes (a multiple of 8, at least
+ * 2048), enqueued on `stream`.  A workspace must be zero-filled once before
+ * its first use -- by this call or by allocating it zero-filled; every
+ * sbl_quant_weights call leaves it ready for the next one. */
 int sbl_workspace_init(void* workspace, int64_t workspace_bytes, sbl_stream stream);
 
 /* Weight preparation: beta, N:M mask, ternary codes, packing -- one pass of
@@ -120,15 +123,39 @@ int sbl_workspace_init(void* workspace, int64_t workspace_bytes, sbl_stream stre
  *   packed     packed codes output (sbl_packed_bytes), or NULL.
  *   meta       [n_out][k/8] BITMAP output for fmt == SBL_FMT_NM (required
  *              there when packed != NULL); ignored for DENSE2.
- *   workspace  device scratch of sbl_workspace_bytes() bytes, 16-byte
- *              aligned, zero-filled before its first use (see
- *              sbl_workspace_init) and left zero-filled by every call.
+ *   workspace  device scratch of at least sbl_workspace_bytes(n_out, k)
+ *              bytes, 16-byte aligned, zero-filled before its first use
+ *              (see sbl_workspace_init) and left ready for the next call.
  *              Calls sharing one workspace must be ordered on one stream.
  */
 int sbl_quant_weights(const uint16_t* w_bf16, int64_t n_out, int64_t k, int32_t n, int32_t m,
                       float* beta, uint8_t* mask_bits, int8_t* codes,
                       int32_t fmt, uint8_t* packed, uint8_t* meta,
                       void* workspace, int64_t workspace_bytes, sbl_stream stream);
+
+/* One matrix of a grouped weight preparation (the arguments of one
+ * sbl_quant_weights call). */
+typedef struct {
+  const uint16_t* w_bf16;
+  int64_t n_out, k;
+  float* beta;
+  uint8_t* mask_bits;      /* nullable                                       */
+  int8_t* codes;           /* nullable                                       */
+  uint8_t* packed;         /* nullable                                       */
+  uint8_t* meta;           /* NM with packed != NULL: required               */
+  void* workspace;         /* sbl_workspace_bytes(n_out, k) bytes, its own   */
+  int64_t workspace_bytes;
+} sbl_quant_item;
+
+/* Weight preparation of several matrices (e.g. the seven of one transformer
+ * block) in three launches per 8 matrices instead of three per matrix.
+ * `items` is a HOST array of `count` (1..256) descriptors sharing the pattern
+ * n:m and `fmt`; each is validated as sbl_quant_weights validates its
+ * arguments, and workspaces must not overlap (SBL_ERR_WORKSPACE), all before
+ * anything is enqueued.  Results are bit-identical to calling
+ * sbl_quant_weights on each item. */
+int sbl_quant_weights_batch(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m,
+                            int32_t fmt, sbl_stream stream);
 
 /* Packing alone: ternary codes (+ mask) -> packed bytes.
  *   codes      [n_out][k] int8 in {-1,0,1} (other values: unspecified bytes).

@@ -11,22 +11,21 @@
 //  * Fast path: values in [2^-31, 2) are multiples of 2^-38; each thread adds
 //    at most 2^14 of them in fp64, whose partial sums stay below 2^15 and so
 //    are exact; the per-thread total is an integer below 2^53 in 2^-38 units.
-//    Workgroup totals go to a 128-bit accumulator (64-bit atomic + carry count).
+//    Each workgroup stores its total in a slot of its own (no atomics: on this
+//    chip same-address device atomics serialize at about 12 ns each).
 //  * Every other nonzero value (tiny, subnormal or >= 2) is rare in weights;
 //    it adds its significand to a per-exponent 64-bit bin with an atomic.
-//  * The last workgroup to finish rebuilds the exact sum as a multi-word
-//    integer, divides it by n_out*k with a bit-serial long division and
-//    rounds once to fp32 (nearest, ties to even), subnormals included.
-//    It then zero-fills the accumulators, so the workspace is ready for the
-//    next call (it must be zero-filled once before its first use).
+//  * A second, one-workgroup-per-matrix launch adds the slots and bins into a
+//    multi-word integer, divides it by n_out*k with a bit-serial long division
+//    and rounds once to fp32 (nearest, ties to even), subnormals included.
+//    It then zero-fills the bins for the next call (they must be zero-filled
+//    once before the first use); the slots are overwritten by every call.
+// Several matrices share each launch (QBatch).
 #include "sbl_internal.h"
 
 namespace sbl {
 
 namespace {
-
-constexpr int kBetaThreads = 256;
-constexpr int64_t kMaxIterPerThread = 2048;   // 8 values each: <= 2^14 values per thread
 
 __device__ __forceinline__ void rare_add(uint64_t* ws, uint32_t mag15) {
   const uint32_t e = mag15 >> 7;
@@ -36,6 +35,10 @@ __device__ __forceinline__ void rare_add(uint64_t* ws, uint32_t mag15) {
 
 __device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // limbs: little-endian 32-bit words of a nonnegative integer (units of 2^-133)
@@ -107,112 +110,155 @@ __device__ float round_quotient(const uint32_t* L, uint64_t n) {
   return ldexpf((float)mant, lsb - 133);
 }
 
-__global__ __launch_bounds__(kBetaThreads) void beta_kernel(const u32x4* __restrict__ w, int64_t nvec,
-                                                           uint64_t* __restrict__ ws,
-                                                           float* __restrict__ beta_out,
-                                                           uint64_t n_total) {
-  double acc0 = 0.0, acc1 = 0.0;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
-    const u32x4 v = ld_stream16(&w[i]);
-    const uint32_t d[4] = {v[0], v[1], v[2], v[3]};
-    bool rare = false;
+__device__ __forceinline__ int find_item(const QBatch& b) {
+  int di = 0;
+  for (int i = 1; i < b.count; ++i)
+    if ((int64_t)blockIdx.x >= b.start[i]) di = i;
+  return di;
+}
+
+// Adds the 8 BF16 magnitudes of one 16-byte vector: fast-window values to the
+// two fp64 sums, the rest to the per-exponent bins.
+__device__ __forceinline__ void consume(const u32x4& v, double& acc0, double& acc1, uint64_t* ws) {
+  bool rare = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = (v[j] << 16) & 0x7FFFFFFFu;   // |w| of the low value as fp32 bits
+    const uint32_t hi = v[j] & 0x7FFF0000u;           // |w| of the high value
+    const bool in_lo = (lo - 0x30000000u) < 0x10000000u;   // [2^-31, 2)
+    const bool in_hi = (hi - 0x30000000u) < 0x10000000u;
+    acc0 += in_lo ? (double)__uint_as_float(lo) : 0.0;
+    acc1 += in_hi ? (double)__uint_as_float(hi) : 0.0;
+    rare |= (!in_lo && lo != 0u) || (!in_hi && hi != 0u);
+  }
+  if (rare) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = (d[j] << 16) & 0x7FFFFFFFu;   // |w| of the low value as fp32 bits
-      const uint32_t hi = d[j] & 0x7FFF0000u;           // |w| of the high value
-      const bool in_lo = (lo - 0x30000000u) < 0x10000000u;   // [2^-31, 2)
-      const bool in_hi = (hi - 0x30000000u) < 0x10000000u;
-      acc0 += in_lo ? (double)__uint_as_float(lo) : 0.0;
-      acc1 += in_hi ? (double)__uint_as_float(hi) : 0.0;
-      rare |= (!in_lo && lo != 0u) || (!in_hi && hi != 0u);
+      const uint32_t lo = v[j] & 0x7FFFu, hi = (v[j] >> 16) & 0x7FFFu;
+      if (lo && ((lo - 0x3000u) >= 0x1000u)) rare_add(ws, lo);
+      if (hi && ((hi - 0x3000u) >= 0x1000u)) rare_add(ws, hi);
     }
-    if (rare) {
+  }
+}
+
+// Workgroup g of a matrix covers vectors [g*256*vpt, (g+1)*256*vpt); thread t
+// reads vectors t, t+256, ... of that range (each load instruction of a wave
+// is 1 KB contiguous), eight loads in flight.
+__global__ __launch_bounds__(kAbsThreads) void absmean_partial_kernel(const QBatch batch) {
+  const int di = find_item(batch);
+  const QDesc& d = batch.d[di];
+  const int64_t wg = (int64_t)blockIdx.x - batch.start[di];
+  const int64_t vpt = d.vpt, nvec = d.nvec;
+  const u32x4* w = d.w + wg * kAbsThreads * vpt + threadIdx.x;
+  const int64_t left = nvec - wg * kAbsThreads * vpt - threadIdx.x;   // vectors from w[0] on
+  uint64_t* ws = d.ws;
+  double acc0 = 0.0, acc1 = 0.0;
+  int64_t j = 0;
+  for (; j + 8 <= vpt; j += 8) {
+    u32x4 v[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = d[j] & 0x7FFFu, hi = (d[j] >> 16) & 0x7FFFu;
-        if (lo && ((lo - 0x3000u) >= 0x1000u)) rare_add(ws, lo);
-        if (hi && ((hi - 0x3000u) >= 0x1000u)) rare_add(ws, hi);
-      }
+    for (int u = 0; u < 8; ++u) {
+      const int64_t off = (j + u) * kAbsThreads;
+      v[u] = off < left ? w[off] : u32x4{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) consume(v[u], acc0, acc1, ws);
+  }
+  for (; j < vpt; ++j) {
+    const int64_t off = j * kAbsThreads;
+    if (off < left) consume(w[off], acc0, acc1, ws);
   }
   // both partial sums are exact multiples of 2^-38 below 2^15
   unsigned long long units =
       (unsigned long long)(acc0 * 0x1p38) + (unsigned long long)(acc1 * 0x1p38);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) units += __shfl_xor(units, off, 64);
-  __shared__ unsigned long long wave_sum[kBetaThreads / 64];
-  __shared__ unsigned long long nz_bins[kBetaThreads / 64];
-  __shared__ uint64_t bins[256];
-  __shared__ bool is_last;
-  __shared__ uint32_t limbs[kLimbs];
+  __shared__ unsigned long long wave_sum[kAbsThreads / 64];
   if ((threadIdx.x & 63) == 0) wave_sum[threadIdx.x >> 6] = units;
-  __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned long long s = 0;
-    for (int i = 0; i < kBetaThreads / 64; ++i) s += wave_sum[i];
-    unsigned long long* lo = reinterpret_cast<unsigned long long*>(&ws[kWsFastLo]);
-    const unsigned long long old = atomicAdd(lo, s);
-    if (old + s < old) atomicAdd(reinterpret_cast<unsigned long long*>(&ws[kWsFastHi]), 1ull);
-    __threadfence();
-    const unsigned long long ticket =
-        atomicAdd(reinterpret_cast<unsigned long long*>(&ws[kWsCount]), 1ull);
-    is_last = ticket == (unsigned long long)gridDim.x - 1;
+    unsigned long long t = 0;
+#pragma unroll
+    for (int i = 0; i < kAbsThreads / 64; ++i) t += wave_sum[i];   // < 2^62
+    ws[kWsSlots + wg] = t;
   }
-  __syncthreads();
-  if (!is_last) return;
-  // Last workgroup: every other one has finished its atomics.  Read the
-  // per-exponent bins in parallel, then leave the workspace zero-filled for
-  // the next call.
-  __threadfence();
+}
+
+// One workgroup per matrix, after the partial-sum launch has finished.
+__global__ __launch_bounds__(kAbsThreads) void absmean_final_kernel(const QBatch batch) {
+  const QDesc& d = batch.d[blockIdx.x];
+  uint64_t* ws = d.ws;
+  // slot sums split in 32-bit halves so that nothing overflows (nb <= 4096)
+  unsigned long long s_lo = 0, s_hi = 0;
+  for (int64_t i = threadIdx.x; i < d.nb; i += kAbsThreads) {
+    const uint64_t v = ws[kWsSlots + i];
+    s_lo += (uint32_t)v;
+    s_hi += v >> 32;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    s_lo += __shfl_xor(s_lo, off, 64);
+    s_hi += __shfl_xor(s_hi, off, 64);
+  }
+  __shared__ unsigned long long part[2][kAbsThreads / 64];
+  __shared__ unsigned long long nz_bins[kAbsThreads / 64];
+  __shared__ uint64_t bins[256];
+  __shared__ uint32_t limbs[kLimbs];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    part[0][wave] = s_lo;
+    part[1][wave] = s_hi;
+  }
   const uint64_t b = ld_agent(&ws[kWsBins + threadIdx.x]);
   bins[threadIdx.x] = b;
-  ws[kWsBins + threadIdx.x] = 0;
+  st_agent(&ws[kWsBins + threadIdx.x], 0);
   const unsigned long long nz = __ballot(b != 0);
-  if ((threadIdx.x & 63) == 0) nz_bins[threadIdx.x >> 6] = nz;
+  if ((threadIdx.x & 63) == 0) nz_bins[wave] = nz;
   __syncthreads();
   if (threadIdx.x != 0) return;
-  const uint64_t fast_lo = ld_agent(&ws[kWsFastLo]);
-  const uint64_t fast_hi = ld_agent(&ws[kWsFastHi]);
-  ws[kWsFastLo] = 0;
-  ws[kWsFastHi] = 0;
-  ws[kWsCount] = 0;
   for (int i = 0; i < kLimbs; ++i) limbs[i] = 0;
-  for (int wv = 0; wv < kBetaThreads / 64; ++wv) {
-    unsigned long long m = nz_bins[wv];
-    while (m) {
-      const int e = wv * 64 + __ffsll(m) - 1;
-      m &= m - 1;
+  unsigned long long lo = 0, hi = 0;
+  for (int i = 0; i < kAbsThreads / 64; ++i) {
+    lo += part[0][i];
+    hi += part[1][i];
+  }
+  for (int wv = 0; wv < kAbsThreads / 64; ++wv) {
+    unsigned long long msk = nz_bins[wv];
+    while (msk) {
+      const int e = wv * 64 + __ffsll(msk) - 1;
+      msk &= msk - 1;
       add_shifted(limbs, bins[e], max(e, 1) - 1);
     }
   }
-  add_shifted(limbs, fast_lo, 95);        // 2^-38 = 2^95 * 2^-133
-  add_shifted(limbs, fast_hi, 95 + 64);
-  beta_out[0] = round_quotient(limbs, n_total);
+  add_shifted(limbs, lo, 95);        // 2^-38 = 2^95 * 2^-133
+  add_shifted(limbs, hi, 95 + 32);
+  d.beta[0] = round_quotient(limbs, (uint64_t)d.nvec * 8u);
 }
 
-__global__ void zero_ws_kernel(uint64_t* ws) {
-  for (int i = threadIdx.x; i < kWsWords; i += blockDim.x) ws[i] = 0;
+__global__ void zero_ws_kernel(uint64_t* ws, int64_t words) {
+  for (int64_t i = threadIdx.x; i < words; i += blockDim.x) ws[i] = 0;
 }
 
 }  // namespace
 
-hipError_t launch_workspace_init(uint64_t* ws, hipStream_t s) {
-  hipLaunchKernelGGL(zero_ws_kernel, dim3(1), dim3(256), 0, s, ws);
+hipError_t launch_workspace_init(uint64_t* ws, int64_t words, hipStream_t s) {
+  hipLaunchKernelGGL(zero_ws_kernel, dim3(1), dim3(256), 0, s, ws, words);
   return hipGetLastError();
 }
 
-hipError_t launch_beta(const uint16_t* w, int64_t total, uint64_t* ws, float* beta,
-                       hipStream_t s) {
-  const int64_t nvec = total / 8;
-  int64_t blocks = (nvec + kBetaThreads * 8 - 1) / (kBetaThreads * 8);
-  blocks = blocks < 1 ? 1 : (blocks > 4096 ? 4096 : blocks);
-  const int64_t min_blocks =
-      (nvec + kBetaThreads * kMaxIterPerThread - 1) / (kBetaThreads * kMaxIterPerThread);
-  if (blocks < min_blocks) blocks = min_blocks;
-  hipLaunchKernelGGL(beta_kernel, dim3((unsigned)blocks), dim3(kBetaThreads), 0, s,
-                     reinterpret_cast<const u32x4*>(w), nvec, ws, beta, (uint64_t)total);
+hipError_t launch_absmean_partial(QBatch& b, hipStream_t s) {
+  int64_t blocks = 0;
+  for (int i = 0; i < b.count; ++i) {
+    b.start[i] = blocks;
+    blocks += b.d[i].nb;
+  }
+  b.start[b.count] = blocks;
+  hipLaunchKernelGGL(absmean_partial_kernel, dim3((unsigned)blocks), dim3(kAbsThreads), 0, s, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_absmean_final(QBatch& b, hipStream_t s) {
+  hipLaunchKernelGGL(absmean_final_kernel, dim3((unsigned)b.count), dim3(kAbsThreads), 0, s, b);
   return hipGetLastError();
 }
 

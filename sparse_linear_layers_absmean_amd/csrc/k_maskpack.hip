@@ -18,6 +18,12 @@
 //    value is the top half of an fp32; RoundClip(w/beta) is nonzero exactly
 //    then (a ratio of exactly 1/2 rounds to even, i.e. to 0).
 //
+// Patterns that drop at most two of a group (8:8, 7:8, 6:8, 4:4, 3:4, 2:4)
+// take the packed path below: two BF16 magnitudes per 32-bit register and
+// v_pk_{min,max,sub}_u16, so a group of 8 costs about 70 VALU operations
+// (the per-key formulation needs about 180).  Other patterns use the
+// per-key kernel.
+//
 // One thread handles one 64-weight chunk (128 bytes of BF16): groups never
 // cross chunks (m divides 64) and chunks never cross rows (64 divides k), so
 // the matrix is processed as a flat array.  Per chunk it writes 16 bytes of
@@ -83,9 +89,13 @@ __device__ __forceinline__ void nm_insert(ChunkOut& o, uint32_t u, int pos2) {
   else o.nm_hi |= v << (pos2 - 64);
 }
 
-__device__ __forceinline__ void store_outputs(const ChunkOut& o, int64_t c, int n, int m,
+// NT > 0: compile-time n (unrolled stores); NT == 0: runtime n
+template <int NT, int M>
+__device__ __forceinline__ void store_outputs(const ChunkOut& o, int64_t c, int n_rt,
                                               uint8_t* mask, int8_t* codes, int fmt,
                                               uint8_t* packed, uint8_t* meta) {
+  const int n = NT > 0 ? NT : n_rt;
+  constexpr int m = M;
   if (mask) reinterpret_cast<uint2*>(mask)[c] = make_uint2((uint32_t)o.keep, (uint32_t)(o.keep >> 32));
   if (codes) {
     uint4* cp = reinterpret_cast<uint4*>(codes) + c * 4;
@@ -103,34 +113,240 @@ __device__ __forceinline__ void store_outputs(const ChunkOut& o, int64_t c, int 
                          (uint32_t)(o.nm_hi >> 32)};
   if ((bytes & 3) == 0) {
     uint32_t* p = reinterpret_cast<uint32_t*>(packed + c * bytes);
-    for (int i = 0; i < bytes / 4; ++i) p[i] = w[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < bytes / 4) p[i] = w[i];
   } else {
     uint16_t* p = reinterpret_cast<uint16_t*>(packed + c * bytes);
-    for (int i = 0; i < bytes / 2; ++i) p[i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < bytes / 2) p[i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
   }
 }
 
-template <int M, int NT>   // NT > 0: compile-time n; NT == 0: runtime n
-__global__ __launch_bounds__(kThreads) void mask_pack_kernel(const uint4* __restrict__ w, int64_t nchunks,
-                                                             int n_rt, const float* __restrict__ beta,
-                                                             uint8_t* __restrict__ mask,
-                                                             int8_t* __restrict__ codes, int fmt,
-                                                             uint8_t* __restrict__ packed,
-                                                             uint8_t* __restrict__ meta) {
+// Loads are staged through LDS: the workgroup reads 256 consecutive chunks
+// (32 KB) with lane-contiguous 16-byte loads, then each thread reads its own
+// 128-byte chunk back (rows padded to 144 bytes: conflict-free).
+constexpr int kPad = 144;
+
+__device__ __forceinline__ int find_item(const QBatch& b) {
+  int di = 0;
+  for (int i = 1; i < b.count; ++i)
+    if ((int64_t)blockIdx.x >= b.start[i]) di = i;
+  return di;
+}
+
+// Words of chunk c0 + threadIdx.x (word i = weights 2i, 2i+1), for a workgroup
+// whose chunks start at c0; `cnt` chunks exist from c0 on.
+__device__ __forceinline__ void load_chunk(const u32x4* __restrict__ w, int64_t c0, int64_t cnt,
+                                           uint8_t* stage, uint32_t (&dw)[32]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int v16 = tid + kThreads * i;                    // 16-byte unit within the block
+    if (v16 < cnt * 8) {
+      const u32x4 v = ld_stream16(&w[c0 * 8 + v16]);
+      *reinterpret_cast<u32x4*>(&stage[(v16 >> 3) * kPad + 16 * (v16 & 7)]) = v;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[tid * kPad + 16 * i]);
+    dw[4 * i] = v[0]; dw[4 * i + 1] = v[1]; dw[4 * i + 2] = v[2]; dw[4 * i + 3] = v[3];
+  }
+}
+
+// ---- packed 16-bit helpers: a 32-bit word holds weight 2i (low half) and 2i+1
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+constexpr uint32_t kOnes = 0x00010001u;
+
+__device__ __forceinline__ u16x2 h2(uint32_t x) { return __builtin_bit_cast(u16x2, x); }
+__device__ __forceinline__ uint32_t w32(u16x2 x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ uint32_t pmin(uint32_t a, uint32_t b) { return w32(__builtin_elementwise_min(h2(a), h2(b))); }
+__device__ __forceinline__ uint32_t pmax(uint32_t a, uint32_t b) { return w32(__builtin_elementwise_max(h2(a), h2(b))); }
+// per half: a > b ? a - b : 0
+__device__ __forceinline__ uint32_t psubsat(uint32_t a, uint32_t b) { return w32(__builtin_elementwise_sub_sat(h2(a), h2(b))); }
+__device__ __forceinline__ uint32_t swap16(uint32_t x) { return __builtin_amdgcn_alignbit(x, x, 16); }
+// A register the optimizer cannot see through: min(sub_sat(a, b), 1) with a
+// visible 1 is rewritten into per-half compares and selects (6 operations
+// per word instead of 2).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm("" : "+v"(x));
+  return x;
+}
+
+// Both halves of the result = the DROP-th smallest magnitude of the group
+// (a multiset order statistic), from min/max networks on packed halves.
+template <int M, int DROP>
+__device__ __forceinline__ uint32_t drop_threshold(const uint32_t* A) {
+  uint32_t lo, hi;
+  if constexpr (M == 8) {
+    const uint32_t a = pmin(A[0], A[1]), b = pmax(A[0], A[1]);
+    const uint32_t c = pmin(A[2], A[3]), d = pmax(A[2], A[3]);
+    lo = pmin(a, c);                                   // per half: smallest of 4
+    hi = pmin(pmax(a, c), pmin(b, d));                 // per half: second smallest of 4
+  } else {
+    lo = pmin(A[0], A[1]);
+    hi = pmax(A[0], A[1]);
+  }
+  if constexpr (DROP == 1) return pmin(lo, swap16(lo));
+  return pmin(pmax(lo, swap16(lo)), pmin(hi, swap16(hi)));
+}
+
+// per-half 0/1 flags of the M/2 words of a group -> M-bit mask (bit j = weight j)
+template <int M>
+__device__ __forceinline__ uint32_t gather_bits(const uint32_t* F) {
+  uint32_t m = F[0];
+#pragma unroll
+  for (int i = 1; i < M / 2; ++i) m |= F[i] << (2 * i);
+  return (m | (m >> 15)) & ((1u << M) - 1u);
+}
+
+template <int M>
+__device__ __forceinline__ void scatter_bits(uint32_t keep, uint32_t* F) {
+  const uint32_t x = keep | (keep << 15);
+#pragma unroll
+  for (int i = 0; i < M / 2; ++i) F[i] = (x >> (2 * i)) & kOnes;
+}
+
+// four 2-bit values in bytes 0..3 -> bits 0..7
+__device__ __forceinline__ uint32_t bytes_to_fields(uint32_t p) {
+  const uint32_t t = p | (p >> 6);
+  return (t | (t >> 12)) & 0xFFu;
+}
+
+// delete the 2-bit field number pos of x (higher fields move down)
+__device__ __forceinline__ uint32_t remove_field(uint32_t x, uint32_t pos) {
+  const uint32_t low = (1u << (2 * pos)) - 1u;
+  return (x & low) | ((x >> 2) & ~low);
+}
+
+// FMT: format computed for `packed` (0 DENSE2, 1 N:M); CODES: int8 codes wanted
+template <int M, int DROP, int FMT, bool CODES>
+__global__ __launch_bounds__(kThreads) void mask_pack_fast_kernel(const QBatch batch) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads * kPad];
+  constexpr int N = M - DROP, WPG = M / 2;
+  const int di = find_item(batch);
+  const QDesc& d = batch.d[di];
+  const int64_t nchunks = d.nvec / 8;
+  const int64_t c0 = ((int64_t)blockIdx.x - batch.start[di]) * kThreads;
+  const int64_t cnt = nchunks - c0 < kThreads ? nchunks - c0 : kThreads;
+  uint32_t dw[32];
+  load_chunk(d.w, c0, cnt, stage, dw);
+  const int64_t c = c0 + threadIdx.x;
+  if (c >= nchunks) return;
+  const float b = fmaxf(d.beta[0], 1e-5f);
+  const uint32_t t2 = (__float_as_uint(b * 0.5f) >> 16) * kOnes;   // |w| > beta_eff/2 <=> mag > t
+  constexpr bool want_d2 = FMT == 0, want_nm = FMT == 1, want_codes = CODES;
+  const uint32_t ones = opaque(kOnes);
+  ChunkOut o = {};
+  uint32_t nmw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int g = 0; g < 64 / M; ++g) {
+    const uint32_t* W = dw + g * WPG;
+    uint32_t A[WPG], F[WPG];
+#pragma unroll
+    for (int i = 0; i < WPG; ++i) A[i] = W[i] & 0x7FFF7FFFu;
+    uint32_t keep = (1u << M) - 1u;
+    if constexpr (DROP == 0) {
+#pragma unroll
+      for (int i = 0; i < WPG; ++i) F[i] = kOnes;
+    } else {
+      const uint32_t S = drop_threshold<M, DROP>(A);
+#pragma unroll
+      for (int i = 0; i < WPG; ++i) F[i] = pmin(psubsat(A[i], S), ones);    // mag > S
+      keep = gather_bits<M>(F);
+      if (__builtin_popcount(keep) != N) {
+        // magnitudes equal to S straddle the cut: keep them, then drop the
+        // highest-indexed ones until n remain (ties go to the lower index)
+        uint32_t E[WPG];
+#pragma unroll
+        for (int i = 0; i < WPG; ++i) E[i] = (F[i] | pmin(psubsat(S, A[i]), ones)) ^ kOnes;
+        uint32_t eq = gather_bits<M>(E);
+        keep |= eq;
+#pragma unroll
+        for (int t = 0; t < DROP; ++t) {
+          if (__builtin_popcount(keep) > N) {
+            const uint32_t top = 1u << (31 - __builtin_clz(eq));
+            keep &= ~top;
+            eq &= ~top;
+          }
+        }
+        scatter_bits<M>(keep, F);
+      }
+    }
+    o.keep |= (uint64_t)keep << (g * M);
+    // per half: index = G + 2*sign, G = (kept and mag > t); u = c + 1 = {1, 2, 1, 0}[index]
+    uint32_t X[WPG];
+#pragma unroll
+    for (int i = 0; i < WPG; ++i) {
+      const uint32_t G = pmin(psubsat(A[i], t2), F[i]);
+      X[i] = ((W[i] >> 14) & 0x00020002u) | G;
+    }
+    uint32_t fields = 0;                               // u of the group, 2 bits each
+#pragma unroll
+    for (int q = 0; q < M / 4; ++q) {
+      // bytes = index of weights 4q .. 4q+3, then u through the byte table
+      const uint32_t idx = __builtin_amdgcn_perm(X[2 * q + 1], X[2 * q], 0x06040200u);
+      const uint32_t P = __builtin_amdgcn_perm(0u, 0x00010201u, idx);
+      const int p = g * M + 4 * q;                     // first weight of the quad
+      if (want_d2) o.d2[p >> 4] |= P << (2 * ((p >> 2) & 3));
+      if (want_codes) o.cb[p >> 2] = ((P | 0x80808080u) - 0x01010101u) ^ 0x80808080u;
+      if (want_nm) fields |= bytes_to_fields(P) << (8 * q);
+    }
+    if (want_nm) {
+      const uint32_t dm = ~keep & ((1u << M) - 1u);    // dropped positions
+      if constexpr (DROP == 2) fields = remove_field(fields, 31 - __builtin_clz(dm));
+      if constexpr (DROP >= 1) fields = remove_field(fields, __builtin_ctz(dm));
+      const int off = g * 2 * N, wi = off >> 5, sh = off & 31;
+      nmw[wi] |= fields << sh;
+      if (sh + 2 * N > 32) nmw[wi + 1] |= fields >> (32 - sh);
+    }
+  }
+  o.nm_lo = (uint64_t)nmw[0] | ((uint64_t)nmw[1] << 32);
+  o.nm_hi = (uint64_t)nmw[2] | ((uint64_t)nmw[3] << 32);
+  store_outputs<N, M>(o, c, N, d.mask, d.codes, FMT, d.packed, d.meta);
+}
+
+template <int M, int DROP>
+void launch_fast(QBatch& b, dim3 grid, hipStream_t s) {
+  bool codes = false, nm = false;
+  for (int i = 0; i < b.count; ++i) {
+    codes = codes || b.d[i].codes != nullptr;
+    nm = nm || (b.d[i].packed != nullptr && b.d[i].fmt == 1);
+  }
+  if (nm && codes)
+    hipLaunchKernelGGL((mask_pack_fast_kernel<M, DROP, 1, true>), grid, dim3(kThreads), 0, s, b);
+  else if (nm)
+    hipLaunchKernelGGL((mask_pack_fast_kernel<M, DROP, 1, false>), grid, dim3(kThreads), 0, s, b);
+  else if (codes)
+    hipLaunchKernelGGL((mask_pack_fast_kernel<M, DROP, 0, true>), grid, dim3(kThreads), 0, s, b);
+  else
+    hipLaunchKernelGGL((mask_pack_fast_kernel<M, DROP, 0, false>), grid, dim3(kThreads), 0, s, b);
+}
+
+// Any n (one thread per chunk, one sort key per weight).
+template <int M>
+__global__ __launch_bounds__(kThreads) void mask_pack_kernel(const QBatch batch, int n) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads * kPad];
   constexpr int SH = (M == 8) ? 3 : 2;
-  const int n = NT > 0 ? NT : n_rt;
-  const float b = fmaxf(beta[0], 1e-5f);
+  const int di = find_item(batch);
+  const QDesc& d = batch.d[di];
+  const int64_t nchunks = d.nvec / 8;
+  uint8_t* __restrict__ packed = d.packed;
+  const int fmt = d.fmt;
+  const float b = fmaxf(d.beta[0], 1e-5f);
   const int thr_mag = (int)(__float_as_uint(b * 0.5f) >> 16);
   const int thr_nz = (thr_mag << SH) | (M - 1);      // key > thr_nz  <=>  |w| > beta_eff/2
   const bool want_nm = packed && fmt == 1;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
+  {
+    const int64_t c0 = ((int64_t)blockIdx.x - batch.start[di]) * kThreads;
+    const int64_t cnt = nchunks - c0 < kThreads ? nchunks - c0 : kThreads;   // chunks in this block
     uint32_t dw[32];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32x4 v = ld_stream16(&w[c * 8 + i]);
-      dw[4 * i] = v[0]; dw[4 * i + 1] = v[1]; dw[4 * i + 2] = v[2]; dw[4 * i + 3] = v[3];
-    }
+    load_chunk(d.w, c0, cnt, stage, dw);
+    const int64_t c = c0 + threadIdx.x;
+    if (c >= nchunks) return;
     ChunkOut o = {};
 #pragma unroll
     for (int g = 0; g < 64 / M; ++g) {
@@ -160,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void mask_pack_kernel(const uint4* __rest
         }
       }
     }
-    store_outputs(o, c, n, M, mask, codes, fmt, packed, meta);
+    store_outputs<0, M>(o, c, n, d.mask, d.codes, fmt, packed, d.meta);
   }
 }
 
@@ -200,35 +416,42 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const uint4* __restrict_
       }
       for (; fmt == 1 && kept < n; ++kept) nm_insert(o, 1u, 2 * (g * n + kept));
     }
-    store_outputs(o, c, n, M, nullptr, nullptr, fmt, packed, meta);
+    store_outputs<0, M>(o, c, n, nullptr, nullptr, fmt, packed, meta);
   }
 }
 
 int64_t grid_for(int64_t nchunks) {
   int64_t blocks = (nchunks + kThreads - 1) / kThreads;
-  return blocks < 1 ? 1 : (blocks > 65536 ? 65536 : blocks);
+  return blocks < 1 ? 1 : (blocks > 16384 ? 16384 : blocks);
 }
 
 }  // namespace
 
-hipError_t launch_mask_pack(const uint16_t* w, int64_t total, int n, int m, const float* beta,
-                            uint8_t* mask, int8_t* codes, int fmt, uint8_t* packed,
-                            uint8_t* meta, hipStream_t s) {
-  const int64_t nchunks = total / kChunk;
-  const dim3 grid((unsigned)grid_for(nchunks)), block(kThreads);
-  const uint4* wv = reinterpret_cast<const uint4*>(w);
-  if (m == 8 && n == 6)
-    hipLaunchKernelGGL((mask_pack_kernel<8, 6>), grid, block, 0, s, wv, nchunks, n, beta, mask, codes, fmt, packed, meta);
-  else if (m == 8 && n == 8)
-    hipLaunchKernelGGL((mask_pack_kernel<8, 8>), grid, block, 0, s, wv, nchunks, n, beta, mask, codes, fmt, packed, meta);
-  else if (m == 4 && n == 2)
-    hipLaunchKernelGGL((mask_pack_kernel<4, 2>), grid, block, 0, s, wv, nchunks, n, beta, mask, codes, fmt, packed, meta);
-  else if (m == 4 && n == 4)
-    hipLaunchKernelGGL((mask_pack_kernel<4, 4>), grid, block, 0, s, wv, nchunks, n, beta, mask, codes, fmt, packed, meta);
+hipError_t launch_mask_pack(QBatch& b, int n, int m, hipStream_t s) {
+  int64_t blocks = 0;
+  for (int i = 0; i < b.count; ++i) {
+    b.start[i] = blocks;
+    blocks += (b.d[i].nvec / 8 + kThreads - 1) / kThreads;
+  }
+  b.start[b.count] = blocks;
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  const int drop = m - n;
+  if (m == 8 && drop == 0)
+    launch_fast<8, 0>(b, grid, s);
+  else if (m == 8 && drop == 1)
+    launch_fast<8, 1>(b, grid, s);
+  else if (m == 8 && drop == 2)
+    launch_fast<8, 2>(b, grid, s);
+  else if (m == 4 && drop == 0)
+    launch_fast<4, 0>(b, grid, s);
+  else if (m == 4 && drop == 1)
+    launch_fast<4, 1>(b, grid, s);
+  else if (m == 4 && drop == 2)
+    launch_fast<4, 2>(b, grid, s);
   else if (m == 8)
-    hipLaunchKernelGGL((mask_pack_kernel<8, 0>), grid, block, 0, s, wv, nchunks, n, beta, mask, codes, fmt, packed, meta);
+    hipLaunchKernelGGL((mask_pack_kernel<8>), grid, block, 0, s, b, n);
   else
-    hipLaunchKernelGGL((mask_pack_kernel<4, 0>), grid, block, 0, s, wv, nchunks, n, beta, mask, codes, fmt, packed, meta);
+    hipLaunchKernelGGL((mask_pack_kernel<4>), grid, block, 0, s, b, n);
   return hipGetLastError();
 }
 

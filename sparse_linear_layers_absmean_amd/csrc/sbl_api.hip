@@ -58,40 +58,103 @@ int64_t sbl_meta_bytes(int64_t n_out, int64_t k, int32_t fmt) {
 }
 
 int64_t sbl_workspace_bytes(int64_t n_out, int64_t k) {
-  (void)n_out;
-  (void)k;
-  return sbl::kWorkspaceBytes;
+  if (n_out < 1 || !k_ok(k) || n_out * k > kMaxElems) return -1;
+  return sbl::workspace_bytes_for(n_out * k);
 }
 
 int sbl_workspace_init(void* workspace, int64_t workspace_bytes, sbl_stream stream) {
   if (!workspace) return SBL_ERR_NULL;
-  if (workspace_bytes < sbl::kWorkspaceBytes) return SBL_ERR_WORKSPACE;
+  if (workspace_bytes < 8 * sbl::kWsSlots || workspace_bytes % 8 != 0) return SBL_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return SBL_ERR_ALIGN;
   return launch_status(sbl::launch_workspace_init(reinterpret_cast<uint64_t*>(workspace),
+                                                  workspace_bytes / 8,
                                                   reinterpret_cast<hipStream_t>(stream)));
 }
+
+}  // extern "C"
+
+namespace {
+
+int check_quant(const sbl_quant_item& it, int32_t n, int32_t m, int32_t fmt) {
+  if (!it.w_bf16 || !it.beta) return SBL_ERR_NULL;
+  if (it.packed && fmt == SBL_FMT_NM && !it.meta) return SBL_ERR_NULL;
+  if (it.n_out < 1 || !k_ok(it.k) || it.n_out * it.k > kMaxElems) return SBL_ERR_SHAPE;
+  if (!it.workspace || it.workspace_bytes < sbl::workspace_bytes_for(it.n_out * it.k))
+    return SBL_ERR_WORKSPACE;
+  if (!nm_ok(n, m)) return SBL_ERR_UNSUPPORTED;
+  if (it.packed && fmt != SBL_FMT_DENSE2 && fmt != SBL_FMT_NM) return SBL_ERR_UNSUPPORTED;
+  if (!aligned(it.w_bf16, 16) || !aligned(it.beta, 4) || !aligned(it.workspace, 16) ||
+      (it.mask_bits && !aligned(it.mask_bits, 16)) || (it.codes && !aligned(it.codes, 16)) ||
+      (it.packed && !aligned(it.packed, 16)) || (it.meta && !aligned(it.meta, 16)))
+    return SBL_ERR_ALIGN;
+  return SBL_OK;
+}
+
+sbl::QDesc to_qdesc(const sbl_quant_item& it, int32_t fmt) {
+  const int64_t total = it.n_out * it.k;
+  const sbl::AbsmeanPlan p = sbl::absmean_plan(total);
+  sbl::QDesc d;
+  d.w = reinterpret_cast<const sbl::u32x4*>(it.w_bf16);
+  d.nvec = total / 8;
+  d.nb = p.nb;
+  d.vpt = p.vpt;
+  d.beta = it.beta;
+  d.ws = reinterpret_cast<uint64_t*>(it.workspace);
+  d.mask = it.mask_bits;
+  d.codes = it.codes;
+  d.packed = it.packed;
+  d.fmt = it.packed ? fmt : SBL_FMT_DENSE2;
+  d.meta = (it.packed && fmt == SBL_FMT_NM) ? it.meta : nullptr;
+  return d;
+}
+
+// beta partial sums, beta, then mask/codes/pack: three launches per group of
+// up to kMaxQDesc matrices
+int launch_quant(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m, int32_t fmt,
+                 hipStream_t s) {
+  for (int i0 = 0; i0 < count; i0 += sbl::kMaxQDesc) {
+    sbl::QBatch b;
+    b.count = count - i0 < sbl::kMaxQDesc ? count - i0 : sbl::kMaxQDesc;
+    for (int i = 0; i < b.count; ++i) b.d[i] = to_qdesc(items[i0 + i], fmt);
+    int st = launch_status(sbl::launch_absmean_partial(b, s));
+    if (st == SBL_OK) st = launch_status(sbl::launch_absmean_final(b, s));
+    if (st == SBL_OK) st = launch_status(sbl::launch_mask_pack(b, n, m, s));
+    if (st != SBL_OK) return st;
+  }
+  return SBL_OK;
+}
+
+bool overlaps(const sbl_quant_item& a, const sbl_quant_item& b) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.workspace), b0 = reinterpret_cast<uintptr_t>(b.workspace);
+  return a0 < b0 + (uintptr_t)b.workspace_bytes && b0 < a0 + (uintptr_t)a.workspace_bytes;
+}
+
+}  // namespace
+
+extern "C" {
 
 int sbl_quant_weights(const uint16_t* w_bf16, int64_t n_out, int64_t k, int32_t n, int32_t m,
                       float* beta, uint8_t* mask_bits, int8_t* codes, int32_t fmt,
                       uint8_t* packed, uint8_t* meta, void* workspace, int64_t workspace_bytes,
                       sbl_stream stream) {
-  if (!w_bf16 || !beta) return SBL_ERR_NULL;
-  if (packed && fmt == SBL_FMT_NM && !meta) return SBL_ERR_NULL;
-  if (!workspace || workspace_bytes < sbl::kWorkspaceBytes) return SBL_ERR_WORKSPACE;
-  if (n_out < 1 || !k_ok(k) || n_out * k > kMaxElems) return SBL_ERR_SHAPE;
-  if (!nm_ok(n, m)) return SBL_ERR_UNSUPPORTED;
-  if (packed && fmt != SBL_FMT_DENSE2 && fmt != SBL_FMT_NM) return SBL_ERR_UNSUPPORTED;
-  if (!aligned(w_bf16, 16) || !aligned(beta, 4) || !aligned(workspace, 16) ||
-      (mask_bits && !aligned(mask_bits, 16)) || (codes && !aligned(codes, 16)) ||
-      (packed && !aligned(packed, 16)) || (meta && !aligned(meta, 16)))
-    return SBL_ERR_ALIGN;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int64_t total = n_out * k;
-  int st = launch_status(sbl::launch_beta(w_bf16, total, reinterpret_cast<uint64_t*>(workspace), beta, s));
+  const sbl_quant_item it = {w_bf16, n_out, k, beta, mask_bits, codes, packed, meta,
+                             workspace, workspace_bytes};
+  const int st = check_quant(it, n, m, fmt);
   if (st != SBL_OK) return st;
-  return launch_status(sbl::launch_mask_pack(w_bf16, total, n, m, beta, mask_bits, codes,
-                                             packed ? fmt : SBL_FMT_DENSE2, packed,
-                                             fmt == SBL_FMT_NM ? meta : nullptr, s));
+  return launch_quant(&it, 1, n, m, fmt, reinterpret_cast<hipStream_t>(stream));
+}
+
+int sbl_quant_weights_batch(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m,
+                            int32_t fmt, sbl_stream stream) {
+  if (!items) return SBL_ERR_NULL;
+  if (count < 1 || count > 256) return SBL_ERR_SHAPE;
+  for (int i = 0; i < count; ++i) {
+    const int st = check_quant(items[i], n, m, fmt);
+    if (st != SBL_OK) return st;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(items[i], items[j])) return SBL_ERR_WORKSPACE;
+  }
+  return launch_quant(items, count, n, m, fmt, reinterpret_cast<hipStream_t>(stream));
 }
 
 int sbl_pack(const int8_t* codes, const uint8_t* mask_bits, int64_t n_out, int64_t k, int32_t n,

@@ -14,29 +14,71 @@ __device__ __forceinline__ u32x4 ld_stream16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// Workspace of the exact beta reduction, in 64-bit words.
-//   [0, 256)  per-exponent sums of BF16 significands (values outside the
-//             fast window), exact integers
-//   256, 257  fast-window sum in units of 2^-38: low word, carry count
-//   258       number of finished workgroups (last one computes beta)
+// Workspace of the exact beta reduction of one matrix, in 64-bit words.
+//   [0, 256)       per-exponent sums of BF16 significands (values outside the
+//                  fast window), exact integers; accumulated with atomics by
+//                  the partial-sum kernel, read and zero-filled again by the
+//                  finalize kernel (so it must be zero before the first use)
+//   [256, 256+nb)  one fast-window partial sum per workgroup of the partial-sum
+//                  kernel (units of 2^-38), overwritten by every call
 constexpr int kWsBins = 0;
-constexpr int kWsFastLo = 256;
-constexpr int kWsFastHi = 257;
-constexpr int kWsCount = 258;
-constexpr int kWsWords = 260;
-constexpr int64_t kWorkspaceBytes = 4096;
+constexpr int kWsSlots = 256;
+
+// Partition of the absmean pass over a matrix of `total` BF16 values: nb
+// workgroups of kAbsThreads threads, vpt 16-byte vectors per thread.  A thread
+// adds at most 2^14 fast-window values (vpt <= 2048), which keeps its fp64
+// partial sums exact.
+constexpr int kAbsThreads = 256;
+struct AbsmeanPlan {
+  int64_t nb, vpt;
+};
+inline AbsmeanPlan absmean_plan(int64_t total) {
+  const int64_t nvec = total / 8;
+  const int64_t per_wg = (int64_t)kAbsThreads * 8;
+  AbsmeanPlan p{(nvec + per_wg - 1) / per_wg, 8};
+  if (p.nb > 1024) {          // big matrices: longer threads, at most 1024 slots (4096 at 2^34)
+    p.vpt = (nvec + 1024 * kAbsThreads - 1) / (1024 * kAbsThreads);
+    if (p.vpt > 2048) p.vpt = 2048;
+    p.nb = (nvec + kAbsThreads * p.vpt - 1) / (kAbsThreads * p.vpt);
+  }
+  if (p.nb < 1) p.nb = 1;
+  return p;
+}
+inline int64_t workspace_bytes_for(int64_t total) {
+  const int64_t bytes = 8 * (kWsSlots + absmean_plan(total).nb);
+  return (bytes + 4095) / 4096 * 4096;
+}
 
 // Weights handled by one thread of the mask/pack kernels (one 128-byte BF16 chunk).
 constexpr int kChunk = 64;
 
-hipError_t launch_workspace_init(uint64_t* ws, hipStream_t s);
+// One matrix of a grouped weight-preparation launch.
+struct QDesc {
+  const u32x4* w;         // BF16 masters as 16-byte vectors (8 values each)
+  int64_t nvec;           // n_out*k/8
+  int64_t nb, vpt;        // absmean partition (AbsmeanPlan)
+  float* beta;
+  uint64_t* ws;
+  uint8_t* mask;          // nullable outputs
+  int8_t* codes;
+  uint8_t* packed;
+  uint8_t* meta;
+  int32_t fmt;            // format of `packed`
+};
+constexpr int kMaxQDesc = 8;
+struct QBatch {
+  QDesc d[kMaxQDesc];
+  int64_t start[kMaxQDesc + 1];   // first workgroup of each item in the current launch
+  int32_t count;
+};
 
-hipError_t launch_beta(const uint16_t* w, int64_t total, uint64_t* ws, float* beta,
-                       hipStream_t s);
+// The three launches of weight preparation, in stream order.  Each fills
+// batch.start for its own grid.
+hipError_t launch_absmean_partial(QBatch& batch, hipStream_t s);
+hipError_t launch_absmean_final(QBatch& batch, hipStream_t s);
+hipError_t launch_mask_pack(QBatch& batch, int n, int m, hipStream_t s);
 
-hipError_t launch_mask_pack(const uint16_t* w, int64_t total, int n, int m, const float* beta,
-                            uint8_t* mask, int8_t* codes, int fmt, uint8_t* packed,
-                            uint8_t* meta, hipStream_t s);
+hipError_t launch_workspace_init(uint64_t* ws, int64_t words, hipStream_t s);
 
 hipError_t launch_pack(const int8_t* codes, const uint8_t* mask, int64_t total, int n, int m,
                        int fmt, uint8_t* packed, uint8_t* meta, hipStream_t s);

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libsbl.so")
 SBL_OK = 0
 SBL_FMT_DENSE2 = 0
 SBL_FMT_NM = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32
@@ -34,6 +34,13 @@ class LinearItem(ctypes.Structure):
     """sbl_linear_item of include/sbl.h."""
     _fields_ = [("packed", _c_p), ("meta", _c_p), ("beta", _c_p), ("xq", _c_p), ("gamma", _c_p),
                 ("m_tok", _c_i64), ("n_out", _c_i64), ("k", _c_i64), ("y", _c_p), ("acc", _c_p)]
+
+
+class QuantItem(ctypes.Structure):
+    """sbl_quant_item of include/sbl.h."""
+    _fields_ = [("w_bf16", _c_p), ("n_out", _c_i64), ("k", _c_i64), ("beta", _c_p),
+                ("mask_bits", _c_p), ("codes", _c_p), ("packed", _c_p), ("meta", _c_p),
+                ("workspace", _c_p), ("workspace_bytes", _c_i64)]
 
 
 class SblError(RuntimeError):
@@ -69,6 +76,9 @@ def load():
     lib.sbl_quant_weights.restype = ctypes.c_int
     lib.sbl_quant_weights.argtypes = [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p,
                                       _c_i32, _c_p, _c_p, _c_p, _c_i64, _c_p]
+    lib.sbl_quant_weights_batch.restype = ctypes.c_int
+    lib.sbl_quant_weights_batch.argtypes = [ctypes.POINTER(QuantItem), _c_i32, _c_i32, _c_i32, _c_i32,
+                                            _c_p]
     lib.sbl_pack.restype = ctypes.c_int
     lib.sbl_pack.argtypes = [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p]
     lib.sbl_quant_acts.restype = ctypes.c_int
@@ -130,13 +140,14 @@ def sbl_meta_bytes(n_out: int, k: int, fmt: int) -> int:
     return load().sbl_meta_bytes(n_out, k, fmt)
 
 
-def sbl_workspace_bytes(n_out: int = 1, k: int = 64) -> int:
+def sbl_workspace_bytes(n_out: int, k: int) -> int:
     return load().sbl_workspace_bytes(n_out, k)
 
 
 def sbl_workspace_init(workspace, stream=None):
+    """Zero-fill a whole workspace tensor (any dtype) with the library's kernel."""
     lib = load()
-    nbytes = lib.sbl_workspace_bytes(1, 64)
+    nbytes = (workspace.numel() * workspace.element_size()) // 8 * 8
     _check("sbl_workspace_init",
            lib.sbl_workspace_init(_ptr(workspace, None, nbytes, "workspace"), nbytes, _stream(stream)))
 
@@ -162,6 +173,33 @@ def sbl_quant_weights(w_bf16, n: int, m: int, beta, workspace, mask_bits=None, c
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream))
     _check("sbl_quant_weights", st)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size() if t is not None else 0
+
+
+def sbl_quant_weights_batch(items, n: int, m: int, fmt: int = SBL_FMT_DENSE2, stream=None):
+    """items: sequence of dicts with keys w (BF16 [n_out][k]), beta, workspace and the
+    optional outputs mask_bits, codes, packed, meta (as in sbl_quant_weights)."""
+    lib = load()
+    arr = (QuantItem * len(items))()
+    for i, it in enumerate(items):
+        w = it["w"]
+        n_out, k = w.shape
+        packed = it.get("packed")
+        pb = lib.sbl_packed_bytes(n_out, k, n, m, fmt) if packed is not None else 0
+        mb = n_out * k // 8
+        ws = it["workspace"]
+        arr[i] = QuantItem(
+            _ptr(w, _W16, n_out * k * 2, "w"), n_out, k, _ptr(it["beta"], torch.float32, 4, "beta"),
+            _ptr(it.get("mask_bits"), torch.uint8, mb, "mask_bits"),
+            _ptr(it.get("codes"), torch.int8, n_out * k, "codes"),
+            _ptr(packed, torch.uint8, max(pb, 0), "packed"),
+            _ptr(it.get("meta"), torch.uint8, mb, "meta") if fmt == SBL_FMT_NM else None,
+            _ptr(ws, None, lib.sbl_workspace_bytes(n_out, k), "workspace"), _nbytes(ws))
+    _check("sbl_quant_weights_batch",
+           lib.sbl_quant_weights_batch(arr, len(items), n, m, fmt, _stream(stream)))
 
 
 def sbl_pack(codes, mask_bits, n: int, m: int, fmt: int, packed, meta=None, stream=None):
@@ -222,9 +260,12 @@ def sbl_linear_batch(items, fmt: int, n: int, m: int, stream=None):
 
 # ---------------------------------------------------------------- allocating conveniences
 
-def new_workspace(device="cuda"):
-    """A zero-filled workspace (sbl_quant_weights leaves it zero-filled again)."""
-    return torch.zeros(sbl_workspace_bytes(), dtype=torch.uint8, device=device)
+def new_workspace(n_out: int, k: int, device="cuda"):
+    """A zero-filled workspace for n_out x k matrices (reusable, call after call)."""
+    nbytes = sbl_workspace_bytes(n_out, k)
+    if nbytes < 0:
+        raise ValueError("unsupported shape")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def quant_weights(w_bf16, n: int, m: int, fmt: int = SBL_FMT_DENSE2, want_codes: bool = False,
@@ -240,7 +281,7 @@ def quant_weights(w_bf16, n: int, m: int, fmt: int = SBL_FMT_DENSE2, want_codes:
     out["packed"] = torch.empty(pb, dtype=torch.uint8, device=dev)
     out["meta"] = out["mask"] if fmt == SBL_FMT_NM else None
     out["codes"] = torch.empty((n_out, k), dtype=torch.int8, device=dev) if want_codes else None
-    ws = workspace if workspace is not None else new_workspace(dev)
+    ws = workspace if workspace is not None else new_workspace(n_out, k, dev)
     sbl_quant_weights(w_bf16, n, m, out["beta"], ws, mask_bits=out["mask"], codes=out["codes"],
                       fmt=fmt, packed=out["packed"], meta=out["meta"], stream=stream)
     return out

@@ -39,7 +39,7 @@ def gpu_quant_weights(bits: np.ndarray, n: int, m: int, fmt: int):
     codes = torch.empty((n_out, k), dtype=torch.int8, device="cuda")
     packed = torch.empty(sbl.sbl_packed_bytes(n_out, k, n, m, fmt), dtype=torch.uint8, device="cuda")
     meta = torch.empty((n_out, k // 8), dtype=torch.uint8, device="cuda") if fmt == FMT_NM else None
-    ws = sbl.new_workspace()
+    ws = sbl.new_workspace(n_out, k)
     sbl.sbl_quant_weights(w, n, m, beta, ws, mask_bits=mask, codes=codes, fmt=fmt, packed=packed,
                           meta=meta)
     return dict(beta=beta, mask=mask, codes=codes, packed=packed, meta=meta)

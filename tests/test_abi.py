@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.sbl_abi_version() == 1
+    assert lib.sbl_abi_version() == 2
     for st in range(7):
         assert len(lib.sbl_status_string(st)) > 0
     assert lib.sbl_last_hip_error() == 0
@@ -63,7 +63,8 @@ def test_packed_and_meta_bytes(lib, n_out, k):
     assert lib.sbl_packed_bytes(n_out, k, 5, 8, 1) == n_out * k * 5 // 32
     assert lib.sbl_meta_bytes(n_out, k, 0) == 0
     assert lib.sbl_meta_bytes(n_out, k, 1) == n_out * k // 8
-    assert lib.sbl_workspace_bytes(n_out, k) >= 2080
+    ws = lib.sbl_workspace_bytes(n_out, k)
+    assert ws % 4096 == 0 and 2048 + 8 <= ws <= 12288
 
 
 def test_packed_bytes_closed_form_bits_per_weight(lib):
@@ -118,6 +119,45 @@ def test_quant_weights_validation(lib):
     assert call(mask=A + 1) == 3
     assert call(codes=A + 4) == 3
     assert call(ws=A + 8) == 3
+
+
+def test_workspace_bytes_cover_one_slot_per_workgroup(lib):
+    # 2 KB of bins + 8 B per absmean workgroup (256 threads x 8 vectors of 8 values
+    # each up to 1024 workgroups, then longer threads; 4096 slots at 2^34 values)
+    assert lib.sbl_workspace_bytes(1, 64) == 4096
+    assert lib.sbl_workspace_bytes(16384, 131072) == 12288      # 2^31 values: 1024 slots
+    assert lib.sbl_workspace_bytes(131072, 131072) == 36864     # 2^34 values: 4096 slots
+    assert lib.sbl_workspace_bytes(0, 64) == -1
+    assert lib.sbl_workspace_bytes(4, 96) == -1
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation runs only on GPU-less hosts")
+def test_quant_weights_batch_validation(lib):
+    from sparse_linear_layers_absmean_amd.sbl import QuantItem
+    f = lib.sbl_quant_weights_batch
+    ws = lib.sbl_workspace_bytes(4, 64)
+
+    def item(**kw):
+        a = dict(w_bf16=A, n_out=4, k=64, beta=A, mask_bits=A, codes=None, packed=A, meta=A,
+                 workspace=A, workspace_bytes=ws)
+        a.update(kw)
+        return QuantItem(**a)
+
+    def call(items, count=None, n=6, m=8, fmt=1):
+        arr = (QuantItem * len(items))(*items)
+        return f(arr, len(items) if count is None else count, n, m, fmt, None)
+
+    assert f(None, 1, 6, 8, 1, None) == 1
+    assert call([item()], count=0) == 2
+    assert call([item()], count=257) == 2
+    assert call([item(), item(w_bf16=None)]) == 1
+    assert call([item(), item(meta=None)]) == 1
+    assert call([item(), item(k=96)]) == 2
+    assert call([item(), item(workspace_bytes=ws - 8)]) == 6
+    assert call([item(), item(workspace=A + ws - 16)]) == 6       # overlaps item 0's workspace
+    assert call([item()], n=9) == 4
+    assert call([item()], fmt=2) == 4
+    assert call([item(), item(w_bf16=A + 2, workspace=A + 2 * ws)]) == 3
 
 
 @pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation runs only on GPU-less hosts")

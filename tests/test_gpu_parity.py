@@ -215,3 +215,60 @@ def test_gemm_multi_tile_ragged(fmt, n, m):
     x = synth.gaussian_acts(rng, m_tok, k, t_row_frac=0.25)
     say(f"gemm multi-tile fmt={fmt} {n}:{m}")
     compare_all(gpu_forward(bits, x, n, m, fmt), oracle_forward(bits, x, n, m), fmt, n_out)
+
+
+def _rare_mixture(rng, n_out, k):
+    kind = rng.integers(0, 5, (n_out, k))
+    mag = np.select([kind == 0, kind == 1, kind == 2, kind == 3],
+                    [0, rng.integers(1, 0x80, (n_out, k)), rng.integers(0x0080, 0x3000, (n_out, k)),
+                     rng.integers(0x3000, 0x4000, (n_out, k))],
+                    rng.integers(0x4000, 0x7F00, (n_out, k)))
+    return (mag | (rng.integers(0, 2, (n_out, k)) << 15)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("fmt,n,m", [(FMT_DENSE2, 6, 8), (FMT_NM, 6, 8), (FMT_NM, 2, 4), (FMT_NM, 5, 8)])
+def test_quant_weights_batch_matches_oracle(fmt, n, m):
+    """Grouped weight preparation (10 matrices: two launch groups) gives the
+    oracle's beta, mask, codes and packed bytes; a second call on the same
+    workspaces (bins left zero by the first) gives the same bits."""
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    rng = np.random.default_rng([31, fmt, n, m])
+    mats = [synth.gaussian_masters(rng, 96, 128), _rare_mixture(rng, 64, 512),
+            synth.gaussian_masters(rng, 200, 320), synth.gaussian_masters(rng, 1, 64),
+            synth.plant_ties(synth.gaussian_masters(rng, 130, 512), rng),
+            synth.gaussian_masters(rng, 1536, 512, outlier_frac=0.01),
+            _rare_mixture(rng, 3, 1024), synth.gaussian_masters(rng, 17, 256),
+            synth.gaussian_masters(rng, 640, 3200), synth.gaussian_masters(rng, 48, 128)]
+    items = []
+    for bits in mats:
+        n_out, k = bits.shape
+        items.append(dict(
+            w=to_dev(bits), beta=torch.empty(1, dtype=torch.float32, device="cuda"),
+            mask_bits=torch.empty((n_out, k // 8), dtype=torch.uint8, device="cuda"),
+            codes=torch.empty((n_out, k), dtype=torch.int8, device="cuda"),
+            packed=torch.empty(sbl.sbl_packed_bytes(n_out, k, n, m, fmt), dtype=torch.uint8,
+                               device="cuda"),
+            meta=torch.empty((n_out, k // 8), dtype=torch.uint8, device="cuda") if fmt == FMT_NM else None,
+            workspace=sbl.new_workspace(n_out, k)))
+    outs = []
+    for rep in range(2):
+        say(f"quant_weights_batch fmt={fmt} {n}:{m} items={len(items)} call {rep}")
+        sbl.sbl_quant_weights_batch(items, n, m, fmt)
+        torch.cuda.synchronize()
+        outs.append([{key: to_np(v) for key, v in it.items() if key not in ("w", "workspace") and v is not None}
+                     for it in items])
+    for bits, g, g2 in zip(mats, outs[0], outs[1]):
+        n_out, k = bits.shape
+        beta, keep, codes = O.quant_weights(bits, n, m)
+        assert g["beta"][0] == beta, (bits.shape, g["beta"][0], beta)
+        assert np.array_equal(g["mask_bits"], O.pack_bitmap(keep))
+        assert np.array_equal(g["codes"], codes)
+        if fmt == FMT_DENSE2:
+            assert np.array_equal(g["packed"].reshape(n_out, -1), O.pack_dense2(codes))
+        else:
+            if (k * n // m) % 4 == 0:
+                assert np.array_equal(g["packed"].reshape(n_out, -1), O.pack_nm(codes, keep, n, m))
+            assert np.array_equal(g["meta"], O.pack_bitmap(keep))
+        for key in g:
+            assert np.array_equal(g[key], g2[key]), key
