@@ -61,15 +61,32 @@ __device__ void add_shifted(uint32_t* L, uint64_t v, int s) {
   }
 }
 
+// RN_fp32(D / n) for a dividend D = W * 2^e + r, 0 <= r < 2^e, with bit 63 of
+// W set, r != 0 exactly when `sticky`, and 64 <= n <= 2^34.  floor(D / (n*2^e))
+// = floor(W / n) = Q (since R + r/2^e < n), and Q >= 2^29 holds more than the
+// 24 bits + guard that rounding needs; whatever is below is only a sticky
+// flag.  Nearest, ties to even, subnormal results included.
+__device__ float round_div(uint64_t W, int e, bool sticky, uint64_t n) {
+  const uint64_t Q = W / n, R = W - Q * n;
+  sticky = sticky || R != 0;
+  const int qb = 64 - __clzll((long long)Q);        // 30 <= qb <= 58
+  int lsb = qb - 24;                                // fp32 unit inside Q for a normal result
+  if (e + lsb < -149) lsb = -149 - e;               // subnormal: the unit is 2^-149
+  if (lsb > qb) return 0.0f;                        // below half the smallest subnormal
+  const uint64_t mant = Q >> lsb;
+  const uint64_t guard = (Q >> (lsb - 1)) & 1u;
+  sticky = sticky || (Q & ((1ull << (lsb - 1)) - 1u)) != 0;
+  const uint64_t m = mant + ((guard && (sticky || (mant & 1u))) ? 1u : 0u);
+  return ldexpf((float)m, e + lsb);
+}
+
 // exact RN_fp32(S * 2^-133 / n) for the integer S held in limbs (shared memory)
 __device__ float round_quotient(const uint32_t* L, uint64_t n) {
   int top = -1;
   for (int i = kLimbs - 1; i >= 0 && top < 0; --i)
     if (L[i]) top = i * 32 + 31 - __clz(L[i]);
   if (top < 0) return 0.0f;
-  // 64-bit window of S whose bit 63 is S's bit `top`; bits of S below the
-  // window only matter as a sticky flag.  The division below consumes at most
-  // log2(n) + 26 <= 61 bits (n <= 2^34), so the window always suffices.
+  // 64-bit window of S whose bit 63 is S's bit `top`; lower bits: sticky
   const int lo = top - 63;
   uint64_t win;
   bool below = false;
@@ -83,31 +100,20 @@ __device__ float round_quotient(const uint32_t* L, uint64_t n) {
   } else {
     win = ((uint64_t)L[0] | ((uint64_t)L[1] << 32)) << (-lo);
   }
-  uint64_t rem = 0, q = 0;
-  bool found = false;
-  int lsb = 0;
-  for (int pos = top; pos >= -17; --pos) {
-    rem = (rem << 1) | (win >> 63);
-    win <<= 1;
-    const uint32_t qb = rem >= n;
-    if (qb) rem -= n;
-    if (!found) {
-      if (qb) {
-        found = true;
-        q = 1;
-        lsb = max(pos - 23, -16);                   // 2^-149 is position -16 in 2^-133 units
-      }
-    } else {
-      q = (q << 1) | qb;
-    }
-    if (found && pos == lsb - 1) break;             // guard bit collected
-  }
-  if (!found) return 0.0f;                          // below 2^-150: rounds to zero
-  const bool sticky = rem != 0 || win != 0 || below;
-  const uint64_t guard = q & 1u;
-  uint64_t mant = q >> 1;
-  if (guard && (sticky || (mant & 1u))) ++mant;
-  return ldexpf((float)mant, lsb - 133);
+  return round_div(win, lo - 133, below, n);
+}
+
+// The same for S = V * 2^95 (fast-window sums only), V = hi * 2^32 + lo with
+// lo, hi < 2^62: registers only.
+__device__ float round_quotient_fast(uint64_t lo, uint64_t hi, uint64_t n) {
+  const uint64_t vlo = lo + (hi << 32);
+  const uint64_t vhi = (hi >> 32) + (vlo < lo ? 1u : 0u);
+  if (vlo == 0 && vhi == 0) return 0.0f;
+  const int top = vhi ? 127 - __clzll((long long)vhi) : 63 - __clzll((long long)vlo);
+  if (top <= 63) return round_div(vlo << (63 - top), top - 63 - 38, false, n);
+  const int s = top - 63;                           // 1 .. 63
+  const uint64_t W = (vlo >> s) | (vhi << (64 - s));
+  return round_div(W, s - 38, (vlo << (64 - s)) != 0, n);
 }
 
 __device__ __forceinline__ int find_item(const QBatch& b) {
@@ -117,56 +123,67 @@ __device__ __forceinline__ int find_item(const QBatch& b) {
   return di;
 }
 
-// Adds the 8 BF16 magnitudes of one 16-byte vector: fast-window values to the
-// two fp64 sums, the rest to the per-exponent bins.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_sub(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) - __builtin_bit_cast(u16x2, b));
+}
+__device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                 __builtin_bit_cast(u16x2, b)));
+}
+
+// Adds the 8 BF16 magnitudes of one 16-byte vector.  One packed test per
+// vector: every magnitude in the fast window [2^-31, 2) (bits 0x3000..0x3FFF)
+// -> two fp64 sums; otherwise (zeros included) value by value, values
+// outside the window to the per-exponent bins.
 __device__ __forceinline__ void consume(const u32x4& v, double& acc0, double& acc1, uint64_t* ws) {
-  bool rare = false;
+  uint32_t a[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t lo = (v[j] << 16) & 0x7FFFFFFFu;   // |w| of the low value as fp32 bits
-    const uint32_t hi = v[j] & 0x7FFF0000u;           // |w| of the high value
-    const bool in_lo = (lo - 0x30000000u) < 0x10000000u;   // [2^-31, 2)
-    const bool in_hi = (hi - 0x30000000u) < 0x10000000u;
-    acc0 += in_lo ? (double)__uint_as_float(lo) : 0.0;
-    acc1 += in_hi ? (double)__uint_as_float(hi) : 0.0;
-    rare |= (!in_lo && lo != 0u) || (!in_hi && hi != 0u);
-  }
-  if (rare) {
+  for (int j = 0; j < 4; ++j) a[j] = v[j] & 0x7FFF7FFFu;
+  const uint32_t t = pk_max(pk_max(pk_sub(a[0], 0x30003000u), pk_sub(a[1], 0x30003000u)),
+                            pk_max(pk_sub(a[2], 0x30003000u), pk_sub(a[3], 0x30003000u)));
+  if ((t & 0xF000F000u) == 0u) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = v[j] & 0x7FFFu, hi = (v[j] >> 16) & 0x7FFFu;
-      if (lo && ((lo - 0x3000u) >= 0x1000u)) rare_add(ws, lo);
-      if (hi && ((hi - 0x3000u) >= 0x1000u)) rare_add(ws, hi);
+      acc0 += (double)__uint_as_float(a[j] << 16);
+      acc1 += (double)__uint_as_float(a[j] & 0xFFFF0000u);
     }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = a[j] & 0xFFFFu, hi = a[j] >> 16;
+    if ((lo - 0x3000u) < 0x1000u) acc0 += (double)__uint_as_float(lo << 16);
+    else if (lo) rare_add(ws, lo);
+    if ((hi - 0x3000u) < 0x1000u) acc1 += (double)__uint_as_float(hi << 16);
+    else if (hi) rare_add(ws, hi);
   }
 }
 
-// Workgroup g of a matrix covers vectors [g*256*vpt, (g+1)*256*vpt); thread t
-// reads vectors t, t+256, ... of that range (each load instruction of a wave
-// is 1 KB contiguous), eight loads in flight.
+// Workgroup g of a matrix covers vectors [g*256*vpt, (g+1)*256*vpt) (vpt is a
+// multiple of 8); thread t reads vectors t, t+256, ... of that range, so each
+// load instruction of a wave reads 1 KB contiguous; eight loads in flight.
+// Buffer loads past the matrix's end return zeros (which add nothing).
 __global__ __launch_bounds__(kAbsThreads) void absmean_partial_kernel(const QBatch batch) {
   const int di = find_item(batch);
   const QDesc& d = batch.d[di];
   const int64_t wg = (int64_t)blockIdx.x - batch.start[di];
-  const int64_t vpt = d.vpt, nvec = d.nvec;
-  const u32x4* w = d.w + wg * kAbsThreads * vpt + threadIdx.x;
-  const int64_t left = nvec - wg * kAbsThreads * vpt - threadIdx.x;   // vectors from w[0] on
+  const int vpt = (int)d.vpt;
+  const int64_t first = wg * kAbsThreads * vpt;
+  const int64_t span = d.nvec - first < (int64_t)kAbsThreads * vpt ? d.nvec - first
+                                                                   : (int64_t)kAbsThreads * vpt;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(d.w + first, span * 16);
   uint64_t* ws = d.ws;
   double acc0 = 0.0, acc1 = 0.0;
-  int64_t j = 0;
-  for (; j + 8 <= vpt; j += 8) {
+  const int voff = threadIdx.x * 16;
+  for (int j = 0; j < vpt; j += 8) {
     u32x4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t off = (j + u) * kAbsThreads;
-      v[u] = off < left ? w[off] : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int u = 0; u < 8; ++u)
+      v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rw, voff + (j + u) * kAbsThreads * 16, 0, 0));
 #pragma unroll
     for (int u = 0; u < 8; ++u) consume(v[u], acc0, acc1, ws);
-  }
-  for (; j < vpt; ++j) {
-    const int64_t off = j * kAbsThreads;
-    if (off < left) consume(w[off], acc0, acc1, ws);
   }
   // both partial sums are exact multiples of 2^-38 below 2^15
   unsigned long long units =
@@ -216,12 +233,18 @@ __global__ __launch_bounds__(kAbsThreads) void absmean_final_kernel(const QBatch
   if ((threadIdx.x & 63) == 0) nz_bins[wave] = nz;
   __syncthreads();
   if (threadIdx.x != 0) return;
-  for (int i = 0; i < kLimbs; ++i) limbs[i] = 0;
   unsigned long long lo = 0, hi = 0;
   for (int i = 0; i < kAbsThreads / 64; ++i) {
     lo += part[0][i];
     hi += part[1][i];
   }
+  bool rare = false;
+  for (int wv = 0; wv < kAbsThreads / 64; ++wv) rare = rare || nz_bins[wv] != 0;
+  if (!rare) {
+    d.beta[0] = round_quotient_fast(lo, hi, (uint64_t)d.nvec * 8u);
+    return;
+  }
+  for (int i = 0; i < kLimbs; ++i) limbs[i] = 0;
   for (int wv = 0; wv < kAbsThreads / 64; ++wv) {
     unsigned long long msk = nz_bins[wv];
     while (msk) {

@@ -72,10 +72,6 @@ __device__ __forceinline__ int bt_off(int r, int c) {
 // n_out and tokens past m_tok need neither branches nor clamping (their
 // results are never stored).  32-bit offsets: the host keeps every buffer of
 // this path below 2 GiB.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-
 template <int KIND>
 __device__ __forceinline__ void load_w(WRaw<KIND>& a, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rm,
                                        int voff_w, int voff_m, int ks) {

@@ -12,11 +12,17 @@
 //    codes into int8 c bytes, a second table (indexed by the metadata bitmap
 //    byte) gives v_perm selectors that scatter them to their k positions and
 //    zero the pruned ones: 2 table reads + 2 v_perm per 8 weights.
-// Work split: a workgroup owns 32 output rows (two 16-row tiles per wave) and
-// its 8 waves split k; a 64-lane load brings 16 rows x 64 weights per tile.
-// Partial int32 tiles are summed through LDS, then rescaled.  Up to 8
-// independent matrices share one launch (grouped GEMV).  Everything integer
-// is exact: |acc| <= 127 k < 2^24.
+// Work split: a workgroup owns TB 16-row tiles of one matrix and TB*ks waves;
+// the ks waves of a tile split k.  ks and TB are chosen per launch so that the
+// grid is about one round of resident waves (a partial second round would run
+// at a fraction of the bandwidth).  When the token rows fit (m_tok*k <= 32 KB)
+// the workgroup stages them in LDS once and reads MFMA B operands from there,
+// with sum_k q computed once per token; otherwise B comes from global memory.
+// Each wave keeps kDepth weight loads in flight.  All global loads are buffer
+// loads: rows, k-blocks and tokens out of range read zeros, so there is no
+// branch around a load.  Partial int32 tiles of the ks waves are summed
+// through LDS, then rescaled.  Up to 8 independent matrices share one launch
+// (grouped GEMV).  Everything integer is exact: |acc| <= 127 k < 2^24.
 #include "sbl_decode.h"
 
 namespace sbl {
@@ -25,114 +31,235 @@ namespace {
 
 using namespace dec;
 
-constexpr int kTW = 2;                 // 16-row tiles per wave
-constexpr int kKS = 8;                 // waves per workgroup (k split)
-constexpr int kGemvThreads = 64 * kKS;
+constexpr int kMaxWaves = 16;          // waves per workgroup, at most
+constexpr int kResidentWaves = 4096;   // one round: 4 waves per SIMD on 1024 SIMDs
+constexpr int kXLdsMax = 32 * 1024;    // token rows staged in LDS up to this many bytes
+constexpr uint32_t kFar = 0x80000000u; // a buffer offset beyond every buffer: reads zeros
 
-template <int KIND>
-struct Frag {
-  u32x4 b[4];
-  ARaw<KIND> a[kTW];
+struct GemvLaunch {
+  LinBatch b;
+  int32_t ks, tb;                      // waves per tile (k split), tiles per workgroup
+};
+
+// Raw weight words of one lane for one 64-weight k-block.  DENSE2: 4 words;
+// 6:8: 3 code words + 2 meta words; 2:4: 2 code words + 2 meta words.
+struct WStage {
+  uint32_t a[5];
+};
+
+struct Rsrc {
+  __amdgpu_buffer_rsrc_t w, m, x;
 };
 
 template <int KIND>
-__device__ __forceinline__ void load_frag(Frag<KIND>& f, const LinDesc& d, int64_t row0, int r, int t,
-                                          int sb, int nkb) {
-  const int g = (threadIdx.x & 63) >> 4;
-  const int kb = 4 * sb + g;
-  const bool kok = kb < nkb;
-  if (kok && t < d.m_tok) {
-    const int8_t* xp = d.xq + (int64_t)t * d.k + (int64_t)kb * 64;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f.b[i] = ld16(xp + 16 * i);
+__device__ __forceinline__ void load_w(WStage& s, const Rsrc& rs, uint32_t ow, uint32_t om, int kb, bool kok) {
+  if constexpr (KIND == kDense2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs.w, kok ? ow + (uint32_t)kb * 16u : kFar, 0, 0);
+    s.a[0] = v[0]; s.a[1] = v[1]; s.a[2] = v[2]; s.a[3] = v[3];
+  } else if constexpr (KIND == kNm68) {
+    const auto c = __builtin_amdgcn_raw_buffer_load_b96(rs.w, kok ? ow + (uint32_t)kb * 12u : kFar, 0, 0);
+    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rs.m, kok ? om + (uint32_t)kb * 8u : kFar, 0, 0);
+    s.a[0] = c[0]; s.a[1] = c[1]; s.a[2] = c[2]; s.a[3] = m[0]; s.a[4] = m[1];
   } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f.b[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int ti = 0; ti < kTW; ++ti) {
-    const int64_t row = row0 + 16 * ti + r;
-    load_a<KIND>(f.a[ti], d, row, kb, kok && row < d.n_out);
+    const auto c = __builtin_amdgcn_raw_buffer_load_b64(rs.w, kok ? ow + (uint32_t)kb * 8u : kFar, 0, 0);
+    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rs.m, kok ? om + (uint32_t)kb * 8u : kFar, 0, 0);
+    s.a[0] = c[0]; s.a[1] = c[1]; s.a[2] = m[0]; s.a[3] = m[1];
   }
 }
 
+// 64 activation bytes of token lane%16 for k-block kb: LDS (XL) or global memory
+template <bool XL>
+__device__ __forceinline__ void load_x(u32x4 (&b)[4], const Rsrc& rs, const uint8_t* xs, uint32_t ox,
+                                       uint32_t zero_off, int kb, bool ok) {
+  if constexpr (XL) {
+    const uint8_t* p = xs + (ok ? ox + (uint32_t)kb * 64u : zero_off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = *reinterpret_cast<const u32x4*>(p + 16 * i);
+  } else {
+    const uint32_t xo = ok ? ox + (uint32_t)kb * 64u : kFar;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      b[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.x, xo, 16 * i, 0));
+  }
+}
+
+// 2-bit fields -> bytes: 4 fields (8 bits) -> 4 bytes, by shifts and masks
+__device__ __forceinline__ uint32_t fields4_to_bytes(uint32_t x) {
+  const uint32_t y = (x | (x << 12)) & 0x000F000Fu;
+  return (y | (y << 6)) & 0x03030303u;
+}
+
+// N:M: 16 weights (operand i of the k-block) as u = c + 1 bytes at the kept
+// positions and 0 at the pruned ones, plus the keep mask as 0/1 bytes; the
+// product is then MFMA(u) - MFMA(keep).  One table read per 8 weights (the
+// v_perm selectors of the bitmap byte); the codes spread arithmetically.
 template <int KIND>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const LinBatch batch) {
+__device__ __forceinline__ void nm_operands(const WStage& s, int i, const NmLut& L, v4i& u, v4i& km) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t plo, phi, mb;
+    if constexpr (KIND == kNm68) {
+      const int G = 2 * i + h;                         // group of 8 within the k-block
+      const uint64_t lo64 = (uint64_t)s.a[0] | ((uint64_t)s.a[1] << 32);
+      const uint64_t hi64 = (uint64_t)s.a[1] | ((uint64_t)s.a[2] << 32);
+      const uint32_t c12 = (12 * G + 12 <= 64) ? (uint32_t)(lo64 >> (12 * G)) : (uint32_t)(hi64 >> (12 * G - 32));
+      plo = fields4_to_bytes(c12 & 0xFFu);
+      const uint32_t h4 = (c12 >> 8) & 0xFu;
+      phi = (h4 | (h4 << 6)) & 0x0303u;
+      mb = (s.a[3 + (G >> 2)] >> (8 * (G & 3))) & 0xFFu;
+    } else {
+      const int P = 2 * i + h;                         // code byte = two groups of 4
+      plo = fields4_to_bytes((s.a[P >> 2] >> (8 * (P & 3))) & 0xFFu);
+      phi = 0u;
+      mb = (s.a[2 + (P >> 2)] >> (8 * (P & 3))) & 0xFFu;
+    }
+    const uint32_t s0 = L.sel[mb][0], s1 = L.sel[mb][1];
+    u[2 * h] = (int32_t)__builtin_amdgcn_perm(phi, plo, s0);
+    u[2 * h + 1] = (int32_t)__builtin_amdgcn_perm(phi, plo, s1);
+    km[2 * h] = (int32_t)__builtin_amdgcn_perm(0x01010101u, 0x01010101u, s0);
+    km[2 * h + 1] = (int32_t)__builtin_amdgcn_perm(0x01010101u, 0x01010101u, s1);
+  }
+}
+
+// One k-block: c += sum u q, ck += sum keep q (DENSE2: keep = every weight,
+// u from the 2-bit word decode), so that acc = c - ck.
+template <int KIND>
+__device__ __forceinline__ void mac(const WStage& s, const u32x4 (&bq)[4], v4i& c, v4i& ck, const NmLut& L) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v4i b = {(int32_t)bq[i][0], (int32_t)bq[i][1], (int32_t)bq[i][2], (int32_t)bq[i][3]};
+    if constexpr (KIND == kDense2) {
+      c = __builtin_amdgcn_mfma_i32_16x16x64_i8(dense2_quad(s.a[i]), b, c, 0, 0, 0);
+      const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+      ck = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, b, ck, 0, 0, 0);
+    } else {
+      v4i u, km;
+      nm_operands<KIND>(s, i, L, u, km);
+      c = __builtin_amdgcn_mfma_i32_16x16x64_i8(u, b, c, 0, 0, 0);
+      ck = __builtin_amdgcn_mfma_i32_16x16x64_i8(km, b, ck, 0, 0, 0);
+    }
+  }
+}
+
+// k-block kb = 4*sb + lane/16: super-block sb covers 256 weights of every row
+template <int KIND, bool XL>
+__global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L) {
+  constexpr int D = XL ? 8 : 4;                      // weight loads in flight per wave
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ NmLut lut;
-  __shared__ int32_t red[kKS][kTW * 4][64];
-  __shared__ int32_t redq[kKS][64];
+  const LinBatch& batch = L.b;
+  const int ks = L.ks;
   if (KIND != kDense2) build_lut<KIND>(lut);
   int di = 0;
   for (int i = 1; i < batch.count; ++i)
     if ((int)blockIdx.x >= batch.start[i]) di = i;
   const LinDesc& d = batch.d[di];
-  const int64_t row0 = (int64_t)((int)blockIdx.x - batch.start[di]) * (16 * kTW);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tw = wave / ks, slice = wave - tw * ks;   // tile of the workgroup, k slice
+  const int64_t row0 = ((int64_t)((int)blockIdx.x - batch.start[di]) * L.tb + tw) * 16;
   const int r = lane & 15, g = lane >> 4;
   const int nkb = d.k / 64;
   const int nsb = (nkb + 3) / 4;
-  const int sb0 = wave * nsb / kKS, sb1 = (wave + 1) * nsb / kKS;
-  if (KIND != kDense2) __syncthreads();
+  const int sb0 = slice * nsb / ks, sb1 = (slice + 1) * nsb / ks;
+  const int nit = row0 < d.n_out ? sb1 - sb0 : 0;   // tiles past the matrix: no work
+  // buffers over this tile's rows (rows past n_out are outside them) and the activations
+  const int64_t rows = d.n_out - row0 < 16 ? (d.n_out - row0 > 0 ? d.n_out - row0 : 0) : 16;
+  const int64_t wbytes = KIND == kDense2 ? d.k / 4 : (KIND == kNm68 ? 3 * (int64_t)d.k / 16 : d.k / 8);
+  Rsrc rs;
+  rs.w = make_rsrc(d.packed + (rows ? row0 * wbytes : 0), rows * wbytes);
+  rs.m = make_rsrc(KIND == kDense2 ? d.packed : d.meta + (rows ? row0 * (d.k / 8) : 0),
+                   KIND == kDense2 ? 0 : rows * (d.k / 8));
+  rs.x = make_rsrc(d.xq, (int64_t)d.m_tok * d.k);
+  const uint32_t ow = (uint32_t)(r * wbytes), om = (uint32_t)(r * (d.k / 8));
+  // LDS: [token rows m_tok*k (XL)][64 zero bytes][reduction ks*tb*4*64 ints]
+  const uint32_t xbytes = XL ? (uint32_t)(d.m_tok * d.k) : 0u;
+  const uint32_t zero_off = xbytes;
+  int32_t* red = reinterpret_cast<int32_t*>(smem + xbytes + 64);
+  const bool r_ok = r < d.m_tok;
+  const uint32_t ox = r_ok ? (uint32_t)(r * d.k) : (XL ? zero_off : kFar);
 
-  v4i c[kTW];
+  WStage wa[D];
+  u32x4 bring[XL ? 1 : D][4];
+  // weight loads of the first stages go out before the activations are staged
 #pragma unroll
-  for (int ti = 0; ti < kTW; ++ti) c[ti] = v4i{0, 0, 0, 0};
-  int qs = 0;
-  if (sb0 < sb1) {
-    Frag<KIND> cur;
-    load_frag<KIND>(cur, d, row0, r, r, sb0, nkb);
-    for (int sb = sb0; sb < sb1; ++sb) {
-      Frag<KIND> nxt;
-      const bool more = sb + 1 < sb1;
-      if (more) load_frag<KIND>(nxt, d, row0, r, r, sb + 1, nkb);
+  for (int j = 0; j < D; ++j) {
+    const int kb = 4 * (sb0 + j) + g;
+    const bool ok = j < nit && kb < nkb;
+    load_w<KIND>(wa[j], rs, ow, om, kb, ok);
+    if constexpr (!XL) load_x<false>(bring[j], rs, smem, ox, zero_off, kb, ok && r_ok);
+  }
+  if constexpr (XL) {
+    for (uint32_t o = threadIdx.x * 16u; o < xbytes; o += blockDim.x * 16u)
+      *reinterpret_cast<u32x4*>(smem + o) =
+          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.x, o, 0, 0));
+    if (threadIdx.x < 4) *reinterpret_cast<u32x4*>(smem + zero_off + 16 * threadIdx.x) = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();                               // activations (and the N:M tables)
+  } else if (KIND != kDense2) {
+    __syncthreads();                               // the N:M tables
+  }
+
+  v4i c = {0, 0, 0, 0}, ck = {0, 0, 0, 0};
+  // Ring of D stages.  The main loop loads unconditionally (stages past the
+  // wave's range read zeros), so the number of loads in flight is static and
+  // each step waits only for its own stage.
+  int it = 0;
+  for (; it + D <= nit; it += D) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const v4i b = {(int32_t)cur.b[i][0], (int32_t)cur.b[i][1], (int32_t)cur.b[i][2],
-                       (int32_t)cur.b[i][3]};
+    for (int j = 0; j < D; ++j) {
+      const int kb = 4 * (sb0 + it + j) + g;
+      u32x4 b[4];
+      if constexpr (XL) load_x<true>(b, rs, smem, ox, zero_off, kb, kb < nkb && r_ok);
+      else {
 #pragma unroll
-        for (int ti = 0; ti < kTW; ++ti)
-          c[ti] = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_a<KIND>(cur.a[ti], i, lut), b, c[ti], 0, 0, 0);
-        if (KIND == kDense2) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) qs = __builtin_amdgcn_sdot4(b[j], 0x01010101, qs, false);
-        }
+        for (int q = 0; q < 4; ++q) b[q] = bring[j][q];
       }
-      if (more) cur = nxt;
+      mac<KIND>(wa[j], b, c, ck, lut);
+      const int sb = sb0 + it + j + D;
+      const int kb2 = 4 * sb + g;
+      const bool ok = sb < sb1 && kb2 < nkb;
+      load_w<KIND>(wa[j], rs, ow, om, kb2, ok);
+      if constexpr (!XL) load_x<false>(bring[j], rs, smem, ox, zero_off, kb2, ok && r_ok);
+      __builtin_amdgcn_sched_barrier(0);            // keep each refill next to its use
     }
   }
-  if (KIND == kDense2) {
-    qs += __shfl_xor(qs, 16, 64);
-    qs += __shfl_xor(qs, 32, 64);                    // sum of q over this wave's k for token lane%16
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    if (it + j < nit) {
+      const int kb = 4 * (sb0 + it + j) + g;
+      u32x4 b[4];
+      if constexpr (XL) load_x<true>(b, rs, smem, ox, zero_off, kb, kb < nkb && r_ok);
+      else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) b[q] = bring[j][q];
+      }
+      mac<KIND>(wa[j], b, c, ck, lut);
+    }
   }
 #pragma unroll
-  for (int ti = 0; ti < kTW; ++ti)
+  for (int v = 0; v < 4; ++v) c[v] -= ck[v];
+  if (ks > 1) {
+    int32_t* rw = red + (tw * ks) * 4 * 64;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][ti * 4 + v][lane] = c[ti][v];
-  redq[wave][lane] = qs;
-  __syncthreads();
-  if (wave >= kTW) return;
-  const int ti = wave;
-  int32_t sum[4] = {0, 0, 0, 0};
-  int32_t qsum = 0;
+    for (int v = 0; v < 4; ++v) rw[(slice * 4 + v) * 64 + lane] = c[v];
+    __syncthreads();
+    if (slice != 0) return;
+    for (int w = 1; w < ks; ++w) {
 #pragma unroll
-  for (int w = 0; w < kKS; ++w) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) sum[v] += red[w][ti * 4 + v][lane];
-    qsum += redq[w][lane];
+      for (int v = 0; v < 4; ++v) c[v] += rw[(w * 4 + v) * 64 + lane];
+    }
   }
   const int t = r;                                   // C[4*(lane/16)+v][lane%16]: column = token
-  if (t >= d.m_tok) return;
+  if (t >= d.m_tok || row0 >= d.n_out) return;
   const float s = out_scale(d.beta, d.gamma, t);
-  const int64_t rbase = row0 + 16 * ti + 4 * g;
+  const int64_t rbase = row0 + 4 * g;
   float* yrow = d.y + (int64_t)t * d.n_out;
   int32_t* arow = d.acc ? d.acc + (int64_t)t * d.n_out : nullptr;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int64_t row = rbase + v;
     if (row < d.n_out) {
-      const int32_t a = sum[v] - (KIND == kDense2 ? qsum : 0);
-      yrow[row] = (float)a * s;
-      if (arow) arow[row] = a;
+      yrow[row] = (float)c[v] * s;
+      if (arow) arow[row] = c[v];
     }
   }
 }
@@ -227,21 +354,47 @@ int kind_of(int fmt, int n, int m) {
   return -1;
 }
 
+template <int KIND>
+void launch_gemv(const GemvLaunch& L, bool xl, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+  if (xl) hipLaunchKernelGGL((gemv_kernel<KIND, true>), grid, block, lds, s, L);
+  else hipLaunchKernelGGL((gemv_kernel<KIND, false>), grid, block, lds, s, L);
+}
+
 hipError_t launch_gemv_group(int kind, const LinDesc* items, int count, hipStream_t s) {
-  LinBatch b = {};
+  GemvLaunch L = {};
+  int tiles = 0, max_nsb = 1;
+  int64_t max_x = 0;
+  for (int i = 0; i < count; ++i) {
+    tiles += (int)((items[i].n_out + 15) / 16);
+    const int nsb = (items[i].k / 64 + 3) / 4;
+    max_nsb = nsb > max_nsb ? nsb : max_nsb;
+    const int64_t xb = (int64_t)items[i].m_tok * items[i].k;
+    max_x = xb > max_x ? xb : max_x;
+  }
+  if (tiles == 0) return hipSuccess;
+  // k split: about one round of resident waves; tiles per workgroup: up to 8 waves
+  int ks = kResidentWaves / tiles;
+  ks = ks < 1 ? 1 : (ks > kMaxWaves ? kMaxWaves : ks);
+  ks = ks > max_nsb ? max_nsb : ks;
+  int tb = 8 / ks;
+  tb = tb < 1 ? 1 : tb;
+  L.ks = ks;
+  L.tb = tb;
   int blocks = 0;
   for (int i = 0; i < count; ++i) {
-    b.d[i] = items[i];
-    b.start[i] = blocks;
-    blocks += (int)((items[i].n_out + 16 * kTW - 1) / (16 * kTW));
+    L.b.d[i] = items[i];
+    L.b.start[i] = blocks;
+    const int t = (int)((items[i].n_out + 15) / 16);
+    blocks += (t + tb - 1) / tb;
   }
-  b.start[count] = blocks;
-  b.count = count;
-  if (blocks == 0) return hipSuccess;
-  const dim3 grid((unsigned)blocks), block(kGemvThreads);
-  if (kind == kDense2) hipLaunchKernelGGL(gemv_kernel<kDense2>, grid, block, 0, s, b);
-  else if (kind == kNm68) hipLaunchKernelGGL(gemv_kernel<kNm68>, grid, block, 0, s, b);
-  else hipLaunchKernelGGL(gemv_kernel<kNm24>, grid, block, 0, s, b);
+  L.b.start[count] = blocks;
+  L.b.count = count;
+  const bool xl = max_x <= kXLdsMax;
+  const size_t lds = (xl ? (size_t)max_x : 0) + 64 + (ks > 1 ? (size_t)ks * tb * 4 * 64 * sizeof(int32_t) : 0);
+  const dim3 grid((unsigned)blocks), block(64 * ks * tb);
+  if (kind == kDense2) launch_gemv<kDense2>(L, xl, grid, block, lds, s);
+  else if (kind == kNm68) launch_gemv<kNm68>(L, xl, grid, block, lds, s);
+  else launch_gemv<kNm24>(L, xl, grid, block, lds, s);
   return hipGetLastError();
 }
 

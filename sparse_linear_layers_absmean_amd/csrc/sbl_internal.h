@@ -14,6 +14,12 @@ __device__ __forceinline__ u32x4 ld_stream16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Buffer resource over `bytes` (< 2^32) bytes at p: raw buffer loads past the
+// end return zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 // Workspace of the exact beta reduction of one matrix, in 64-bit words.
 //   [0, 256)       per-exponent sums of BF16 significands (values outside the
 //                  fast window), exact integers; accumulated with atomics by
@@ -38,6 +44,7 @@ inline AbsmeanPlan absmean_plan(int64_t total) {
   AbsmeanPlan p{(nvec + per_wg - 1) / per_wg, 8};
   if (p.nb > 1024) {          // big matrices: longer threads, at most 1024 slots (4096 at 2^34)
     p.vpt = (nvec + 1024 * kAbsThreads - 1) / (1024 * kAbsThreads);
+    p.vpt = (p.vpt + 7) / 8 * 8;                        // whole batches of 8 loads
     if (p.vpt > 2048) p.vpt = 2048;
     p.nb = (nvec + kAbsThreads * p.vpt - 1) / (kAbsThreads * p.vpt);
   }
