@@ -63,7 +63,31 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM measurement")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-gemv-sweep", action="store_true",
+                   help="skip the GEMV weight-bandwidth table over the decode configurations")
+    p.add_argument("--copy-calibration-mb", type=float, default=0.0,
+                   help="before the run, copy a buffer of this many MB 3 times (a known-size copy "
+                        "kernel for scaling hardware byte counters)")
     return p.parse_args()
+
+
+def recorded_traffic(call, workload, fmt):
+    """HBM bytes per call from the committed counter summary (profiles/traffic.json),
+    or None when there is none for this workload and format or when any kernel
+    source it was taken with has changed since (its SHA-256 differs)."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as fh:
+            rec = json.load(fh)[call]
+        if rec.get("workload") != workload or rec.get("format") != fmt:
+            return None
+        for path, digest in rec["sources_sha256"].items():
+            with open(os.path.join(ROOT, path), "rb") as fh:
+                if hashlib.sha256(fh.read()).hexdigest() != digest:
+                    return None
+        return rec["bytes_per_call"]
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def block(h, f):
@@ -104,6 +128,14 @@ def main():
     sbl.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration_mb > 0:
+        nb = int(args.copy_calibration_mb * 1e6) // 16 * 16
+        src = torch.ones(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wname, h, f, m_tok, desc = WORKLOADS[args.workload]
     if args.m_tok:
         m_tok = args.m_tok
@@ -228,7 +260,8 @@ def main():
 
     per_call = {
         "sbl_quant_weights": roof(qw_bytes, qw_ms, "sbl_quant_weights_batch over the 7 matrices: "
-                                  "absmean_partial + absmean_final + mask_pack kernels", 1),
+                                  "absmean_partial + absmean_final + mask_pack kernels", 1,
+                                  recorded_traffic("sbl_quant_weights", args.workload, args.fmt)),
         "sbl_quant_acts": roof(qa_bytes, qa_ms, "quant_acts_kernel", len(groups)),
         "sbl_linear": roof(lin_bytes, lin_ms, "gemv_kernel (grouped: qkv, o, gate+up, down)",
                            len(groups)),
@@ -236,6 +269,11 @@ def main():
     dominant = max(per_call, key=lambda kk: {"sbl_quant_weights": qw_ms, "sbl_quant_acts": qa_ms,
                                               "sbl_linear": lin_ms}[kk])
     gemv_gbps = weight_bytes / (lin_ms * 1e-3) / 1e9
+
+    # ---------------- GEMV weight bandwidth over the decode configurations
+    gemv = None
+    if not args.no_gemv_sweep:
+        gemv = gemv_sweep(torch, np, sbl, dev, synth)
 
     # ---------------- prefill GEMM (3B block, M = 2048 tokens), int8 ops
     prefill = None
@@ -248,6 +286,19 @@ def main():
         cpu = cpu_baseline(np, synth, wname, mats, m_tok, n, m, fmt, args.cpu_seconds, step_bytes)
 
     value = step_bytes / (step_ms * 1e-3) / 1e9
+    # the GEMV's roofline at the largest decode configuration (70B block, M = 1,
+    # this run's format) when the sweep ran; else the step's own GEMV launches
+    roofline_gemv = {"bound": "hbm", "achieved": round(gemv_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "workload": desc, "note": "packed weight bytes / sbl_linear_batch time"}
+    if gemv:
+        big = [g for g in gemv if g["block"] == "70b" and g["format"] == args.fmt and g["m_tok"] == 1]
+        if big:
+            roofline_gemv = {"bound": "hbm", "achieved": big[0]["weight_GBps"], "peak": HBM_PEAK_GBPS,
+                             "unit": "GB/s", "frac": big[0]["frac"], "traffic": None,
+                             "workload": "Decode GEMV, M=1, 70B-class block (hidden 8192, FFN 28672), "
+                                         f"{args.fmt}, 4 grouped launches",
+                             "note": "packed weight bytes (codes + metadata) / time of the block's launches"}
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -265,17 +316,83 @@ def main():
                    "block_weights": block_w, "rotation_copies": copies,
                    "step_algorithmic_bytes": step_bytes},
         "roofline": dict(per_call[dominant], call=dominant),
-        "roofline_gemv": {"bound": "hbm", "achieved": round(gemv_gbps, 1), "peak": HBM_PEAK_GBPS,
-                          "unit": "GB/s", "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4),
-                          "traffic": None, "weight_bytes_per_step": weight_bytes,
-                          "note": "packed weight bytes / sbl_linear_batch time, 4 grouped launches per block"},
+        "roofline_gemv": roofline_gemv,
         "per_call": per_call,
+        "gemv": gemv,
         "prefill": prefill,
         "cpu_baseline": cpu,
         "input_gen_s": round(gen_s, 1),
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
+
+
+def gemv_sweep(torch, np, sbl, dev, synth):
+    """Packed-weight GB/s of the grouped GEMV (sbl_linear_batch, 4 launches per
+    block: q/k/v, o, gate/up, down) for the decode configurations.  The packed
+    bytes are seeded random (the GEMV's time does not depend on the code
+    values); every block uses distinct buffers from a pool of >= 600 MB, so the
+    256 MB Infinity Cache cannot serve one launch from the previous one.  Each
+    block's 4 launches are one HIP graph; HIP events bracket the replays."""
+    cases = [("0p7b", 1536, 4096, 1), ("3b", 3200, 8640, 1), ("3b", 3200, 8640, 4),
+             ("3b", 3200, 8640, 8), ("70b", 8192, 28672, 1)]
+    groups = [[0, 1, 2], [3], [4, 5], [6]]
+    out = []
+    for wl, h, f, m_tok in cases:
+        mats = synth.block_shapes(h, f)
+        for fname, (fmt, n, m) in FORMATS.items():
+            nbytes = [sbl.sbl_packed_bytes(no, k, n, m, fmt) for _, no, k in mats]
+            mbytes = [no * k // 8 if fmt == 1 else 0 for _, no, k in mats]
+            block_bytes = sum(nbytes) + sum(mbytes)
+            copies = max(2, int(np.ceil(600e6 / block_bytes)))
+            gen = torch.Generator(device=dev).manual_seed(7)
+            pool = []
+            for _ in range(copies):
+                items = []
+                for i, (_, no, k) in enumerate(mats):
+                    packed = torch.randint(0, 256, (nbytes[i],), dtype=torch.uint8, device=dev, generator=gen)
+                    if fmt == 0:
+                        packed &= 0x55                            # 2-bit fields u in {0, 1}
+                    meta = (torch.randint(0, 256, (no, k // 8), dtype=torch.uint8, device=dev, generator=gen)
+                            if fmt == 1 else None)
+                    items.append(dict(packed=packed, meta=meta, beta=torch.full((1,), 0.02, device=dev),
+                                      n_out=no, y=torch.empty((m_tok, no), device=dev)))
+                pool.append(items)
+            xs = [torch.randint(-127, 128, (m_tok, mats[grp[0]][2]), dtype=torch.int8, device=dev,
+                                generator=gen) for grp in groups]
+            gam = torch.ones(m_tok, device=dev)
+
+            def run(c):
+                for gi, grp in enumerate(groups):
+                    sbl.sbl_linear_batch([dict(pool[c][i], xq=xs[gi], gamma=gam) for i in grp], fmt, n, m)
+
+            graphs = []
+            for c in range(copies):
+                run(c)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    run(c)
+                graphs.append(g)
+            reps = max(40, 2 * copies)
+            for r in range(copies):
+                graphs[r].replay()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for r in range(reps):
+                graphs[r % copies].replay()
+            b.record()
+            b.synchronize()
+            us = a.elapsed_time(b) * 1e3 / reps
+            gbps = block_bytes / (us * 1e-6) / 1e9
+            out.append({"block": wl, "format": fname, "m_tok": m_tok, "weight_bytes": block_bytes,
+                        "us_per_block": round(us, 2), "weight_GBps": round(gbps, 1),
+                        "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+            del pool, graphs, xs
+            torch.cuda.empty_cache()
+    return out
 
 
 def bench_prefill(torch, np, synth, sbl, dev, tm):
