@@ -4,26 +4,27 @@
 // is a dense contraction, so it runs on gfx950 int8 MFMA
 // (v_mfma_i32_32x32x32_i8, 32 rows x 32 tokens x 32 k per instruction).
 //
-// Tiling: a workgroup (4 waves) owns 256 weight rows x 256 tokens; wave w
-// owns rows 64w .. +64 (2 MFMA row tiles) x all 256 tokens (8 column
-// tiles): 16 accumulator tiles (256 AGPRs), one wave per SIMD.  Splitting
-// the rows (not the tokens) across waves means every weight operand is
-// decoded exactly once per workgroup; VALU work interleaved with MFMAs is
-// what limits a one-wave-per-SIMD int8 GEMM, so it is kept minimal.
-// The k loop advances 64 k per step (two MFMA sub-steps):
-//  * activations: each step's 256 token x 64 byte int8 tile is fetched into
-//    registers kDepth steps ahead with buffer loads, written to one of two
-//    LDS buffers one step ahead of use, and read back as B operands; 16-byte
-//    chunks are XOR-swizzled so consecutive tokens read distinct banks.
-//    Each B operand feeds 2 MFMAs (one per row tile).
-//  * weights: every lane fetches its packed words kDepth-1 steps ahead
-//    straight into registers and decodes them into A operands (7 VALU ops
-//    per 16 weights; N:M via LDS tables + v_perm); each A operand feeds 8
-//    MFMAs.
+// Tiling: a workgroup of 4 waves owns 32*KRT*4 weight rows x 32*KCT tokens;
+// wave w owns KRT row tiles (32 rows each) x all KCT token tiles, so every
+// weight operand is decoded exactly once per workgroup.  The k loop advances
+// 128 k per step (four 32-k MFMA sub-steps); the MFMA's k order is free as
+// long as A and B agree, so lane half g of a row takes the row's 64-weight
+// block 2*step + g whole, with one load per row tile per step, and uses only
+// the words it loaded (loads are the scarce resource here: the cost of a
+// vector memory instruction grows with the cache lines it touches, not with
+// its bytes).
+//  * activations: each step's token x 128 byte tile is fetched (eight tokens,
+//    whole 128-byte lines, per instruction) into registers kDepth steps
+//    ahead, written to one of two LDS buffers one step ahead of use and read
+//    back as B operands; the 16-byte chunks of a token row are XOR-swizzled
+//    by the token index so that consecutive tokens read distinct banks.
+//  * weights: fetched kDepth-1 steps ahead straight into registers and
+//    decoded into A operands (7 VALU ops per 16 weights; N:M via LDS tables
+//    + v_perm); each A operand feeds KCT MFMAs.
 //  * the per-step workgroup barrier waits only for LDS traffic, never for
 //    the global loads in flight.
-// The deep register pipeline keeps several steps of global loads in flight,
-// which one wave per SIMD needs to cover HBM / Infinity Cache latency.
+// K need only be a multiple of 64: in a last half step the second half reads
+// zeros (weights and activations), which adds nothing.
 // DENSE2 feeds u = c + 1 to the MFMA and subtracts sum_k q per token at the
 // end; the threads that stage activations into LDS accumulate those sums
 // with v_dot4 as they go (once per byte, not once per wave).  N:M decodes
@@ -39,53 +40,50 @@ using namespace dec;
 
 typedef int32_t v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 64;             // k per step
+constexpr int kBK = 128;            // k per step
 constexpr int kThreads = 256;
 constexpr int kDepth = 2;           // steps of loads in flight (registers)
 constexpr int kUnroll = 2;          // lcm(kDepth, 2 LDS buffers)
+constexpr uint32_t kFar = 0x80000000u;   // a buffer offset beyond every buffer: reads zeros
 
-// Raw weight bytes of one lane for one 64-k step of one row tile.  Lane
-// group g uses the 16-weight words 2h + g (h = 0, 1) of the row's 64-weight
-// block; raw data are kept untouched until decode so that no load result is
-// consumed early (which would force a wait on the whole prefetch pipeline).
+// Raw weight bytes of one lane for one step of one row tile: the whole
+// 64-weight block 2*step + g of the lane's row (g = lane half).  Raw data are
+// kept untouched until decode so that no load result is consumed early
+// (which would force a wait on the whole prefetch pipeline).
 template <int KIND> struct WRaw;
-template <> struct WRaw<kDense2> { uint32_t w[2]; };                 // words g and 2 + g
-template <> struct WRaw<kNm68> { uint32_t c[3]; uint32_t m[2]; };    // whole block: 12 code bytes, 8 meta bytes
-template <> struct WRaw<kNm24> { uint32_t c[2]; uint32_t m[2]; };    // whole block: 8 code bytes, 8 meta bytes
+template <> struct WRaw<kDense2> { uint32_t w[4]; };                 // 4 words of 16 weights
+template <> struct WRaw<kNm68> { uint32_t c[3]; uint32_t m[2]; };    // 12 code bytes, 8 meta bytes
+template <> struct WRaw<kNm24> { uint32_t c[2]; uint32_t m[2]; };    // 8 code bytes, 8 meta bytes
 
 __device__ __forceinline__ v4i lds_ld16(const uint8_t* p) {
   const u32x4 v = *reinterpret_cast<const u32x4*>(p);
   return v4i{(int32_t)v[0], (int32_t)v[1], (int32_t)v[2], (int32_t)v[3]};
 }
 
-// byte offset of 16-byte chunk c of token row r in an LDS activation tile.
-// The XOR swizzle makes the 16-byte reads of 8 (and of 16) consecutive rows
-// at the same chunk land in distinct bank groups: rows are 64 bytes, so rows
-// r and r+2 (128-byte banking) or r and r+4 (256-byte banking) would
-// otherwise collide.
-template <int kBK_ = kBK>
-__device__ __forceinline__ int bt_off(int r, int c) {
-  return r * kBK + 16 * (c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1)));
-}
+// byte offset of 16-byte chunk c (0..7) of token row r in an LDS activation
+// tile of 128-byte rows: XOR-swizzled by r so that 8 consecutive rows reading
+// the same chunk hit 8 distinct 16-byte bank groups.
+__device__ __forceinline__ int bt_off(int r, int c) { return r * kBK + 16 * (c ^ (r & 7)); }
 
 // Buffer resources: loads past the end of a buffer return zeros, so rows past
 // n_out and tokens past m_tok need neither branches nor clamping (their
 // results are never stored).  32-bit offsets: the host keeps every buffer of
-// this path below 2 GiB.
+// this path below 2 GiB.  kb: the lane's 64-weight block; past the row's
+// last block the offset is kFar (zeros).
 template <int KIND>
 __device__ __forceinline__ void load_w(WRaw<KIND>& a, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rm,
-                                       int voff_w, int voff_m, int ks) {
+                                       int voff_w, int voff_m, int kb, bool ok) {
   if constexpr (KIND == kDense2) {
-    a.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, voff_w, 16 * ks, 0);
-    a.w[1] = __builtin_amdgcn_raw_buffer_load_b32(rw, voff_w + 8, 16 * ks, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? voff_w + 16 * kb : kFar, 0, 0);
+    a.w[0] = v[0]; a.w[1] = v[1]; a.w[2] = v[2]; a.w[3] = v[3];
   } else if constexpr (KIND == kNm68) {
-    const auto c = __builtin_amdgcn_raw_buffer_load_b96(rw, voff_w, 12 * ks, 0);
-    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rm, voff_m, 8 * ks, 0);
+    const auto c = __builtin_amdgcn_raw_buffer_load_b96(rw, ok ? voff_w + 12 * kb : kFar, 0, 0);
+    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rm, ok ? voff_m + 8 * kb : kFar, 0, 0);
     a.c[0] = c[0]; a.c[1] = c[1]; a.c[2] = c[2];
     a.m[0] = m[0]; a.m[1] = m[1];
   } else {
-    const auto c = __builtin_amdgcn_raw_buffer_load_b64(rw, voff_w, 8 * ks, 0);
-    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rm, voff_m, 8 * ks, 0);
+    const auto c = __builtin_amdgcn_raw_buffer_load_b64(rw, ok ? voff_w + 8 * kb : kFar, 0, 0);
+    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rm, ok ? voff_m + 8 * kb : kFar, 0, 0);
     a.c[0] = c[0]; a.c[1] = c[1];
     a.m[0] = m[0]; a.m[1] = m[1];
   }
@@ -96,17 +94,18 @@ __device__ __forceinline__ void load_w(WRaw<KIND>& a, __amdgpu_buffer_rsrc_t rw,
 // flight across it; the "memory" clobber keeps LDS accesses on their side.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// A operand (16 weights, k order) of sub-step h (0: first 32 k, 1: second):
-// word w = 2h + g of the 64-weight block.
+// A operand (16 weights, k order) of sub-step j: word j of the lane's block.
 template <int KIND>
-__device__ __forceinline__ v4i decode_w(const WRaw<KIND>& a, int h, int g, const NmLut& L) {
+__device__ __forceinline__ v4i decode_w(const WRaw<KIND>& a, int j, const NmLut& L) {
   if constexpr (KIND == kDense2) {
-    return dense2_quad(a.w[h]);
+    return dense2_quad(a.w[j]);
   } else if constexpr (KIND == kNm68) {
-    // word w: codes = bits 24w .. 24w+23 of the 96-bit block, meta = bytes 2w, 2w+1
-    const uint32_t c24 = h == 0 ? (g ? __builtin_amdgcn_alignbit(a.c[1], a.c[0], 24) : a.c[0])
-                                : (g ? (a.c[2] >> 8) : __builtin_amdgcn_alignbit(a.c[2], a.c[1], 16));
-    const uint32_t m16 = (g ? (a.m[h] >> 16) : a.m[h]);
+    // word j: codes = bits 24j .. 24j+23 of the 96-bit block, meta = bytes 2j, 2j+1
+    const uint32_t c24 = j == 0 ? a.c[0]
+                       : j == 1 ? __builtin_amdgcn_alignbit(a.c[1], a.c[0], 24)
+                       : j == 2 ? __builtin_amdgcn_alignbit(a.c[2], a.c[1], 16)
+                                : (a.c[2] >> 8);
+    const uint32_t m16 = (j & 1) ? (a.m[j >> 1] >> 16) : a.m[j >> 1];
     v4i r;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -119,9 +118,9 @@ __device__ __forceinline__ v4i decode_w(const WRaw<KIND>& a, int h, int g, const
     }
     return r;
   } else {
-    // word w: codes = bytes 2w, 2w+1, meta = bytes 2w, 2w+1
-    const uint32_t c16 = g ? (a.c[h] >> 16) : a.c[h];
-    const uint32_t m16 = g ? (a.m[h] >> 16) : a.m[h];
+    // word j: codes = bytes 2j, 2j+1, meta = bytes 2j, 2j+1
+    const uint32_t c16 = (j & 1) ? (a.c[j >> 1] >> 16) : a.c[j >> 1];
+    const uint32_t m16 = (j & 1) ? (a.m[j >> 1] >> 16) : a.m[j >> 1];
     v4i r;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -154,33 +153,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const LinBatch batch)
   const int64_t n0 = (int64_t)tile_n * kBM;
   const int64_t t0 = (int64_t)tile_t * kBN;
   const int64_t K = d.k;
-  const int nks = (int)(K / kBK);
+  const int nks = (int)((K + kBK - 1) / kBK);      // steps; the last may be half (K % 128 == 64)
+  const int nkb = (int)(K / 64);                    // 64-weight blocks per row
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 31, g = lane >> 5;
   __shared__ int32_t qsum_lds[kBN];
 
-  // activation staging: thread -> token (tid >> 2) + 64p, 16-byte chunk tid & 3
-  const int st_tok = tid >> 2, st_chunk = tid & 3;
+  // activation staging: thread -> token (tid >> 3) + 32p, 16-byte chunk tid & 7
+  // (eight tokens' whole 128-byte rows per load instruction)
+  const int st_tok = tid >> 3, st_chunk = tid & 7;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(d.xq, (int64_t)d.m_tok * K);
   int voff_b[kStPasses];
 #pragma unroll
-  for (int p = 0; p < kStPasses; ++p) voff_b[p] = (int)((t0 + st_tok + 64 * p) * K + 16 * st_chunk);
+  for (int p = 0; p < kStPasses; ++p) voff_b[p] = (int)((t0 + st_tok + 32 * p) * K + 16 * st_chunk);
   auto load_b = [&](int ks, u32x4* r) {
+    const bool ok = kBK * ks + 16 * st_chunk < K;   // false: second half of a last half step
 #pragma unroll
     for (int p = 0; p < kStPasses; ++p) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, voff_b[p], kBK * ks, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? voff_b[p] + kBK * ks : (int)kFar, 0, 0);
       r[p] = u32x4{v[0], v[1], v[2], v[3]};
     }
   };
   int qpart[kStPasses] = {};                         // DENSE2: per staged token, sum of its q bytes
-  auto store_b = [&](int buf, const u32x4* r) {
+  // `real`: the staged step exists (only those count towards the q sums)
+  auto store_b = [&](int buf, const u32x4* r, bool real) {
 #pragma unroll
     for (int p = 0; p < kStPasses; ++p) {
-      *reinterpret_cast<u32x4*>(&btile[buf][bt_off(st_tok + 64 * p, st_chunk)]) = r[p];
-      if (KIND == kDense2) {
+      *reinterpret_cast<u32x4*>(&btile[buf][bt_off(st_tok + 32 * p, st_chunk)]) = r[p];
+      if (KIND == kDense2) {                        // branchless: a branch here costs the
+        int q = 0;                                  // loop its exact load wait counts
 #pragma unroll
-        for (int j = 0; j < 4; ++j) qpart[p] = __builtin_amdgcn_sdot4((int)r[p][j], 0x01010101, qpart[p], false);
+        for (int j = 0; j < 4; ++j) q = __builtin_amdgcn_sdot4((int)r[p][j], 0x01010101, q, false);
+        qpart[p] += real ? q : 0;
       }
     }
   };
@@ -192,12 +197,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const LinBatch batch)
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     const int64_t row = n0 + 32 * kRT * wave + 32 * rt + li;
-    voff_w[rt] = (int)(row * wrow_bytes + (KIND == kDense2 ? 4 * g : 0));
+    voff_w[rt] = (int)(row * wrow_bytes);
     voff_m[rt] = (int)(row * (K / 8));
   }
   auto load_wall = [&](int ks, WRaw<KIND>* a) {
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) load_w<KIND>(a[rt], rw, rm, voff_w[rt], voff_m[rt], ks);
+    for (int rt = 0; rt < kRT; ++rt) load_w<KIND>(a[rt], rw, rm, voff_w[rt], voff_m[rt], 2 * ks + g, 2 * ks + g < nkb);
   };
 
   v16i acc[kRT][kCT];
@@ -217,52 +222,65 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const LinBatch batch)
     }
   }
   if (KIND != kDense2) __syncthreads();             // tables built
-  store_b(0, bst[0]);
+  store_b(0, bst[0], true);
+  // Drain the prologue's loads once: the loop header's wait counts must hold
+  // on the entry path too, and there the scheduler leaves step 0's weights as
+  // the youngest loads, which would cost a full drain on every step.
+  // (gfx9 s_waitcnt encoding: vmcnt 0, expcnt 7, lgkmcnt 15.)
+  __builtin_amdgcn_s_waitcnt(0xF70);
   lds_barrier();
 
-  // one 64-k step; u = ks mod kUnroll fixes the register slot and LDS buffer
-  auto step = [&](const int ks, const int u) {
+  // one 64-k step; u = ks mod kUnroll fixes the register slot and LDS buffer.
+  // In the main loop (tail == false) the refills are unconditional: a refill
+  // past the last step only fills a slot nobody reads (buffer loads stay in
+  // bounds), and without branches around loads the compiler can wait for
+  // exactly the stage it needs instead of draining every load in flight.
+  auto step = [&](const int ks, const int u, const bool tail) {
     const int slot = u % kDepth;                    // == ks % kDepth (kUnroll is a multiple of kDepth)
     // activations of step ks + kDepth go to the slot step ks vacated (it is in LDS)
-    if (ks + kDepth < nks) load_b(ks + kDepth, bst[slot]);
+    if (!tail || ks + kDepth < nks) load_b(ks + kDepth, bst[slot]);
     const uint8_t* bt = &btile[u & 1][0];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {                   // 32-k MFMA sub-steps
-      v4i b[kCT];
+    for (int j = 0; j < 4; ++j) {                   // 32-k MFMA sub-steps: lane half g takes
+      v4i b[kCT];                                   // k = 128 ks + 64 g + 16 j .. +15
 #pragma unroll
-      for (int ct = 0; ct < kCT; ++ct) b[ct] = lds_ld16(bt + bt_off(32 * ct + li, 2 * h + g));
+      for (int ct = 0; ct < kCT; ++ct) b[ct] = lds_ld16(bt + bt_off(32 * ct + li, 4 * g + j));
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
-        const v4i a = decode_w<KIND>(wr[slot][rt], h, g, lut);
+        const v4i a = decode_w<KIND>(wr[slot][rt], j, lut);
 #pragma unroll
         for (int ct = 0; ct < kCT; ++ct)
           acc[rt][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[ct], acc[rt][ct], 0, 0, 0);
       }
     }
     // weights of step ks + kDepth reuse the slot just consumed
-    if (ks + kDepth < nks) load_wall(ks + kDepth, wr[slot]);
-    if (ks + 1 < nks) store_b((u + 1) & 1, bst[(u + 1) % kDepth]);
+    if (!tail || ks + kDepth < nks) load_wall(ks + kDepth, wr[slot]);
+    if (!tail || ks + 1 < nks) store_b((u + 1) & 1, bst[(u + 1) % kDepth], ks + 1 < nks);
     lds_barrier();
+    // no decode of a later step's weights may be hoisted into this one: there
+    // its loads are still the youngest in flight (a full drain)
+    __builtin_amdgcn_sched_barrier(0);
   };
-  // main loop without exits (keeps the accumulators resident in AGPRs),
-  // then the remaining nks % kUnroll steps
+  // main loop without exits (keeps the accumulators resident in AGPRs) over
+  // the steps whose refills are all real or harmless, then the last ones
   int ks0 = 0;
   for (; ks0 + kUnroll <= nks; ks0 += kUnroll) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) step(ks0 + u, u);
+    for (int u = 0; u < kUnroll; ++u) step(ks0 + u, u, false);
   }
 #pragma unroll
   for (int u = 0; u < kUnroll - 1; ++u)
-    if (ks0 + u < nks) step(ks0 + u, u);
+    if (ks0 + u < nks) step(ks0 + u, u, true);
 
-  // per-token sums of q (DENSE2): the 4 threads staging a token hold its 4 chunks
+  // per-token sums of q (DENSE2): the 8 threads staging a token hold its 8 chunks
   if (KIND == kDense2) {
 #pragma unroll
     for (int p = 0; p < kStPasses; ++p) {
       int v = qpart[p];
       v += __shfl_xor(v, 1, 64);
       v += __shfl_xor(v, 2, 64);
-      if (st_chunk == 0) qsum_lds[st_tok + 64 * p] = v;
+      v += __shfl_xor(v, 4, 64);
+      if (st_chunk == 0) qsum_lds[st_tok + 32 * p] = v;
     }
     __syncthreads();
   }
@@ -309,8 +327,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const LinBatch batch)
 // A launch costs whole rounds of 256 CUs: small tiles fill the chip when a
 // product has few large tiles (tile quantization), large tiles reuse operands.
 struct TileShape { int rows, toks, slots; double round_cost; };
-constexpr TileShape kShapes[] = {{256, 256, 1, 1.0}, {256, 128, 1, 0.59}, {128, 256, 1, 0.59},
-                                 {128, 128, 3, 0.75}};
+constexpr TileShape kShapes[] = {{256, 256, 1, 1.0}, {256, 128, 1, 0.63}, {128, 256, 1, 0.70},
+                                 {128, 128, 3, 0.90}};
 
 int pick_shape(const LinearArgs* items, int count) {
   int best = 0;
