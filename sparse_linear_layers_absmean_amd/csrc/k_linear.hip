@@ -5,19 +5,21 @@
 // int8 MFMA formulation (gfx950 v_mfma_i32_16x16x64_i8): weights are the A
 // operand (16 output rows x 64 k), activations the B operand (64 k x 16
 // tokens).  A lane holds 16 consecutive k of one row (A) or one token (B).
+//  * Both formats feed the MFMA u = c + 1 bytes at every k position, so that
+//    sum_k u q = sum_k c q + sum_k q: acc = MFMA(u, q) - MFMA(ones, q).  The
+//    second MFMA runs on the matrix pipe, which the decode leaves mostly idle.
 //  * DENSE2: one 16-weight word decodes with 7 VALU ops into four dwords of
-//    u = c + 1 bytes in natural k order; then sum_k u q = sum_k c q + sum_k q,
-//    so acc = MFMA result - sum_k q, with sum_k q from v_dot4 against 0x01010101.
-//  * N:M 6:8 and 2:4: per group, a 256-entry LDS table spreads the 2-bit kept
-//    codes into int8 c bytes, a second table (indexed by the metadata bitmap
-//    byte) gives v_perm selectors that scatter them to their k positions and
-//    zero the pruned ones: 2 table reads + 2 v_perm per 8 weights.
+//    u bytes (the word-transposed layout makes each dword one shift + mask).
+//  * N:M 6:8 and 2:4: per 8 weights, the 2-bit kept codes spread into bytes
+//    by shifts and masks, one LDS table read (indexed by the metadata bitmap
+//    byte) gives two v_perm selectors, and two v_perm place the codes at
+//    their k positions, with a pad byte u = 1 at the pruned ones.
 // Work split: a workgroup owns TB 16-row tiles of one matrix and TB*ks waves;
 // the ks waves of a tile split k.  ks and TB are chosen per launch so that the
 // grid is about one round of resident waves (a partial second round would run
 // at a fraction of the bandwidth).  When the token rows fit (m_tok*k <= 32 KB)
-// the workgroup stages them in LDS once and reads MFMA B operands from there,
-// with sum_k q computed once per token; otherwise B comes from global memory.
+// the workgroup stages them in LDS once and reads MFMA B operands from there;
+// otherwise B comes from global memory.
 // Each wave keeps kDepth weight loads in flight.  All global loads are buffer
 // loads: rows, k-blocks and tokens out of range read zeros, so there is no
 // branch around a load.  Partial int32 tiles of the ks waves are summed
@@ -34,6 +36,7 @@ using namespace dec;
 constexpr int kMaxWaves = 16;          // waves per workgroup, at most
 constexpr int kResidentWaves = 4096;   // one round: 4 waves per SIMD on 1024 SIMDs
 constexpr int kXLdsMax = 32 * 1024;    // token rows staged in LDS up to this many bytes
+constexpr int kXMinWaves = 4;          // XL launches have at least this many waves per workgroup
 constexpr uint32_t kFar = 0x80000000u; // a buffer offset beyond every buffer: reads zeros
 
 struct GemvLaunch {
@@ -89,67 +92,108 @@ __device__ __forceinline__ uint32_t fields4_to_bytes(uint32_t x) {
   return (y | (y << 6)) & 0x03030303u;
 }
 
-// N:M: 16 weights (operand i of the k-block) as u = c + 1 bytes at the kept
-// positions and 0 at the pruned ones, plus the keep mask as 0/1 bytes; the
-// product is then MFMA(u) - MFMA(keep).  One table read per 8 weights (the
-// v_perm selectors of the bitmap byte); the codes spread arithmetically.
+// v_perm selectors of the N:M decode, per bitmap byte: output byte p takes
+// the code byte of its rank among the kept positions, or a pad byte holding
+// u = 1 (code 0) where p is pruned.  The code bytes sit in bytes 0..3 (and
+// 4, 5 for 6:8) of the {hi, lo} source pair; the pad is byte 6 (6:8) or 4 (2:4).
 template <int KIND>
-__device__ __forceinline__ void nm_operands(const WStage& s, int i, const NmLut& L, v4i& u, v4i& km) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    uint32_t plo, phi, mb;
-    if constexpr (KIND == kNm68) {
-      const int G = 2 * i + h;                         // group of 8 within the k-block
-      const uint64_t lo64 = (uint64_t)s.a[0] | ((uint64_t)s.a[1] << 32);
-      const uint64_t hi64 = (uint64_t)s.a[1] | ((uint64_t)s.a[2] << 32);
-      const uint32_t c12 = (12 * G + 12 <= 64) ? (uint32_t)(lo64 >> (12 * G)) : (uint32_t)(hi64 >> (12 * G - 32));
-      plo = fields4_to_bytes(c12 & 0xFFu);
-      const uint32_t h4 = (c12 >> 8) & 0xFu;
-      phi = (h4 | (h4 << 6)) & 0x0303u;
-      mb = (s.a[3 + (G >> 2)] >> (8 * (G & 3))) & 0xFFu;
-    } else {
-      const int P = 2 * i + h;                         // code byte = two groups of 4
-      plo = fields4_to_bytes((s.a[P >> 2] >> (8 * (P & 3))) & 0xFFu);
-      phi = 0u;
-      mb = (s.a[2 + (P >> 2)] >> (8 * (P & 3))) & 0xFFu;
+__device__ void build_gemv_sel(uint32_t (*sel)[2]) {
+  for (int x = threadIdx.x; x < 256; x += blockDim.x) {
+    uint32_t s0 = 0, s1 = 0;
+    int ra = 0, rb = 0;
+    for (int p = 0; p < 8; ++p) {
+      const bool kept = (x >> p) & 1;
+      uint32_t v;
+      if (KIND == kNm68) {
+        v = 6u;
+        if (kept && ra < 6) v = (uint32_t)ra++;
+      } else {                                     // two 4-groups: codes 0,1 then 2,3
+        v = 4u;
+        if (p < 4) { if (kept && ra < 2) v = (uint32_t)ra++; }
+        else { if (kept && rb < 2) v = (uint32_t)(2 + rb++); }
+      }
+      if (p < 4) s0 |= v << (8 * p);
+      else s1 |= v << (8 * (p - 4));
     }
-    const uint32_t s0 = L.sel[mb][0], s1 = L.sel[mb][1];
-    u[2 * h] = (int32_t)__builtin_amdgcn_perm(phi, plo, s0);
-    u[2 * h + 1] = (int32_t)__builtin_amdgcn_perm(phi, plo, s1);
-    km[2 * h] = (int32_t)__builtin_amdgcn_perm(0x01010101u, 0x01010101u, s0);
-    km[2 * h + 1] = (int32_t)__builtin_amdgcn_perm(0x01010101u, 0x01010101u, s1);
+    sel[x][0] = s0;
+    sel[x][1] = s1;
   }
 }
 
-// One k-block: c += sum u q, ck += sum keep q (DENSE2: keep = every weight,
-// u from the 2-bit word decode), so that acc = c - ck.
-template <int KIND>
-__device__ __forceinline__ void mac(const WStage& s, const u32x4 (&bq)[4], v4i& c, v4i& ck, const NmLut& L) {
+// One k-block: c += sum u q over its 64 weights (and, if CK, ck += sum q), so
+// that acc = c - sum_k q.  u = c + 1 everywhere: DENSE2 decodes it from the 2-bit
+// words; N:M scatters the kept codes and pads the pruned positions with
+// u = 1.  N:M: the selector reads of 8 (or, under register pressure, twice 4)
+// groups go out first, the codes spread into bytes while they are in flight,
+// then 2 v_perm per 8 weights.
+template <int KIND, int HALVES, bool CK>
+__device__ __forceinline__ void mac(const WStage& s, const u32x4 (&bq)[4], v4i& c, v4i& ck,
+                                    const uint32_t (*sel)[2]) {
+  const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  if constexpr (KIND == kDense2) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const v4i b = {(int32_t)bq[i][0], (int32_t)bq[i][1], (int32_t)bq[i][2], (int32_t)bq[i][3]};
-    if constexpr (KIND == kDense2) {
+    for (int i = 0; i < 4; ++i) {
+      const v4i b = {(int32_t)bq[i][0], (int32_t)bq[i][1], (int32_t)bq[i][2], (int32_t)bq[i][3]};
       c = __builtin_amdgcn_mfma_i32_16x16x64_i8(dense2_quad(s.a[i]), b, c, 0, 0, 0);
-      const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-      ck = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, b, ck, 0, 0, 0);
-    } else {
-      v4i u, km;
-      nm_operands<KIND>(s, i, L, u, km);
-      c = __builtin_amdgcn_mfma_i32_16x16x64_i8(u, b, c, 0, 0, 0);
-      ck = __builtin_amdgcn_mfma_i32_16x16x64_i8(km, b, ck, 0, 0, 0);
+      if constexpr (CK) ck = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, b, ck, 0, 0, 0);
+    }
+  } else {
+    constexpr int MW = KIND == kNm68 ? 3 : 2;      // first metadata word in the stage
+    constexpr int NB = 8 / HALVES;                 // groups of 8 weights per batch
+#pragma unroll
+    for (int hb = 0; hb < HALVES; ++hb) {
+      uint32_t s0[NB], s1[NB], plo[NB], phi[NB];
+#pragma unroll
+      for (int gg = 0; gg < NB; ++gg) {
+        const int G = hb * NB + gg;
+        const uint32_t mb = (s.a[MW + (G >> 2)] >> (8 * (G & 3))) & 0xFFu;
+        const uint2 v = *reinterpret_cast<const uint2*>(&sel[mb][0]);
+        s0[gg] = v.x;
+        s1[gg] = v.y;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int gg = 0; gg < NB; ++gg) {
+        const int G = hb * NB + gg;
+        if constexpr (KIND == kNm68) {
+          const uint64_t lo64 = (uint64_t)s.a[0] | ((uint64_t)s.a[1] << 32);
+          const uint64_t hi64 = (uint64_t)s.a[1] | ((uint64_t)s.a[2] << 32);
+          const uint32_t c12 = (12 * G + 12 <= 64) ? (uint32_t)(lo64 >> (12 * G)) : (uint32_t)(hi64 >> (12 * G - 32));
+          plo[gg] = fields4_to_bytes(c12 & 0xFFu);
+          const uint32_t h4 = (c12 >> 8) & 0xFu;
+          phi[gg] = ((h4 | (h4 << 6)) & 0x0303u) | 0x00010000u;
+        } else {
+          plo[gg] = fields4_to_bytes((s.a[G >> 2] >> (8 * (G & 3))) & 0xFFu);
+          phi[gg] = 0x01010101u;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ii = 0; ii < NB / 2; ++ii) {
+        const int i = hb * (NB / 2) + ii;
+        const v4i b = {(int32_t)bq[i][0], (int32_t)bq[i][1], (int32_t)bq[i][2], (int32_t)bq[i][3]};
+        v4i u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int gg = 2 * ii + h;
+          u[2 * h] = (int32_t)__builtin_amdgcn_perm(phi[gg], plo[gg], s0[gg]);
+          u[2 * h + 1] = (int32_t)__builtin_amdgcn_perm(phi[gg], plo[gg], s1[gg]);
+        }
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(u, b, c, 0, 0, 0);
+        if constexpr (CK) ck = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, b, ck, 0, 0, 0);
+      }
     }
   }
 }
 
 // k-block kb = 4*sb + lane/16: super-block sb covers 256 weights of every row
-template <int KIND, bool XL>
+template <int KIND, bool XL, int D>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L) {
-  constexpr int D = XL ? 8 : 4;                      // weight loads in flight per wave
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ NmLut lut;
+  __shared__ uint32_t sel[256][2];
+  __shared__ int32_t qs[16];                          // XL: sum_k q per token
   const LinBatch& batch = L.b;
   const int ks = L.ks;
-  if (KIND != kDense2) build_lut<KIND>(lut);
   int di = 0;
   for (int i = 1; i < batch.count; ++i)
     if ((int)blockIdx.x >= batch.start[i]) di = i;
@@ -178,9 +222,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
   const bool r_ok = r < d.m_tok;
   const uint32_t ox = r_ok ? (uint32_t)(r * d.k) : (XL ? zero_off : kFar);
 
+  // XL: the activation loads go out first, so that they return ahead of the
+  // weight stages; each thread stages up to kXPer 16-byte pieces.
+  constexpr int kXPer = kXLdsMax / (16 * 64 * kXMinWaves);
+  u32x4 xv[XL ? kXPer : 1];
+  const int nxl = XL ? (int)((xbytes + blockDim.x * 16u - 1) / (blockDim.x * 16u)) : 0;   // <= kXPer
+  if constexpr (XL) {
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const uint32_t o = (threadIdx.x + i * blockDim.x) * 16u;
+      if (i < nxl)
+        xv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.x, o < xbytes ? o : kFar, 0, 0));
+    }
+    if (threadIdx.x < 16) qs[threadIdx.x] = 0;
+  }
   WStage wa[D];
   u32x4 bring[XL ? 1 : D][4];
-  // weight loads of the first stages go out before the activations are staged
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     const int kb = 4 * (sb0 + j) + g;
@@ -188,12 +245,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
     load_w<KIND>(wa[j], rs, ow, om, kb, ok);
     if constexpr (!XL) load_x<false>(bring[j], rs, smem, ox, zero_off, kb, ok && r_ok);
   }
+  if (KIND != kDense2) build_gemv_sel<KIND>(sel);
   if constexpr (XL) {
-    for (uint32_t o = threadIdx.x * 16u; o < xbytes; o += blockDim.x * 16u)
-      *reinterpret_cast<u32x4*>(smem + o) =
-          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.x, o, 0, 0));
     if (threadIdx.x < 4) *reinterpret_cast<u32x4*>(smem + zero_off + 16 * threadIdx.x) = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();                               // activations (and the N:M tables)
+    __syncthreads();                               // qs cleared
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const uint32_t o = (threadIdx.x + i * blockDim.x) * 16u;
+      if (i < nxl && o < xbytes) {
+        *reinterpret_cast<u32x4*>(smem + o) = xv[i];
+        int q = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) q = __builtin_amdgcn_sdot4((int)xv[i][w], 0x01010101, q, false);
+        atomicAdd(&qs[o / (uint32_t)d.k], q);
+      }
+    }
+    __syncthreads();                               // activations, sum q and the N:M tables
   } else if (KIND != kDense2) {
     __syncthreads();                               // the N:M tables
   }
@@ -213,7 +280,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
 #pragma unroll
         for (int q = 0; q < 4; ++q) b[q] = bring[j][q];
       }
-      mac<KIND>(wa[j], b, c, ck, lut);
+      mac<KIND, XL ? 1 : 2, !XL>(wa[j], b, c, ck, sel);
       const int sb = sb0 + it + j + D;
       const int kb2 = 4 * sb + g;
       const bool ok = sb < sb1 && kb2 < nkb;
@@ -232,34 +299,47 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
 #pragma unroll
         for (int q = 0; q < 4; ++q) b[q] = bring[j][q];
       }
-      mac<KIND>(wa[j], b, c, ck, lut);
+      mac<KIND, XL ? 1 : 2, !XL>(wa[j], b, c, ck, sel);
     }
   }
+  if constexpr (!XL) {
 #pragma unroll
-  for (int v = 0; v < 4; ++v) c[v] -= ck[v];
+    for (int v = 0; v < 4; ++v) c[v] -= ck[v];
+  }
+  // Partial tiles of the ks waves meet in LDS; wave s then finishes the output
+  // rows 4*(lane/16) + v with v = s (mod ks): C[4*(lane/16)+v][lane%16], column = token.
+  const int t = r;
   if (ks > 1) {
     int32_t* rw = red + (tw * ks) * 4 * 64;
 #pragma unroll
     for (int v = 0; v < 4; ++v) rw[(slice * 4 + v) * 64 + lane] = c[v];
     __syncthreads();
-    if (slice != 0) return;
-    for (int w = 1; w < ks; ++w) {
+    if (slice >= 4) return;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) c[v] += rw[(w * 4 + v) * 64 + lane];
+    for (int v = 0; v < 4; ++v) {
+      if (v % ks != slice) continue;
+      int32_t part[kMaxWaves];
+#pragma unroll
+      for (int w = 0; w < kMaxWaves; ++w) part[w] = w < ks ? rw[(w * 4 + v) * 64 + lane] : 0;
+      int32_t a = 0;
+#pragma unroll
+      for (int w = 0; w < kMaxWaves; ++w) a += part[w];
+      c[v] = a;
     }
   }
-  const int t = r;                                   // C[4*(lane/16)+v][lane%16]: column = token
   if (t >= d.m_tok || row0 >= d.n_out) return;
-  const float s = out_scale(d.beta, d.gamma, t);
+  const float sc = out_scale(d.beta, d.gamma, t);
+  const int32_t qt = XL ? qs[t] : 0;
   const int64_t rbase = row0 + 4 * g;
   float* yrow = d.y + (int64_t)t * d.n_out;
   int32_t* arow = d.acc ? d.acc + (int64_t)t * d.n_out : nullptr;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int64_t row = rbase + v;
-    if (row < d.n_out) {
-      yrow[row] = (float)c[v] * s;
-      if (arow) arow[row] = c[v];
+    if ((ks == 1 || v % ks == slice) && row < d.n_out) {
+      const int32_t a = c[v] - qt;
+      yrow[row] = (float)a * sc;
+      if (arow) arow[row] = a;
     }
   }
 }
@@ -354,10 +434,17 @@ int kind_of(int fmt, int n, int m) {
   return -1;
 }
 
+// D = weight stages in flight per wave: the wave's whole k range when it is short
 template <int KIND>
-void launch_gemv(const GemvLaunch& L, bool xl, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-  if (xl) hipLaunchKernelGGL((gemv_kernel<KIND, true>), grid, block, lds, s, L);
-  else hipLaunchKernelGGL((gemv_kernel<KIND, false>), grid, block, lds, s, L);
+void launch_gemv(const GemvLaunch& L, bool xl, int spw, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+  if (xl) {
+    if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, true, 2>), grid, block, lds, s, L);
+    else if (spw <= 4) hipLaunchKernelGGL((gemv_kernel<KIND, true, 4>), grid, block, lds, s, L);
+    else hipLaunchKernelGGL((gemv_kernel<KIND, true, 8>), grid, block, lds, s, L);
+  } else {
+    if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, false, 2>), grid, block, lds, s, L);
+    else hipLaunchKernelGGL((gemv_kernel<KIND, false, 4>), grid, block, lds, s, L);
+  }
 }
 
 hipError_t launch_gemv_group(int kind, const LinDesc* items, int count, hipStream_t s) {
@@ -378,6 +465,9 @@ hipError_t launch_gemv_group(int kind, const LinDesc* items, int count, hipStrea
   ks = ks > max_nsb ? max_nsb : ks;
   int tb = 8 / ks;
   tb = tb < 1 ? 1 : tb;
+  const bool xl = max_x <= kXLdsMax;
+  if (xl && ks * tb < kXMinWaves) tb = (kXMinWaves + ks - 1) / ks;   // the staging needs the threads
+  const int spw = (max_nsb + ks - 1) / ks;          // stages per wave
   L.ks = ks;
   L.tb = tb;
   int blocks = 0;
@@ -389,12 +479,11 @@ hipError_t launch_gemv_group(int kind, const LinDesc* items, int count, hipStrea
   }
   L.b.start[count] = blocks;
   L.b.count = count;
-  const bool xl = max_x <= kXLdsMax;
   const size_t lds = (xl ? (size_t)max_x : 0) + 64 + (ks > 1 ? (size_t)ks * tb * 4 * 64 * sizeof(int32_t) : 0);
   const dim3 grid((unsigned)blocks), block(64 * ks * tb);
-  if (kind == kDense2) launch_gemv<kDense2>(L, xl, grid, block, lds, s);
-  else if (kind == kNm68) launch_gemv<kNm68>(L, xl, grid, block, lds, s);
-  else launch_gemv<kNm24>(L, xl, grid, block, lds, s);
+  if (kind == kDense2) launch_gemv<kDense2>(L, xl, spw, grid, block, lds, s);
+  else if (kind == kNm68) launch_gemv<kNm68>(L, xl, spw, grid, block, lds, s);
+  else launch_gemv<kNm24>(L, xl, spw, grid, block, lds, s);
   return hipGetLastError();
 }
 
