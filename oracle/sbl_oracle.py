@@ -38,8 +38,9 @@ listed with its reason in the design notes):
     divisor is exact.
   * rescale: y = RN_fp32(fp32(acc) * RN_fp32(RN_fp32(beta_eff * gamma_eff) * 2^-7)).
   * byte formats (the pages only speak of "metadata" for the kernel) are
-    defined in `pack_dense2`, `pack_bitmap` and `pack_nm` below; they are
-    this implementation's choice, not the pages'.
+    defined in `pack_dense2`, `pack_bitmap` and `pack_nm` below, and the
+    storage order of the packed streams in `to_panels`; they are this
+    implementation's choice, not the pages'.
 
 Non-finite inputs are a precondition violation: the functions raise.
 
@@ -283,6 +284,46 @@ def unpack_nm(packed: np.ndarray, bitmap: np.ndarray, n: int, m: int, k: int) ->
     codes = np.zeros((n_out, k), dtype=np.int8)
     codes[keep] = (kept_u.astype(np.int16) - 1).astype(np.int8).ravel()
     return codes
+
+
+# --------------------------------------------------------------------------
+# a5: storage order of a packed stream (this implementation's choice, like the
+#     byte formats above; the pages fix neither)
+# --------------------------------------------------------------------------
+
+PANEL_BLOCKS = 4        # 64-weight blocks per panel: panels are 256 weights wide along k
+
+
+def to_panels(rows: np.ndarray, block_bytes: int) -> np.ndarray:
+    """Panel-major storage of a row-major packed stream.
+
+    `rows` is [n_out][row_bytes], every 64-weight block of a row taking
+    `block_bytes` bytes (DENSE2 16, N:M codes 16*n/m, bitmap 8).  The k axis
+    is cut into panels of PANEL_BLOCKS blocks; panel p holds, row after row,
+    the bytes of blocks 4p .. 4p+3 of every row (a last panel may hold fewer
+    blocks).  Returns the flat byte string.
+    """
+    r = np.asarray(rows, dtype=np.uint8)
+    if r.ndim != 2 or r.shape[1] % block_bytes:
+        raise ValueError("rows must be [n_out][whole blocks]")
+    width = PANEL_BLOCKS * block_bytes
+    return np.concatenate([r[:, s:s + width].reshape(-1) for s in range(0, r.shape[1], width)])
+
+
+def from_panels(flat: np.ndarray, n_out: int, row_bytes: int, block_bytes: int, rows=None) -> np.ndarray:
+    """Inverse of `to_panels`: the row-major bytes of all rows, or of `rows`."""
+    f = np.asarray(flat, dtype=np.uint8).reshape(-1)
+    if f.size != n_out * row_bytes or row_bytes % block_bytes:
+        raise ValueError("size mismatch")
+    sel = np.arange(n_out) if rows is None else np.asarray(rows, dtype=np.int64)
+    width = PANEL_BLOCKS * block_bytes
+    out = np.empty((sel.size, row_bytes), dtype=np.uint8)
+    for s in range(0, row_bytes, width):
+        w = min(width, row_bytes - s)
+        base = n_out * s                          # every earlier panel is full
+        idx = base + sel[:, None] * w + np.arange(w)[None, :]
+        out[:, s:s + w] = f[idx]
+    return out
 
 
 # --------------------------------------------------------------------------

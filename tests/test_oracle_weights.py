@@ -189,3 +189,31 @@ def test_dense2_layout_per_element_and_word_decode():
                 d = (int(words[b]) >> (2 * s)) & 0x03030303
                 got = [((d >> (8 * j)) & 3) - 1 for j in range(4)]
                 assert got == codes[r, 16 * b + 4 * s: 16 * b + 4 * s + 4].tolist()
+
+
+def test_panel_order_hand_example():
+    # 2 rows x 5 blocks of 16 bytes (k = 320, DENSE2): panel 0 = blocks 0..3 of
+    # row 0 then of row 1 (64 bytes each), panel 1 = block 4 of row 0, then row 1
+    rows = np.arange(160, dtype=np.uint8).reshape(2, 80)
+    want = list(range(0, 64)) + list(range(80, 144)) + list(range(64, 80)) + list(range(144, 160))
+    assert O.to_panels(rows, 16).tolist() == want
+
+
+def test_panel_order_per_byte_and_inverse():
+    # per-byte statement: byte j of row r (block kb = j // b) sits at
+    # n_out * (4b * (kb // 4)) + r * (blocks in that panel) * b + (j - 4b * (kb // 4))
+    rng = np.random.default_rng(68)
+    for n_out, nkb, b in [(3, 7, 16), (5, 4, 12), (2, 9, 8), (1, 6, 10), (4, 1, 16)]:
+        rows = rng.integers(0, 256, (n_out, nkb * b)).astype(np.uint8)
+        flat = O.to_panels(rows, b)
+        assert flat.size == rows.size
+        for r in range(n_out):
+            for j in range(nkb * b):
+                p = (j // b) // 4
+                nb = min(4, nkb - 4 * p)
+                assert flat[n_out * 4 * b * p + r * nb * b + (j - 4 * b * p)] == rows[r, j]
+        assert np.array_equal(O.from_panels(flat, n_out, nkb * b, b), rows)
+        pick = rng.choice(n_out, min(2, n_out), replace=False)
+        assert np.array_equal(O.from_panels(flat, n_out, nkb * b, b, rows=pick), rows[pick])
+    one = rng.integers(0, 256, (1, 5 * 16)).astype(np.uint8)
+    assert np.array_equal(O.to_panels(one, 16), one[0])        # one row: storage = row order
