@@ -449,10 +449,10 @@ def cpu_baseline(np, synth, wname, mats, m_tok, n, m, fmt, budget_s, step_bytes)
                 t = time.perf_counter()
                 beta, keep, codes = O.quant_weights(bits, n, m)
                 if fmt == 1:
-                    O.pack_nm(codes, keep, n, m)
-                    O.pack_bitmap(keep)
+                    O.to_panels(O.pack_nm(codes, keep, n, m), 16 * n // m)
+                    O.to_panels(O.pack_bitmap(keep), 8)
                 else:
-                    O.pack_dense2(codes)
+                    O.to_panels(O.pack_dense2(codes), 16)
                 q, gamma = O.quant_acts(x)
                 O.linear(codes, q, beta, gamma)
                 t_total += time.perf_counter() - t

@@ -38,19 +38,29 @@
  *    fp32(acc) is exact); m in {4, 8}; 1 <= n <= m; n_out*k <= 2^34.
  *
  * Byte formats (our own; the pages only say the kernel receives N:M
- * "metadata"):
- *  DENSE2  [n_out][k/4] bytes, 2 bits per weight holding u = c + 1 in
- *          {0,1,2} (3 is never written).  Weight kk of row r lives in byte
- *          r*(k/4) + 4*(kk/16) + kk%4, at bit offset 2*((kk/4)%4): in every
- *          16-weight little-endian word, (word >> 2s) & 0x03030303 gives the
- *          u of weights 4s..4s+3 in byte order, i.e. an int8 MFMA operand in
- *          natural k order after 7 VALU ops per 16 weights.
- *  BITMAP  [n_out][k/8] bytes: byte r*(k/8) + k/8, bit k%8 = 1 when kept.
+ * "metadata").  The content of one row:
+ *  DENSE2  k/4 bytes, 2 bits per weight holding u = c + 1 in {0,1,2} (3 is
+ *          never written).  Weight kk lives in row byte 4*(kk/16) + kk%4, at
+ *          bit offset 2*((kk/4)%4): in every 16-weight little-endian word,
+ *          (word >> 2s) & 0x03030303 gives the u of weights 4s..4s+3 in byte
+ *          order, i.e. an int8 MFMA operand in natural k order after 7 VALU
+ *          ops per 16 weights.
+ *  BITMAP  k/8 bytes: row byte kk/8, bit kk%8 = 1 when weight kk is kept.
  *          Serves as the mask output and as the N:M metadata.
- *  NM      [n_out][k*n/(4m)] bytes: the kept positions of row r, in
- *          ascending k, are numbered i = 0 .. k*n/m - 1; byte
- *          r*(k*n/(4m)) + i/4, bits 2*(i%4)..+1 hold u = c + 1.  Always used
- *          together with its BITMAP metadata.
+ *  NM      k*n/(4m) bytes: the kept positions of the row, in ascending k, are
+ *          numbered i = 0 .. k*n/m - 1; row byte i/4, bits 2*(i%4)..+1 hold
+ *          u = c + 1.  Always used together with its BITMAP metadata.
+ * Storage order.  The mask output (mask_bits) and the int8 codes are
+ * row-major: [n_out][k/8] and [n_out][k].  The packed stream (`packed`) and
+ * the N:M metadata (`meta`) are PANEL-MAJOR: each row's content is a
+ * sequence of 64-weight blocks of b bytes (DENSE2 16, NM 16*n/m, BITMAP 8);
+ * the k axis is cut into panels of 4 blocks (256 weights), and panel p holds,
+ * row after row, the bytes of blocks 4p .. 4p+3 of every row (the last panel
+ * holds fewer when k % 256 != 0).  Block kb of row r therefore starts at
+ *   (kb/4) * 4*b*n_out  +  r * nb * b  +  (kb%4) * b,
+ * where nb is the number of blocks in panel kb/4.  A 16-row decode tile then
+ * reads one contiguous run per panel, and a launch sweeps memory in address
+ * order.  Sizes are unchanged: sbl_packed_bytes and sbl_meta_bytes.
  */
 #ifndef SBL_H
 #define SBL_H
@@ -62,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SBL_ABI_VERSION 2
+#define SBL_ABI_VERSION 3
 
 typedef enum {
   SBL_OK = 0,
@@ -121,8 +131,8 @@ int sbl_workspace_init(void* workspace, int64_t workspace_bytes, sbl_stream stre
  *   codes      [n_out][k] int8 output in {-1,0,1} (already masked), or NULL.
  *   fmt        format of `packed`.
  *   packed     packed codes output (sbl_packed_bytes), or NULL.
- *   meta       [n_out][k/8] BITMAP output for fmt == SBL_FMT_NM (required
- *              there when packed != NULL); ignored for DENSE2.
+ *   meta       BITMAP metadata output, panel-major, for fmt == SBL_FMT_NM
+ *              (required there when packed != NULL); ignored for DENSE2.
  *   workspace  device scratch of at least sbl_workspace_bytes(n_out, k)
  *              bytes, 16-byte aligned, zero-filled before its first use
  *              (see sbl_workspace_init) and left ready for the next call.
@@ -163,8 +173,8 @@ int sbl_quant_weights_batch(const sbl_quant_item* items, int32_t count, int32_t 
  *              NM takes, per group, the codes of the first n kept positions
  *              in ascending k; a group with fewer than n kept bits is padded
  *              with code 0.
- *   packed     output (sbl_packed_bytes).
- *   meta       NM only: receives a copy of mask_bits, or NULL to skip.
+ *   packed     output (sbl_packed_bytes), panel-major.
+ *   meta       NM only: receives mask_bits in panel-major order, or NULL to skip.
  */
 int sbl_pack(const int8_t* codes, const uint8_t* mask_bits, int64_t n_out, int64_t k,
              int32_t n, int32_t m, int32_t fmt, uint8_t* packed, uint8_t* meta,

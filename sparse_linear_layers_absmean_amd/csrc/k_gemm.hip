@@ -65,25 +65,26 @@ __device__ __forceinline__ v4i lds_ld16(const uint8_t* p) {
 // the same chunk hit 8 distinct 16-byte bank groups.
 __device__ __forceinline__ int bt_off(int r, int c) { return r * kBK + 16 * (c ^ (r & 7)); }
 
-// Buffer resources: loads past the end of a buffer return zeros, so rows past
-// n_out and tokens past m_tok need neither branches nor clamping (their
-// results are never stored).  32-bit offsets: the host keeps every buffer of
-// this path below 2 GiB.  kb: the lane's 64-weight block; past the row's
-// last block the offset is kFar (zeros).
+// Buffer resources: loads past the end of a buffer return zeros, so tokens
+// past m_tok need neither branches nor clamping.  Weights are stored
+// panel-major (panel_offset); rows past n_out of a last tile read other rows'
+// bytes or zeros, and their results are never stored.  32-bit offsets: the
+// host keeps every buffer of this path below 2 GiB.  Past the row's last block
+// the offset is kFar (zeros).
 template <int KIND>
 __device__ __forceinline__ void load_w(WRaw<KIND>& a, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rm,
-                                       int voff_w, int voff_m, int kb, bool ok) {
+                                       uint32_t ow, uint32_t om, bool ok) {
   if constexpr (KIND == kDense2) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? voff_w + 16 * kb : kFar, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? ow : kFar, 0, 0);
     a.w[0] = v[0]; a.w[1] = v[1]; a.w[2] = v[2]; a.w[3] = v[3];
   } else if constexpr (KIND == kNm68) {
-    const auto c = __builtin_amdgcn_raw_buffer_load_b96(rw, ok ? voff_w + 12 * kb : kFar, 0, 0);
-    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rm, ok ? voff_m + 8 * kb : kFar, 0, 0);
+    const auto c = __builtin_amdgcn_raw_buffer_load_b96(rw, ok ? ow : kFar, 0, 0);
+    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rm, ok ? om : kFar, 0, 0);
     a.c[0] = c[0]; a.c[1] = c[1]; a.c[2] = c[2];
     a.m[0] = m[0]; a.m[1] = m[1];
   } else {
-    const auto c = __builtin_amdgcn_raw_buffer_load_b64(rw, ok ? voff_w + 8 * kb : kFar, 0, 0);
-    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rm, ok ? voff_m + 8 * kb : kFar, 0, 0);
+    const auto c = __builtin_amdgcn_raw_buffer_load_b64(rw, ok ? ow : kFar, 0, 0);
+    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rm, ok ? om : kFar, 0, 0);
     a.c[0] = c[0]; a.c[1] = c[1];
     a.m[0] = m[0]; a.m[1] = m[1];
   }
@@ -189,20 +190,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const LinBatch batch)
       }
     }
   };
-  // weights: row tile rt of this wave = rows n0 + 32*kRT*wn + 32rt + li
-  const int64_t wrow_bytes = KIND == kDense2 ? K / 4 : (KIND == kNm68 ? 3 * K / 16 : K / 8);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(d.packed, d.n_out * wrow_bytes);
+  // weights: row tile rt of this wave = rows n0 + 32*kRT*wn + 32rt + li; the
+  // lane's block 2*ks + g lies in panel ks/2 at block position 2*(ks&1) + g
+  constexpr uint32_t bw = KIND == kDense2 ? 16u : (KIND == kNm68 ? 12u : 8u);   // bytes per block
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(d.packed, d.n_out * nkb * (int64_t)bw);
   const __amdgpu_buffer_rsrc_t rm = make_rsrc(KIND == kDense2 ? d.packed : d.meta, d.n_out * (K / 8));
-  int voff_w[kRT], voff_m[kRT];
+  const int nfull = nkb / 4;                        // full panels
+  const uint32_t nbl = (uint32_t)(nkb - 4 * nfull); // blocks of a last partial panel
+  const uint32_t pb_w = 4u * bw * (uint32_t)d.n_out, pb_m = 32u * (uint32_t)d.n_out;
+  uint32_t full_w[kRT], full_m[kRT], last_w[kRT], last_m[kRT];
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
-    const int64_t row = n0 + 32 * kRT * wave + 32 * rt + li;
-    voff_w[rt] = (int)(row * wrow_bytes);
-    voff_m[rt] = (int)(row * (K / 8));
+    const uint32_t row = (uint32_t)(n0 + 32 * kRT * wave + 32 * rt + li);
+    full_w[rt] = row * 4u * bw;
+    full_m[rt] = row * 32u;
+    last_w[rt] = row * nbl * bw;
+    last_m[rt] = row * nbl * 8u;
   }
   auto load_wall = [&](int ks, WRaw<KIND>* a) {
+    const int p = ks >> 1;
+    const bool full = p < nfull;
+    const uint32_t bi = (uint32_t)(2 * (ks & 1) + g);
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) load_w<KIND>(a[rt], rw, rm, voff_w[rt], voff_m[rt], 2 * ks + g, 2 * ks + g < nkb);
+    for (int rt = 0; rt < kRT; ++rt)
+      load_w<KIND>(a[rt], rw, rm, (uint32_t)p * pb_w + (full ? full_w[rt] : last_w[rt]) + bi * bw,
+                   (uint32_t)p * pb_m + (full ? full_m[rt] : last_m[rt]) + bi * 8u, 2 * ks + g < nkb);
   };
 
   v16i acc[kRT][kCT];

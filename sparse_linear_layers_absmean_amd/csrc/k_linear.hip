@@ -54,18 +54,35 @@ struct Rsrc {
   __amdgpu_buffer_rsrc_t w, m, x;
 };
 
+// Bytes of one 64-weight block in the packed stream of each kind
+template <int KIND> constexpr uint32_t kBlockBytes = KIND == kDense2 ? 16u : (KIND == kNm68 ? 12u : 8u);
+
+// Panel-major addressing of a lane's blocks (panel_offset): block 4p + g of
+// row `row` sits at p * pb + row * (blocks in panel p) * b + g * b.  The lane
+// keeps the row terms of full panels and of the last, partial one.
+struct PanelLane {
+  uint32_t pb_w, pb_m;          // bytes of one full panel: codes, metadata
+  uint32_t full_w, full_m;      // row * 4 * b
+  uint32_t last_w, last_m;      // row * (blocks in the last panel) * b
+  int nfull;                    // full panels
+};
+
 template <int KIND>
-__device__ __forceinline__ void load_w(WStage& s, const Rsrc& rs, uint32_t ow, uint32_t om, int kb, bool kok) {
+__device__ __forceinline__ void load_w(WStage& s, const Rsrc& rs, const PanelLane& pl, int p, int g, bool kok) {
+  constexpr uint32_t bw = kBlockBytes<KIND>;
+  const bool full = p < pl.nfull;
+  const uint32_t ow = kok ? (uint32_t)p * pl.pb_w + (full ? pl.full_w : pl.last_w) + (uint32_t)g * bw : kFar;
+  const uint32_t om = kok ? (uint32_t)p * pl.pb_m + (full ? pl.full_m : pl.last_m) + (uint32_t)g * 8u : kFar;
   if constexpr (KIND == kDense2) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs.w, kok ? ow + (uint32_t)kb * 16u : kFar, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs.w, ow, 0, 0);
     s.a[0] = v[0]; s.a[1] = v[1]; s.a[2] = v[2]; s.a[3] = v[3];
   } else if constexpr (KIND == kNm68) {
-    const auto c = __builtin_amdgcn_raw_buffer_load_b96(rs.w, kok ? ow + (uint32_t)kb * 12u : kFar, 0, 0);
-    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rs.m, kok ? om + (uint32_t)kb * 8u : kFar, 0, 0);
+    const auto c = __builtin_amdgcn_raw_buffer_load_b96(rs.w, ow, 0, 0);
+    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rs.m, om, 0, 0);
     s.a[0] = c[0]; s.a[1] = c[1]; s.a[2] = c[2]; s.a[3] = m[0]; s.a[4] = m[1];
   } else {
-    const auto c = __builtin_amdgcn_raw_buffer_load_b64(rs.w, kok ? ow + (uint32_t)kb * 8u : kFar, 0, 0);
-    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rs.m, kok ? om + (uint32_t)kb * 8u : kFar, 0, 0);
+    const auto c = __builtin_amdgcn_raw_buffer_load_b64(rs.w, ow, 0, 0);
+    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rs.m, om, 0, 0);
     s.a[0] = c[0]; s.a[1] = c[1]; s.a[2] = m[0]; s.a[3] = m[1];
   }
 }
@@ -206,15 +223,26 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
   const int nsb = (nkb + 3) / 4;
   const int sb0 = slice * nsb / ks, sb1 = (slice + 1) * nsb / ks;
   const int nit = row0 < d.n_out ? sb1 - sb0 : 0;   // tiles past the matrix: no work
-  // buffers over this tile's rows (rows past n_out are outside them) and the activations
-  const int64_t rows = d.n_out - row0 < 16 ? (d.n_out - row0 > 0 ? d.n_out - row0 : 0) : 16;
-  const int64_t wbytes = KIND == kDense2 ? d.k / 4 : (KIND == kNm68 ? 3 * (int64_t)d.k / 16 : d.k / 8);
+  // buffers over the whole packed matrix (the host keeps them below 2^31 bytes)
+  // and the activations.  Rows past n_out of a last tile read other rows'
+  // bytes (or zeros past the end); their results are never stored.
+  constexpr uint32_t bw = kBlockBytes<KIND>;
   Rsrc rs;
-  rs.w = make_rsrc(d.packed + (rows ? row0 * wbytes : 0), rows * wbytes);
-  rs.m = make_rsrc(KIND == kDense2 ? d.packed : d.meta + (rows ? row0 * (d.k / 8) : 0),
-                   KIND == kDense2 ? 0 : rows * (d.k / 8));
+  rs.w = make_rsrc(d.packed, d.n_out * (int64_t)nkb * bw);
+  rs.m = make_rsrc(KIND == kDense2 ? d.packed : d.meta, KIND == kDense2 ? 0 : d.n_out * (int64_t)nkb * 8);
   rs.x = make_rsrc(d.xq, (int64_t)d.m_tok * d.k);
-  const uint32_t ow = (uint32_t)(r * wbytes), om = (uint32_t)(r * (d.k / 8));
+  PanelLane pl;
+  {
+    const uint32_t row = (uint32_t)(row0 + r);
+    const uint32_t nbl = (uint32_t)(nkb - 4 * (nkb / 4));          // blocks in a last partial panel
+    pl.pb_w = 4u * bw * (uint32_t)d.n_out;
+    pl.pb_m = 32u * (uint32_t)d.n_out;
+    pl.full_w = row * 4u * bw;
+    pl.full_m = row * 32u;
+    pl.last_w = row * nbl * bw;
+    pl.last_m = row * nbl * 8u;
+    pl.nfull = nkb / 4;
+  }
   // LDS: [token rows m_tok*k (XL)][64 zero bytes][reduction ks*tb*4*64 ints]
   const uint32_t xbytes = XL ? (uint32_t)(d.m_tok * d.k) : 0u;
   const uint32_t zero_off = xbytes;
@@ -242,7 +270,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
   for (int j = 0; j < D; ++j) {
     const int kb = 4 * (sb0 + j) + g;
     const bool ok = j < nit && kb < nkb;
-    load_w<KIND>(wa[j], rs, ow, om, kb, ok);
+    load_w<KIND>(wa[j], rs, pl, sb0 + j, g, ok);
     if constexpr (!XL) load_x<false>(bring[j], rs, smem, ox, zero_off, kb, ok && r_ok);
   }
   if (KIND != kDense2) build_gemv_sel<KIND>(sel);
@@ -284,7 +312,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
       const int sb = sb0 + it + j + D;
       const int kb2 = 4 * sb + g;
       const bool ok = sb < sb1 && kb2 < nkb;
-      load_w<KIND>(wa[j], rs, ow, om, kb2, ok);
+      load_w<KIND>(wa[j], rs, pl, sb, g, ok);
       if constexpr (!XL) load_x<false>(bring[j], rs, smem, ox, zero_off, kb2, ok && r_ok);
       __builtin_amdgcn_sched_barrier(0);            // keep each refill next to its use
     }
@@ -349,6 +377,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
 // the whole k; weights decoded to natural-order int8 bytes per 16 k.
 // ---------------------------------------------------------------------------
 
+// 16 weights at offset k0 (a multiple of 16) of one 64-weight block, from the
+// block's codes and bitmap bytes
 template <int M>
 __device__ v4i nm_bytes16(const uint8_t* __restrict__ codes_row, const uint8_t* __restrict__ meta_row,
                           int n, int64_t k0) {
@@ -392,17 +422,17 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(const uint8_t* __re
   const int64_t t = tok0 + (lane & 15);
   const int g = lane >> 4;
   const bool row_ok = r < n_out, tok_ok = t < m_tok;
-  const int64_t row_bytes = FMT == 0 ? k / 4 : k * n / (4 * M);
-  const uint8_t* wrow = packed + (row_ok ? r : 0) * row_bytes;
-  const uint8_t* mrow = FMT == 0 ? nullptr : meta + (row_ok ? r : 0) * (k / 8);
+  const int64_t nkb = k / 64, bw = FMT == 0 ? 16 : 16 * n / M;      // bytes per 64-weight block
+  const int64_t rr = row_ok ? r : 0;
   const int8_t* xrow = xq + (tok_ok ? t : 0) * k;
   v4i c = {0, 0, 0, 0};
   int qs = 0;
   for (int64_t kb = 0; kb < k; kb += 64) {
     const int64_t kk = kb + 16 * g;
+    const uint8_t* wblk = packed + panel_offset(n_out, nkb, bw, rr, kb / 64);     // panel-major blocks
     v4i a = {0, 0, 0, 0};
-    if (FMT == 0) a = dense2_quad(row_ok ? reinterpret_cast<const uint32_t*>(wrow)[kk >> 4] : 0x55555555u);
-    else if (row_ok) a = nm_bytes16<M>(wrow, mrow, n, kk);
+    if (FMT == 0) a = dense2_quad(row_ok ? reinterpret_cast<const uint32_t*>(wblk)[g] : 0x55555555u);
+    else if (row_ok) a = nm_bytes16<M>(wblk, meta + panel_offset(n_out, nkb, 8, rr, kb / 64), n, 16 * g);
     u32x4 nb = {0u, 0u, 0u, 0u};
     if (tok_ok) nb = ld16(xrow + kk);
     const v4i b = {(int32_t)nb[0], (int32_t)nb[1], (int32_t)nb[2], (int32_t)nb[3]};
@@ -500,6 +530,13 @@ hipError_t launch_linear_generic(const LinearArgs& a, int fmt, int n, int m, hip
   return hipGetLastError();
 }
 
+// whether the GEMV's 32-bit buffer offsets cover this product
+bool gemv_fits(const LinearArgs& a, int kind) {
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t bw = kind == kDense2 ? 16 : (kind == kNm68 ? 12 : 8);
+  return a.n_out * (a.k / 64) * bw < lim && a.n_out * (a.k / 8) < lim;
+}
+
 hipError_t launch_linear_batch(const LinearArgs* items, int count, int fmt, int n, int m,
                                hipStream_t s) {
   const int kind = kind_of(fmt, n, m);
@@ -510,7 +547,8 @@ hipError_t launch_linear_batch(const LinearArgs* items, int count, int fmt, int 
     const LinearArgs& a = items[i];
     if (a.m_tok == 0 || a.n_out == 0) continue;
     hipError_t e = hipSuccess;
-    if (kind < 0 || (a.m_tok > kGemvMaxTokens && !gemm_fits(a, kind))) {
+    if (kind < 0 || (a.m_tok > kGemvMaxTokens && !gemm_fits(a, kind)) ||
+        (a.m_tok <= kGemvMaxTokens && !gemv_fits(a, kind))) {
       e = launch_linear_generic(a, fmt, n, m, s);
     } else if (a.m_tok <= kGemvMaxTokens) {
       gemv[nv++] = to_desc(a);

@@ -27,7 +27,8 @@
 // One thread handles one 64-weight chunk (128 bytes of BF16): groups never
 // cross chunks (m divides 64) and chunks never cross rows (64 divides k), so
 // the matrix is processed as a flat array.  Per chunk it writes 16 bytes of
-// DENSE2, 8 bytes of bitmap, 64*n/m/4 bytes of N:M codes and 64 code bytes.
+// DENSE2, 8 bytes of bitmap, 64*n/m/4 bytes of N:M codes and 64 code bytes;
+// the packed stream and the N:M metadata go to their panel-major places.
 // DENSE2 word layout: see d2_shift.
 #include "sbl_internal.h"
 
@@ -90,10 +91,12 @@ __device__ __forceinline__ void nm_insert(ChunkOut& o, uint32_t u, int pos2) {
 }
 
 // NT > 0: compile-time n (unrolled stores); NT == 0: runtime n
+// Chunk c = block kb of row c / nkb: mask bits and codes go row-major, the
+// packed stream and the N:M metadata panel-major (panel_offset).
 template <int NT, int M>
 __device__ __forceinline__ void store_outputs(const ChunkOut& o, int64_t c, int n_rt,
                                               uint8_t* mask, int8_t* codes, int fmt,
-                                              uint8_t* packed, uint8_t* meta) {
+                                              uint8_t* packed, uint8_t* meta, int64_t n_out, int nkb) {
   const int n = NT > 0 ? NT : n_rt;
   constexpr int m = M;
   if (mask) reinterpret_cast<uint2*>(mask)[c] = make_uint2((uint32_t)o.keep, (uint32_t)(o.keep >> 32));
@@ -103,21 +106,26 @@ __device__ __forceinline__ void store_outputs(const ChunkOut& o, int64_t c, int 
     for (int i = 0; i < 4; ++i) cp[i] = make_uint4(o.cb[4 * i], o.cb[4 * i + 1], o.cb[4 * i + 2], o.cb[4 * i + 3]);
   }
   if (!packed) return;
+  const uint32_t row = (uint32_t)c / (uint32_t)nkb, kb = (uint32_t)c - row * (uint32_t)nkb;   // c < 2^28
   if (fmt == 0) {
-    reinterpret_cast<uint4*>(packed)[c] = make_uint4(o.d2[0], o.d2[1], o.d2[2], o.d2[3]);
+    *reinterpret_cast<uint4*>(packed + panel_offset(n_out, nkb, 16, row, kb)) =
+        make_uint4(o.d2[0], o.d2[1], o.d2[2], o.d2[3]);
     return;
   }
-  if (meta) reinterpret_cast<uint2*>(meta)[c] = make_uint2((uint32_t)o.keep, (uint32_t)(o.keep >> 32));
+  if (meta)
+    *reinterpret_cast<uint2*>(meta + panel_offset(n_out, nkb, 8, row, kb)) =
+        make_uint2((uint32_t)o.keep, (uint32_t)(o.keep >> 32));
   const int bytes = 16 * n / m;             // even; a multiple of 4 unless m == 8 and n is odd
+  uint8_t* const dst = packed + panel_offset(n_out, nkb, bytes, row, kb);
   const uint32_t w[4] = {(uint32_t)o.nm_lo, (uint32_t)(o.nm_lo >> 32), (uint32_t)o.nm_hi,
                          (uint32_t)(o.nm_hi >> 32)};
   if ((bytes & 3) == 0) {
-    uint32_t* p = reinterpret_cast<uint32_t*>(packed + c * bytes);
+    uint32_t* p = reinterpret_cast<uint32_t*>(dst);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (i < bytes / 4) p[i] = w[i];
   } else {
-    uint16_t* p = reinterpret_cast<uint16_t*>(packed + c * bytes);
+    uint16_t* p = reinterpret_cast<uint16_t*>(dst);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (i < bytes / 2) p[i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
@@ -306,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void mask_pack_fast_kernel(const QBatch b
   }
   o.nm_lo = (uint64_t)nmw[0] | ((uint64_t)nmw[1] << 32);
   o.nm_hi = (uint64_t)nmw[2] | ((uint64_t)nmw[3] << 32);
-  store_outputs<N, M>(o, c, N, d.mask, d.codes, FMT, d.packed, d.meta);
+  store_outputs<N, M>(o, c, N, d.mask, d.codes, FMT, d.packed, d.meta, d.n_out, d.nkb);
 }
 
 template <int M, int DROP>
@@ -376,16 +384,17 @@ __global__ __launch_bounds__(kThreads) void mask_pack_kernel(const QBatch batch,
         }
       }
     }
-    store_outputs<0, M>(o, c, n, d.mask, d.codes, fmt, packed, d.meta);
+    store_outputs<0, M>(o, c, n, d.mask, d.codes, fmt, packed, d.meta, d.n_out, d.nkb);
   }
 }
 
 // Packing of caller-supplied codes (+ mask for N:M).
 template <int M>
 __global__ __launch_bounds__(kThreads) void pack_kernel(const uint4* __restrict__ codes, const uint2* __restrict__ maskv,
-                                                        int64_t nchunks, int n, int fmt,
+                                                        int64_t n_out, int nkb, int n, int fmt,
                                                         uint8_t* __restrict__ packed,
                                                         uint8_t* __restrict__ meta) {
+  const int64_t nchunks = n_out * nkb;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
     uint32_t cw[16];
@@ -416,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const uint4* __restrict_
       }
       for (; fmt == 1 && kept < n; ++kept) nm_insert(o, 1u, 2 * (g * n + kept));
     }
-    store_outputs<0, M>(o, c, n, nullptr, nullptr, fmt, packed, meta);
+    store_outputs<0, M>(o, c, n, nullptr, nullptr, fmt, packed, meta, n_out, nkb);
   }
 }
 
@@ -455,16 +464,17 @@ hipError_t launch_mask_pack(QBatch& b, int n, int m, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_pack(const int8_t* codes, const uint8_t* mask, int64_t total, int n, int m,
+hipError_t launch_pack(const int8_t* codes, const uint8_t* mask, int64_t n_out, int64_t k, int n, int m,
                        int fmt, uint8_t* packed, uint8_t* meta, hipStream_t s) {
-  const int64_t nchunks = total / kChunk;
+  const int nkb = (int)(k / kChunk);
+  const int64_t nchunks = n_out * nkb;
   const dim3 grid((unsigned)grid_for(nchunks)), block(kThreads);
   const uint4* cv = reinterpret_cast<const uint4*>(codes);
   const uint2* mv = reinterpret_cast<const uint2*>(mask);
   if (m == 8)
-    hipLaunchKernelGGL((pack_kernel<8>), grid, block, 0, s, cv, mv, nchunks, n, fmt, packed, meta);
+    hipLaunchKernelGGL((pack_kernel<8>), grid, block, 0, s, cv, mv, n_out, nkb, n, fmt, packed, meta);
   else
-    hipLaunchKernelGGL((pack_kernel<4>), grid, block, 0, s, cv, mv, nchunks, n, fmt, packed, meta);
+    hipLaunchKernelGGL((pack_kernel<4>), grid, block, 0, s, cv, mv, n_out, nkb, n, fmt, packed, meta);
   return hipGetLastError();
 }
 

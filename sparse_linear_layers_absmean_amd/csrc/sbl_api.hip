@@ -105,6 +105,8 @@ sbl::QDesc to_qdesc(const sbl_quant_item& it, int32_t fmt) {
   d.packed = it.packed;
   d.fmt = it.packed ? fmt : SBL_FMT_DENSE2;
   d.meta = (it.packed && fmt == SBL_FMT_NM) ? it.meta : nullptr;
+  d.n_out = it.n_out;
+  d.nkb = (int32_t)(it.k / 64);
   return d;
 }
 
@@ -167,7 +169,7 @@ int sbl_pack(const int8_t* codes, const uint8_t* mask_bits, int64_t n_out, int64
   if (!aligned(codes, 16) || !aligned(packed, 16) || (mask_bits && !aligned(mask_bits, 16)) ||
       (meta && !aligned(meta, 16)))
     return SBL_ERR_ALIGN;
-  return launch_status(sbl::launch_pack(codes, mask_bits, n_out * k, n, m, fmt, packed,
+  return launch_status(sbl::launch_pack(codes, mask_bits, n_out, k, n, m, fmt, packed,
                                         fmt == SBL_FMT_NM ? meta : nullptr,
                                         reinterpret_cast<hipStream_t>(stream)));
 }

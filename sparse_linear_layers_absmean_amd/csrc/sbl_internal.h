@@ -59,6 +59,19 @@ inline int64_t workspace_bytes_for(int64_t total) {
 // Weights handled by one thread of the mask/pack kernels (one 128-byte BF16 chunk).
 constexpr int kChunk = 64;
 
+// Panel-major storage of a packed stream (DENSE2 or N:M codes, N:M metadata).
+// A row's stream is a sequence of 64-weight blocks of `b` bytes each; the k
+// axis is cut into panels of kPanelBlocks blocks (256 weights), and panel p
+// stores, row after row, the bytes of blocks kPanelBlocks*p ... of every row
+// (the last panel may hold fewer blocks).  Byte offset of block kb of `row`:
+constexpr int kPanelBlocks = 4;
+__host__ __device__ __forceinline__ int64_t panel_offset(int64_t n_out, int64_t nkb, int64_t b, int64_t row,
+                                                         int64_t kb) {
+  const int64_t p = kb / kPanelBlocks;
+  const int64_t nb = nkb - kPanelBlocks * p < kPanelBlocks ? nkb - kPanelBlocks * p : kPanelBlocks;
+  return p * kPanelBlocks * b * n_out + row * nb * b + (kb - kPanelBlocks * p) * b;
+}
+
 // One matrix of a grouped weight-preparation launch.
 struct QDesc {
   const u32x4* w;         // BF16 masters as 16-byte vectors (8 values each)
@@ -70,6 +83,8 @@ struct QDesc {
   int8_t* codes;
   uint8_t* packed;
   uint8_t* meta;
+  int64_t n_out;          // rows; k / 64 blocks per row (panel layout of packed, meta)
+  int32_t nkb;
   int32_t fmt;            // format of `packed`
 };
 constexpr int kMaxQDesc = 8;
@@ -87,7 +102,7 @@ hipError_t launch_mask_pack(QBatch& batch, int n, int m, hipStream_t s);
 
 hipError_t launch_workspace_init(uint64_t* ws, int64_t words, hipStream_t s);
 
-hipError_t launch_pack(const int8_t* codes, const uint8_t* mask, int64_t total, int n, int m,
+hipError_t launch_pack(const int8_t* codes, const uint8_t* mask, int64_t n_out, int64_t k, int n, int m,
                        int fmt, uint8_t* packed, uint8_t* meta, hipStream_t s);
 
 hipError_t launch_quant_acts(const float* x, int64_t m_tok, int64_t k, int8_t* xq, float* gamma,

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libsbl.so")
 SBL_OK = 0
 SBL_FMT_DENSE2 = 0
 SBL_FMT_NM = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32

@@ -65,7 +65,24 @@ def oracle_forward(bits: np.ndarray, x: np.ndarray, n: int, m: int):
     r["bitmap"] = O.pack_bitmap(r["keep"])
     r["dense2"] = O.pack_dense2(r["codes"])
     r["nm"] = O.pack_nm(r["codes"], r["keep"], n, m) if (bits.shape[1] * n // m) % 4 == 0 else None
+    r["n"], r["m"] = n, m
     return r
+
+
+def block_bytes(fmt: int, n: int, m: int) -> int:
+    """Bytes of one 64-weight block of the packed stream."""
+    return 16 if fmt == FMT_DENSE2 else 16 * n // m
+
+
+def packed_rows(flat, n_out: int, k: int, fmt: int, n: int, m: int, rows=None):
+    """Row-major content of a panel-major packed stream (all rows or `rows`)."""
+    b = block_bytes(fmt, n, m)
+    return O.from_panels(np.asarray(flat).reshape(-1), n_out, k // 64 * b, b, rows)
+
+
+def meta_rows(flat, n_out: int, k: int, rows=None):
+    """Row-major BITMAP of panel-major N:M metadata (all rows or `rows`)."""
+    return O.from_panels(np.asarray(flat).reshape(-1), n_out, k // 8, 8, rows)
 
 
 def check_y(y_gpu, y_ref, acc_ref):
@@ -80,11 +97,13 @@ def compare_all(g, r, fmt: int, n_out: int):
     assert g["beta"][0] == r["beta"], (g["beta"][0], r["beta"])
     assert np.array_equal(g["mask"], r["bitmap"])
     assert np.array_equal(g["codes"], r["codes"])
+    k = g["codes"].shape[1]
     if fmt == FMT_DENSE2:
-        assert np.array_equal(g["packed"].reshape(n_out, -1), r["dense2"])
+        assert np.array_equal(packed_rows(g["packed"], n_out, k, fmt, 8, 8), r["dense2"])
     else:
-        assert np.array_equal(g["packed"].reshape(n_out, -1), r["nm"])
-        assert np.array_equal(g["meta"], r["bitmap"])
+        n, m = r["n"], r["m"]
+        assert np.array_equal(packed_rows(g["packed"], n_out, k, fmt, n, m), r["nm"])
+        assert np.array_equal(meta_rows(g["meta"], n_out, k), r["bitmap"])
     assert np.array_equal(g["gamma"], r["gamma"])
     assert np.array_equal(g["xq"], r["q"])
     assert np.array_equal(g["acc"], r["acc"])

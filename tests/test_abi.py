@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.sbl_abi_version() == 2
+    assert lib.sbl_abi_version() == 3
     for st in range(7):
         assert len(lib.sbl_status_string(st)) > 0
     assert lib.sbl_last_hip_error() == 0

@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import FMT_DENSE2, FMT_NM, check_y, say, to_dev, to_np
+from gpu_util import FMT_DENSE2, FMT_NM, check_y, meta_rows, packed_rows, say, to_dev, to_np
 from oracle import sbl_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -99,12 +99,12 @@ def run_block(wname, h, f, m_tok, fmt, n, m, which=None, n_rows=40, n_toks=48):
         bitmap = O.pack_bitmap(keep)
         rows_t = torch.from_numpy(rows).cuda()
         assert np.array_equal(to_np(it["mask_bits"][rows_t]), bitmap), i
-        packed = it["packed"].view(no, -1)[rows_t]
+        packed = packed_rows(to_np(it["packed"]), no, k, fmt, n, m, rows=rows)
         if fmt == FMT_DENSE2:
-            assert np.array_equal(to_np(packed), O.pack_dense2(codes)), i
+            assert np.array_equal(packed, O.pack_dense2(codes)), i
         else:
-            assert np.array_equal(to_np(packed), O.pack_nm(codes, keep, n, m)), i
-            assert np.array_equal(to_np(it["meta"][rows_t]), bitmap), i
+            assert np.array_equal(packed, O.pack_nm(codes, keep, n, m)), i
+            assert np.array_equal(meta_rows(to_np(it["meta"]), no, k, rows=rows), bitmap), i
         lin, q_s, g_s, toks = results[i]
         toks_t = torch.from_numpy(toks).cuda()
         acc = to_np(lin["acc"][toks_t][:, rows_t])

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import FMT_DENSE2, FMT_NM, check_y, oracle_forward, say, to_dev, to_np
+from gpu_util import FMT_DENSE2, FMT_NM, check_y, oracle_forward, packed_rows, say, to_dev, to_np
 from oracle import sbl_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -79,7 +79,7 @@ def test_step_graph_replays_match_eager(fmt, n, m, m_tok):
         assert np.array_equal(eager[i]["acc"], r["acc"])
         check_y(eager[i]["y"], r["y"], r["acc"])
         want = O.pack_dense2(r["codes"]) if fmt == FMT_DENSE2 else r["nm"]
-        assert np.array_equal(eager[i]["packed"].reshape(no, -1), want)
+        assert np.array_equal(packed_rows(eager[i]["packed"], no, k, fmt, n, m), want)
 
     g = torch.cuda.CUDAGraph()
     clear()

@@ -9,7 +9,7 @@ import pytest
 import synth
 from oracle import sbl_oracle as O
 from gpu_util import (FMT_DENSE2, FMT_NM, check_y, compare_all, gpu_forward, gpu_quant_weights,
-                      oracle_forward, say, to_dev, to_np)
+                      meta_rows, oracle_forward, packed_rows, say, to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -148,9 +148,9 @@ def test_pack_standalone(n, m):
         sbl.sbl_pack(to_dev(codes), to_dev(bitmap), n, m, fmt, packed, meta)
         torch.cuda.synchronize()
         want = O.pack_dense2(codes) if fmt == FMT_DENSE2 else O.pack_nm(codes, keep, n, m)
-        assert np.array_equal(to_np(packed).reshape(n_out, -1), want)
+        assert np.array_equal(packed_rows(to_np(packed), n_out, k, fmt, n, m), want)
         if meta is not None:
-            assert np.array_equal(to_np(meta), bitmap)
+            assert np.array_equal(meta_rows(to_np(meta), n_out, k), bitmap)
 
 
 def test_deterministic_repeat():
@@ -265,10 +265,10 @@ def test_quant_weights_batch_matches_oracle(fmt, n, m):
         assert np.array_equal(g["mask_bits"], O.pack_bitmap(keep))
         assert np.array_equal(g["codes"], codes)
         if fmt == FMT_DENSE2:
-            assert np.array_equal(g["packed"].reshape(n_out, -1), O.pack_dense2(codes))
+            assert np.array_equal(packed_rows(g["packed"], n_out, k, fmt, n, m), O.pack_dense2(codes))
         else:
             if (k * n // m) % 4 == 0:
-                assert np.array_equal(g["packed"].reshape(n_out, -1), O.pack_nm(codes, keep, n, m))
-            assert np.array_equal(g["meta"], O.pack_bitmap(keep))
+                assert np.array_equal(packed_rows(g["packed"], n_out, k, fmt, n, m), O.pack_nm(codes, keep, n, m))
+            assert np.array_equal(meta_rows(g["meta"], n_out, k), O.pack_bitmap(keep))
         for key in g:
             assert np.array_equal(g[key], g2[key]), key
