@@ -464,13 +464,14 @@ int kind_of(int fmt, int n, int m) {
   return -1;
 }
 
-// D = weight stages in flight per wave: the wave's whole k range when it is short
+// D = weight stages in flight per wave: the wave's whole k range when it is
+// short, else 4 (with the panel-major layout the waves of a launch sweep the
+// matrix together, and a shallower ring keeps the sweep's front compact)
 template <int KIND>
 void launch_gemv(const GemvLaunch& L, bool xl, int spw, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
   if (xl) {
     if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, true, 2>), grid, block, lds, s, L);
-    else if (spw <= 4) hipLaunchKernelGGL((gemv_kernel<KIND, true, 4>), grid, block, lds, s, L);
-    else hipLaunchKernelGGL((gemv_kernel<KIND, true, 8>), grid, block, lds, s, L);
+    else hipLaunchKernelGGL((gemv_kernel<KIND, true, 4>), grid, block, lds, s, L);
   } else {
     if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, false, 2>), grid, block, lds, s, L);
     else hipLaunchKernelGGL((gemv_kernel<KIND, false, 4>), grid, block, lds, s, L);
