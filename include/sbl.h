@@ -133,6 +133,8 @@ int sbl_workspace_init(void* workspace, int64_t workspace_bytes, sbl_stream stre
  *   packed     packed codes output (sbl_packed_bytes), or NULL.
  *   meta       BITMAP metadata output, panel-major, for fmt == SBL_FMT_NM
  *              (required there when packed != NULL); ignored for DENSE2.
+ *              Must not overlap mask_bits (SBL_ERR_SHAPE): the two hold the
+ *              same bits in different orders.
  *   workspace  device scratch of at least sbl_workspace_bytes(n_out, k)
  *              bytes, 16-byte aligned, zero-filled before its first use
  *              (see sbl_workspace_init) and left ready for the next call.
@@ -227,6 +229,25 @@ typedef struct {
  * calling sbl_linear on each item. */
 int sbl_linear_batch(const sbl_linear_item* items, int32_t count, int32_t fmt, int32_t n,
                      int32_t m, sbl_stream stream);
+
+/* Activation quantization and the products that consume it, in one call: the
+ * layer input x is quantized exactly as sbl_quant_acts does (bitnet.cpp
+ * article, "Fundamento matematico", item 2) and every item's product is
+ * computed from it as sbl_linear_batch does (item 3).  Typical use: the q, k
+ * and v projections of one input.
+ *   x          [m_tok][k] fp32 input shared by every item.
+ *   xq, gamma  [m_tok][k] int8 and [m_tok] fp32 OUTPUTS (required), written
+ *              as sbl_quant_acts writes them.
+ *   items      1..256 products; each must have this m_tok and k; their xq
+ *              and gamma fields are ignored (the call uses its own).
+ * For decode-sized inputs (m_tok <= 16, at most 8 items, activations small
+ * enough to stage per workgroup) a single launch quantizes inside the
+ * product's workgroups; otherwise the call runs sbl_quant_acts and then
+ * sbl_linear_batch.  Validation as those two calls; results (xq, gamma, y,
+ * acc) are bit-identical to them. */
+int sbl_linear_acts_batch(const float* x, int64_t m_tok, int64_t k, int8_t* xq, float* gamma,
+                          const sbl_linear_item* items, int32_t count, int32_t fmt, int32_t n, int32_t m,
+                          sbl_stream stream);
 
 #ifdef __cplusplus
 }

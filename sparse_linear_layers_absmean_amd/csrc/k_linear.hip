@@ -37,6 +37,16 @@ constexpr int kMaxWaves = 16;          // waves per workgroup, at most
 constexpr int kResidentWaves = 4096;   // one round: 4 waves per SIMD on 1024 SIMDs
 constexpr int kXLdsMax = 32 * 1024;    // token rows staged in LDS up to this many bytes
 constexpr int kXMinWaves = 4;          // XL launches have at least this many waves per workgroup
+constexpr int kXFPer = 3;              // fused quantization: 16-value pieces of x per thread, at most
+
+// Activation quantization, identical to the standalone quantizer: step
+// s = max(gamma, 1e-5) / 128 (exact scaling), q = clamp(rint(x / s), -127, 127)
+// with one IEEE fp32 division.
+__device__ __forceinline__ float act_step(float gamma) { return fmaxf(gamma, 1e-5f) * 0.0078125f; }
+__device__ __forceinline__ uint32_t act_q(float v, float s) {
+  const float r = fminf(fmaxf(rintf(v / s), -127.0f), 127.0f);
+  return (uint32_t)((int32_t)r) & 0xFFu;
+}
 constexpr uint32_t kFar = 0x80000000u; // a buffer offset beyond every buffer: reads zeros
 
 struct GemvLaunch {
@@ -204,11 +214,13 @@ __device__ __forceinline__ void mac(const WStage& s, const u32x4 (&bq)[4], v4i& 
 }
 
 // k-block kb = 4*sb + lane/16: super-block sb covers 256 weights of every row
-template <int KIND, bool XL, int D>
+template <int KIND, bool XL, int D, bool XF>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L) {
+  static_assert(!XF || XL, "the fused activation quantization stages through LDS");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t sel[256][2];
   __shared__ int32_t qs[16];                          // XL: sum_k q per token
+  __shared__ uint32_t gbits[16];                      // XF: gamma per token (fp32 bits)
   const LinBatch& batch = L.b;
   const int ks = L.ks;
   int di = 0;
@@ -252,10 +264,24 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
 
   // XL: the activation loads go out first, so that they return ahead of the
   // weight stages; each thread stages up to kXPer 16-byte pieces.
-  constexpr int kXPer = kXLdsMax / (16 * 64 * kXMinWaves);
-  u32x4 xv[XL ? kXPer : 1];
+  // XF: the same pieces come as 16 fp32 values each (kXFPer per thread at most).
+  constexpr int kXPer = XF ? kXFPer : kXLdsMax / (16 * 64 * kXMinWaves);
+  u32x4 xv[XL && !XF ? kXPer : 1];
+  float4 xf4[XF ? kXPer : 1][4];
   const int nxl = XL ? (int)((xbytes + blockDim.x * 16u - 1) / (blockDim.x * 16u)) : 0;   // <= kXPer
-  if constexpr (XL) {
+  if constexpr (XF) {
+    const __amdgpu_buffer_rsrc_t rf = make_rsrc(d.x, (int64_t)xbytes * 4);
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const uint32_t o = (threadIdx.x + i * blockDim.x) * 16u;
+      if (i < nxl) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xf4[i][j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rf, o < xbytes ? 4 * o + 16 * j : kFar, 0, 0));
+      }
+    }
+    if (threadIdx.x < 16) { qs[threadIdx.x] = 0; gbits[threadIdx.x] = 0u; }
+  } else if constexpr (XL) {
 #pragma unroll
     for (int i = 0; i < kXPer; ++i) {
       const uint32_t o = (threadIdx.x + i * blockDim.x) * 16u;
@@ -274,7 +300,47 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
     if constexpr (!XL) load_x<false>(bring[j], rs, smem, ox, zero_off, kb, ok && r_ok);
   }
   if (KIND != kDense2) build_gemv_sel<KIND>(sel);
-  if constexpr (XL) {
+  if constexpr (XF) {
+    // per-token absmax (bitnet.cpp article, "Fundamento matematico", item 2),
+    // then the same quantization as the activation quantizer, staged into LDS
+    if (threadIdx.x < 4) *reinterpret_cast<u32x4*>(smem + zero_off + 16 * threadIdx.x) = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();                               // qs, gbits cleared
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const uint32_t o = (threadIdx.x + i * blockDim.x) * 16u;
+      if (i < nxl && o < xbytes) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xf4[i][j].x), fabsf(xf4[i][j].y)),
+                               fmaxf(fabsf(xf4[i][j].z), fabsf(xf4[i][j].w))));
+        atomicMax(&gbits[o / (uint32_t)d.k], __float_as_uint(mx));   // order of non-negative floats = of their bits
+      }
+    }
+    __syncthreads();                               // gamma per token
+    const bool publish = blockIdx.x == 0 && d.xq_out != nullptr;
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const uint32_t o = (threadIdx.x + i * blockDim.x) * 16u;
+      if (i < nxl && o < xbytes) {
+        const float sc = act_step(__uint_as_float(gbits[o / (uint32_t)d.k]));
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          v[j] = act_q(xf4[i][j].x, sc) | (act_q(xf4[i][j].y, sc) << 8) | (act_q(xf4[i][j].z, sc) << 16) |
+                 (act_q(xf4[i][j].w, sc) << 24);
+        *reinterpret_cast<u32x4*>(smem + o) = v;
+        if (publish) *reinterpret_cast<u32x4*>(d.xq_out + o) = v;
+        int q = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) q = __builtin_amdgcn_sdot4((int)v[w], 0x01010101, q, false);
+        atomicAdd(&qs[o / (uint32_t)d.k], q);
+      }
+    }
+    if (blockIdx.x == 0 && d.gamma_out != nullptr && threadIdx.x < (unsigned)d.m_tok)
+      d.gamma_out[threadIdx.x] = __uint_as_float(gbits[threadIdx.x]);
+    __syncthreads();                               // activations, sum q and the N:M tables
+  } else if constexpr (XL) {
     if (threadIdx.x < 4) *reinterpret_cast<u32x4*>(smem + zero_off + 16 * threadIdx.x) = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();                               // qs cleared
 #pragma unroll
@@ -356,7 +422,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
     }
   }
   if (t >= d.m_tok || row0 >= d.n_out) return;
-  const float sc = out_scale(d.beta, d.gamma, t);
+  const float sc = XF ? out_scale_g(d.beta, __uint_as_float(gbits[t])) : out_scale(d.beta, d.gamma, t);
   const int32_t qt = XL ? qs[t] : 0;
   const int64_t rbase = row0 + 4 * g;
   float* yrow = d.y + (int64_t)t * d.n_out;
@@ -468,18 +534,26 @@ int kind_of(int fmt, int n, int m) {
 // short, else 4 (with the panel-major layout the waves of a launch sweep the
 // matrix together, and a shallower ring keeps the sweep's front compact)
 template <int KIND>
-void launch_gemv(const GemvLaunch& L, bool xl, int spw, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-  if (xl) {
-    if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, true, 2>), grid, block, lds, s, L);
-    else hipLaunchKernelGGL((gemv_kernel<KIND, true, 4>), grid, block, lds, s, L);
+void launch_gemv(const GemvLaunch& L, bool xl, bool xf, int spw, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+  if (xf) {
+    if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, true, 2, true>), grid, block, lds, s, L);
+    else hipLaunchKernelGGL((gemv_kernel<KIND, true, 4, true>), grid, block, lds, s, L);
+  } else if (xl) {
+    if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, true, 2, false>), grid, block, lds, s, L);
+    else hipLaunchKernelGGL((gemv_kernel<KIND, true, 4, false>), grid, block, lds, s, L);
   } else {
-    if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, false, 2>), grid, block, lds, s, L);
-    else hipLaunchKernelGGL((gemv_kernel<KIND, false, 4>), grid, block, lds, s, L);
+    if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, false, 2, false>), grid, block, lds, s, L);
+    else hipLaunchKernelGGL((gemv_kernel<KIND, false, 4, false>), grid, block, lds, s, L);
   }
 }
 
-hipError_t launch_gemv_group(int kind, const LinDesc* items, int count, hipStream_t s) {
-  GemvLaunch L = {};
+// Launch shape of a grouped GEMV: k split (waves per tile) and tiles per
+// workgroup, about one round of resident waves.
+struct GemvShape {
+  int ks, tb, spw;
+  bool xl;
+};
+GemvShape gemv_shape(const LinDesc* items, int count) {
   int tiles = 0, max_nsb = 1;
   int64_t max_x = 0;
   for (int i = 0; i < count; ++i) {
@@ -489,32 +563,58 @@ hipError_t launch_gemv_group(int kind, const LinDesc* items, int count, hipStrea
     const int64_t xb = (int64_t)items[i].m_tok * items[i].k;
     max_x = xb > max_x ? xb : max_x;
   }
+  GemvShape g;
+  g.ks = tiles > 0 ? kResidentWaves / tiles : 1;
+  g.ks = g.ks < 1 ? 1 : (g.ks > kMaxWaves ? kMaxWaves : g.ks);
+  g.ks = g.ks > max_nsb ? max_nsb : g.ks;
+  g.tb = 8 / g.ks;
+  g.tb = g.tb < 1 ? 1 : g.tb;
+  g.xl = max_x <= kXLdsMax;
+  if (g.xl && g.ks * g.tb < kXMinWaves) g.tb = (kXMinWaves + g.ks - 1) / g.ks;   // the staging needs the threads
+  g.spw = (max_nsb + g.ks - 1) / g.ks;            // stages per wave
+  return g;
+}
+
+// whether the fused activation quantization covers m_tok x k activations at this shape
+bool gemv_fuses(const GemvShape& g, int64_t m_tok, int64_t k) {
+  return g.xl && m_tok * k <= (int64_t)16 * kXFPer * 64 * g.ks * g.tb;
+}
+
+// xf: fp32 activations shared by every item, quantized inside the launch
+// (the caller has checked gemv_fuses); xq_out / gamma_out: where the launch
+// publishes them (nullable).
+hipError_t launch_gemv_group(int kind, const LinDesc* items, int count, hipStream_t s, const float* xf = nullptr,
+                             int8_t* xq_out = nullptr, float* gamma_out = nullptr) {
+  GemvLaunch L = {};
+  int tiles = 0;
+  int64_t max_x = 0;
+  for (int i = 0; i < count; ++i) {
+    tiles += (int)((items[i].n_out + 15) / 16);
+    const int64_t xb = (int64_t)items[i].m_tok * items[i].k;
+    max_x = xb > max_x ? xb : max_x;
+  }
   if (tiles == 0) return hipSuccess;
-  // k split: about one round of resident waves; tiles per workgroup: up to 8 waves
-  int ks = kResidentWaves / tiles;
-  ks = ks < 1 ? 1 : (ks > kMaxWaves ? kMaxWaves : ks);
-  ks = ks > max_nsb ? max_nsb : ks;
-  int tb = 8 / ks;
-  tb = tb < 1 ? 1 : tb;
-  const bool xl = max_x <= kXLdsMax;
-  if (xl && ks * tb < kXMinWaves) tb = (kXMinWaves + ks - 1) / ks;   // the staging needs the threads
-  const int spw = (max_nsb + ks - 1) / ks;          // stages per wave
-  L.ks = ks;
-  L.tb = tb;
+  const GemvShape g = gemv_shape(items, count);
+  L.ks = g.ks;
+  L.tb = g.tb;
   int blocks = 0;
   for (int i = 0; i < count; ++i) {
     L.b.d[i] = items[i];
+    L.b.d[i].x = xf;
+    L.b.d[i].xq_out = xq_out;
+    L.b.d[i].gamma_out = gamma_out;
     L.b.start[i] = blocks;
     const int t = (int)((items[i].n_out + 15) / 16);
-    blocks += (t + tb - 1) / tb;
+    blocks += (t + g.tb - 1) / g.tb;
   }
   L.b.start[count] = blocks;
   L.b.count = count;
-  const size_t lds = (xl ? (size_t)max_x : 0) + 64 + (ks > 1 ? (size_t)ks * tb * 4 * 64 * sizeof(int32_t) : 0);
-  const dim3 grid((unsigned)blocks), block(64 * ks * tb);
-  if (kind == kDense2) launch_gemv<kDense2>(L, xl, spw, grid, block, lds, s);
-  else if (kind == kNm68) launch_gemv<kNm68>(L, xl, spw, grid, block, lds, s);
-  else launch_gemv<kNm24>(L, xl, spw, grid, block, lds, s);
+  const size_t lds = (g.xl ? (size_t)max_x : 0) + 64 + (g.ks > 1 ? (size_t)g.ks * g.tb * 4 * 64 * sizeof(int32_t) : 0);
+  const dim3 grid((unsigned)blocks), block(64 * g.ks * g.tb);
+  const bool xf_on = xf != nullptr;
+  if (kind == kDense2) launch_gemv<kDense2>(L, g.xl, xf_on, g.spw, grid, block, lds, s);
+  else if (kind == kNm68) launch_gemv<kNm68>(L, g.xl, xf_on, g.spw, grid, block, lds, s);
+  else launch_gemv<kNm24>(L, g.xl, xf_on, g.spw, grid, block, lds, s);
   return hipGetLastError();
 }
 
@@ -572,6 +672,24 @@ hipError_t launch_linear_batch(const LinearArgs* items, int count, int fmt, int 
   }
   if (nm) return launch_gemm_group(gemm, nm, kind, s);
   return hipSuccess;
+}
+
+hipError_t launch_linear_acts(const float* x, int64_t m_tok, int64_t k, int8_t* xq, float* gamma,
+                              const LinearArgs* items, int count, int fmt, int n, int m, hipStream_t s) {
+  const int kind = kind_of(fmt, n, m);
+  bool fuse = kind >= 0 && m_tok <= kGemvMaxTokens && count <= kMaxDesc;
+  LinDesc ds[kMaxDesc];
+  int nd = 0;
+  for (int i = 0; fuse && i < count; ++i) {
+    if (items[i].n_out == 0) continue;
+    if (!gemv_fits(items[i], kind)) fuse = false;
+    else ds[nd++] = to_desc(items[i]);
+  }
+  fuse = fuse && nd > 0 && gemv_fuses(gemv_shape(ds, nd), m_tok, k);
+  if (fuse) return launch_gemv_group(kind, ds, nd, s, x, xq, gamma);
+  const hipError_t e = launch_quant_acts(x, m_tok, k, xq, gamma, s);
+  if (e != hipSuccess) return e;
+  return launch_linear_batch(items, count, fmt, n, m, s);
 }
 
 }  // namespace sbl

@@ -75,10 +75,19 @@ int sbl_workspace_init(void* workspace, int64_t workspace_bytes, sbl_stream stre
 
 namespace {
 
+bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a && b && a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
 int check_quant(const sbl_quant_item& it, int32_t n, int32_t m, int32_t fmt) {
   if (!it.w_bf16 || !it.beta) return SBL_ERR_NULL;
   if (it.packed && fmt == SBL_FMT_NM && !it.meta) return SBL_ERR_NULL;
   if (it.n_out < 1 || !k_ok(it.k) || it.n_out * it.k > kMaxElems) return SBL_ERR_SHAPE;
+  // the row-major mask and the panel-major metadata are different byte orders
+  if (it.packed && fmt == SBL_FMT_NM &&
+      ranges_overlap(it.mask_bits, it.n_out * (it.k / 8), it.meta, it.n_out * (it.k / 8)))
+    return SBL_ERR_SHAPE;
   if (!it.workspace || it.workspace_bytes < sbl::workspace_bytes_for(it.n_out * it.k))
     return SBL_ERR_WORKSPACE;
   if (!nm_ok(n, m)) return SBL_ERR_UNSUPPORTED;
@@ -227,6 +236,29 @@ int sbl_linear(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t 
   if (st != SBL_OK || m_tok == 0 || n_out == 0) return st;
   const sbl::LinearArgs a = to_args(it, fmt);
   return launch_status(sbl::launch_linear_batch(&a, 1, fmt, n, m, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int sbl_linear_acts_batch(const float* x, int64_t m_tok, int64_t k, int8_t* xq, float* gamma,
+                          const sbl_linear_item* items, int32_t count, int32_t fmt, int32_t n, int32_t m,
+                          sbl_stream stream) {
+  if (!items) return SBL_ERR_NULL;
+  if (count < 1 || count > 256) return SBL_ERR_SHAPE;
+  if (m_tok < 0 || m_tok > kMaxTokens || !k_ok(k)) return SBL_ERR_SHAPE;
+  if (m_tok > 0 && (!x || !xq || !gamma)) return SBL_ERR_NULL;
+  if (m_tok > 0 && (!aligned(x, 16) || !aligned(xq, 16) || !aligned(gamma, 4))) return SBL_ERR_ALIGN;
+  sbl::LinearArgs args[256];
+  for (int i = 0; i < count; ++i) {
+    sbl_linear_item it = items[i];
+    if (it.m_tok != m_tok || it.k != k) return SBL_ERR_SHAPE;
+    it.xq = xq;
+    it.gamma = gamma;
+    const int st = check_linear(it, fmt, n, m);
+    if (st != SBL_OK) return st;
+    args[i] = to_args(it, fmt);
+  }
+  if (m_tok == 0) return SBL_OK;
+  return launch_status(sbl::launch_linear_acts(x, m_tok, k, xq, gamma, args, count, fmt, n, m,
+                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
 int sbl_linear_batch(const sbl_linear_item* items, int32_t count, int32_t fmt, int32_t n,

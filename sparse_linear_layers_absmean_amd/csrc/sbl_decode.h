@@ -23,10 +23,14 @@ __device__ __forceinline__ v4i dense2_quad(uint32_t w) {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-__device__ __forceinline__ float out_scale(const float* beta, const float* gamma, int64_t t) {
+__device__ __forceinline__ float out_scale_g(const float* beta, float gamma) {
   const float b = fmaxf(beta[0], 1e-5f);
-  const float g = fmaxf(gamma[t], 1e-5f);
+  const float g = fmaxf(gamma, 1e-5f);
   return (b * g) * 0.0078125f;   // RN(RN(beta*gamma) * 2^-7); the power of two is exact
+}
+
+__device__ __forceinline__ float out_scale(const float* beta, const float* gamma, int64_t t) {
+  return out_scale_g(beta, gamma[t]);
 }
 
 // LDS lookup tables of the N:M decode
@@ -72,6 +76,11 @@ struct LinDesc {
   int32_t k;
   int32_t m_tok;
   int32_t tiles_n;        // GEMM: row tiles of this matrix
+  // GEMV with the activation quantization fused in: fp32 input, and the
+  // quantized activations and scales to publish (nullable; written once)
+  const float* x;
+  int8_t* xq_out;
+  float* gamma_out;
 };
 
 inline LinDesc to_desc(const LinearArgs& a) {
@@ -79,6 +88,7 @@ inline LinDesc to_desc(const LinearArgs& a) {
   d.packed = a.packed; d.meta = a.meta; d.xq = a.xq; d.gamma = a.gamma; d.beta = a.beta;
   d.y = a.y; d.acc = a.acc; d.n_out = a.n_out; d.k = (int32_t)a.k; d.m_tok = (int32_t)a.m_tok;
   d.tiles_n = 0;
+  d.x = nullptr; d.xq_out = nullptr; d.gamma_out = nullptr;
   return d;
 }
 

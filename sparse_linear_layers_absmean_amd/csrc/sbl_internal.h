@@ -125,6 +125,12 @@ constexpr int64_t kGemvMaxTokens = 16;
 hipError_t launch_linear_batch(const LinearArgs* items, int count, int fmt, int n, int m,
                                hipStream_t s);
 
+// Activation quantization of x into xq / gamma and the products of every item
+// from them (each item: m_tok x k activations, xq / gamma set to these).  For
+// decode-sized inputs that fit, one GEMV launch does both.
+hipError_t launch_linear_acts(const float* x, int64_t m_tok, int64_t k, int8_t* xq, float* gamma,
+                              const LinearArgs* items, int count, int fmt, int n, int m, hipStream_t s);
+
 // any shape, any n:m (one wave per 16 rows x 16 tokens)
 hipError_t launch_linear_generic(const LinearArgs& a, int fmt, int n, int m, hipStream_t s);
 

@@ -88,6 +88,9 @@ def load():
                                _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]
     lib.sbl_linear_batch.restype = ctypes.c_int
     lib.sbl_linear_batch.argtypes = [ctypes.POINTER(LinearItem), _c_i32, _c_i32, _c_i32, _c_i32, _c_p]
+    lib.sbl_linear_acts_batch.restype = ctypes.c_int
+    lib.sbl_linear_acts_batch.argtypes = [_c_p, _c_i64, _c_i64, _c_p, _c_p, ctypes.POINTER(LinearItem),
+                                          _c_i32, _c_i32, _c_i32, _c_i32, _c_p]
     if lib.sbl_abi_version() != ABI_VERSION:
         raise RuntimeError("libsbl.so ABI version mismatch: rebuild it")
     _lib = lib
@@ -258,6 +261,28 @@ def sbl_linear_batch(items, fmt: int, n: int, m: int, stream=None):
     _check("sbl_linear_batch", lib.sbl_linear_batch(arr, len(items), fmt, n, m, _stream(stream)))
 
 
+def sbl_linear_acts_batch(x, xq, gamma, items, fmt: int, n: int, m: int, stream=None):
+    """x: [m_tok][k] fp32 input; xq, gamma: its quantized form (outputs);
+    items: sequence of dicts with keys packed, meta, beta, n_out, y[, acc]."""
+    lib = load()
+    m_tok, k = x.shape
+    arr = (LinearItem * len(items))()
+    for i, it in enumerate(items):
+        n_out = it["n_out"]
+        pb = lib.sbl_packed_bytes(n_out, k, n, m, fmt) if n_out > 0 else 0
+        arr[i] = LinearItem(
+            _ptr(it["packed"], torch.uint8, max(pb, 0), "packed"),
+            _ptr(it.get("meta"), torch.uint8, n_out * k // 8, "meta") if fmt == SBL_FMT_NM else None,
+            _ptr(it["beta"], torch.float32, 4, "beta"), None, None, m_tok, n_out, k,
+            _ptr(it["y"], torch.float32, m_tok * n_out * 4, "y"),
+            _ptr(it.get("acc"), torch.int32, m_tok * n_out * 4, "acc"))
+    st = lib.sbl_linear_acts_batch(_ptr(x, torch.float32, m_tok * k * 4, "x"), m_tok, k,
+                                   _ptr(xq, torch.int8, m_tok * k, "xq"),
+                                   _ptr(gamma, torch.float32, m_tok * 4, "gamma"), arr, len(items), fmt, n, m,
+                                   _stream(stream))
+    _check("sbl_linear_acts_batch", st)
+
+
 # ---------------------------------------------------------------- allocating conveniences
 
 def new_workspace(n_out: int, k: int, device="cuda"):
@@ -279,7 +304,7 @@ def quant_weights(w_bf16, n: int, m: int, fmt: int = SBL_FMT_DENSE2, want_codes:
     if pb < 0:
         raise ValueError("unsupported shape or pattern")
     out["packed"] = torch.empty(pb, dtype=torch.uint8, device=dev)
-    out["meta"] = out["mask"] if fmt == SBL_FMT_NM else None
+    out["meta"] = torch.empty((n_out, k // 8), dtype=torch.uint8, device=dev) if fmt == SBL_FMT_NM else None
     out["codes"] = torch.empty((n_out, k), dtype=torch.int8, device=dev) if want_codes else None
     ws = workspace if workspace is not None else new_workspace(n_out, k, dev)
     sbl_quant_weights(w_bf16, n, m, out["beta"], ws, mask_bits=out["mask"], codes=out["codes"],

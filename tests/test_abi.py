@@ -113,6 +113,7 @@ def test_quant_weights_validation(lib):
     assert call(n=0) == 4
     assert call(n=9) == 4
     assert call(fmt=3) == 4
+    assert call(fmt=1, meta=A + 16) == 2            # N:M metadata overlapping the mask output
     assert call(w=A + 2) == 3
     assert call(beta=A + 2) == 3
     assert call(packed=A + 8) == 3
@@ -138,7 +139,7 @@ def test_quant_weights_batch_validation(lib):
     ws = lib.sbl_workspace_bytes(4, 64)
 
     def item(**kw):
-        a = dict(w_bf16=A, n_out=4, k=64, beta=A, mask_bits=A, codes=None, packed=A, meta=A,
+        a = dict(w_bf16=A, n_out=4, k=64, beta=A, mask_bits=A, codes=None, packed=A, meta=A + (1 << 16),
                  workspace=A, workspace_bytes=ws)
         a.update(kw)
         return QuantItem(**a)
@@ -218,3 +219,36 @@ def test_linear_validation(lib):
     assert call([(6, A + 4)]) == 3
     assert call([(11, A + 2)]) == 3
     assert call([(12, A + 1)]) == 3
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation runs only on GPU-less hosts")
+def test_linear_acts_batch_validation(lib):
+    from sparse_linear_layers_absmean_amd.sbl import LinearItem
+    f = lib.sbl_linear_acts_batch
+
+    def item(**kw):
+        a = dict(packed=A, meta=A, beta=A, xq=None, gamma=None, m_tok=4, n_out=16, k=64, y=A, acc=None)
+        a.update(kw)
+        return LinearItem(**a)
+
+    def call(items, x=A, m_tok=4, k=64, xq=A, gamma=A, count=None, fmt=1, n=6, m=8):
+        arr = (LinearItem * len(items))(*items)
+        return f(x, m_tok, k, xq, gamma, arr, len(items) if count is None else count, fmt, n, m, None)
+
+    assert f(A, 4, 64, A, A, None, 1, 1, 6, 8, None) == 1
+    assert call([item()], count=0) == 2
+    assert call([item()], count=257) == 2
+    assert call([item()], k=96) == 2
+    assert call([item()], m_tok=-1) == 2
+    assert call([item(m_tok=3)]) == 2                 # items must share m_tok and k
+    assert call([item(), item(k=128)]) == 2
+    assert call([item()], x=None) == 1
+    assert call([item()], xq=None) == 1
+    assert call([item()], gamma=None) == 1
+    assert call([item()], x=A + 4) == 3
+    assert call([item()], xq=A + 8) == 3
+    assert call([item(), item(meta=None)]) == 1       # NM needs meta
+    assert call([item(), item(y=A + 2)]) == 3
+    assert call([item()], n=9) == 4
+    assert call([item()], fmt=2) == 4
+    assert call([item(m_tok=0)], m_tok=0, x=None, xq=None, gamma=None) == 0   # no tokens: no-op

@@ -1,0 +1,94 @@
+"""Activation quantization fused into the product (sbl_linear_acts_batch):
+the fused launch and the fallback (sbl_quant_acts, then sbl_linear_batch) must
+give bit-identical xq, gamma, acc and y, and both must match the oracle
+(int8 activations, gamma and int32 acc bit for bit; y within 1e-6 relative)."""
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import FMT_DENSE2, FMT_NM, check_y, say, to_dev, to_np
+from oracle import sbl_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+# (label, [(n_out, k)], m_tok, fmt, n, m); every item of a case shares k
+CASES = [
+    ("qkv 0.7B M=1", [(1536, 1536)] * 3, 1, FMT_NM, 6, 8),
+    ("gate/up 0.7B M=4", [(4096, 1536)] * 2, 4, FMT_DENSE2, 6, 8),
+    ("down 0.7B M=1", [(1536, 4096)], 1, FMT_NM, 2, 4),
+    ("o 3B M=2", [(3200, 3200)], 2, FMT_NM, 6, 8),
+    ("down 3B M=1", [(3200, 8640)], 1, FMT_NM, 6, 8),
+    ("ragged rows, partial panel, M=3", [(33, 320), (17, 320)], 3, FMT_DENSE2, 6, 8),
+    ("one tile, M=16", [(16, 64)], 16, FMT_NM, 6, 8),
+    ("wide input, M=16 (not fused)", [(64, 4096)], 16, FMT_NM, 6, 8),
+    ("nine items (not fused)", [(48, 256)] * 9, 2, FMT_NM, 2, 4),
+    ("empty item among others", [(40, 512), (0, 512), (24, 512)], 1, FMT_DENSE2, 6, 8),
+]
+
+
+def _prepare(rng, shapes, n, m, fmt):
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    items, host = [], []
+    for no, k in shapes:
+        if no == 0:
+            items.append(dict(packed=torch.empty(16, dtype=torch.uint8, device="cuda"),
+                              meta=torch.empty(16, dtype=torch.uint8, device="cuda"),
+                              beta=torch.ones(1, device="cuda"), n_out=0,
+                              y=torch.empty(16, device="cuda")))
+            host.append(None)
+            continue
+        bits = synth.gaussian_masters(rng, no, k)
+        o = sbl.quant_weights(to_dev(bits), n, m, fmt=fmt)
+        items.append(dict(packed=o["packed"], meta=o["meta"], beta=o["beta"], n_out=no))
+        host.append(bits)
+    return items, host
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fused_matches_separate_and_oracle(case):
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    label, shapes, m_tok, fmt, n, m = case
+    k = shapes[0][1]
+    rng = np.random.default_rng([71, len(label), m_tok, fmt, n])
+    say(f"fused acts: {label}")
+    items, host = _prepare(rng, shapes, n, m, fmt)
+    x = synth.gaussian_acts(rng, m_tok, k, hot_channels=4)
+    x[0, 5] = 0.0
+    if m_tok > 1:
+        x[1, :] = 0.0                                # all-zero token: gamma = 0, scale floor 1e-5
+    xd = to_dev(x.astype(np.float32))
+
+    def run(fused):
+        xq = torch.full((m_tok, k), 77, dtype=torch.int8, device="cuda")
+        gamma = torch.full((m_tok,), -1.0, device="cuda")
+        outs = [dict(it, y=torch.full((m_tok, max(it["n_out"], 1)), 3.0, device="cuda"),
+                     acc=torch.full((m_tok, max(it["n_out"], 1)), 7, dtype=torch.int32, device="cuda"))
+                for it in items]
+        if fused:
+            sbl.sbl_linear_acts_batch(xd, xq, gamma, outs, fmt, n, m)
+        else:
+            sbl.sbl_quant_acts(xd, xq, gamma)
+            sbl.sbl_linear_batch([dict(o, xq=xq, gamma=gamma) for o in outs], fmt, n, m)
+        torch.cuda.synchronize()
+        return to_np(xq), to_np(gamma), [(to_np(o["y"]), to_np(o["acc"])) for o in outs]
+
+    fq, fg, fres = run(True)
+    sq, sg, sres = run(False)
+    assert np.array_equal(fq, sq)
+    assert np.array_equal(fg.view(np.uint32), sg.view(np.uint32))
+    q_ref, g_ref = O.quant_acts(x)
+    assert np.array_equal(fq, q_ref)
+    assert np.array_equal(fg, g_ref)
+    for (fy, fa), (sy, sa), bits, (no, _) in zip(fres, sres, host, shapes):
+        assert np.array_equal(fa, sa)
+        assert np.array_equal(fy.view(np.uint32), sy.view(np.uint32))
+        if bits is None:
+            assert np.all(fa == 7) and np.all(fy == 3.0)   # an empty product writes nothing
+            continue
+        beta, keep, codes = O.quant_weights(bits, n, m)
+        acc_ref, y_ref = O.linear(codes, q_ref, beta, g_ref)
+        assert np.array_equal(fa, acc_ref)
+        check_y(fy, y_ref, acc_ref)
