@@ -3,10 +3,12 @@
 
 A step is one pass of the whole path over one batch of synthetic input: for
 each of the 7 matrices of a transformer block (q, k, v, o, gate, up, down)
-  sbl_quant_weights  exact absmean beta + N:M mask from the BF16 masters +
-                     ternary codes + packing (the per-training-step recompute)
-  sbl_quant_acts     per-token absmax int8 activations
-  sbl_linear         ternary x int8 product + fp32 rescale (GEMV at decode)
+  sbl_quant_weights      exact absmean beta + N:M mask from the BF16 masters +
+                         ternary codes + packing (the per-training-step recompute)
+  sbl_linear_acts_batch  per input of the block (q/k/v, o, gate/up, down): its
+                         per-token absmax int8 quantization and the ternary x
+                         int8 products + fp32 rescale that read it (one fused
+                         GEMV launch at decode sizes)
 Default workload: decode of a 0.7B-class block (hidden 1536, FFN 4096), one
 token, 6:8 N:M format.  Inputs are seeded synthetic data resident in HBM; the
 steps rotate over enough distinct copies (>= 512 MB) that the 256 MB
@@ -182,11 +184,17 @@ def main():
         for gi in range(len(groups)):
             sbl.sbl_quant_acts(xs[c][gi], acts[c][gi]["xq"], acts[c][gi]["gamma"])
 
+    def la_all(c, pool=None):
+        # per input: its quantization and the products that read it (one fused
+        # launch for decode-sized inputs, else sbl_quant_acts + sbl_linear_batch)
+        src = outs[c] if pool is None else pool
+        for gi in range(len(groups)):
+            sbl.sbl_linear_acts_batch(xs[c][gi], acts[c][gi]["xq"], acts[c][gi]["gamma"],
+                                      [src[i] for i in groups[gi]], fmt, n, m)
+
     def step(c):
         qw_all(c)
-        for gi in range(len(groups)):
-            sbl.sbl_quant_acts(xs[c][gi], acts[c][gi]["xq"], acts[c][gi]["gamma"])
-            sbl.sbl_linear_batch(items_of(c, gi), fmt, n, m)
+        la_all(c)
 
     # ---------------- algorithmic bytes
     def packed_b(no, k):
@@ -246,11 +254,13 @@ def main():
     qw_graphs = [capture(lambda c=c: qw_all(c)) for c in range(copies)]
     qa_graphs = [capture(lambda c=c: qa_all(c)) for c in range(copies)]
     lin_graphs = [capture(lambda c=c: lin_all(c)) for c in range(gemv_copies)]
+    la_graphs = [capture(lambda c=c: la_all(c % copies, gemv_pool[c % gemv_copies])) for c in range(gemv_copies)]
 
     reps = max(20, args.steps)
     qw_ms = time_graphs(qw_graphs, reps)
     qa_ms = time_graphs(qa_graphs, reps)
     lin_ms = time_graphs(lin_graphs, max(reps, 2 * gemv_copies))
+    la_ms = time_graphs(la_graphs, max(reps, 2 * gemv_copies))
 
     def roof(bytes_per, ms, kernel, launches, traffic=None):
         gbps = bytes_per / (ms * 1e-3) / 1e9
@@ -258,16 +268,20 @@ def main():
                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernel,
                 "launches_per_step": launches, "avg_launch_us": round(ms * 1e3 / launches, 3)}
 
+    # the step's two calls, then (for reference) the same work as separate calls
     per_call = {
         "sbl_quant_weights": roof(qw_bytes, qw_ms, "sbl_quant_weights_batch over the 7 matrices: "
                                   "absmean_partial + absmean_final + mask_pack kernels", 1,
                                   recorded_traffic("sbl_quant_weights", args.workload, args.fmt)),
-        "sbl_quant_acts": roof(qa_bytes, qa_ms, "quant_acts_kernel", len(groups)),
-        "sbl_linear": roof(lin_bytes, lin_ms, "gemv_kernel (grouped: qkv, o, gate+up, down)",
+        "sbl_linear_acts_batch": roof(qa_bytes + lin_bytes, la_ms,
+                                      "gemv_kernel with the activation quantization fused in "
+                                      "(grouped: qkv, o, gate+up, down)", len(groups)),
+        "sbl_quant_acts": roof(qa_bytes, qa_ms, "quant_acts_kernel (separate call)", len(groups)),
+        "sbl_linear": roof(lin_bytes, lin_ms, "gemv_kernel (separate call; grouped: qkv, o, gate+up, down)",
                            len(groups)),
     }
-    dominant = max(per_call, key=lambda kk: {"sbl_quant_weights": qw_ms, "sbl_quant_acts": qa_ms,
-                                              "sbl_linear": lin_ms}[kk])
+    dominant = max(["sbl_quant_weights", "sbl_linear_acts_batch"],
+                   key=lambda kk: {"sbl_quant_weights": qw_ms, "sbl_linear_acts_batch": la_ms}[kk])
     gemv_gbps = weight_bytes / (lin_ms * 1e-3) / 1e9
 
     # ---------------- GEMV weight bandwidth over the decode configurations
@@ -418,10 +432,10 @@ def bench_prefill(torch, np, synth, sbl, dev, tm):
                                        beta=items[i][0]["beta"], xq=items[i][1], gamma=items[i][2],
                                        n_out=items[i][4], y=items[i][3]) for i in grp], fmt, n, m)
 
-    for _ in range(2):
+    for _ in range(3):
         run()
     torch.cuda.synchronize()
-    reps = 5
+    reps = 20
     tm.start()
     for _ in range(reps):
         run()
