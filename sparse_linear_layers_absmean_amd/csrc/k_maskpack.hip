@@ -165,6 +165,39 @@ __device__ __forceinline__ void load_chunk(const u32x4* __restrict__ w, int64_t 
   }
 }
 
+// Split form of load_chunk for software pipelining: issue_chunk starts the
+// loads of the kThreads chunks from c0 (those below nchunks) into registers;
+// commit_chunk waits for the previous group's readers, stages them through
+// LDS and returns this thread's chunk.
+constexpr int kCPT = 2;   // chunk groups per workgroup of the fused mask/pack kernel
+
+__device__ __forceinline__ void issue_chunk(const u32x4* __restrict__ w, int64_t c0, int64_t nchunks, u32x4 (&r)[8]) {
+  const int64_t cnt = nchunks - c0 < kThreads ? (nchunks - c0 > 0 ? nchunks - c0 : 0) : kThreads;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int v16 = threadIdx.x + kThreads * i;
+    r[i] = v16 < cnt * 8 ? ld_stream16(&w[c0 * 8 + v16]) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+__device__ __forceinline__ void commit_chunk(int64_t c0, int64_t nchunks, const u32x4 (&r)[8], uint8_t* stage,
+                                             uint32_t (&dw)[32]) {
+  const int64_t cnt = nchunks - c0 < kThreads ? (nchunks - c0 > 0 ? nchunks - c0 : 0) : kThreads;
+  const int tid = threadIdx.x;
+  __syncthreads();                                         // the previous group's readers are done
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int v16 = tid + kThreads * i;
+    if (v16 < cnt * 8) *reinterpret_cast<u32x4*>(&stage[(v16 >> 3) * kPad + 16 * (v16 & 7)]) = r[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[tid * kPad + 16 * i]);
+    dw[4 * i] = v[0]; dw[4 * i + 1] = v[1]; dw[4 * i + 2] = v[2]; dw[4 * i + 3] = v[3];
+  }
+}
+
 // ---- packed 16-bit helpers: a 32-bit word holds weight 2i (low half) and 2i+1
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 constexpr uint32_t kOnes = 0x00010001u;
@@ -232,20 +265,8 @@ __device__ __forceinline__ uint32_t remove_field(uint32_t x, uint32_t pos) {
 
 // FMT: format computed for `packed` (0 DENSE2, 1 N:M); CODES: int8 codes wanted
 template <int M, int DROP, int FMT, bool CODES>
-__global__ __launch_bounds__(kThreads) void mask_pack_fast_kernel(const QBatch batch) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads * kPad];
+__device__ __forceinline__ void mask_pack_chunk(const uint32_t (&dw)[32], int64_t c, const QDesc& d, uint32_t t2) {
   constexpr int N = M - DROP, WPG = M / 2;
-  const int di = find_item(batch);
-  const QDesc& d = batch.d[di];
-  const int64_t nchunks = d.nvec / 8;
-  const int64_t c0 = ((int64_t)blockIdx.x - batch.start[di]) * kThreads;
-  const int64_t cnt = nchunks - c0 < kThreads ? nchunks - c0 : kThreads;
-  uint32_t dw[32];
-  load_chunk(d.w, c0, cnt, stage, dw);
-  const int64_t c = c0 + threadIdx.x;
-  if (c >= nchunks) return;
-  const float b = fmaxf(d.beta[0], 1e-5f);
-  const uint32_t t2 = (__float_as_uint(b * 0.5f) >> 16) * kOnes;   // |w| > beta_eff/2 <=> mag > t
   constexpr bool want_d2 = FMT == 0, want_nm = FMT == 1, want_codes = CODES;
   const uint32_t ones = opaque(kOnes);
   ChunkOut o = {};
@@ -315,6 +336,30 @@ __global__ __launch_bounds__(kThreads) void mask_pack_fast_kernel(const QBatch b
   o.nm_lo = (uint64_t)nmw[0] | ((uint64_t)nmw[1] << 32);
   o.nm_hi = (uint64_t)nmw[2] | ((uint64_t)nmw[3] << 32);
   store_outputs<N, M>(o, c, N, d.mask, d.codes, FMT, d.packed, d.meta, d.n_out, d.nkb);
+}
+
+// A workgroup takes kCPT consecutive groups of kThreads chunks; the loads of
+// the next group are in flight while the current one is computed.
+template <int M, int DROP, int FMT, bool CODES>
+__global__ __launch_bounds__(kThreads) void mask_pack_fast_kernel(const QBatch batch) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads * kPad];
+  const int di = find_item(batch);
+  const QDesc& d = batch.d[di];
+  const int64_t nchunks = d.nvec / 8;
+  const int64_t g0 = ((int64_t)blockIdx.x - batch.start[di]) * kThreads * kCPT;
+  u32x4 r[8];
+  issue_chunk(d.w, g0, nchunks, r);
+  const float b = fmaxf(d.beta[0], 1e-5f);
+  const uint32_t t2 = (__float_as_uint(b * 0.5f) >> 16) * kOnes;   // |w| > beta_eff/2 <=> mag > t
+#pragma unroll
+  for (int j = 0; j < kCPT; ++j) {
+    const int64_t cg = g0 + (int64_t)j * kThreads;
+    uint32_t dw[32];
+    commit_chunk(cg, nchunks, r, stage, dw);
+    if (j + 1 < kCPT) issue_chunk(d.w, cg + kThreads, nchunks, r);
+    const int64_t c = cg + threadIdx.x;
+    if (c < nchunks) mask_pack_chunk<M, DROP, FMT, CODES>(dw, c, d, t2);
+  }
 }
 
 template <int M, int DROP>
@@ -437,14 +482,16 @@ int64_t grid_for(int64_t nchunks) {
 }  // namespace
 
 hipError_t launch_mask_pack(QBatch& b, int n, int m, hipStream_t s) {
+  const int drop = m - n;
+  const bool fast = drop <= 2;
+  const int64_t per_block = fast ? (int64_t)kThreads * kCPT : kThreads;   // chunks per workgroup
   int64_t blocks = 0;
   for (int i = 0; i < b.count; ++i) {
     b.start[i] = blocks;
-    blocks += (b.d[i].nvec / 8 + kThreads - 1) / kThreads;
+    blocks += (b.d[i].nvec / 8 + per_block - 1) / per_block;
   }
   b.start[b.count] = blocks;
   const dim3 grid((unsigned)blocks), block(kThreads);
-  const int drop = m - n;
   if (m == 8 && drop == 0)
     launch_fast<8, 0>(b, grid, s);
   else if (m == 8 && drop == 1)
