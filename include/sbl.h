@@ -108,15 +108,16 @@ int64_t sbl_packed_bytes(int64_t n_out, int64_t k, int32_t n, int32_t m, int32_t
 int64_t sbl_meta_bytes(int64_t n_out, int64_t k, int32_t fmt);
 
 /* Bytes of device workspace sbl_quant_weights needs for an n_out x k matrix
- * (the exact beta reduction: 2 KB of per-exponent bins plus one 8-byte
- * partial sum per workgroup, rounded up to 4 KB; 12 KB or less up to 2^31
- * values).  Returns -1 for invalid arguments. */
+ * (the exact beta reduction: per workgroup of its first pass an 8-byte
+ * partial sum and a 48-byte exact sum of out-of-range magnitudes, rounded up
+ * to 4 KB; 56 KB or less up to 2^31 values, 224 KB at 2^34).  Returns -1 for
+ * invalid arguments. */
 int64_t sbl_workspace_bytes(int64_t n_out, int64_t k);
 
-/* Zero-fill a workspace of `workspace_bytes` bytes (a multiple of 8, at least
- * 2048), enqueued on `stream`.  A workspace must be zero-filled once before
- * its first use -- by this call or by allocating it zero-filled; every
- * sbl_quant_weights call leaves it ready for the next one. */
+/* Zero-fill a workspace of `workspace_bytes` bytes (a multiple of 8),
+ * enqueued on `stream`.  Optional: every sbl_quant_weights call writes the
+ * workspace words it reads, so a workspace carries no state from one call to
+ * the next and needs no initialization. */
 int sbl_workspace_init(void* workspace, int64_t workspace_bytes, sbl_stream stream);
 
 /* Weight preparation: beta, N:M mask, ternary codes, packing -- one pass of
@@ -133,12 +134,11 @@ int sbl_workspace_init(void* workspace, int64_t workspace_bytes, sbl_stream stre
  *   packed     packed codes output (sbl_packed_bytes), or NULL.
  *   meta       BITMAP metadata output, panel-major, for fmt == SBL_FMT_NM
  *              (required there when packed != NULL); ignored for DENSE2.
- *              Must not overlap mask_bits (SBL_ERR_SHAPE): the two hold the
- *              same bits in different orders.
+ *   The outputs mask_bits, codes, packed and (NM) meta must not share
+ *   any byte (SBL_ERR_SHAPE).
  *   workspace  device scratch of at least sbl_workspace_bytes(n_out, k)
- *              bytes, 16-byte aligned, zero-filled before its first use
- *              (see sbl_workspace_init) and left ready for the next call.
- *              Calls sharing one workspace must be ordered on one stream.
+ *              bytes, 16-byte aligned, any contents.  Calls sharing one
+ *              workspace must be ordered on one stream.
  */
 int sbl_quant_weights(const uint16_t* w_bf16, int64_t n_out, int64_t k, int32_t n, int32_t m,
                       float* beta, uint8_t* mask_bits, int8_t* codes,
@@ -160,7 +160,7 @@ typedef struct {
 } sbl_quant_item;
 
 /* Weight preparation of several matrices (e.g. the seven of one transformer
- * block) in three launches per 8 matrices instead of three per matrix.
+ * block) in two launches per 8 matrices instead of two per matrix.
  * `items` is a HOST array of `count` (1..256) descriptors sharing the pattern
  * n:m and `fmt`; each is validated as sbl_quant_weights validates its
  * arguments, and workspaces must not overlap (SBL_ERR_WORKSPACE), all before

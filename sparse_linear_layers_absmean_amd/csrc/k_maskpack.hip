@@ -30,7 +30,10 @@
 // DENSE2, 8 bytes of bitmap, 64*n/m/4 bytes of N:M codes and 64 code bytes;
 // the packed stream and the N:M metadata go to their panel-major places.
 // DENSE2 word layout: see d2_shift.
-#include "sbl_internal.h"
+// beta itself is finalized at the start of every workgroup from the absmean
+// pass's partial sums (sbl_beta.h), while the first chunk loads are in flight.
+#include "sbl_beta.h"
+#include "sbl_select.h"
 
 namespace sbl {
 
@@ -198,58 +201,7 @@ __device__ __forceinline__ void commit_chunk(int64_t c0, int64_t nchunks, const 
   }
 }
 
-// ---- packed 16-bit helpers: a 32-bit word holds weight 2i (low half) and 2i+1
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-constexpr uint32_t kOnes = 0x00010001u;
-
-__device__ __forceinline__ u16x2 h2(uint32_t x) { return __builtin_bit_cast(u16x2, x); }
-__device__ __forceinline__ uint32_t w32(u16x2 x) { return __builtin_bit_cast(uint32_t, x); }
-__device__ __forceinline__ uint32_t pmin(uint32_t a, uint32_t b) { return w32(__builtin_elementwise_min(h2(a), h2(b))); }
-__device__ __forceinline__ uint32_t pmax(uint32_t a, uint32_t b) { return w32(__builtin_elementwise_max(h2(a), h2(b))); }
-// per half: a > b ? a - b : 0
-__device__ __forceinline__ uint32_t psubsat(uint32_t a, uint32_t b) { return w32(__builtin_elementwise_sub_sat(h2(a), h2(b))); }
-__device__ __forceinline__ uint32_t swap16(uint32_t x) { return __builtin_amdgcn_alignbit(x, x, 16); }
-// A register the optimizer cannot see through: min(sub_sat(a, b), 1) with a
-// visible 1 is rewritten into per-half compares and selects (6 operations
-// per word instead of 2).
-__device__ __forceinline__ uint32_t opaque(uint32_t x) {
-  asm("" : "+v"(x));
-  return x;
-}
-
-// Both halves of the result = the DROP-th smallest magnitude of the group
-// (a multiset order statistic), from min/max networks on packed halves.
-template <int M, int DROP>
-__device__ __forceinline__ uint32_t drop_threshold(const uint32_t* A) {
-  uint32_t lo, hi;
-  if constexpr (M == 8) {
-    const uint32_t a = pmin(A[0], A[1]), b = pmax(A[0], A[1]);
-    const uint32_t c = pmin(A[2], A[3]), d = pmax(A[2], A[3]);
-    lo = pmin(a, c);                                   // per half: smallest of 4
-    hi = pmin(pmax(a, c), pmin(b, d));                 // per half: second smallest of 4
-  } else {
-    lo = pmin(A[0], A[1]);
-    hi = pmax(A[0], A[1]);
-  }
-  if constexpr (DROP == 1) return pmin(lo, swap16(lo));
-  return pmin(pmax(lo, swap16(lo)), pmin(hi, swap16(hi)));
-}
-
-// per-half 0/1 flags of the M/2 words of a group -> M-bit mask (bit j = weight j)
-template <int M>
-__device__ __forceinline__ uint32_t gather_bits(const uint32_t* F) {
-  uint32_t m = F[0];
-#pragma unroll
-  for (int i = 1; i < M / 2; ++i) m |= F[i] << (2 * i);
-  return (m | (m >> 15)) & ((1u << M) - 1u);
-}
-
-template <int M>
-__device__ __forceinline__ void scatter_bits(uint32_t keep, uint32_t* F) {
-  const uint32_t x = keep | (keep << 15);
-#pragma unroll
-  for (int i = 0; i < M / 2; ++i) F[i] = (x >> (2 * i)) & kOnes;
-}
+using namespace sel;
 
 // four 2-bit values in bytes 0..3 -> bits 0..7
 __device__ __forceinline__ uint32_t bytes_to_fields(uint32_t p) {
@@ -277,34 +229,7 @@ __device__ __forceinline__ void mask_pack_chunk(const uint32_t (&dw)[32], int64_
     uint32_t A[WPG], F[WPG];
 #pragma unroll
     for (int i = 0; i < WPG; ++i) A[i] = W[i] & 0x7FFF7FFFu;
-    uint32_t keep = (1u << M) - 1u;
-    if constexpr (DROP == 0) {
-#pragma unroll
-      for (int i = 0; i < WPG; ++i) F[i] = kOnes;
-    } else {
-      const uint32_t S = drop_threshold<M, DROP>(A);
-#pragma unroll
-      for (int i = 0; i < WPG; ++i) F[i] = pmin(psubsat(A[i], S), ones);    // mag > S
-      keep = gather_bits<M>(F);
-      if (__builtin_popcount(keep) != N) {
-        // magnitudes equal to S straddle the cut: keep them, then drop the
-        // highest-indexed ones until n remain (ties go to the lower index)
-        uint32_t E[WPG];
-#pragma unroll
-        for (int i = 0; i < WPG; ++i) E[i] = (F[i] | pmin(psubsat(S, A[i]), ones)) ^ kOnes;
-        uint32_t eq = gather_bits<M>(E);
-        keep |= eq;
-#pragma unroll
-        for (int t = 0; t < DROP; ++t) {
-          if (__builtin_popcount(keep) > N) {
-            const uint32_t top = 1u << (31 - __builtin_clz(eq));
-            keep &= ~top;
-            eq &= ~top;
-          }
-        }
-        scatter_bits<M>(keep, F);
-      }
-    }
+    const uint32_t keep = select_keep<M, DROP>(A, F, ones);
     o.keep |= (uint64_t)keep << (g * M);
     // per half: index = G + 2*sign, G = (kept and mag > t); u = c + 1 = {1, 2, 1, 0}[index]
     uint32_t X[WPG];
@@ -339,17 +264,23 @@ __device__ __forceinline__ void mask_pack_chunk(const uint32_t (&dw)[32], int64_
 }
 
 // A workgroup takes kCPT consecutive groups of kThreads chunks; the loads of
-// the next group are in flight while the current one is computed.
+// the next group are in flight while the current one is computed.  beta is
+// finalized at the start, while the first group's loads are in flight.
 template <int M, int DROP, int FMT, bool CODES>
 __global__ __launch_bounds__(kThreads) void mask_pack_fast_kernel(const QBatch batch) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads * kPad];
   const int di = find_item(batch);
   const QDesc& d = batch.d[di];
   const int64_t nchunks = d.nvec / 8;
-  const int64_t g0 = ((int64_t)blockIdx.x - batch.start[di]) * kThreads * kCPT;
+  const int64_t lwg = (int64_t)blockIdx.x - batch.start[di];
+  const int64_t g0 = lwg * kThreads * kCPT;
+  // beta's inputs are loaded first, so that it is computed while the chunk
+  // loads are in flight (loads complete in issue order)
+  beta::SlotLoads sl = {};
+  if (!batch.beta_ready) sl = beta::load_slots(d);
   u32x4 r[8];
   issue_chunk(d.w, g0, nchunks, r);
-  const float b = fmaxf(d.beta[0], 1e-5f);
+  const float b = fmaxf(batch.beta_ready ? d.beta[0] : beta::finish_beta(d, beta::sum_slots(sl), lwg == 0), 1e-5f);
   const uint32_t t2 = (__float_as_uint(b * 0.5f) >> 16) * kOnes;   // |w| > beta_eff/2 <=> mag > t
 #pragma unroll
   for (int j = 0; j < kCPT; ++j) {
@@ -362,21 +293,23 @@ __global__ __launch_bounds__(kThreads) void mask_pack_fast_kernel(const QBatch b
   }
 }
 
+template <int M, int DROP, int FMT, bool CODES>
+void launch_fast_kernel(const QBatch& b, hipStream_t s) {
+  hipLaunchKernelGGL((mask_pack_fast_kernel<M, DROP, FMT, CODES>), dim3((unsigned)b.start[b.count]),
+                     dim3(kThreads), 0, s, b);
+}
+
 template <int M, int DROP>
-void launch_fast(QBatch& b, dim3 grid, hipStream_t s) {
+void launch_fast(const QBatch& b, hipStream_t s) {
   bool codes = false, nm = false;
   for (int i = 0; i < b.count; ++i) {
     codes = codes || b.d[i].codes != nullptr;
     nm = nm || (b.d[i].packed != nullptr && b.d[i].fmt == 1);
   }
-  if (nm && codes)
-    hipLaunchKernelGGL((mask_pack_fast_kernel<M, DROP, 1, true>), grid, dim3(kThreads), 0, s, b);
-  else if (nm)
-    hipLaunchKernelGGL((mask_pack_fast_kernel<M, DROP, 1, false>), grid, dim3(kThreads), 0, s, b);
-  else if (codes)
-    hipLaunchKernelGGL((mask_pack_fast_kernel<M, DROP, 0, true>), grid, dim3(kThreads), 0, s, b);
-  else
-    hipLaunchKernelGGL((mask_pack_fast_kernel<M, DROP, 0, false>), grid, dim3(kThreads), 0, s, b);
+  if (nm && codes) launch_fast_kernel<M, DROP, 1, true>(b, s);
+  else if (nm) launch_fast_kernel<M, DROP, 1, false>(b, s);
+  else if (codes) launch_fast_kernel<M, DROP, 0, true>(b, s);
+  else launch_fast_kernel<M, DROP, 0, false>(b, s);
 }
 
 // Any n (one thread per chunk, one sort key per weight).
@@ -389,12 +322,13 @@ __global__ __launch_bounds__(kThreads) void mask_pack_kernel(const QBatch batch,
   const int64_t nchunks = d.nvec / 8;
   uint8_t* __restrict__ packed = d.packed;
   const int fmt = d.fmt;
-  const float b = fmaxf(d.beta[0], 1e-5f);
+  const int64_t lwg = (int64_t)blockIdx.x - batch.start[di];
+  const float b = fmaxf(batch.beta_ready ? d.beta[0] : beta::workgroup_beta(d, lwg == 0), 1e-5f);
   const int thr_mag = (int)(__float_as_uint(b * 0.5f) >> 16);
   const int thr_nz = (thr_mag << SH) | (M - 1);      // key > thr_nz  <=>  |w| > beta_eff/2
   const bool want_nm = packed && fmt == 1;
   {
-    const int64_t c0 = ((int64_t)blockIdx.x - batch.start[di]) * kThreads;
+    const int64_t c0 = lwg * kThreads;
     const int64_t cnt = nchunks - c0 < kThreads ? nchunks - c0 : kThreads;   // chunks in this block
     uint32_t dw[32];
     load_chunk(d.w, c0, cnt, stage, dw);
@@ -481,7 +415,7 @@ int64_t grid_for(int64_t nchunks) {
 
 }  // namespace
 
-hipError_t launch_mask_pack(QBatch& b, int n, int m, hipStream_t s) {
+hipError_t launch_mask_pack(QBatch& b, int n, int m, hipStream_t s, bool dry, int64_t* grid_out) {
   const int drop = m - n;
   const bool fast = drop <= 2;
   const int64_t per_block = fast ? (int64_t)kThreads * kCPT : kThreads;   // chunks per workgroup
@@ -491,23 +425,17 @@ hipError_t launch_mask_pack(QBatch& b, int n, int m, hipStream_t s) {
     blocks += (b.d[i].nvec / 8 + per_block - 1) / per_block;
   }
   b.start[b.count] = blocks;
+  if (grid_out) *grid_out = blocks;
+  if (dry) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(kThreads);
-  if (m == 8 && drop == 0)
-    launch_fast<8, 0>(b, grid, s);
-  else if (m == 8 && drop == 1)
-    launch_fast<8, 1>(b, grid, s);
-  else if (m == 8 && drop == 2)
-    launch_fast<8, 2>(b, grid, s);
-  else if (m == 4 && drop == 0)
-    launch_fast<4, 0>(b, grid, s);
-  else if (m == 4 && drop == 1)
-    launch_fast<4, 1>(b, grid, s);
-  else if (m == 4 && drop == 2)
-    launch_fast<4, 2>(b, grid, s);
-  else if (m == 8)
-    hipLaunchKernelGGL((mask_pack_kernel<8>), grid, block, 0, s, b, n);
-  else
-    hipLaunchKernelGGL((mask_pack_kernel<4>), grid, block, 0, s, b, n);
+  if (m == 8 && drop == 0) launch_fast<8, 0>(b, s);
+  else if (m == 8 && drop == 1) launch_fast<8, 1>(b, s);
+  else if (m == 8 && drop == 2) launch_fast<8, 2>(b, s);
+  else if (m == 4 && drop == 0) launch_fast<4, 0>(b, s);
+  else if (m == 4 && drop == 1) launch_fast<4, 1>(b, s);
+  else if (m == 4 && drop == 2) launch_fast<4, 2>(b, s);
+  else if (m == 8) hipLaunchKernelGGL((mask_pack_kernel<8>), grid, block, 0, s, b, n);
+  else hipLaunchKernelGGL((mask_pack_kernel<4>), grid, block, 0, s, b, n);
   return hipGetLastError();
 }
 

@@ -64,7 +64,7 @@ int64_t sbl_workspace_bytes(int64_t n_out, int64_t k) {
 
 int sbl_workspace_init(void* workspace, int64_t workspace_bytes, sbl_stream stream) {
   if (!workspace) return SBL_ERR_NULL;
-  if (workspace_bytes < 8 * sbl::kWsSlots || workspace_bytes % 8 != 0) return SBL_ERR_WORKSPACE;
+  if (workspace_bytes < 8 || workspace_bytes % 8 != 0) return SBL_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return SBL_ERR_ALIGN;
   return launch_status(sbl::launch_workspace_init(reinterpret_cast<uint64_t*>(workspace),
                                                   workspace_bytes / 8,
@@ -84,10 +84,19 @@ int check_quant(const sbl_quant_item& it, int32_t n, int32_t m, int32_t fmt) {
   if (!it.w_bf16 || !it.beta) return SBL_ERR_NULL;
   if (it.packed && fmt == SBL_FMT_NM && !it.meta) return SBL_ERR_NULL;
   if (it.n_out < 1 || !k_ok(it.k) || it.n_out * it.k > kMaxElems) return SBL_ERR_SHAPE;
-  // the row-major mask and the panel-major metadata are different byte orders
-  if (it.packed && fmt == SBL_FMT_NM &&
-      ranges_overlap(it.mask_bits, it.n_out * (it.k / 8), it.meta, it.n_out * (it.k / 8)))
-    return SBL_ERR_SHAPE;
+  // outputs must not share bytes (e.g. the row-major mask and the
+  // panel-major metadata hold the same bits in different orders)
+  if (nm_ok(n, m) && (fmt == SBL_FMT_DENSE2 || fmt == SBL_FMT_NM)) {
+    const int64_t mask_b = it.n_out * (it.k / 8);
+    const int64_t packed_b = fmt == SBL_FMT_DENSE2 ? it.n_out * (it.k / 4) : it.n_out * (it.k / m) * n / 4;
+    const void* meta = (it.packed && fmt == SBL_FMT_NM) ? it.meta : nullptr;
+    const void* packed = it.packed;
+    if (ranges_overlap(it.mask_bits, mask_b, meta, mask_b) || ranges_overlap(it.mask_bits, mask_b, packed, packed_b) ||
+        ranges_overlap(it.codes, it.n_out * it.k, packed, packed_b) ||
+        ranges_overlap(it.codes, it.n_out * it.k, it.mask_bits, mask_b) ||
+        ranges_overlap(it.codes, it.n_out * it.k, meta, mask_b) || ranges_overlap(packed, packed_b, meta, mask_b))
+      return SBL_ERR_SHAPE;
+  }
   if (!it.workspace || it.workspace_bytes < sbl::workspace_bytes_for(it.n_out * it.k))
     return SBL_ERR_WORKSPACE;
   if (!nm_ok(n, m)) return SBL_ERR_UNSUPPORTED;
@@ -119,17 +128,33 @@ sbl::QDesc to_qdesc(const sbl_quant_item& it, int32_t fmt) {
   return d;
 }
 
-// beta partial sums, beta, then mask/codes/pack: three launches per group of
-// up to kMaxQDesc matrices
+// Per group of up to kMaxQDesc matrices: the absmean pass, then the
+// mask/pack pass.  Up to about one round of mask/pack workgroups (three per
+// CU on 256 CUs) each finalizes beta itself, saving a launch; beyond that the
+// repeated finalization would sit on the critical path of every round, so the
+// finalize kernel runs once in between.  A call that wants only beta runs
+// just the finalize kernel.
+constexpr int64_t kPrologueMaxWorkgroups = 1024;
+
 int launch_quant(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m, int32_t fmt,
                  hipStream_t s) {
   for (int i0 = 0; i0 < count; i0 += sbl::kMaxQDesc) {
     sbl::QBatch b;
     b.count = count - i0 < sbl::kMaxQDesc ? count - i0 : sbl::kMaxQDesc;
-    for (int i = 0; i < b.count; ++i) b.d[i] = to_qdesc(items[i0 + i], fmt);
+    b.beta_ready = 0;
+    bool outputs = false;
+    for (int i = 0; i < b.count; ++i) {
+      b.d[i] = to_qdesc(items[i0 + i], fmt);
+      outputs = outputs || b.d[i].mask || b.d[i].codes || b.d[i].packed;
+    }
+    int64_t grid = 0;
+    bool wide = false;                              // a matrix with more than 1024 partial sums
+    for (int i = 0; i < b.count; ++i) wide = wide || b.d[i].nb > 4 * sbl::kAbsThreads;
+    (void)sbl::launch_mask_pack(b, n, m, s, true, &grid);
+    b.beta_ready = !outputs || wide || grid > kPrologueMaxWorkgroups;
     int st = launch_status(sbl::launch_absmean_partial(b, s));
-    if (st == SBL_OK) st = launch_status(sbl::launch_absmean_final(b, s));
-    if (st == SBL_OK) st = launch_status(sbl::launch_mask_pack(b, n, m, s));
+    if (st == SBL_OK && b.beta_ready) st = launch_status(sbl::launch_absmean_final(b, s));
+    if (st == SBL_OK && outputs) st = launch_status(sbl::launch_mask_pack(b, n, m, s));
     if (st != SBL_OK) return st;
   }
   return SBL_OK;

@@ -1,0 +1,238 @@
+// Final step of the exact absmean scale: beta = RN_fp32(S / (n_out*k)) from
+// the partial sums the absmean pass left in the workspace (layout in
+// sbl_internal.h).  Every workgroup that needs beta computes it itself at its
+// start (the sums are a few KB, read from L2), so no separate launch sits
+// between the two passes.
+//  * No slot flagged (the normal case): the fast-window sums alone, added in
+//    registers and rounded once.
+//  * Otherwise the flagged slots' exact out-of-window sums join them: each
+//    thread adds its slots' 32-bit limbs column by column (a column sum stays
+//    below 2^44), the columns are reduced across the workgroup, and one thread
+//    carries them into a multi-word integer (units of 2^-133).
+// No atomics and nothing written to the workspace.
+#pragma once
+
+#include "sbl_internal.h"
+
+namespace sbl {
+namespace beta {
+
+constexpr uint64_t kRareFlag = 1ull << 63;
+
+// limbs: little-endian 32-bit words of a nonnegative integer (units of
+// 2^-133); arrays hold kLimbs + 2 words, since add_shifted touches the two
+// words above the one it starts in (the sum itself stays below 2^384)
+constexpr int kLimbs = 12;
+
+__device__ inline void add_shifted(uint32_t* L, uint64_t v, int s) {
+  if (v == 0) return;
+  const int li = s >> 5, sh = s & 31;
+  const uint64_t lo = v << sh;
+  const uint32_t hi = sh ? (uint32_t)(v >> (64 - sh)) : 0u;
+  uint64_t t = (uint64_t)L[li] + (uint32_t)lo;
+  L[li] = (uint32_t)t;
+  t = (uint64_t)L[li + 1] + (uint32_t)(lo >> 32) + (t >> 32);
+  L[li + 1] = (uint32_t)t;
+  t = (uint64_t)L[li + 2] + hi + (t >> 32);
+  L[li + 2] = (uint32_t)t;
+  for (int i = li + 3; i < kLimbs && (t >> 32); ++i) {
+    t = (uint64_t)L[i] + (t >> 32);
+    L[i] = (uint32_t)t;
+  }
+}
+
+// RN_fp32(D / n) for a dividend D = W * 2^e + r, 0 <= r < 2^e, with bit 63 of
+// W set, r != 0 exactly when `sticky`, and 64 <= n <= 2^34.  floor(D / (n*2^e))
+// = floor(W / n) = Q (since R + r/2^e < n), and Q >= 2^29 holds more than the
+// 24 bits + guard that rounding needs; whatever is below is only a sticky
+// flag.  Nearest, ties to even, subnormal results included.
+__device__ inline float round_div(uint64_t W, int e, bool sticky, uint64_t n) {
+  const uint64_t Q = W / n, R = W - Q * n;
+  sticky = sticky || R != 0;
+  const int qb = 64 - __clzll((long long)Q);        // 30 <= qb <= 58
+  int lsb = qb - 24;                                // fp32 unit inside Q for a normal result
+  if (e + lsb < -149) lsb = -149 - e;               // subnormal: the unit is 2^-149
+  if (lsb > qb) return 0.0f;                        // below half the smallest subnormal
+  const uint64_t mant = Q >> lsb;
+  const uint64_t guard = (Q >> (lsb - 1)) & 1u;
+  sticky = sticky || (Q & ((1ull << (lsb - 1)) - 1u)) != 0;
+  const uint64_t m = mant + ((guard && (sticky || (mant & 1u))) ? 1u : 0u);
+  return ldexpf((float)m, e + lsb);
+}
+
+// exact RN_fp32(S * 2^-133 / n) for the integer S held in limbs
+__device__ inline float round_quotient(const uint32_t* L, uint64_t n) {
+  int top = -1;
+  for (int i = kLimbs - 1; i >= 0 && top < 0; --i)
+    if (L[i]) top = i * 32 + 31 - __clz(L[i]);
+  if (top < 0) return 0.0f;
+  // 64-bit window of S whose bit 63 is S's bit `top`; lower bits: sticky
+  const int lo = top - 63;
+  uint64_t win;
+  bool below = false;
+  if (lo >= 0) {
+    const int li = lo >> 5, sh = lo & 31;
+    const uint64_t a = (uint64_t)L[li] | ((uint64_t)L[li + 1] << 32);
+    const uint64_t c = (li + 2 < kLimbs) ? L[li + 2] : 0u;
+    win = (a >> sh) | (sh ? (c << (64 - sh)) : 0u);
+    for (int i = 0; i < li && !below; ++i) below = L[i] != 0;
+    below = below || (L[li] & ((1u << sh) - 1u)) != 0;
+  } else {
+    win = ((uint64_t)L[0] | ((uint64_t)L[1] << 32)) << (-lo);
+  }
+  return round_div(win, lo - 133, below, n);
+}
+
+// The same for S = V * 2^95 (fast-window sums only), V = hi * 2^32 + lo with
+// lo, hi < 2^62: registers only.
+__device__ inline float round_quotient_fast(uint64_t lo, uint64_t hi, uint64_t n) {
+  const uint64_t vlo = lo + (hi << 32);
+  const uint64_t vhi = (hi >> 32) + (vlo < lo ? 1u : 0u);
+  if (vlo == 0 && vhi == 0) return 0.0f;
+  const int top = vhi ? 127 - __clzll((long long)vhi) : 63 - __clzll((long long)vlo);
+  if (top <= 63) return round_div(vlo << (63 - top), top - 63 - 38, false, n);
+  const int s = top - 63;                           // 1 .. 63
+  const uint64_t W = (vlo >> s) | (vhi << (64 - s));
+  return round_div(W, s - 38, (vlo << (64 - s)) != 0, n);
+}
+
+// The first pass's partial sums as one thread loads them: slots tid + u*256
+// (u < 4) of a matrix with nb <= 1024.
+struct SlotLoads {
+  uint64_t v[4];
+};
+
+__device__ __forceinline__ SlotLoads load_slots(const QDesc& d) {
+  SlotLoads sl;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = threadIdx.x + u * kAbsThreads;
+    sl.v[u] = i < d.nb ? d.ws[i] : 0ull;
+  }
+  return sl;
+}
+
+// One thread's share of the slots: fast-window sums split in 32-bit halves
+// (nothing overflows for nb <= 4096) and flags, bit b = slot tid + b*kThreads
+// flagged.
+struct SlotSums {
+  unsigned long long lo = 0, hi = 0;
+  uint32_t flags = 0;
+  __device__ __forceinline__ void add(uint64_t v, int b) {
+    flags |= (uint32_t)(v >> 63) << b;
+    lo += (uint32_t)v;
+    hi += (v & ~kRareFlag) >> 32;
+  }
+};
+
+// beta of matrix d (unclamped) from every thread's SlotSums, returned to every
+// thread of the workgroup.  All kThreads threads must call it (it
+// synchronizes the workgroup); `store` makes this workgroup write d.beta.
+__device__ inline float finish_beta(const QDesc& d, SlotSums ss, bool store) {
+  constexpr int kCols = 2 * kWsLimbWords;
+  static_assert(kCols == kLimbs, "one column per limb");
+  __shared__ unsigned long long part[2][kAbsThreads / 64];
+  __shared__ uint32_t rare_w[kAbsThreads / 64];
+  __shared__ unsigned long long cols[kAbsThreads / 64][kCols];
+  __shared__ uint32_t limbs[kLimbs + 2];
+  __shared__ float beta_s;
+  const int tid = threadIdx.x, wave = tid >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    ss.lo += __shfl_xor(ss.lo, off, 64);
+    ss.hi += __shfl_xor(ss.hi, off, 64);
+  }
+  const bool any_rare = __ballot(ss.flags != 0) != 0;
+  if ((tid & 63) == 0) {
+    part[0][wave] = ss.lo;
+    part[1][wave] = ss.hi;
+    rare_w[wave] = any_rare ? 1u : 0u;
+  }
+  __syncthreads();
+  unsigned long long lo = 0, hi = 0;
+  uint32_t flagged = 0;
+#pragma unroll
+  for (int i = 0; i < kAbsThreads / 64; ++i) {
+    lo += part[0][i];
+    hi += part[1][i];
+    flagged |= rare_w[i];
+  }
+  const uint64_t n = (uint64_t)d.nvec * 8u;
+  if (!flagged) {                                   // uniform across the workgroup
+    if (tid == 0) {
+      const float b = round_quotient_fast(lo, hi, n);
+      beta_s = b;
+      if (store) d.beta[0] = b;
+    }
+    __syncthreads();
+    return beta_s;
+  }
+  // rare path: column sums of the flagged slots' limbs
+  unsigned long long c[kCols];
+#pragma unroll
+  for (int j = 0; j < kCols; ++j) c[j] = 0;
+  const uint64_t* recs = d.ws + ws_limb_base(d.nb);
+  for (uint32_t f = ss.flags; f; f &= f - 1) {
+    const int64_t i = tid + (int64_t)(__ffs(f) - 1) * kAbsThreads;
+    uint64_t w[kWsLimbWords];
+#pragma unroll
+    for (int j = 0; j < kWsLimbWords; ++j) w[j] = recs[kWsLimbWords * i + j];
+#pragma unroll
+    for (int j = 0; j < kWsLimbWords; ++j) {
+      c[2 * j] += (uint32_t)w[j];
+      c[2 * j + 1] += w[j] >> 32;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kCols; ++j) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) c[j] += __shfl_xor(c[j], off, 64);
+  }
+  if ((tid & 63) == 0) {
+#pragma unroll
+    for (int j = 0; j < kCols; ++j) cols[wave][j] = c[j];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int i = 0; i < kLimbs + 2; ++i) limbs[i] = 0;
+    for (int j = 0; j < kCols; ++j) {
+      unsigned long long t = 0;
+      for (int wv = 0; wv < kAbsThreads / 64; ++wv) t += cols[wv][j];
+      add_shifted(limbs, t, 32 * j);
+    }
+    add_shifted(limbs, lo, 95);        // 2^-38 = 2^95 * 2^-133
+    add_shifted(limbs, hi, 95 + 32);
+    const float bt = round_quotient(limbs, n);
+    beta_s = bt;
+    if (store) d.beta[0] = bt;
+  }
+  __syncthreads();
+  return beta_s;
+}
+
+// Slot sums of preloaded slot values (nb <= 1024).
+__device__ __forceinline__ SlotSums sum_slots(const SlotLoads& sl) {
+  SlotSums ss;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) ss.add(sl.v[u], u);
+  return ss;
+}
+
+// beta of matrix d for any nb <= 4096 (loads included); all threads must call it.
+__device__ inline float workgroup_beta(const QDesc& d, bool store) {
+  SlotSums ss;
+  for (int64_t i0 = 0, r = 0; i0 < d.nb; i0 += 4 * kAbsThreads, ++r) {
+    uint64_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + threadIdx.x + u * kAbsThreads;
+      v[u] = i < d.nb ? d.ws[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ss.add(v[u], (int)(4 * r) + u);
+  }
+  return finish_beta(d, ss, store);
+}
+
+}  // namespace beta
+}  // namespace sbl

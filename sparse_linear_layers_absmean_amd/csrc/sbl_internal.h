@@ -20,30 +20,35 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// Workspace of the exact beta reduction of one matrix, in 64-bit words.
-//   [0, 256)       per-exponent sums of BF16 significands (values outside the
-//                  fast window), exact integers; accumulated with atomics by
-//                  the partial-sum kernel, read and zero-filled again by the
-//                  finalize kernel (so it must be zero before the first use)
-//   [256, 256+nb)  one fast-window partial sum per workgroup of the partial-sum
-//                  kernel (units of 2^-38), overwritten by every call
-constexpr int kWsBins = 0;
-constexpr int kWsSlots = 256;
+// Workspace of the exact beta reduction of one matrix, in 64-bit words
+// (written by the absmean pass of every call, read after it; no state is
+// carried from one call to the next):
+//   [0, nb)           fast-window partial sum of absmean workgroup i (units of
+//                     2^-38); bit 63 set when the workgroup also met values
+//                     outside the window
+//   [lb + 6i, +6)     lb = nb rounded up to 8: for a flagged workgroup i, the
+//                     exact sum of its out-of-window magnitudes as 12
+//                     little-endian 32-bit limbs (units of 2^-133); not
+//                     written for other workgroups
+__host__ __device__ __forceinline__ int64_t ws_limb_base(int64_t nb) { return (nb + 7) / 8 * 8; }
+constexpr int kWsLimbWords = 6;
 
 // Partition of the absmean pass over a matrix of `total` BF16 values: nb
 // workgroups of kAbsThreads threads, vpt 16-byte vectors per thread.  A thread
 // adds at most 2^14 fast-window values (vpt <= 2048), which keeps its fp64
 // partial sums exact.
 constexpr int kAbsThreads = 256;
+constexpr int kAbsMinVpt = 8;      // one batch of 8 loads per thread at least
+constexpr int kAbsMaxSlots = 1024; // partial sums per matrix while vpt <= 2048
 struct AbsmeanPlan {
   int64_t nb, vpt;
 };
 inline AbsmeanPlan absmean_plan(int64_t total) {
   const int64_t nvec = total / 8;
-  const int64_t per_wg = (int64_t)kAbsThreads * 8;
-  AbsmeanPlan p{(nvec + per_wg - 1) / per_wg, 8};
-  if (p.nb > 1024) {          // big matrices: longer threads, at most 1024 slots (4096 at 2^34)
-    p.vpt = (nvec + 1024 * kAbsThreads - 1) / (1024 * kAbsThreads);
+  const int64_t per_wg = (int64_t)kAbsThreads * kAbsMinVpt;
+  AbsmeanPlan p{(nvec + per_wg - 1) / per_wg, kAbsMinVpt};
+  if (p.nb > kAbsMaxSlots) {  // big matrices: longer threads, at most 1024 slots (4096 at 2^34)
+    p.vpt = (nvec + kAbsMaxSlots * kAbsThreads - 1) / (kAbsMaxSlots * kAbsThreads);
     p.vpt = (p.vpt + 7) / 8 * 8;                        // whole batches of 8 loads
     if (p.vpt > 2048) p.vpt = 2048;
     p.nb = (nvec + kAbsThreads * p.vpt - 1) / (kAbsThreads * p.vpt);
@@ -52,7 +57,8 @@ inline AbsmeanPlan absmean_plan(int64_t total) {
   return p;
 }
 inline int64_t workspace_bytes_for(int64_t total) {
-  const int64_t bytes = 8 * (kWsSlots + absmean_plan(total).nb);
+  const int64_t nb = absmean_plan(total).nb;
+  const int64_t bytes = 8 * (ws_limb_base(nb) + kWsLimbWords * nb);
   return (bytes + 4095) / 4096 * 4096;
 }
 
@@ -92,13 +98,19 @@ struct QBatch {
   QDesc d[kMaxQDesc];
   int64_t start[kMaxQDesc + 1];   // first workgroup of each item in the current launch
   int32_t count;
+  int32_t beta_ready;             // mask/pack: beta already in d.beta (else finalized per workgroup)
 };
 
-// The three launches of weight preparation, in stream order.  Each fills
-// batch.start for its own grid.
+// Weight preparation in stream order: the absmean pass (partial sums), then
+// the mask/pack pass.  A mask/pack launch of about one round of workgroups
+// finalizes beta at the start of each workgroup; a larger one (and a call
+// that wants only beta) is preceded by the one-workgroup-per-matrix finalize
+// kernel, and reads beta (batch.beta_ready).  Each fills batch.start for its
+// own grid; launch_mask_pack returns its workgroup count in *grid when
+// `dry` (nothing launched).
 hipError_t launch_absmean_partial(QBatch& batch, hipStream_t s);
 hipError_t launch_absmean_final(QBatch& batch, hipStream_t s);
-hipError_t launch_mask_pack(QBatch& batch, int n, int m, hipStream_t s);
+hipError_t launch_mask_pack(QBatch& batch, int n, int m, hipStream_t s, bool dry = false, int64_t* grid = nullptr);
 
 hipError_t launch_workspace_init(uint64_t* ws, int64_t words, hipStream_t s);
 

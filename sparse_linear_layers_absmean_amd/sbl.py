@@ -286,7 +286,7 @@ def sbl_linear_acts_batch(x, xq, gamma, items, fmt: int, n: int, m: int, stream=
 # ---------------------------------------------------------------- allocating conveniences
 
 def new_workspace(n_out: int, k: int, device="cuda"):
-    """A zero-filled workspace for n_out x k matrices (reusable, call after call)."""
+    """A workspace for n_out x k matrices (reusable, call after call; any contents)."""
     nbytes = sbl_workspace_bytes(n_out, k)
     if nbytes < 0:
         raise ValueError("unsupported shape")

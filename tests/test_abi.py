@@ -64,7 +64,7 @@ def test_packed_and_meta_bytes(lib, n_out, k):
     assert lib.sbl_meta_bytes(n_out, k, 0) == 0
     assert lib.sbl_meta_bytes(n_out, k, 1) == n_out * k // 8
     ws = lib.sbl_workspace_bytes(n_out, k)
-    assert ws % 4096 == 0 and 2048 + 8 <= ws <= 12288
+    assert ws % 4096 == 0 and 4096 <= ws <= 57344
 
 
 def test_packed_bytes_closed_form_bits_per_weight(lib):
@@ -91,7 +91,8 @@ S = ctypes.c_void_p
 def test_quant_weights_validation(lib):
     f = lib.sbl_quant_weights
     ws = lib.sbl_workspace_bytes(4, 64)
-    ok = dict(w=A, n_out=4, k=64, n=6, m=8, beta=A, mask=A, codes=A, fmt=0, packed=A, meta=A,
+    MK, CD, PK, MT = A + (1 << 16), A + (2 << 16), A + (3 << 16), A + (4 << 16)   # disjoint outputs
+    ok = dict(w=A, n_out=4, k=64, n=6, m=8, beta=A, mask=MK, codes=CD, fmt=0, packed=PK, meta=MT,
               ws=A, wsb=ws, s=None)
 
     def call(**kw):
@@ -113,21 +114,26 @@ def test_quant_weights_validation(lib):
     assert call(n=0) == 4
     assert call(n=9) == 4
     assert call(fmt=3) == 4
-    assert call(fmt=1, meta=A + 16) == 2            # N:M metadata overlapping the mask output
+    assert call(fmt=1, meta=MK + 16) == 2           # N:M metadata overlapping the mask output
+    assert call(packed=MK + 16) == 2                # DENSE2 slots overlapping the mask
+    assert call(codes=PK - 64) == 2                 # codes running into the packed stream
+    assert call(fmt=1, meta=PK + 16) == 2           # metadata inside the N:M codes
     assert call(w=A + 2) == 3
     assert call(beta=A + 2) == 3
-    assert call(packed=A + 8) == 3
-    assert call(mask=A + 1) == 3
-    assert call(codes=A + 4) == 3
+    assert call(packed=PK + 8) == 3
+    assert call(mask=MK + 1) == 3
+    assert call(codes=CD + 4) == 3
     assert call(ws=A + 8) == 3
 
 
 def test_workspace_bytes_cover_one_slot_per_workgroup(lib):
-    # 2 KB of bins + 8 B per absmean workgroup (256 threads x 8 vectors of 8 values
-    # each up to 1024 workgroups, then longer threads; 4096 slots at 2^34 values)
+    # per absmean workgroup (256 threads x 8 vectors of 8 values each, up to 1024
+    # workgroups, then longer threads; 4096 at 2^34 values): an 8-byte sum and a
+    # 48-byte record, the sums padded to 64 bytes, the whole rounded up to 4 KB
     assert lib.sbl_workspace_bytes(1, 64) == 4096
-    assert lib.sbl_workspace_bytes(16384, 131072) == 12288      # 2^31 values: 1024 slots
-    assert lib.sbl_workspace_bytes(131072, 131072) == 36864     # 2^34 values: 4096 slots
+    assert lib.sbl_workspace_bytes(256, 4096) == 4096              # 64 slots: 512 + 3072 bytes
+    assert lib.sbl_workspace_bytes(16384, 131072) == 57344        # 2^31 values: 1024 slots
+    assert lib.sbl_workspace_bytes(131072, 131072) == 229376      # 2^34 values: 4096 slots
     assert lib.sbl_workspace_bytes(0, 64) == -1
     assert lib.sbl_workspace_bytes(4, 96) == -1
 
@@ -139,7 +145,7 @@ def test_quant_weights_batch_validation(lib):
     ws = lib.sbl_workspace_bytes(4, 64)
 
     def item(**kw):
-        a = dict(w_bf16=A, n_out=4, k=64, beta=A, mask_bits=A, codes=None, packed=A, meta=A + (1 << 16),
+        a = dict(w_bf16=A, n_out=4, k=64, beta=A, mask_bits=A, codes=None, packed=A + (2 << 16), meta=A + (1 << 16),
                  workspace=A, workspace_bytes=ws)
         a.update(kw)
         return QuantItem(**a)

@@ -230,7 +230,7 @@ def _rare_mixture(rng, n_out, k):
 def test_quant_weights_batch_matches_oracle(fmt, n, m):
     """Grouped weight preparation (10 matrices: two launch groups) gives the
     oracle's beta, mask, codes and packed bytes; a second call on the same
-    workspaces (bins left zero by the first) gives the same bits."""
+    workspaces gives the same bits."""
     import torch
     from sparse_linear_layers_absmean_amd import sbl
     rng = np.random.default_rng([31, fmt, n, m])
