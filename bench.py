@@ -271,7 +271,7 @@ def main():
     # the step's two calls, then (for reference) the same work as separate calls
     per_call = {
         "sbl_quant_weights": roof(qw_bytes, qw_ms, "sbl_quant_weights_batch over the 7 matrices: "
-                                  "absmean_partial + absmean_final + mask_pack kernels", 1,
+                                  "absmean_partial + mask_pack kernels (beta finalized inside mask_pack)", 1,
                                   recorded_traffic("sbl_quant_weights", args.workload, args.fmt)),
         "sbl_linear_acts_batch": roof(qa_bytes + lin_bytes, la_ms,
                                       "gemv_kernel with the activation quantization fused in "

@@ -84,6 +84,10 @@ __device__ __forceinline__ void consume(const u32x4& v, double& acc0, double& ac
 // multiple of 8); thread t reads vectors t, t+256, ... of that range, so each
 // load instruction of a wave reads 1 KB contiguous; 8 or 16 loads in flight.
 // Buffer loads past the matrix's end return zeros (which add nothing).
+// NT: nontemporal loads, for groups of matrices too large for the 256 MB
+// Infinity Cache to hold until the mask/pack pass reads them again (13B
+// block: 251 µs per call instead of 273 µs; 0.7B block: 39.4 instead of 38.4).
+template <bool NT>
 __global__ __launch_bounds__(kAbsThreads) void absmean_partial_kernel(const QBatch batch) {
   const int di = find_item(batch);
   const QDesc& d = batch.d[di];
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(kAbsThreads) void absmean_partial_kernel(const QBat
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rw, voff + (j + u) * kAbsThreads * 16, 0, 0));
+                                           rw, voff + (j + u) * kAbsThreads * 16, 0, NT ? 2 : 0));
   };
   auto process8 = [&](const u32x4 (&v)[8]) {
 #pragma unroll
@@ -175,6 +179,8 @@ __global__ void zero_ws_kernel(uint64_t* ws, int64_t words) {
   for (int64_t i = threadIdx.x; i < words; i += blockDim.x) ws[i] = 0;
 }
 
+constexpr int64_t kAbsStreamBytes = int64_t(128) << 20;   // masters per launch above which loads are nontemporal
+
 }  // namespace
 
 hipError_t launch_workspace_init(uint64_t* ws, int64_t words, hipStream_t s) {
@@ -189,7 +195,12 @@ hipError_t launch_absmean_partial(QBatch& b, hipStream_t s) {
     blocks += b.d[i].nb;
   }
   b.start[b.count] = blocks;
-  hipLaunchKernelGGL(absmean_partial_kernel, dim3((unsigned)blocks), dim3(kAbsThreads), 0, s, b);
+  int64_t bytes = 0;
+  for (int i = 0; i < b.count; ++i) bytes += b.d[i].nvec * 16;
+  if (bytes > kAbsStreamBytes)
+    hipLaunchKernelGGL(absmean_partial_kernel<true>, dim3((unsigned)blocks), dim3(kAbsThreads), 0, s, b);
+  else
+    hipLaunchKernelGGL(absmean_partial_kernel<false>, dim3((unsigned)blocks), dim3(kAbsThreads), 0, s, b);
   return hipGetLastError();
 }
 

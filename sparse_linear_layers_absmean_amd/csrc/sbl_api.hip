@@ -135,6 +135,7 @@ sbl::QDesc to_qdesc(const sbl_quant_item& it, int32_t fmt) {
 // finalize kernel runs once in between.  A call that wants only beta runs
 // just the finalize kernel.
 constexpr int64_t kPrologueMaxWorkgroups = 1024;
+constexpr int64_t kPrologueMaxSlots = 512;       // every wave loads all partial sums (beta::kWaveSlots)
 
 int launch_quant(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m, int32_t fmt,
                  hipStream_t s) {
@@ -148,8 +149,8 @@ int launch_quant(const sbl_quant_item* items, int32_t count, int32_t n, int32_t 
       outputs = outputs || b.d[i].mask || b.d[i].codes || b.d[i].packed;
     }
     int64_t grid = 0;
-    bool wide = false;                              // a matrix with more than 1024 partial sums
-    for (int i = 0; i < b.count; ++i) wide = wide || b.d[i].nb > 4 * sbl::kAbsThreads;
+    bool wide = false;                              // a matrix with more than 512 partial sums
+    for (int i = 0; i < b.count; ++i) wide = wide || b.d[i].nb > kPrologueMaxSlots;
     (void)sbl::launch_mask_pack(b, n, m, s, true, &grid);
     b.beta_ready = !outputs || wide || grid > kPrologueMaxWorkgroups;
     int st = launch_status(sbl::launch_absmean_partial(b, s));

@@ -2,13 +2,13 @@
 // the partial sums the absmean pass left in the workspace (layout in
 // sbl_internal.h).  Every workgroup that needs beta computes it itself at its
 // start (the sums are a few KB, read from L2), so no separate launch sits
-// between the two passes.
+// between the two passes; in the normal case each wave does it alone.
 //  * No slot flagged (the normal case): the fast-window sums alone, added in
 //    registers and rounded once.
-//  * Otherwise the flagged slots' exact out-of-window sums join them: each
-//    thread adds its slots' 32-bit limbs column by column (a column sum stays
-//    below 2^44), the columns are reduced across the workgroup, and one thread
-//    carries them into a multi-word integer (units of 2^-133).
+//  * Otherwise the flagged slots' exact out-of-window sums join them: their
+//    32-bit limbs are added column by column in LDS (a column sum stays below
+//    2^44), and one thread carries the columns into a multi-word integer
+//    (units of 2^-133).
 // No atomics and nothing written to the workspace.
 #pragma once
 
@@ -96,113 +96,57 @@ __device__ inline float round_quotient_fast(uint64_t lo, uint64_t hi, uint64_t n
   return round_div(W, s - 38, (vlo << (64 - s)) != 0, n);
 }
 
-// The first pass's partial sums as one thread loads them: slots tid + u*256
-// (u < 4) of a matrix with nb <= 1024.
+// Per-wave finalize (no barrier, no LDS): every wave of a workgroup loads all
+// nb <= kWaveSlots partial sums itself, lane l taking slots l + 64u (u < 8),
+// so the loads can be issued ahead of LDS-direct loads and beta computed while
+// those are in flight (a workgroup barrier would first wait for them).
+constexpr int kWaveSlots = 512;
 struct SlotLoads {
-  uint64_t v[4];
+  uint64_t v[kWaveSlots / 64];
 };
 
 __device__ __forceinline__ SlotLoads load_slots(const QDesc& d) {
   SlotLoads sl;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t i = threadIdx.x + u * kAbsThreads;
+  for (int u = 0; u < kWaveSlots / 64; ++u) {
+    const int64_t i = lane + 64 * u;
     sl.v[u] = i < d.nb ? d.ws[i] : 0ull;
   }
   return sl;
 }
 
-// One thread's share of the slots: fast-window sums split in 32-bit halves
-// (nothing overflows for nb <= 4096) and flags, bit b = slot tid + b*kThreads
-// flagged.
-struct SlotSums {
-  unsigned long long lo = 0, hi = 0;
-  uint32_t flags = 0;
-  __device__ __forceinline__ void add(uint64_t v, int b) {
-    flags |= (uint32_t)(v >> 63) << b;
-    lo += (uint32_t)v;
-    hi += (v & ~kRareFlag) >> 32;
-  }
-};
-
-// beta of matrix d (unclamped) from every thread's SlotSums, returned to every
-// thread of the workgroup.  All kThreads threads must call it (it
-// synchronizes the workgroup); `store` makes this workgroup write d.beta.
-__device__ inline float finish_beta(const QDesc& d, SlotSums ss, bool store) {
+// Out-of-window path (some slot flagged; uniform across the workgroup):
+// beta from the fast-window total V = lo + hi*2^32 (units of 2^-38) and the
+// flagged slots' records, whose 32-bit limbs are added column by column in
+// LDS (a column sum stays below 2^44); one thread carries the columns into a
+// multi-word integer (units of 2^-133).  All threads call it.
+__device__ inline float rare_beta(const QDesc& d, unsigned long long lo, unsigned long long hi, bool store) {
   constexpr int kCols = 2 * kWsLimbWords;
   static_assert(kCols == kLimbs, "one column per limb");
-  __shared__ unsigned long long part[2][kAbsThreads / 64];
-  __shared__ uint32_t rare_w[kAbsThreads / 64];
-  __shared__ unsigned long long cols[kAbsThreads / 64][kCols];
+  __shared__ unsigned long long cols[kCols];
   __shared__ uint32_t limbs[kLimbs + 2];
   __shared__ float beta_s;
-  const int tid = threadIdx.x, wave = tid >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    ss.lo += __shfl_xor(ss.lo, off, 64);
-    ss.hi += __shfl_xor(ss.hi, off, 64);
-  }
-  const bool any_rare = __ballot(ss.flags != 0) != 0;
-  if ((tid & 63) == 0) {
-    part[0][wave] = ss.lo;
-    part[1][wave] = ss.hi;
-    rare_w[wave] = any_rare ? 1u : 0u;
-  }
+  const int tid = threadIdx.x;
+  if (tid < kCols) cols[tid] = 0;
   __syncthreads();
-  unsigned long long lo = 0, hi = 0;
-  uint32_t flagged = 0;
-#pragma unroll
-  for (int i = 0; i < kAbsThreads / 64; ++i) {
-    lo += part[0][i];
-    hi += part[1][i];
-    flagged |= rare_w[i];
-  }
-  const uint64_t n = (uint64_t)d.nvec * 8u;
-  if (!flagged) {                                   // uniform across the workgroup
-    if (tid == 0) {
-      const float b = round_quotient_fast(lo, hi, n);
-      beta_s = b;
-      if (store) d.beta[0] = b;
-    }
-    __syncthreads();
-    return beta_s;
-  }
-  // rare path: column sums of the flagged slots' limbs
-  unsigned long long c[kCols];
-#pragma unroll
-  for (int j = 0; j < kCols; ++j) c[j] = 0;
   const uint64_t* recs = d.ws + ws_limb_base(d.nb);
-  for (uint32_t f = ss.flags; f; f &= f - 1) {
-    const int64_t i = tid + (int64_t)(__ffs(f) - 1) * kAbsThreads;
-    uint64_t w[kWsLimbWords];
-#pragma unroll
-    for (int j = 0; j < kWsLimbWords; ++j) w[j] = recs[kWsLimbWords * i + j];
+  for (int64_t i = tid; i < d.nb; i += kAbsThreads) {
+    if ((d.ws[i] >> 63) == 0) continue;
 #pragma unroll
     for (int j = 0; j < kWsLimbWords; ++j) {
-      c[2 * j] += (uint32_t)w[j];
-      c[2 * j + 1] += w[j] >> 32;
+      const uint64_t w = recs[kWsLimbWords * i + j];
+      atomicAdd(&cols[2 * j], (unsigned long long)(uint32_t)w);
+      atomicAdd(&cols[2 * j + 1], (unsigned long long)(w >> 32));
     }
-  }
-#pragma unroll
-  for (int j = 0; j < kCols; ++j) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) c[j] += __shfl_xor(c[j], off, 64);
-  }
-  if ((tid & 63) == 0) {
-#pragma unroll
-    for (int j = 0; j < kCols; ++j) cols[wave][j] = c[j];
   }
   __syncthreads();
   if (tid == 0) {
     for (int i = 0; i < kLimbs + 2; ++i) limbs[i] = 0;
-    for (int j = 0; j < kCols; ++j) {
-      unsigned long long t = 0;
-      for (int wv = 0; wv < kAbsThreads / 64; ++wv) t += cols[wv][j];
-      add_shifted(limbs, t, 32 * j);
-    }
+    for (int j = 0; j < kCols; ++j) add_shifted(limbs, cols[j], 32 * j);
     add_shifted(limbs, lo, 95);        // 2^-38 = 2^95 * 2^-133
     add_shifted(limbs, hi, 95 + 32);
-    const float bt = round_quotient(limbs, n);
+    const float bt = round_quotient(limbs, (uint64_t)d.nvec * 8u);
     beta_s = bt;
     if (store) d.beta[0] = bt;
   }
@@ -210,28 +154,75 @@ __device__ inline float finish_beta(const QDesc& d, SlotSums ss, bool store) {
   return beta_s;
 }
 
-// Slot sums of preloaded slot values (nb <= 1024).
-__device__ __forceinline__ SlotSums sum_slots(const SlotLoads& sl) {
-  SlotSums ss;
+// beta of matrix d (unclamped) from slot values every wave loaded
+// (load_slots, nb <= kWaveSlots), returned to every thread.  All threads of
+// the workgroup call it; `store` makes this workgroup write d.beta.
+__device__ inline float finish_beta(const QDesc& d, const SlotLoads& sl, bool store) {
+  // sums split in 32-bit halves so that nothing overflows
+  unsigned long long lo = 0, hi = 0;
+  uint32_t flags = 0;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) ss.add(sl.v[u], u);
-  return ss;
+  for (int u = 0; u < kWaveSlots / 64; ++u) {
+    flags |= (uint32_t)(sl.v[u] >> 63);
+    lo += (uint32_t)sl.v[u];
+    hi += (sl.v[u] & ~kRareFlag) >> 32;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo += __shfl_xor(lo, off, 64);
+    hi += __shfl_xor(hi, off, 64);
+  }
+  if (__ballot(flags != 0) != 0) return rare_beta(d, lo, hi, store);   // uniform
+  float b = 0.0f;
+  if ((threadIdx.x & 63) == 0) b = round_quotient_fast(lo, hi, (uint64_t)d.nvec * 8u);
+  b = __shfl(b, 0, 64);
+  if (store && threadIdx.x == 0) d.beta[0] = b;
+  return b;
 }
 
-// beta of matrix d for any nb <= 4096 (loads included); all threads must call it.
+// beta of matrix d for any nb <= 4096 (loads included); all threads call it.
 __device__ inline float workgroup_beta(const QDesc& d, bool store) {
-  SlotSums ss;
-  for (int64_t i0 = 0, r = 0; i0 < d.nb; i0 += 4 * kAbsThreads, ++r) {
-    uint64_t v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = i0 + threadIdx.x + u * kAbsThreads;
-      v[u] = i < d.nb ? d.ws[i] : 0ull;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) ss.add(v[u], (int)(4 * r) + u);
+  if (d.nb <= kWaveSlots) return finish_beta(d, load_slots(d), store);
+  __shared__ unsigned long long part[2][kAbsThreads / 64];
+  __shared__ uint32_t rare_w[kAbsThreads / 64];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  unsigned long long lo = 0, hi = 0;
+  uint32_t flags = 0;
+  for (int64_t i = tid; i < d.nb; i += kAbsThreads) {
+    const uint64_t v = d.ws[i];
+    flags |= (uint32_t)(v >> 63);
+    lo += (uint32_t)v;
+    hi += (v & ~kRareFlag) >> 32;
   }
-  return finish_beta(d, ss, store);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo += __shfl_xor(lo, off, 64);
+    hi += __shfl_xor(hi, off, 64);
+  }
+  const bool any = __ballot(flags != 0) != 0;
+  if ((tid & 63) == 0) {
+    part[0][wave] = lo;
+    part[1][wave] = hi;
+    rare_w[wave] = any ? 1u : 0u;
+  }
+  __syncthreads();
+  lo = hi = 0;
+  uint32_t flagged = 0;
+#pragma unroll
+  for (int i = 0; i < kAbsThreads / 64; ++i) {
+    lo += part[0][i];
+    hi += part[1][i];
+    flagged |= rare_w[i];
+  }
+  if (flagged) return rare_beta(d, lo, hi, store);
+  __shared__ float beta_s;
+  if (tid == 0) {
+    const float b = round_quotient_fast(lo, hi, (uint64_t)d.nvec * 8u);
+    beta_s = b;
+    if (store) d.beta[0] = b;
+  }
+  __syncthreads();
+  return beta_s;
 }
 
 }  // namespace beta
