@@ -19,8 +19,9 @@
 //    back as B operands; the 16-byte chunks of a token row are XOR-swizzled
 //    by the token index so that consecutive tokens read distinct banks.
 //  * weights: fetched kDepth-1 steps ahead straight into registers and
-//    decoded into A operands (7 VALU ops per 16 weights; N:M via LDS tables
-//    + v_perm); each A operand feeds KCT MFMAs.
+//    decoded into A operands (7 VALU ops per 16 weights; N:M: codes spread
+//    arithmetically, one LDS selector read per 8 weights, v_perm); each A
+//    operand feeds KCT MFMAs.
 //  * the per-step workgroup barrier waits only for LDS traffic, never for
 //    the global loads in flight.
 // K need only be a multiple of 64: in a last half step the second half reads
@@ -95,6 +96,18 @@ __device__ __forceinline__ void load_w(WRaw<KIND>& a, __amdgpu_buffer_rsrc_t rw,
 // flight across it; the "memory" clobber keeps LDS accesses on their side.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Four 2-bit codes u (bits 2i, 2i+1 of x's low byte) -> four int8
+// c = u - 1 bytes, arithmetically: two shift-or-mask rounds put code i in
+// byte i, then v_perm maps u in {0, 1, 2} to {0xFF, 0x00, 0x01}.  (A table in
+// LDS would cost a lane-random LDS read instead, and those reads, not the
+// MFMAs, bound the N:M decode.)
+__device__ __forceinline__ uint32_t spread4(uint32_t x) {
+  x &= 0xFFu;
+  const uint32_t y = (x | (x << 12)) & 0x000F000Fu;   // codes 0,1 in bits 0-3, codes 2,3 in bits 16-19
+  const uint32_t z = (y | (y << 6)) & 0x03030303u;    // code i in byte i
+  return __builtin_amdgcn_perm(0u, 0x000100FFu, z);
+}
+
 // A operand (16 weights, k order) of sub-step j: word j of the lane's block.
 template <int KIND>
 __device__ __forceinline__ v4i decode_w(const WRaw<KIND>& a, int j, const NmLut& L) {
@@ -112,8 +125,8 @@ __device__ __forceinline__ v4i decode_w(const WRaw<KIND>& a, int j, const NmLut&
     for (int q = 0; q < 2; ++q) {
       const uint32_t c12 = (c24 >> (12 * q)) & 0xFFFu;
       const uint32_t mb = (m16 >> (8 * q)) & 0xFFu;
-      const uint32_t lo = L.spread[c12 & 0xFFu];
-      const uint32_t hi = L.spread[c12 >> 8];
+      const uint32_t lo = spread4(c12);
+      const uint32_t hi = spread4(c12 >> 8);
       r[2 * q] = (int32_t)__builtin_amdgcn_perm(hi, lo, L.sel[mb][0]);
       r[2 * q + 1] = (int32_t)__builtin_amdgcn_perm(hi, lo, L.sel[mb][1]);
     }
@@ -125,7 +138,7 @@ __device__ __forceinline__ v4i decode_w(const WRaw<KIND>& a, int j, const NmLut&
     v4i r;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const uint32_t v = L.spread[(c16 >> (8 * q)) & 0xFFu];
+      const uint32_t v = spread4(c16 >> (8 * q));
       const uint32_t mb = (m16 >> (8 * q)) & 0xFFu;
       r[2 * q] = (int32_t)__builtin_amdgcn_perm(v, v, L.sel[mb][0]);
       r[2 * q + 1] = (int32_t)__builtin_amdgcn_perm(v, v, L.sel[mb][1]);
