@@ -409,6 +409,7 @@ hipError_t launch_shape(const LinearArgs* items, int count, int kind, hipStream_
 }  // namespace
 
 hipError_t launch_gemm_group(const LinearArgs* items, int count, int kind, hipStream_t s) {
+  if (kind == kNm24) return launch_gemm24_group(items, count, s);
 #ifdef SBL_GEMM_FORCE_SHAPE
   switch (SBL_GEMM_FORCE_SHAPE) {
 #else

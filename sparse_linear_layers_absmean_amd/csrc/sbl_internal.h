@@ -153,4 +153,8 @@ hipError_t launch_gemm_group(const LinearArgs* items, int count, int kind, hipSt
 // whether the GEMM's 32-bit buffer offsets cover this product
 bool gemm_fits(const LinearArgs& a, int kind);
 
+// N:M 2:4 products on the sparse MFMA (v_smfmac_i32_16x16x128_i8); called by
+// launch_gemm_group for kind 2
+hipError_t launch_gemm24_group(const LinearArgs* items, int count, hipStream_t s);
+
 }  // namespace sbl
