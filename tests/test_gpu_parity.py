@@ -217,6 +217,19 @@ def test_gemm_multi_tile_ragged(fmt, n, m):
     compare_all(gpu_forward(bits, x, n, m, fmt), oracle_forward(bits, x, n, m), fmt, n_out)
 
 
+@pytest.mark.parametrize("n_out,k,m_tok", [(1, 64, 17), (33, 128, 40), (257, 576, 129), (520, 1216, 260),
+                                           (64, 512, 128)])
+def test_gemm24_edge_shapes(n_out, k, m_tok):
+    """The 2:4 sparse-MFMA GEMM at its boundaries: one row, a lone half 128-k
+    step (K = 64), K covering the unrolled loop plus a tail, 17 tokens (just
+    above the decode range), ragged and exact tiles (64 rows x 128 tokens)."""
+    rng = np.random.default_rng([37, n_out, k, m_tok])
+    bits = synth.plant_ties(synth.gaussian_masters(rng, n_out, k), rng)
+    x = synth.gaussian_acts(rng, m_tok, k, t_row_frac=0.25)
+    say(f"gemm 2:4 sparse MFMA n_out={n_out} k={k} m_tok={m_tok}")
+    compare_all(gpu_forward(bits, x, 2, 4, FMT_NM), oracle_forward(bits, x, 2, 4), FMT_NM, n_out)
+
+
 def _rare_mixture(rng, n_out, k):
     kind = rng.integers(0, 5, (n_out, k))
     mag = np.select([kind == 0, kind == 1, kind == 2, kind == 3],
