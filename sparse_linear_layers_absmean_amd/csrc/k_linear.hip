@@ -35,7 +35,10 @@ using namespace dec;
 
 constexpr int kMaxWaves = 16;          // waves per workgroup, at most
 constexpr int kResidentWaves = 4096;   // one round: 4 waves per SIMD on 1024 SIMDs
-constexpr int kXLdsMax = 32 * 1024;    // token rows staged in LDS up to this many bytes
+constexpr int kXLdsMax = 32 * 1024;    // token rows staged through registers into LDS up to this many bytes
+constexpr int kXBigMax = 128 * 1024;   // ... and by LDS-direct loads up to this many (one workgroup per CU)
+constexpr int kBigLdsAttr = 150 * 1024;  // dynamic LDS the LDS-direct mode may request
+constexpr int64_t kXBigMinWeights = int64_t(128) << 20;   // weights per launch for the LDS-direct mode
 constexpr int kXMinWaves = 4;          // XL launches have at least this many waves per workgroup
 constexpr int kXFPer = 3;              // fused quantization: 16-value pieces of x per thread, at most
 
@@ -213,10 +216,20 @@ __device__ __forceinline__ void mac(const WStage& s, const u32x4 (&bq)[4], v4i& 
   }
 }
 
-// k-block kb = 4*sb + lane/16: super-block sb covers 256 weights of every row
-template <int KIND, bool XL, int D, bool XF>
+// LDS-direct load: lane l's 16 bytes at buffer offset voff land at lds + 16*l
+// (zeros past the buffer); counted by vmcnt.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+// k-block kb = 4*sb + lane/16: super-block sb covers 256 weights of every row.
+// XLM: how the token rows reach LDS: 0 not at all (read from memory per
+// k-block), 1 through registers, issued first (m_tok*k <= kXLdsMax), 2 by
+// LDS-direct loads (m_tok*k <= kXBigMax; the region is rounded up to 1 KB).
+template <int KIND, int XLM, int D, bool XF>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L) {
-  static_assert(!XF || XL, "the fused activation quantization stages through LDS");
+  constexpr bool XL = XLM != 0;
+  static_assert(!XF || XLM == 1, "the fused activation quantization stages through registers");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t sel[256][2];
   __shared__ int32_t qs[16];                          // XL: sum_k q per token
@@ -258,7 +271,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
   // LDS: [token rows m_tok*k (XL)][64 zero bytes][reduction ks*tb*4*64 ints]
   const uint32_t xbytes = XL ? (uint32_t)(d.m_tok * d.k) : 0u;
   const uint32_t zero_off = xbytes;
-  int32_t* red = reinterpret_cast<int32_t*>(smem + xbytes + 64);
+  const uint32_t xreg = XLM == 2 ? (xbytes + 1023u) & ~1023u : xbytes;
+  int32_t* red = reinterpret_cast<int32_t*>(smem + xreg + 64);
   const bool r_ok = r < d.m_tok;
   const uint32_t ox = r_ok ? (uint32_t)(r * d.k) : (XL ? zero_off : kFar);
 
@@ -266,9 +280,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
   // weight stages; each thread stages up to kXPer 16-byte pieces.
   // XF: the same pieces come as 16 fp32 values each (kXFPer per thread at most).
   constexpr int kXPer = XF ? kXFPer : kXLdsMax / (16 * 64 * kXMinWaves);
-  u32x4 xv[XL && !XF ? kXPer : 1];
+  u32x4 xv[XLM == 1 && !XF ? kXPer : 1];
   float4 xf4[XF ? kXPer : 1][4];
-  const int nxl = XL ? (int)((xbytes + blockDim.x * 16u - 1) / (blockDim.x * 16u)) : 0;   // <= kXPer
+  const int nxl = XL ? (int)((xbytes + blockDim.x * 16u - 1) / (blockDim.x * 16u)) : 0;   // XLM 1: <= kXPer
   if constexpr (XF) {
     const __amdgpu_buffer_rsrc_t rf = make_rsrc(d.x, (int64_t)xbytes * 4);
 #pragma unroll
@@ -281,12 +295,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
       }
     }
     if (threadIdx.x < 16) { qs[threadIdx.x] = 0; gbits[threadIdx.x] = 0u; }
-  } else if constexpr (XL) {
+  } else if constexpr (XLM == 1) {
 #pragma unroll
     for (int i = 0; i < kXPer; ++i) {
       const uint32_t o = (threadIdx.x + i * blockDim.x) * 16u;
       if (i < nxl)
         xv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.x, o < xbytes ? o : kFar, 0, 0));
+    }
+    if (threadIdx.x < 16) qs[threadIdx.x] = 0;
+  } else if constexpr (XLM == 2) {
+    // piece i of thread t = bytes (t + i*blockDim)*16 .. +15; a wave's
+    // instruction fills one 1 KB block of LDS (zeros past xbytes), and only
+    // blocks inside the rounded region xreg are issued
+    for (int i = 0; i < nxl; ++i) {
+      const uint32_t blk = (uint32_t)(wave * 64 + i * (int)blockDim.x) * 16u;   // wave-uniform
+      if (blk < xreg) dma16(rs.x, smem + blk, (threadIdx.x + i * blockDim.x) * 16u);
     }
     if (threadIdx.x < 16) qs[threadIdx.x] = 0;
   }
@@ -340,6 +363,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
     if (blockIdx.x == 0 && d.gamma_out != nullptr && threadIdx.x < (unsigned)d.m_tok)
       d.gamma_out[threadIdx.x] = __uint_as_float(gbits[threadIdx.x]);
     __syncthreads();                               // activations, sum q and the N:M tables
+  } else if constexpr (XLM == 2) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0): this thread's LDS-direct pieces have landed
+    if (threadIdx.x < 4) *reinterpret_cast<u32x4*>(smem + zero_off + 16 * threadIdx.x) = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();                               // every piece, qs cleared
+    for (int i = 0; i < nxl; ++i) {
+      const uint32_t o = (threadIdx.x + i * blockDim.x) * 16u;
+      if (o < xbytes) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(smem + o);
+        int q = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) q = __builtin_amdgcn_sdot4((int)v[w], 0x01010101, q, false);
+        atomicAdd(&qs[o / (uint32_t)d.k], q);
+      }
+    }
+    __syncthreads();                               // sum q and the N:M tables
   } else if constexpr (XL) {
     if (threadIdx.x < 4) *reinterpret_cast<u32x4*>(smem + zero_off + 16 * threadIdx.x) = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();                               // qs cleared
@@ -534,16 +572,25 @@ int kind_of(int fmt, int n, int m) {
 // short, else 4 (with the panel-major layout the waves of a launch sweep the
 // matrix together, and a shallower ring keeps the sweep's front compact)
 template <int KIND>
-void launch_gemv(const GemvLaunch& L, bool xl, bool xf, int spw, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+void launch_gemv(const GemvLaunch& L, int xlm, bool xf, int spw, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
   if (xf) {
-    if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, true, 2, true>), grid, block, lds, s, L);
-    else hipLaunchKernelGGL((gemv_kernel<KIND, true, 4, true>), grid, block, lds, s, L);
-  } else if (xl) {
-    if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, true, 2, false>), grid, block, lds, s, L);
-    else hipLaunchKernelGGL((gemv_kernel<KIND, true, 4, false>), grid, block, lds, s, L);
+    if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, 1, 2, true>), grid, block, lds, s, L);
+    else hipLaunchKernelGGL((gemv_kernel<KIND, 1, 4, true>), grid, block, lds, s, L);
+  } else if (xlm == 1) {
+    if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, 1, 2, false>), grid, block, lds, s, L);
+    else hipLaunchKernelGGL((gemv_kernel<KIND, 1, 4, false>), grid, block, lds, s, L);
+  } else if (xlm == 2) {
+    // more dynamic LDS than the default limit: raised once per kernel
+    static const bool raised = hipFuncSetAttribute((const void*)gemv_kernel<KIND, 2, 2, false>,
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, kBigLdsAttr) == hipSuccess &&
+                               hipFuncSetAttribute((const void*)gemv_kernel<KIND, 2, 4, false>,
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, kBigLdsAttr) == hipSuccess;
+    (void)raised;
+    if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, 2, 2, false>), grid, block, lds, s, L);
+    else hipLaunchKernelGGL((gemv_kernel<KIND, 2, 4, false>), grid, block, lds, s, L);
   } else {
-    if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, false, 2, false>), grid, block, lds, s, L);
-    else hipLaunchKernelGGL((gemv_kernel<KIND, false, 4, false>), grid, block, lds, s, L);
+    if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, 0, 2, false>), grid, block, lds, s, L);
+    else hipLaunchKernelGGL((gemv_kernel<KIND, 0, 4, false>), grid, block, lds, s, L);
   }
 }
 
@@ -551,17 +598,18 @@ void launch_gemv(const GemvLaunch& L, bool xl, bool xf, int spw, dim3 grid, dim3
 // workgroup, about one round of resident waves.
 struct GemvShape {
   int ks, tb, spw;
-  bool xl;
+  int xlm;    // token-row staging: 0 none, 1 registers, 2 LDS-direct (gemv_kernel's XLM)
 };
 GemvShape gemv_shape(const LinDesc* items, int count) {
   int tiles = 0, max_nsb = 1;
-  int64_t max_x = 0;
+  int64_t max_x = 0, weights = 0;
   for (int i = 0; i < count; ++i) {
     tiles += (int)((items[i].n_out + 15) / 16);
     const int nsb = (items[i].k / 64 + 3) / 4;
     max_nsb = nsb > max_nsb ? nsb : max_nsb;
     const int64_t xb = (int64_t)items[i].m_tok * items[i].k;
     max_x = xb > max_x ? xb : max_x;
+    weights += items[i].n_out * (int64_t)items[i].k;
   }
   GemvShape g;
   g.ks = tiles > 0 ? kResidentWaves / tiles : 1;
@@ -569,15 +617,19 @@ GemvShape gemv_shape(const LinDesc* items, int count) {
   g.ks = g.ks > max_nsb ? max_nsb : g.ks;
   g.tb = 8 / g.ks;
   g.tb = g.tb < 1 ? 1 : g.tb;
-  g.xl = max_x <= kXLdsMax;
-  if (g.xl && g.ks * g.tb < kXMinWaves) g.tb = (kXMinWaves + g.ks - 1) / g.ks;   // the staging needs the threads
+  // LDS-direct staging pays for its full-size workgroups and its staging pass
+  // only on long weight streams (70B-class widths: +23-30% at 8-16 tokens;
+  // 3B-class launches: 6-10% slower)
+  g.xlm = max_x <= kXLdsMax ? 1 : (max_x <= kXBigMax && weights >= kXBigMinWeights ? 2 : 0);
+  if (g.xlm == 1 && g.ks * g.tb < kXMinWaves) g.tb = (kXMinWaves + g.ks - 1) / g.ks;   // the staging needs the threads
+  if (g.xlm == 2) g.tb = kMaxWaves / g.ks;                // one workgroup per CU (LDS): make it a full one
   g.spw = (max_nsb + g.ks - 1) / g.ks;            // stages per wave
   return g;
 }
 
 // whether the fused activation quantization covers m_tok x k activations at this shape
 bool gemv_fuses(const GemvShape& g, int64_t m_tok, int64_t k) {
-  return g.xl && m_tok * k <= (int64_t)16 * kXFPer * 64 * g.ks * g.tb;
+  return g.xlm == 1 && m_tok * k <= (int64_t)16 * kXFPer * 64 * g.ks * g.tb;
 }
 
 // xf: fp32 activations shared by every item, quantized inside the launch
@@ -609,12 +661,13 @@ hipError_t launch_gemv_group(int kind, const LinDesc* items, int count, hipStrea
   }
   L.b.start[count] = blocks;
   L.b.count = count;
-  const size_t lds = (g.xl ? (size_t)max_x : 0) + 64 + (g.ks > 1 ? (size_t)g.ks * g.tb * 4 * 64 * sizeof(int32_t) : 0);
+  const size_t xreg = g.xlm == 2 ? ((size_t)max_x + 1023) & ~(size_t)1023 : (g.xlm == 1 ? (size_t)max_x : 0);
+  const size_t lds = xreg + 64 + (g.ks > 1 ? (size_t)g.ks * g.tb * 4 * 64 * sizeof(int32_t) : 0);
   const dim3 grid((unsigned)blocks), block(64 * g.ks * g.tb);
   const bool xf_on = xf != nullptr;
-  if (kind == kDense2) launch_gemv<kDense2>(L, g.xl, xf_on, g.spw, grid, block, lds, s);
-  else if (kind == kNm68) launch_gemv<kNm68>(L, g.xl, xf_on, g.spw, grid, block, lds, s);
-  else launch_gemv<kNm24>(L, g.xl, xf_on, g.spw, grid, block, lds, s);
+  if (kind == kDense2) launch_gemv<kDense2>(L, g.xlm, xf_on, g.spw, grid, block, lds, s);
+  else if (kind == kNm68) launch_gemv<kNm68>(L, g.xlm, xf_on, g.spw, grid, block, lds, s);
+  else launch_gemv<kNm24>(L, g.xlm, xf_on, g.spw, grid, block, lds, s);
   return hipGetLastError();
 }
 
