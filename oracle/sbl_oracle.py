@@ -9,7 +9,8 @@ from the seeded generators in `synth.py`, which hold none of this arithmetic.
 Sources (the method pages; sections, equations and items named per page):
   [SB-es]  "Sparse-BitNet: 1.58-bit LLMs are Naturally Friendly to
            Semi-Structured Sparsity", gist.science Spanish summary,
-           "Resumen tecnico", sections 1 (Problema) and 2 (Metodologia).
+           "Resumen tecnico", sections 1 (Problema), 2 (Metodologia) and
+           3 (Contribuciones Clave; item 3: the training-design ablations).
   [SB-ar]  the same paper, gist.science Arabic summary, section 2
            (Methodology): items "Ternary Quantization", "Dynamic N:M
            Masking", "Mask Generation", "Quant-Then-Mask Order".
@@ -111,8 +112,9 @@ def rational_to_f32(num: int, den: int) -> np.float32:
 #     [BN-spec] absmean weights
 # --------------------------------------------------------------------------
 
-def absmean_exact(bits: np.ndarray) -> Fraction:
-    """Exact mean of |w| over every BF16 value of the matrix.
+def absmean_exact(bits: np.ndarray, keep=None) -> Fraction:
+    """Exact mean of |w| over every BF16 value of the matrix, or over the
+    values where `keep` is true (the mask-then-quant ablation).
 
     A finite BF16 magnitude is sig * 2^(max(e,1) - 134) with e the biased
     exponent and sig = mantissa | (e != 0) << 7, i.e. an integer number of
@@ -123,6 +125,10 @@ def absmean_exact(bits: np.ndarray) -> Fraction:
     if b.size == 0:
         raise ValueError("empty weight matrix")
     _check_finite_bf16(b)
+    if keep is not None:
+        b = b[np.asarray(keep, dtype=bool).ravel()]
+        if b.size == 0:
+            raise ValueError("nothing kept")
     mag = (b & 0x7FFF).astype(np.int64)
     e = mag >> 7
     sig = (mag & 0x7F) | ((e != 0).astype(np.int64) << 7)
@@ -135,9 +141,10 @@ def absmean_exact(bits: np.ndarray) -> Fraction:
     return Fraction(total, b.size << 133)
 
 
-def absmean_beta(bits: np.ndarray) -> np.float32:
-    """beta = RN_fp32(mean |w|): one scale per weight matrix."""
-    f = absmean_exact(bits)
+def absmean_beta(bits: np.ndarray, keep=None) -> np.float32:
+    """beta = RN_fp32(mean |w|): one scale per weight matrix (over the kept
+    values only when `keep` is given)."""
+    f = absmean_exact(bits, keep)
     return rational_to_f32(f.numerator, f.denominator)
 
 
@@ -176,11 +183,18 @@ def nm_keep(bits: np.ndarray, n: int, m: int) -> np.ndarray:
     rank_j = #{i : |w_i| > |w_j|} + #{i < j : |w_i| == |w_j|}; keep_j = rank_j < n.
     """
     b = np.asarray(bits, dtype=np.uint16)
-    n_out, k = b.shape
+    _check_finite_bf16(b)
+    return top_n_keep(np.abs(bf16_to_f32(b)), n, m)
+
+
+def top_n_keep(mag: np.ndarray, n: int, m: int) -> np.ndarray:
+    """The same rank rule for any magnitudes [n_out][k] (|w| of the masters,
+    or |c| of the codes for the masks-from-quantized-weights ablation)."""
+    mag = np.asarray(mag)
+    n_out, k = mag.shape
     if m < 1 or n < 1 or n > m or k % m:
         raise ValueError("bad N:M pattern for this shape")
-    _check_finite_bf16(b)
-    mag = np.abs(bf16_to_f32(b)).reshape(n_out, k // m, m)
+    mag = mag.reshape(n_out, k // m, m)
     keep = np.empty((n_out, k // m, m), dtype=bool)
     idx = np.arange(m)
     lower = idx[None, :] < idx[:, None]          # lower[j, i] = i < j
@@ -199,11 +213,34 @@ def nm_keep(bits: np.ndarray, n: int, m: int) -> np.ndarray:
 # [SB-ar] "Quant-Then-Mask Order"
 # --------------------------------------------------------------------------
 
-def quant_weights(bits: np.ndarray, n: int, m: int):
-    """(beta, keep, codes) with codes = RoundClip(w/beta_eff, -1, 1) * keep."""
-    beta = absmean_beta(bits)
-    keep = nm_keep(bits, n, m)
-    codes = ternarize(bits, beta) * keep.astype(np.int8)
+QUANT_THEN_MASK, MASK_THEN_QUANT, MASK_FROM_CODES = "quant_then_mask", "mask_then_quant", "mask_from_codes"
+
+
+def quant_weights(bits: np.ndarray, n: int, m: int, order: str = QUANT_THEN_MASK):
+    """(beta, keep, codes) with codes = RoundClip(w/beta_eff, -1, 1) * keep.
+
+    order (the pages' training-design ablations, [SB-es] section 3 item 3):
+      quant_then_mask  the method: beta over every master, mask from the masters;
+      mask_then_quant  mask from the masters first, beta over the kept masters only;
+      mask_from_codes  beta over every master, then the mask from |codes|
+                       (top n per group, ties to the lower index), instead of
+                       from the masters.
+    """
+    if order == QUANT_THEN_MASK:
+        beta = absmean_beta(bits)
+        keep = nm_keep(bits, n, m)
+        codes = ternarize(bits, beta) * keep.astype(np.int8)
+    elif order == MASK_THEN_QUANT:
+        keep = nm_keep(bits, n, m)
+        beta = absmean_beta(bits, keep)
+        codes = ternarize(bits, beta) * keep.astype(np.int8)
+    elif order == MASK_FROM_CODES:
+        beta = absmean_beta(bits)
+        c = ternarize(bits, beta)
+        keep = top_n_keep(np.abs(c), n, m)
+        codes = c * keep.astype(np.int8)
+    else:
+        raise ValueError(f"unknown order {order!r}")
     return beta, keep, codes.astype(np.int8)
 
 
