@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SBL_ABI_VERSION 3
+#define SBL_ABI_VERSION 4
 
 typedef enum {
   SBL_OK = 0,
@@ -168,6 +168,27 @@ typedef struct {
  * sbl_quant_weights on each item. */
 int sbl_quant_weights_batch(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m,
                             int32_t fmt, sbl_stream stream);
+
+/* The pages' weight-preparation ablations (Sparse-BitNet summary, Spanish,
+ * section 3 "Contribuciones Clave", item 3: the training-design analysis,
+ * which finds masks from the continuous masters and the quant-then-mask order
+ * better than the alternatives).  Flags of sbl_quant_weights_batch_ex:
+ *   SBL_QW_DEFAULT          the method (what sbl_quant_weights_batch does).
+ *   SBL_QW_BETA_KEPT        mask-then-quant: the n:m mask comes first (from the
+ *                           masters, as usual) and beta is the exact mean of
+ *                           |w| over the kept weights only (n_out*k*n/m of
+ *                           them); the codes use that beta.
+ *   SBL_QW_MASK_FROM_CODES  the mask keeps the n largest |code| of every group
+ *                           (codes from beta over every weight; equal |code|
+ *                           goes to the lower index) instead of the n largest
+ *                           master magnitudes.
+ * The two are exclusive; other bits or both together give SBL_ERR_UNSUPPORTED
+ * before anything is checked or enqueued.  Outputs and formats are those of
+ * sbl_quant_weights_batch.  The variants run slower kernels (per-key
+ * selection) than the method's own path. */
+enum { SBL_QW_DEFAULT = 0, SBL_QW_BETA_KEPT = 1, SBL_QW_MASK_FROM_CODES = 2 };
+int sbl_quant_weights_batch_ex(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m,
+                               int32_t fmt, int32_t flags, sbl_stream stream);
 
 /* Packing alone: ternary codes (+ mask) -> packed bytes.
  *   codes      [n_out][k] int8 in {-1,0,1} (other values: unspecified bytes).

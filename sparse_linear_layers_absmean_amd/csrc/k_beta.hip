@@ -23,6 +23,7 @@
 //    kernel does it when beta is the only output.
 // Several matrices share each launch (QBatch).
 #include "sbl_beta.h"
+#include "sbl_select.h"
 
 namespace sbl {
 
@@ -80,6 +81,38 @@ __device__ __forceinline__ void consume(const u32x4& v, double& acc0, double& ac
   }
 }
 
+// The same for the mask-then-quant variant: only the halves whose bit is set
+// in `keep` (bit 2j: low half of word j, bit 2j+1: high half) are added.  The
+// fast-window test still looks at every value (a dropped value outside the
+// window only sends the vector to the per-value path).
+__device__ __forceinline__ void consume_kept(const u32x4& v, uint32_t keep, double& acc0, double& acc1,
+                                             unsigned long long* bins, uint32_t& rare) {
+  uint32_t a[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a[j] = v[j] & 0x7FFF7FFFu;
+  const uint32_t t = pk_max(pk_max(pk_sub(a[0], 0x30003000u), pk_sub(a[1], 0x30003000u)),
+                            pk_max(pk_sub(a[2], 0x30003000u), pk_sub(a[3], 0x30003000u)));
+  if ((t & 0xF000F000u) == 0u) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t mlo = ((keep >> (2 * j)) & 1u) ? 0xFFFFu : 0u;
+      const uint32_t mhi = ((keep >> (2 * j + 1)) & 1u) ? 0xFFFF0000u : 0u;
+      acc0 += (double)__uint_as_float((a[j] & mlo) << 16);
+      acc1 += (double)__uint_as_float(a[j] & mhi);
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = ((keep >> (2 * j)) & 1u) ? (a[j] & 0xFFFFu) : 0u;
+    const uint32_t hi = ((keep >> (2 * j + 1)) & 1u) ? (a[j] >> 16) : 0u;
+    if ((lo - 0x3000u) < 0x1000u) acc0 += (double)__uint_as_float(lo << 16);
+    else if (lo) rare_add(bins, lo, rare);
+    if ((hi - 0x3000u) < 0x1000u) acc1 += (double)__uint_as_float(hi << 16);
+    else if (hi) rare_add(bins, hi, rare);
+  }
+}
+
 // Workgroup g of a matrix covers vectors [g*256*vpt, (g+1)*256*vpt) (vpt is a
 // multiple of 8); thread t reads vectors t, t+256, ... of that range, so each
 // load instruction of a wave reads 1 KB contiguous; 8 or 16 loads in flight.
@@ -87,8 +120,11 @@ __device__ __forceinline__ void consume(const u32x4& v, double& acc0, double& ac
 // NT: nontemporal loads, for groups of matrices too large for the 256 MB
 // Infinity Cache to hold until the mask/pack pass reads them again (13B
 // block: 251 µs per call instead of 273 µs; 0.7B block: 39.4 instead of 38.4).
-template <bool NT>
-__global__ __launch_bounds__(kAbsThreads) void absmean_partial_kernel(const QBatch batch) {
+// KM > 0 (mask-then-quant): only the weights an n:KM mask keeps are summed
+// (Sparse-BitNet summary, section 3 item 3, the ablated order); a 16-byte
+// vector is one group of 8 or two groups of 4, selected by the rank rule.
+template <bool NT, int KM>
+__global__ __launch_bounds__(kAbsThreads) void absmean_partial_kernel(const QBatch batch, int n) {
   const int di = find_item(batch);
   const QDesc& d = batch.d[di];
   const int64_t wg = (int64_t)blockIdx.x - batch.start[di];
@@ -114,7 +150,18 @@ __global__ __launch_bounds__(kAbsThreads) void absmean_partial_kernel(const QBat
   };
   auto process8 = [&](const u32x4 (&v)[8]) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) consume(v[u], acc0, acc1, bins, rare);
+    for (int u = 0; u < 8; ++u) {
+      if constexpr (KM == 0) {
+        consume(v[u], acc0, acc1, bins, rare);
+      } else {
+        uint32_t A[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) A[j] = v[u][j] & 0x7FFF7FFFu;
+        const uint32_t keep = KM == 8 ? sel::keep_by_rank<8>(A, n)
+                                      : sel::keep_by_rank<4>(A, n) | (sel::keep_by_rank<4>(A + 2, n) << 4);
+        consume_kept(v[u], keep, acc0, acc1, bins, rare);
+      }
+    }
   };
   u32x4 va[8], vb[8];
   load8(va, 0);
@@ -198,9 +245,23 @@ hipError_t launch_absmean_partial(QBatch& b, hipStream_t s) {
   int64_t bytes = 0;
   for (int i = 0; i < b.count; ++i) bytes += b.d[i].nvec * 16;
   if (bytes > kAbsStreamBytes)
-    hipLaunchKernelGGL(absmean_partial_kernel<true>, dim3((unsigned)blocks), dim3(kAbsThreads), 0, s, b);
+    hipLaunchKernelGGL((absmean_partial_kernel<true, 0>), dim3((unsigned)blocks), dim3(kAbsThreads), 0, s, b, 0);
   else
-    hipLaunchKernelGGL(absmean_partial_kernel<false>, dim3((unsigned)blocks), dim3(kAbsThreads), 0, s, b);
+    hipLaunchKernelGGL((absmean_partial_kernel<false, 0>), dim3((unsigned)blocks), dim3(kAbsThreads), 0, s, b, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_absmean_partial_kept(QBatch& b, int n, int m, hipStream_t s) {
+  int64_t blocks = 0;
+  for (int i = 0; i < b.count; ++i) {
+    b.start[i] = blocks;
+    blocks += b.d[i].nb;
+  }
+  b.start[b.count] = blocks;
+  if (m == 8)
+    hipLaunchKernelGGL((absmean_partial_kernel<false, 8>), dim3((unsigned)blocks), dim3(kAbsThreads), 0, s, b, n);
+  else
+    hipLaunchKernelGGL((absmean_partial_kernel<false, 4>), dim3((unsigned)blocks), dim3(kAbsThreads), 0, s, b, n);
   return hipGetLastError();
 }
 

@@ -327,8 +327,10 @@ void launch_fast(const QBatch& b, hipStream_t s) {
 }
 
 // Any n (one thread per chunk, one sort key per weight).
+// mfc: the keys rank |code| (nonzero or not) instead of |w| (the masks-from-
+// quantized-weights ablation; ties still go to the lower index).
 template <int M>
-__global__ __launch_bounds__(kThreads) void mask_pack_kernel(const QBatch batch, int n) {
+__global__ __launch_bounds__(kThreads) void mask_pack_kernel(const QBatch batch, int n, int mfc) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads * kPad];
   constexpr int SH = (M == 8) ? 3 : 2;
   const int di = find_item(batch);
@@ -339,7 +341,6 @@ __global__ __launch_bounds__(kThreads) void mask_pack_kernel(const QBatch batch,
   const int64_t lwg = (int64_t)blockIdx.x - batch.start[di];
   const float b = fmaxf(batch.beta_ready ? d.beta[0] : beta::workgroup_beta(d, lwg == 0), 1e-5f);
   const int thr_mag = (int)(__float_as_uint(b * 0.5f) >> 16);
-  const int thr_nz = (thr_mag << SH) | (M - 1);      // key > thr_nz  <=>  |w| > beta_eff/2
   const bool want_nm = packed && fmt == 1;
   {
     const int64_t c0 = lwg * kThreads;
@@ -353,11 +354,14 @@ __global__ __launch_bounds__(kThreads) void mask_pack_kernel(const QBatch batch,
     for (int g = 0; g < 64 / M; ++g) {
       int key[M];
       uint32_t sgn[M];
+      bool nzc[M];                                   // code nonzero before the mask: |w| > beta_eff/2
 #pragma unroll
       for (int j = 0; j < M; ++j) {
         const int idx = g * M + j;
         const uint32_t h = (idx & 1) ? (dw[idx >> 1] >> 16) : (dw[idx >> 1] & 0xFFFFu);
-        key[j] = (int)(((h & 0x7FFFu) << SH) | (uint32_t)(M - 1 - j));
+        nzc[j] = (int)(h & 0x7FFFu) > thr_mag;
+        const uint32_t rank_mag = mfc ? (nzc[j] ? 1u : 0u) : (h & 0x7FFFu);
+        key[j] = (int)((rank_mag << SH) | (uint32_t)(M - 1 - j));
         sgn[j] = h >> 15;
       }
       const int thr = group_threshold<M>(key, n);
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void mask_pack_kernel(const QBatch batch,
       for (int j = 0; j < M; ++j) {
         const int idx = g * M + j;
         const bool keep = key[j] > thr;
-        const bool nz = keep && key[j] > thr_nz;
+        const bool nz = keep && nzc[j];
         const uint32_t u = nz ? (sgn[j] ? 0u : 2u) : 1u;
         o.d2[idx >> 4] |= u << d2_shift(idx);
         o.keep |= (uint64_t)keep << idx;
@@ -429,9 +433,10 @@ int64_t grid_for(int64_t nchunks) {
 
 }  // namespace
 
-hipError_t launch_mask_pack(QBatch& b, int n, int m, hipStream_t s, bool dry, int64_t* grid_out) {
+hipError_t launch_mask_pack(QBatch& b, int n, int m, hipStream_t s, bool dry, int64_t* grid_out,
+                            bool mask_from_codes) {
   const int drop = m - n;
-  const bool fast = drop <= 2;
+  const bool fast = drop <= 2 && !mask_from_codes;
   const int64_t per_block = fast ? (int64_t)kThreads * kCPT : kThreads;   // chunks per workgroup
   int64_t blocks = 0;
   for (int i = 0; i < b.count; ++i) {
@@ -442,14 +447,14 @@ hipError_t launch_mask_pack(QBatch& b, int n, int m, hipStream_t s, bool dry, in
   if (grid_out) *grid_out = blocks;
   if (dry) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(kThreads);
-  if (m == 8 && drop == 0) launch_fast<8, 0>(b, s);
+  if (!fast && m == 8) hipLaunchKernelGGL((mask_pack_kernel<8>), grid, block, 0, s, b, n, mask_from_codes ? 1 : 0);
+  else if (!fast) hipLaunchKernelGGL((mask_pack_kernel<4>), grid, block, 0, s, b, n, mask_from_codes ? 1 : 0);
+  else if (m == 8 && drop == 0) launch_fast<8, 0>(b, s);
   else if (m == 8 && drop == 1) launch_fast<8, 1>(b, s);
   else if (m == 8 && drop == 2) launch_fast<8, 2>(b, s);
   else if (m == 4 && drop == 0) launch_fast<4, 0>(b, s);
   else if (m == 4 && drop == 1) launch_fast<4, 1>(b, s);
   else if (m == 4 && drop == 2) launch_fast<4, 2>(b, s);
-  else if (m == 8) hipLaunchKernelGGL((mask_pack_kernel<8>), grid, block, 0, s, b, n);
-  else hipLaunchKernelGGL((mask_pack_kernel<4>), grid, block, 0, s, b, n);
   return hipGetLastError();
 }
 

@@ -114,6 +114,7 @@ sbl::QDesc to_qdesc(const sbl_quant_item& it, int32_t fmt) {
   sbl::QDesc d;
   d.w = reinterpret_cast<const sbl::u32x4*>(it.w_bf16);
   d.nvec = total / 8;
+  d.count = total;
   d.nb = p.nb;
   d.vpt = p.vpt;
   d.beta = it.beta;
@@ -137,8 +138,9 @@ sbl::QDesc to_qdesc(const sbl_quant_item& it, int32_t fmt) {
 constexpr int64_t kPrologueMaxWorkgroups = 1024;
 constexpr int64_t kPrologueMaxSlots = 512;       // every wave loads all partial sums (beta::kWaveSlots)
 
-int launch_quant(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m, int32_t fmt,
+int launch_quant(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m, int32_t fmt, int32_t flags,
                  hipStream_t s) {
+  const bool kept = (flags & SBL_QW_BETA_KEPT) != 0, mfc = (flags & SBL_QW_MASK_FROM_CODES) != 0;
   for (int i0 = 0; i0 < count; i0 += sbl::kMaxQDesc) {
     sbl::QBatch b;
     b.count = count - i0 < sbl::kMaxQDesc ? count - i0 : sbl::kMaxQDesc;
@@ -146,16 +148,17 @@ int launch_quant(const sbl_quant_item* items, int32_t count, int32_t n, int32_t 
     bool outputs = false;
     for (int i = 0; i < b.count; ++i) {
       b.d[i] = to_qdesc(items[i0 + i], fmt);
+      if (kept) b.d[i].count = b.d[i].count / m * n;   // k % m == 0: exact
       outputs = outputs || b.d[i].mask || b.d[i].codes || b.d[i].packed;
     }
     int64_t grid = 0;
     bool wide = false;                              // a matrix with more than 512 partial sums
     for (int i = 0; i < b.count; ++i) wide = wide || b.d[i].nb > kPrologueMaxSlots;
-    (void)sbl::launch_mask_pack(b, n, m, s, true, &grid);
+    (void)sbl::launch_mask_pack(b, n, m, s, true, &grid, mfc);
     b.beta_ready = !outputs || wide || grid > kPrologueMaxWorkgroups;
-    int st = launch_status(sbl::launch_absmean_partial(b, s));
+    int st = launch_status(kept ? sbl::launch_absmean_partial_kept(b, n, m, s) : sbl::launch_absmean_partial(b, s));
     if (st == SBL_OK && b.beta_ready) st = launch_status(sbl::launch_absmean_final(b, s));
-    if (st == SBL_OK && outputs) st = launch_status(sbl::launch_mask_pack(b, n, m, s));
+    if (st == SBL_OK && outputs) st = launch_status(sbl::launch_mask_pack(b, n, m, s, false, nullptr, mfc));
     if (st != SBL_OK) return st;
   }
   return SBL_OK;
@@ -178,11 +181,19 @@ int sbl_quant_weights(const uint16_t* w_bf16, int64_t n_out, int64_t k, int32_t 
                              workspace, workspace_bytes};
   const int st = check_quant(it, n, m, fmt);
   if (st != SBL_OK) return st;
-  return launch_quant(&it, 1, n, m, fmt, reinterpret_cast<hipStream_t>(stream));
+  return launch_quant(&it, 1, n, m, fmt, 0, reinterpret_cast<hipStream_t>(stream));
 }
 
 int sbl_quant_weights_batch(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m,
                             int32_t fmt, sbl_stream stream) {
+  return sbl_quant_weights_batch_ex(items, count, n, m, fmt, SBL_QW_DEFAULT, stream);
+}
+
+int sbl_quant_weights_batch_ex(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m,
+                               int32_t fmt, int32_t flags, sbl_stream stream) {
+  if ((flags & ~(SBL_QW_BETA_KEPT | SBL_QW_MASK_FROM_CODES)) != 0 ||
+      flags == (SBL_QW_BETA_KEPT | SBL_QW_MASK_FROM_CODES))
+    return SBL_ERR_UNSUPPORTED;
   if (!items) return SBL_ERR_NULL;
   if (count < 1 || count > 256) return SBL_ERR_SHAPE;
   for (int i = 0; i < count; ++i) {
@@ -191,7 +202,7 @@ int sbl_quant_weights_batch(const sbl_quant_item* items, int32_t count, int32_t 
     for (int j = 0; j < i; ++j)
       if (overlaps(items[i], items[j])) return SBL_ERR_WORKSPACE;
   }
-  return launch_quant(items, count, n, m, fmt, reinterpret_cast<hipStream_t>(stream));
+  return launch_quant(items, count, n, m, fmt, flags, reinterpret_cast<hipStream_t>(stream));
 }
 
 int sbl_pack(const int8_t* codes, const uint8_t* mask_bits, int64_t n_out, int64_t k, int32_t n,

@@ -42,14 +42,15 @@ __device__ inline void add_shifted(uint32_t* L, uint64_t v, int s) {
 }
 
 // RN_fp32(D / n) for a dividend D = W * 2^e + r, 0 <= r < 2^e, with bit 63 of
-// W set, r != 0 exactly when `sticky`, and 64 <= n <= 2^34.  floor(D / (n*2^e))
+// W set, r != 0 exactly when `sticky`, and 1 <= n <= 2^34.  floor(D / (n*2^e))
 // = floor(W / n) = Q (since R + r/2^e < n), and Q >= 2^29 holds more than the
 // 24 bits + guard that rounding needs; whatever is below is only a sticky
-// flag.  Nearest, ties to even, subnormal results included.
+// flag (with n >= 1, Q < 2^64 as well).  Nearest, ties to even, subnormal
+// results included.
 __device__ inline float round_div(uint64_t W, int e, bool sticky, uint64_t n) {
   const uint64_t Q = W / n, R = W - Q * n;
   sticky = sticky || R != 0;
-  const int qb = 64 - __clzll((long long)Q);        // 30 <= qb <= 58
+  const int qb = 64 - __clzll((long long)Q);        // 30 <= qb <= 64
   int lsb = qb - 24;                                // fp32 unit inside Q for a normal result
   if (e + lsb < -149) lsb = -149 - e;               // subnormal: the unit is 2^-149
   if (lsb > qb) return 0.0f;                        // below half the smallest subnormal
@@ -146,7 +147,7 @@ __device__ inline float rare_beta(const QDesc& d, unsigned long long lo, unsigne
     for (int j = 0; j < kCols; ++j) add_shifted(limbs, cols[j], 32 * j);
     add_shifted(limbs, lo, 95);        // 2^-38 = 2^95 * 2^-133
     add_shifted(limbs, hi, 95 + 32);
-    const float bt = round_quotient(limbs, (uint64_t)d.nvec * 8u);
+    const float bt = round_quotient(limbs, (uint64_t)d.count);
     beta_s = bt;
     if (store) d.beta[0] = bt;
   }
@@ -174,7 +175,7 @@ __device__ inline float finish_beta(const QDesc& d, const SlotLoads& sl, bool st
   }
   if (__ballot(flags != 0) != 0) return rare_beta(d, lo, hi, store);   // uniform
   float b = 0.0f;
-  if ((threadIdx.x & 63) == 0) b = round_quotient_fast(lo, hi, (uint64_t)d.nvec * 8u);
+  if ((threadIdx.x & 63) == 0) b = round_quotient_fast(lo, hi, (uint64_t)d.count);
   b = __shfl(b, 0, 64);
   if (store && threadIdx.x == 0) d.beta[0] = b;
   return b;
@@ -217,7 +218,7 @@ __device__ inline float workgroup_beta(const QDesc& d, bool store) {
   if (flagged) return rare_beta(d, lo, hi, store);
   __shared__ float beta_s;
   if (tid == 0) {
-    const float b = round_quotient_fast(lo, hi, (uint64_t)d.nvec * 8u);
+    const float b = round_quotient_fast(lo, hi, (uint64_t)d.count);
     beta_s = b;
     if (store) d.beta[0] = b;
   }

@@ -82,6 +82,7 @@ __host__ __device__ __forceinline__ int64_t panel_offset(int64_t n_out, int64_t 
 struct QDesc {
   const u32x4* w;         // BF16 masters as 16-byte vectors (8 values each)
   int64_t nvec;           // n_out*k/8
+  int64_t count;          // values beta averages over: n_out*k, or the kept ones (n_out*k*n/m)
   int64_t nb, vpt;        // absmean partition (AbsmeanPlan)
   float* beta;
   uint64_t* ws;
@@ -109,8 +110,13 @@ struct QBatch {
 // own grid; launch_mask_pack returns its workgroup count in *grid when
 // `dry` (nothing launched).
 hipError_t launch_absmean_partial(QBatch& batch, hipStream_t s);
+// The mask-then-quant variant: only the magnitudes the n:m mask keeps are summed.
+hipError_t launch_absmean_partial_kept(QBatch& batch, int n, int m, hipStream_t s);
 hipError_t launch_absmean_final(QBatch& batch, hipStream_t s);
-hipError_t launch_mask_pack(QBatch& batch, int n, int m, hipStream_t s, bool dry = false, int64_t* grid = nullptr);
+// mask_from_codes: the mask keeps the n largest |code| per group (ties to the
+// lower index) instead of the n largest master magnitudes.
+hipError_t launch_mask_pack(QBatch& batch, int n, int m, hipStream_t s, bool dry = false, int64_t* grid = nullptr,
+                            bool mask_from_codes = false);
 
 hipError_t launch_workspace_init(uint64_t* ws, int64_t words, hipStream_t s);
 

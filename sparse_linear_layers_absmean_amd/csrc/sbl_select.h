@@ -103,5 +103,30 @@ __device__ __forceinline__ uint32_t select_keep(const uint32_t* A, uint32_t* F, 
   }
 }
 
+// Keep bits of one group of M from its M/2 words of magnitudes (sign bits
+// cleared) for any n, by the rank rule: key_j = mag_j << log2(M) | (M-1-j) is
+// unique in the group and orders by magnitude, then lower index; the n largest
+// keys are kept.  (About M*M compares: for the patterns and variants the
+// packed networks above do not cover.)
+template <int M>
+__device__ __forceinline__ uint32_t keep_by_rank(const uint32_t* A, int n) {
+  constexpr int SH = M == 8 ? 3 : 2;
+  int key[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    const uint32_t h = (j & 1) ? (A[j >> 1] >> 16) : (A[j >> 1] & 0xFFFFu);
+    key[j] = (int)((h << SH) | (uint32_t)(M - 1 - j));
+  }
+  uint32_t keep = 0;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    int above = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) above += key[i] > key[j];
+    keep |= (above < n ? 1u : 0u) << j;
+  }
+  return keep;
+}
+
 }  // namespace sel
 }  // namespace sbl

@@ -21,7 +21,9 @@ LIB_PATH = os.path.join(_HERE, "libsbl.so")
 SBL_OK = 0
 SBL_FMT_DENSE2 = 0
 SBL_FMT_NM = 1
-ABI_VERSION = 3
+# weight-preparation variants (sbl_quant_weights_batch_ex flags)
+SBL_QW_DEFAULT, SBL_QW_BETA_KEPT, SBL_QW_MASK_FROM_CODES = 0, 1, 2
+ABI_VERSION = 4
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32
@@ -79,6 +81,9 @@ def load():
     lib.sbl_quant_weights_batch.restype = ctypes.c_int
     lib.sbl_quant_weights_batch.argtypes = [ctypes.POINTER(QuantItem), _c_i32, _c_i32, _c_i32, _c_i32,
                                             _c_p]
+    lib.sbl_quant_weights_batch_ex.restype = ctypes.c_int
+    lib.sbl_quant_weights_batch_ex.argtypes = [ctypes.POINTER(QuantItem), _c_i32, _c_i32, _c_i32, _c_i32,
+                                               _c_i32, _c_p]
     lib.sbl_pack.restype = ctypes.c_int
     lib.sbl_pack.argtypes = [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p]
     lib.sbl_quant_acts.restype = ctypes.c_int
@@ -182,7 +187,7 @@ def _nbytes(t):
     return t.numel() * t.element_size() if t is not None else 0
 
 
-def sbl_quant_weights_batch(items, n: int, m: int, fmt: int = SBL_FMT_DENSE2, stream=None):
+def sbl_quant_weights_batch(items, n: int, m: int, fmt: int = SBL_FMT_DENSE2, stream=None, flags: int = 0):
     """items: sequence of dicts with keys w (BF16 [n_out][k]), beta, workspace and the
     optional outputs mask_bits, codes, packed, meta (as in sbl_quant_weights)."""
     lib = load()
@@ -201,8 +206,12 @@ def sbl_quant_weights_batch(items, n: int, m: int, fmt: int = SBL_FMT_DENSE2, st
             _ptr(packed, torch.uint8, max(pb, 0), "packed"),
             _ptr(it.get("meta"), torch.uint8, mb, "meta") if fmt == SBL_FMT_NM else None,
             _ptr(ws, None, lib.sbl_workspace_bytes(n_out, k), "workspace"), _nbytes(ws))
-    _check("sbl_quant_weights_batch",
-           lib.sbl_quant_weights_batch(arr, len(items), n, m, fmt, _stream(stream)))
+    if flags:
+        _check("sbl_quant_weights_batch_ex",
+               lib.sbl_quant_weights_batch_ex(arr, len(items), n, m, fmt, flags, _stream(stream)))
+    else:
+        _check("sbl_quant_weights_batch",
+               lib.sbl_quant_weights_batch(arr, len(items), n, m, fmt, _stream(stream)))
 
 
 def sbl_pack(codes, mask_bits, n: int, m: int, fmt: int, packed, meta=None, stream=None):

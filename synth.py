@@ -102,6 +102,18 @@ def plant_ties(bits: np.ndarray, rng, m: int = 8, frac_exact: float = 0.25,
     return b.reshape(bits.shape)
 
 
+def rare_mixture(rng, n_out: int, k: int) -> np.ndarray:
+    """BF16 bit patterns drawn in five equal parts: zeros, subnormals, tiny
+    normals (below 2^-31), mid-range normals and large values up to 2^127,
+    each with a random sign.  Stresses every range of the scale sums."""
+    kind = rng.integers(0, 5, (n_out, k))
+    mag = np.select([kind == 0, kind == 1, kind == 2, kind == 3],
+                    [0, rng.integers(1, 0x80, (n_out, k)), rng.integers(0x0080, 0x3000, (n_out, k)),
+                     rng.integers(0x3000, 0x4000, (n_out, k))],
+                    rng.integers(0x4000, 0x7F00, (n_out, k)))
+    return (mag | (rng.integers(0, 2, (n_out, k)) << 15)).astype(np.uint16)
+
+
 def gaussian_acts(rng, m_tok: int, k: int, hot_channels: int = 0, hot_scale: float = 20.0,
                   t_row_frac: float = 0.0, t_nu: float = 4.0) -> np.ndarray:
     x = rng.standard_normal((m_tok, k), dtype=np.float32)

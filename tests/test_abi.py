@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.sbl_abi_version() == 3
+    assert lib.sbl_abi_version() == 4
     for st in range(7):
         assert len(lib.sbl_status_string(st)) > 0
     assert lib.sbl_last_hip_error() == 0
@@ -165,6 +165,23 @@ def test_quant_weights_batch_validation(lib):
     assert call([item()], n=9) == 4
     assert call([item()], fmt=2) == 4
     assert call([item(), item(w_bf16=A + 2, workspace=A + 2 * ws)]) == 3
+
+    # the variant entry point: flags are checked first, then the same item checks
+    fx = lib.sbl_quant_weights_batch_ex
+
+    def call_ex(items, flags, n=6, m=8, fmt=1):
+        arr = (QuantItem * len(items))(*items)
+        return fx(arr, len(items), n, m, fmt, flags, None)
+
+    assert call_ex([item()], 4) == 4                               # unknown bit
+    assert call_ex([item()], -1) == 4
+    assert call_ex([item()], 3) == 4                               # the two variants exclude each other
+    assert fx(None, 1, 6, 8, 1, 1, None) == 1
+    for flags in (0, 1, 2):
+        assert call_ex([item()], flags, n=9) == 4
+        assert call_ex([item(), item(k=96)], flags) == 2
+        assert call_ex([item(), item(workspace=A + ws - 16)], flags) == 6
+        assert call_ex([item(), item(w_bf16=A + 2, workspace=A + 2 * ws)], flags) == 3
 
 
 @pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation runs only on GPU-less hosts")

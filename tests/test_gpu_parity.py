@@ -230,15 +230,6 @@ def test_gemm24_edge_shapes(n_out, k, m_tok):
     compare_all(gpu_forward(bits, x, 2, 4, FMT_NM), oracle_forward(bits, x, 2, 4), FMT_NM, n_out)
 
 
-def _rare_mixture(rng, n_out, k):
-    kind = rng.integers(0, 5, (n_out, k))
-    mag = np.select([kind == 0, kind == 1, kind == 2, kind == 3],
-                    [0, rng.integers(1, 0x80, (n_out, k)), rng.integers(0x0080, 0x3000, (n_out, k)),
-                     rng.integers(0x3000, 0x4000, (n_out, k))],
-                    rng.integers(0x4000, 0x7F00, (n_out, k)))
-    return (mag | (rng.integers(0, 2, (n_out, k)) << 15)).astype(np.uint16)
-
-
 @pytest.mark.parametrize("fmt,n,m", [(FMT_DENSE2, 6, 8), (FMT_NM, 6, 8), (FMT_NM, 2, 4), (FMT_NM, 5, 8)])
 def test_quant_weights_batch_matches_oracle(fmt, n, m):
     """Grouped weight preparation (10 matrices: two launch groups) gives the
@@ -247,11 +238,11 @@ def test_quant_weights_batch_matches_oracle(fmt, n, m):
     import torch
     from sparse_linear_layers_absmean_amd import sbl
     rng = np.random.default_rng([31, fmt, n, m])
-    mats = [synth.gaussian_masters(rng, 96, 128), _rare_mixture(rng, 64, 512),
+    mats = [synth.gaussian_masters(rng, 96, 128), synth.rare_mixture(rng, 64, 512),
             synth.gaussian_masters(rng, 200, 320), synth.gaussian_masters(rng, 1, 64),
             synth.plant_ties(synth.gaussian_masters(rng, 130, 512), rng),
             synth.gaussian_masters(rng, 1536, 512, outlier_frac=0.01),
-            _rare_mixture(rng, 3, 1024), synth.gaussian_masters(rng, 17, 256),
+            synth.rare_mixture(rng, 3, 1024), synth.gaussian_masters(rng, 17, 256),
             synth.gaussian_masters(rng, 640, 3200), synth.gaussian_masters(rng, 48, 128)]
     items = []
     for bits in mats:

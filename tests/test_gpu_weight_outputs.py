@@ -28,16 +28,6 @@ PATTERNS = [(FMT_DENSE2, 6, 8), (FMT_NM, 6, 8), (FMT_NM, 2, 4), (FMT_DENSE2, 3, 
             (FMT_NM, 5, 8)]
 
 
-def _rare_mixture(rng, n_out, k):
-    """Zeros, subnormals, tiny, fast-window and large magnitudes in equal parts."""
-    kind = rng.integers(0, 5, (n_out, k))
-    mag = np.select([kind == 0, kind == 1, kind == 2, kind == 3],
-                    [0, rng.integers(1, 0x80, (n_out, k)), rng.integers(0x0080, 0x3000, (n_out, k)),
-                     rng.integers(0x3000, 0x4000, (n_out, k))],
-                    rng.integers(0x4000, 0x7F00, (n_out, k)))
-    return (mag | (rng.integers(0, 2, (n_out, k)) << 15)).astype(np.uint16)
-
-
 def _item(bits, outs, fmt, n, m):
     import torch
     from sparse_linear_layers_absmean_amd import sbl
@@ -91,7 +81,7 @@ def _run(mats, subsets, fmt, n, m, label):
 def test_output_subsets(fmt, n, m, subset):
     rng = np.random.default_rng([57, fmt, n, m, len(subset)])
     mats = [synth.gaussian_masters(rng, 300, 1024),
-            _rare_mixture(rng, 256, 1024),                # several workgroups of both passes flagged
+            synth.rare_mixture(rng, 256, 1024),                # several workgroups of both passes flagged
             synth.plant_ties(synth.gaussian_masters(rng, 130, 1536), rng)]
     _run(mats, [subset] * 3, fmt, n, m, subset)
 
@@ -101,7 +91,7 @@ def test_mixed_output_batches(fmt, n, m):
     """Items of one batch with different output sets (a beta-only item gets
     its beta from the mask/pack launch of the others)."""
     rng = np.random.default_rng([58, fmt, n, m])
-    mats = [synth.gaussian_masters(rng, 200, 512), _rare_mixture(rng, 96, 1024),
+    mats = [synth.gaussian_masters(rng, 200, 512), synth.rare_mixture(rng, 96, 1024),
             synth.gaussian_masters(rng, 64, 256), synth.gaussian_masters(rng, 33, 320)]
     _run(mats, ["packed", "beta", "mask", "codes"], fmt, n, m, "mixed, one beta-only")
     _run(mats, ["packed", "mask+packed", "mask", "packed"], fmt, n, m, "mixed")
