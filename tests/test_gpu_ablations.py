@@ -10,6 +10,8 @@ sbl_quant_weights_batch_ex, against the oracle bit for bit:
 Every output (beta, mask bitmap, codes, packed stream, meta) is compared; each
 case runs twice on the same workspaces (filled with 0xFF bytes first)."""
 
+import math
+
 import numpy as np
 import pytest
 
@@ -119,3 +121,43 @@ def test_flags_rejected():
             sbl.sbl_quant_weights_batch([it], 6, 8, FMT_NM, flags=flags)
     torch.cuda.synchronize()
     assert to_np(it["beta"])[0] == -1.0                   # nothing ran
+
+
+def _binomial_zero_fraction(n, m, p):
+    """Zero-code fraction after an n:m mask when each code of a group is
+    nonzero independently with probability p: the mask keeps min(n, B) of the
+    B nonzero codes (they are the largest magnitudes, or the largest |code|)."""
+    e_kept = sum(min(n, b) * math.comb(m, b) * p ** b * (1 - p) ** (m - b) for b in range(m + 1))
+    return 1 - e_kept / m
+
+
+@pytest.mark.parametrize("flag", [0, QW_BETA_KEPT, QW_MASK_FROM_CODES])
+def test_sparsity_sweep(flag):
+    """The pages' sparsity sweep 8:8 ... 2:8 (and 2:4) on one Gaussian matrix:
+    every output bit-exact with the oracle, and the zero-code fraction of the
+    GPU codes at the binomial closed form where it applies (the method's order
+    and masks from codes; mask-then-quant has a different scale)."""
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    rng = np.random.default_rng([65, flag])
+    bits = synth.gaussian_masters(rng, 512, 2048)
+    p = 1 - math.erf(1 / (2 * math.sqrt(math.pi)))     # P(code != 0) for Gaussian masters
+    order = ORDER.get(flag, O.QUANT_THEN_MASK)
+    fracs = []
+    for n, m in [(8, 8), (7, 8), (6, 8), (5, 8), (4, 8), (3, 8), (2, 8), (2, 4)]:
+        it = _item(bits, FMT_NM, n, m)
+        say(f"sweep flag={flag} {n}:{m}")
+        sbl.sbl_quant_weights_batch([it], n, m, FMT_NM, flags=flag)
+        torch.cuda.synchronize()
+        beta, keep, codes = O.quant_weights(bits, n, m, order)
+        g_codes = to_np(it["codes"])
+        assert to_np(it["beta"])[0] == beta
+        assert np.array_equal(g_codes, codes)
+        assert np.array_equal(to_np(it["mask_bits"]), O.pack_bitmap(keep))
+        zf = float((g_codes == 0).mean())
+        say(f"  zero fraction {zf:.4f}")
+        if flag != QW_BETA_KEPT:
+            assert abs(zf - _binomial_zero_fraction(n, m, p)) < 3e-3
+        if m == 8:
+            fracs.append(zf)
+    assert all(a < b for a, b in zip(fracs, fracs[1:]))  # sparser patterns zero more codes
