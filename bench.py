@@ -174,11 +174,11 @@ def main():
         src = outs[c] if pool is None else pool
         return [dict(src[i], xq=acts[c][gi]["xq"], gamma=acts[c][gi]["gamma"]) for i in groups[gi]]
 
-    def qw_all(c):
+    def qw_all(c, flags=0):
         sbl.sbl_quant_weights_batch(
             [dict(w=masters[c][i], beta=outs[c][i]["beta"], packed=outs[c][i]["packed"],
                   meta=outs[c][i]["meta"], workspace=wss[c][i]) for i in range(len(mats))],
-            n, m, fmt)
+            n, m, fmt, flags=flags)
 
     def qa_all(c):
         for gi in range(len(groups)):
@@ -252,12 +252,14 @@ def main():
             sbl.sbl_linear_batch(items_of(c % copies, gi, gemv_pool[c % gemv_copies]), fmt, n, m)
 
     qw_graphs = [capture(lambda c=c: qw_all(c)) for c in range(copies)]
+    qw2_graphs = [capture(lambda c=c: qw_all(c, sbl.SBL_QW_TWO_PASS)) for c in range(copies)]
     qa_graphs = [capture(lambda c=c: qa_all(c)) for c in range(copies)]
     lin_graphs = [capture(lambda c=c: lin_all(c)) for c in range(gemv_copies)]
     la_graphs = [capture(lambda c=c: la_all(c % copies, gemv_pool[c % gemv_copies])) for c in range(gemv_copies)]
 
     reps = max(20, args.steps)
     qw_ms = time_graphs(qw_graphs, reps)
+    qw2_ms = time_graphs(qw2_graphs, reps)
     qa_ms = time_graphs(qa_graphs, reps)
     lin_ms = time_graphs(lin_graphs, max(reps, 2 * gemv_copies))
     la_ms = time_graphs(la_graphs, max(reps, 2 * gemv_copies))
@@ -270,9 +272,11 @@ def main():
 
     # the step's two calls, then (for reference) the same work as separate calls
     per_call = {
-        "sbl_quant_weights": roof(qw_bytes, qw_ms, "sbl_quant_weights_batch over the 7 matrices: "
-                                  "absmean_partial + mask_pack kernels (beta finalized inside mask_pack)", 1,
-                                  recorded_traffic("sbl_quant_weights", args.workload, args.fmt)),
+        "sbl_quant_weights": roof(qw_bytes, qw_ms, "sbl_quant_weights_batch over the 7 matrices in one launch: "
+                                  "resident_kernel (masters held in registers while the exact beta completes)",
+                                  1, recorded_traffic("sbl_quant_weights", args.workload, args.fmt)),
+        "sbl_quant_weights_two_pass": roof(qw_bytes, qw2_ms, "the same call with SBL_QW_TWO_PASS: "
+                                           "absmean_partial + mask_pack kernels (masters read twice)", 1),
         "sbl_linear_acts_batch": roof(qa_bytes + lin_bytes, la_ms,
                                       "gemv_kernel with the activation quantization fused in "
                                       "(grouped: qkv, o, gate+up, down)", len(groups)),

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SBL_ABI_VERSION 4
+#define SBL_ABI_VERSION 5
 
 typedef enum {
   SBL_OK = 0,
@@ -160,7 +160,11 @@ typedef struct {
 } sbl_quant_item;
 
 /* Weight preparation of several matrices (e.g. the seven of one transformer
- * block) in two launches per 8 matrices instead of two per matrix.
+ * block) in two launches per 8 matrices instead of two per matrix, or in one
+ * when the 8 (or fewer) matrices fit on the chip at once (about 33M weights
+ * on MI355X; patterns dropping at most 2 of a group).  The one-launch path
+ * keeps the masters in registers while beta is completed, so it reads them
+ * once instead of twice.
  * `items` is a HOST array of `count` (1..256) descriptors sharing the pattern
  * n:m and `fmt`; each is validated as sbl_quant_weights validates its
  * arguments, and workspaces must not overlap (SBL_ERR_WORKSPACE), all before
@@ -182,11 +186,24 @@ int sbl_quant_weights_batch(const sbl_quant_item* items, int32_t count, int32_t 
  *                           (codes from beta over every weight; equal |code|
  *                           goes to the lower index) instead of the n largest
  *                           master magnitudes.
- * The two are exclusive; other bits or both together give SBL_ERR_UNSUPPORTED
- * before anything is checked or enqueued.  Outputs and formats are those of
+ * The two are exclusive.  Outputs and formats are those of
  * sbl_quant_weights_batch.  The variants run slower kernels (per-key
- * selection) than the method's own path. */
-enum { SBL_QW_DEFAULT = 0, SBL_QW_BETA_KEPT = 1, SBL_QW_MASK_FROM_CODES = 2 };
+ * selection) than the method's own path, always in two launches.
+ * Two more bits select how the method itself runs (same results, bit for bit):
+ *   SBL_QW_TWO_PASS         always the two-launch path.
+ *   SBL_QW_NO_WAIT          one-launch path: no workgroup waits for another's
+ *                           partial sum; each computes the ones not yet there
+ *                           from the masters (the fallback that bounds every
+ *                           wait, forced; for testing).
+ * Unknown bits, or BETA_KEPT with MASK_FROM_CODES, give SBL_ERR_UNSUPPORTED
+ * before anything is checked or enqueued. */
+enum {
+  SBL_QW_DEFAULT = 0,
+  SBL_QW_BETA_KEPT = 1,
+  SBL_QW_MASK_FROM_CODES = 2,
+  SBL_QW_TWO_PASS = 4,
+  SBL_QW_NO_WAIT = 8
+};
 int sbl_quant_weights_batch_ex(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m,
                                int32_t fmt, int32_t flags, sbl_stream stream);
 

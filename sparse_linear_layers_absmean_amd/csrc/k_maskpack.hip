@@ -32,7 +32,7 @@
 // DENSE2 word layout: see d2_shift.
 // beta itself is finalized at the start of every workgroup from the absmean
 // pass's partial sums (sbl_beta.h), while the first chunk loads are in flight.
-#include "sbl_beta.h"
+#include "sbl_partial.h"
 #include "sbl_select.h"
 
 namespace sbl {
@@ -222,9 +222,12 @@ __device__ __forceinline__ uint32_t remove_field(uint32_t x, uint32_t pos) {
   return (x & low) | ((x >> 2) & ~low);
 }
 
-// FMT: format computed for `packed` (0 DENSE2, 1 N:M); CODES: int8 codes wanted
-template <int M, int DROP, int FMT, bool CODES>
-__device__ __forceinline__ void mask_pack_chunk(const uint32_t (&dw)[32], int64_t c, const QDesc& d, uint32_t t2) {
+// FMT: format computed for `packed` (0 DENSE2, 1 N:M); CODES: int8 codes wanted;
+// PRESEL: the keep bits are given (keep64, bit j = weight j of the chunk)
+// instead of selected here.  get_words(g, W) supplies the M/2 words of group g.
+template <int M, int DROP, int FMT, bool CODES, bool PRESEL, class GetWords>
+__device__ __forceinline__ void mask_pack_chunk_from(GetWords get_words, int64_t c, const QDesc& d, uint32_t t2,
+                                                     uint64_t keep64) {
   constexpr int N = M - DROP, WPG = M / 2;
   constexpr bool want_d2 = FMT == 0, want_nm = FMT == 1, want_codes = CODES;
   const uint32_t ones = opaque(kOnes);
@@ -232,11 +235,18 @@ __device__ __forceinline__ void mask_pack_chunk(const uint32_t (&dw)[32], int64_
   uint32_t nmw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int g = 0; g < 64 / M; ++g) {
-    const uint32_t* W = dw + g * WPG;
+    uint32_t W[WPG];
+    get_words(g, W);
     uint32_t A[WPG], F[WPG];
 #pragma unroll
     for (int i = 0; i < WPG; ++i) A[i] = W[i] & 0x7FFF7FFFu;
-    const uint32_t keep = select_keep<M, DROP>(A, F, ones);
+    uint32_t keep;
+    if constexpr (PRESEL) {
+      keep = (uint32_t)(keep64 >> (g * M)) & ((1u << M) - 1u);
+      scatter_bits<M>(keep, F);
+    } else {
+      keep = select_keep<M, DROP>(A, F, ones);
+    }
     o.keep |= (uint64_t)keep << (g * M);
     // per half: index = G + 2*sign, G = (kept and mag > t); u = c + 1 = {1, 2, 1, 0}[index]
     uint32_t X[WPG];
@@ -268,6 +278,17 @@ __device__ __forceinline__ void mask_pack_chunk(const uint32_t (&dw)[32], int64_
   o.nm_lo = (uint64_t)nmw[0] | ((uint64_t)nmw[1] << 32);
   o.nm_hi = (uint64_t)nmw[2] | ((uint64_t)nmw[3] << 32);
   store_outputs<N, M>(o, c, N, d.mask, d.codes, FMT, d.packed, d.meta, d.n_out, d.nkb);
+}
+
+// The same for a chunk held in registers (word i = weights 2i, 2i+1).
+template <int M, int DROP, int FMT, bool CODES>
+__device__ __forceinline__ void mask_pack_chunk(const uint32_t (&dw)[32], int64_t c, const QDesc& d, uint32_t t2) {
+  mask_pack_chunk_from<M, DROP, FMT, CODES, false>(
+      [&](int g, uint32_t* W) {
+#pragma unroll
+        for (int i = 0; i < M / 2; ++i) W[i] = dw[g * (M / 2) + i];
+      },
+      c, d, t2, 0);
 }
 
 // A workgroup takes kCPT consecutive groups of kThreads chunks; the next
@@ -324,6 +345,291 @@ void launch_fast(const QBatch& b, hipStream_t s) {
   else if (nm) launch_fast_kernel<M, DROP, 1, false>(b, s);
   else if (codes) launch_fast_kernel<M, DROP, 0, true>(b, s);
   else launch_fast_kernel<M, DROP, 0, false>(b, s);
+}
+
+// ---------------------------------------------------------------- resident: one launch
+// The whole weight preparation of a batch in one launch, for batches whose
+// masters fit in the registers of one round of workgroups (the two-pass path
+// reads them twice: beta must be complete before any code is known).
+// Workgroup j of a matrix holds chunks [cpw j, cpw j + cpw) in registers
+// (cpw = d.vpt <= 1024; thread t: 16-byte vectors t + 256u, u < 32, so each
+// load instruction of a wave reads 1 KB contiguous), adds their magnitudes exactly, publishes its
+// partial sum in slot j (sbl_partial.h) and then waits until every slot of
+// its matrix is complete for this call.  The N:M selection does not depend on
+// beta, so it is made in the first phase, vector by vector as the loads
+// arrive (a 16-byte vector is one group of 8, or two of 4).  Then beta is
+// finalized per wave (sbl_beta.h) and the chunks, with their keep bits, go
+// through LDS (the same swizzled layout as the LDS-direct staging above) to
+// the mask/pack code of the two-pass kernel, minus its selection.
+//
+// Completion of a slot for a call (no workspace initialization needed, and
+// graph replays of one launch stay distinct):
+//  * the workspace holds a generation word; a workgroup reads it at its start
+//    and targets e = generation + 1;
+//  * a slot is complete for target e when its tag equals tag(e, matrix, slot),
+//    a bijection of e for a fixed slot (tags of earlier calls differ);
+//  * every workspace word is stored and loaded as a relaxed agent-scope
+//    atomic (coherent across the XCDs' L2 caches without cache-wide
+//    writebacks or invalidates, which would serialize over hundreds of
+//    workgroups); the slot's owner stores the sum and record, waits until
+//    those stores are complete (s_waitcnt vmcnt(0)), then stores the tag, so
+//    a waiter that has seen the tag reads the sum and record it tags;
+//  * the wait is bounded: after max_polls polls a workgroup computes the
+//    missing partial sums itself from the masters, stores and tags them.  The
+//    sums are exact, so every writer of a slot writes the same bits, and a
+//    result never depends on who computed it.  (The host launches this
+//    kernel only when the occupancy of the chip holds every workgroup at
+//    once; the bound covers the case where other work delays some of them.)
+//  * after its wait, workgroup 0 of the matrix, and every workgroup that
+//    computed a missing sum, moves the generation from e - 1 to e (compare
+//    and swap).  Every owner has read the generation before its tag exists,
+//    so no workgroup that waits on its own reads it after the move; a late
+//    one (started after the move) targets e + 1, completes every slot for it
+//    (waiting or computing) and moves the generation on.  The next call thus
+//    always targets a value above every tag written so far.
+constexpr int kResR = kResChunksPerThread;        // chunks per thread held in registers
+constexpr int kResChunks = kThreads * kResR;      // chunks per workgroup
+static_assert(kResChunks == kResChunksPerWg, "resident partition");
+constexpr int kResMaxSlots = beta::kWaveSlots;    // slots per matrix (the per-wave finalize)
+
+__device__ __forceinline__ uint64_t res_tag(uint64_t e, const QDesc& d, int64_t slot) {
+  uint64_t x = e + ((uint64_t)(uintptr_t)d.w ^ ((uint64_t)slot * 0x9E3779B97F4A7C15ull));
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;     // odd multipliers and xor-shifts: bijective
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return x ^ (x >> 31);
+}
+
+__device__ __forceinline__ uint64_t load_agent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The tag store of a slot whose sum and record this thread has just stored:
+// they are complete before the tag is written.
+__device__ __forceinline__ void res_store_tag(uint64_t* p, uint64_t tag) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  beta::ws_store<true>(p, tag);
+}
+
+// Slot j's partial sum straight from the masters (a workgroup that stopped
+// waiting for it); stores and tags it like its owner.  All threads call it.
+__device__ __forceinline__ void res_compute_slot(const QDesc& d, int64_t j, uint64_t tag, unsigned long long* bins) {
+  const int64_t nchunks = d.nvec / 8, c0 = j * d.vpt;
+  const int64_t span = nchunks - c0 < d.vpt ? nchunks - c0 : d.vpt;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(d.w + 8 * c0, span * 128);
+  __syncthreads();                                   // earlier users of bins are done
+  bins[threadIdx.x] = 0;
+  __syncthreads();
+  double acc0 = 0.0, acc1 = 0.0;
+  uint32_t rare = 0;
+#pragma unroll 1
+  for (int u = 0; u < 8 * kResR; u += 4) {
+    u32x4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rw, (threadIdx.x + kThreads * (u + q)) * 16, 0, 0));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) part::consume(v[q], acc0, acc1, bins, rare);
+  }
+  part::publish_partial<true>(d.ws, d.nb, j, acc0, acc1, rare, bins);
+  if (threadIdx.x == 0) res_store_tag(d.ws + ws_res_gen(d.nb) + 1 + j, tag);
+}
+
+template <int M, int DROP, int FMT, bool CODES>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void resident_kernel(
+    const QBatch batch, uint32_t max_polls) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads * 128];
+  __shared__ __attribute__((aligned(8))) uint8_t kstage[kThreads * 8];   // keep bits of the staged chunks
+  __shared__ unsigned long long bins[256];
+  __shared__ unsigned long long missing[kResMaxSlots / 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int di = find_item(batch);
+  const QDesc& d = batch.d[di];
+  const int64_t slot = (int64_t)blockIdx.x - batch.start[di];
+  const int64_t c0 = slot * d.vpt;
+  const int64_t span = d.nvec / 8 - c0 < d.vpt ? d.nvec / 8 - c0 : d.vpt;
+  const int64_t cend = c0 + span;                    // this workgroup's chunks: [c0, cend)
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(d.w + 8 * c0, span * 128);
+  uint64_t* const gen = d.ws + ws_res_gen(d.nb);
+  uint64_t* const tags = gen + 1;
+  bins[tid] = 0;
+  __syncthreads();
+  const uint64_t e = load_agent(gen) + 1;            // this call's target
+  u32x4 v[8 * kResR];
+#pragma unroll
+  for (int u = 0; u < 8 * kResR; ++u)
+    v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (tid + kThreads * u) * 16, 0, kNt));
+  // the magnitudes join the exact sum as the vectors arrive, and the sum is
+  // published at once; the N:M selection (which beta does not affect) is made
+  // after that, while the other workgroups' sums are still on their way (a
+  // vector is one group of 8, or two groups of 4)
+  double acc0 = 0.0, acc1 = 0.0;
+  uint32_t rare = 0;
+#pragma unroll
+  for (int u = 0; u < 8 * kResR; ++u)
+    if (u < 8 || 32 * u + (tid >> 3) < span) part::consume(v[u], acc0, acc1, bins, rare);
+  part::publish_partial<true>(d.ws, d.nb, slot, acc0, acc1, rare, bins);
+  if (tid == 0) res_store_tag(tags + slot, res_tag(e, d, slot));
+  uint32_t kp[2 * kResR] = {};                       // keep bits of vector u: byte u % 4 of kp[u / 4]
+  {
+    const uint32_t ones = opaque(kOnes);
+#pragma unroll
+    for (int u = 0; u < 8 * kResR; ++u) {
+      if (u >= 8 && 32 * u + (tid >> 3) >= span) continue;   // past this workgroup's chunks
+      uint32_t A[4], F[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) A[i] = v[u][i] & 0x7FFF7FFFu;
+      uint32_t keep;
+      if constexpr (M == 8) keep = select_keep<8, DROP>(A, F, ones);
+      else keep = select_keep<4, DROP>(A, F, ones) | (select_keep<4, DROP>(A + 2, F + 2, ones) << 4);
+      kp[u >> 2] |= keep << (8 * (u & 3));
+    }
+  }
+  // wave 0 waits for the other slots (lane l: slots l + 64u).  A lane polls
+  // only the tags it has not yet seen complete, and the wave backs off while
+  // many are missing: every workgroup of a matrix polls the same few lines,
+  // and early finishers would otherwise load them while the masters stream.
+  if (tid < 64) {
+    uint32_t polls = 0, lane_miss = 0;
+#pragma unroll
+    for (int u = 0; u < kResMaxSlots / 64; ++u)
+      if (lane + 64 * u < d.nb) lane_miss |= 1u << u;
+    for (;;) {
+      uint64_t t[kResMaxSlots / 64];                 // the loads in flight together, then the compares
+#pragma unroll
+      for (int u = 0; u < kResMaxSlots / 64; ++u)
+        t[u] = ((lane_miss >> u) & 1u) ? load_agent(tags + lane + 64 * u) : 0ull;
+#pragma unroll
+      for (int u = 0; u < kResMaxSlots / 64; ++u)
+        if (((lane_miss >> u) & 1u) && t[u] == res_tag(e, d, lane + 64 * u)) lane_miss &= ~(1u << u);
+      const unsigned long long waiting = __ballot(lane_miss != 0);
+      if (waiting == 0 || polls >= max_polls) break;   // uniform in the wave
+      ++polls;
+      if (__popcll(waiting) > 8) __builtin_amdgcn_s_sleep(32);   // ~2000 cycles
+      else __builtin_amdgcn_s_sleep(2);
+    }
+#pragma unroll
+    for (int u = 0; u < kResMaxSlots / 64; ++u) {
+      const unsigned long long mu = __ballot((lane_miss >> u) & 1u);
+      if (lane == 0) missing[u] = mu;
+    }
+  }
+  __syncthreads();
+  bool helped = false;
+#pragma unroll 1
+  for (int u = 0; u < kResMaxSlots / 64; ++u) {
+    unsigned long long mu = missing[u];
+    while (mu) {                                     // uniform: LDS value
+      const int64_t j = 64 * u + __ffsll(mu) - 1;
+      mu &= mu - 1;
+      res_compute_slot(d, j, res_tag(e, d, j), bins);
+      helped = true;
+    }
+  }
+  __syncthreads();                                   // every slot is tagged for e (seen or computed)
+  if (tid == 0 && (slot == 0 || helped)) {
+    uint64_t expected = e - 1;
+    __hip_atomic_compare_exchange_strong(gen, &expected, e, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const float b = fmaxf(beta::finish_beta<true>(d, beta::load_slots<true>(d), slot == 0), 1e-5f);
+  if (!d.mask && !d.codes && !d.packed) return;      // beta only (uniform)
+  const uint32_t t2 = (__float_as_uint(b * 0.5f) >> 16) * kOnes;   // |w| > beta_eff/2 <=> mag > t
+  const uint32_t sw = (uint32_t)(tid >> 3) & 7u;
+#pragma unroll
+  for (int g = 0; g < kResR; ++g) {
+    if (c0 + (int64_t)g * kThreads >= cend) break;      // uniform
+    if (g) __syncthreads();                           // the previous group has been read
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {                     // vector tid + 256(8g + q): row 32q + tid/8, piece tid%8
+      const int u = 8 * g + q;
+      const uint32_t r = 32u * q + ((uint32_t)tid >> 3), pc = (uint32_t)tid & 7u;
+      *reinterpret_cast<u32x4*>(&stage[r * 128u + 16u * (pc ^ sw)]) = v[u];
+      kstage[r * 8u + pc] = (uint8_t)(kp[u >> 2] >> (8 * (u & 3)));
+    }
+    __syncthreads();
+    const uint2 kk = *reinterpret_cast<const uint2*>(&kstage[tid * 8]);
+    const int64_t c = c0 + (int64_t)g * kThreads + tid;
+    // this thread's chunk is row tid of the stage (piece p at 16 (p ^ tid % 8));
+    // group q of it is read when needed
+    const uint8_t* row = stage + tid * 128u;
+    if (c < cend)
+      mask_pack_chunk_from<M, DROP, FMT, CODES, true>(
+          [&](int q, uint32_t* W) {
+            const uint32_t off = 16u * ((uint32_t)(q * M / 8) ^ ((uint32_t)tid & 7u)) + (M == 4 ? 8u * (q & 1) : 0u);
+            if constexpr (M == 8) {
+              const u32x4 x = *reinterpret_cast<const u32x4*>(row + off);
+              W[0] = x[0]; W[1] = x[1]; W[2] = x[2]; W[3] = x[3];
+            } else {
+              const uint2 x = *reinterpret_cast<const uint2*>(row + off);
+              W[0] = x.x; W[1] = x.y;
+            }
+          },
+          c, d, t2, (uint64_t)kk.x | ((uint64_t)kk.y << 32));
+  }
+}
+
+// Partition of a batch over `cap` co-resident workgroups: every matrix gets
+// whole workgroups of cpw chunks, cpw the same for the batch and as small as
+// the co-resident workgroups allow, so that every CU gets about the same
+// share of the loads and of the selection work of the first phase (the
+// slowest workgroup of a matrix holds up all the others); at most
+// kResChunks (registers), and the slots must fit in the workspace.
+bool res_partition(QBatch& b, int64_t cap) {
+  int64_t total = 0;
+  for (int i = 0; i < b.count; ++i) total += b.d[i].nvec / 8;
+  if (cap <= b.count) return false;
+  int64_t cpw = (total + (cap - b.count) - 1) / (cap - b.count);
+  cpw = cpw < kThreads ? kThreads : (cpw + 7) / 8 * 8;
+  if (cpw > kResChunks) return false;
+  int64_t blocks = 0;
+  for (int i = 0; i < b.count; ++i) {
+    const int64_t nb = (b.d[i].nvec / 8 + cpw - 1) / cpw;
+    if (nb > kResMaxSlots || ws_res_words(nb) > b.d[i].ws_words) return false;
+    b.d[i].nb = nb;
+    b.d[i].vpt = cpw;
+    b.start[i] = blocks;
+    blocks += nb;
+  }
+  b.start[b.count] = blocks;
+  return blocks <= cap;
+}
+
+template <int M, int DROP, int FMT, bool CODES>
+bool launch_resident_kernel(QBatch& b, uint32_t max_polls, hipStream_t s, hipError_t* err) {
+  static int capacity[64];                           // co-resident workgroups per device (0: unknown)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (capacity[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, resident_kernel<M, DROP, FMT, CODES>, kThreads, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return false;
+    capacity[dev] = per_cu * cus > 0 ? per_cu * cus : -1;
+  }
+  QBatch r = b;
+  if (!res_partition(r, capacity[dev])) return false;
+  hipLaunchKernelGGL((resident_kernel<M, DROP, FMT, CODES>), dim3((unsigned)r.start[r.count]), dim3(kThreads), 0,
+                     s, r, max_polls);
+  *err = hipGetLastError();
+  b = r;
+  return true;
+}
+
+template <int M, int DROP>
+bool launch_resident_m(QBatch& b, uint32_t max_polls, hipStream_t s, hipError_t* err) {
+  bool codes = false, nm = false;
+  for (int i = 0; i < b.count; ++i) {
+    codes = codes || b.d[i].codes != nullptr;
+    nm = nm || (b.d[i].packed != nullptr && b.d[i].fmt == 1);
+  }
+  if (nm && codes) return launch_resident_kernel<M, DROP, 1, true>(b, max_polls, s, err);
+  if (nm) return launch_resident_kernel<M, DROP, 1, false>(b, max_polls, s, err);
+  if (codes) return launch_resident_kernel<M, DROP, 0, true>(b, max_polls, s, err);
+  return launch_resident_kernel<M, DROP, 0, false>(b, max_polls, s, err);
 }
 
 // Any n (one thread per chunk, one sort key per weight).
@@ -456,6 +762,17 @@ hipError_t launch_mask_pack(QBatch& b, int n, int m, hipStream_t s, bool dry, in
   else if (m == 4 && drop == 1) launch_fast<4, 1>(b, s);
   else if (m == 4 && drop == 2) launch_fast<4, 2>(b, s);
   return hipGetLastError();
+}
+
+bool launch_resident(QBatch& b, int n, int m, uint32_t max_polls, hipStream_t s, hipError_t* err) {
+  const int drop = m - n;
+  if (m == 8 && drop == 0) return launch_resident_m<8, 0>(b, max_polls, s, err);
+  if (m == 8 && drop == 1) return launch_resident_m<8, 1>(b, max_polls, s, err);
+  if (m == 8 && drop == 2) return launch_resident_m<8, 2>(b, max_polls, s, err);
+  if (m == 4 && drop == 0) return launch_resident_m<4, 0>(b, max_polls, s, err);
+  if (m == 4 && drop == 1) return launch_resident_m<4, 1>(b, max_polls, s, err);
+  if (m == 4 && drop == 2) return launch_resident_m<4, 2>(b, max_polls, s, err);
+  return false;
 }
 
 hipError_t launch_pack(const int8_t* codes, const uint8_t* mask, int64_t n_out, int64_t k, int n, int m,

@@ -119,6 +119,7 @@ sbl::QDesc to_qdesc(const sbl_quant_item& it, int32_t fmt) {
   d.vpt = p.vpt;
   d.beta = it.beta;
   d.ws = reinterpret_cast<uint64_t*>(it.workspace);
+  d.ws_words = it.workspace_bytes / 8;
   d.mask = it.mask_bits;
   d.codes = it.codes;
   d.packed = it.packed;
@@ -129,18 +130,25 @@ sbl::QDesc to_qdesc(const sbl_quant_item& it, int32_t fmt) {
   return d;
 }
 
-// Per group of up to kMaxQDesc matrices: the absmean pass, then the
-// mask/pack pass.  Up to about one round of mask/pack workgroups (three per
+// Per group of up to kMaxQDesc matrices: one launch when the group fits on
+// the chip (launch_resident decides; the method's order, at most two dropped
+// per group), else the absmean pass, then the mask/pack pass.  Up to about one round of mask/pack workgroups (three per
 // CU on 256 CUs) each finalizes beta itself, saving a launch; beyond that the
 // repeated finalization would sit on the critical path of every round, so the
 // finalize kernel runs once in between.  A call that wants only beta runs
 // just the finalize kernel.
 constexpr int64_t kPrologueMaxWorkgroups = 1024;
 constexpr int64_t kPrologueMaxSlots = 512;       // every wave loads all partial sums (beta::kWaveSlots)
+// polls of the one-launch kernel's wait for other workgroups' partial sums
+// before it computes them itself (each poll is a memory round trip, ~1 µs)
+constexpr uint32_t kResidentPolls = 1u << 16;
+
 
 int launch_quant(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m, int32_t fmt, int32_t flags,
                  hipStream_t s) {
   const bool kept = (flags & SBL_QW_BETA_KEPT) != 0, mfc = (flags & SBL_QW_MASK_FROM_CODES) != 0;
+  const bool one_launch = (flags & (SBL_QW_BETA_KEPT | SBL_QW_MASK_FROM_CODES | SBL_QW_TWO_PASS)) == 0;
+  const uint32_t polls = (flags & SBL_QW_NO_WAIT) ? 0u : kResidentPolls;
   for (int i0 = 0; i0 < count; i0 += sbl::kMaxQDesc) {
     sbl::QBatch b;
     b.count = count - i0 < sbl::kMaxQDesc ? count - i0 : sbl::kMaxQDesc;
@@ -150,6 +158,14 @@ int launch_quant(const sbl_quant_item* items, int32_t count, int32_t n, int32_t 
       b.d[i] = to_qdesc(items[i0 + i], fmt);
       if (kept) b.d[i].count = b.d[i].count / m * n;   // k % m == 0: exact
       outputs = outputs || b.d[i].mask || b.d[i].codes || b.d[i].packed;
+    }
+    if (one_launch && outputs) {
+      hipError_t err = hipSuccess;
+      if (sbl::launch_resident(b, n, m, polls, s, &err)) {
+        const int st = launch_status(err);
+        if (st != SBL_OK) return st;
+        continue;
+      }
     }
     int64_t grid = 0;
     bool wide = false;                              // a matrix with more than 512 partial sums
@@ -191,8 +207,8 @@ int sbl_quant_weights_batch(const sbl_quant_item* items, int32_t count, int32_t 
 
 int sbl_quant_weights_batch_ex(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m,
                                int32_t fmt, int32_t flags, sbl_stream stream) {
-  if ((flags & ~(SBL_QW_BETA_KEPT | SBL_QW_MASK_FROM_CODES)) != 0 ||
-      flags == (SBL_QW_BETA_KEPT | SBL_QW_MASK_FROM_CODES))
+  if ((flags & ~(SBL_QW_BETA_KEPT | SBL_QW_MASK_FROM_CODES | SBL_QW_TWO_PASS | SBL_QW_NO_WAIT)) != 0 ||
+      (flags & (SBL_QW_BETA_KEPT | SBL_QW_MASK_FROM_CODES)) == (SBL_QW_BETA_KEPT | SBL_QW_MASK_FROM_CODES))
     return SBL_ERR_UNSUPPORTED;
   if (!items) return SBL_ERR_NULL;
   if (count < 1 || count > 256) return SBL_ERR_SHAPE;

@@ -19,6 +19,22 @@ namespace beta {
 
 constexpr uint64_t kRareFlag = 1ull << 63;
 
+// Workspace words are read and written plainly between launches.  Inside the
+// one-launch kernel, where workgroups on different XCDs (each with its own L2)
+// exchange them, they are accessed as relaxed agent-scope atomics instead:
+// those loads and stores are coherent across the XCDs by themselves, with no
+// cache-wide writeback or invalidate.
+template <bool AGENT>
+__device__ __forceinline__ uint64_t ws_load(const uint64_t* p) {
+  if constexpr (AGENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+template <bool AGENT>
+__device__ __forceinline__ void ws_store(uint64_t* p, uint64_t v) {
+  if constexpr (AGENT) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+
 // limbs: little-endian 32-bit words of a nonnegative integer (units of
 // 2^-133); arrays hold kLimbs + 2 words, since add_shifted touches the two
 // words above the one it starts in (the sum itself stays below 2^384)
@@ -106,13 +122,14 @@ struct SlotLoads {
   uint64_t v[kWaveSlots / 64];
 };
 
+template <bool AGENT = false>
 __device__ __forceinline__ SlotLoads load_slots(const QDesc& d) {
   SlotLoads sl;
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int u = 0; u < kWaveSlots / 64; ++u) {
     const int64_t i = lane + 64 * u;
-    sl.v[u] = i < d.nb ? d.ws[i] : 0ull;
+    sl.v[u] = i < d.nb ? ws_load<AGENT>(d.ws + i) : 0ull;
   }
   return sl;
 }
@@ -122,6 +139,7 @@ __device__ __forceinline__ SlotLoads load_slots(const QDesc& d) {
 // flagged slots' records, whose 32-bit limbs are added column by column in
 // LDS (a column sum stays below 2^44); one thread carries the columns into a
 // multi-word integer (units of 2^-133).  All threads call it.
+template <bool AGENT = false>
 __device__ inline float rare_beta(const QDesc& d, unsigned long long lo, unsigned long long hi, bool store) {
   constexpr int kCols = 2 * kWsLimbWords;
   static_assert(kCols == kLimbs, "one column per limb");
@@ -133,10 +151,10 @@ __device__ inline float rare_beta(const QDesc& d, unsigned long long lo, unsigne
   __syncthreads();
   const uint64_t* recs = d.ws + ws_limb_base(d.nb);
   for (int64_t i = tid; i < d.nb; i += kAbsThreads) {
-    if ((d.ws[i] >> 63) == 0) continue;
+    if ((ws_load<AGENT>(d.ws + i) >> 63) == 0) continue;
 #pragma unroll
     for (int j = 0; j < kWsLimbWords; ++j) {
-      const uint64_t w = recs[kWsLimbWords * i + j];
+      const uint64_t w = ws_load<AGENT>(recs + kWsLimbWords * i + j);
       atomicAdd(&cols[2 * j], (unsigned long long)(uint32_t)w);
       atomicAdd(&cols[2 * j + 1], (unsigned long long)(w >> 32));
     }
@@ -158,6 +176,7 @@ __device__ inline float rare_beta(const QDesc& d, unsigned long long lo, unsigne
 // beta of matrix d (unclamped) from slot values every wave loaded
 // (load_slots, nb <= kWaveSlots), returned to every thread.  All threads of
 // the workgroup call it; `store` makes this workgroup write d.beta.
+template <bool AGENT = false>
 __device__ inline float finish_beta(const QDesc& d, const SlotLoads& sl, bool store) {
   // sums split in 32-bit halves so that nothing overflows
   unsigned long long lo = 0, hi = 0;
@@ -173,7 +192,7 @@ __device__ inline float finish_beta(const QDesc& d, const SlotLoads& sl, bool st
     lo += __shfl_xor(lo, off, 64);
     hi += __shfl_xor(hi, off, 64);
   }
-  if (__ballot(flags != 0) != 0) return rare_beta(d, lo, hi, store);   // uniform
+  if (__ballot(flags != 0) != 0) return rare_beta<AGENT>(d, lo, hi, store);   // uniform
   float b = 0.0f;
   if ((threadIdx.x & 63) == 0) b = round_quotient_fast(lo, hi, (uint64_t)d.count);
   b = __shfl(b, 0, 64);

@@ -32,6 +32,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
 //                     written for other workgroups
 __host__ __device__ __forceinline__ int64_t ws_limb_base(int64_t nb) { return (nb + 7) / 8 * 8; }
 constexpr int kWsLimbWords = 6;
+// The one-launch (resident) weight preparation uses the same two regions for
+// its nb slots, then one generation word and nb slot tags (a slot is
+// complete for a call when its tag is that call's; k_maskpack.hip):
+__host__ __device__ __forceinline__ int64_t ws_res_gen(int64_t nb) { return ws_limb_base(nb) + kWsLimbWords * nb; }
+__host__ __device__ __forceinline__ int64_t ws_res_words(int64_t nb) { return ws_res_gen(nb) + 1 + nb; }
+// Its workgroups of 256 threads hold at most 2 chunks of 64 weights per thread.
+constexpr int kResChunksPerThread = 2;
+constexpr int64_t kResChunksPerWg = 256 * kResChunksPerThread;
 
 // Partition of the absmean pass over a matrix of `total` BF16 values: nb
 // workgroups of kAbsThreads threads, vpt 16-byte vectors per thread.  A thread
@@ -83,9 +91,10 @@ struct QDesc {
   const u32x4* w;         // BF16 masters as 16-byte vectors (8 values each)
   int64_t nvec;           // n_out*k/8
   int64_t count;          // values beta averages over: n_out*k, or the kept ones (n_out*k*n/m)
-  int64_t nb, vpt;        // absmean partition (AbsmeanPlan)
+  int64_t nb, vpt;        // absmean partition (AbsmeanPlan); one launch: nb slots of vpt chunks
   float* beta;
   uint64_t* ws;
+  int64_t ws_words;       // workspace size
   uint8_t* mask;          // nullable outputs
   int8_t* codes;
   uint8_t* packed;
@@ -113,6 +122,14 @@ hipError_t launch_absmean_partial(QBatch& batch, hipStream_t s);
 // The mask-then-quant variant: only the magnitudes the n:m mask keeps are summed.
 hipError_t launch_absmean_partial_kept(QBatch& batch, int n, int m, hipStream_t s);
 hipError_t launch_absmean_final(QBatch& batch, hipStream_t s);
+// One launch for the whole weight preparation of a batch that fits on the
+// chip at once (returns false, launching nothing, when it does not or the
+// pattern drops more than two of a group): every thread keeps its masters in
+// registers while the partial sums of its matrix are completed.  max_polls
+// bounds the wait for other workgroups' partial sums; the missing ones are
+// then computed directly (0: at once).  Fills batch.start and sets d.nb to
+// the one-launch partition.
+bool launch_resident(QBatch& batch, int n, int m, uint32_t max_polls, hipStream_t s, hipError_t* err);
 // mask_from_codes: the mask keeps the n largest |code| per group (ties to the
 // lower index) instead of the n largest master magnitudes.
 hipError_t launch_mask_pack(QBatch& batch, int n, int m, hipStream_t s, bool dry = false, int64_t* grid = nullptr,

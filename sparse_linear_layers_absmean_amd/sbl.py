@@ -21,9 +21,10 @@ LIB_PATH = os.path.join(_HERE, "libsbl.so")
 SBL_OK = 0
 SBL_FMT_DENSE2 = 0
 SBL_FMT_NM = 1
-# weight-preparation variants (sbl_quant_weights_batch_ex flags)
+# weight-preparation variants and execution choices (sbl_quant_weights_batch_ex flags)
 SBL_QW_DEFAULT, SBL_QW_BETA_KEPT, SBL_QW_MASK_FROM_CODES = 0, 1, 2
-ABI_VERSION = 4
+SBL_QW_TWO_PASS, SBL_QW_NO_WAIT = 4, 8
+ABI_VERSION = 5
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32

@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.sbl_abi_version() == 4
+    assert lib.sbl_abi_version() == 5
     for st in range(7):
         assert len(lib.sbl_status_string(st)) > 0
     assert lib.sbl_last_hip_error() == 0
@@ -173,11 +173,12 @@ def test_quant_weights_batch_validation(lib):
         arr = (QuantItem * len(items))(*items)
         return fx(arr, len(items), n, m, fmt, flags, None)
 
-    assert call_ex([item()], 4) == 4                               # unknown bit
+    assert call_ex([item()], 16) == 4                              # unknown bit
     assert call_ex([item()], -1) == 4
     assert call_ex([item()], 3) == 4                               # the two variants exclude each other
+    assert call_ex([item()], 3 | 4) == 4
     assert fx(None, 1, 6, 8, 1, 1, None) == 1
-    for flags in (0, 1, 2):
+    for flags in (0, 1, 2, 4, 8, 12, 5, 10):
         assert call_ex([item()], flags, n=9) == 4
         assert call_ex([item(), item(k=96)], flags) == 2
         assert call_ex([item(), item(workspace=A + ws - 16)], flags) == 6

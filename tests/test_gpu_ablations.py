@@ -116,7 +116,7 @@ def test_flags_rejected():
     from sparse_linear_layers_absmean_amd import sbl
     rng = np.random.default_rng(64)
     it = _item(synth.gaussian_masters(rng, 16, 64), FMT_NM, 6, 8)
-    for flags in (3, 4, -1):
+    for flags in (3, 16, -1):
         with pytest.raises(RuntimeError):
             sbl.sbl_quant_weights_batch([it], 6, 8, FMT_NM, flags=flags)
     torch.cuda.synchronize()

@@ -1,9 +1,10 @@
-"""Weight preparation with every subset of outputs.
+"""Weight preparation with every subset of outputs, in one launch (the
+masters held on the chip) and in two (SBL_QW_TWO_PASS).
 
-beta is finalized at the start of the mask/pack pass, or by its own kernel
-when beta is the only output, from the partial sums the absmean pass wrote
-into the workspace (exact out-of-range sums for the workgroups that met
-such values).  Workspaces start out filled with 0xFF bytes (they need no
+In the two-launch path beta is finalized at the start of the mask/pack
+pass, or by its own kernel when beta is the only output, from the partial
+sums the absmean pass wrote into the workspace (exact out-of-range sums for
+the workgroups that met such values).  Workspaces start out filled with 0xFF bytes (they need no
 initialization); each case runs twice on the same workspaces and is compared
 with the oracle bit for bit."""
 
@@ -63,27 +64,29 @@ def _check(bits, g, fmt, n, m):
             assert np.array_equal(meta_rows(g["meta"], n_out, k), O.pack_bitmap(keep))
 
 
-def _run(mats, subsets, fmt, n, m, label):
+def _run(mats, subsets, fmt, n, m, label, flags=0):
     import torch
     from sparse_linear_layers_absmean_amd import sbl
     items = [_item(bits, SUBSETS[s], fmt, n, m) for bits, s in zip(mats, subsets)]
     for rep in range(2):
-        say(f"weight outputs {label} fmt={fmt} {n}:{m} call {rep}")
-        sbl.sbl_quant_weights_batch(items, n, m, fmt)
+        say(f"weight outputs {label} fmt={fmt} {n}:{m} flags={flags} call {rep}")
+        sbl.sbl_quant_weights_batch(items, n, m, fmt, flags=flags)
         torch.cuda.synchronize()
         for bits, it in zip(mats, items):
             g = {key: to_np(v) for key, v in it.items() if key not in ("w", "workspace") and v is not None}
             _check(bits, g, fmt, n, m)
 
 
+# 0: one launch where the batch fits on the chip (all of these); 4: SBL_QW_TWO_PASS
+@pytest.mark.parametrize("flags", [0, 4])
 @pytest.mark.parametrize("subset", list(SUBSETS))
 @pytest.mark.parametrize("fmt,n,m", PATTERNS)
-def test_output_subsets(fmt, n, m, subset):
+def test_output_subsets(fmt, n, m, subset, flags):
     rng = np.random.default_rng([57, fmt, n, m, len(subset)])
     mats = [synth.gaussian_masters(rng, 300, 1024),
             synth.rare_mixture(rng, 256, 1024),                # several workgroups of both passes flagged
             synth.plant_ties(synth.gaussian_masters(rng, 130, 1536), rng)]
-    _run(mats, [subset] * 3, fmt, n, m, subset)
+    _run(mats, [subset] * 3, fmt, n, m, subset, flags)
 
 
 @pytest.mark.parametrize("fmt,n,m", [(FMT_DENSE2, 6, 8), (FMT_NM, 2, 4)])
@@ -93,8 +96,9 @@ def test_mixed_output_batches(fmt, n, m):
     rng = np.random.default_rng([58, fmt, n, m])
     mats = [synth.gaussian_masters(rng, 200, 512), synth.rare_mixture(rng, 96, 1024),
             synth.gaussian_masters(rng, 64, 256), synth.gaussian_masters(rng, 33, 320)]
-    _run(mats, ["packed", "beta", "mask", "codes"], fmt, n, m, "mixed, one beta-only")
-    _run(mats, ["packed", "mask+packed", "mask", "packed"], fmt, n, m, "mixed")
+    for flags in (0, 4):
+        _run(mats, ["packed", "beta", "mask", "codes"], fmt, n, m, "mixed, one beta-only", flags)
+        _run(mats, ["packed", "mask+packed", "mask", "packed"], fmt, n, m, "mixed", flags)
 
 
 @pytest.mark.parametrize("fmt,n,m", [(FMT_NM, 6, 8), (FMT_DENSE2, 2, 4)])
@@ -107,4 +111,6 @@ def test_few_out_of_range_values(fmt, n, m):
     flat = bits.reshape(-1)
     idx = rng.choice(flat.size, 5, replace=False)
     flat[idx] = np.array([0x0001, 0x8123, 0x2F00, 0x4100, 0xC3A5], np.uint16)   # 2^-133 .. 330
-    _run([bits, synth.gaussian_masters(rng, 64, 4096)], ["packed", "mask+packed"], fmt, n, m, "few flagged")
+    for flags in (0, 4):
+        _run([bits, synth.gaussian_masters(rng, 64, 4096)], ["packed", "mask+packed"], fmt, n, m, "few flagged",
+             flags)
