@@ -441,7 +441,7 @@ template <int M, int DROP, int FMT, bool CODES>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void resident_kernel(
     const QBatch batch, uint32_t max_polls) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads * 128];
-  __shared__ __attribute__((aligned(8))) uint8_t kstage[kThreads * 8];   // keep bits of the staged chunks
+  __shared__ __attribute__((aligned(8))) uint8_t kstage[kResR][kThreads * 8];   // keep bits, per chunk row
   __shared__ unsigned long long bins[256];
   __shared__ unsigned long long missing[kResMaxSlots / 64];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -472,8 +472,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (u < 8 || 32 * u + (tid >> 3) < span) part::consume(v[u], acc0, acc1, bins, rare);
   part::publish_partial<true>(d.ws, d.nb, slot, acc0, acc1, rare, bins);
   if (tid == 0) res_store_tag(tags + slot, res_tag(e, d, slot));
-  uint32_t kp[2 * kResR] = {};                       // keep bits of vector u: byte u % 4 of kp[u / 4]
   {
+    // keep bits of vector u (chunk row r = 32 (u % 8) + tid / 8 of group u / 8,
+    // piece tid % 8) go to LDS, read per chunk in the second phase
     const uint32_t ones = opaque(kOnes);
 #pragma unroll
     for (int u = 0; u < 8 * kResR; ++u) {
@@ -484,7 +485,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       uint32_t keep;
       if constexpr (M == 8) keep = select_keep<8, DROP>(A, F, ones);
       else keep = select_keep<4, DROP>(A, F, ones) | (select_keep<4, DROP>(A + 2, F + 2, ones) << 4);
-      kp[u >> 2] |= keep << (8 * (u & 3));
+      kstage[u >> 3][(32u * (u & 7) + ((uint32_t)tid >> 3)) * 8u + ((uint32_t)tid & 7u)] = (uint8_t)keep;
     }
   }
   // wave 0 waits for the other slots (lane l: slots l + 64u).  A lane polls
@@ -547,10 +548,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       const int u = 8 * g + q;
       const uint32_t r = 32u * q + ((uint32_t)tid >> 3), pc = (uint32_t)tid & 7u;
       *reinterpret_cast<u32x4*>(&stage[r * 128u + 16u * (pc ^ sw)]) = v[u];
-      kstage[r * 8u + pc] = (uint8_t)(kp[u >> 2] >> (8 * (u & 3)));
     }
     __syncthreads();
-    const uint2 kk = *reinterpret_cast<const uint2*>(&kstage[tid * 8]);
+    const uint2 kk = *reinterpret_cast<const uint2*>(&kstage[g][tid * 8]);
     const int64_t c = c0 + (int64_t)g * kThreads + tid;
     // this thread's chunk is row tid of the stage (piece p at 16 (p ^ tid % 8));
     // group q of it is read when needed
