@@ -43,6 +43,11 @@ listed with its reason in the design notes):
     storage order of the packed streams in `to_panels`; they are this
     implementation's choice, not the pages'.
 
+Backward (dual straight-through estimator; readings listed with the
+function `backward`): the scales are constants, the incoming gradient is
+BF16, dX passes only where the activation clamp did not act, and dW reaches
+every master (pruned ones included).
+
 Non-finite inputs are a precondition violation: the functions raise.
 
 Pinned by tests/test_oracle_*.py (exact-rational brute force, enumeration of
@@ -411,6 +416,72 @@ def rescale(acc: np.ndarray, beta, gamma: np.ndarray) -> np.ndarray:
 def linear(codes: np.ndarray, q: np.ndarray, beta, gamma: np.ndarray):
     acc = contract(codes, q)
     return acc, rescale(acc, beta, gamma)
+
+
+# --------------------------------------------------------------------------
+# Backward of the layer: the dual straight-through estimator
+#   [SB-es] section 2, "Estrategia de Entrenamiento" (Dual STE: gradients reach
+#   every master weight, the pruned ones included);
+#   [SB-ar] section 2, item 3 (quantization STE: identity inside the clipping
+#   range; mask STE: dense gradient flow to all masters).
+# The scales beta and gamma are treated as constants (no gradient through
+# them), the incoming gradient dY is BF16, and the results are fp32.
+# --------------------------------------------------------------------------
+
+FP32_UNIT = 2.0 ** -24      # unit roundoff of fp32 (round to nearest)
+
+
+def clip_pass(x: np.ndarray, gamma: np.ndarray) -> np.ndarray:
+    """1.0 where the activation quantizer's clamp did not act, else 0.0.
+
+    The quantizer's STE passes the gradient inside the clipping range: where
+    |rint(RN_fp32(128 x / gamma_eff))| <= 127, evaluated exactly as in
+    quant_acts (the same fp32 division and half-to-even rint)."""
+    x = np.asarray(x, dtype=np.float32)
+    g_eff = np.maximum(np.asarray(gamma, dtype=np.float32), EPS_SCALE)
+    s = (g_eff / np.float32(QB)).astype(np.float32)
+    t = np.rint((x / s[:, None]).astype(np.float32))
+    return (np.abs(t) <= Q_CLIP).astype(np.float64)
+
+
+def dequant_acts(q: np.ndarray, gamma: np.ndarray) -> np.ndarray:
+    """x_hat[t, k] = RN_fp32(gamma_eff[t] * q[t, k]) * 2^-7 (fp32): the
+    activation the forward product used, in real terms."""
+    g_eff = np.maximum(np.asarray(gamma, dtype=np.float32), EPS_SCALE)
+    prod = (g_eff[:, None] * np.asarray(q, dtype=np.float32)).astype(np.float32)
+    return (prod * np.float32(1.0 / QB)).astype(np.float32)
+
+
+def backward(codes: np.ndarray, beta, x: np.ndarray, q: np.ndarray, gamma: np.ndarray,
+             dy_bits: np.ndarray, clip: bool = True):
+    """Gradients of the layer y = (beta C) x_hat^T under the dual STE.
+
+      dX[t, k] = beta_eff * sum_n dY[t, n] C[n, k] * clip_pass(x)[t, k]
+      dW[n, k] = sum_t dY[t, n] x_hat[t, k]      for EVERY (n, k), pruned or not
+
+    Returned in float64 (the real values), with elementwise bounds for an
+    fp32 evaluation whose products are exact and whose L-term sums are
+    accumulated in fp32 in any order: |fp32 result - real| <= bound, from
+    |sum error| <= (L - 1) u sum|terms| plus one rounding of the result
+    (u = 2^-24; dW's sums have 3L terms, x_hat being split exactly into three
+    BF16 parts).  Masked dX entries are exactly 0."""
+    c = np.asarray(codes, dtype=np.float64)
+    dy = bf16_to_f32(np.asarray(dy_bits, dtype=np.uint16)).astype(np.float64)
+    if not np.all(np.isfinite(dy)):
+        raise ValueError("non-finite gradient")
+    if dy.shape[1] != c.shape[0]:
+        raise ValueError("n_out mismatch")
+    b = float(beta_eff(beta))
+    n_out, t = c.shape[0], dy.shape[0]
+    s = dy @ c                                          # [m_tok][k]
+    s_abs = np.abs(dy) @ np.abs(c)
+    mask = clip_pass(x, gamma) if clip else np.ones_like(s)
+    dx = b * s * mask
+    dx_bound = (n_out + 1) * FP32_UNIT * b * s_abs * mask
+    xh = dequant_acts(q, gamma).astype(np.float64)
+    dw = dy.T @ xh                                      # [n_out][k]
+    dw_bound = (3 * t + 2) * FP32_UNIT * (np.abs(dy).T @ np.abs(xh))
+    return dict(dx=dx, dx_bound=dx_bound, dw=dw, dw_bound=dw_bound, clip=mask)
 
 
 def forward(bits: np.ndarray, x: np.ndarray, n: int, m: int):
