@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SBL_ABI_VERSION 5
+#define SBL_ABI_VERSION 6
 
 typedef enum {
   SBL_OK = 0,
@@ -286,6 +286,39 @@ int sbl_linear_batch(const sbl_linear_item* items, int32_t count, int32_t fmt, i
 int sbl_linear_acts_batch(const float* x, int64_t m_tok, int64_t k, int8_t* xq, float* gamma,
                           const sbl_linear_item* items, int32_t count, int32_t fmt, int32_t n, int32_t m,
                           sbl_stream stream);
+
+/* Backward of the layer under the dual straight-through estimator
+ * (Sparse-BitNet summaries: Spanish section 2, "Estrategia de Entrenamiento",
+ * Dual STE; Arabic section 2, item 3): the quantizers pass the gradient as
+ * the identity inside their clipping range, and the mask passes it densely
+ * to every master weight, the pruned ones included.  beta and gamma are
+ * treated as constants.
+ *   dy_bf16     [m_tok][n_out] BF16 bit patterns: the gradient of y.
+ *   packed, meta, fmt, n, m, beta
+ *               the layer's packed weights and scale, as given to sbl_linear
+ *               (used for dx; N:M metadata must keep exactly n per group,
+ *               as sbl_quant_weights writes it).
+ *   x           [m_tok][k] fp32: the layer input (used for dx: the clip mask).
+ *   xq, gamma   [m_tok][k] int8 and [m_tok] fp32 from sbl_quant_acts(x)
+ *               (gamma for both outputs, xq for dw).
+ *   dx          [m_tok][k] fp32 output, or NULL:
+ *                 dx = RN(beta_eff * sum_n dy[t][n] c[n][k]) where
+ *                 |rint(128 x[t][k] / gamma_eff[t])| <= 127 (evaluated as
+ *                 in sbl_quant_acts), else 0.
+ *   dw          [n_out][k] fp32 output, or NULL:
+ *                 dw = sum_t dy[t][n] x_hat[t][k] for EVERY (n, k), with
+ *                 x_hat = RN_fp32(gamma_eff[t] * xq[t][k]) * 2^-7.
+ * Products are exact and sums are accumulated in fp32, in an unspecified
+ * order (error at most (L + 1) * 2^-24 * sum|terms| for L terms; dw's sums
+ * have 3 m_tok terms, x_hat being split exactly into three BF16 parts).
+ * Requires m_tok >= 1, n_out % 8 == 0 (SBL_ERR_SHAPE), k % 64 == 0;
+ * alignment 16 bytes for dy_bf16, packed, meta and xq, 4 for the rest;
+ * outputs must not overlap each other or any input (SBL_ERR_SHAPE).  With
+ * both outputs NULL the call does nothing. */
+int sbl_linear_backward(const uint16_t* dy_bf16, int64_t m_tok, int64_t n_out, int64_t k,
+                        const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
+                        const float* beta, const float* x, const int8_t* xq, const float* gamma,
+                        float* dx, float* dw, sbl_stream stream);
 
 #ifdef __cplusplus
 }

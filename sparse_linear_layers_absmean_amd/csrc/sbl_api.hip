@@ -327,4 +327,58 @@ int sbl_linear_batch(const sbl_linear_item* items, int32_t count, int32_t fmt, i
   return launch_status(sbl::launch_linear_batch(args, count, fmt, n, m, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int sbl_linear_backward(const uint16_t* dy_bf16, int64_t m_tok, int64_t n_out, int64_t k, const uint8_t* packed,
+                        const uint8_t* meta, int32_t fmt, int32_t n, int32_t m, const float* beta, const float* x,
+                        const int8_t* xq, const float* gamma, float* dx, float* dw, sbl_stream stream) {
+  if (m_tok < 1 || m_tok > kMaxTokens || n_out < 8 || n_out % 8 != 0 || !k_ok(k) || n_out * k > kMaxElems)
+    return SBL_ERR_SHAPE;
+  if (!dx && !dw) return SBL_OK;
+  if (!dy_bf16 || !gamma) return SBL_ERR_NULL;
+  if (dx) {
+    if (!packed || !beta || !x) return SBL_ERR_NULL;
+    if (fmt != SBL_FMT_DENSE2 && fmt != SBL_FMT_NM) return SBL_ERR_UNSUPPORTED;
+    if (fmt == SBL_FMT_NM && !nm_ok(n, m)) return SBL_ERR_UNSUPPORTED;
+    if (fmt == SBL_FMT_NM && !meta) return SBL_ERR_NULL;
+  }
+  if (dw && !xq) return SBL_ERR_NULL;
+  if (!aligned(dy_bf16, 16) || !aligned(gamma, 4) || (dx && (!aligned(packed, 16) || !aligned(beta, 4) ||
+                                                              !aligned(x, 4) || !aligned(dx, 4) ||
+                                                              (fmt == SBL_FMT_NM && !aligned(meta, 16)))) ||
+      (dw && (!aligned(xq, 16) || !aligned(dw, 4))))
+    return SBL_ERR_ALIGN;
+  // outputs must not overlap each other or any input
+  const int64_t dyb = m_tok * n_out * 2, xb = m_tok * k * 4, xqb = m_tok * k, gb = m_tok * 4;
+  const int64_t dxb = m_tok * k * 4, dwb = n_out * k * 4;
+  const int64_t pb = fmt == SBL_FMT_NM && nm_ok(n, m) ? n_out * (k / m) * n / 4 : n_out * (k / 4);
+  const void* outs[2] = {dx, dw};
+  const int64_t outb[2] = {dxb, dwb};
+  if (ranges_overlap(dx, dxb, dw, dwb)) return SBL_ERR_SHAPE;
+  for (int o = 0; o < 2; ++o) {
+    if (!outs[o]) continue;
+    if (ranges_overlap(outs[o], outb[o], dy_bf16, dyb) || ranges_overlap(outs[o], outb[o], gamma, gb) ||
+        (dx && (ranges_overlap(outs[o], outb[o], x, xb) || ranges_overlap(outs[o], outb[o], packed, pb) ||
+                ranges_overlap(outs[o], outb[o], beta, 4) ||
+                (fmt == SBL_FMT_NM && ranges_overlap(outs[o], outb[o], meta, n_out * (k / 8))))) ||
+        (dw && ranges_overlap(outs[o], outb[o], xq, xqb)))
+      return SBL_ERR_SHAPE;
+  }
+  sbl::BackwardArgs a;
+  a.dy = dy_bf16;
+  a.m_tok = m_tok;
+  a.n_out = n_out;
+  a.k = k;
+  a.packed = packed;
+  a.meta = fmt == SBL_FMT_NM ? meta : nullptr;
+  a.fmt = fmt;
+  a.n = n;
+  a.m = m;
+  a.beta = beta;
+  a.x = x;
+  a.xq = xq;
+  a.gamma = gamma;
+  a.dx = dx;
+  a.dw = dw;
+  return launch_status(sbl::launch_backward(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

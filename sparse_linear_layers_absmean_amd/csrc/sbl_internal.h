@@ -180,4 +180,20 @@ bool gemm_fits(const LinearArgs& a, int kind);
 // launch_gemm_group for kind 2
 hipError_t launch_gemm24_group(const LinearArgs* items, int count, hipStream_t s);
 
+// Backward of the layer (k_backward.hip): dx and/or dw (each nullable).
+struct BackwardArgs {
+  const uint16_t* dy;             // [m_tok][n_out] BF16
+  int64_t m_tok, n_out, k;        // n_out % 8 == 0, k % 64 == 0
+  const uint8_t* packed;          // dx: the layer's packed weights
+  const uint8_t* meta;
+  int32_t fmt, n, m;
+  const float* beta;
+  const float* x;                 // dx: the layer input (clip mask)
+  const int8_t* xq;               // dw: its int8 codes
+  const float* gamma;
+  float* dx;                      // [m_tok][k]
+  float* dw;                      // [n_out][k]
+};
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
+
 }  // namespace sbl

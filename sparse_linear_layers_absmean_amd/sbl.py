@@ -24,7 +24,7 @@ SBL_FMT_NM = 1
 # weight-preparation variants and execution choices (sbl_quant_weights_batch_ex flags)
 SBL_QW_DEFAULT, SBL_QW_BETA_KEPT, SBL_QW_MASK_FROM_CODES = 0, 1, 2
 SBL_QW_TWO_PASS, SBL_QW_NO_WAIT = 4, 8
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32
@@ -97,6 +97,9 @@ def load():
     lib.sbl_linear_acts_batch.restype = ctypes.c_int
     lib.sbl_linear_acts_batch.argtypes = [_c_p, _c_i64, _c_i64, _c_p, _c_p, ctypes.POINTER(LinearItem),
                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_p]
+    lib.sbl_linear_backward.restype = ctypes.c_int
+    lib.sbl_linear_backward.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                                        _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]
     if lib.sbl_abi_version() != ABI_VERSION:
         raise RuntimeError("libsbl.so ABI version mismatch: rebuild it")
     _lib = lib
@@ -251,6 +254,28 @@ def sbl_linear(packed, meta, fmt: int, n: int, m: int, beta, xq, gamma, n_out: i
                         _ptr(y, torch.float32, m_tok * n_out * 4, "y"),
                         _ptr(acc, torch.int32, m_tok * n_out * 4, "acc"), _stream(stream))
     _check("sbl_linear", st)
+
+
+def sbl_linear_backward(dy, packed, meta, fmt: int, n: int, m: int, beta, x, xq, gamma, dx=None, dw=None,
+                        stream=None):
+    """Backward of the layer (dual straight-through estimator): dy BF16 [m_tok][n_out];
+    dx fp32 [m_tok][k] and/or dw fp32 [n_out][k] outputs (either may be None)."""
+    lib = load()
+    m_tok, n_out = dy.shape
+    k = (xq if xq is not None else x).shape[1]
+    pb = lib.sbl_packed_bytes(n_out, k, n, m, fmt) if dx is not None else 0
+    st = lib.sbl_linear_backward(
+        _ptr(dy, _W16, m_tok * n_out * 2, "dy"), m_tok, n_out, k,
+        _ptr(packed, torch.uint8, max(pb, 0), "packed") if dx is not None else None,
+        _ptr(meta, torch.uint8, n_out * k // 8, "meta") if dx is not None and fmt == SBL_FMT_NM else None,
+        fmt, n, m,
+        _ptr(beta, torch.float32, 4, "beta") if dx is not None else None,
+        _ptr(x, torch.float32, m_tok * k * 4, "x") if dx is not None else None,
+        _ptr(xq, torch.int8, m_tok * k, "xq") if dw is not None else None,
+        _ptr(gamma, torch.float32, m_tok * 4, "gamma"),
+        _ptr(dx, torch.float32, m_tok * k * 4, "dx"), _ptr(dw, torch.float32, n_out * k * 4, "dw"),
+        _stream(stream))
+    _check("sbl_linear_backward", st)
 
 
 def sbl_linear_batch(items, fmt: int, n: int, m: int, stream=None):

@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.sbl_abi_version() == 5
+    assert lib.sbl_abi_version() == 6
     for st in range(7):
         assert len(lib.sbl_status_string(st)) > 0
     assert lib.sbl_last_hip_error() == 0
@@ -276,3 +276,33 @@ def test_linear_acts_batch_validation(lib):
     assert call([item()], n=9) == 4
     assert call([item()], fmt=2) == 4
     assert call([item(m_tok=0)], m_tok=0, x=None, xq=None, gamma=None) == 0   # no tokens: no-op
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation runs only on GPU-less hosts")
+def test_backward_validation(lib):
+    f = lib.sbl_linear_backward
+    F = 1 << 40                                             # far apart fake buffers
+
+    def call(dy=A, m_tok=4, n_out=16, k=64, packed=A + F, meta=A + 2 * F, fmt=1, n=6, m=8, beta=A + 3 * F,
+             x=A + 4 * F, xq=A + 5 * F, gamma=A + 6 * F, dx=A + 7 * F, dw=A + 8 * F):
+        return f(dy, m_tok, n_out, k, packed, meta, fmt, n, m, beta, x, xq, gamma, dx, dw, None)
+
+    assert call(dx=None, dw=None) == 0                     # nothing asked: no-op
+    assert call(m_tok=0) == 2
+    assert call(n_out=12) == 2                             # n_out % 8
+    assert call(k=96) == 2
+    assert call(dy=None) == 1
+    assert call(gamma=None) == 1
+    assert call(packed=None) == 1
+    assert call(packed=None, dx=None) != 1                 # dw alone needs no weights
+    assert call(xq=None) == 1
+    assert call(xq=None, dw=None) != 1                     # dx alone needs no codes
+    assert call(meta=None) == 1
+    assert call(meta=None, fmt=0) != 1                     # DENSE2 needs no metadata
+    assert call(fmt=2) == 4
+    assert call(n=9) == 4
+    assert call(dy=A + 8) == 3
+    assert call(xq=A + 5 * F + 4) == 3
+    assert call(dw=A + 7 * F + 64) == 2                    # overlaps dx
+    assert call(dx=A + 16) == 2                            # overlaps dy
+    assert call(dw=A + 5 * F + 16) == 2                    # overlaps xq
