@@ -294,10 +294,11 @@ def main():
         gemv = gemv_sweep(torch, np, sbl, dev, synth)
 
     # ---------------- prefill GEMM (3B block, M = 2048 tokens), int8 ops
-    prefill = prefill_24 = None
+    prefill = prefill_24 = backward = None
     if not args.no_prefill:
         prefill = bench_prefill(torch, np, synth, sbl, dev, tm)
         prefill_24 = bench_prefill(torch, np, synth, sbl, dev, tm, n=2, m=4)
+        backward = bench_backward(torch, np, synth, sbl, dev, tm)
 
     # ---------------- CPU oracle baseline
     cpu = None
@@ -340,6 +341,7 @@ def main():
         "gemv": gemv,
         "prefill": prefill,
         "prefill_2of4_sparse_mfma": prefill_24,
+        "backward": backward,
         "cpu_baseline": cpu,
         "input_gen_s": round(gen_s, 1),
         "device": torch.cuda.get_device_name(0),
@@ -456,6 +458,57 @@ def bench_prefill(torch, np, synth, sbl, dev, tm, n=6, m=8):
             "ms_per_block": round(ms, 4), "int8_TOPS": round(tops, 2),
             "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS,
                          "unit": "TOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": None}}
+
+
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_backward(torch, np, synth, sbl, dev, tm, n=6, m=8):
+    """Backward of a 3B-class block at M = 2048 tokens, 6:8 weights: sbl_linear_backward (dX and dW
+    of the 7 matrices) on the BF16 matrix cores.  Algorithmic flops 2*M*N*K per gradient; dW runs
+    three BF16 products per step (x_hat split exactly into three parts), counted separately."""
+    wname, h, f, m_tok = "b3_prefill", 3200, 8640, 2048
+    fmt = 1
+    mats = synth.block_shapes(h, f)
+    g = torch.Generator(device=dev).manual_seed(11)
+    items = []
+    for i, (_, no, k) in enumerate(mats):
+        w = torch.from_numpy(synth.workload_masters(wname, i, no, k).view(np.int16)).to(dev)
+        o = sbl.quant_weights(w, n, m, fmt=fmt)
+        x = torch.from_numpy(synth.workload_acts(wname, i, m_tok, k)).to(dev)
+        xq, gamma = sbl.quant_acts(x)
+        dy = (torch.randn((m_tok, no), generator=g, device=dev) * 0.05).to(torch.bfloat16)
+        dx = torch.empty((m_tok, k), dtype=torch.float32, device=dev)
+        dw = torch.empty((no, k), dtype=torch.float32, device=dev)
+        items.append((o, x, xq, gamma, dy, dx, dw, no, k))
+        del w
+
+    def run(which):
+        for o, x, xq, gamma, dy, dx, dw, no, k in items:
+            sbl.sbl_linear_backward(dy, o["packed"], o["meta"], fmt, n, m, o["beta"], x, xq, gamma,
+                                    dx=dx if which in ("dx", "both") else None,
+                                    dw=dw if which in ("dw", "both") else None)
+
+    res = {}
+    for which in ("dx", "dw", "both"):
+        for _ in range(2):
+            run(which)
+        torch.cuda.synchronize()
+        reps = 5
+        tm.start()
+        for _ in range(reps):
+            run(which)
+        res[which] = tm.stop_ms() / reps
+    flops = sum(2 * m_tok * no * k for *_, no, k in items)
+    tf = {w: (flops * (2 if w == "both" else 1)) / (res[w] * 1e-3) / 1e12 for w in res}
+    mfma_tf_dw = 3 * flops / (res["dw"] * 1e-3) / 1e12
+    return {"workload": f"Backward (dX and dW), M=2048 tokens, 3B-class block (hidden 3200, FFN 8640), {n}:{m} N:M",
+            "kernel": "backward_dx_kernel, backward_dw_kernel (v_mfma_f32_32x32x16_bf16)",
+            "ms_per_block": {w: round(v, 3) for w, v in res.items()},
+            "algorithmic_TFLOPS": {w: round(v, 1) for w, v in tf.items()},
+            "dw_mfma_TFLOPS": round(mfma_tf_dw, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf["both"], 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf["both"] / BF16_PEAK_TFLOPS, 4), "traffic": None}}
 
 
 def cpu_baseline(np, synth, wname, mats, m_tok, n, m, fmt, budget_s, step_bytes):

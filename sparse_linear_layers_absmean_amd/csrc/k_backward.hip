@@ -14,7 +14,7 @@
 // fp32 accumulation) with exact products: C is {-1, 0, 1}, and x_hat (24
 // significant bits) is split exactly into three BF16 parts, so dW takes
 // three MFMA per step.  One 128 x 128 output tile per workgroup of 4 waves
-// (each 64 x 64: 2 x 2 MFMA tiles), 32 of the contracted index per LDS stage.
+// (each 64 x 64: 2 x 2 MFMA tiles), 64 of the contracted index per LDS stage.
 //   dX: i = token, j = feature, l = output channel; A = dY rows, B = C decoded
 //       from the packed weights (DENSE2 or N:M + bitmap, panel-major).
 //   dW: i = output channel, j = feature, l = token; A = dY^T, B = x_hat.
@@ -29,8 +29,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBT = 256;          // threads
 constexpr int kTile = 128;        // output tile edge
-constexpr int kStep = 32;         // contracted indices per LDS stage
-constexpr int kRow = kStep + 8;   // LDS row length in bf16 (80 bytes: 16-byte aligned, bank-spread)
+constexpr int kStep = 64;         // contracted indices per LDS stage
+constexpr int kRow = kStep + 8;   // LDS row length in bf16 (144 bytes: 16-byte aligned, bank-spread)
 
 constexpr uint16_t kOne = 0x3F80u, kMinusOne = 0xBF80u;   // BF16 1.0, -1.0
 
@@ -38,12 +38,12 @@ __device__ __forceinline__ bf16x8 lds_vec(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
-// the 2 x 2 MFMA tiles of this wave for one LDS stage (two 16-deep sub-steps);
+// the 2 x 2 MFMA tiles of this wave for one LDS stage (16-deep sub-steps);
 // A_s: [kTile][kRow] by i, B_s: [kTile][kRow] by j, both l-contiguous
 __device__ __forceinline__ void mma_stage(const uint16_t* A_s, const uint16_t* B_s, f32x16 (&acc)[2][2], int wi,
                                           int wj, int li, int g) {
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < kStep / 16; ++s) {
     bf16x8 a[2], b[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -77,19 +77,27 @@ __device__ __forceinline__ uint32_t quarter_fields(const PackedW& W, int64_t row
     return f;
   }
   // N:M: the kept weights of the block, in ascending order, hold consecutive
-  // 2-bit codes; exactly n per group of m
+  // 2-bit codes; exactly n per group of m, so the quarter's first kept weight
+  // is number 16 qq n / m, and its codes take at most 32 bits from bit
+  // s = 32 qq n / m on: three halfwords (those inside the block) hold them
   const int bb = 16 * W.n / W.m;                           // code bytes per block (even)
   const uint16_t* cp = reinterpret_cast<const uint16_t*>(W.packed + panel_offset(W.n_out, W.nkb, bb, row, kb));
   const uint2 mv = *reinterpret_cast<const uint2*>(W.meta + panel_offset(W.n_out, W.nkb, 8, row, kb));
-  const uint64_t keep = (uint64_t)mv.x | ((uint64_t)mv.y << 32);
+  const uint32_t keep = (uint32_t)(((uint64_t)mv.x | ((uint64_t)mv.y << 32)) >> (16 * qq)) & 0xFFFFu;
+  const int s0 = 32 * qq * W.n / W.m, h0 = s0 >> 4;
+  uint64_t win = 0;
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (h0 + j < bb / 2) win |= (uint64_t)cp[h0 + j] << (16 * j);
+  win >>= s0 & 15;                                         // bit 0: the quarter's first code
   uint32_t f = 0;
+  int idx = 0;
+#pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int p = 16 * qq + e;
     uint32_t u = 1u;                                       // pruned: code 0
-    if ((keep >> p) & 1u) {
-      const int g0 = p / W.m * W.m;
-      const int idx = p / W.m * W.n + __popcll((keep >> g0) & ((1ull << (p - g0)) - 1ull));
-      u = (cp[idx >> 3] >> (2 * (idx & 7))) & 3u;
+    if ((keep >> e) & 1u) {
+      u = (uint32_t)(win >> (2 * idx)) & 3u;
+      ++idx;
     }
     f |= u << (2 * e);
   }
@@ -108,19 +116,20 @@ __global__ __launch_bounds__(kBT) void backward_dx_kernel(const uint16_t* __rest
   f32x16 acc[2][2] = {};
   for (int64_t n0 = 0; n0 < n_out; n0 += kStep) {
     __syncthreads();                                       // the previous stage has been read
-    {  // A: dY[t0 + r][n0 .. n0 + 31], two 16-byte halves per row (n_out % 8 == 0)
+    {  // A: dY[t0 + r][n0 .. n0 + 63], four 16-byte pieces per thread (n_out % 8 == 0)
       const int r = tid >> 1, h = tid & 1;
       const int64_t t = t0 + r;
 #pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        const int64_t nn = n0 + 16 * h + 8 * v;
+      for (int v = 0; v < 4; ++v) {
+        const int64_t nn = n0 + 32 * h + 8 * v;
         u32x4 val = {0u, 0u, 0u, 0u};
         if (t < m_tok && nn < n_out) val = *reinterpret_cast<const u32x4*>(dy + t * n_out + nn);
-        *reinterpret_cast<u32x4*>(A_s + r * kRow + 16 * h + 8 * v) = val;
+        *reinterpret_cast<u32x4*>(A_s + r * kRow + 32 * h + 8 * v) = val;
       }
     }
-    {  // B: C[n0 + nl][k0 + 64 bb + 16 qq + e] -> B_s[64 bb + 16 qq + e][nl]
-      const int nl = tid >> 3, bb = (tid >> 2) & 1, qq = tid & 3;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {  // B: C[n0 + nl][k0 + 64 bb + 16 qq + e] -> B_s[64 bb + 16 qq + e][nl]
+      const int nl = 32 * half + (tid >> 3), bb = (tid >> 2) & 1, qq = tid & 3;
       const int64_t row = n0 + nl;
       const int kb = (int)(k0 / 64) + bb;
       uint32_t f = 0x55555555u;                            // u = 1 everywhere: code 0
@@ -173,32 +182,25 @@ __global__ __launch_bounds__(kBT) void backward_dw_kernel(const uint16_t* __rest
   const int wi = wave >> 1, wj = wave & 1;
   const int64_t n0 = (int64_t)blockIdx.y * kTile, k0 = (int64_t)blockIdx.x * kTile;
   f32x16 acc[2][2] = {};
-  const int r = tid >> 3, c16 = 16 * (tid & 7);            // staging: token row r of the stage, 16 columns
+  const int r = tid >> 2, c32 = 32 * (tid & 3);            // staging: token row r of the stage, 32 columns
   for (int64_t t0 = 0; t0 < m_tok; t0 += kStep) {
     __syncthreads();
     const int64_t t = t0 + r;
-    {  // A: dY[t][n0 + c16 .. +15] -> A_s[c16 + e][r]
-      uint16_t h[16] = {};
 #pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        const int64_t nn = n0 + c16 + 8 * v;
-        if (t < m_tok && nn < n_out) {
-          const u32x4 val = *reinterpret_cast<const u32x4*>(dy + t * n_out + nn);
+    for (int v = 0; v < 4; ++v) {  // A: dY[t][n0 + c32 + 8v .. +7] -> A_s[c32 + 8v + e][r]
+      const int64_t nn = n0 + c32 + 8 * v;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (t < m_tok && nn < n_out) val = *reinterpret_cast<const u32x4*>(dy + t * n_out + nn);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            h[8 * v + 2 * e] = (uint16_t)val[e];
-            h[8 * v + 2 * e + 1] = (uint16_t)(val[e] >> 16);
-          }
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) A_s[(c16 + e) * kRow + r] = h[e];
+      for (int e = 0; e < 8; ++e) A_s[(c32 + 8 * v + e) * kRow + r] = (uint16_t)(val[e >> 1] >> (16 * (e & 1)));
     }
-    {  // B: x_hat[t][k0 + c16 .. +15] in three parts -> B_s[p][c16 + e][r]
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {  // B: x_hat[t][k0 + c32 + 16v .. +15] in three parts -> B_s[p][..][r]
+      const int c = c32 + 16 * v;
       u32x4 qv = {0u, 0u, 0u, 0u};
       float ge = 0.0f;
-      if (t < m_tok && k0 + c16 < k) {
-        qv = *reinterpret_cast<const u32x4*>(xq + t * k + k0 + c16);
+      if (t < m_tok && k0 + c < k) {
+        qv = *reinterpret_cast<const u32x4*>(xq + t * k + k0 + c);
         ge = fmaxf(gamma[t], 1e-5f);
       }
 #pragma unroll
@@ -207,9 +209,9 @@ __global__ __launch_bounds__(kBT) void backward_dw_kernel(const uint16_t* __rest
         const float xh = (ge * (float)qe) * (1.0f / 128.0f);
         uint16_t h1, h2, h3;
         split3(xh, h1, h2, h3);
-        B_s[0][(c16 + e) * kRow + r] = h1;
-        B_s[1][(c16 + e) * kRow + r] = h2;
-        B_s[2][(c16 + e) * kRow + r] = h3;
+        B_s[0][(c + e) * kRow + r] = h1;
+        B_s[1][(c + e) * kRow + r] = h2;
+        B_s[2][(c + e) * kRow + r] = h3;
       }
     }
     __syncthreads();
