@@ -43,6 +43,9 @@ listed with its reason in the design notes):
     storage order of the packed streams in `to_panels`; they are this
     implementation's choice, not the pages'.
 
+Group scales (`quant_weights_grouped`, `rescale_grouped`): one absmean
+beta per block of consecutive output rows instead of one per matrix.
+
 Backward (dual straight-through estimator; readings listed with the
 function `backward`): the scales are constants, the incoming gradient is
 BF16, dX passes only where the activation clamp did not act, and dW reaches
@@ -416,6 +419,42 @@ def rescale(acc: np.ndarray, beta, gamma: np.ndarray) -> np.ndarray:
 def linear(codes: np.ndarray, q: np.ndarray, beta, gamma: np.ndarray):
     acc = contract(codes, q)
     return acc, rescale(acc, beta, gamma)
+
+
+# --------------------------------------------------------------------------
+# Group scales  [BN-cpp] section "Cuantizacion y normalizacion de grupos": the
+# scale is computed per group of weights instead of per matrix, so groups need
+# no communication.  Reading: a group is a block of rows_per_group consecutive
+# output rows (the last one may be shorter); each has its own exact absmean
+# beta, and its codes use it.  The mask does not depend on beta.  gamma stays
+# per token.
+# --------------------------------------------------------------------------
+
+def quant_weights_grouped(bits: np.ndarray, n: int, m: int, rows_per_group: int):
+    """(betas fp32 [G], keep bool, codes int8): quant-then-mask with one beta per row group."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    n_out = bits.shape[0]
+    if rows_per_group < 1:
+        raise ValueError("rows_per_group must be positive")
+    keep = nm_keep(bits, n, m)
+    betas, codes = [], np.zeros(bits.shape, np.int8)
+    for r0 in range(0, n_out, rows_per_group):
+        sl = slice(r0, min(n_out, r0 + rows_per_group))
+        b = absmean_beta(bits[sl])
+        betas.append(b)
+        codes[sl] = ternarize(bits[sl], b)
+    codes = (codes * keep).astype(np.int8)
+    return np.array(betas, np.float32), keep, codes
+
+
+def rescale_grouped(acc: np.ndarray, betas: np.ndarray, rows_per_group: int, gamma: np.ndarray) -> np.ndarray:
+    """y[t, r] = RN(fp32(acc) * RN(RN(beta_eff[r // rows_per_group] * gamma_eff[t]) * 2^-7))."""
+    acc = np.asarray(acc)
+    b = np.maximum(np.asarray(betas, dtype=np.float32), EPS_SCALE)
+    b_rows = np.repeat(b, rows_per_group)[:acc.shape[1]]
+    g = np.maximum(np.asarray(gamma, dtype=np.float32), EPS_SCALE)
+    s = ((g[:, None] * b_rows[None, :]).astype(np.float32) * np.float32(1.0 / QB)).astype(np.float32)
+    return (acc.astype(np.float32) * s).astype(np.float32)
 
 
 # --------------------------------------------------------------------------

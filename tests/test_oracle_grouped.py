@@ -1,0 +1,84 @@
+"""Pins for the oracle's group scales: one exact absmean beta per block of
+consecutive output rows ([BN-cpp] "Cuantizacion y normalizacion de grupos").
+
+Independent routes: one group is the per-matrix method; every group equals
+the per-matrix method on its own rows (the per-matrix oracle is pinned
+elsewhere); closed-form betas on constant-magnitude rows; locality (changing
+one group's masters changes only that group); the grouped rescale against
+an exact-Fraction evaluation of its two roundings."""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import sbl_oracle as O
+
+
+def test_one_group_is_the_method():
+    rng = np.random.default_rng(400)
+    bits = synth.gaussian_masters(rng, 40, 128)
+    betas, keep, codes = O.quant_weights_grouped(bits, 6, 8, 40)
+    beta, keep1, codes1 = O.quant_weights(bits, 6, 8)
+    assert betas.tolist() == [beta] and np.array_equal(keep, keep1) and np.array_equal(codes, codes1)
+    betas, _, _ = O.quant_weights_grouped(bits, 6, 8, 1000)      # a group larger than the matrix
+    assert betas.tolist() == [beta]
+
+
+@pytest.mark.parametrize("rpg", [1, 3, 16, 25])
+def test_each_group_is_the_method_on_its_rows(rpg):
+    rng = np.random.default_rng([401, rpg])
+    bits = synth.gaussian_masters(rng, 50, 64, outlier_frac=0.02)
+    betas, keep, codes = O.quant_weights_grouped(bits, 2, 4, rpg)
+    assert len(betas) == -(-50 // rpg)
+    for g, r0 in enumerate(range(0, 50, rpg)):
+        sl = slice(r0, min(50, r0 + rpg))
+        b, k1, c1 = O.quant_weights(bits[sl], 2, 4)
+        assert betas[g] == b and np.array_equal(keep[sl], k1) and np.array_equal(codes[sl], c1)
+
+
+def test_closed_form_constant_rows():
+    """Rows of group g all hold magnitude a_g (signs alternate): beta_g = a_g, and
+    every kept code is +-1 (|w| = beta > beta/2)."""
+    mags = [0.015625, 0.25, 0.0078125]
+    rows = []
+    for a in mags:
+        for _ in range(4):
+            rows.append(np.where(np.arange(64) % 2 == 0, a, -a))
+    bits = synth.f32_to_bf16_bits(np.array(rows, np.float32))
+    betas, keep, codes = O.quant_weights_grouped(bits, 6, 8, 4)
+    assert betas.tolist() == mags
+    assert np.all(np.abs(codes[keep]) == 1) and np.all(codes[~keep] == 0)
+
+
+def test_groups_are_local():
+    rng = np.random.default_rng(402)
+    bits = synth.gaussian_masters(rng, 24, 128)
+    b0, _, c0 = O.quant_weights_grouped(bits, 6, 8, 8)
+    bits2 = bits.copy()
+    bits2[8:16] = synth.gaussian_masters(rng, 8, 128, sigma=0.5)
+    b1, _, c1 = O.quant_weights_grouped(bits2, 6, 8, 8)
+    assert b0[0] == b1[0] and b0[2] == b1[2] and b0[1] != b1[1]
+    assert np.array_equal(c0[:8], c1[:8]) and np.array_equal(c0[16:], c1[16:])
+
+
+def test_rescale_grouped_two_roundings():
+    rng = np.random.default_rng(403)
+    acc = rng.integers(-40000, 40000, (3, 10)).astype(np.int32)
+    betas = np.array([0.0113, 0.0207, 0.0042, 3e-6], np.float32)   # the last one below the floor
+    gamma = np.array([1.7, 0.0, 250.0], np.float32)
+    y = O.rescale_grouped(acc, betas, 3, gamma)
+
+    def rn32(fr):
+        return Fraction(float(np.float32(float(fr))))   # exact for the values that arise here
+
+    for t in range(3):
+        g = Fraction(float(max(np.float32(gamma[t]), np.float32(1e-5))))
+        for r in range(10):
+            b = Fraction(float(max(np.float32(betas[r // 3]), np.float32(1e-5))))
+            s = rn32(rn32(b * g) / 128)
+            want = np.float32(float(Fraction(int(acc[t, r])) * s))
+            assert y[t, r] == want
+    # one group: the per-matrix rescale
+    assert np.array_equal(O.rescale_grouped(acc, betas[:1], 10, gamma), O.rescale(acc, betas[0], gamma))
