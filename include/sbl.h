@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SBL_ABI_VERSION 6
+#define SBL_ABI_VERSION 7
 
 typedef enum {
   SBL_OK = 0,
@@ -286,6 +286,37 @@ int sbl_linear_batch(const sbl_linear_item* items, int32_t count, int32_t fmt, i
 int sbl_linear_acts_batch(const float* x, int64_t m_tok, int64_t k, int8_t* xq, float* gamma,
                           const sbl_linear_item* items, int32_t count, int32_t fmt, int32_t n, int32_t m,
                           sbl_stream stream);
+
+/* Group scales (BitNet.cpp article, "Cuantizacion y normalizacion de
+ * grupos": parameters computed per group instead of per matrix, so groups
+ * need no communication).  A group is a block of rows_per_group consecutive
+ * output rows (the last may be shorter); G = ceil(n_out / rows_per_group).
+ *
+ * Workspace bytes for sbl_quant_weights_grouped (-1 if invalid). */
+int64_t sbl_workspace_bytes_grouped(int64_t n_out, int64_t k, int64_t rows_per_group);
+
+/* sbl_quant_weights with one beta per row group: beta[g] = RN_fp32 of the
+ * exact mean of |w| over group g's rows, and row r's codes use
+ * max(beta[r / rows_per_group], 1e-5).  The mask does not depend on beta.
+ *   beta       [G] fp32 output.
+ *   workspace  sbl_workspace_bytes_grouped(n_out, k, rows_per_group) bytes.
+ * Everything else (outputs, formats, validation, errors) as
+ * sbl_quant_weights; rows_per_group < 1 or more than 65535 groups gives
+ * SBL_ERR_SHAPE, and beta must not overlap the other buffers.
+ * rows_per_group = 1: one beta per row. */
+int sbl_quant_weights_grouped(const uint16_t* w_bf16, int64_t n_out, int64_t k, int32_t n, int32_t m,
+                              int64_t rows_per_group, float* beta, uint8_t* mask_bits, int8_t* codes,
+                              int32_t fmt, uint8_t* packed, uint8_t* meta,
+                              void* workspace, int64_t workspace_bytes, sbl_stream stream);
+
+/* sbl_linear with one beta per row group:
+ *   y[t][r] = RN(fp32(acc[t][r]) * RN(RN(beta_eff[r / rows_per_group] *
+ *             gamma_eff[t]) * 2^-7)).
+ *   acc        [m_tok][n_out] int32, REQUIRED (written: the exact products).
+ * Validation as sbl_linear; rows_per_group < 1 gives SBL_ERR_SHAPE. */
+int sbl_linear_grouped(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
+                       const float* beta, int64_t rows_per_group, const int8_t* xq, const float* gamma,
+                       int64_t m_tok, int64_t n_out, int64_t k, float* y, int32_t* acc, sbl_stream stream);
 
 /* Backward of the layer under the dual straight-through estimator
  * (Sparse-BitNet summaries: Spanish section 2, "Estrategia de Entrenamiento",

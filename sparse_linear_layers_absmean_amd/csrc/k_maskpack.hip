@@ -646,7 +646,7 @@ __global__ __launch_bounds__(kThreads) void mask_pack_kernel(const QBatch batch,
   const int fmt = d.fmt;
   const int64_t lwg = (int64_t)blockIdx.x - batch.start[di];
   const float b = fmaxf(batch.beta_ready ? d.beta[0] : beta::workgroup_beta(d, lwg == 0), 1e-5f);
-  const int thr_mag = (int)(__float_as_uint(b * 0.5f) >> 16);
+  int thr_mag = (int)(__float_as_uint(b * 0.5f) >> 16);
   const bool want_nm = packed && fmt == 1;
   {
     const int64_t c0 = lwg * kThreads;
@@ -655,6 +655,8 @@ __global__ __launch_bounds__(kThreads) void mask_pack_kernel(const QBatch batch,
     load_chunk(d.w, c0, cnt, stage, dw);
     const int64_t c = c0 + threadIdx.x;
     if (c >= nchunks) return;
+    if (d.beta_rows > 0)                             // group scales: the beta of this chunk's row group
+      thr_mag = (int)(__float_as_uint(fmaxf(d.beta[c / d.nkb / d.beta_rows], 1e-5f) * 0.5f) >> 16);
     ChunkOut o = {};
 #pragma unroll
     for (int g = 0; g < 64 / M; ++g) {
@@ -742,7 +744,9 @@ int64_t grid_for(int64_t nchunks) {
 hipError_t launch_mask_pack(QBatch& b, int n, int m, hipStream_t s, bool dry, int64_t* grid_out,
                             bool mask_from_codes) {
   const int drop = m - n;
-  const bool fast = drop <= 2 && !mask_from_codes;
+  bool grouped = false;                              // group scales: the per-key kernel reads beta per row
+  for (int i = 0; i < b.count; ++i) grouped = grouped || b.d[i].beta_rows > 0;
+  const bool fast = drop <= 2 && !mask_from_codes && !grouped;
   const int64_t per_block = fast ? (int64_t)kThreads * kCPT : kThreads;   // chunks per workgroup
   int64_t blocks = 0;
   for (int i = 0; i < b.count; ++i) {

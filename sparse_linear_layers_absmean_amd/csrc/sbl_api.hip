@@ -120,6 +120,7 @@ sbl::QDesc to_qdesc(const sbl_quant_item& it, int32_t fmt) {
   d.beta = it.beta;
   d.ws = reinterpret_cast<uint64_t*>(it.workspace);
   d.ws_words = it.workspace_bytes / 8;
+  d.beta_rows = 0;
   d.mask = it.mask_bits;
   d.codes = it.codes;
   d.packed = it.packed;
@@ -325,6 +326,61 @@ int sbl_linear_batch(const sbl_linear_item* items, int32_t count, int32_t fmt, i
     args[i] = to_args(items[i], fmt);
   }
   return launch_status(sbl::launch_linear_batch(args, count, fmt, n, m, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int64_t sbl_workspace_bytes_grouped(int64_t n_out, int64_t k, int64_t rows_per_group) {
+  if (n_out < 1 || !k_ok(k) || n_out * k > kMaxElems || rows_per_group < 1) return -1;
+  const sbl::GroupPlan p = sbl::group_plan(n_out, k, rows_per_group);
+  if (p.groups > 65535) return -1;                   // one grid row per group
+  return (8 * p.groups * p.region + 4095) / 4096 * 4096;
+}
+
+int sbl_quant_weights_grouped(const uint16_t* w_bf16, int64_t n_out, int64_t k, int32_t n, int32_t m,
+                              int64_t rows_per_group, float* beta, uint8_t* mask_bits, int8_t* codes, int32_t fmt,
+                              uint8_t* packed, uint8_t* meta, void* workspace, int64_t workspace_bytes,
+                              sbl_stream stream) {
+  if (rows_per_group < 1) return SBL_ERR_SHAPE;
+  // the per-matrix checks (their workspace size aside), then the group workspace's size
+  const sbl_quant_item it{w_bf16, n_out, k, beta, mask_bits, codes, packed, meta, workspace, INT64_MAX};
+  int st = check_quant(it, n, m, fmt);
+  if (st != SBL_OK) return st;
+  const int64_t need = sbl_workspace_bytes_grouped(n_out, k, rows_per_group);
+  if (need < 0) return SBL_ERR_SHAPE;                // more than 65535 groups
+  if (workspace_bytes < need) return SBL_ERR_WORKSPACE;
+  const int64_t groups = (n_out + rows_per_group - 1) / rows_per_group;
+  const int64_t mask_b = n_out * (k / 8);
+  const int64_t packed_b = fmt == SBL_FMT_DENSE2 ? n_out * (k / 4) : n_out * (k / m) * n / 4;
+  if (ranges_overlap(beta, 4 * groups, mask_bits, mask_b) || ranges_overlap(beta, 4 * groups, codes, n_out * k) ||
+      ranges_overlap(beta, 4 * groups, packed, packed_b) ||
+      ranges_overlap(beta, 4 * groups, packed && fmt == SBL_FMT_NM ? meta : nullptr, mask_b) ||
+      ranges_overlap(beta, 4 * groups, workspace, workspace_bytes))
+    return SBL_ERR_SHAPE;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = launch_status(sbl::launch_grouped_beta(w_bf16, n_out, k, rows_per_group, beta,
+                                              reinterpret_cast<uint64_t*>(workspace), s));
+  if (st != SBL_OK || (!mask_bits && !codes && !packed)) return st;
+  sbl::QBatch b;
+  b.count = 1;
+  b.beta_ready = 1;
+  b.d[0] = to_qdesc(it, fmt);
+  b.d[0].beta_rows = rows_per_group;
+  return launch_status(sbl::launch_mask_pack(b, n, m, s));
+}
+
+int sbl_linear_grouped(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
+                       const float* beta, int64_t rows_per_group, const int8_t* xq, const float* gamma, int64_t m_tok,
+                       int64_t n_out, int64_t k, float* y, int32_t* acc, sbl_stream stream) {
+  if (rows_per_group < 1) return SBL_ERR_SHAPE;
+  const sbl_linear_item it{packed, meta, beta, xq, gamma, m_tok, n_out, k, y, acc};
+  const int st = check_linear(it, fmt, n, m);
+  if (st != SBL_OK || m_tok == 0 || n_out == 0) return st;
+  if (!acc) return SBL_ERR_NULL;
+  if (ranges_overlap(y, m_tok * n_out * 4, acc, m_tok * n_out * 4)) return SBL_ERR_SHAPE;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const sbl::LinearArgs a = to_args(it, fmt);
+  const int st2 = launch_status(sbl::launch_linear_batch(&a, 1, fmt, n, m, s));
+  if (st2 != SBL_OK) return st2;
+  return launch_status(sbl::launch_rescale_grouped(acc, beta, rows_per_group, gamma, m_tok, n_out, y, s));
 }
 
 int sbl_linear_backward(const uint16_t* dy_bf16, int64_t m_tok, int64_t n_out, int64_t k, const uint8_t* packed,

@@ -95,6 +95,7 @@ struct QDesc {
   float* beta;
   uint64_t* ws;
   int64_t ws_words;       // workspace size
+  int64_t beta_rows;      // > 0: group scales, beta[row / beta_rows] (mask/pack kernel only)
   uint8_t* mask;          // nullable outputs
   int8_t* codes;
   uint8_t* packed;
@@ -179,6 +180,24 @@ bool gemm_fits(const LinearArgs& a, int kind);
 // N:M 2:4 products on the sparse MFMA (v_smfmac_i32_16x16x128_i8); called by
 // launch_gemm_group for kind 2
 hipError_t launch_gemm24_group(const LinearArgs* items, int count, hipStream_t s);
+
+// Group scales (k_grouped.hip): one exact absmean beta per block of
+// rows_per_group output rows.  Workspace: one region per group of
+// grouped_region_words(..) words (the absmean slot layout of one group).
+struct GroupPlan {
+  int64_t groups, nb, vpt, region;   // region: words per group
+};
+inline GroupPlan group_plan(int64_t n_out, int64_t k, int64_t rows_per_group) {
+  const int64_t rpg = rows_per_group < n_out ? rows_per_group : n_out;
+  const AbsmeanPlan p = absmean_plan(rpg * k);
+  return GroupPlan{(n_out + rpg - 1) / rpg, p.nb, p.vpt, ws_limb_base(p.nb) + kWsLimbWords * p.nb};
+}
+// beta[g] for every group (partial sums, then one finalizing workgroup per group)
+hipError_t launch_grouped_beta(const uint16_t* w, int64_t n_out, int64_t k, int64_t rows_per_group, float* beta,
+                               uint64_t* ws, hipStream_t s);
+// y[t][r] = fp32(acc[t][r]) * RN(RN(beta_eff[r / rows_per_group] * gamma_eff[t]) * 2^-7)
+hipError_t launch_rescale_grouped(const int32_t* acc, const float* beta, int64_t rows_per_group, const float* gamma,
+                                  int64_t m_tok, int64_t n_out, float* y, hipStream_t s);
 
 // Backward of the layer (k_backward.hip): dx and/or dw (each nullable).
 struct BackwardArgs {

@@ -24,7 +24,7 @@ SBL_FMT_NM = 1
 # weight-preparation variants and execution choices (sbl_quant_weights_batch_ex flags)
 SBL_QW_DEFAULT, SBL_QW_BETA_KEPT, SBL_QW_MASK_FROM_CODES = 0, 1, 2
 SBL_QW_TWO_PASS, SBL_QW_NO_WAIT = 4, 8
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32
@@ -97,6 +97,14 @@ def load():
     lib.sbl_linear_acts_batch.restype = ctypes.c_int
     lib.sbl_linear_acts_batch.argtypes = [_c_p, _c_i64, _c_i64, _c_p, _c_p, ctypes.POINTER(LinearItem),
                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_p]
+    lib.sbl_workspace_bytes_grouped.restype = _c_i64
+    lib.sbl_workspace_bytes_grouped.argtypes = [_c_i64, _c_i64, _c_i64]
+    lib.sbl_quant_weights_grouped.restype = ctypes.c_int
+    lib.sbl_quant_weights_grouped.argtypes = [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i64, _c_p, _c_p, _c_p,
+                                              _c_i32, _c_p, _c_p, _c_p, _c_i64, _c_p]
+    lib.sbl_linear_grouped.restype = ctypes.c_int
+    lib.sbl_linear_grouped.argtypes = [_c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_i64, _c_p, _c_p,
+                                       _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]
     lib.sbl_linear_backward.restype = ctypes.c_int
     lib.sbl_linear_backward.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
                                         _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]
@@ -254,6 +262,43 @@ def sbl_linear(packed, meta, fmt: int, n: int, m: int, beta, xq, gamma, n_out: i
                         _ptr(y, torch.float32, m_tok * n_out * 4, "y"),
                         _ptr(acc, torch.int32, m_tok * n_out * 4, "acc"), _stream(stream))
     _check("sbl_linear", st)
+
+
+def sbl_workspace_bytes_grouped(n_out: int, k: int, rows_per_group: int) -> int:
+    return load().sbl_workspace_bytes_grouped(n_out, k, rows_per_group)
+
+
+def sbl_quant_weights_grouped(w_bf16, n: int, m: int, rows_per_group: int, beta, workspace, mask_bits=None,
+                              codes=None, fmt: int = SBL_FMT_DENSE2, packed=None, meta=None, stream=None):
+    """Group scales: beta fp32 [ceil(n_out / rows_per_group)], one per block of output rows."""
+    lib = load()
+    n_out, k = w_bf16.shape
+    groups = -(-n_out // rows_per_group) if rows_per_group > 0 else 1
+    pb = lib.sbl_packed_bytes(n_out, k, n, m, fmt) if packed is not None else 0
+    st = lib.sbl_quant_weights_grouped(
+        _ptr(w_bf16, _W16, n_out * k * 2, "w_bf16"), n_out, k, n, m, rows_per_group,
+        _ptr(beta, torch.float32, 4 * groups, "beta"),
+        _ptr(mask_bits, torch.uint8, n_out * k // 8, "mask_bits"), _ptr(codes, torch.int8, n_out * k, "codes"),
+        fmt, _ptr(packed, torch.uint8, max(pb, 0), "packed"),
+        _ptr(meta, torch.uint8, n_out * k // 8, "meta") if fmt == SBL_FMT_NM else None,
+        _ptr(workspace, None, max(lib.sbl_workspace_bytes_grouped(n_out, k, rows_per_group), 0), "workspace"),
+        _nbytes(workspace), _stream(stream))
+    _check("sbl_quant_weights_grouped", st)
+
+
+def sbl_linear_grouped(packed, meta, fmt: int, n: int, m: int, beta, rows_per_group: int, xq, gamma, n_out: int, y,
+                       acc, stream=None):
+    lib = load()
+    m_tok, k = xq.shape
+    groups = -(-n_out // rows_per_group) if rows_per_group > 0 else 1
+    pb = lib.sbl_packed_bytes(n_out, k, n, m, fmt) if n_out > 0 else 0
+    st = lib.sbl_linear_grouped(_ptr(packed, torch.uint8, max(pb, 0), "packed"),
+                                _ptr(meta, torch.uint8, n_out * k // 8, "meta") if fmt == SBL_FMT_NM else None,
+                                fmt, n, m, _ptr(beta, torch.float32, 4 * groups, "beta"), rows_per_group,
+                                _ptr(xq, torch.int8, m_tok * k, "xq"), _ptr(gamma, torch.float32, m_tok * 4, "gamma"),
+                                m_tok, n_out, k, _ptr(y, torch.float32, m_tok * n_out * 4, "y"),
+                                _ptr(acc, torch.int32, m_tok * n_out * 4, "acc"), _stream(stream))
+    _check("sbl_linear_grouped", st)
 
 
 def sbl_linear_backward(dy, packed, meta, fmt: int, n: int, m: int, beta, x, xq, gamma, dx=None, dw=None,

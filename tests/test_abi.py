@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.sbl_abi_version() == 6
+    assert lib.sbl_abi_version() == 7
     for st in range(7):
         assert len(lib.sbl_status_string(st)) > 0
     assert lib.sbl_last_hip_error() == 0
@@ -306,3 +306,42 @@ def test_backward_validation(lib):
     assert call(dw=A + 7 * F + 64) == 2                    # overlaps dx
     assert call(dx=A + 16) == 2                            # overlaps dy
     assert call(dw=A + 5 * F + 16) == 2                    # overlaps xq
+
+
+def test_grouped_workspace_sizes(lib):
+    # per group: its absmean slots (8 bytes, padded to 64) + 48-byte records, rounded up to 4 KB overall
+    assert lib.sbl_workspace_bytes_grouped(4, 64, 1) == 4096              # 4 groups x 14 words
+    assert lib.sbl_workspace_bytes_grouped(8640, 3200, 1) == 970752       # one slot per row
+    assert lib.sbl_workspace_bytes_grouped(5120, 5120, 5120) == 45056     # one group: 800 slots
+    assert lib.sbl_workspace_bytes_grouped(5120, 5120, 99999) == 45056    # a group larger than the matrix
+    assert lib.sbl_workspace_bytes_grouped(4, 64, 0) == -1
+    assert lib.sbl_workspace_bytes_grouped(4, 96, 1) == -1
+    assert lib.sbl_workspace_bytes_grouped(65536, 64, 1) == -1          # more groups than grid rows
+    assert lib.sbl_workspace_bytes_grouped(65535, 64, 1) > 0
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation runs only on GPU-less hosts")
+def test_grouped_validation(lib):
+    fq = lib.sbl_quant_weights_grouped
+    F = 1 << 40
+    ws = lib.sbl_workspace_bytes_grouped(16, 64, 4)
+
+    def q(rpg=4, beta=A + F, packed=A + 2 * F, meta=A + 3 * F, workspace=A + 4 * F, wsb=ws, fmt=1, n=6):
+        return fq(A, 16, 64, n, 8, rpg, beta, None, None, fmt, packed, meta, workspace, wsb, None)
+
+    assert q(rpg=0) == 2
+    assert q(wsb=ws - 8) == 6
+    assert q(workspace=None) == 6
+    assert q(beta=None) == 1
+    assert q(n=9) == 4
+    assert q(beta=A + 2 * F + 8) == 2                       # beta (4 groups) overlaps packed
+    assert q(beta=A + 4 * F + 16) == 2                      # beta overlaps the workspace
+    fl = lib.sbl_linear_grouped
+
+    def lin(rpg=4, acc=A + 5 * F, y=A + 6 * F, fmt=1):
+        return fl(A + 2 * F, A + 3 * F, fmt, 6, 8, A + F, rpg, A + 7 * F, A + 8 * F, 2, 16, 64, y, acc, None)
+
+    assert lin(rpg=0) == 2
+    assert lin(acc=None) == 1
+    assert lin(acc=A + 6 * F + 4) == 2                      # acc overlaps y
+    assert lin(fmt=3) == 4

@@ -1,0 +1,76 @@
+"""Group scales on the GPU (one exact absmean beta per block of output rows):
+sbl_quant_weights_grouped and sbl_linear_grouped against the oracle, bit for
+bit for beta, mask, codes, packed bytes, metadata and acc; y within the usual
+1e-6 relative."""
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import FMT_DENSE2, FMT_NM, check_y, meta_rows, packed_rows, say, to_dev, to_np
+from oracle import sbl_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(bits, x, n, m, fmt, rpg, label):
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    n_out, k = bits.shape
+    groups = -(-n_out // rpg)
+    say(f"grouped {label} {n_out}x{k} rows_per_group={rpg} {n}:{m} fmt={fmt}")
+    beta = torch.full((groups,), -1.0, device="cuda")
+    mask = torch.empty((n_out, k // 8), dtype=torch.uint8, device="cuda")
+    codes = torch.empty((n_out, k), dtype=torch.int8, device="cuda")
+    packed = torch.empty(sbl.sbl_packed_bytes(n_out, k, n, m, fmt), dtype=torch.uint8, device="cuda")
+    meta = torch.empty((n_out, k // 8), dtype=torch.uint8, device="cuda") if fmt == FMT_NM else None
+    ws = torch.full((sbl.sbl_workspace_bytes_grouped(n_out, k, rpg),), 0xFF, dtype=torch.uint8, device="cuda")
+    w = to_dev(bits)
+    for rep in range(2):                                     # the same workspace twice
+        sbl.sbl_quant_weights_grouped(w, n, m, rpg, beta, ws, mask_bits=mask, codes=codes, fmt=fmt, packed=packed,
+                                      meta=meta)
+    xq, gamma = sbl.quant_acts(to_dev(x.astype(np.float32)))
+    y = torch.empty((x.shape[0], n_out), dtype=torch.float32, device="cuda")
+    acc = torch.empty((x.shape[0], n_out), dtype=torch.int32, device="cuda")
+    sbl.sbl_linear_grouped(packed, meta, fmt, n, m, beta, rpg, xq, gamma, n_out, y, acc)
+    torch.cuda.synchronize()
+    betas, keep, c = O.quant_weights_grouped(bits, n, m, rpg)
+    assert np.array_equal(to_np(beta), betas)
+    assert np.array_equal(to_np(mask), O.pack_bitmap(keep))
+    assert np.array_equal(to_np(codes), c)
+    if fmt == FMT_DENSE2:
+        assert np.array_equal(packed_rows(to_np(packed), n_out, k, fmt, n, m), O.pack_dense2(c))
+    else:
+        if (k * n // m) % 4 == 0:
+            assert np.array_equal(packed_rows(to_np(packed), n_out, k, fmt, n, m), O.pack_nm(c, keep, n, m))
+        assert np.array_equal(meta_rows(to_np(meta), n_out, k), O.pack_bitmap(keep))
+    q, g = O.quant_acts(x)
+    acc_ref = O.contract(c, q)
+    assert np.array_equal(to_np(acc), acc_ref)
+    check_y(to_np(y), O.rescale_grouped(acc_ref, betas, rpg, g), acc_ref)
+
+
+@pytest.mark.parametrize("fmt,n,m", [(FMT_NM, 6, 8), (FMT_DENSE2, 6, 8), (FMT_NM, 2, 4), (FMT_NM, 5, 8)])
+@pytest.mark.parametrize("n_out,k,rpg", [(64, 128, 1), (300, 1024, 16), (130, 1536, 64), (100, 640, 1000)])
+def test_grouped_matches_oracle(n_out, k, rpg, fmt, n, m):
+    rng = np.random.default_rng([95, n_out, k, rpg, fmt, n, m])
+    bits = synth.gaussian_masters(rng, n_out, k, outlier_frac=0.01)
+    x = synth.gaussian_acts(rng, 3, k, hot_channels=2)
+    _run(bits, x, n, m, fmt, rpg, "gaussian")
+
+
+@pytest.mark.parametrize("rpg", [1, 7, 256])
+def test_grouped_rare_values(rpg):
+    """Zeros, subnormals, tiny and large magnitudes: exact out-of-window sums per group."""
+    rng = np.random.default_rng([96, rpg])
+    bits = synth.rare_mixture(rng, 260, 512)
+    x = synth.gaussian_acts(rng, 2, 512)
+    _run(bits, x, 6, 8, FMT_NM, rpg, "rare mixture")
+
+
+def test_grouped_large_groups_decode_and_prefill():
+    """Groups spanning many absmean workgroups; GEMV (4 tokens) and GEMM (40 tokens) products."""
+    rng = np.random.default_rng(97)
+    bits = synth.gaussian_masters(rng, 2048, 4096)
+    for t in (4, 40):
+        _run(bits, synth.gaussian_acts(rng, t, 4096), 6, 8, FMT_NM, 512, f"{t} tokens")
