@@ -65,6 +65,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM measurement")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-qw-sweep", action="store_true", help="skip the weight-preparation sweep")
     p.add_argument("--no-gemv-sweep", action="store_true",
                    help="skip the GEMV weight-bandwidth table over the decode configurations")
     p.add_argument("--copy-calibration-mb", type=float, default=0.0,
@@ -292,6 +293,7 @@ def main():
     gemv = None
     if not args.no_gemv_sweep:
         gemv = gemv_sweep(torch, np, sbl, dev, synth)
+    qw_sweep = None if args.no_qw_sweep else weight_prep_sweep(torch, np, sbl, dev, synth, tm)
 
     # ---------------- prefill GEMM (3B block, M = 2048 tokens), int8 ops
     prefill = prefill_24 = backward = None
@@ -339,6 +341,7 @@ def main():
         "roofline_gemv": roofline_gemv,
         "per_call": per_call,
         "gemv": gemv,
+        "weight_prep": qw_sweep,
         "prefill": prefill,
         "prefill_2of4_sparse_mfma": prefill_24,
         "backward": backward,
@@ -347,6 +350,56 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
+
+
+def weight_prep_sweep(torch, np, sbl, dev, synth, tm):
+    """sbl_quant_weights_batch over whole blocks (7 matrices, 6:8 N:M output), the per-step
+    weight preparation: algorithmic bytes (masters read once + packed codes and metadata
+    written) per second.  Masters are N(0, 0.02) BF16 drawn on the device; each block
+    rotates over >= 2 distinct copies totalling >= 600 MB; HIP graphs, HIP events."""
+    n, m, fmt = 6, 8, 1
+    cases = [("0p7b", 1536, 4096), ("3b", 3200, 8640), ("13b", 5120, 13824)]
+    out = []
+    for wl, h, f in cases:
+        mats = synth.block_shapes(h, f)
+        bw = sum(no * k for _, no, k in mats)
+        copies = max(2, int(np.ceil(600e6 / (2 * bw))))
+        g = torch.Generator(device=dev).manual_seed(5)
+        pool = []
+        for c in range(copies):
+            its = []
+            for _, no, k in mats:
+                w = (torch.randn((no, k), generator=g, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16)
+                its.append(dict(w=w, beta=torch.empty(1, device=dev),
+                                packed=torch.empty(sbl.sbl_packed_bytes(no, k, n, m, fmt), dtype=torch.uint8,
+                                                   device=dev),
+                                meta=torch.empty((no, k // 8), dtype=torch.uint8, device=dev),
+                                workspace=sbl.new_workspace(no, k, dev)))
+            pool.append(its)
+        graphs = []
+        for c in range(copies):
+            sbl.sbl_quant_weights_batch(pool[c], n, m, fmt)
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                sbl.sbl_quant_weights_batch(pool[c], n, m, fmt)
+            graphs.append(gr)
+        reps = max(20, 2 * copies)
+        for r in range(copies):
+            graphs[r].replay()
+        torch.cuda.synchronize()
+        tm.start()
+        for r in range(reps):
+            graphs[r % copies].replay()
+        us = tm.stop_ms() / reps * 1e3
+        alg = sum(2 * no * k + sbl.sbl_packed_bytes(no, k, n, m, fmt) + no * k // 8 for _, no, k in mats)
+        gbps = alg / (us * 1e-6) / 1e9
+        out.append({"block": wl, "weights": bw, "us_per_call": round(us, 2), "alg_GBps": round(gbps, 1),
+                    "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                    "path": "one launch (resident_kernel)" if bw * 2 <= 67e6 else "two launches (absmean + mask_pack)"})
+        del pool, graphs
+        torch.cuda.empty_cache()
+    return out
 
 
 def gemv_sweep(torch, np, sbl, dev, synth):
