@@ -45,6 +45,9 @@ listed with its reason in the design notes):
 
 Group scales (`quant_weights_grouped`, `rescale_grouped`): one absmean
 beta per block of consecutive output rows instead of one per matrix.
+Activation groups (`quant_acts_kgrouped`, `linear_kgrouped`): one gamma per
+token and block of kg features; each block's product is rescaled on its own
+and the blocks' fp32 results are added in ascending block order.
 
 Backward (dual straight-through estimator; readings listed with the
 function `backward`): the scales are constants, the incoming gradient is
@@ -455,6 +458,37 @@ def rescale_grouped(acc: np.ndarray, betas: np.ndarray, rows_per_group: int, gam
     g = np.maximum(np.asarray(gamma, dtype=np.float32), EPS_SCALE)
     s = ((g[:, None] * b_rows[None, :]).astype(np.float32) * np.float32(1.0 / QB)).astype(np.float32)
     return (acc.astype(np.float32) * s).astype(np.float32)
+
+
+def quant_acts_kgrouped(x: np.ndarray, kg: int):
+    """Activation groups along k: (q int8 [m_tok][k], gamma fp32 [m_tok][k // kg]),
+    gamma[t, j] = max |x| over features [j kg, (j + 1) kg) of token t, and each
+    feature quantized with its block's gamma exactly as quant_acts does."""
+    x = np.asarray(x, dtype=np.float32)
+    t, k = x.shape
+    if kg < 1 or k % kg:
+        raise ValueError("kg must divide k")
+    q = np.zeros((t, k), np.int8)
+    gam = np.zeros((t, k // kg), np.float32)
+    for j in range(k // kg):
+        q[:, j * kg:(j + 1) * kg], gam[:, j] = quant_acts(x[:, j * kg:(j + 1) * kg])
+    return q, gam
+
+
+def linear_kgrouped(codes: np.ndarray, q: np.ndarray, betas: np.ndarray, rows_per_group: int,
+                    gamma: np.ndarray, kg: int):
+    """(acc int32 [m_tok][n_out][G], y fp32): per feature block j the exact
+    product acc_j, rescaled with beta of the row's group and gamma[t, j] (the two
+    roundings of rescale), and the blocks' fp32 results added in ascending j."""
+    c = np.asarray(codes, dtype=np.int8)
+    qq = np.asarray(q, dtype=np.int8)
+    n_out, k = c.shape
+    groups = k // kg
+    acc = np.stack([contract(c[:, j * kg:(j + 1) * kg], qq[:, j * kg:(j + 1) * kg]) for j in range(groups)], axis=2)
+    y = np.zeros((qq.shape[0], n_out), np.float32)
+    for j in range(groups):
+        y = (y + rescale_grouped(acc[:, :, j], betas, rows_per_group, np.asarray(gamma)[:, j])).astype(np.float32)
+    return acc, y
 
 
 # --------------------------------------------------------------------------

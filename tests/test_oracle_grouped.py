@@ -82,3 +82,56 @@ def test_rescale_grouped_two_roundings():
             assert y[t, r] == want
     # one group: the per-matrix rescale
     assert np.array_equal(O.rescale_grouped(acc, betas[:1], 10, gamma), O.rescale(acc, betas[0], gamma))
+
+
+def test_kgroups_one_group_is_the_method():
+    rng = np.random.default_rng(404)
+    bits = synth.gaussian_masters(rng, 24, 192)
+    x = synth.gaussian_acts(rng, 3, 192, hot_channels=2)
+    beta, keep, codes = O.quant_weights(bits, 6, 8)
+    q1, g1 = O.quant_acts(x)
+    q, g = O.quant_acts_kgrouped(x, 192)
+    assert np.array_equal(q, q1) and np.array_equal(g[:, 0], g1)
+    acc, y = O.linear_kgrouped(codes, q, np.array([beta]), 24, g, 192)
+    a1, y1 = O.linear(codes, q1, beta, g1)
+    assert np.array_equal(acc[:, :, 0], a1) and np.array_equal(y, y1)
+
+
+def test_kgroups_blocks_are_independent_quantizations():
+    """Each feature block is the per-token quantizer on that block alone; a hot
+    channel only coarsens its own block; the block products add up to the
+    whole-row product when gamma is the same everywhere."""
+    rng = np.random.default_rng(405)
+    x = synth.gaussian_acts(rng, 4, 256)
+    x[:, 70] = 100.0                                     # a hot channel in block 1 of 4 (kg = 64)
+    q, g = O.quant_acts_kgrouped(x, 64)
+    for j in range(4):
+        qj, gj = O.quant_acts(x[:, 64 * j:64 * (j + 1)])
+        assert np.array_equal(q[:, 64 * j:64 * (j + 1)], qj) and np.array_equal(g[:, j], gj)
+    assert np.all(g[:, 1] > 10 * g[:, 0])
+    bits = synth.gaussian_masters(rng, 16, 256)
+    beta, keep, codes = O.quant_weights(bits, 6, 8)
+    acc, _ = O.linear_kgrouped(codes, q, np.array([beta]), 16, g, 64)
+    assert np.array_equal(acc.sum(axis=2), O.contract(codes, q))
+
+
+def test_kgroups_sum_in_block_order():
+    """y is the fp32 sum of the blocks' rescaled products in ascending order,
+    checked by a direct loop with Fraction-exact per-block terms."""
+    from fractions import Fraction
+    rng = np.random.default_rng(406)
+    bits = synth.gaussian_masters(rng, 8, 192)
+    x = synth.gaussian_acts(rng, 2, 192)
+    betas, keep, codes = O.quant_weights_grouped(bits, 2, 4, 3)
+    q, g = O.quant_acts_kgrouped(x, 64)
+    acc, y = O.linear_kgrouped(codes, q, betas, 3, g, 64)
+    for t in range(2):
+        for r in range(8):
+            tot = np.float32(0)
+            b = Fraction(float(max(np.float32(betas[r // 3]), np.float32(1e-5))))
+            for j in range(3):
+                gj = Fraction(float(max(np.float32(g[t, j]), np.float32(1e-5))))
+                s = Fraction(float(np.float32(float(b * gj)))) / 128
+                term = np.float32(float(Fraction(int(acc[t, r, j])) * s))
+                tot = np.float32(tot + term)
+            assert y[t, r] == tot
