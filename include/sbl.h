@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SBL_ABI_VERSION 7
+#define SBL_ABI_VERSION 8
 
 typedef enum {
   SBL_OK = 0,
@@ -317,6 +317,27 @@ int sbl_quant_weights_grouped(const uint16_t* w_bf16, int64_t n_out, int64_t k, 
 int sbl_linear_grouped(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
                        const float* beta, int64_t rows_per_group, const int8_t* xq, const float* gamma,
                        int64_t m_tok, int64_t n_out, int64_t k, float* y, int32_t* acc, sbl_stream stream);
+
+/* Activation groups along k (the same article and section): one gamma per
+ * token and block of kg consecutive features (kg a multiple of 64 dividing
+ * k; k / kg <= 65535, m_tok <= 65535).
+ *   gamma      [m_tok][k / kg] fp32 output: gamma[t][j] = max |x| over block j.
+ *   xq         [m_tok][k] int8 output: each feature quantized as
+ *              sbl_quant_acts does, with its block's gamma.
+ * Alignment 4 bytes for x and gamma; buffers must not overlap. */
+int sbl_quant_acts_kgrouped(const float* x, int64_t m_tok, int64_t k, int64_t kg, int8_t* xq, float* gamma,
+                            sbl_stream stream);
+
+/* Products with activation groups (and beta per row group; rows_per_group
+ * >= n_out for one beta per matrix):
+ *   y[t][r] = sum over blocks j, in ascending order, in fp32, of
+ *             RN(fp32(acc_j[t][r]) * RN(RN(beta_eff[r / rows_per_group] *
+ *             gamma_eff[t][j]) * 2^-7)),  acc_j = the exact product of block j.
+ * xq and gamma from sbl_quant_acts_kgrouped with the same kg.  Validation as
+ * sbl_linear; a plain reference kernel (one wave per output), not tuned. */
+int sbl_linear_kgrouped(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
+                        const float* beta, int64_t rows_per_group, const int8_t* xq, const float* gamma, int64_t kg,
+                        int64_t m_tok, int64_t n_out, int64_t k, float* y, sbl_stream stream);
 
 /* Backward of the layer under the dual straight-through estimator
  * (Sparse-BitNet summaries: Spanish section 2, "Estrategia de Entrenamiento",

@@ -7,7 +7,8 @@ package does not load the library: `sbl.load()` (or the first call) does.
 
 from .sbl import (SBL_FMT_DENSE2, SBL_FMT_NM, SblError, linear, load, new_workspace, quant_acts,
                   quant_weights, sbl_abi_version, sbl_linear, sbl_linear_acts_batch, sbl_linear_backward,
-                  sbl_linear_batch, sbl_linear_grouped, sbl_meta_bytes, sbl_quant_weights_grouped,
+                  sbl_linear_batch, sbl_linear_grouped, sbl_linear_kgrouped, sbl_meta_bytes,
+                  sbl_quant_acts_kgrouped, sbl_quant_weights_grouped,
                   sbl_workspace_bytes_grouped,
                   sbl_pack,
                   sbl_packed_bytes, sbl_quant_acts, sbl_quant_weights, sbl_quant_weights_batch,
@@ -17,7 +18,8 @@ from .sbl import (SBL_FMT_DENSE2, SBL_FMT_NM, SblError, linear, load, new_worksp
 __all__ = [
     "SBL_FMT_DENSE2", "SBL_FMT_NM", "SblError", "linear", "load", "new_workspace", "quant_acts",
     "quant_weights", "sbl_abi_version", "sbl_linear", "sbl_linear_acts_batch", "sbl_linear_backward",
-    "sbl_linear_batch", "sbl_linear_grouped", "sbl_meta_bytes", "sbl_quant_weights_grouped",
+    "sbl_linear_batch", "sbl_linear_grouped", "sbl_linear_kgrouped", "sbl_meta_bytes",
+    "sbl_quant_acts_kgrouped", "sbl_quant_weights_grouped",
     "sbl_workspace_bytes_grouped",
     "sbl_pack",
     "sbl_packed_bytes", "sbl_quant_acts", "sbl_quant_weights", "sbl_quant_weights_batch",

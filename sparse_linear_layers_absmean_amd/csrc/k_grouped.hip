@@ -77,7 +77,98 @@ __global__ void rescale_grouped_kernel(const int32_t* __restrict__ acc, const fl
   }
 }
 
+// Activation groups along k: workgroup (j, t) quantizes features
+// [j kg, (j + 1) kg) of token t with that block's own gamma = max |x| over the
+// block, exactly as the per-token quantizer does over a whole row:
+// s = max(gamma, 1e-5) / 128 (exact), q = clamp(rint(x / s), -127, 127).
+__global__ __launch_bounds__(256) void quant_acts_kgrouped_kernel(const float* __restrict__ x, int64_t k, int64_t kg,
+                                                                  int8_t* __restrict__ xq, float* __restrict__ gamma) {
+  const int64_t j = blockIdx.x, t = blockIdx.y, groups = k / kg;
+  const float* xr = x + t * k + j * kg;
+  float mx = 0.0f;
+  for (int64_t i = threadIdx.x; i < kg; i += 256) mx = fmaxf(mx, fabsf(xr[i]));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  const float g = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float sc = fmaxf(g, 1e-5f) * 0.0078125f;
+  int8_t* qr = xq + t * k + j * kg;
+  for (int64_t i = threadIdx.x; i < kg; i += 256) {
+    const float r = rintf(xr[i] / sc);
+    qr[i] = (int8_t)(int32_t)fminf(fmaxf(r, -127.0f), 127.0f);
+  }
+  if (threadIdx.x == 0) gamma[t * groups + j] = g;
+}
+
+// Products with activation groups: one wave per (output row, token).  Lane l
+// takes weight l of every 64-weight block (decoded from the packed stream),
+// block j's exact int32 product is reduced across the wave, rescaled with
+// beta of the row's group and gamma[t][j] (the two roundings of the
+// per-matrix epilogue), and the blocks' fp32 results are added in ascending j.
+__device__ __forceinline__ int code_of(const uint8_t* packed, const uint8_t* meta, int64_t n_out, int nkb, int fmt,
+                                       int n, int m, int64_t row, int kb, int p) {
+  uint32_t u;
+  if (fmt == 0) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(packed + panel_offset(n_out, nkb, 16, row, kb) + 4 * (p >> 4));
+    const int e = p & 15;
+    u = (w >> (8 * (e & 3) + 2 * (e >> 2))) & 3u;
+  } else {
+    const uint2 mv = *reinterpret_cast<const uint2*>(meta + panel_offset(n_out, nkb, 8, row, kb));
+    const uint64_t keep = (uint64_t)mv.x | ((uint64_t)mv.y << 32);
+    if (!((keep >> p) & 1u)) return 0;
+    const int g0 = p / m * m;
+    const int idx = p / m * n + __popcll((keep >> g0) & ((1ull << (p - g0)) - 1ull));
+    const uint8_t* cp = packed + panel_offset(n_out, nkb, 16 * n / m, row, kb);
+    u = (cp[idx >> 2] >> (2 * (idx & 3))) & 3u;
+  }
+  return (int)u - 1;
+}
+
+__global__ __launch_bounds__(256) void linear_kgrouped_kernel(const uint8_t* __restrict__ packed,
+                                                              const uint8_t* __restrict__ meta, int fmt, int n, int m,
+                                                              const float* __restrict__ beta, int64_t rpg,
+                                                              const int8_t* __restrict__ xq,
+                                                              const float* __restrict__ gamma, int64_t kg,
+                                                              int64_t n_out, int64_t k, float* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), t = blockIdx.y;
+  if (row >= n_out) return;                                 // uniform in the wave
+  const int nkb = (int)(k / 64);
+  const int64_t groups = k / kg, bpg = kg / 64;
+  const float b = fmaxf(beta[row / rpg], 1e-5f);
+  float yacc = 0.0f;
+  for (int64_t j = 0; j < groups; ++j) {
+    int part = 0;
+    for (int64_t i = 0; i < bpg; ++i) {
+      const int kb = (int)(j * bpg + i);
+      part += code_of(packed, meta, n_out, nkb, fmt, n, m, row, kb, lane) * (int)xq[t * k + 64 * (int64_t)kb + lane];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+    const float sc = (b * fmaxf(gamma[t * groups + j], 1e-5f)) * (1.0f / 128.0f);
+    yacc = yacc + (float)part * sc;
+  }
+  if (lane == 0) y[t * n_out + row] = yacc;
+}
+
 }  // namespace
+
+hipError_t launch_quant_acts_kgrouped(const float* x, int64_t m_tok, int64_t k, int64_t kg, int8_t* xq, float* gamma,
+                                      hipStream_t s) {
+  hipLaunchKernelGGL(quant_acts_kgrouped_kernel, dim3((unsigned)(k / kg), (unsigned)m_tok), dim3(256), 0, s, x, k, kg,
+                     xq, gamma);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_kgrouped(const uint8_t* packed, const uint8_t* meta, int fmt, int n, int m, const float* beta,
+                                  int64_t rows_per_group, const int8_t* xq, const float* gamma, int64_t kg,
+                                  int64_t m_tok, int64_t n_out, int64_t k, float* y, hipStream_t s) {
+  hipLaunchKernelGGL(linear_kgrouped_kernel, dim3((unsigned)((n_out + 3) / 4), (unsigned)m_tok), dim3(256), 0, s,
+                     packed, meta, fmt, n, m, beta, rows_per_group, xq, gamma, kg, n_out, k, y);
+  return hipGetLastError();
+}
 
 hipError_t launch_grouped_beta(const uint16_t* w, int64_t n_out, int64_t k, int64_t rows_per_group, float* beta,
                                uint64_t* ws, hipStream_t s) {

@@ -383,6 +383,35 @@ int sbl_linear_grouped(const uint8_t* packed, const uint8_t* meta, int32_t fmt, 
   return launch_status(sbl::launch_rescale_grouped(acc, beta, rows_per_group, gamma, m_tok, n_out, y, s));
 }
 
+int sbl_quant_acts_kgrouped(const float* x, int64_t m_tok, int64_t k, int64_t kg, int8_t* xq, float* gamma,
+                            sbl_stream stream) {
+  if (m_tok < 0 || m_tok > 65535 || !k_ok(k) || kg < 64 || kg % 64 != 0 || k % kg != 0 || k / kg > 65535)
+    return SBL_ERR_SHAPE;
+  if (m_tok == 0) return SBL_OK;
+  if (!x || !xq || !gamma) return SBL_ERR_NULL;
+  if (!aligned(x, 4) || !aligned(gamma, 4)) return SBL_ERR_ALIGN;
+  if (ranges_overlap(x, m_tok * k * 4, xq, m_tok * k) || ranges_overlap(x, m_tok * k * 4, gamma, m_tok * (k / kg) * 4) ||
+      ranges_overlap(xq, m_tok * k, gamma, m_tok * (k / kg) * 4))
+    return SBL_ERR_SHAPE;
+  return launch_status(sbl::launch_quant_acts_kgrouped(x, m_tok, k, kg, xq, gamma,
+                                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+int sbl_linear_kgrouped(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
+                        const float* beta, int64_t rows_per_group, const int8_t* xq, const float* gamma, int64_t kg,
+                        int64_t m_tok, int64_t n_out, int64_t k, float* y, sbl_stream stream) {
+  if (rows_per_group < 1 || kg < 64 || kg % 64 != 0 || k % kg != 0 || m_tok > 65535) return SBL_ERR_SHAPE;
+  const sbl_linear_item it{packed, meta, beta, xq, gamma, m_tok, n_out, k, y, nullptr};
+  const int st = check_linear(it, fmt, n, m);
+  if (st != SBL_OK || m_tok == 0 || n_out == 0) return st;
+  if (ranges_overlap(y, m_tok * n_out * 4, gamma, m_tok * (k / kg) * 4) ||
+      ranges_overlap(y, m_tok * n_out * 4, beta, 4 * ((n_out + rows_per_group - 1) / rows_per_group)))
+    return SBL_ERR_SHAPE;
+  return launch_status(sbl::launch_linear_kgrouped(packed, fmt == SBL_FMT_NM ? meta : nullptr, fmt, n, m, beta,
+                                                   rows_per_group, xq, gamma, kg, m_tok, n_out, k, y,
+                                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
 int sbl_linear_backward(const uint16_t* dy_bf16, int64_t m_tok, int64_t n_out, int64_t k, const uint8_t* packed,
                         const uint8_t* meta, int32_t fmt, int32_t n, int32_t m, const float* beta, const float* x,
                         const int8_t* xq, const float* gamma, float* dx, float* dw, sbl_stream stream) {

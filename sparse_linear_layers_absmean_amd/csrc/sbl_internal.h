@@ -199,6 +199,13 @@ hipError_t launch_grouped_beta(const uint16_t* w, int64_t n_out, int64_t k, int6
 hipError_t launch_rescale_grouped(const int32_t* acc, const float* beta, int64_t rows_per_group, const float* gamma,
                                   int64_t m_tok, int64_t n_out, float* y, hipStream_t s);
 
+// Activation groups along k (kg features per gamma; kg % 64 == 0, k % kg == 0)
+hipError_t launch_quant_acts_kgrouped(const float* x, int64_t m_tok, int64_t k, int64_t kg, int8_t* xq, float* gamma,
+                                      hipStream_t s);
+hipError_t launch_linear_kgrouped(const uint8_t* packed, const uint8_t* meta, int fmt, int n, int m, const float* beta,
+                                  int64_t rows_per_group, const int8_t* xq, const float* gamma, int64_t kg,
+                                  int64_t m_tok, int64_t n_out, int64_t k, float* y, hipStream_t s);
+
 // Backward of the layer (k_backward.hip): dx and/or dw (each nullable).
 struct BackwardArgs {
   const uint16_t* dy;             // [m_tok][n_out] BF16

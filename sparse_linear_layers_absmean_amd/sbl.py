@@ -24,7 +24,7 @@ SBL_FMT_NM = 1
 # weight-preparation variants and execution choices (sbl_quant_weights_batch_ex flags)
 SBL_QW_DEFAULT, SBL_QW_BETA_KEPT, SBL_QW_MASK_FROM_CODES = 0, 1, 2
 SBL_QW_TWO_PASS, SBL_QW_NO_WAIT = 4, 8
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32
@@ -105,6 +105,11 @@ def load():
     lib.sbl_linear_grouped.restype = ctypes.c_int
     lib.sbl_linear_grouped.argtypes = [_c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_i64, _c_p, _c_p,
                                        _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]
+    lib.sbl_quant_acts_kgrouped.restype = ctypes.c_int
+    lib.sbl_quant_acts_kgrouped.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]
+    lib.sbl_linear_kgrouped.restype = ctypes.c_int
+    lib.sbl_linear_kgrouped.argtypes = [_c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_i64, _c_p, _c_p, _c_i64,
+                                        _c_i64, _c_i64, _c_i64, _c_p, _c_p]
     lib.sbl_linear_backward.restype = ctypes.c_int
     lib.sbl_linear_backward.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
                                         _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]
@@ -299,6 +304,31 @@ def sbl_linear_grouped(packed, meta, fmt: int, n: int, m: int, beta, rows_per_gr
                                 m_tok, n_out, k, _ptr(y, torch.float32, m_tok * n_out * 4, "y"),
                                 _ptr(acc, torch.int32, m_tok * n_out * 4, "acc"), _stream(stream))
     _check("sbl_linear_grouped", st)
+
+
+def sbl_quant_acts_kgrouped(x, kg: int, xq, gamma, stream=None):
+    """x fp32 [m_tok][k] -> xq int8 [m_tok][k], gamma fp32 [m_tok][k // kg]."""
+    lib = load()
+    m_tok, k = x.shape
+    st = lib.sbl_quant_acts_kgrouped(_ptr(x, torch.float32, m_tok * k * 4, "x"), m_tok, k, kg,
+                                     _ptr(xq, torch.int8, m_tok * k, "xq"),
+                                     _ptr(gamma, torch.float32, m_tok * (k // kg) * 4, "gamma"), _stream(stream))
+    _check("sbl_quant_acts_kgrouped", st)
+
+
+def sbl_linear_kgrouped(packed, meta, fmt: int, n: int, m: int, beta, rows_per_group: int, xq, gamma, kg: int,
+                        n_out: int, y, stream=None):
+    lib = load()
+    m_tok, k = xq.shape
+    groups = -(-n_out // rows_per_group) if rows_per_group > 0 else 1
+    pb = lib.sbl_packed_bytes(n_out, k, n, m, fmt) if n_out > 0 else 0
+    st = lib.sbl_linear_kgrouped(_ptr(packed, torch.uint8, max(pb, 0), "packed"),
+                                 _ptr(meta, torch.uint8, n_out * k // 8, "meta") if fmt == SBL_FMT_NM else None,
+                                 fmt, n, m, _ptr(beta, torch.float32, 4 * groups, "beta"), rows_per_group,
+                                 _ptr(xq, torch.int8, m_tok * k, "xq"),
+                                 _ptr(gamma, torch.float32, m_tok * (k // kg) * 4, "gamma"), kg, m_tok, n_out, k,
+                                 _ptr(y, torch.float32, m_tok * n_out * 4, "y"), _stream(stream))
+    _check("sbl_linear_kgrouped", st)
 
 
 def sbl_linear_backward(dy, packed, meta, fmt: int, n: int, m: int, beta, x, xq, gamma, dx=None, dw=None,

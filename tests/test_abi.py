@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.sbl_abi_version() == 7
+    assert lib.sbl_abi_version() == 8
     for st in range(7):
         assert len(lib.sbl_status_string(st)) > 0
     assert lib.sbl_last_hip_error() == 0
@@ -345,3 +345,25 @@ def test_grouped_validation(lib):
     assert lin(acc=None) == 1
     assert lin(acc=A + 6 * F + 4) == 2                      # acc overlaps y
     assert lin(fmt=3) == 4
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation runs only on GPU-less hosts")
+def test_kgrouped_validation(lib):
+    F = 1 << 40
+    qa = lib.sbl_quant_acts_kgrouped
+    assert qa(A, 2, 256, 96, A + F, A + 2 * F, None) == 2          # kg % 64
+    assert qa(A, 2, 256, 192, A + F, A + 2 * F, None) == 2         # kg does not divide k
+    assert qa(A, 0, 256, 64, None, None, None) == 0                # no tokens: no-op
+    assert qa(None, 2, 256, 64, A + F, A + 2 * F, None) == 1
+    assert qa(A + 2, 2, 256, 64, A + F, A + 2 * F, None) == 3
+    assert qa(A, 2, 256, 64, A + 16, A + 2 * F, None) == 2         # xq overlaps x
+    lk = lib.sbl_linear_kgrouped
+
+    def lin(rpg=4, kg=64, y=A + 6 * F, gamma=A + 8 * F, fmt=1):
+        return lk(A + 2 * F, A + 3 * F, fmt, 6, 8, A + F, rpg, A + 7 * F, gamma, kg, 2, 16, 256, y, None)
+
+    assert lin(rpg=0) == 2
+    assert lin(kg=100) == 2
+    assert lin(kg=512) == 2
+    assert lin(fmt=3) == 4
+    assert lin(y=A + 8 * F + 4) == 2                                # y overlaps gamma

@@ -74,3 +74,35 @@ def test_grouped_large_groups_decode_and_prefill():
     bits = synth.gaussian_masters(rng, 2048, 4096)
     for t in (4, 40):
         _run(bits, synth.gaussian_acts(rng, t, 4096), 6, 8, FMT_NM, 512, f"{t} tokens")
+
+
+@pytest.mark.parametrize("fmt,n,m", [(FMT_NM, 6, 8), (FMT_DENSE2, 6, 8), (FMT_NM, 2, 4), (FMT_NM, 5, 8)])
+@pytest.mark.parametrize("n_out,k,kg,t,rpg", [(64, 256, 64, 3, 64), (130, 1536, 512, 5, 16), (100, 640, 128, 1, 1000),
+                                               (72, 4096, 4096, 2, 8)])
+def test_activation_groups_match_oracle(n_out, k, kg, t, rpg, fmt, n, m):
+    """gamma per token and block of kg features, beta per row group: xq and gamma
+    bit for bit, and y bit for bit (the same fp32 operations in the same order)."""
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    rng = np.random.default_rng([98, n_out, k, kg, t, fmt, n, m])
+    bits = synth.gaussian_masters(rng, n_out, k)
+    x = synth.gaussian_acts(rng, t, k, hot_channels=3)
+    say(f"activation groups {n_out}x{k} kg={kg} t={t} rows_per_group={rpg} {n}:{m} fmt={fmt}")
+    groups = -(-n_out // rpg)
+    beta = torch.empty(groups, device="cuda")
+    packed = torch.empty(sbl.sbl_packed_bytes(n_out, k, n, m, fmt), dtype=torch.uint8, device="cuda")
+    meta = torch.empty((n_out, k // 8), dtype=torch.uint8, device="cuda") if fmt == FMT_NM else None
+    ws = torch.empty(sbl.sbl_workspace_bytes_grouped(n_out, k, rpg), dtype=torch.uint8, device="cuda")
+    sbl.sbl_quant_weights_grouped(to_dev(bits), n, m, rpg, beta, ws, fmt=fmt, packed=packed, meta=meta)
+    xq = torch.empty((t, k), dtype=torch.int8, device="cuda")
+    gamma = torch.empty((t, k // kg), dtype=torch.float32, device="cuda")
+    sbl.sbl_quant_acts_kgrouped(to_dev(x.astype(np.float32)), kg, xq, gamma)
+    y = torch.empty((t, n_out), dtype=torch.float32, device="cuda")
+    sbl.sbl_linear_kgrouped(packed, meta, fmt, n, m, beta, rpg, xq, gamma, kg, n_out, y)
+    torch.cuda.synchronize()
+    q, g = O.quant_acts_kgrouped(x, kg)
+    assert np.array_equal(to_np(xq), q) and np.array_equal(to_np(gamma), g)
+    betas, keep, codes = O.quant_weights_grouped(bits, n, m, rpg)
+    assert np.array_equal(to_np(beta), betas)
+    _, y_ref = O.linear_kgrouped(codes, q, betas, rpg, g, kg)
+    assert np.array_equal(to_np(y), y_ref)
