@@ -291,8 +291,12 @@ def main():
 
     # ---------------- GEMV weight bandwidth over the decode configurations
     gemv = None
+    read_peak = None
     if not args.no_gemv_sweep:
         gemv = gemv_sweep(torch, np, sbl, dev, synth)
+        read_peak = stream_read_peak(torch, dev, tm)
+        for row in gemv:
+            row["frac_of_measured_stream"] = round(row["weight_GBps"] / read_peak["reference_GBps"], 4)
     qw_sweep = None if args.no_qw_sweep else weight_prep_sweep(torch, np, sbl, dev, synth, tm)
 
     # ---------------- prefill GEMM (3B block, M = 2048 tokens), int8 ops
@@ -341,6 +345,7 @@ def main():
         "roofline_gemv": roofline_gemv,
         "per_call": per_call,
         "gemv": gemv,
+        "measured_stream": read_peak,
         "weight_prep": qw_sweep,
         "prefill": prefill,
         "prefill_2of4_sparse_mfma": prefill_24,
@@ -400,6 +405,31 @@ def weight_prep_sweep(torch, np, sbl, dev, synth, tm):
         del pool, graphs
         torch.cuda.empty_cache()
     return out
+
+
+def stream_read_peak(torch, dev, tm):
+    """Measured streaming rates for reference (library kernels, not part of the path),
+    HIP events around 10 runs each: torch's fp32 sum over 2 GB (bytes read), and a
+    1 GB device-to-device copy (bytes read + written)."""
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        tm.start()
+        for _ in range(10):
+            fn()
+        return tm.stop_ms() / 10
+
+    a = torch.ones(512 << 20, dtype=torch.float32, device=dev)
+    sum_gbps = (2 << 30) / (timed(lambda: a.sum()) * 1e-3) / 1e9
+    del a
+    src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    copy_gbps = (2 << 30) / (timed(lambda: dst.copy_(src)) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"sum_fp32_GBps": round(sum_gbps, 1), "copy_GBps": round(copy_gbps, 1),
+            "reference_GBps": round(max(sum_gbps, copy_gbps), 1)}
 
 
 def gemv_sweep(torch, np, sbl, dev, synth):
@@ -462,8 +492,12 @@ def gemv_sweep(torch, np, sbl, dev, synth):
             b.synchronize()
             us = a.elapsed_time(b) * 1e3 / reps
             gbps = block_bytes / (us * 1e-6) / 1e9
+            # all HBM bytes of the block's products: weights, int8 activations, gamma, fp32 outputs
+            hbm = block_bytes + sum(m_tok * mats[g_[0]][2] + 4 * m_tok for g_ in groups) + \
+                sum(4 * m_tok * no for _, no, _k in mats)
             out.append({"block": wl, "format": fname, "m_tok": m_tok, "weight_bytes": block_bytes,
                         "us_per_block": round(us, 2), "weight_GBps": round(gbps, 1),
+                        "hbm_GBps": round(hbm / (us * 1e-6) / 1e9, 1),
                         "frac": round(gbps / HBM_PEAK_GBPS, 4)})
             del pool, graphs, xs
             torch.cuda.empty_cache()
@@ -509,6 +543,7 @@ def bench_prefill(torch, np, synth, sbl, dev, tm, n=6, m=8):
     return {"workload": f"Prefill GEMM, M=2048 tokens, 3B-class block (hidden 3200, FFN 8640), {n}:{m} N:M",
             "kernel": kernel,
             "ms_per_block": round(ms, 4), "int8_TOPS": round(tops, 2),
+            "useful_TOPS": round(tops * n / m, 2),
             "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS,
                          "unit": "TOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": None}}
 
