@@ -63,6 +63,7 @@ def parse():
     p.add_argument("--pool-mb", type=float, default=560.0,
                    help="minimum bytes of distinct BF16 master copies the steps rotate over")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--no-group-scales", action="store_true", help="skip the group-scale timings")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM measurement")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-qw-sweep", action="store_true", help="skip the weight-preparation sweep")
@@ -305,6 +306,7 @@ def main():
         prefill = bench_prefill(torch, np, synth, sbl, dev, tm)
         prefill_24 = bench_prefill(torch, np, synth, sbl, dev, tm, n=2, m=4)
         backward = bench_backward(torch, np, synth, sbl, dev, tm)
+    group_scales = None if args.no_group_scales else bench_group_scales(torch, np, sbl, dev, synth, tm)
 
     # ---------------- CPU oracle baseline
     cpu = None
@@ -350,6 +352,7 @@ def main():
         "prefill": prefill,
         "prefill_2of4_sparse_mfma": prefill_24,
         "backward": backward,
+        "group_scales": group_scales,
         "cpu_baseline": cpu,
         "input_gen_s": round(gen_s, 1),
         "device": torch.cuda.get_device_name(0),
@@ -404,6 +407,105 @@ def weight_prep_sweep(torch, np, sbl, dev, synth, tm):
                     "path": "one launch (resident_kernel)" if bw * 2 <= 67e6 else "two launches (absmean + mask_pack)"})
         del pool, graphs
         torch.cuda.empty_cache()
+    return out
+
+
+def bench_group_scales(torch, np, sbl, dev, synth, tm, rpg=128, kg=320, n=6, m=8):
+    """Group scales on a 3B-class block (hidden 3200, FFN 8640), 6:8 N:M, M = 1: weight
+    preparation with beta per block of rows (rows_per_group 1 and rpg), and the decode
+    products with beta per row group (sbl_linear_grouped) and with gamma per block of kg
+    features as well (sbl_quant_acts_kgrouped + sbl_linear_kgrouped), beside the per-matrix
+    sbl_linear (kg = 320 = 5 x 64 divides both k = 3200 and k = 8640).  Each block's calls are
+    one HIP graph; every block uses distinct buffers from a pool of >= 600 MB.
+    Rates are algorithmic bytes: masters read + packed codes and metadata written for the
+    weights, packed codes and metadata read for the products."""
+    fmt = 1
+    mats = synth.block_shapes(3200, 8640)
+    bw = sum(no * k for _, no, k in mats)
+    g = torch.Generator(device=dev).manual_seed(7)
+    pb = [sbl.sbl_packed_bytes(no, k, n, m, fmt) for _, no, k in mats]
+    wbytes = sum(pb) + sum(no * k // 8 for _, no, k in mats)
+
+    def timed(fn, copies, reps):
+        graphs = []
+        for c in range(copies):
+            fn(c)
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                fn(c)
+            graphs.append(gr)
+        for gr in graphs:
+            gr.replay()
+        torch.cuda.synchronize()
+        tm.start()
+        for r in range(reps):
+            graphs[r % copies].replay()
+        us = tm.stop_ms() / reps * 1e3
+        del graphs
+        return us
+
+    out = {"workload": f"3B-class block (hidden 3200, FFN 8640), {n}:{m} N:M, M=1", "weight_prep": [],
+           "products": []}
+    copies = max(2, int(np.ceil(600e6 / (2 * bw))))
+    masters = [[(torch.randn((no, k), generator=g, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16)
+                for _, no, k in mats] for _ in range(copies)]
+    outs = [[dict(packed=torch.empty(pb[i], dtype=torch.uint8, device=dev),
+                  meta=torch.empty((no, k // 8), dtype=torch.uint8, device=dev)) for i, (_, no, k) in enumerate(mats)]
+            for _ in range(copies)]
+    for r in (1, rpg):
+        betas = [torch.empty(-(-no // r), device=dev) for _, no, k in mats]
+        wss = [torch.empty(sbl.sbl_workspace_bytes_grouped(no, k, r), dtype=torch.uint8, device=dev)
+               for _, no, k in mats]
+
+        def prep(c):
+            for i, (_, no, k) in enumerate(mats):
+                sbl.sbl_quant_weights_grouped(masters[c][i], n, m, r, betas[i], wss[i], fmt=fmt,
+                                              packed=outs[c][i]["packed"], meta=outs[c][i]["meta"])
+        us = timed(prep, copies, max(10, 2 * copies))
+        gbps = (2 * bw + wbytes) / (us * 1e-6) / 1e9
+        out["weight_prep"].append({"rows_per_group": r, "groups": sum(-(-no // r) for _, no, k in mats),
+                                   "us_per_block": round(us, 1), "alg_GBps": round(gbps, 1),
+                                   "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+    del masters
+    torch.cuda.empty_cache()
+    # products: the rpg-grouped betas of the last preparation; a pool of packed copies
+    pcopies = max(2, int(np.ceil(600e6 / wbytes)))
+    pool = [[{k2: v.clone() for k2, v in o.items()} for o in outs[0]] for _ in range(pcopies)]
+    beta1 = [b[:1].contiguous() for b in betas]
+    xs = [torch.randn((1, k), generator=g, device=dev) for _, no, k in mats]
+    acts = [sbl.quant_acts(x) for x in xs]
+    gq = [(torch.empty((1, k), dtype=torch.int8, device=dev), torch.empty((1, k // kg), device=dev))
+          for _, no, k in mats]
+    ys = [torch.empty((1, no), device=dev) for _, no, k in mats]
+    accs = [torch.empty((1, no), dtype=torch.int32, device=dev) for _, no, k in mats]
+
+    def plain(c):
+        for i, (_, no, k) in enumerate(mats):
+            sbl.sbl_linear(pool[c][i]["packed"], pool[c][i]["meta"], fmt, n, m, beta1[i], acts[i][0], acts[i][1],
+                           no, ys[i], None)
+
+    def grouped(c):
+        for i, (_, no, k) in enumerate(mats):
+            sbl.sbl_linear_grouped(pool[c][i]["packed"], pool[c][i]["meta"], fmt, n, m, betas[i], rpg,
+                                   acts[i][0], acts[i][1], no, ys[i], accs[i])
+
+    def kgrouped(c):
+        for i, (_, no, k) in enumerate(mats):
+            sbl.sbl_quant_acts_kgrouped(xs[i], kg, gq[i][0], gq[i][1])
+            sbl.sbl_linear_kgrouped(pool[c][i]["packed"], pool[c][i]["meta"], fmt, n, m, betas[i], rpg,
+                                    gq[i][0], gq[i][1], kg, no, ys[i])
+
+    for name, fn, what in (("sbl_linear", plain, "per-matrix beta and gamma (one launch per matrix)"),
+                           ("sbl_linear_grouped", grouped, f"beta per {rpg} rows: GEMV + grouped rescale"),
+                           ("sbl_linear_kgrouped", kgrouped,
+                            f"beta per {rpg} rows, gamma per {kg} features: activation quant + product")):
+        us = timed(fn, pcopies, max(20, 2 * pcopies))
+        gbps = wbytes / (us * 1e-6) / 1e9
+        out["products"].append({"call": name, "scales": what, "us_per_block": round(us, 1),
+                                "weight_GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+    del pool, outs
+    torch.cuda.empty_cache()
     return out
 
 
@@ -600,34 +702,54 @@ def bench_backward(torch, np, synth, sbl, dev, tm, n=6, m=8):
 
 
 def cpu_baseline(np, synth, wname, mats, m_tok, n, m, fmt, budget_s, step_bytes):
-    """The CPU oracle, untuned, on the same workload: whole blocks until the budget is spent."""
+    """The CPU oracle, untuned, on the same workload: whole blocks until the
+    budget is spent.  Each stage is one oracle call, timed on its own, in the
+    order the oracle's quant_weights and linear compose them."""
     from threadpoolctl import threadpool_limits
 
     from oracle import sbl_oracle as O
-    done_bytes, blocks, t_total = 0, 0, 0.0
+    done_bytes, blocks, t_total, weights, ops = 0, 0, 0.0, 0, 0
+    stages = dict.fromkeys(("beta", "mask", "codes", "pack", "quant_acts", "contract", "rescale"), 0.0)
+
+    def timed(name, fn, *a):
+        t = time.perf_counter()
+        r = fn(*a)
+        stages[name] += time.perf_counter() - t
+        return r
+
     with threadpool_limits(1):
         while t_total < budget_s and blocks < 3:
             for i, (_, no, k) in enumerate(mats):
                 bits = synth.workload_masters(wname, i, no, k)
                 first = {0: 0, 1: 0, 2: 0, 3: 3, 4: 4, 5: 4, 6: 6}[i]    # shared block inputs
                 x = synth.workload_acts(wname, first, m_tok, k)
-                t = time.perf_counter()
-                beta, keep, codes = O.quant_weights(bits, n, m)
+                beta = timed("beta", O.absmean_beta, bits)
+                keep = timed("mask", O.nm_keep, bits, n, m)
+                codes = timed("codes", lambda: (O.ternarize(bits, beta) * keep.astype(np.int8)).astype(np.int8))
                 if fmt == 1:
-                    O.to_panels(O.pack_nm(codes, keep, n, m), 16 * n // m)
-                    O.to_panels(O.pack_bitmap(keep), 8)
+                    timed("pack", lambda: (O.to_panels(O.pack_nm(codes, keep, n, m), 16 * n // m),
+                                           O.to_panels(O.pack_bitmap(keep), 8)))
                 else:
-                    O.to_panels(O.pack_dense2(codes), 16)
-                q, gamma = O.quant_acts(x)
-                O.linear(codes, q, beta, gamma)
-                t_total += time.perf_counter() - t
+                    timed("pack", lambda: O.to_panels(O.pack_dense2(codes), 16))
+                q, gamma = timed("quant_acts", O.quant_acts, x)
+                acc = timed("contract", O.contract, codes, q)
+                timed("rescale", O.rescale, acc, beta, gamma)
+                weights += no * k
+                ops += 2 * m_tok * no * k
             blocks += 1
             done_bytes += step_bytes
+            t_total = sum(stages.values())
     gbps = done_bytes / t_total / 1e9
+    try:
+        model = next(ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name"))
+    except (OSError, StopIteration):
+        model = None
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{blocks} full block step(s) of the same workload ({len(mats)} matrices), "
                       f"{t_total:.1f} s single-threaded NumPy",
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "stages_s": {k: round(v, 4) for k, v in stages.items()},
+            "weights_per_s": round(weights / t_total, 1), "ops_per_s": round(ops / t_total, 1),
+            "host_cpus": len(os.sched_getaffinity(0)), "host_cpu_model": model}
 
 
 if __name__ == "__main__":

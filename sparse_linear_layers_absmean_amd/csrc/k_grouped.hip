@@ -102,55 +102,116 @@ __global__ __launch_bounds__(256) void quant_acts_kgrouped_kernel(const float* _
   if (threadIdx.x == 0) gamma[t * groups + j] = g;
 }
 
-// Products with activation groups: one wave per (output row, token).  Lane l
-// takes weight l of every 64-weight block (decoded from the packed stream),
-// block j's exact int32 product is reduced across the wave, rescaled with
-// beta of the row's group and gamma[t][j] (the two roundings of the
-// per-matrix epilogue), and the blocks' fp32 results are added in ascending j.
-__device__ __forceinline__ int code_of(const uint8_t* packed, const uint8_t* meta, int64_t n_out, int nkb, int fmt,
-                                       int n, int m, int64_t row, int kb, int p) {
-  uint32_t u;
-  if (fmt == 0) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(packed + panel_offset(n_out, nkb, 16, row, kb) + 4 * (p >> 4));
-    const int e = p & 15;
-    u = (w >> (8 * (e & 3) + 2 * (e >> 2))) & 3u;
-  } else {
-    const uint2 mv = *reinterpret_cast<const uint2*>(meta + panel_offset(n_out, nkb, 8, row, kb));
-    const uint64_t keep = (uint64_t)mv.x | ((uint64_t)mv.y << 32);
-    if (!((keep >> p) & 1u)) return 0;
-    const int g0 = p / m * m;
-    const int idx = p / m * n + __popcll((keep >> g0) & ((1ull << (p - g0)) - 1ull));
-    const uint8_t* cp = packed + panel_offset(n_out, nkb, 16 * n / m, row, kb);
-    u = (cp[idx >> 2] >> (2 * (idx & 3))) & 3u;
+// Products with activation groups: one single-wave workgroup per (output row,
+// token).  A pass covers one panel (4 k-blocks): lanes 16c .. 16c+15 take
+// k-block 4p + c, 4 consecutive weights each, and the 16 lanes' int32 sums
+// make that k-block's exact product, kept in LDS.  Then lane j adds up the
+// k-blocks of feature block j (an exact int32 sum) and rescales it with beta
+// of the row's group and gamma[t][j] (the two roundings of the per-matrix
+// epilogue), and lane 0 adds the blocks' fp32 results in ascending j.
+constexpr int kKgPanels = 8;       // panels whose loads are issued together
+
+// The 4 codes (as int, -1/0/+1) of weights 4e .. 4e+3 of k-block kb of `row`.
+// N:M: the kept codes of a block are stored in ascending position, 2 bits
+// each; those of the 4 weights are consecutive, so they lie in 2 bytes.  Each
+// lane loads byte e of its block's codes (with the keep bitmap and the
+// activations, all independent loads); the two bytes a lane needs then come
+// from the 16 lanes of its block by cross-lane reads.
+struct KgLoad {
+  uint32_t w;        // DENSE2: the word holding the 4 fields; N:M: code byte e, then the lane's 2 code bytes
+  uint64_t keep;     // N:M: the block's keep bitmap
+  uint32_t x;        // the 4 int8 activations
+};
+
+__device__ __forceinline__ KgLoad kg_issue(const uint8_t* packed, const uint8_t* meta, const int8_t* xr,
+                                           int64_t n_out, int nkb, int fmt, int n, int m, int64_t row, int kb, int e) {
+  KgLoad L = {0u, 0ull, 0u};
+  if (kb < nkb) {
+    L.x = *reinterpret_cast<const uint32_t*>(xr + 64 * (int64_t)kb + 4 * e);
+    if (fmt == 0) {
+      L.w = *reinterpret_cast<const uint32_t*>(packed + panel_offset(n_out, nkb, 16, row, kb) + 4 * (e >> 2));
+    } else {
+      const uint2 mv = *reinterpret_cast<const uint2*>(meta + panel_offset(n_out, nkb, 8, row, kb));
+      L.keep = (uint64_t)mv.x | ((uint64_t)mv.y << 32);
+      if (e < 16 * n / m) L.w = packed[panel_offset(n_out, nkb, 16 * n / m, row, kb) + e];
+    }
   }
-  return (int)u - 1;
+  return L;
 }
 
-__global__ __launch_bounds__(256) void linear_kgrouped_kernel(const uint8_t* __restrict__ packed,
-                                                              const uint8_t* __restrict__ meta, int fmt, int n, int m,
-                                                              const float* __restrict__ beta, int64_t rpg,
-                                                              const int8_t* __restrict__ xq,
-                                                              const float* __restrict__ gamma, int64_t kg,
-                                                              int64_t n_out, int64_t k, float* __restrict__ y) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), t = blockIdx.y;
-  if (row >= n_out) return;                                 // uniform in the wave
-  const int nkb = (int)(k / 64);
-  const int64_t groups = k / kg, bpg = kg / 64;
-  const float b = fmaxf(beta[row / rpg], 1e-5f);
-  float yacc = 0.0f;
-  for (int64_t j = 0; j < groups; ++j) {
-    int part = 0;
-    for (int64_t i = 0; i < bpg; ++i) {
-      const int kb = (int)(j * bpg + i);
-      part += code_of(packed, meta, n_out, nkb, fmt, n, m, row, kb, lane) * (int)xq[t * k + 64 * (int64_t)kb + lane];
-    }
+// N:M: gather the lane's 2 code bytes (uniform in the wave: every lane takes part)
+__device__ __forceinline__ void kg_gather(KgLoad& L, int n, int m, int lane) {
+  const int e = lane & 15, p0 = 4 * e, g0 = p0 / m * m;
+  const int idx0 = p0 / m * n + __popcll((L.keep >> g0) & ((1ull << (p0 - g0)) - 1ull));
+  // idx0 can be the block's code count when none of the 4 is kept (n <= 4 of
+  // 8): both byte indexes stay inside the block, and then no field is used
+  const int last = (16 * n / m) - 1;                      // the block's last code byte
+  const int b0 = (idx0 >> 2) <= last ? (idx0 >> 2) : last;
+  const int b1 = b0 + 1 <= last ? b0 + 1 : last;
+  const int base = lane & ~15;
+  const uint32_t v0 = (uint32_t)__shfl((int)L.w, base + b0, 64), v1 = (uint32_t)__shfl((int)L.w, base + b1, 64);
+  L.w = (v0 | (v1 << 8)) >> (2 * (idx0 & 3));
+}
+
+__device__ __forceinline__ int kg_dot(const KgLoad& L, int fmt, int e) {
+  int s = 0, j = 0;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-    const float sc = (b * fmaxf(gamma[t * groups + j], 1e-5f)) * (1.0f / 128.0f);
-    yacc = yacc + (float)part * sc;
+  for (int i = 0; i < 4; ++i) {
+    int c;
+    if (fmt == 0) {
+      c = (int)((L.w >> (8 * i + 2 * (e & 3))) & 3u) - 1;
+    } else {
+      const bool kept = (L.keep >> (4 * e + i)) & 1u;
+      c = kept ? (int)((L.w >> (2 * j)) & 3u) - 1 : 0;
+      j += kept ? 1 : 0;
+    }
+    s += c * (int)(int8_t)(L.x >> (8 * i));
   }
-  if (lane == 0) y[t * n_out + row] = yacc;
+  return s;
+}
+
+__global__ __launch_bounds__(64) void linear_kgrouped_kernel(const uint8_t* __restrict__ packed,
+                                                             const uint8_t* __restrict__ meta, int fmt, int n, int m,
+                                                             const float* __restrict__ beta, int64_t rpg,
+                                                             const int8_t* __restrict__ xq,
+                                                             const float* __restrict__ gamma, int64_t kg,
+                                                             int64_t n_out, int64_t k, float* __restrict__ y) {
+  extern __shared__ int32_t kbsum[];                       // [nkb] k-block sums, then [groups] fp32 terms
+  const int lane = threadIdx.x, c = lane >> 4, e = lane & 15;
+  const int64_t row = blockIdx.x, t = blockIdx.y;
+  const int nkb = (int)(k / 64);
+  const int groups = (int)(k / kg), bpg = (int)(kg / 64);
+  const int8_t* xr = xq + t * k;
+  for (int kb0 = 0; kb0 < nkb; kb0 += 4 * kKgPanels) {
+    KgLoad L[kKgPanels];
+#pragma unroll
+    for (int u = 0; u < kKgPanels; ++u)
+      L[u] = kg_issue(packed, meta, xr, n_out, nkb, fmt, n, m, row, kb0 + 4 * u + c, e);
+#pragma unroll
+    for (int u = 0; u < kKgPanels; ++u) {
+      const int kb = kb0 + 4 * u + c;
+      if (fmt != 0) kg_gather(L[u], n, m, lane);
+      int s = kb < nkb ? kg_dot(L[u], fmt, e) : 0;
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);   // within the 16 lanes
+      if (e == 0 && kb < nkb) kbsum[kb] = s;
+    }
+  }
+  __syncthreads();
+  float* term = reinterpret_cast<float*>(kbsum + nkb);
+  const float b = fmaxf(beta[row / rpg], 1e-5f);
+  for (int j = lane; j < groups; j += 64) {
+    int s = 0;
+    for (int i = 0; i < bpg; ++i) s += kbsum[j * bpg + i];
+    const float sc = (b * fmaxf(gamma[t * groups + j], 1e-5f)) * (1.0f / 128.0f);
+    term[j] = (float)s * sc;
+  }
+  __syncthreads();
+  if (lane == 0) {
+    float yacc = 0.0f;
+    for (int j = 0; j < groups; ++j) yacc = yacc + term[j];
+    y[t * n_out + row] = yacc;
+  }
 }
 
 }  // namespace
@@ -165,8 +226,10 @@ hipError_t launch_quant_acts_kgrouped(const float* x, int64_t m_tok, int64_t k, 
 hipError_t launch_linear_kgrouped(const uint8_t* packed, const uint8_t* meta, int fmt, int n, int m, const float* beta,
                                   int64_t rows_per_group, const int8_t* xq, const float* gamma, int64_t kg,
                                   int64_t m_tok, int64_t n_out, int64_t k, float* y, hipStream_t s) {
-  hipLaunchKernelGGL(linear_kgrouped_kernel, dim3((unsigned)((n_out + 3) / 4), (unsigned)m_tok), dim3(256), 0, s,
-                     packed, meta, fmt, n, m, beta, rows_per_group, xq, gamma, kg, n_out, k, y);
+  // LDS: k/64 int32 block sums and k/kg fp32 terms, at most 2 * 2048 words
+  const size_t lds = (size_t)(k / 64 + k / kg) * 4;
+  hipLaunchKernelGGL(linear_kgrouped_kernel, dim3((unsigned)n_out, (unsigned)m_tok), dim3(64), lds, s, packed, meta,
+                     fmt, n, m, beta, rows_per_group, xq, gamma, kg, n_out, k, y);
   return hipGetLastError();
 }
 
