@@ -103,71 +103,72 @@ __global__ __launch_bounds__(256) void quant_acts_kgrouped_kernel(const float* _
 }
 
 // Products with activation groups: one single-wave workgroup per (output row,
-// token).  A pass covers one panel (4 k-blocks): lanes 16c .. 16c+15 take
-// k-block 4p + c, 4 consecutive weights each, and the 16 lanes' int32 sums
-// make that k-block's exact product, kept in LDS.  Then lane j adds up the
+// token).  A pass covers 16 k-blocks (4 panels): lanes 4c .. 4c+3 take
+// k-block c, 16 consecutive weights each, and the 4 lanes' int32 sums make
+// that k-block's exact product, kept in LDS.  Then lane j adds up the
 // k-blocks of feature block j (an exact int32 sum) and rescales it with beta
 // of the row's group and gamma[t][j] (the two roundings of the per-matrix
-// epilogue), and lane 0 adds the blocks' fp32 results in ascending j.
-constexpr int kKgPanels = 8;       // panels whose loads are issued together
+// epilogue), and the blocks' fp32 results are added in ascending j.
+//
+// Weights go in as u = c + 1 in {0, 1, 2} (pruned positions u = 1), so that
+// sum c x = sum u x - sum x, both as v_dot4_i32_i8 over bytes.
+constexpr int kKgPasses = 2;       // passes whose loads are issued together
 
-// The 4 codes (as int, -1/0/+1) of weights 4e .. 4e+3 of k-block kb of `row`.
-// N:M: the kept codes of a block are stored in ascending position, 2 bits
-// each; those of the 4 weights are consecutive, so they lie in 2 bytes.  Each
-// lane loads byte e of its block's codes (with the keep bitmap and the
-// activations, all independent loads); the two bytes a lane needs then come
-// from the 16 lanes of its block by cross-lane reads.
 struct KgLoad {
-  uint32_t w;        // DENSE2: the word holding the 4 fields; N:M: code byte e, then the lane's 2 code bytes
+  u32x4 x;           // the 16 int8 activations
+  uint32_t w;        // DENSE2: the word of the 16 fields; N:M: code bytes 4q .. 4q+3 of the block
   uint64_t keep;     // N:M: the block's keep bitmap
-  uint32_t x;        // the 4 int8 activations
 };
 
+// Every load is independent of the others (no address depends on loaded data).
 __device__ __forceinline__ KgLoad kg_issue(const uint8_t* packed, const uint8_t* meta, const int8_t* xr,
-                                           int64_t n_out, int nkb, int fmt, int n, int m, int64_t row, int kb, int e) {
-  KgLoad L = {0u, 0ull, 0u};
+                                           int64_t n_out, int nkb, int fmt, int n, int m, int64_t row, int kb, int q) {
+  KgLoad L = {u32x4{0u, 0u, 0u, 0u}, 0u, 0ull};
   if (kb < nkb) {
-    L.x = *reinterpret_cast<const uint32_t*>(xr + 64 * (int64_t)kb + 4 * e);
+    L.x = *reinterpret_cast<const u32x4*>(xr + 64 * (int64_t)kb + 16 * q);
     if (fmt == 0) {
-      L.w = *reinterpret_cast<const uint32_t*>(packed + panel_offset(n_out, nkb, 16, row, kb) + 4 * (e >> 2));
+      L.w = *reinterpret_cast<const uint32_t*>(packed + panel_offset(n_out, nkb, 16, row, kb) + 4 * q);
     } else {
       const uint2 mv = *reinterpret_cast<const uint2*>(meta + panel_offset(n_out, nkb, 8, row, kb));
       L.keep = (uint64_t)mv.x | ((uint64_t)mv.y << 32);
-      if (e < 16 * n / m) L.w = packed[panel_offset(n_out, nkb, 16 * n / m, row, kb) + e];
+      const int bb = 16 * n / m;                          // code bytes of a block
+      const uint8_t* cp = packed + panel_offset(n_out, nkb, bb, row, kb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * q + i < bb) L.w |= (uint32_t)cp[4 * q + i] << (8 * i);
     }
   }
   return L;
 }
 
-// N:M: gather the lane's 2 code bytes (uniform in the wave: every lane takes part)
-__device__ __forceinline__ void kg_gather(KgLoad& L, int n, int m, int lane) {
-  const int e = lane & 15, p0 = 4 * e, g0 = p0 / m * m;
-  const int idx0 = p0 / m * n + __popcll((L.keep >> g0) & ((1ull << (p0 - g0)) - 1ull));
-  // idx0 can be the block's code count when none of the 4 is kept (n <= 4 of
-  // 8): both byte indexes stay inside the block, and then no field is used
-  const int last = (16 * n / m) - 1;                      // the block's last code byte
-  const int b0 = (idx0 >> 2) <= last ? (idx0 >> 2) : last;
-  const int b1 = b0 + 1 <= last ? b0 + 1 : last;
-  const int base = lane & ~15;
-  const uint32_t v0 = (uint32_t)__shfl((int)L.w, base + b0, 64), v1 = (uint32_t)__shfl((int)L.w, base + b1, 64);
-  L.w = (v0 | (v1 << 8)) >> (2 * (idx0 & 3));
-}
-
-__device__ __forceinline__ int kg_dot(const KgLoad& L, int fmt, int e) {
-  int s = 0, j = 0;
+// The 16 weights' u as bytes.  N:M: m divides 16, so the lane's weights hold
+// exactly 16 n / m kept codes, stored from code index 16 q n / m on; their
+// 32 n / m bits come from the block's 4 lanes (cross-lane reads, uniform in
+// the wave: every lane takes part).
+__device__ __forceinline__ void kg_decode(const KgLoad& L, int fmt, int n, int m, int lane, uint32_t (&u)[4]) {
+  const int q = lane & 3;
+  if (fmt == 0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int c;
-    if (fmt == 0) {
-      c = (int)((L.w >> (8 * i + 2 * (e & 3))) & 3u) - 1;
-    } else {
-      const bool kept = (L.keep >> (4 * e + i)) & 1u;
-      c = kept ? (int)((L.w >> (2 * j)) & 3u) - 1 : 0;
-      j += kept ? 1 : 0;
-    }
-    s += c * (int)(int8_t)(L.x >> (8 * i));
+    for (int j = 0; j < 4; ++j) u[j] = (L.w >> (2 * j)) & 0x03030303u;   // element 4j + b at bits 8b + 2j
+    return;
   }
-  return s;
+  const int bit0 = q * 32 * n / m;                        // first field's bit in the block's codes
+  const int d0 = bit0 >> 5, base = lane & ~3;
+  const int d1 = d0 + 1 <= 3 ? d0 + 1 : 3;               // d0 = 3 only when n = m (shift 0)
+  const uint32_t lo = (uint32_t)__shfl((int)L.w, base + d0, 64), hi = (uint32_t)__shfl((int)L.w, base + d1, 64);
+  uint32_t f = (uint32_t)((((uint64_t)hi << 32) | lo) >> (bit0 & 31));
+  const uint32_t kp = (uint32_t)(L.keep >> (16 * q)) & 0xFFFFu;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const bool kept = (kp >> (4 * j + b)) & 1u;
+      v |= (kept ? (f & 3u) : 1u) << (8 * b);
+      f = kept ? f >> 2 : f;
+    }
+    u[j] = v;
+  }
 }
 
 __global__ __launch_bounds__(64) void linear_kgrouped_kernel(const uint8_t* __restrict__ packed,
@@ -177,41 +178,52 @@ __global__ __launch_bounds__(64) void linear_kgrouped_kernel(const uint8_t* __re
                                                              const float* __restrict__ gamma, int64_t kg,
                                                              int64_t n_out, int64_t k, float* __restrict__ y) {
   extern __shared__ int32_t kbsum[];                       // [nkb] k-block sums, then [groups] fp32 terms
-  const int lane = threadIdx.x, c = lane >> 4, e = lane & 15;
+  const int lane = threadIdx.x, c = lane >> 2, q = lane & 3;
   const int64_t row = blockIdx.x, t = blockIdx.y;
   const int nkb = (int)(k / 64);
   const int groups = (int)(k / kg), bpg = (int)(kg / 64);
   const int8_t* xr = xq + t * k;
-  for (int kb0 = 0; kb0 < nkb; kb0 += 4 * kKgPanels) {
-    KgLoad L[kKgPanels];
+  for (int kb0 = 0; kb0 < nkb; kb0 += 16 * kKgPasses) {
+    KgLoad L[kKgPasses];
 #pragma unroll
-    for (int u = 0; u < kKgPanels; ++u)
-      L[u] = kg_issue(packed, meta, xr, n_out, nkb, fmt, n, m, row, kb0 + 4 * u + c, e);
+    for (int v = 0; v < kKgPasses; ++v) L[v] = kg_issue(packed, meta, xr, n_out, nkb, fmt, n, m, row, kb0 + 16 * v + c, q);
 #pragma unroll
-    for (int u = 0; u < kKgPanels; ++u) {
-      const int kb = kb0 + 4 * u + c;
-      if (fmt != 0) kg_gather(L[u], n, m, lane);
-      int s = kb < nkb ? kg_dot(L[u], fmt, e) : 0;
+    for (int v = 0; v < kKgPasses; ++v) {
+      const int kb = kb0 + 16 * v + c;
+      uint32_t u[4];
+      kg_decode(L[v], fmt, n, m, lane, u);
+      int s = 0, sx = 0;
 #pragma unroll
-      for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);   // within the 16 lanes
-      if (e == 0 && kb < nkb) kbsum[kb] = s;
+      for (int j = 0; j < 4; ++j) {
+        s = __builtin_amdgcn_sdot4((int)u[j], (int)L[v].x[j], s, false);
+        sx = __builtin_amdgcn_sdot4(0x01010101, (int)L[v].x[j], sx, false);
+      }
+      s -= sx;
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);                           // the k-block's 4 lanes
+      if (q == 0 && kb < nkb) kbsum[kb] = s;
     }
   }
   __syncthreads();
   float* term = reinterpret_cast<float*>(kbsum + nkb);
   const float b = fmaxf(beta[row / rpg], 1e-5f);
+  float tj = 0.0f;
   for (int j = lane; j < groups; j += 64) {
     int s = 0;
     for (int i = 0; i < bpg; ++i) s += kbsum[j * bpg + i];
     const float sc = (b * fmaxf(gamma[t * groups + j], 1e-5f)) * (1.0f / 128.0f);
-    term[j] = (float)s * sc;
+    tj = (float)s * sc;
+    term[j] = tj;
   }
-  __syncthreads();
-  if (lane == 0) {
-    float yacc = 0.0f;
+  float yacc = 0.0f;
+  if (groups <= 64) {                                      // the terms sit in lanes 0 .. groups-1
+    for (int j = 0; j < groups; ++j)
+      yacc = yacc + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tj), j));
+  } else {
+    __syncthreads();
     for (int j = 0; j < groups; ++j) yacc = yacc + term[j];
-    y[t * n_out + row] = yacc;
   }
+  if (lane == 0) y[t * n_out + row] = yacc;
 }
 
 }  // namespace

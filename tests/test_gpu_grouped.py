@@ -78,7 +78,7 @@ def test_grouped_large_groups_decode_and_prefill():
 
 @pytest.mark.parametrize("fmt,n,m", [(FMT_NM, 6, 8), (FMT_DENSE2, 6, 8), (FMT_NM, 2, 4), (FMT_NM, 5, 8)])
 @pytest.mark.parametrize("n_out,k,kg,t,rpg", [(64, 256, 64, 3, 64), (130, 1536, 512, 5, 16), (100, 640, 128, 1, 1000),
-                                               (72, 4096, 4096, 2, 8)])
+                                               (72, 4096, 4096, 2, 8), (40, 8192, 64, 2, 8)])
 def test_activation_groups_match_oracle(n_out, k, kg, t, rpg, fmt, n, m):
     """gamma per token and block of kg features, beta per row group: xq and gamma
     bit for bit, and y bit for bit (the same fp32 operations in the same order)."""
