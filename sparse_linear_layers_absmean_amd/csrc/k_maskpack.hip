@@ -324,7 +324,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       dma_group(rw, (uint32_t)((j + 1) * kThreads), stage);
     }
     const int64_t c = cg + threadIdx.x;
-    if (c < nchunks) mask_pack_chunk<M, DROP, FMT, CODES>(dw, c, d, t2);
+    if (c < nchunks) {
+      // group scales (beta complete before the launch): the beta of this chunk's row group
+      const uint32_t tc =
+          d.beta_rows > 0 ? (__float_as_uint(fmaxf(d.beta[c / d.nkb / d.beta_rows], 1e-5f) * 0.5f) >> 16) * kOnes : t2;
+      mask_pack_chunk<M, DROP, FMT, CODES>(dw, c, d, tc);
+    }
   }
 }
 
@@ -744,9 +749,9 @@ int64_t grid_for(int64_t nchunks) {
 hipError_t launch_mask_pack(QBatch& b, int n, int m, hipStream_t s, bool dry, int64_t* grid_out,
                             bool mask_from_codes) {
   const int drop = m - n;
-  bool grouped = false;                              // group scales: the per-key kernel reads beta per row
+  bool grouped = false;                              // group scales: beta per row group, complete beforehand
   for (int i = 0; i < b.count; ++i) grouped = grouped || b.d[i].beta_rows > 0;
-  const bool fast = drop <= 2 && !mask_from_codes && !grouped;
+  const bool fast = drop <= 2 && !mask_from_codes && (!grouped || b.beta_ready);
   const int64_t per_block = fast ? (int64_t)kThreads * kCPT : kThreads;   // chunks per workgroup
   int64_t blocks = 0;
   for (int i = 0; i < b.count; ++i) {

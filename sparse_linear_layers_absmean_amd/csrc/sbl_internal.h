@@ -95,7 +95,7 @@ struct QDesc {
   float* beta;
   uint64_t* ws;
   int64_t ws_words;       // workspace size
-  int64_t beta_rows;      // > 0: group scales, beta[row / beta_rows] (mask/pack kernel only)
+  int64_t beta_rows;      // > 0: group scales, beta[row / beta_rows] (mask/pack kernels, beta complete)
   uint8_t* mask;          // nullable outputs
   int8_t* codes;
   uint8_t* packed;
