@@ -106,3 +106,37 @@ def test_activation_groups_match_oracle(n_out, k, kg, t, rpg, fmt, n, m):
     assert np.array_equal(to_np(beta), betas)
     _, y_ref = O.linear_kgrouped(codes, q, betas, rpg, g, kg)
     assert np.array_equal(to_np(y), y_ref)
+
+
+@pytest.mark.parametrize("rpg", [1, 128])
+@pytest.mark.parametrize("idx", [4, 6])
+def test_group_scales_at_benchmark_shapes(idx, rpg):
+    """The group-scale benchmark's configuration: a 3B-class gate (8640 x 3200)
+    or down (3200 x 8640) matrix of the decode workload, 6:8 N:M, M = 1.
+    Weights and the beta-per-row-group product against the oracle in full,
+    then the activation-group product (gamma per 320 features) bit for bit."""
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    name, n_out, k = synth.block_shapes(3200, 8640)[idx]
+    bits = synth.workload_masters("b3", idx, n_out, k)
+    x = synth.workload_acts("b3", idx, 1, k)
+    _run(bits, x, 6, 8, FMT_NM, rpg, f"3B {name}")
+    kg = 320
+    say(f"activation groups 3B {name} kg={kg} rows_per_group={rpg}")
+    groups = -(-n_out // rpg)
+    beta = torch.empty(groups, device="cuda")
+    packed = torch.empty(sbl.sbl_packed_bytes(n_out, k, 6, 8, FMT_NM), dtype=torch.uint8, device="cuda")
+    meta = torch.empty((n_out, k // 8), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(sbl.sbl_workspace_bytes_grouped(n_out, k, rpg), dtype=torch.uint8, device="cuda")
+    sbl.sbl_quant_weights_grouped(to_dev(bits), 6, 8, rpg, beta, ws, fmt=FMT_NM, packed=packed, meta=meta)
+    xq = torch.empty((1, k), dtype=torch.int8, device="cuda")
+    gamma = torch.empty((1, k // kg), dtype=torch.float32, device="cuda")
+    sbl.sbl_quant_acts_kgrouped(to_dev(x.astype(np.float32)), kg, xq, gamma)
+    y = torch.empty((1, n_out), dtype=torch.float32, device="cuda")
+    sbl.sbl_linear_kgrouped(packed, meta, FMT_NM, 6, 8, beta, rpg, xq, gamma, kg, n_out, y)
+    torch.cuda.synchronize()
+    q, g = O.quant_acts_kgrouped(x, kg)
+    assert np.array_equal(to_np(xq), q) and np.array_equal(to_np(gamma), g)
+    betas, keep, codes = O.quant_weights_grouped(bits, 6, 8, rpg)
+    _, y_ref = O.linear_kgrouped(codes, q, betas, rpg, g, kg)
+    assert np.array_equal(to_np(y), y_ref)
