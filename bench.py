@@ -120,8 +120,8 @@ class Timer:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding is a design note, not a measured path", file=sys.stderr)
+        print(f"bench.py: the library runs and is measured on one GPU (asked for --gpus {args.gpus}); "
+              "sharding across GPUs is described, not implemented", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
