@@ -307,6 +307,7 @@ def main():
         prefill_24 = bench_prefill(torch, np, synth, sbl, dev, tm, n=2, m=4)
         backward = bench_backward(torch, np, synth, sbl, dev, tm)
     group_scales = None if args.no_group_scales else bench_group_scales(torch, np, sbl, dev, synth, tm)
+    library_gemm = None if args.no_prefill else library_gemm_reference(torch, dev, tm)
 
     # ---------------- CPU oracle baseline
     cpu = None
@@ -348,6 +349,7 @@ def main():
         "per_call": per_call,
         "gemv": gemv,
         "measured_stream": read_peak,
+        "measured_library_gemm": library_gemm,
         "weight_prep": qw_sweep,
         "prefill": prefill,
         "prefill_2of4_sparse_mfma": prefill_24,
@@ -532,6 +534,43 @@ def stream_read_peak(torch, dev, tm):
     torch.cuda.empty_cache()
     return {"sum_fp32_GBps": round(sum_gbps, 1), "copy_GBps": round(copy_gbps, 1),
             "reference_GBps": round(max(sum_gbps, copy_gbps), 1)}
+
+
+def library_gemm_reference(torch, dev, tm):
+    """Measured matrix-core rates of library GEMMs (references, not part of the path), HIP events
+    around 10 runs each, at the 3B-class gate shape with 2048 tokens (2048 x 3200 by 3200 x 8640):
+    int8 x int8 -> int32 (torch._int_mm) for the prefill GEMM, and BF16 (torch.matmul, fp32
+    accumulation) for the backward's products."""
+    m_tok, k, n_out = 2048, 3200, 8640
+    flops = 2 * m_tok * k * n_out
+    out = {"shape": f"{m_tok} x {k} by {k} x {n_out}"}
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        tm.start()
+        for _ in range(10):
+            fn()
+        return tm.stop_ms() / 10
+
+    g = torch.Generator(device=dev).manual_seed(3)
+    try:
+        a = torch.randint(-127, 128, (m_tok, k), generator=g, device=dev, dtype=torch.int8)
+        b = torch.randint(-1, 2, (n_out, k), generator=g, device=dev, dtype=torch.int8).t()
+        ms = timed(lambda: torch._int_mm(a, b))
+        out["int8_TOPS"] = round(flops / (ms * 1e-3) / 1e12, 1)
+        out["int8_frac"] = round(flops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
+    except (RuntimeError, AttributeError) as e:
+        out["int8_error"] = str(e).splitlines()[0][:160]
+    a = torch.randn((m_tok, k), generator=g, device=dev).to(torch.bfloat16)
+    b = torch.randn((k, n_out), generator=g, device=dev).to(torch.bfloat16)
+    ms = timed(lambda: torch.matmul(a, b))
+    out["bf16_TFLOPS"] = round(flops / (ms * 1e-3) / 1e12, 1)
+    out["bf16_frac"] = round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    del a, b
+    torch.cuda.empty_cache()
+    return out
 
 
 def gemv_sweep(torch, np, sbl, dev, synth):
