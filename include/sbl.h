@@ -334,7 +334,8 @@ int sbl_quant_acts_kgrouped(const float* x, int64_t m_tok, int64_t k, int64_t kg
  *             RN(fp32(acc_j[t][r]) * RN(RN(beta_eff[r / rows_per_group] *
  *             gamma_eff[t][j]) * 2^-7)),  acc_j = the exact product of block j.
  * xq and gamma from sbl_quant_acts_kgrouped with the same kg.  Validation as
- * sbl_linear; a plain reference kernel (one wave per output), not tuned. */
+ * sbl_linear.  One single-wave workgroup per output (a decode kernel: the
+ * weights are read again for every token; no matrix cores). */
 int sbl_linear_kgrouped(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
                         const float* beta, int64_t rows_per_group, const int8_t* xq, const float* gamma, int64_t kg,
                         int64_t m_tok, int64_t n_out, int64_t k, float* y, sbl_stream stream);
