@@ -9,7 +9,8 @@ oracle and the HIP path can be fed from it without sharing any method code.
 Distributions:
   * master weights: fp32 N(0, 0.02^2), rounded to BF16 (round to nearest even);
     the 3B-class blocks scale a seeded 1% of entries by 10 before rounding;
-    the 13B-class training workload then plants exact and near ties.
+    the 13B-class training workload then plants exact and near ties on the
+    6:8 keep boundary (`plant_ties`).
   * activations: fp32 N(0, 1); the 3B decode workload scales 8 seeded channels
     by 20; the 3B prefill workload draws a seeded 25% of rows from Student-t(4).
 
@@ -68,37 +69,49 @@ def gaussian_masters(rng, n_out: int, k: int, sigma: float = 0.02,
     return f32_to_bf16_bits(w)
 
 
-def plant_ties(bits: np.ndarray, rng, m: int = 8, frac_exact: float = 0.25,
+def plant_ties(bits: np.ndarray, rng, m: int = 8, n: int = 6, frac_exact: float = 0.25,
                frac_near: float = 0.25) -> np.ndarray:
-    """Plant exact and near magnitude ties inside groups of m along k.
+    """Plant exact and near magnitude ties on the n:m keep boundary.
 
-    In a seeded `frac_exact` of the groups, two other positions take the
-    magnitude of a randomly chosen position (signs kept): exact ties.  In a
-    disjoint `frac_near` of the groups, two other positions take that magnitude
-    plus or minus one BF16 ulp: near ties.  Only bit patterns are copied.
+    Groups are m consecutive positions of a row.  The boundary magnitude b of
+    a group is its n-th largest |w| (the smallest one an n:m mask keeps).
+      * In a seeded `frac_exact` of the groups, three positions take the
+        magnitude b: one of the m - n positions below the boundary and two
+        others drawn at random (never the position holding b).  Each such
+        group then has equal magnitudes on both sides of the boundary.
+      * In a disjoint `frac_near` of the groups, one position below the
+        boundary takes b + s and another random position b - s, with
+        s = +-1 BF16 ulp: the n-th and (n+1)-th largest magnitudes then
+        differ by at most one ulp.
+    Signs are kept; only the 15 magnitude bits change.
     """
     b = bits.reshape(-1, m).copy()
     g = b.shape[0]
-    u = rng.random(g)
-    src = rng.integers(0, m, g)
-    # two distinct destinations different from the source
-    d1 = (src + 1 + rng.integers(0, m - 1, g)) % m
-    d2 = (src + 1 + rng.integers(0, m - 1, g)) % m
-    d2 = np.where(d2 == d1, (d1 + 1) % m, d2)
-    d2 = np.where(d2 == src, (d2 + 1) % m, d2)
-    d2 = np.where(d2 == d1, (d1 + 1) % m, d2)
     rows = np.arange(g)
-    mag = (b[rows, src] & 0x7FFF).astype(np.int32)
+    mag = (b & 0x7FFF).astype(np.int32)
+    order = np.argsort(-mag, axis=1, kind="stable")
+    src = order[:, n - 1]
+    bmag = mag[rows, src]
+    u = rng.random(g)
     exact = u < frac_exact
     near = (u >= frac_exact) & (u < frac_exact + frac_near)
-    step = np.where(rng.random(g) < 0.5, -1, 1)
-    near_mag = np.clip(mag + step, 1, 0x7F7F)
-    for d, extra in ((d1, 0), (d2, 1)):
-        sign = b[rows, d] & 0x8000
-        new_exact = (sign | mag).astype(np.uint16)
-        new_near = (sign | (near_mag if extra else np.clip(mag - step, 1, 0x7F7F))).astype(np.uint16)
-        b[rows[exact], d[exact]] = new_exact[exact]
-        b[rows[near], d[near]] = new_near[near]
+    low = order[rows, n + rng.integers(0, m - n, g)]
+    keys = rng.random((g, m))
+    keys[rows, src] = 2.0
+    keys[rows, low] = 2.0
+    others = np.argsort(keys, axis=1)[:, :2]
+    s = np.where(rng.random(g) < 0.5, -1, 1)
+
+    def put(sel, col, value):
+        r, c = rows[sel], col[sel]
+        v = np.clip(value[sel], 0, 0x7F7F)
+        b[r, c] = (b[r, c] & 0x8000) | v.astype(np.uint16)
+
+    put(exact, low, bmag)
+    put(exact, others[:, 0], bmag)
+    put(exact, others[:, 1], bmag)
+    put(near, low, bmag + s)
+    put(near, others[:, 0], bmag - s)
     return b.reshape(bits.shape)
 
 

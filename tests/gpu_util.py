@@ -3,7 +3,9 @@
 
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -11,6 +13,48 @@ from oracle import sbl_oracle as O
 
 FMT_DENSE2, FMT_NM = 0, 1
 Y_RTOL = 1e-6          # fp32 outputs: relative error bound (exact zeros where acc == 0)
+
+
+def _workers() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def par_map(fn, args):
+    """fn over args on a thread pool, results in order (the oracle's NumPy
+    array operations release the interpreter lock)."""
+    args = list(args)
+    if len(args) <= 1:
+        return [fn(a) for a in args]
+    with ThreadPoolExecutor(min(_workers(), len(args))) as ex:
+        return list(ex.map(fn, args))
+
+
+def _row_blocks(n_rows: int):
+    step = max(16, -(-n_rows // (4 * _workers())))
+    return [(r, min(r + step, n_rows)) for r in range(0, n_rows, step)]
+
+
+def oracle_weight_rows(bits: np.ndarray, beta, n: int, m: int):
+    """The oracle's mask and masked codes for a whole matrix, by row blocks
+    (rows are independent given beta): (keep bool, codes int8)."""
+    def one(rr):
+        b = bits[rr[0]:rr[1]]
+        keep = O.nm_keep(b, n, m)
+        return keep, O.ternarize(b, beta) * keep.astype(np.int8)
+    parts = par_map(one, _row_blocks(bits.shape[0]))
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+
+def oracle_packed_panels(codes: np.ndarray, keep: np.ndarray, fmt: int, n: int, m: int):
+    """The oracle's packed stream and N:M metadata (None for DENSE2), in the
+    panel-major storage order, flat."""
+    def one(rr):
+        c, kp = codes[rr[0]:rr[1]], keep[rr[0]:rr[1]]
+        return O.pack_dense2(c) if fmt == FMT_DENSE2 else O.pack_nm(c, kp, n, m)
+    rows = np.concatenate(par_map(one, _row_blocks(codes.shape[0])))
+    packed = O.to_panels(rows, block_bytes(fmt, n, m))
+    meta = O.to_panels(O.pack_bitmap(keep), 8) if fmt == FMT_NM else None
+    return packed, meta
 
 
 def say(*a):

@@ -102,10 +102,10 @@ def test_beta_subnormal_mean_and_zero_matrix():
 
 
 def test_ties_planted():
-    bits = synth.plant_ties(synth.gaussian_masters(np.random.default_rng(5), 128, 512),
-                            np.random.default_rng(6))
+    base = synth.gaussian_masters(np.random.default_rng(5), 128, 512)
     x = synth.gaussian_acts(np.random.default_rng(8), 3, 512)
     for n, m in [(6, 8), (2, 4)]:
+        bits = synth.plant_ties(base, np.random.default_rng(6), m=m, n=n)
         for fmt, fname in FORMATS:
             say(f"ties {n}:{m} {fname}")
             compare_all(gpu_forward(bits, x, n, m, fmt), oracle_forward(bits, x, n, m), fmt, 128)
@@ -185,7 +185,9 @@ def test_linear_batch_matches_single_calls(fmt, n, m):
     from sparse_linear_layers_absmean_amd import sbl
     rng = np.random.default_rng([21, fmt, n, m])
     shapes = [(96, 128, 1), (200, 320, 3), (33, 64, 16), (130, 512, 2), (64, 192, 40), (17, 256, 1),
-              (300, 640, 5), (48, 128, 8), (80, 384, 1), (16, 64, 1)]
+              (300, 640, 5), (48, 128, 8), (80, 384, 1), (16, 64, 1),
+              # several items above the decode range: one grouped GEMM launch (2:4: sparse MFMA)
+              (300, 640, 33), (130, 512, 200), (520, 1216, 150)]
     items, refs = [], []
     for n_out, k, m_tok in shapes:
         bits = synth.gaussian_masters(rng, n_out, k)
@@ -224,7 +226,7 @@ def test_gemm24_edge_shapes(n_out, k, m_tok):
     step (K = 64), K covering the unrolled loop plus a tail, 17 tokens (just
     above the decode range), ragged and exact tiles (64 rows x 128 tokens)."""
     rng = np.random.default_rng([37, n_out, k, m_tok])
-    bits = synth.plant_ties(synth.gaussian_masters(rng, n_out, k), rng)
+    bits = synth.plant_ties(synth.gaussian_masters(rng, n_out, k), rng, m=4, n=2)
     x = synth.gaussian_acts(rng, m_tok, k, t_row_frac=0.25)
     say(f"gemm 2:4 sparse MFMA n_out={n_out} k={k} m_tok={m_tok}")
     compare_all(gpu_forward(bits, x, 2, 4, FMT_NM), oracle_forward(bits, x, 2, 4), FMT_NM, n_out)
