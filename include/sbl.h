@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SBL_ABI_VERSION 8
+#define SBL_ABI_VERSION 9
 
 typedef enum {
   SBL_OK = 0,
@@ -206,6 +206,32 @@ enum {
 };
 int sbl_quant_weights_batch_ex(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m,
                                int32_t fmt, int32_t flags, sbl_stream stream);
+
+/* Allocation-free weight preparation, for callers that cannot allocate
+ * device memory (code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation): sbl_quant_weights_batch with the
+ * exact-beta scratch taken from a fixed array inside the library instead of
+ * the items' workspaces, whose workspace and workspace_bytes fields are
+ * ignored.
+ *  - The array holds SBL_NOALLOC_SCRATCH_BYTES (4 MiB) on every GPU the
+ *    library runs on, until the process ends.  Item i takes
+ *    sbl_workspace_bytes(n_out, k) of it, rounded up to 256 bytes; a batch
+ *    needing more in all returns SBL_ERR_WORKSPACE before anything is
+ *    enqueued (73 items of up to 2^31 weights each always fit).
+ *  - The array of the CURRENT device is used; `stream` must belong to it.
+ *    The first call on a device looks up the array's address once; no call
+ *    allocates or frees memory.
+ *  - Every call on one GPU shares that GPU's array: calls that can overlap
+ *    on one GPU (different streams or threads without ordering) race and
+ *    give undefined results.  Order them, e.g. on one stream.
+ *  - Nothing in the array has to start at zero, and it needs no clearing
+ *    between calls: a call reads only words it writes itself, plus one
+ *    generation word per item whose starting value does not matter.
+ * Validation and errors as sbl_quant_weights_batch; results are
+ * bit-identical to it. */
+#define SBL_NOALLOC_SCRATCH_BYTES (4 << 20)
+int sbl_quant_weights_batch_noalloc(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m,
+                                    int32_t fmt, sbl_stream stream);
 
 /* Packing alone: ternary codes (+ mask) -> packed bytes.
  *   codes      [n_out][k] int8 in {-1,0,1} (other values: unspecified bytes).

@@ -12,6 +12,7 @@ from .sbl import (SBL_FMT_DENSE2, SBL_FMT_NM, SblError, linear, load, new_worksp
                   sbl_workspace_bytes_grouped,
                   sbl_pack,
                   sbl_packed_bytes, sbl_quant_acts, sbl_quant_weights, sbl_quant_weights_batch,
+                  sbl_quant_weights_batch_noalloc,
                   sbl_workspace_bytes,
                   sbl_workspace_init)
 
@@ -23,6 +24,7 @@ __all__ = [
     "sbl_workspace_bytes_grouped",
     "sbl_pack",
     "sbl_packed_bytes", "sbl_quant_acts", "sbl_quant_weights", "sbl_quant_weights_batch",
+    "sbl_quant_weights_batch_noalloc",
     "sbl_workspace_bytes",
     "sbl_workspace_init",
 ]

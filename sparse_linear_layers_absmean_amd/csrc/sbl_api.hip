@@ -1,4 +1,6 @@
 // C ABI of libsbl: host-side validation and kernel dispatch.  See include/sbl.h.
+#include <mutex>
+
 #include "sbl.h"
 #include "sbl_internal.h"
 
@@ -80,7 +82,9 @@ bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
   return a && b && a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
 }
 
-int check_quant(const sbl_quant_item& it, int32_t n, int32_t m, int32_t fmt) {
+// own_ws: the item brings its workspace (checked here); false when the call
+// supplies the scratch itself (sbl_quant_weights_batch_noalloc).
+int check_quant(const sbl_quant_item& it, int32_t n, int32_t m, int32_t fmt, bool own_ws = true) {
   if (!it.w_bf16 || !it.beta) return SBL_ERR_NULL;
   if (it.packed && fmt == SBL_FMT_NM && !it.meta) return SBL_ERR_NULL;
   if (it.n_out < 1 || !k_ok(it.k) || it.n_out * it.k > kMaxElems) return SBL_ERR_SHAPE;
@@ -97,11 +101,11 @@ int check_quant(const sbl_quant_item& it, int32_t n, int32_t m, int32_t fmt) {
         ranges_overlap(it.codes, it.n_out * it.k, meta, mask_b) || ranges_overlap(packed, packed_b, meta, mask_b))
       return SBL_ERR_SHAPE;
   }
-  if (!it.workspace || it.workspace_bytes < sbl::workspace_bytes_for(it.n_out * it.k))
+  if (own_ws && (!it.workspace || it.workspace_bytes < sbl::workspace_bytes_for(it.n_out * it.k)))
     return SBL_ERR_WORKSPACE;
   if (!nm_ok(n, m)) return SBL_ERR_UNSUPPORTED;
   if (it.packed && fmt != SBL_FMT_DENSE2 && fmt != SBL_FMT_NM) return SBL_ERR_UNSUPPORTED;
-  if (!aligned(it.w_bf16, 16) || !aligned(it.beta, 4) || !aligned(it.workspace, 16) ||
+  if (!aligned(it.w_bf16, 16) || !aligned(it.beta, 4) || (own_ws && !aligned(it.workspace, 16)) ||
       (it.mask_bits && !aligned(it.mask_bits, 16)) || (it.codes && !aligned(it.codes, 16)) ||
       (it.packed && !aligned(it.packed, 16)) || (it.meta && !aligned(it.meta, 16)))
     return SBL_ERR_ALIGN;
@@ -220,6 +224,68 @@ int sbl_quant_weights_batch_ex(const sbl_quant_item* items, int32_t count, int32
       if (overlaps(items[i], items[j])) return SBL_ERR_WORKSPACE;
   }
   return launch_quant(items, count, n, m, fmt, flags, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free weight preparation: the exact-beta scratch of every item
+// comes from one fixed device array per GPU instead of caller workspaces.
+// The array's name is a host-side stand-in; its device address on each GPU
+// is looked up once (hipGetSymbolAddress, with that device current) and only
+// that address is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[SBL_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};         // device address of `scratch` per device
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+int current_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return launch_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return SBL_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return launch_status(e);
+    if (!p) return launch_status(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SBL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sbl_quant_weights_batch_noalloc(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m,
+                                    int32_t fmt, sbl_stream stream) {
+  if (!items) return SBL_ERR_NULL;
+  if (count < 1 || count > 256) return SBL_ERR_SHAPE;
+  sbl_quant_item local[256];
+  int64_t offset[256];
+  int64_t used = 0;
+  for (int i = 0; i < count; ++i) {
+    const int st = check_quant(items[i], n, m, fmt, false);
+    if (st != SBL_OK) return st;
+    local[i] = items[i];
+    local[i].workspace_bytes = sbl::workspace_bytes_for(items[i].n_out * items[i].k);
+    offset[i] = used;
+    used += (local[i].workspace_bytes + 255) / 256 * 256;
+    if (used > SBL_NOALLOC_SCRATCH_BYTES) return SBL_ERR_WORKSPACE;
+  }
+  void* base = nullptr;
+  const int st = current_scratch(&base);
+  if (st != SBL_OK) return st;
+  for (int i = 0; i < count; ++i) local[i].workspace = static_cast<uint8_t*>(base) + offset[i];
+  return launch_quant(local, count, n, m, fmt, 0, reinterpret_cast<hipStream_t>(stream));
 }
 
 int sbl_pack(const int8_t* codes, const uint8_t* mask_bits, int64_t n_out, int64_t k, int32_t n,

@@ -24,7 +24,7 @@ SBL_FMT_NM = 1
 # weight-preparation variants and execution choices (sbl_quant_weights_batch_ex flags)
 SBL_QW_DEFAULT, SBL_QW_BETA_KEPT, SBL_QW_MASK_FROM_CODES = 0, 1, 2
 SBL_QW_TWO_PASS, SBL_QW_NO_WAIT = 4, 8
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32
@@ -85,6 +85,9 @@ def load():
     lib.sbl_quant_weights_batch_ex.restype = ctypes.c_int
     lib.sbl_quant_weights_batch_ex.argtypes = [ctypes.POINTER(QuantItem), _c_i32, _c_i32, _c_i32, _c_i32,
                                                _c_i32, _c_p]
+    lib.sbl_quant_weights_batch_noalloc.restype = ctypes.c_int
+    lib.sbl_quant_weights_batch_noalloc.argtypes = [ctypes.POINTER(QuantItem), _c_i32, _c_i32, _c_i32, _c_i32,
+                                                    _c_p]
     lib.sbl_pack.restype = ctypes.c_int
     lib.sbl_pack.argtypes = [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p]
     lib.sbl_quant_acts.restype = ctypes.c_int
@@ -204,10 +207,7 @@ def _nbytes(t):
     return t.numel() * t.element_size() if t is not None else 0
 
 
-def sbl_quant_weights_batch(items, n: int, m: int, fmt: int = SBL_FMT_DENSE2, stream=None, flags: int = 0):
-    """items: sequence of dicts with keys w (BF16 [n_out][k]), beta, workspace and the
-    optional outputs mask_bits, codes, packed, meta (as in sbl_quant_weights)."""
-    lib = load()
+def _quant_items(lib, items, n: int, m: int, fmt: int, workspaces: bool = True):
     arr = (QuantItem * len(items))()
     for i, it in enumerate(items):
         w = it["w"]
@@ -215,20 +215,38 @@ def sbl_quant_weights_batch(items, n: int, m: int, fmt: int = SBL_FMT_DENSE2, st
         packed = it.get("packed")
         pb = lib.sbl_packed_bytes(n_out, k, n, m, fmt) if packed is not None else 0
         mb = n_out * k // 8
-        ws = it["workspace"]
+        ws = it["workspace"] if workspaces else None
         arr[i] = QuantItem(
             _ptr(w, _W16, n_out * k * 2, "w"), n_out, k, _ptr(it["beta"], torch.float32, 4, "beta"),
             _ptr(it.get("mask_bits"), torch.uint8, mb, "mask_bits"),
             _ptr(it.get("codes"), torch.int8, n_out * k, "codes"),
             _ptr(packed, torch.uint8, max(pb, 0), "packed"),
             _ptr(it.get("meta"), torch.uint8, mb, "meta") if fmt == SBL_FMT_NM else None,
-            _ptr(ws, None, lib.sbl_workspace_bytes(n_out, k), "workspace"), _nbytes(ws))
+            _ptr(ws, None, lib.sbl_workspace_bytes(n_out, k), "workspace") if workspaces else None,
+            _nbytes(ws))
+    return arr
+
+
+def sbl_quant_weights_batch(items, n: int, m: int, fmt: int = SBL_FMT_DENSE2, stream=None, flags: int = 0):
+    """items: sequence of dicts with keys w (BF16 [n_out][k]), beta, workspace and the
+    optional outputs mask_bits, codes, packed, meta (as in sbl_quant_weights)."""
+    lib = load()
+    arr = _quant_items(lib, items, n, m, fmt)
     if flags:
         _check("sbl_quant_weights_batch_ex",
                lib.sbl_quant_weights_batch_ex(arr, len(items), n, m, fmt, flags, _stream(stream)))
     else:
         _check("sbl_quant_weights_batch",
                lib.sbl_quant_weights_batch(arr, len(items), n, m, fmt, _stream(stream)))
+
+
+def sbl_quant_weights_batch_noalloc(items, n: int, m: int, fmt: int = SBL_FMT_DENSE2, stream=None):
+    """sbl_quant_weights_batch without caller workspaces: the library's fixed
+    per-GPU scratch array serves every item (a "workspace" key is ignored)."""
+    lib = load()
+    arr = _quant_items(lib, items, n, m, fmt, workspaces=False)
+    _check("sbl_quant_weights_batch_noalloc",
+           lib.sbl_quant_weights_batch_noalloc(arr, len(items), n, m, fmt, _stream(stream)))
 
 
 def sbl_pack(codes, mask_bits, n: int, m: int, fmt: int, packed, meta=None, stream=None):

@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.sbl_abi_version() == 8
+    assert lib.sbl_abi_version() == 9
     for st in range(7):
         assert len(lib.sbl_status_string(st)) > 0
     assert lib.sbl_last_hip_error() == 0
@@ -367,3 +367,39 @@ def test_kgrouped_validation(lib):
     assert lin(kg=512) == 2
     assert lin(fmt=3) == 4
     assert lin(y=A + 8 * F + 4) == 2                                # y overlaps gamma
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation runs only on GPU-less hosts")
+def test_quant_weights_batch_noalloc_validation(lib):
+    """The allocation-free entry point validates items as the batch call does
+    (workspace fields ignored) and rejects batches whose exact-beta scratch
+    exceeds the library's fixed array, all before any HIP call."""
+    from sparse_linear_layers_absmean_amd.sbl import QuantItem
+    f = lib.sbl_quant_weights_batch_noalloc
+    limit = 4 << 20
+
+    def item(**kw):
+        a = dict(w_bf16=A, n_out=4, k=64, beta=A, mask_bits=A, codes=None, packed=A + (2 << 16), meta=A + (1 << 16),
+                 workspace=None, workspace_bytes=0)
+        a.update(kw)
+        return QuantItem(**a)
+
+    def call(items, count=None, n=6, m=8, fmt=1):
+        arr = (QuantItem * len(items))(*items)
+        return f(arr, len(items) if count is None else count, n, m, fmt, None)
+
+    assert f(None, 1, 6, 8, 1, None) == 1
+    assert call([item()], count=0) == 2
+    assert call([item()], count=257) == 2
+    assert call([item(), item(w_bf16=None)]) == 1
+    assert call([item(), item(meta=None)]) == 1
+    assert call([item(), item(k=96)]) == 2
+    assert call([item()], n=9) == 4
+    assert call([item()], fmt=2) == 4
+    assert call([item(), item(w_bf16=A + 2)]) == 3
+    # scratch: 2^34-weight items need the largest workspace each; too many of them overflow
+    big = lib.sbl_workspace_bytes(1 << 17, 1 << 17)
+    fits = limit // (-(-big // 256) * 256)
+    assert call([item(n_out=1 << 17, k=1 << 17, mask_bits=None, packed=None, meta=None)] * (fits + 1)) == 6
+    small = lib.sbl_workspace_bytes(1 << 15, 1 << 16)            # 2^31 weights
+    assert limit // small >= 73
