@@ -1,29 +1,36 @@
 #!/usr/bin/env python3
 """Benchmark of the Sparse-BitLinear hot path on one MI355X.
 
-A step is one pass of the whole path over one batch of synthetic input: for
-each of the 7 matrices of a transformer block (q, k, v, o, gate, up, down)
-  sbl_quant_weights      exact absmean beta + N:M mask from the BF16 masters +
-                         ternary codes + packing (the per-training-step recompute)
-  sbl_linear_acts_batch  per input of the block (q/k/v, o, gate/up, down): its
-                         per-token absmax int8 quantization and the ternary x
-                         int8 products + fp32 rescale that read it (one fused
-                         GEMV launch at decode sizes)
-Default workload: decode of a 0.7B-class block (hidden 1536, FFN 4096), one
-token, 6:8 N:M format.  Inputs are seeded synthetic data resident in HBM; the
-steps rotate over enough distinct copies (>= 512 MB) that the 256 MB
-Infinity Cache cannot serve a step from the previous one.
+Headline (`value`): decode of a 70B-class transformer block (hidden 8192,
+FFN 28672: q, k, v, o 8192x8192, gate, up 28672x8192, down 8192x28672), one
+token, 6:8 N:M packed ternary weights.  A step is the block's decode pass:
+for each of its 4 inputs (q/k/v share one, o, gate/up share one, down)
+`sbl_linear_acts_batch` quantizes the token (per-token absmax int8) and runs
+the ternary x int8 products with the fp32 rescale, one fused GEMV launch per
+input.  The weights were prepared before the timed region by
+`sbl_quant_weights_batch` (exact absmean beta, 6:8 mask from the BF16
+masters, ternary codes, packing), as a decoder prepares them once at load.
+`value` is the packed weight bytes (codes + metadata) streamed per second.
+Steps rotate over distinct copies of the packed weights (>= 560 MB), so the
+256 MB Infinity Cache cannot serve a step from the previous one.
 
-Printed: one JSON line.  `value` is the step's algorithmic bytes (BF16
-masters read once, packed codes written and read, activations, outputs) per
-second; the `roofline*` objects give per-kernel rates from HIP-event timing of
-back-to-back launches; `cpu_baseline` times the CPU oracle on a bounded
-sample of the same workload.
+Side measurements in the same line: prefill GEMMs (3B-class block, 2048
+tokens, 6:8 / DENSE2 on the dense int8 MFMA, 2:4 on the sparse MFMA; 13B-class
+block, 4096 tokens), the 13B training-step path (per-step weight preparation
++ forward GEMMs), the weight-preparation sweep, the whole path on a 0.7B-class
+block, the GEMV table over every decode configuration, the backward, the group
+scales, library reference rates, and the CPU oracle on a bounded sample of
+the headline workload.
+
+Printed: one JSON line.  `--sections` selects parts (for profiler runs);
+`--record-traffic` turns two rocprofv3 counter runs into profiles/traffic.json.
 """
 
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -35,21 +42,22 @@ if ROOT not in sys.path:
 
 METRIC = "Sparse-BitLinear GEMV weight GB/s + prefill int8 TOPS, as % of MI355X peak"
 HBM_PEAK_GBPS = 8000.0
-INT8_PEAK_TOPS = 5000.0
+INT8_PEAK_TOPS = 5000.0           # dense int8 matrix cores
+INT8_SPARSE_PEAK_TOPS = 10000.0   # 2:4 structured-sparse int8 matrix cores (dense-equivalent ops)
+BF16_PEAK_TFLOPS = 2500.0
 
 FORMATS = {"dense2": (0, 6, 8), "nm68": (1, 6, 8), "nm24": (1, 2, 4)}
+GROUPS = [[0, 1, 2], [3], [4, 5], [6]]          # q/k/v, o, gate/up, down share an input
 
-WORKLOADS = {
-    # name: (synth workload, hidden, ffn, m_tok, description)
-    "decode_0p7b": ("b0p7", 1536, 4096, 1,
-                    "Decode GEMV, M=1 token, 0.7B-class block: hidden 1536, FFN 4096"),
-    "decode_3b": ("b3", 3200, 8640, 1, "Decode GEMV, 3B-class block: hidden 3200, FFN 8640"),
-    "prefill_3b": ("b3_prefill", 3200, 8640, 2048,
-                   "Prefill GEMM, M=2048 tokens, 3B-class block: hidden 3200, FFN 8640"),
-    "train_13b": ("b13", 5120, 13824, 4096,
-                  "Training-step path, 13B-class block: hidden 5120, FFN 13824, M=4096"),
-    "decode_70b": ("b70", 8192, 28672, 1, "Decode GEMV, M=1, 70B-class block: hidden 8192, FFN 28672"),
+BLOCKS = {
+    # name: (synth workload, hidden, ffn, description)
+    "0p7b": ("b0p7", 1536, 4096, "0.7B-class block (hidden 1536, FFN 4096)"),
+    "3b": ("b3", 3200, 8640, "3B-class block (hidden 3200, FFN 8640)"),
+    "13b": ("b13", 5120, 13824, "13B-class block (hidden 5120, FFN 13824)"),
+    "70b": ("b70", 8192, 28672, "70B-class block (hidden 8192, FFN 28672)"),
 }
+SECTIONS = ("headline", "gemv", "prefill", "train13b", "weight_prep", "step0p7b", "backward",
+            "group_scales", "references", "cpu")
 
 
 def parse():
@@ -57,54 +65,136 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="decode_0p7b", choices=sorted(WORKLOADS))
+    p.add_argument("--block", default="70b", choices=sorted(BLOCKS), help="headline decode block")
     p.add_argument("--fmt", default="nm68", choices=sorted(FORMATS))
-    p.add_argument("--m-tok", type=int, default=None)
-    p.add_argument("--pool-mb", type=float, default=560.0,
-                   help="minimum bytes of distinct BF16 master copies the steps rotate over")
-    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    p.add_argument("--no-group-scales", action="store_true", help="skip the group-scale timings")
-    p.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM measurement")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--no-qw-sweep", action="store_true", help="skip the weight-preparation sweep")
-    p.add_argument("--no-gemv-sweep", action="store_true",
-                   help="skip the GEMV weight-bandwidth table over the decode configurations")
+    p.add_argument("--m-tok", type=int, default=1)
+    p.add_argument("--sections", default=",".join(SECTIONS),
+                   help="comma list of parts to run (default: all): " + ",".join(SECTIONS))
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration-mb", type=float, default=0.0,
                    help="before the run, copy a buffer of this many MB 3 times (a known-size copy "
-                        "kernel for scaling hardware byte counters)")
+                        "for scaling hardware byte counters)")
+    p.add_argument("--record-traffic", metavar="KEY", default=None,
+                   help="do not run: read two rocprofv3 counter runs (--fetch-dir, --write-dir) and "
+                        "record KEY's bytes per launch in profiles/traffic.json")
+    p.add_argument("--fetch-dir")
+    p.add_argument("--write-dir")
+    p.add_argument("--kernel", help="kernel-name prefix of the launches to count (--record-traffic)")
+    p.add_argument("--launches", type=int, help="launches of that kernel per step (--record-traffic)")
+    p.add_argument("--count", type=int,
+                   help="count the last COUNT launches of that kernel (--record-traffic; default "
+                        "launches x steps: the timed steps, which end the profiled run)")
+    p.add_argument("--prefill-cases", default="3b:nm68,3b:dense2,3b:nm24,13b:nm68,13b:dense2",
+                   help="prefill cases block:format, in this order")
+    p.add_argument("--summary", help="text summary to write under profiles/ (--record-traffic)")
+    p.add_argument("--command", help="the profiled command, quoted in the summary (--record-traffic)")
     return p.parse_args()
 
 
-def recorded_traffic(call, workload, fmt):
-    """HBM bytes per call from the committed counter summary (profiles/traffic.json),
-    or None when there is none for this workload and format or when any kernel
-    source it was taken with has changed since (its SHA-256 differs)."""
-    import hashlib
+# --------------------------------------------------------------------------- traffic records
+
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = sorted(glob.glob(os.path.join("sparse_linear_layers_absmean_amd", "csrc", "*"), root_dir=ROOT))
+
+
+def _sources_sha():
+    out = {}
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            out[rel] = hashlib.sha256(fh.read()).hexdigest()
+    return out
+
+
+def recorded_traffic(key):
+    """HBM bytes per launch recorded for `key` in profiles/traffic.json, or None
+    when there is no record or any kernel source has changed since (SHA-256)."""
     try:
-        with open(os.path.join(ROOT, "profiles", "traffic.json")) as fh:
-            rec = json.load(fh)[call]
-        if rec.get("workload") != workload or rec.get("format") != fmt:
+        with open(TRAFFIC_JSON) as fh:
+            rec = json.load(fh)[key]
+        if rec["sources_sha256"] != _sources_sha():
             return None
-        for path, digest in rec["sources_sha256"].items():
-            with open(os.path.join(ROOT, path), "rb") as fh:
-                if hashlib.sha256(fh.read()).hexdigest() != digest:
-                    return None
-        return rec["bytes_per_call"]
+        return rec["bytes_per_launch"]
     except (OSError, KeyError, ValueError):
         return None
 
 
-def block(h, f):
-    import synth
-    return synth.block_shapes(h, f)
+def _counter_rows(d):
+    import csv
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    with open(files[0]) as fh:
+        return list(csv.DictReader(fh))
 
+
+def record_traffic(args):
+    """Bytes per launch of one kernel from a FETCH_SIZE run and a WRITE_SIZE run
+    of the same command, each scaled by what the counter reads for the known
+    copy of --copy-calibration-mb (the first dispatch of the blit kernel that
+    copies it).  The counted launches are the last --count dispatches of the
+    kernel (default launches x steps: the timed steps, which end the run)."""
+    res = {}
+    for name, d in (("FETCH_SIZE", args.fetch_dir), ("WRITE_SIZE", args.write_dir)):
+        rows = [r for r in _counter_rows(d) if r["Counter_Name"] == name]
+        cal_bytes = None
+        per_dispatch = {}
+        for r in rows:
+            per_dispatch.setdefault(r["Dispatch_Id"], [r, 0.0])[1] += float(r["Counter_Value"])
+        ordered = sorted(per_dispatch.values(), key=lambda rv: int(rv[0]["Dispatch_Id"]))
+        copies = [v for r, v in ordered if "copyBuffer" in r["Kernel_Name"]]
+        if not copies:
+            raise SystemExit("calibration copy not found (run with --copy-calibration-mb)")
+        cal_bytes = float(args.copy_calibration_mb) * 1e6 // 16 * 16
+        # a copy reads and writes its size once
+        factor = cal_bytes / (copies[0] * 1024.0)
+        mine = [(r, v) for r, v in ordered
+                if r["Kernel_Name"].split("(")[0].replace("void ", "").strip().startswith(args.kernel)]
+        count = args.count or args.launches * args.steps
+        if len(mine) < count:
+            raise SystemExit(f"only {len(mine)} launches of {args.kernel} in {d}")
+        use = mine[-count:]
+        kib = [v for _, v in use]
+        res[name] = dict(factor=factor, bytes_per_launch=sum(kib) * 1024.0 * factor / len(kib),
+                         copy_kib=copies[0], launches=len(kib),
+                         kernels=sorted({r["Kernel_Name"].split("(")[0] for r, _ in use}))
+    total = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            allrec = json.load(fh)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[args.record_traffic] = {
+        "kernel": args.kernel, "launches_per_step": args.launches,
+        "bytes_per_launch": round(total), "read_bytes_per_launch": round(res["FETCH_SIZE"]["bytes_per_launch"]),
+        "write_bytes_per_launch": round(res["WRITE_SIZE"]["bytes_per_launch"]),
+        "fetch_factor": round(res["FETCH_SIZE"]["factor"], 4), "write_factor": round(res["WRITE_SIZE"]["factor"], 4),
+        "summary": args.summary, "sources_sha256": _sources_sha()}
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(allrec, fh, indent=1, sort_keys=True)
+    if args.summary:
+        f, w = res["FETCH_SIZE"], res["WRITE_SIZE"]
+        with open(os.path.join(ROOT, args.summary), "w") as fh:
+            fh.write(f"# HBM traffic: {args.record_traffic}\n\n")
+            fh.write("Commands (two counter passes of the same run, MI355X):\n")
+            for c in ("FETCH_SIZE", "WRITE_SIZE"):
+                fh.write(f"    cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <out> -o run -- {args.command}\n")
+            fh.write(f"\nCalibration: the {args.copy_calibration_mb:g} MB device copy (copyBuffer blit kernel) reads "
+                     f"{f['copy_kib']:.1f} KiB\nby FETCH_SIZE and writes {w['copy_kib']:.1f} KiB by WRITE_SIZE, so "
+                     f"bytes = FETCH_SIZE*1024*{f['factor']:.4f} and WRITE_SIZE*1024*{w['factor']:.4f}.\n\n")
+            fh.write(f"Counted: the last {f['launches']} launches of {', '.join(f['kernels'])} "
+                     f"({args.launches} per step, the timed steps).\n")
+            fh.write(f"Per launch (average): read {f['bytes_per_launch'] / 1e6:.3f} MB, "
+                     f"written {w['bytes_per_launch'] / 1e6:.3f} MB, total {total / 1e6:.3f} MB.\n")
+    print(json.dumps(allrec[args.record_traffic]))
+
+
+# --------------------------------------------------------------------------- timing helpers
 
 class Timer:
-    """HIP events on torch's current stream (every libsbl launch goes there)."""
+    """HIP events on torch's current stream (every libsbl call here is issued there,
+    graph replays included)."""
 
-    def __init__(self):
-        import torch
-        self.torch = torch
+    def __init__(self, torch):
         self.a = torch.cuda.Event(enable_timing=True)
         self.b = torch.cuda.Event(enable_timing=True)
 
@@ -117,294 +207,326 @@ class Timer:
         return self.a.elapsed_time(self.b)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: the library runs and is measured on one GPU (asked for --gpus {args.gpus}); "
-              "sharding across GPUs is described, not implemented", file=sys.stderr)
-        sys.exit(2)
-    import numpy as np
-    import torch
+def capture(torch, fn):
+    """One eager run (every kernel loaded), then a HIP graph of fn."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def time_graphs(torch, tm, graphs, reps, warm=None):
+    for r in range(len(graphs) if warm is None else warm):
+        graphs[r % len(graphs)].replay()
+    torch.cuda.synchronize()
+    tm.start()
+    for r in range(reps):
+        graphs[r % len(graphs)].replay()
+    return tm.stop_ms() / reps
+
+
+def rot_copies(per_copy_bytes, floor=560e6, cap=64):
+    return int(min(cap, max(2, -(-floor // per_copy_bytes))))
+
+
+def mats_of(block):
+    import synth
+    _, h, f, _ = BLOCKS[block]
+    return synth.block_shapes(h, f)
+
+
+def synth_masters(block, mats):
+    """The block's BF16 masters from the seeded CPU generators, one thread per matrix."""
+    from concurrent.futures import ThreadPoolExecutor
 
     import synth
-    from sparse_linear_layers_absmean_amd import sbl
+    wname = BLOCKS[block][0] if block != "3b" else "b3_prefill"
+    with ThreadPoolExecutor(len(mats)) as ex:
+        return list(ex.map(lambda i: synth.workload_masters(wname, i, mats[i][1], mats[i][2]), range(len(mats))))
 
-    sbl.load()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.copy_calibration_mb > 0:
-        nb = int(args.copy_calibration_mb * 1e6) // 16 * 16
-        src = torch.ones(nb, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    wname, h, f, m_tok, desc = WORKLOADS[args.workload]
-    if args.m_tok:
-        m_tok = args.m_tok
+
+def device_masters(torch, dev, gen, no, k):
+    """N(0, 0.02) masters rounded to BF16, drawn on the device (same distribution as
+    the CPU generators; used where drawing ~1e9 values on the host would take minutes)."""
+    return (torch.randn((no, k), generator=gen, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16)
+
+
+def prepare_packed(torch, sbl, dev, masters, mats, n, m, fmt):
+    """sbl_quant_weights_batch over the block (7 matrices, one call); returns per-matrix
+    dicts with beta, packed and meta."""
+    outs, items = [], []
+    for (_, no, k), w in zip(mats, masters):
+        o = dict(beta=torch.empty(1, dtype=torch.float32, device=dev),
+                 packed=torch.empty(sbl.sbl_packed_bytes(no, k, n, m, fmt), dtype=torch.uint8, device=dev),
+                 meta=torch.empty((no, k // 8), dtype=torch.uint8, device=dev) if fmt == 1 else None, n_out=no)
+        outs.append(o)
+        items.append(dict(w=w, beta=o["beta"], packed=o["packed"], meta=o["meta"],
+                          workspace=sbl.new_workspace(no, k, dev)))
+    sbl.sbl_quant_weights_batch(items, n, m, fmt)
+    torch.cuda.synchronize()
+    return outs
+
+
+def packed_bytes(sbl, no, k, n, m, fmt):
+    return sbl.sbl_packed_bytes(no, k, n, m, fmt) + max(0, sbl.sbl_meta_bytes(no, k, fmt))
+
+
+def clone_packed(outs):
+    return [dict(o, packed=o["packed"].clone(), meta=o["meta"].clone() if o["meta"] is not None else None)
+            for o in outs]
+
+
+# --------------------------------------------------------------------------- headline: decode step
+
+def bench_decode_step(torch, np, sbl, dev, tm, args):
+    """The decode pass of one block (4 fused activation-quant + GEMV launches) over
+    packed weights prepared by sbl_quant_weights_batch; graph replays over rotating
+    copies of the packed weights."""
+    import synth
     fmt, n, m = FORMATS[args.fmt]
-    mats = block(h, f)
-    block_w = sum(no * k for _, no, k in mats)
-    copies = max(2, int(np.ceil(args.pool_mb * 1e6 / (2 * block_w))))
-    copies = min(copies, 64)
-
-    # ---------------- inputs: seeded synthetic, resident in HBM
-    t0 = time.time()
-    masters = [[torch.from_numpy(synth.workload_masters(wname, i, no, k, copy=c).view(np.int16)).to(dev)
-                for i, (_, no, k) in enumerate(mats)] for c in range(copies)]
-    # a block's matrices read 4 inputs: q/k/v share one, o one, gate/up one, down one
-    groups = [[0, 1, 2], [3], [4, 5], [6]]
-    xs = [[torch.from_numpy(synth.workload_acts(wname, grp[0], m_tok, mats[grp[0]][2], copy=c)).to(dev)
-           for grp in groups] for c in range(copies)]
-    gen_s = time.time() - t0
-
-    def alloc_out(no, k):
-        pb = sbl.sbl_packed_bytes(no, k, n, m, fmt)
-        return dict(beta=torch.empty(1, dtype=torch.float32, device=dev),
-                    packed=torch.empty(pb, dtype=torch.uint8, device=dev),
-                    meta=torch.empty((no, k // 8), dtype=torch.uint8, device=dev) if fmt == 1 else None,
-                    y=torch.empty((m_tok, no), dtype=torch.float32, device=dev), n_out=no)
-
-    outs = [[alloc_out(no, k) for (_, no, k) in mats] for _ in range(copies)]
-    acts = [[dict(xq=torch.empty((m_tok, mats[grp[0]][2]), dtype=torch.int8, device=dev),
-                  gamma=torch.empty(m_tok, dtype=torch.float32, device=dev)) for grp in groups]
-            for _ in range(copies)]
-    wss = [[sbl.new_workspace(no, k, dev) for (_, no, k) in mats] for _ in range(copies)]
-
-    def items_of(c, gi, pool=None):
-        src = outs[c] if pool is None else pool
-        return [dict(src[i], xq=acts[c][gi]["xq"], gamma=acts[c][gi]["gamma"]) for i in groups[gi]]
-
-    def qw_all(c, flags=0):
-        sbl.sbl_quant_weights_batch(
-            [dict(w=masters[c][i], beta=outs[c][i]["beta"], packed=outs[c][i]["packed"],
-                  meta=outs[c][i]["meta"], workspace=wss[c][i]) for i in range(len(mats))],
-            n, m, fmt, flags=flags)
-
-    def qa_all(c):
-        for gi in range(len(groups)):
-            sbl.sbl_quant_acts(xs[c][gi], acts[c][gi]["xq"], acts[c][gi]["gamma"])
-
-    def la_all(c, pool=None):
-        # per input: its quantization and the products that read it (one fused
-        # launch for decode-sized inputs, else sbl_quant_acts + sbl_linear_batch)
-        src = outs[c] if pool is None else pool
-        for gi in range(len(groups)):
-            sbl.sbl_linear_acts_batch(xs[c][gi], acts[c][gi]["xq"], acts[c][gi]["gamma"],
-                                      [src[i] for i in groups[gi]], fmt, n, m)
+    mats = mats_of(args.block)
+    m_tok = args.m_tok
+    gen = torch.Generator(device=dev).manual_seed(1)
+    if args.block == "70b":
+        masters = [device_masters(torch, dev, gen, no, k) for _, no, k in mats]
+        master_src = "N(0,0.02) BF16 masters drawn on the device (torch, seed 1)"
+    else:
+        masters = [torch.from_numpy(b.view(np.int16)).to(dev) for b in synth_masters(args.block, mats)]
+        master_src = f"seeded synthetic masters ({BLOCKS[args.block][0]} recipe)"
+    outs = prepare_packed(torch, sbl, dev, masters, mats, n, m, fmt)
+    del masters
+    torch.cuda.empty_cache()
+    wbytes = sum(packed_bytes(sbl, no, k, n, m, fmt) for _, no, k in mats)
+    copies = rot_copies(wbytes)
+    pool = [outs] + [clone_packed(outs) for _ in range(copies - 1)]
+    wname = BLOCKS[args.block][0]
+    xs = [torch.from_numpy(synth.workload_acts(wname, grp[0], m_tok, mats[grp[0]][2])).to(dev) for grp in GROUPS]
+    acts = [dict(xq=torch.empty((m_tok, x.shape[1]), dtype=torch.int8, device=dev),
+                 gamma=torch.empty(m_tok, dtype=torch.float32, device=dev)) for x in xs]
+    ys = [torch.empty((m_tok, no), dtype=torch.float32, device=dev) for _, no, _k in mats]
 
     def step(c):
-        qw_all(c)
-        la_all(c)
+        for gi, grp in enumerate(GROUPS):
+            sbl.sbl_linear_acts_batch(xs[gi], acts[gi]["xq"], acts[gi]["gamma"],
+                                      [dict(pool[c][i], y=ys[i]) for i in grp], fmt, n, m)
 
-    # ---------------- algorithmic bytes
-    def packed_b(no, k):
-        return sbl.sbl_packed_bytes(no, k, n, m, fmt) + max(0, sbl.sbl_meta_bytes(no, k, fmt))
-
-    qw_bytes = sum(2 * no * k + packed_b(no, k) for _, no, k in mats)
-    qa_bytes = sum(m_tok * mats[grp[0]][2] * 5 + 4 * m_tok for grp in groups)
-    lin_bytes = sum(packed_b(no, k) + m_tok * k + 4 * m_tok + 4 * m_tok * no + 4 for _, no, k in mats)
-    step_bytes = qw_bytes + qa_bytes + lin_bytes
-    weight_bytes = sum(packed_b(no, k) for _, no, k in mats)
-
-    # ---------------- HIP graphs: one per rotation copy, so that host launch
-    # overhead stays out of the timed region (the step has no memset nodes)
-    def capture(fn):
-        fn()                                  # eager run first: every kernel loaded
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn()
-        return g
-
-    step_graphs = [capture(lambda c=c: step(c)) for c in range(copies)]
-
-    # ---------------- whole-step timing
-    for s in range(args.warmup):
-        step_graphs[s % copies].replay()
-    torch.cuda.synchronize()
-    tm = Timer()
-    tm.start()
-    for s in range(args.steps):
-        step_graphs[s % copies].replay()
-    step_ms = tm.stop_ms() / args.steps
-    torch.cuda.synchronize()
-
-    # ---------------- per-call rates: graphs of one call kind, replayed back to back
-    def time_graphs(graphs, reps):
-        for r in range(min(reps, len(graphs))):
-            graphs[r % len(graphs)].replay()
-        torch.cuda.synchronize()
-        tm.start()
-        for r in range(reps):
-            graphs[r % len(graphs)].replay()
-        return tm.stop_ms() / reps
-
-    # GEMV pool: distinct packed buffers totalling >= 512 MB (cold Infinity Cache)
-    gemv_copies = max(copies, int(np.ceil(560e6 / weight_bytes)))
-    gemv_pool = []
-    for c in range(gemv_copies):
-        gemv_pool.append([dict(o, packed=o["packed"].clone(),
-                               meta=o["meta"].clone() if o["meta"] is not None else None)
-                          for o in outs[c % copies]])
-
-    def lin_all(c):
-        for gi in range(len(groups)):
-            sbl.sbl_linear_batch(items_of(c % copies, gi, gemv_pool[c % gemv_copies]), fmt, n, m)
-
-    qw_graphs = [capture(lambda c=c: qw_all(c)) for c in range(copies)]
-    qw2_graphs = [capture(lambda c=c: qw_all(c, sbl.SBL_QW_TWO_PASS)) for c in range(copies)]
-    qa_graphs = [capture(lambda c=c: qa_all(c)) for c in range(copies)]
-    lin_graphs = [capture(lambda c=c: lin_all(c)) for c in range(gemv_copies)]
-    la_graphs = [capture(lambda c=c: la_all(c % copies, gemv_pool[c % gemv_copies])) for c in range(gemv_copies)]
-
-    reps = max(20, args.steps)
-    qw_ms = time_graphs(qw_graphs, reps)
-    qw2_ms = time_graphs(qw2_graphs, reps)
-    qa_ms = time_graphs(qa_graphs, reps)
-    lin_ms = time_graphs(lin_graphs, max(reps, 2 * gemv_copies))
-    la_ms = time_graphs(la_graphs, max(reps, 2 * gemv_copies))
-
-    def roof(bytes_per, ms, kernel, launches, traffic=None):
-        gbps = bytes_per / (ms * 1e-3) / 1e9
-        return {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernel,
-                "launches_per_step": launches, "avg_launch_us": round(ms * 1e3 / launches, 3)}
-
-    # the step's two calls, then (for reference) the same work as separate calls
-    per_call = {
-        "sbl_quant_weights": roof(qw_bytes, qw_ms, "sbl_quant_weights_batch over the 7 matrices in one launch: "
-                                  "resident_kernel (masters held in registers while the exact beta completes)",
-                                  1, recorded_traffic("sbl_quant_weights", args.workload, args.fmt)),
-        "sbl_quant_weights_two_pass": roof(qw_bytes, qw2_ms, "the same call with SBL_QW_TWO_PASS: "
-                                           "absmean_partial + mask_pack kernels (masters read twice)", 1),
-        "sbl_linear_acts_batch": roof(qa_bytes + lin_bytes, la_ms,
-                                      "gemv_kernel with the activation quantization fused in "
-                                      "(grouped: qkv, o, gate+up, down)", len(groups)),
-        "sbl_quant_acts": roof(qa_bytes, qa_ms, "quant_acts_kernel (separate call)", len(groups)),
-        "sbl_linear": roof(lin_bytes, lin_ms, "gemv_kernel (separate call; grouped: qkv, o, gate+up, down)",
-                           len(groups)),
-    }
-    dominant = max(["sbl_quant_weights", "sbl_linear_acts_batch"],
-                   key=lambda kk: {"sbl_quant_weights": qw_ms, "sbl_linear_acts_batch": la_ms}[kk])
-    gemv_gbps = weight_bytes / (lin_ms * 1e-3) / 1e9
-
-    # ---------------- GEMV weight bandwidth over the decode configurations
-    gemv = None
-    read_peak = None
-    if not args.no_gemv_sweep:
-        gemv = gemv_sweep(torch, np, sbl, dev, synth)
-        read_peak = stream_read_peak(torch, dev, tm)
-        for row in gemv:
-            row["frac_of_measured_stream"] = round(row["weight_GBps"] / read_peak["reference_GBps"], 4)
-    qw_sweep = None if args.no_qw_sweep else weight_prep_sweep(torch, np, sbl, dev, synth, tm)
-
-    # ---------------- prefill GEMM (3B block, M = 2048 tokens), int8 ops
-    prefill = prefill_24 = backward = None
-    if not args.no_prefill:
-        prefill = bench_prefill(torch, np, synth, sbl, dev, tm)
-        prefill_24 = bench_prefill(torch, np, synth, sbl, dev, tm, n=2, m=4)
-        backward = bench_backward(torch, np, synth, sbl, dev, tm)
-    group_scales = None if args.no_group_scales else bench_group_scales(torch, np, sbl, dev, synth, tm)
-    library_gemm = None if args.no_prefill else library_gemm_reference(torch, dev, tm)
-
-    # ---------------- CPU oracle baseline
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(np, synth, wname, mats, m_tok, n, m, fmt, args.cpu_seconds, step_bytes)
-
-    value = step_bytes / (step_ms * 1e-3) / 1e9
-    # the GEMV's roofline at the largest decode configuration (70B block, M = 1,
-    # this run's format) when the sweep ran; else the step's own GEMV launches
-    roofline_gemv = {"bound": "hbm", "achieved": round(gemv_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "workload": desc, "note": "packed weight bytes / sbl_linear_batch time"}
-    if gemv:
-        big = [g for g in gemv if g["block"] == "70b" and g["format"] == args.fmt and g["m_tok"] == 1]
-        if big:
-            roofline_gemv = {"bound": "hbm", "achieved": big[0]["weight_GBps"], "peak": HBM_PEAK_GBPS,
-                             "unit": "GB/s", "frac": big[0]["frac"], "traffic": None,
-                             "workload": "Decode GEMV, M=1, 70B-class block (hidden 8192, FFN 28672), "
-                                         f"{args.fmt}, 4 grouped launches",
-                             "note": "packed weight bytes (codes + metadata) / time of the block's launches"}
-    line = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "int8",
-        "data": "synthetic (seeded N(0,0.02) BF16 masters, N(0,1) fp32 activations)",
-        "config": {"workload": desc, "format": args.fmt, "m_tok": m_tok, "matrices": len(mats),
-                   "block_weights": block_w, "rotation_copies": copies,
-                   "step_algorithmic_bytes": step_bytes},
-        "roofline": dict(per_call[dominant], call=dominant),
-        "roofline_gemv": roofline_gemv,
-        "per_call": per_call,
-        "gemv": gemv,
-        "measured_stream": read_peak,
-        "measured_library_gemm": library_gemm,
-        "weight_prep": qw_sweep,
-        "prefill": prefill,
-        "prefill_2of4_sparse_mfma": prefill_24,
-        "backward": backward,
-        "group_scales": group_scales,
-        "cpu_baseline": cpu,
-        "input_gen_s": round(gen_s, 1),
-        "device": torch.cuda.get_device_name(0),
-    }
-    print(json.dumps(line), flush=True)
+    graphs = [capture(torch, lambda c=c: step(c)) for c in range(copies)]
+    step_ms = time_graphs(torch, tm, graphs, args.steps, warm=args.warmup)
+    launches = len(GROUPS)
+    alg = wbytes + sum(m_tok * mats[g[0]][2] * 5 + 4 * m_tok for g in GROUPS) + \
+        sum(4 * m_tok * no for _, no, _k in mats)
+    gbps = wbytes / (step_ms * 1e-3) / 1e9
+    achieved = alg / (step_ms * 1e-3) / 1e9
+    key = f"gemv_decode_{args.block}_{args.fmt}_m{m_tok}"
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": recorded_traffic(key),
+            "kernel": "gemv_kernel with the activation quantization fused in (sbl_linear_acts_batch)",
+            "call": "sbl_linear_acts_batch", "launches_per_step": launches,
+            "alg_bytes_per_launch": round(alg / launches), "avg_launch_us": round(step_ms * 1e3 / launches, 3),
+            "note": "algorithmic bytes (packed weights + metadata, fp32 input read, int8 input and gamma "
+                    "written, fp32 outputs) per launch / average launch time (HIP events around the timed "
+                    "graph replays, gaps included); traffic: counter bytes per launch (profiles/traffic.json)"}
+    del graphs, pool
+    torch.cuda.empty_cache()
+    return dict(step_ms=step_ms, gbps=gbps, wbytes=wbytes, copies=copies, roofline=roof,
+                master_src=master_src, weights=sum(no * k for _, no, k in mats))
 
 
-def weight_prep_sweep(torch, np, sbl, dev, synth, tm):
-    """sbl_quant_weights_batch over whole blocks (7 matrices, 6:8 N:M output), the per-step
-    weight preparation: algorithmic bytes (masters read once + packed codes and metadata
-    written) per second.  Masters are N(0, 0.02) BF16 drawn on the device; each block
-    rotates over >= 2 distinct copies totalling >= 600 MB; HIP graphs, HIP events."""
-    n, m, fmt = 6, 8, 1
-    cases = [("0p7b", 1536, 4096), ("3b", 3200, 8640), ("13b", 5120, 13824)]
+# --------------------------------------------------------------------------- GEMV table
+
+def gemv_sweep(torch, np, sbl, dev, tm):
+    """Packed-weight GB/s of the grouped GEMV (sbl_linear_batch: 4 launches per block) for
+    the decode configurations.  The packed bytes are seeded random valid codes (the GEMV's
+    time does not depend on their values); blocks rotate over >= 600 MB of distinct
+    buffers; each block's 4 launches are one HIP graph."""
+    cases = [("0p7b", 1), ("3b", 1), ("3b", 4), ("3b", 8), ("70b", 1), ("70b", 8)]
     out = []
-    for wl, h, f in cases:
-        mats = synth.block_shapes(h, f)
+    for blk, m_tok in cases:
+        mats = mats_of(blk)
+        for fname, (fmt, n, m) in FORMATS.items():
+            nbytes = [sbl.sbl_packed_bytes(no, k, n, m, fmt) for _, no, k in mats]
+            mbytes = [no * k // 8 if fmt == 1 else 0 for _, no, k in mats]
+            bb = sum(nbytes) + sum(mbytes)
+            copies = rot_copies(bb, 600e6)
+            gen = torch.Generator(device=dev).manual_seed(7)
+            pool = []
+            for _ in range(copies):
+                items = []
+                for i, (_, no, k) in enumerate(mats):
+                    packed = torch.randint(0, 256, (nbytes[i],), dtype=torch.uint8, device=dev, generator=gen)
+                    if fmt == 0:
+                        packed &= 0x55                            # 2-bit fields u in {0, 1}
+                    meta = (torch.randint(0, 256, (no, k // 8), dtype=torch.uint8, device=dev, generator=gen)
+                            if fmt == 1 else None)
+                    items.append(dict(packed=packed, meta=meta, beta=torch.full((1,), 0.02, device=dev),
+                                      n_out=no, y=torch.empty((m_tok, no), device=dev)))
+                pool.append(items)
+            xs = [torch.randint(-127, 128, (m_tok, mats[grp[0]][2]), dtype=torch.int8, device=dev,
+                                generator=gen) for grp in GROUPS]
+            gam = torch.ones(m_tok, device=dev)
+
+            def run(c):
+                for gi, grp in enumerate(GROUPS):
+                    sbl.sbl_linear_batch([dict(pool[c][i], xq=xs[gi], gamma=gam) for i in grp], fmt, n, m)
+
+            graphs = [capture(torch, lambda c=c: run(c)) for c in range(copies)]
+            us = time_graphs(torch, tm, graphs, max(40, 2 * copies)) * 1e3
+            gbps = bb / (us * 1e-6) / 1e9
+            hbm = bb + sum(m_tok * mats[g_[0]][2] + 4 * m_tok for g_ in GROUPS) + \
+                sum(4 * m_tok * no for _, no, _k in mats)
+            out.append({"block": blk, "format": fname, "m_tok": m_tok, "weight_bytes": bb,
+                        "us_per_block": round(us, 2), "weight_GBps": round(gbps, 1),
+                        "hbm_GBps": round(hbm / (us * 1e-6) / 1e9, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+            del pool, graphs, xs
+            torch.cuda.empty_cache()
+    return out
+
+
+# --------------------------------------------------------------------------- prefill GEMMs
+
+def bench_prefill(torch, np, sbl, dev, tm, masters_by_block, cases):
+    """Prefill products of whole blocks (4 grouped launches of sbl_linear_batch on
+    int8 activations from sbl_quant_acts), graph replays rotating over 2 copies of the
+    packed weights: 3B-class block at 2048 tokens (6:8 N:M and 6:8-masked DENSE2 on the
+    dense int8 MFMA, 2:4 N:M on the 2:4 sparse MFMA) and 13B-class block at 4096 tokens
+    (6:8 N:M, DENSE2).  TOPS count the dense-equivalent 2*M*N*K int8 operations; the
+    sparse-MFMA path is priced against the sparse peak."""
+    import synth
+    tokens = {"3b": 2048, "13b": 4096}
+    cases = [(c.split(":")[0], tokens[c.split(":")[0]], c.split(":")[1]) for c in cases.split(",")]
+    out = []
+    for blk, m_tok, fname in cases:
+        fmt, n, m = FORMATS[fname]
+        mats = mats_of(blk)
+        masters = [torch.from_numpy(b.view(np.int16)).to(dev) for b in masters_by_block[blk]]
+        outs = prepare_packed(torch, sbl, dev, masters, mats, n, m, fmt)
+        del masters
+        pool = [outs, clone_packed(outs)]
+        wname = "b3_prefill" if blk == "3b" else BLOCKS[blk][0]
+        acts = []
+        for grp in GROUPS:
+            x = torch.from_numpy(synth.workload_acts(wname, grp[0], m_tok, mats[grp[0]][2])).to(dev)
+            acts.append(sbl.quant_acts(x))
+            del x
+        ys = [torch.empty((m_tok, no), dtype=torch.float32, device=dev) for _, no, _k in mats]
+
+        def run(c):
+            for gi, grp in enumerate(GROUPS):
+                sbl.sbl_linear_batch([dict(pool[c][i], xq=acts[gi][0], gamma=acts[gi][1], y=ys[i]) for i in grp],
+                                     fmt, n, m)
+
+        graphs = [capture(torch, lambda c=c: run(c)) for c in range(2)]
+        ms = time_graphs(torch, tm, graphs, 10)
+        ops = sum(2 * m_tok * no * k for _, no, k in mats)
+        tops = ops / (ms * 1e-3) / 1e12
+        sparse = fname == "nm24"
+        peak = INT8_SPARSE_PEAK_TOPS if sparse else INT8_PEAK_TOPS
+        key = f"gemm_prefill_{blk}_{fname}_m{m_tok}"
+        kernel = ("gemm24_kernel (v_smfmac_i32_16x16x128_i8, 2:4 sparse)" if sparse
+                  else "gemm_kernel (v_mfma_i32_32x32x32_i8)")
+        out.append({"block": blk, "format": fname, "m_tok": m_tok, "kernel": kernel,
+                    "workload": f"Prefill GEMM, M={m_tok} tokens, {BLOCKS[blk][3]}, {fname}",
+                    "ms_per_block": round(ms, 4), "int8_TOPS": round(tops, 1),
+                    "useful_TOPS": round(tops * n / m, 1),
+                    "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": peak, "unit": "TOP/s",
+                                 "frac": round(tops / peak, 4), "traffic": recorded_traffic(key),
+                                 "peak_kind": "int8 2:4 sparse MFMA (dense-equivalent ops)" if sparse
+                                 else "int8 dense MFMA",
+                                 "avg_launch_us": round(ms * 1e3 / len(GROUPS), 2)}})
+        del graphs, pool, outs, acts, ys
+        torch.cuda.empty_cache()
+    return out
+
+
+# --------------------------------------------------------------------------- 13B training-step path
+
+def bench_train13b(torch, np, sbl, dev, tm, masters13):
+    """The training-step path of a 13B-class block: per-step weight preparation from the
+    BF16 masters (exact beta, 6:8 mask with planted near-ties, codes, N:M packing) and
+    the forward products at 4096 tokens (activation quantization + GEMM per input).
+    Graph replays over 2 copies of masters and activations."""
+    import synth
+    fmt, n, m = FORMATS["nm68"]
+    mats = mats_of("13b")
+    m_tok = 4096
+    copies = 2
+    m0 = [torch.from_numpy(b.view(np.int16)).to(dev) for b in masters13]
+    x0 = [torch.from_numpy(synth.workload_acts("b13", grp[0], m_tok, mats[grp[0]][2])).to(dev) for grp in GROUPS]
+    state = []
+    for c in range(copies):
+        ms_ = m0 if c == 0 else [t.clone() for t in m0]
+        xs = x0 if c == 0 else [t.clone() for t in x0]
+        outs = [dict(beta=torch.empty(1, device=dev),
+                     packed=torch.empty(sbl.sbl_packed_bytes(no, k, n, m, fmt), dtype=torch.uint8, device=dev),
+                     meta=torch.empty((no, k // 8), dtype=torch.uint8, device=dev), n_out=no,
+                     y=torch.empty((m_tok, no), device=dev)) for _, no, k in mats]
+        wss = [sbl.new_workspace(no, k, dev) for _, no, k in mats]
+        acts = [dict(xq=torch.empty((m_tok, x.shape[1]), dtype=torch.int8, device=dev),
+                     gamma=torch.empty(m_tok, device=dev)) for x in xs]
+        state.append((ms_, xs, outs, wss, acts))
+
+    def prep(c):
+        ms_, xs, outs, wss, acts = state[c]
+        sbl.sbl_quant_weights_batch([dict(w=ms_[i], beta=outs[i]["beta"], packed=outs[i]["packed"],
+                                          meta=outs[i]["meta"], workspace=wss[i]) for i in range(len(mats))],
+                                    n, m, fmt)
+
+    def fwd(c):
+        ms_, xs, outs, wss, acts = state[c]
+        for gi, grp in enumerate(GROUPS):
+            sbl.sbl_linear_acts_batch(xs[gi], acts[gi]["xq"], acts[gi]["gamma"], [outs[i] for i in grp],
+                                      fmt, n, m)
+
+    step_g = [capture(torch, lambda c=c: (prep(c), fwd(c))) for c in range(copies)]
+    prep_g = [capture(torch, lambda c=c: prep(c)) for c in range(copies)]
+    fwd_g = [capture(torch, lambda c=c: fwd(c)) for c in range(copies)]
+    step_ms = time_graphs(torch, tm, step_g, 10)
+    prep_us = time_graphs(torch, tm, prep_g, 20) * 1e3
+    fwd_ms = time_graphs(torch, tm, fwd_g, 10)
+    weights = sum(no * k for _, no, k in mats)
+    prep_alg = sum(2 * no * k + packed_bytes(sbl, no, k, n, m, fmt) for _, no, k in mats)
+    ops = 2 * m_tok * weights
+    del step_g, prep_g, fwd_g, state
+    torch.cuda.empty_cache()
+    return {"workload": f"Training-step path, {BLOCKS['13b'][3]}, 6:8 N:M, M=4096 tokens, "
+                        "masters with near-ties planted on the keep boundary",
+            "ms_per_step": round(step_ms, 4), "weight_prep_us": round(prep_us, 1),
+            "weight_prep_GBps": round(prep_alg / (prep_us * 1e-6) / 1e9, 1),
+            "weight_prep_frac": round(prep_alg / (prep_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "forward_ms": round(fwd_ms, 4), "forward_int8_TOPS": round(ops / (fwd_ms * 1e-3) / 1e12, 1),
+            "forward_frac": round(ops / (fwd_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+            "calls": "sbl_quant_weights_batch (7 matrices), then per input sbl_linear_acts_batch "
+                     "(quant_acts_kernel + gemm_kernel)"}
+
+
+# --------------------------------------------------------------------------- weight preparation sweep
+
+def weight_prep_sweep(torch, np, sbl, dev, tm):
+    """sbl_quant_weights_batch over whole blocks (7 matrices, 6:8 N:M output), the
+    per-step weight preparation: algorithmic bytes (masters read once + packed codes and
+    metadata written) per second.  N(0, 0.02) BF16 masters drawn on the device; each
+    block rotates over >= 2 distinct copies totalling >= 600 MB; HIP graphs."""
+    n, m, fmt = 6, 8, 1
+    out = []
+    for blk in ("0p7b", "3b", "13b"):
+        mats = mats_of(blk)
         bw = sum(no * k for _, no, k in mats)
-        copies = max(2, int(np.ceil(600e6 / (2 * bw))))
+        copies = rot_copies(2 * bw, 600e6)
         g = torch.Generator(device=dev).manual_seed(5)
         pool = []
         for c in range(copies):
-            its = []
-            for _, no, k in mats:
-                w = (torch.randn((no, k), generator=g, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16)
-                its.append(dict(w=w, beta=torch.empty(1, device=dev),
-                                packed=torch.empty(sbl.sbl_packed_bytes(no, k, n, m, fmt), dtype=torch.uint8,
-                                                   device=dev),
-                                meta=torch.empty((no, k // 8), dtype=torch.uint8, device=dev),
-                                workspace=sbl.new_workspace(no, k, dev)))
-            pool.append(its)
-        graphs = []
-        for c in range(copies):
-            sbl.sbl_quant_weights_batch(pool[c], n, m, fmt)
-            torch.cuda.synchronize()
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr):
-                sbl.sbl_quant_weights_batch(pool[c], n, m, fmt)
-            graphs.append(gr)
-        reps = max(20, 2 * copies)
-        for r in range(copies):
-            graphs[r].replay()
-        torch.cuda.synchronize()
-        tm.start()
-        for r in range(reps):
-            graphs[r % copies].replay()
-        us = tm.stop_ms() / reps * 1e3
-        alg = sum(2 * no * k + sbl.sbl_packed_bytes(no, k, n, m, fmt) + no * k // 8 for _, no, k in mats)
+            pool.append([dict(w=device_masters(torch, dev, g, no, k), beta=torch.empty(1, device=dev),
+                              packed=torch.empty(sbl.sbl_packed_bytes(no, k, n, m, fmt), dtype=torch.uint8,
+                                                 device=dev),
+                              meta=torch.empty((no, k // 8), dtype=torch.uint8, device=dev),
+                              workspace=sbl.new_workspace(no, k, dev)) for _, no, k in mats])
+        graphs = [capture(torch, lambda c=c: sbl.sbl_quant_weights_batch(pool[c], n, m, fmt)) for c in range(copies)]
+        us = time_graphs(torch, tm, graphs, max(20, 2 * copies)) * 1e3
+        alg = sum(2 * no * k + packed_bytes(sbl, no, k, n, m, fmt) for _, no, k in mats)
         gbps = alg / (us * 1e-6) / 1e9
-        out.append({"block": wl, "weights": bw, "us_per_call": round(us, 2), "alg_GBps": round(gbps, 1),
+        out.append({"block": blk, "weights": bw, "us_per_call": round(us, 2), "alg_GBps": round(gbps, 1),
                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
                     "path": "one launch (resident_kernel)" if bw * 2 <= 67e6 else "two launches (absmean + mask_pack)"})
         del pool, graphs
@@ -412,46 +534,123 @@ def weight_prep_sweep(torch, np, sbl, dev, synth, tm):
     return out
 
 
-def bench_group_scales(torch, np, sbl, dev, synth, tm, rpg=128, kg=320, n=6, m=8):
-    """Group scales on a 3B-class block (hidden 3200, FFN 8640), 6:8 N:M, M = 1: weight
-    preparation with beta per block of rows (rows_per_group 1 and rpg), and the decode
-    products with beta per row group (sbl_linear_grouped) and with gamma per block of kg
-    features as well (sbl_quant_acts_kgrouped + sbl_linear_kgrouped), beside the per-matrix
-    sbl_linear (kg = 320 = 5 x 64 divides both k = 3200 and k = 8640).  Each block's calls are
-    one HIP graph; every block uses distinct buffers from a pool of >= 600 MB.
-    Rates are algorithmic bytes: masters read + packed codes and metadata written for the
-    weights, packed codes and metadata read for the products."""
+# --------------------------------------------------------------------------- whole path, 0.7B block
+
+def bench_step0p7b(torch, np, sbl, dev, tm):
+    """The whole path on a 0.7B-class block, one token, 6:8 N:M: per step the weight
+    preparation of the 7 matrices (one launch) and the 4 fused activation-quant + GEMV
+    launches; graph replays rotating over >= 560 MB of master copies.  Rate: all of the
+    step's algorithmic bytes (masters read, packed written and read, activations,
+    outputs) per second."""
+    import synth
+    fmt, n, m = FORMATS["nm68"]
+    mats = mats_of("0p7b")
+    m_tok = 1
+    bw = sum(no * k for _, no, k in mats)
+    copies = rot_copies(2 * bw)
+    base = synth_masters("0p7b", mats)
+    st = []
+    for c in range(copies):
+        masters = [torch.from_numpy(b.view(np.int16)).to(dev) for b in base]
+        xs = [torch.from_numpy(synth.workload_acts("b0p7", grp[0], m_tok, mats[grp[0]][2], copy=c)).to(dev)
+              for grp in GROUPS]
+        outs = [dict(beta=torch.empty(1, device=dev),
+                     packed=torch.empty(sbl.sbl_packed_bytes(no, k, n, m, fmt), dtype=torch.uint8, device=dev),
+                     meta=torch.empty((no, k // 8), dtype=torch.uint8, device=dev), n_out=no,
+                     y=torch.empty((m_tok, no), device=dev)) for _, no, k in mats]
+        wss = [sbl.new_workspace(no, k, dev) for _, no, k in mats]
+        acts = [dict(xq=torch.empty((m_tok, x.shape[1]), dtype=torch.int8, device=dev),
+                     gamma=torch.empty(m_tok, device=dev)) for x in xs]
+        st.append((masters, xs, outs, wss, acts))
+
+    def step(c):
+        masters, xs, outs, wss, acts = st[c]
+        sbl.sbl_quant_weights_batch([dict(w=masters[i], beta=outs[i]["beta"], packed=outs[i]["packed"],
+                                          meta=outs[i]["meta"], workspace=wss[i]) for i in range(len(mats))],
+                                    n, m, fmt)
+        for gi, grp in enumerate(GROUPS):
+            sbl.sbl_linear_acts_batch(xs[gi], acts[gi]["xq"], acts[gi]["gamma"], [outs[i] for i in grp], fmt, n, m)
+
+    graphs = [capture(torch, lambda c=c: step(c)) for c in range(copies)]
+    ms = time_graphs(torch, tm, graphs, 50)
+    pb = sum(packed_bytes(sbl, no, k, n, m, fmt) for _, no, k in mats)
+    alg = 2 * bw + 2 * pb + sum(m_tok * mats[g[0]][2] * 5 + 4 * m_tok for g in GROUPS) + \
+        sum(4 * m_tok * no for _, no, _k in mats)
+    del graphs, st
+    torch.cuda.empty_cache()
+    return {"workload": "Whole path, M=1 token, 0.7B-class block (hidden 1536, FFN 4096), 6:8 N:M: "
+                        "weight preparation + fused activation quantization and GEMV",
+            "us_per_step": round(ms * 1e3, 2), "alg_bytes": alg,
+            "alg_GBps": round(alg / (ms * 1e-3) / 1e9, 1),
+            "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+# --------------------------------------------------------------------------- backward
+
+def bench_backward(torch, np, sbl, dev, tm, masters3b):
+    """Backward of a 3B-class block at 2048 tokens, 6:8 weights: sbl_linear_backward (dX
+    and dW of the 7 matrices) on the BF16 matrix cores.  Algorithmic flops 2*M*N*K per
+    gradient; dW runs three BF16 products per step (x_hat split exactly into three parts)."""
+    import synth
+    fmt, n, m = FORMATS["nm68"]
+    m_tok = 2048
+    mats = mats_of("3b")
+    g = torch.Generator(device=dev).manual_seed(11)
+    items = []
+    for i, (_, no, k) in enumerate(mats):
+        w = torch.from_numpy(masters3b[i].view(np.int16)).to(dev)
+        o = sbl.quant_weights(w, n, m, fmt=fmt)
+        x = torch.from_numpy(synth.workload_acts("b3_prefill", i, m_tok, k)).to(dev)
+        xq, gamma = sbl.quant_acts(x)
+        dy = (torch.randn((m_tok, no), generator=g, device=dev) * 0.05).to(torch.bfloat16)
+        items.append((o, x, xq, gamma, dy, torch.empty((m_tok, k), device=dev), torch.empty((no, k), device=dev)))
+        del w
+
+    def run(which):
+        for o, x, xq, gamma, dy, dx, dw in items:
+            sbl.sbl_linear_backward(dy, o["packed"], o["meta"], fmt, n, m, o["beta"], x, xq, gamma,
+                                    dx=dx if which in ("dx", "both") else None,
+                                    dw=dw if which in ("dw", "both") else None)
+
+    res = {}
+    for which in ("dx", "dw", "both"):
+        for _ in range(2):
+            run(which)
+        torch.cuda.synchronize()
+        tm.start()
+        for _ in range(5):
+            run(which)
+        res[which] = tm.stop_ms() / 5
+    flops = sum(2 * m_tok * no * k for _, no, k in mats)
+    tf = {w: (flops * (2 if w == "both" else 1)) / (res[w] * 1e-3) / 1e12 for w in res}
+    del items
+    torch.cuda.empty_cache()
+    return {"workload": "Backward (dX and dW), M=2048 tokens, 3B-class block (hidden 3200, FFN 8640), 6:8 N:M",
+            "kernel": "backward_dx_kernel, backward_dw_kernel (v_mfma_f32_32x32x16_bf16)",
+            "ms_per_block": {w: round(v, 3) for w, v in res.items()},
+            "algorithmic_TFLOPS": {w: round(v, 1) for w, v in tf.items()},
+            "dw_mfma_TFLOPS": round(3 * flops / (res["dw"] * 1e-3) / 1e12, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf["both"], 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf["both"] / BF16_PEAK_TFLOPS, 4), "traffic": None}}
+
+
+# --------------------------------------------------------------------------- group scales
+
+def bench_group_scales(torch, np, sbl, dev, tm, rpg=128, kg=320, n=6, m=8):
+    """Group scales on a 3B-class block, 6:8 N:M, M = 1: weight preparation with beta per
+    block of rows (rows_per_group 1 and rpg), and the decode products with beta per row
+    group and with gamma per block of kg features, beside the per-matrix sbl_linear.  Each
+    block's calls are one HIP graph; every block uses distinct buffers (>= 600 MB)."""
     fmt = 1
-    mats = synth.block_shapes(3200, 8640)
+    mats = mats_of("3b")
     bw = sum(no * k for _, no, k in mats)
     g = torch.Generator(device=dev).manual_seed(7)
     pb = [sbl.sbl_packed_bytes(no, k, n, m, fmt) for _, no, k in mats]
     wbytes = sum(pb) + sum(no * k // 8 for _, no, k in mats)
-
-    def timed(fn, copies, reps):
-        graphs = []
-        for c in range(copies):
-            fn(c)
-            torch.cuda.synchronize()
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr):
-                fn(c)
-            graphs.append(gr)
-        for gr in graphs:
-            gr.replay()
-        torch.cuda.synchronize()
-        tm.start()
-        for r in range(reps):
-            graphs[r % copies].replay()
-        us = tm.stop_ms() / reps * 1e3
-        del graphs
-        return us
-
     out = {"workload": f"3B-class block (hidden 3200, FFN 8640), {n}:{m} N:M, M=1", "weight_prep": [],
            "products": []}
-    copies = max(2, int(np.ceil(600e6 / (2 * bw))))
-    masters = [[(torch.randn((no, k), generator=g, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16)
-                for _, no, k in mats] for _ in range(copies)]
+    copies = rot_copies(2 * bw, 600e6)
+    masters = [[device_masters(torch, dev, g, no, k) for _, no, k in mats] for _ in range(copies)]
     outs = [[dict(packed=torch.empty(pb[i], dtype=torch.uint8, device=dev),
                   meta=torch.empty((no, k // 8), dtype=torch.uint8, device=dev)) for i, (_, no, k) in enumerate(mats)]
             for _ in range(copies)]
@@ -464,15 +663,16 @@ def bench_group_scales(torch, np, sbl, dev, synth, tm, rpg=128, kg=320, n=6, m=8
             for i, (_, no, k) in enumerate(mats):
                 sbl.sbl_quant_weights_grouped(masters[c][i], n, m, r, betas[i], wss[i], fmt=fmt,
                                               packed=outs[c][i]["packed"], meta=outs[c][i]["meta"])
-        us = timed(prep, copies, max(10, 2 * copies))
+        graphs = [capture(torch, lambda c=c: prep(c)) for c in range(copies)]
+        us = time_graphs(torch, tm, graphs, max(10, 2 * copies)) * 1e3
         gbps = (2 * bw + wbytes) / (us * 1e-6) / 1e9
         out["weight_prep"].append({"rows_per_group": r, "groups": sum(-(-no // r) for _, no, k in mats),
                                    "us_per_block": round(us, 1), "alg_GBps": round(gbps, 1),
                                    "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+        del graphs
     del masters
     torch.cuda.empty_cache()
-    # products: the rpg-grouped betas of the last preparation; a pool of packed copies
-    pcopies = max(2, int(np.ceil(600e6 / wbytes)))
+    pcopies = rot_copies(wbytes, 600e6)
     pool = [[{k2: v.clone() for k2, v in o.items()} for o in outs[0]] for _ in range(pcopies)]
     beta1 = [b[:1].contiguous() for b in betas]
     xs = [torch.randn((1, k), generator=g, device=dev) for _, no, k in mats]
@@ -502,49 +702,24 @@ def bench_group_scales(torch, np, sbl, dev, synth, tm, rpg=128, kg=320, n=6, m=8
                            ("sbl_linear_grouped", grouped, f"beta per {rpg} rows: GEMV + grouped rescale"),
                            ("sbl_linear_kgrouped", kgrouped,
                             f"beta per {rpg} rows, gamma per {kg} features: activation quant + product")):
-        us = timed(fn, pcopies, max(20, 2 * pcopies))
+        graphs = [capture(torch, lambda c=c: fn(c)) for c in range(pcopies)]
+        us = time_graphs(torch, tm, graphs, max(20, 2 * pcopies)) * 1e3
         gbps = wbytes / (us * 1e-6) / 1e9
         out["products"].append({"call": name, "scales": what, "us_per_block": round(us, 1),
                                 "weight_GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+        del graphs
     del pool, outs
     torch.cuda.empty_cache()
     return out
 
 
-def stream_read_peak(torch, dev, tm):
-    """Measured streaming rates for reference (library kernels, not part of the path),
-    HIP events around 10 runs each: torch's fp32 sum over 2 GB (bytes read), and a
-    1 GB device-to-device copy (bytes read + written)."""
-    def timed(fn):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        tm.start()
-        for _ in range(10):
-            fn()
-        return tm.stop_ms() / 10
+# --------------------------------------------------------------------------- library references
 
-    a = torch.ones(512 << 20, dtype=torch.float32, device=dev)
-    sum_gbps = (2 << 30) / (timed(lambda: a.sum()) * 1e-3) / 1e9
-    del a
-    src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    copy_gbps = (2 << 30) / (timed(lambda: dst.copy_(src)) * 1e-3) / 1e9
-    del src, dst
-    torch.cuda.empty_cache()
-    return {"sum_fp32_GBps": round(sum_gbps, 1), "copy_GBps": round(copy_gbps, 1),
-            "reference_GBps": round(max(sum_gbps, copy_gbps), 1)}
-
-
-def library_gemm_reference(torch, dev, tm):
-    """Measured matrix-core rates of library GEMMs (references, not part of the path), HIP events
-    around 10 runs each, at the 3B-class gate shape with 2048 tokens (2048 x 3200 by 3200 x 8640):
-    int8 x int8 -> int32 (torch._int_mm) for the prefill GEMM, and BF16 (torch.matmul, fp32
-    accumulation) for the backward's products."""
-    m_tok, k, n_out = 2048, 3200, 8640
-    flops = 2 * m_tok * k * n_out
-    out = {"shape": f"{m_tok} x {k} by {k} x {n_out}"}
-
+def references(torch, dev, tm):
+    """Measured library rates for reference (not part of the path), HIP events around 10
+    runs each: torch's fp32 sum over 2 GB (bytes read), a 1 GB device copy (read +
+    written), and two GEMMs at the 3B-class gate shape with 2048 tokens (2048 x 3200 by
+    3200 x 8640): int8 -> int32 (torch._int_mm) and BF16 (torch.matmul)."""
     def timed(fn):
         for _ in range(3):
             fn()
@@ -554,241 +729,187 @@ def library_gemm_reference(torch, dev, tm):
             fn()
         return tm.stop_ms() / 10
 
+    out = {}
+    a = torch.ones(512 << 20, dtype=torch.float32, device=dev)
+    out["sum_fp32_GBps"] = round((2 << 30) / (timed(lambda: a.sum()) * 1e-3) / 1e9, 1)
+    del a
+    src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    out["copy_GBps"] = round((2 << 30) / (timed(lambda: dst.copy_(src)) * 1e-3) / 1e9, 1)
+    del src, dst
+    m_tok, k, n_out = 2048, 3200, 8640
+    flops = 2 * m_tok * k * n_out
+    out["gemm_shape"] = f"{m_tok} x {k} by {k} x {n_out}"
     g = torch.Generator(device=dev).manual_seed(3)
     try:
         a = torch.randint(-127, 128, (m_tok, k), generator=g, device=dev, dtype=torch.int8)
         b = torch.randint(-1, 2, (n_out, k), generator=g, device=dev, dtype=torch.int8).t()
-        ms = timed(lambda: torch._int_mm(a, b))
-        out["int8_TOPS"] = round(flops / (ms * 1e-3) / 1e12, 1)
-        out["int8_frac"] = round(flops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
+        t = flops / (timed(lambda: torch._int_mm(a, b)) * 1e-3) / 1e12
+        out["int8_TOPS"], out["int8_frac"] = round(t, 1), round(t / INT8_PEAK_TOPS, 4)
     except (RuntimeError, AttributeError) as e:
         out["int8_error"] = str(e).splitlines()[0][:160]
     a = torch.randn((m_tok, k), generator=g, device=dev).to(torch.bfloat16)
     b = torch.randn((k, n_out), generator=g, device=dev).to(torch.bfloat16)
-    ms = timed(lambda: torch.matmul(a, b))
-    out["bf16_TFLOPS"] = round(flops / (ms * 1e-3) / 1e12, 1)
-    out["bf16_frac"] = round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    t = flops / (timed(lambda: torch.matmul(a, b)) * 1e-3) / 1e12
+    out["bf16_TFLOPS"], out["bf16_frac"] = round(t, 1), round(t / BF16_PEAK_TFLOPS, 4)
     del a, b
     torch.cuda.empty_cache()
     return out
 
 
-def gemv_sweep(torch, np, sbl, dev, synth):
-    """Packed-weight GB/s of the grouped GEMV (sbl_linear_batch, 4 launches per
-    block: q/k/v, o, gate/up, down) for the decode configurations.  The packed
-    bytes are seeded random (the GEMV's time does not depend on the code
-    values); every block uses distinct buffers from a pool of >= 600 MB, so the
-    256 MB Infinity Cache cannot serve one launch from the previous one.  Each
-    block's 4 launches are one HIP graph; HIP events bracket the replays."""
-    cases = [("0p7b", 1536, 4096, 1), ("3b", 3200, 8640, 1), ("3b", 3200, 8640, 4),
-             ("3b", 3200, 8640, 8), ("70b", 8192, 28672, 1)]
-    groups = [[0, 1, 2], [3], [4, 5], [6]]
-    out = []
-    for wl, h, f, m_tok in cases:
-        mats = synth.block_shapes(h, f)
-        for fname, (fmt, n, m) in FORMATS.items():
-            nbytes = [sbl.sbl_packed_bytes(no, k, n, m, fmt) for _, no, k in mats]
-            mbytes = [no * k // 8 if fmt == 1 else 0 for _, no, k in mats]
-            block_bytes = sum(nbytes) + sum(mbytes)
-            copies = max(2, int(np.ceil(600e6 / block_bytes)))
-            gen = torch.Generator(device=dev).manual_seed(7)
-            pool = []
-            for _ in range(copies):
-                items = []
-                for i, (_, no, k) in enumerate(mats):
-                    packed = torch.randint(0, 256, (nbytes[i],), dtype=torch.uint8, device=dev, generator=gen)
-                    if fmt == 0:
-                        packed &= 0x55                            # 2-bit fields u in {0, 1}
-                    meta = (torch.randint(0, 256, (no, k // 8), dtype=torch.uint8, device=dev, generator=gen)
-                            if fmt == 1 else None)
-                    items.append(dict(packed=packed, meta=meta, beta=torch.full((1,), 0.02, device=dev),
-                                      n_out=no, y=torch.empty((m_tok, no), device=dev)))
-                pool.append(items)
-            xs = [torch.randint(-127, 128, (m_tok, mats[grp[0]][2]), dtype=torch.int8, device=dev,
-                                generator=gen) for grp in groups]
-            gam = torch.ones(m_tok, device=dev)
+# --------------------------------------------------------------------------- CPU oracle baseline
 
-            def run(c):
-                for gi, grp in enumerate(groups):
-                    sbl.sbl_linear_batch([dict(pool[c][i], xq=xs[gi], gamma=gam) for i in grp], fmt, n, m)
+def cpu_baseline(np, args, budget_s):
+    """The CPU oracle, untuned, on a bounded sample of the headline workload: the decode
+    of 1024 rows of the block's first matrix shape (8192 wide at 70B), one token.
+    Untimed, once: the oracle's own weight preparation and packing of those rows (a
+    decoder's load time).  Timed, repeated until about budget_s seconds: reading the
+    packed format back (the oracle's panel-order and N:M unpacking), the activation
+    quantization, the contraction and the rescale."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
-            graphs = []
-            for c in range(copies):
-                run(c)
-                torch.cuda.synchronize()
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    run(c)
-                graphs.append(g)
-            reps = max(40, 2 * copies)
-            for r in range(copies):
-                graphs[r].replay()
-            torch.cuda.synchronize()
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            for r in range(reps):
-                graphs[r % copies].replay()
-            b.record()
-            b.synchronize()
-            us = a.elapsed_time(b) * 1e3 / reps
-            gbps = block_bytes / (us * 1e-6) / 1e9
-            # all HBM bytes of the block's products: weights, int8 activations, gamma, fp32 outputs
-            hbm = block_bytes + sum(m_tok * mats[g_[0]][2] + 4 * m_tok for g_ in groups) + \
-                sum(4 * m_tok * no for _, no, _k in mats)
-            out.append({"block": wl, "format": fname, "m_tok": m_tok, "weight_bytes": block_bytes,
-                        "us_per_block": round(us, 2), "weight_GBps": round(gbps, 1),
-                        "hbm_GBps": round(hbm / (us * 1e-6) / 1e9, 1),
-                        "frac": round(gbps / HBM_PEAK_GBPS, 4)})
-            del pool, graphs, xs
-            torch.cuda.empty_cache()
-    return out
-
-
-def bench_prefill(torch, np, synth, sbl, dev, tm, n=6, m=8):
-    """3B-class block at M = 2048 tokens, N:M n:m weights: sbl_linear (GEMM) TOPS.  2:4 runs on
-    the sparse MFMA; its TOPS count the dense-equivalent 2*M*N*K ops and are priced against the
-    dense int8 peak."""
-    wname, h, f, m_tok = "b3_prefill", 3200, 8640, 2048
-    fmt = 1
-    mats = synth.block_shapes(h, f)
-    items = []
-    for i, (_, no, k) in enumerate(mats):
-        w = torch.from_numpy(synth.workload_masters(wname, i, no, k).view(np.int16)).to(dev)
-        o = sbl.quant_weights(w, n, m, fmt=fmt)
-        x = torch.from_numpy(synth.workload_acts(wname, i, m_tok, k)).to(dev)
-        xq, gamma = sbl.quant_acts(x)
-        y = torch.empty((m_tok, no), dtype=torch.float32, device=dev)
-        items.append((o, xq, gamma, y, no, k))
-        del w, x
-
-    groups = [[0, 1, 2], [3], [4, 5], [6]]          # q/k/v, o, gate/up, down
-
-    def run():
-        for grp in groups:
-            sbl.sbl_linear_batch([dict(packed=items[i][0]["packed"], meta=items[i][0]["meta"],
-                                       beta=items[i][0]["beta"], xq=items[i][1], gamma=items[i][2],
-                                       n_out=items[i][4], y=items[i][3]) for i in grp], fmt, n, m)
-
-    for _ in range(3):
-        run()
-    torch.cuda.synchronize()
-    reps = 20
-    tm.start()
-    for _ in range(reps):
-        run()
-    ms = tm.stop_ms() / reps
-    ops = sum(2 * m_tok * no * k for *_, no, k in items)
-    tops = ops / (ms * 1e-3) / 1e12
-    kernel = "gemm24_kernel (v_smfmac_i32_16x16x128_i8)" if (n, m) == (2, 4) else "gemm_kernel (v_mfma_i32_32x32x32_i8)"
-    return {"workload": f"Prefill GEMM, M=2048 tokens, 3B-class block (hidden 3200, FFN 8640), {n}:{m} N:M",
-            "kernel": kernel,
-            "ms_per_block": round(ms, 4), "int8_TOPS": round(tops, 2),
-            "useful_TOPS": round(tops * n / m, 2),
-            "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS,
-                         "unit": "TOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": None}}
-
-
-BF16_PEAK_TFLOPS = 2500.0
-
-
-def bench_backward(torch, np, synth, sbl, dev, tm, n=6, m=8):
-    """Backward of a 3B-class block at M = 2048 tokens, 6:8 weights: sbl_linear_backward (dX and dW
-    of the 7 matrices) on the BF16 matrix cores.  Algorithmic flops 2*M*N*K per gradient; dW runs
-    three BF16 products per step (x_hat split exactly into three parts), counted separately."""
-    wname, h, f, m_tok = "b3_prefill", 3200, 8640, 2048
-    fmt = 1
-    mats = synth.block_shapes(h, f)
-    g = torch.Generator(device=dev).manual_seed(11)
-    items = []
-    for i, (_, no, k) in enumerate(mats):
-        w = torch.from_numpy(synth.workload_masters(wname, i, no, k).view(np.int16)).to(dev)
-        o = sbl.quant_weights(w, n, m, fmt=fmt)
-        x = torch.from_numpy(synth.workload_acts(wname, i, m_tok, k)).to(dev)
-        xq, gamma = sbl.quant_acts(x)
-        dy = (torch.randn((m_tok, no), generator=g, device=dev) * 0.05).to(torch.bfloat16)
-        dx = torch.empty((m_tok, k), dtype=torch.float32, device=dev)
-        dw = torch.empty((no, k), dtype=torch.float32, device=dev)
-        items.append((o, x, xq, gamma, dy, dx, dw, no, k))
-        del w
-
-    def run(which):
-        for o, x, xq, gamma, dy, dx, dw, no, k in items:
-            sbl.sbl_linear_backward(dy, o["packed"], o["meta"], fmt, n, m, o["beta"], x, xq, gamma,
-                                    dx=dx if which in ("dx", "both") else None,
-                                    dw=dw if which in ("dw", "both") else None)
-
-    res = {}
-    for which in ("dx", "dw", "both"):
-        for _ in range(2):
-            run(which)
-        torch.cuda.synchronize()
-        reps = 5
-        tm.start()
-        for _ in range(reps):
-            run(which)
-        res[which] = tm.stop_ms() / reps
-    flops = sum(2 * m_tok * no * k for *_, no, k in items)
-    tf = {w: (flops * (2 if w == "both" else 1)) / (res[w] * 1e-3) / 1e12 for w in res}
-    mfma_tf_dw = 3 * flops / (res["dw"] * 1e-3) / 1e12
-    return {"workload": f"Backward (dX and dW), M=2048 tokens, 3B-class block (hidden 3200, FFN 8640), {n}:{m} N:M",
-            "kernel": "backward_dx_kernel, backward_dw_kernel (v_mfma_f32_32x32x16_bf16)",
-            "ms_per_block": {w: round(v, 3) for w, v in res.items()},
-            "algorithmic_TFLOPS": {w: round(v, 1) for w, v in tf.items()},
-            "dw_mfma_TFLOPS": round(mfma_tf_dw, 1),
-            "roofline": {"bound": "mfma", "achieved": round(tf["both"], 1), "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf["both"] / BF16_PEAK_TFLOPS, 4), "traffic": None}}
-
-
-def cpu_baseline(np, synth, wname, mats, m_tok, n, m, fmt, budget_s, step_bytes):
-    """The CPU oracle, untuned, on the same workload: whole blocks until the
-    budget is spent.  Each stage is one oracle call, timed on its own, in the
-    order the oracle's quant_weights and linear compose them."""
-    from threadpoolctl import threadpool_limits
-
+    import synth
     from oracle import sbl_oracle as O
-    done_bytes, blocks, t_total, weights, ops = 0, 0, 0.0, 0, 0
-    stages = dict.fromkeys(("beta", "mask", "codes", "pack", "quant_acts", "contract", "rescale"), 0.0)
-
-    def timed(name, fn, *a):
-        t = time.perf_counter()
-        r = fn(*a)
-        stages[name] += time.perf_counter() - t
-        return r
-
-    with threadpool_limits(1):
-        while t_total < budget_s and blocks < 3:
-            for i, (_, no, k) in enumerate(mats):
-                bits = synth.workload_masters(wname, i, no, k)
-                first = {0: 0, 1: 0, 2: 0, 3: 3, 4: 4, 5: 4, 6: 6}[i]    # shared block inputs
-                x = synth.workload_acts(wname, first, m_tok, k)
-                beta = timed("beta", O.absmean_beta, bits)
-                keep = timed("mask", O.nm_keep, bits, n, m)
-                codes = timed("codes", lambda: (O.ternarize(bits, beta) * keep.astype(np.int8)).astype(np.int8))
-                if fmt == 1:
-                    timed("pack", lambda: (O.to_panels(O.pack_nm(codes, keep, n, m), 16 * n // m),
-                                           O.to_panels(O.pack_bitmap(keep), 8)))
-                else:
-                    timed("pack", lambda: O.to_panels(O.pack_dense2(codes), 16))
-                q, gamma = timed("quant_acts", O.quant_acts, x)
-                acc = timed("contract", O.contract, codes, q)
-                timed("rescale", O.rescale, acc, beta, gamma)
-                weights += no * k
-                ops += 2 * m_tok * no * k
-            blocks += 1
-            done_bytes += step_bytes
-            t_total = sum(stages.values())
-    gbps = done_bytes / t_total / 1e9
+    fmt, n, m = FORMATS[args.fmt]
+    _, no, k = mats_of(args.block)[0]
+    wname = BLOCKS[args.block][0]
+    rows = 1024
+    x = synth.workload_acts(wname, 0, args.m_tok, k)
+    bits = synth.workload_masters(wname, 0, no, k)[:rows]
+    beta, keep, codes = O.quant_weights(bits, n, m)
+    if fmt == 1:
+        stored = (O.to_panels(O.pack_nm(codes, keep, n, m), 16 * n // m), O.to_panels(O.pack_bitmap(keep), 8))
+    else:
+        stored = (O.to_panels(O.pack_dense2(codes), 16), None)
+    nbytes = sum(a.size for a in stored if a is not None)
+    cores = len(os.sched_getaffinity(0))
+    stages = dict.fromkeys(("unpack", "quant_acts", "contract", "rescale"), 0.0)
+    reps = 0
+    with threadpool_limits(cores):
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        while sum(stages.values()) < budget_s and reps < 1000:
+            t = time.perf_counter()
+            if fmt == 1:
+                c2 = O.unpack_nm(O.from_panels(stored[0], rows, k * n // (4 * m), 16 * n // m),
+                                 O.from_panels(stored[1], rows, k // 8, 8), n, m, k)
+            else:
+                c2 = O.unpack_dense2(O.from_panels(stored[0], rows, k // 4, 16), k)
+            t1 = time.perf_counter()
+            q, gamma = O.quant_acts(x)
+            t2 = time.perf_counter()
+            acc = O.contract(c2, q)
+            t3 = time.perf_counter()
+            O.rescale(acc, beta, gamma)
+            t4 = time.perf_counter()
+            for s_, dt in zip(stages, (t1 - t, t2 - t1, t3 - t2, t4 - t3)):
+                stages[s_] += dt
+            reps += 1
+    total = sum(stages.values())
     try:
         model = next(ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name"))
     except (OSError, StopIteration):
         model = None
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{blocks} full block step(s) of the same workload ({len(mats)} matrices), "
-                      f"{t_total:.1f} s single-threaded NumPy",
-            "stages_s": {k: round(v, 4) for k, v in stages.items()},
-            "weights_per_s": round(weights / t_total, 1), "ops_per_s": round(ops / t_total, 1),
-            "host_cpus": len(os.sched_getaffinity(0)), "host_cpu_model": model}
+    return {"value": round(reps * nbytes / total / 1e9, 5), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} decodes of {rows} x {k} rows of the block's first matrix ({args.fmt}, "
+                      f"M={args.m_tok}): {total:.1f} s of timed oracle work (NumPy; BLAS contraction on "
+                      f"{threads} threads, other stages one thread); packed weight bytes per second",
+            "stages_s": {s_: round(v, 4) for s_, v in stages.items()},
+            "weights_per_s": round(reps * rows * k / total, 1), "host_cpus": cores, "host_cpu_model": model}
+
+
+# --------------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.record_traffic:
+        record_traffic(args)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU (asked for --gpus {args.gpus}): the path runs on one MI355X "
+              "here; how it would shard across GPUs is described, not built", file=sys.stderr)
+        sys.exit(2)
+    sections = set(args.sections.split(","))
+    bad = sections - set(SECTIONS)
+    if bad:
+        raise SystemExit(f"unknown sections: {sorted(bad)}")
+    import numpy as np
+    import torch
+
+    from sparse_linear_layers_absmean_amd import sbl
+
+    sbl.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tm = Timer(torch)
+    if args.copy_calibration_mb > 0:
+        nb = int(args.copy_calibration_mb * 1e6) // 16 * 16
+        src = torch.ones(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    t0 = time.time()
+    line = {}
+    masters = {}
+    pre_blocks = {c.split(":")[0] for c in args.prefill_cases.split(",")} if "prefill" in sections else set()
+    if "backward" in sections or "3b" in pre_blocks:
+        masters["3b"] = synth_masters("3b", mats_of("3b"))
+    if "train13b" in sections or "13b" in pre_blocks:
+        masters["13b"] = synth_masters("13b", mats_of("13b"))
+    if "prefill" in sections:
+        line["prefill"] = bench_prefill(torch, np, sbl, dev, tm, masters, args.prefill_cases)
+    if "train13b" in sections:
+        line["train_step_13b"] = bench_train13b(torch, np, sbl, dev, tm, masters["13b"])
+    masters.pop("13b", None)
+    if "weight_prep" in sections:
+        line["weight_prep"] = weight_prep_sweep(torch, np, sbl, dev, tm)
+    if "step0p7b" in sections:
+        line["step_0p7b"] = bench_step0p7b(torch, np, sbl, dev, tm)
+    if "gemv" in sections:
+        line["gemv"] = gemv_sweep(torch, np, sbl, dev, tm)
+    if "backward" in sections:
+        line["backward"] = bench_backward(torch, np, sbl, dev, tm, masters["3b"])
+    masters.clear()
+    if "group_scales" in sections:
+        line["group_scales"] = bench_group_scales(torch, np, sbl, dev, tm)
+    if "references" in sections:
+        line["measured_library"] = references(torch, dev, tm)
+    head = None
+    if "headline" in sections:
+        # last, so that the timed steps end a profiled run
+        head = bench_decode_step(torch, np, sbl, dev, tm, args)
+    cpu = cpu_baseline(np, args, args.cpu_seconds) if "cpu" in sections else None
+    desc = f"Decode GEMV, M={args.m_tok} token(s), {BLOCKS[args.block][3]}, {args.fmt} packed ternary weights"
+    out = {
+        "metric": METRIC,
+        "value": round(head["gbps"], 1) if head else None,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["step_ms"], 5) if head else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic: " + (head["master_src"] if head else "") + ", N(0,1) fp32 activations; "
+                "seeded CPU generators elsewhere",
+        "config": {"workload": desc, "format": args.fmt, "m_tok": args.m_tok, "matrices": 7,
+                   "block_weights": head["weights"] if head else None,
+                   "packed_weight_bytes_per_step": head["wbytes"] if head else None,
+                   "rotation_copies": head["copies"] if head else None,
+                   "step": "per input (q/k/v, o, gate/up, down): sbl_linear_acts_batch = per-token int8 "
+                           "quantization + ternary x int8 GEMV + fp32 rescale, one fused launch; weights "
+                           "prepared by sbl_quant_weights_batch before timing"},
+        "roofline": head["roofline"] if head else None,
+        "frac_of_hbm_peak": round(head["gbps"] / HBM_PEAK_GBPS, 4) if head else None,
+    }
+    out.update(line)
+    out["cpu_baseline"] = cpu
+    out["bench_s"] = round(time.time() - t0, 1)
+    out["device"] = torch.cuda.get_device_name(0)
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":
