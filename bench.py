@@ -12,7 +12,9 @@ input.  The weights were prepared before the timed region by
 masters, ternary codes, packing), as a decoder prepares them once at load.
 `value` is the packed weight bytes (codes + metadata) streamed per second.
 Steps rotate over distinct copies of the packed weights (>= 560 MB), so the
-256 MB Infinity Cache cannot serve a step from the previous one.
+256 MB Infinity Cache cannot serve a step from the previous one; one HIP graph
+holds a pass over all copies (as a model's decode graph holds all its
+layers), so a graph's own launch cost is shared by several steps.
 
 Side measurements in the same line: prefill GEMMs (3B-class block, 2048
 tokens, 6:8 / DENSE2 on the dense int8 MFMA, 2:4 on the sparse MFMA; 13B-class
@@ -207,24 +209,34 @@ class Timer:
         return self.a.elapsed_time(self.b)
 
 
-def capture(torch, fn):
-    """One eager run (every kernel loaded), then a HIP graph of fn."""
-    fn()
+def timed_steps(torch, tm, fn, copies, steps, warm=None):
+    """ms per call of fn(c), timing exactly `steps` calls that rotate over the
+    copies c = 0, 1, ...: one HIP graph holds a pass over all copies (so the
+    per-replay launch cost of a graph is shared by `copies` steps, as in a
+    model whose decode graph holds every layer), a second one the remainder."""
+    fn(0)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        fn()
-    return g
 
+    def graph(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in range(n):
+                fn(c)
+        return g
 
-def time_graphs(torch, tm, graphs, reps, warm=None):
-    for r in range(len(graphs) if warm is None else warm):
-        graphs[r % len(graphs)].replay()
+    full = graph(copies)
+    rem = graph(steps % copies) if steps % copies else None
+    for _ in range(max(1, -(-(copies if warm is None else warm) // copies))):
+        full.replay()
     torch.cuda.synchronize()
     tm.start()
-    for r in range(reps):
-        graphs[r % len(graphs)].replay()
-    return tm.stop_ms() / reps
+    for _ in range(steps // copies):
+        full.replay()
+    if rem is not None:
+        rem.replay()
+    ms = tm.stop_ms() / steps
+    del full, rem
+    return ms
 
 
 def rot_copies(per_copy_bytes, floor=560e6, cap=64):
@@ -312,8 +324,7 @@ def bench_decode_step(torch, np, sbl, dev, tm, args):
             sbl.sbl_linear_acts_batch(xs[gi], acts[gi]["xq"], acts[gi]["gamma"],
                                       [dict(pool[c][i], y=ys[i]) for i in grp], fmt, n, m)
 
-    graphs = [capture(torch, lambda c=c: step(c)) for c in range(copies)]
-    step_ms = time_graphs(torch, tm, graphs, args.steps, warm=args.warmup)
+    step_ms = timed_steps(torch, tm, step, copies, args.steps, warm=args.warmup)
     launches = len(GROUPS)
     alg = wbytes + sum(m_tok * mats[g[0]][2] * 5 + 4 * m_tok for g in GROUPS) + \
         sum(4 * m_tok * no for _, no, _k in mats)
@@ -328,7 +339,7 @@ def bench_decode_step(torch, np, sbl, dev, tm, args):
             "note": "algorithmic bytes (packed weights + metadata, fp32 input read, int8 input and gamma "
                     "written, fp32 outputs) per launch / average launch time (HIP events around the timed "
                     "graph replays, gaps included); traffic: counter bytes per launch (profiles/traffic.json)"}
-    del graphs, pool
+    del pool
     torch.cuda.empty_cache()
     return dict(step_ms=step_ms, gbps=gbps, wbytes=wbytes, copies=copies, roofline=roof,
                 master_src=master_src, weights=sum(no * k for _, no, k in mats))
@@ -371,15 +382,14 @@ def gemv_sweep(torch, np, sbl, dev, tm):
                 for gi, grp in enumerate(GROUPS):
                     sbl.sbl_linear_batch([dict(pool[c][i], xq=xs[gi], gamma=gam) for i in grp], fmt, n, m)
 
-            graphs = [capture(torch, lambda c=c: run(c)) for c in range(copies)]
-            us = time_graphs(torch, tm, graphs, max(40, 2 * copies)) * 1e3
+            us = timed_steps(torch, tm, run, copies, 8 * copies) * 1e3
             gbps = bb / (us * 1e-6) / 1e9
             hbm = bb + sum(m_tok * mats[g_[0]][2] + 4 * m_tok for g_ in GROUPS) + \
                 sum(4 * m_tok * no for _, no, _k in mats)
             out.append({"block": blk, "format": fname, "m_tok": m_tok, "weight_bytes": bb,
                         "us_per_block": round(us, 2), "weight_GBps": round(gbps, 1),
                         "hbm_GBps": round(hbm / (us * 1e-6) / 1e9, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)})
-            del pool, graphs, xs
+            del pool, xs
             torch.cuda.empty_cache()
     return out
 
@@ -417,8 +427,7 @@ def bench_prefill(torch, np, sbl, dev, tm, masters_by_block, cases):
                 sbl.sbl_linear_batch([dict(pool[c][i], xq=acts[gi][0], gamma=acts[gi][1], y=ys[i]) for i in grp],
                                      fmt, n, m)
 
-        graphs = [capture(torch, lambda c=c: run(c)) for c in range(2)]
-        ms = time_graphs(torch, tm, graphs, 10)
+        ms = timed_steps(torch, tm, run, 2, 10)
         ops = sum(2 * m_tok * no * k for _, no, k in mats)
         tops = ops / (ms * 1e-3) / 1e12
         sparse = fname == "nm24"
@@ -435,7 +444,7 @@ def bench_prefill(torch, np, sbl, dev, tm, masters_by_block, cases):
                                  "peak_kind": "int8 2:4 sparse MFMA (dense-equivalent ops)" if sparse
                                  else "int8 dense MFMA",
                                  "avg_launch_us": round(ms * 1e3 / len(GROUPS), 2)}})
-        del graphs, pool, outs, acts, ys
+        del pool, outs, acts, ys
         torch.cuda.empty_cache()
     return out
 
@@ -479,16 +488,13 @@ def bench_train13b(torch, np, sbl, dev, tm, masters13):
             sbl.sbl_linear_acts_batch(xs[gi], acts[gi]["xq"], acts[gi]["gamma"], [outs[i] for i in grp],
                                       fmt, n, m)
 
-    step_g = [capture(torch, lambda c=c: (prep(c), fwd(c))) for c in range(copies)]
-    prep_g = [capture(torch, lambda c=c: prep(c)) for c in range(copies)]
-    fwd_g = [capture(torch, lambda c=c: fwd(c)) for c in range(copies)]
-    step_ms = time_graphs(torch, tm, step_g, 10)
-    prep_us = time_graphs(torch, tm, prep_g, 20) * 1e3
-    fwd_ms = time_graphs(torch, tm, fwd_g, 10)
+    step_ms = timed_steps(torch, tm, lambda c: (prep(c), fwd(c)), copies, 10)
+    prep_us = timed_steps(torch, tm, prep, copies, 20) * 1e3
+    fwd_ms = timed_steps(torch, tm, fwd, copies, 10)
     weights = sum(no * k for _, no, k in mats)
     prep_alg = sum(2 * no * k + packed_bytes(sbl, no, k, n, m, fmt) for _, no, k in mats)
     ops = 2 * m_tok * weights
-    del step_g, prep_g, fwd_g, state
+    del state
     torch.cuda.empty_cache()
     return {"workload": f"Training-step path, {BLOCKS['13b'][3]}, 6:8 N:M, M=4096 tokens, "
                         "masters with near-ties planted on the keep boundary",
@@ -522,14 +528,14 @@ def weight_prep_sweep(torch, np, sbl, dev, tm):
                                                  device=dev),
                               meta=torch.empty((no, k // 8), dtype=torch.uint8, device=dev),
                               workspace=sbl.new_workspace(no, k, dev)) for _, no, k in mats])
-        graphs = [capture(torch, lambda c=c: sbl.sbl_quant_weights_batch(pool[c], n, m, fmt)) for c in range(copies)]
-        us = time_graphs(torch, tm, graphs, max(20, 2 * copies)) * 1e3
+        us = timed_steps(torch, tm, lambda c: sbl.sbl_quant_weights_batch(pool[c], n, m, fmt), copies,
+                         max(20, 2 * copies)) * 1e3
         alg = sum(2 * no * k + packed_bytes(sbl, no, k, n, m, fmt) for _, no, k in mats)
         gbps = alg / (us * 1e-6) / 1e9
         out.append({"block": blk, "weights": bw, "us_per_call": round(us, 2), "alg_GBps": round(gbps, 1),
                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
                     "path": "one launch (resident_kernel)" if bw * 2 <= 67e6 else "two launches (absmean + mask_pack)"})
-        del pool, graphs
+        del pool
         torch.cuda.empty_cache()
     return out
 
@@ -571,12 +577,11 @@ def bench_step0p7b(torch, np, sbl, dev, tm):
         for gi, grp in enumerate(GROUPS):
             sbl.sbl_linear_acts_batch(xs[gi], acts[gi]["xq"], acts[gi]["gamma"], [outs[i] for i in grp], fmt, n, m)
 
-    graphs = [capture(torch, lambda c=c: step(c)) for c in range(copies)]
-    ms = time_graphs(torch, tm, graphs, 50)
+    ms = timed_steps(torch, tm, step, copies, 10 * copies)
     pb = sum(packed_bytes(sbl, no, k, n, m, fmt) for _, no, k in mats)
     alg = 2 * bw + 2 * pb + sum(m_tok * mats[g[0]][2] * 5 + 4 * m_tok for g in GROUPS) + \
         sum(4 * m_tok * no for _, no, _k in mats)
-    del graphs, st
+    del st
     torch.cuda.empty_cache()
     return {"workload": "Whole path, M=1 token, 0.7B-class block (hidden 1536, FFN 4096), 6:8 N:M: "
                         "weight preparation + fused activation quantization and GEMV",
@@ -663,13 +668,11 @@ def bench_group_scales(torch, np, sbl, dev, tm, rpg=128, kg=320, n=6, m=8):
             for i, (_, no, k) in enumerate(mats):
                 sbl.sbl_quant_weights_grouped(masters[c][i], n, m, r, betas[i], wss[i], fmt=fmt,
                                               packed=outs[c][i]["packed"], meta=outs[c][i]["meta"])
-        graphs = [capture(torch, lambda c=c: prep(c)) for c in range(copies)]
-        us = time_graphs(torch, tm, graphs, max(10, 2 * copies)) * 1e3
+        us = timed_steps(torch, tm, prep, copies, max(10, 2 * copies)) * 1e3
         gbps = (2 * bw + wbytes) / (us * 1e-6) / 1e9
         out["weight_prep"].append({"rows_per_group": r, "groups": sum(-(-no // r) for _, no, k in mats),
                                    "us_per_block": round(us, 1), "alg_GBps": round(gbps, 1),
                                    "frac": round(gbps / HBM_PEAK_GBPS, 4)})
-        del graphs
     del masters
     torch.cuda.empty_cache()
     pcopies = rot_copies(wbytes, 600e6)
@@ -702,12 +705,10 @@ def bench_group_scales(torch, np, sbl, dev, tm, rpg=128, kg=320, n=6, m=8):
                            ("sbl_linear_grouped", grouped, f"beta per {rpg} rows: GEMV + grouped rescale"),
                            ("sbl_linear_kgrouped", kgrouped,
                             f"beta per {rpg} rows, gamma per {kg} features: activation quant + product")):
-        graphs = [capture(torch, lambda c=c: fn(c)) for c in range(pcopies)]
-        us = time_graphs(torch, tm, graphs, max(20, 2 * pcopies)) * 1e3
+        us = timed_steps(torch, tm, fn, pcopies, max(20, 2 * pcopies)) * 1e3
         gbps = wbytes / (us * 1e-6) / 1e9
         out["products"].append({"call": name, "scales": what, "us_per_block": round(us, 1),
                                 "weight_GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)})
-        del graphs
     del pool, outs
     torch.cuda.empty_cache()
     return out

@@ -39,9 +39,7 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,6 +48,24 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed building libsbl.so")
     if verbose and res.stderr.strip():
         sys.stderr.write(res.stderr)
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every source to an object in parallel (each is its own
+    translation unit), then link the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
+    srcs = sources()
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
+    cmds = [[hipcc(), *compile_flags, "-I", os.path.join(ROOT, "include"), "-c", s, "-o", o]
+            for s, o in zip(srcs, objs)]
+    jobs = jobs or max(1, min(len(cmds), len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -25,6 +25,7 @@
 // branch around a load.  Partial int32 tiles of the ks waves are summed
 // through LDS, then rescaled.  Up to 8 independent matrices share one launch
 // (grouped GEMV).  Everything integer is exact: |acc| <= 127 k < 2^24.
+#include "sbl_actq.h"
 #include "sbl_decode.h"
 
 namespace sbl {
@@ -40,16 +41,8 @@ constexpr int kXBigMax = 128 * 1024;   // ... and by LDS-direct loads up to this
 constexpr int kBigLdsAttr = 150 * 1024;  // dynamic LDS the LDS-direct mode may request
 constexpr int64_t kXBigMinWeights = int64_t(128) << 20;   // weights per launch for the LDS-direct mode
 constexpr int kXMinWaves = 4;          // XL launches have at least this many waves per workgroup
-constexpr int kXFPer = 3;              // fused quantization: 16-value pieces of x per thread, at most
+constexpr int kXFPer = 4;              // fused quantization: 16-value pieces of x per thread, at most
 
-// Activation quantization, identical to the standalone quantizer: step
-// s = max(gamma, 1e-5) / 128 (exact scaling), q = clamp(rint(x / s), -127, 127)
-// with one IEEE fp32 division.
-__device__ __forceinline__ float act_step(float gamma) { return fmaxf(gamma, 1e-5f) * 0.0078125f; }
-__device__ __forceinline__ uint32_t act_q(float v, float s) {
-  const float r = fminf(fmaxf(rintf(v / s), -127.0f), 127.0f);
-  return (uint32_t)((int32_t)r) & 0xFFu;
-}
 constexpr uint32_t kFar = 0x80000000u; // a buffer offset beyond every buffer: reads zeros
 
 struct GemvLaunch {
@@ -334,9 +327,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
       if (i < nxl && o < xbytes) {
         float mx = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xf4[i][j].x), fabsf(xf4[i][j].y)),
-                               fmaxf(fabsf(xf4[i][j].z), fabsf(xf4[i][j].w))));
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, actq::absmax4(xf4[i][j]));
         atomicMax(&gbits[o / (uint32_t)d.k], __float_as_uint(mx));   // order of non-negative floats = of their bits
       }
     }
@@ -346,12 +337,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
     for (int i = 0; i < kXPer; ++i) {
       const uint32_t o = (threadIdx.x + i * blockDim.x) * 16u;
       if (i < nxl && o < xbytes) {
-        const float sc = act_step(__uint_as_float(gbits[o / (uint32_t)d.k]));
+        // the standalone quantizer's step (same bits)
+        const actq::Step st = actq::make_step(__uint_as_float(gbits[o / (uint32_t)d.k]));
         u32x4 v;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          v[j] = act_q(xf4[i][j].x, sc) | (act_q(xf4[i][j].y, sc) << 8) | (act_q(xf4[i][j].z, sc) << 16) |
-                 (act_q(xf4[i][j].w, sc) << 24);
+        for (int j = 0; j < 4; ++j) v[j] = actq::q_word(xf4[i][j], st);
         *reinterpret_cast<u32x4*>(smem + o) = v;
         if (publish) *reinterpret_cast<u32x4*>(d.xq_out + o) = v;
         int q = 0;
@@ -627,9 +617,14 @@ GemvShape gemv_shape(const LinDesc* items, int count) {
   return g;
 }
 
-// whether the fused activation quantization covers m_tok x k activations at this shape
+// whether the fused activation quantization covers m_tok x k activations at
+// this shape, and pays: every workgroup reads and quantizes the whole input,
+// so beyond kXFuseMax values per launch the standalone quantizer (one launch,
+// ~3.5 us) costs less (measured, 70B-class widths: 8192 inputs fused +1-2 us
+// per launch against +3.5 us; 28672 inputs fused +8 us against +5 us)
+constexpr int64_t kXFuseMax = 16384;
 bool gemv_fuses(const GemvShape& g, int64_t m_tok, int64_t k) {
-  return g.xlm == 1 && m_tok * k <= (int64_t)16 * kXFPer * 64 * g.ks * g.tb;
+  return g.xlm == 1 && m_tok * k <= kXFuseMax && m_tok * k <= (int64_t)16 * kXFPer * 64 * g.ks * g.tb;
 }
 
 // xf: fp32 activations shared by every item, quantized inside the launch

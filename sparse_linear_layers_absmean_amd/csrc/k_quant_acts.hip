@@ -5,57 +5,81 @@
 // 2^(b-1); BitNet spec: 8-bit activations.  Per token (one row of x):
 //   gamma = max_k |x|                      (exact, any order)
 //   s     = max(gamma, 1e-5) / 128         (exact power-of-two scaling)
-//   q     = clamp(rint(x / s), -127, 127)  (one IEEE fp32 division, rint to even)
-// One workgroup per token: a wavefront max-reduction, then a second sweep
-// over the row (now L2-resident) that writes 4 int8 per 16-byte load.
-#include "sbl_internal.h"
+//   q     = clamp(rint(x / s), -127, 127)  (the IEEE quotient, rint to even;
+//                                           evaluated as in sbl_actq.h)
+// One workgroup per token.  Every thread issues the loads of all its 16-byte
+// pieces of the row at once and keeps them in registers (up to PER pieces),
+// so a row costs one memory round trip; the wavefront max-reduction and the
+// quantization then run from registers.  Rows longer than THREADS*PER pieces
+// take a second sweep over the row (by then in L2).  Decode-sized batches use
+// 1024-thread workgroups (a few tokens must still fill many waves), larger
+// batches 256-thread ones.
+#include "sbl_actq.h"
 
 namespace sbl {
 
 namespace {
 
-constexpr int kThreads = 256;
-
-__device__ __forceinline__ uint32_t q_byte(float v, float s) {
-  const float r = rintf(v / s);
-  const float c = fminf(fmaxf(r, -127.0f), 127.0f);
-  return (uint32_t)((int32_t)c) & 0xFFu;
-}
-
-__global__ __launch_bounds__(kThreads) void quant_acts_kernel(const float4* __restrict__ x, int64_t k4,
-                                                              uint32_t* __restrict__ xq,
-                                                              float* __restrict__ gamma) {
+template <int THREADS, int PER>
+__global__ __launch_bounds__(THREADS) void quant_acts_kernel(const float4* __restrict__ x, int64_t k4,
+                                                             uint32_t* __restrict__ xq,
+                                                             float* __restrict__ gamma) {
+  constexpr int kWaves = THREADS / 64;
   const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
   const float4* xr = x + row * k4;
+  uint32_t* qr = xq + row * k4;
+  const bool held = k4 <= (int64_t)THREADS * PER;
+  // pieces past the row read zeros (buffer loads), so every load is issued
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(xr, held ? k4 * 16 : 0);
+  float4 v[PER];
   float mx = 0.0f;
-  for (int64_t i = threadIdx.x; i < k4; i += kThreads) {
-    const float4 v = xr[i];
-    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  if (held) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      v[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(tid + i * THREADS) * 16u, 0, 0));
+#pragma unroll
+    for (int i = 0; i < PER; ++i) mx = fmaxf(mx, actq::absmax4(v[i]));
+  } else {
+    for (int64_t i = tid; i < k4; i += 4 * THREADS) {
+      float4 w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = i + u * THREADS < k4 ? xr[i + u * THREADS] : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) mx = fmaxf(mx, actq::absmax4(w[u]));
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  __shared__ float wmax[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+  __shared__ float wmax[kWaves];
+  if ((tid & 63) == 0) wmax[tid >> 6] = mx;
   __syncthreads();
   float g = wmax[0];
 #pragma unroll
-  for (int i = 1; i < kThreads / 64; ++i) g = fmaxf(g, wmax[i]);
-  const float s = fmaxf(g, 1e-5f) * 0.0078125f;
-  uint32_t* qr = xq + row * k4;
-  for (int64_t i = threadIdx.x; i < k4; i += kThreads) {
-    const float4 v = xr[i];
-    qr[i] = q_byte(v.x, s) | (q_byte(v.y, s) << 8) | (q_byte(v.z, s) << 16) | (q_byte(v.w, s) << 24);
+  for (int i = 1; i < kWaves; ++i) g = fmaxf(g, wmax[i]);
+  const actq::Step st = actq::make_step(g);
+  if (held) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int64_t idx = tid + (int64_t)i * THREADS;
+      if (idx < k4) qr[idx] = actq::q_word(v[i], st);
+    }
+  } else {
+    for (int64_t i = tid; i < k4; i += THREADS) qr[i] = actq::q_word(xr[i], st);
   }
-  if (threadIdx.x == 0) gamma[row] = g;
+  if (tid == 0) gamma[row] = g;
 }
 
 }  // namespace
 
 hipError_t launch_quant_acts(const float* x, int64_t m_tok, int64_t k, int8_t* xq, float* gamma,
                              hipStream_t s) {
-  hipLaunchKernelGGL(quant_acts_kernel, dim3((unsigned)m_tok), dim3(kThreads), 0, s,
-                     reinterpret_cast<const float4*>(x), k / 4, reinterpret_cast<uint32_t*>(xq),
-                     gamma);
+  const float4* x4 = reinterpret_cast<const float4*>(x);
+  uint32_t* q4 = reinterpret_cast<uint32_t*>(xq);
+  if (m_tok < 128)
+    hipLaunchKernelGGL((quant_acts_kernel<1024, 8>), dim3((unsigned)m_tok), dim3(1024), 0, s, x4, k / 4, q4, gamma);
+  else
+    hipLaunchKernelGGL((quant_acts_kernel<256, 16>), dim3((unsigned)m_tok), dim3(256), 0, s, x4, k / 4, q4, gamma);
   return hipGetLastError();
 }
 

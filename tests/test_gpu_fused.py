@@ -19,6 +19,8 @@ CASES = [
     ("down 0.7B M=1", [(1536, 4096)], 1, FMT_NM, 2, 4),
     ("o 3B M=2", [(3200, 3200)], 2, FMT_NM, 6, 8),
     ("down 3B M=1", [(3200, 8640)], 1, FMT_NM, 6, 8),
+    ("down 70B M=1 (28672 inputs, fused)", [(64, 28672)], 1, FMT_NM, 6, 8),
+    ("down 70B M=2 (not fused)", [(48, 28672)], 2, FMT_DENSE2, 6, 8),
     ("ragged rows, partial panel, M=3", [(33, 320), (17, 320)], 3, FMT_DENSE2, 6, 8),
     ("one tile, M=16", [(16, 64)], 16, FMT_NM, 6, 8),
     ("wide input, M=16 (not fused)", [(64, 4096)], 16, FMT_NM, 6, 8),
@@ -92,3 +94,55 @@ def test_fused_matches_separate_and_oracle(case):
         acc_ref, y_ref = O.linear(codes, q_ref, beta, g_ref)
         assert np.array_equal(fa, acc_ref)
         check_y(fy, y_ref, acc_ref)
+
+
+def _near_half_rows(rng, n_rows, k):
+    """Rows whose values sit at and next to the rounding boundaries of the
+    quantizer: x = (j + 1/2) * s moved by up to 3 fp32 ulps, with s = gamma/128
+    for a gamma planted at position 0 (a power-of-two multiple or a random
+    value).  The rest of each row is filled with such values for random j."""
+    x = np.zeros((n_rows, k), np.float32)
+    for t in range(n_rows):
+        gamma = np.float32(3.0) if t % 2 == 0 else np.float32(rng.uniform(0.3, 40.0))
+        s = np.float32(gamma) * np.float32(1.0 / 128)
+        j = rng.integers(-128, 128, k - 1)
+        base = ((j + 0.5) * np.float64(s)).astype(np.float32)
+        steps = rng.integers(-3, 4, k - 1)
+        v = base.copy()
+        for d in (1, -1):
+            for _ in range(3):
+                mv = steps * d > 0
+                v[mv] = np.nextafter(v[mv], np.float32(d * np.inf))
+                steps = np.where(mv, steps - d, steps)
+        v = np.clip(v, -gamma, gamma)
+        x[t, 0] = gamma
+        x[t, 1:] = v
+    return x
+
+
+@pytest.mark.parametrize("m_tok,k", [(3, 4096), (130, 1024), (1, 28672)])
+def test_quant_acts_near_half_integers(m_tok, k):
+    """Values within a few ulps of the half-integers of x/s: the quantizer's
+    multiply-and-check evaluation must give the IEEE quotient's rounding
+    everywhere (the standalone quantizer in both workgroup shapes, and the
+    quantization fused into the GEMV)."""
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    rng = np.random.default_rng([73, m_tok, k])
+    x = _near_half_rows(rng, m_tok, k)
+    say(f"near-half activations m_tok={m_tok} k={k}")
+    q_ref, g_ref = O.quant_acts(x)
+    xq, gamma = sbl.quant_acts(to_dev(x))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(xq), q_ref)
+    assert np.array_equal(to_np(gamma), g_ref)
+    if m_tok <= 16:
+        bits = synth.gaussian_masters(rng, 32, k)
+        o = sbl.quant_weights(to_dev(bits), 6, 8, fmt=FMT_NM)
+        xq2 = torch.empty((m_tok, k), dtype=torch.int8, device="cuda")
+        g2 = torch.empty(m_tok, device="cuda")
+        y = torch.empty((m_tok, 32), device="cuda")
+        sbl.sbl_linear_acts_batch(to_dev(x), xq2, g2, [dict(o, n_out=32, y=y)], FMT_NM, 6, 8)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(xq2), q_ref)
+        assert np.array_equal(to_np(g2), g_ref)
