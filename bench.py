@@ -79,6 +79,9 @@ def parse():
     p.add_argument("--record-traffic", metavar="KEY", default=None,
                    help="do not run: read two rocprofv3 counter runs (--fetch-dir, --write-dir) and "
                         "record KEY's bytes per launch in profiles/traffic.json")
+    p.add_argument("--trace-summary", metavar="DIR", default=None,
+                   help="do not run: summarize a rocprofv3 --kernel-trace --stats output directory "
+                        "(per-kernel table; with --kernel/--count/--launches, the timed launches)")
     p.add_argument("--fetch-dir")
     p.add_argument("--write-dir")
     p.add_argument("--kernel", help="kernel-name prefix of the launches to count (--record-traffic)")
@@ -88,6 +91,7 @@ def parse():
                         "launches x steps: the timed steps, which end the profiled run)")
     p.add_argument("--prefill-cases", default="3b:nm68,3b:dense2,3b:nm24,13b:nm68,13b:dense2",
                    help="prefill cases block:format, in this order")
+    p.add_argument("--prep-blocks", default="0p7b,3b,13b", help="blocks of the weight-preparation sweep")
     p.add_argument("--summary", help="text summary to write under profiles/ (--record-traffic)")
     p.add_argument("--command", help="the profiled command, quoted in the summary (--record-traffic)")
     return p.parse_args()
@@ -107,15 +111,16 @@ def _sources_sha():
     return out
 
 
-def recorded_traffic(key):
-    """HBM bytes per launch recorded for `key` in profiles/traffic.json, or None
-    when there is no record or any kernel source has changed since (SHA-256)."""
+def recorded_traffic(key, field="bytes_per_launch"):
+    """HBM bytes per launch (or per step) recorded for `key` in
+    profiles/traffic.json, or None when there is no record or any kernel
+    source has changed since (SHA-256)."""
     try:
         with open(TRAFFIC_JSON) as fh:
             rec = json.load(fh)[key]
         if rec["sources_sha256"] != _sources_sha():
             return None
-        return rec["bytes_per_launch"]
+        return rec[field]
     except (OSError, KeyError, ValueError):
         return None
 
@@ -129,16 +134,74 @@ def _counter_rows(d):
         return list(csv.DictReader(fh))
 
 
+def _short_name(full, args_too=False):
+    """Kernel name without return type, namespaces and (unless args_too)
+    template arguments: 'void sbl::(anonymous namespace)::gemv_kernel<1, 1, 2, true>(...)'
+    -> 'gemv_kernel' (or 'gemv_kernel<1, 1, 2, true>')."""
+    nm = full.replace("(anonymous namespace)::", "").replace("void ", "").strip()
+    nm = nm.split("(")[0].split("::")[-1]
+    return nm if args_too else nm.split("<")[0]
+
+
+def trace_summary(args):
+    """Text summary of a kernel-trace run: every kernel's calls and durations
+    (from the --stats table), then, for --kernel prefixes, the last --count
+    dispatches (the timed steps) with their mean duration per launch and per
+    step of --launches launches."""
+    import csv
+    d = args.trace_summary
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    out = [f"# Kernel time: {args.record_traffic or os.path.basename(d.rstrip('/'))}", "",
+           "Command (MI355X, one GPU):",
+           f"    cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- {args.command}", ""]
+    if stats:
+        with open(stats[0]) as fh:
+            rows = list(csv.DictReader(fh))
+        out.append(f"{'kernel':70s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}")
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:25]:
+            out.append(f"{_short_name(r['Name'], True)[:70]:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                       f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
+    if trace and args.kernel:
+        with open(trace[0]) as fh:
+            rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
+        prefixes = args.kernel.split(",")
+        mine = [r for r in rows if any(_short_name(r["Kernel_Name"]).startswith(p) for p in prefixes)]
+        use = mine[-args.count:]
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in use]
+        span = (int(use[-1]["End_Timestamp"]) - int(use[0]["Start_Timestamp"])) / 1e3
+        steps = len(use) // args.launches
+        out += ["", f"Timed launches: the last {len(use)} dispatches of {args.kernel} "
+                    f"({args.launches} per step, {steps} steps).",
+                f"  mean kernel duration per launch: {sum(durs) / len(durs):.2f} us "
+                f"(kernel time per step {sum(durs) / steps:.2f} us)",
+                f"  first start to last end: {span:.1f} us = {span / steps:.2f} us per step "
+                f"(kernel time plus the gaps between dependent launches)"]
+        per_pos = {}
+        for i, (r, t) in enumerate(zip(use, durs)):
+            per_pos.setdefault(i % args.launches, []).append((_short_name(r["Kernel_Name"], True), t,
+                                                               r.get("Grid_Size_X") or r.get("Grid_Size")))
+        for pos, v in sorted(per_pos.items()):
+            out.append(f"  launch {pos}: {v[0][0][:60]} grid {v[0][2]}: mean {sum(t for _, t, _ in v) / len(v):.2f} us")
+    text = "\n".join(out) + "\n"
+    if args.summary:
+        with open(os.path.join(ROOT, args.summary), "w") as fh:
+            fh.write(text)
+    print(text)
+
+
 def record_traffic(args):
-    """Bytes per launch of one kernel from a FETCH_SIZE run and a WRITE_SIZE run
-    of the same command, each scaled by what the counter reads for the known
-    copy of --copy-calibration-mb (the first dispatch of the blit kernel that
-    copies it).  The counted launches are the last --count dispatches of the
-    kernel (default launches x steps: the timed steps, which end the run)."""
+    """Bytes per launch of the counted kernels from a FETCH_SIZE run and a
+    WRITE_SIZE run of the same command, each scaled by what the counter reads
+    for the known copy of --copy-calibration-mb (the first dispatch of the
+    blit kernel that copies it).  --kernel is a comma list of kernel-name
+    prefixes; the counted dispatches are the last --count of those kernels
+    (default launches x steps: the timed steps, which end the run), and
+    --launches of them make one step."""
+    prefixes = args.kernel.split(",")
     res = {}
     for name, d in (("FETCH_SIZE", args.fetch_dir), ("WRITE_SIZE", args.write_dir)):
         rows = [r for r in _counter_rows(d) if r["Counter_Name"] == name]
-        cal_bytes = None
         per_dispatch = {}
         for r in rows:
             per_dispatch.setdefault(r["Dispatch_Id"], [r, 0.0])[1] += float(r["Counter_Value"])
@@ -147,27 +210,27 @@ def record_traffic(args):
         if not copies:
             raise SystemExit("calibration copy not found (run with --copy-calibration-mb)")
         cal_bytes = float(args.copy_calibration_mb) * 1e6 // 16 * 16
-        # a copy reads and writes its size once
-        factor = cal_bytes / (copies[0] * 1024.0)
-        mine = [(r, v) for r, v in ordered
-                if r["Kernel_Name"].split("(")[0].replace("void ", "").strip().startswith(args.kernel)]
+        factor = cal_bytes / (copies[0] * 1024.0)     # a copy reads and writes its size once
+        base = [(_short_name(r["Kernel_Name"]), r, v) for r, v in ordered]
+        mine = [(r, v) for nm, r, v in base if any(nm.startswith(p) for p in prefixes)]
         count = args.count or args.launches * args.steps
         if len(mine) < count:
             raise SystemExit(f"only {len(mine)} launches of {args.kernel} in {d}")
         use = mine[-count:]
-        kib = [v for _, v in use]
-        res[name] = dict(factor=factor, bytes_per_launch=sum(kib) * 1024.0 * factor / len(kib),
-                         copy_kib=copies[0], launches=len(kib),
-                         kernels=sorted({r["Kernel_Name"].split("(")[0] for r, _ in use}))
-    total = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
+        kib = sum(v for _, v in use)
+        res[name] = dict(factor=factor, bytes_per_launch=kib * 1024.0 * factor / count,
+                         copy_kib=copies[0], launches=count,
+                         kernels=sorted({_short_name(r["Kernel_Name"], True) for r, _ in use}))
+    per_launch = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
     try:
         with open(TRAFFIC_JSON) as fh:
             allrec = json.load(fh)
     except (OSError, ValueError):
         allrec = {}
     allrec[args.record_traffic] = {
-        "kernel": args.kernel, "launches_per_step": args.launches,
-        "bytes_per_launch": round(total), "read_bytes_per_launch": round(res["FETCH_SIZE"]["bytes_per_launch"]),
+        "kernels": args.kernel, "launches_per_step": args.launches,
+        "bytes_per_launch": round(per_launch), "bytes_per_step": round(per_launch * args.launches),
+        "read_bytes_per_launch": round(res["FETCH_SIZE"]["bytes_per_launch"]),
         "write_bytes_per_launch": round(res["WRITE_SIZE"]["bytes_per_launch"]),
         "fetch_factor": round(res["FETCH_SIZE"]["factor"], 4), "write_factor": round(res["WRITE_SIZE"]["factor"], 4),
         "summary": args.summary, "sources_sha256": _sources_sha()}
@@ -184,9 +247,10 @@ def record_traffic(args):
                      f"{f['copy_kib']:.1f} KiB\nby FETCH_SIZE and writes {w['copy_kib']:.1f} KiB by WRITE_SIZE, so "
                      f"bytes = FETCH_SIZE*1024*{f['factor']:.4f} and WRITE_SIZE*1024*{w['factor']:.4f}.\n\n")
             fh.write(f"Counted: the last {f['launches']} launches of {', '.join(f['kernels'])} "
-                     f"({args.launches} per step, the timed steps).\n")
+                     f"({args.launches} per step: the timed steps).\n")
             fh.write(f"Per launch (average): read {f['bytes_per_launch'] / 1e6:.3f} MB, "
-                     f"written {w['bytes_per_launch'] / 1e6:.3f} MB, total {total / 1e6:.3f} MB.\n")
+                     f"written {w['bytes_per_launch'] / 1e6:.3f} MB, total {per_launch / 1e6:.3f} MB; "
+                     f"per step {per_launch * args.launches / 1e6:.3f} MB.\n")
     print(json.dumps(allrec[args.record_traffic]))
 
 
@@ -325,7 +389,9 @@ def bench_decode_step(torch, np, sbl, dev, tm, args):
                                       [dict(pool[c][i], y=ys[i]) for i in grp], fmt, n, m)
 
     step_ms = timed_steps(torch, tm, step, copies, args.steps, warm=args.warmup)
-    launches = len(GROUPS)
+    # kernel launches per step: one fused GEMV per input, plus a standalone
+    # quantizer for inputs above 16384 values (the call's documented rule)
+    launches = len(GROUPS) + sum(1 for g in GROUPS if m_tok * mats[g[0]][2] > 16384)
     alg = wbytes + sum(m_tok * mats[g[0]][2] * 5 + 4 * m_tok for g in GROUPS) + \
         sum(4 * m_tok * no for _, no, _k in mats)
     gbps = wbytes / (step_ms * 1e-3) / 1e9
@@ -333,8 +399,10 @@ def bench_decode_step(torch, np, sbl, dev, tm, args):
     key = f"gemv_decode_{args.block}_{args.fmt}_m{m_tok}"
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": recorded_traffic(key),
-            "kernel": "gemv_kernel with the activation quantization fused in (sbl_linear_acts_batch)",
+            "kernel": "gemv_kernel with the activation quantization fused in (sbl_linear_acts_batch; "
+                      "quant_acts_kernel first for inputs above 16384 values)",
             "call": "sbl_linear_acts_batch", "launches_per_step": launches,
+            "traffic_per_step": recorded_traffic(key, "bytes_per_step"),
             "alg_bytes_per_launch": round(alg / launches), "avg_launch_us": round(step_ms * 1e3 / launches, 3),
             "note": "algorithmic bytes (packed weights + metadata, fp32 input read, int8 input and gamma "
                     "written, fp32 outputs) per launch / average launch time (HIP events around the timed "
@@ -509,14 +577,14 @@ def bench_train13b(torch, np, sbl, dev, tm, masters13):
 
 # --------------------------------------------------------------------------- weight preparation sweep
 
-def weight_prep_sweep(torch, np, sbl, dev, tm):
+def weight_prep_sweep(torch, np, sbl, dev, tm, blocks):
     """sbl_quant_weights_batch over whole blocks (7 matrices, 6:8 N:M output), the
     per-step weight preparation: algorithmic bytes (masters read once + packed codes and
     metadata written) per second.  N(0, 0.02) BF16 masters drawn on the device; each
     block rotates over >= 2 distinct copies totalling >= 600 MB; HIP graphs."""
     n, m, fmt = 6, 8, 1
     out = []
-    for blk in ("0p7b", "3b", "13b"):
+    for blk in blocks.split(","):
         mats = mats_of(blk)
         bw = sum(no * k for _, no, k in mats)
         copies = rot_copies(2 * bw, 600e6)
@@ -532,8 +600,10 @@ def weight_prep_sweep(torch, np, sbl, dev, tm):
                          max(20, 2 * copies)) * 1e3
         alg = sum(2 * no * k + packed_bytes(sbl, no, k, n, m, fmt) for _, no, k in mats)
         gbps = alg / (us * 1e-6) / 1e9
+        counted = recorded_traffic(f"weight_prep_{blk}_nm68", "bytes_per_step")
         out.append({"block": blk, "weights": bw, "us_per_call": round(us, 2), "alg_GBps": round(gbps, 1),
-                    "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                    "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic_bytes_per_call": counted,
+                    "counted_GBps": round(counted / (us * 1e-6) / 1e9, 1) if counted else None,
                     "path": "one launch (resident_kernel)" if bw * 2 <= 67e6 else "two launches (absmean + mask_pack)"})
         del pool
         torch.cuda.empty_cache()
@@ -822,6 +892,9 @@ def cpu_baseline(np, args, budget_s):
 
 def main():
     args = parse()
+    if args.trace_summary:
+        trace_summary(args)
+        return
     if args.record_traffic:
         record_traffic(args)
         return
@@ -864,7 +937,7 @@ def main():
         line["train_step_13b"] = bench_train13b(torch, np, sbl, dev, tm, masters["13b"])
     masters.pop("13b", None)
     if "weight_prep" in sections:
-        line["weight_prep"] = weight_prep_sweep(torch, np, sbl, dev, tm)
+        line["weight_prep"] = weight_prep_sweep(torch, np, sbl, dev, tm, args.prep_blocks)
     if "step0p7b" in sections:
         line["step_0p7b"] = bench_step0p7b(torch, np, sbl, dev, tm)
     if "gemv" in sections:

@@ -304,10 +304,9 @@ int sbl_linear_batch(const sbl_linear_item* items, int32_t count, int32_t fmt, i
  *              as sbl_quant_acts writes them.
  *   items      1..256 products; each must have this m_tok and k; their xq
  *              and gamma fields are ignored (the call uses its own).
- * For decode-sized inputs (m_tok <= 16, at most 8 items, activations small
- * enough to stage per workgroup) a single launch quantizes inside the
- * product's workgroups; otherwise the call runs sbl_quant_acts and then
- * sbl_linear_batch.  Validation as those two calls; results (xq, gamma, y,
+ * For decode-sized inputs (m_tok <= 16, at most 8 items, m_tok * k <= 16384
+ * values) a single launch quantizes inside the product's workgroups; otherwise
+ * the call runs sbl_quant_acts and then sbl_linear_batch.  Validation as those two calls; results (xq, gamma, y,
  * acc) are bit-identical to them. */
 int sbl_linear_acts_batch(const float* x, int64_t m_tok, int64_t k, int8_t* xq, float* gamma,
                           const sbl_linear_item* items, int32_t count, int32_t fmt, int32_t n, int32_t m,

@@ -379,7 +379,9 @@ void launch_fast(const QBatch& b, hipStream_t s) {
 //    workgroups); the slot's owner stores the sum and record, waits until
 //    those stores are complete (s_waitcnt vmcnt(0)), then stores the tag, so
 //    a waiter that has seen the tag reads the sum and record it tags;
-//  * the wait is bounded: after max_polls polls a workgroup computes the
+//  * the wait is bounded in time: after max_ticks ticks of the chip's
+//    constant real-time counter (s_memrealtime; 100 ticks per microsecond on
+//    MI355X, the rate the host reads from the device) a workgroup computes the
 //    missing partial sums itself from the masters, stores and tags them.  The
 //    sums are exact, so every writer of a slot writes the same bits, and a
 //    result never depends on who computed it.  (The host launches this
@@ -397,9 +399,12 @@ constexpr int kResChunks = kThreads * kResR;      // chunks per workgroup
 static_assert(kResChunks == kResChunksPerWg, "resident partition");
 constexpr int kResMaxSlots = beta::kWaveSlots;    // slots per matrix (the per-wave finalize)
 
+// The mix is the published SplitMix64 output function (golden-ratio
+// increment, then two xor-shift-multiply rounds with its constants): odd
+// multipliers and xor-shifts, so bijective in e for a fixed slot.
 __device__ __forceinline__ uint64_t res_tag(uint64_t e, const QDesc& d, int64_t slot) {
   uint64_t x = e + ((uint64_t)(uintptr_t)d.w ^ ((uint64_t)slot * 0x9E3779B97F4A7C15ull));
-  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;     // odd multipliers and xor-shifts: bijective
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
   x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
   return x ^ (x >> 31);
 }
@@ -444,7 +449,7 @@ __device__ __forceinline__ void res_compute_slot(const QDesc& d, int64_t j, uint
 
 template <int M, int DROP, int FMT, bool CODES>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void resident_kernel(
-    const QBatch batch, uint32_t max_polls) {
+    const QBatch batch, uint32_t max_ticks) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads * 128];
   __shared__ __attribute__((aligned(8))) uint8_t kstage[kResR][kThreads * 8];   // keep bits, per chunk row
   __shared__ unsigned long long bins[256];
@@ -498,7 +503,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // many are missing: every workgroup of a matrix polls the same few lines,
   // and early finishers would otherwise load them while the masters stream.
   if (tid < 64) {
-    uint32_t polls = 0, lane_miss = 0;
+    uint32_t lane_miss = 0;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
 #pragma unroll
     for (int u = 0; u < kResMaxSlots / 64; ++u)
       if (lane + 64 * u < d.nb) lane_miss |= 1u << u;
@@ -511,8 +517,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       for (int u = 0; u < kResMaxSlots / 64; ++u)
         if (((lane_miss >> u) & 1u) && t[u] == res_tag(e, d, lane + 64 * u)) lane_miss &= ~(1u << u);
       const unsigned long long waiting = __ballot(lane_miss != 0);
-      if (waiting == 0 || polls >= max_polls) break;   // uniform in the wave
-      ++polls;
+      if (waiting == 0 || __builtin_amdgcn_s_memrealtime() - t0 >= max_ticks) break;   // uniform in the wave
       if (__popcll(waiting) > 8) __builtin_amdgcn_s_sleep(32);   // ~2000 cycles
       else __builtin_amdgcn_s_sleep(2);
     }
@@ -603,7 +608,7 @@ bool res_partition(QBatch& b, int64_t cap) {
 }
 
 template <int M, int DROP, int FMT, bool CODES>
-bool launch_resident_kernel(QBatch& b, uint32_t max_polls, hipStream_t s, hipError_t* err) {
+bool launch_resident_kernel(QBatch& b, uint32_t max_ticks, hipStream_t s, hipError_t* err) {
   static int capacity[64];                           // co-resident workgroups per device (0: unknown)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
@@ -618,23 +623,23 @@ bool launch_resident_kernel(QBatch& b, uint32_t max_polls, hipStream_t s, hipErr
   QBatch r = b;
   if (!res_partition(r, capacity[dev])) return false;
   hipLaunchKernelGGL((resident_kernel<M, DROP, FMT, CODES>), dim3((unsigned)r.start[r.count]), dim3(kThreads), 0,
-                     s, r, max_polls);
+                     s, r, max_ticks);
   *err = hipGetLastError();
   b = r;
   return true;
 }
 
 template <int M, int DROP>
-bool launch_resident_m(QBatch& b, uint32_t max_polls, hipStream_t s, hipError_t* err) {
+bool launch_resident_m(QBatch& b, uint32_t max_ticks, hipStream_t s, hipError_t* err) {
   bool codes = false, nm = false;
   for (int i = 0; i < b.count; ++i) {
     codes = codes || b.d[i].codes != nullptr;
     nm = nm || (b.d[i].packed != nullptr && b.d[i].fmt == 1);
   }
-  if (nm && codes) return launch_resident_kernel<M, DROP, 1, true>(b, max_polls, s, err);
-  if (nm) return launch_resident_kernel<M, DROP, 1, false>(b, max_polls, s, err);
-  if (codes) return launch_resident_kernel<M, DROP, 0, true>(b, max_polls, s, err);
-  return launch_resident_kernel<M, DROP, 0, false>(b, max_polls, s, err);
+  if (nm && codes) return launch_resident_kernel<M, DROP, 1, true>(b, max_ticks, s, err);
+  if (nm) return launch_resident_kernel<M, DROP, 1, false>(b, max_ticks, s, err);
+  if (codes) return launch_resident_kernel<M, DROP, 0, true>(b, max_ticks, s, err);
+  return launch_resident_kernel<M, DROP, 0, false>(b, max_ticks, s, err);
 }
 
 // Any n (one thread per chunk, one sort key per weight).
@@ -773,14 +778,14 @@ hipError_t launch_mask_pack(QBatch& b, int n, int m, hipStream_t s, bool dry, in
   return hipGetLastError();
 }
 
-bool launch_resident(QBatch& b, int n, int m, uint32_t max_polls, hipStream_t s, hipError_t* err) {
+bool launch_resident(QBatch& b, int n, int m, uint32_t max_ticks, hipStream_t s, hipError_t* err) {
   const int drop = m - n;
-  if (m == 8 && drop == 0) return launch_resident_m<8, 0>(b, max_polls, s, err);
-  if (m == 8 && drop == 1) return launch_resident_m<8, 1>(b, max_polls, s, err);
-  if (m == 8 && drop == 2) return launch_resident_m<8, 2>(b, max_polls, s, err);
-  if (m == 4 && drop == 0) return launch_resident_m<4, 0>(b, max_polls, s, err);
-  if (m == 4 && drop == 1) return launch_resident_m<4, 1>(b, max_polls, s, err);
-  if (m == 4 && drop == 2) return launch_resident_m<4, 2>(b, max_polls, s, err);
+  if (m == 8 && drop == 0) return launch_resident_m<8, 0>(b, max_ticks, s, err);
+  if (m == 8 && drop == 1) return launch_resident_m<8, 1>(b, max_ticks, s, err);
+  if (m == 8 && drop == 2) return launch_resident_m<8, 2>(b, max_ticks, s, err);
+  if (m == 4 && drop == 0) return launch_resident_m<4, 0>(b, max_ticks, s, err);
+  if (m == 4 && drop == 1) return launch_resident_m<4, 1>(b, max_ticks, s, err);
+  if (m == 4 && drop == 2) return launch_resident_m<4, 2>(b, max_ticks, s, err);
   return false;
 }
 

@@ -144,16 +144,35 @@ sbl::QDesc to_qdesc(const sbl_quant_item& it, int32_t fmt) {
 // just the finalize kernel.
 constexpr int64_t kPrologueMaxWorkgroups = 1024;
 constexpr int64_t kPrologueMaxSlots = 512;       // every wave loads all partial sums (beta::kWaveSlots)
-// polls of the one-launch kernel's wait for other workgroups' partial sums
-// before it computes them itself (each poll is a memory round trip, ~1 µs)
-constexpr uint32_t kResidentPolls = 1u << 16;
+// Bound of the one-launch kernel's wait for other workgroups' partial sums
+// before it computes the missing ones itself, in microseconds of the chip's
+// constant real-time counter.  On an idle chip every sum arrives within ~15 us
+// of the launch; the bound only acts when other work delays workgroups.
+constexpr uint32_t kResidentWaitUs = 100;
+
+// real-time counter ticks per microsecond of the current device (queried once
+// per device; 100 on MI355X)
+uint32_t ticks_per_us() {
+  static std::mutex mu;
+  static int rate_khz[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 100;
+  std::lock_guard<std::mutex> lock(mu);
+  if (rate_khz[dev] <= 0) {
+    int r = 0;
+    if (hipDeviceGetAttribute(&r, hipDeviceAttributeWallClockRate, dev) != hipSuccess || r <= 0) r = 100000;
+    rate_khz[dev] = r;
+  }
+  const uint32_t t = (uint32_t)(rate_khz[dev] / 1000);
+  return t > 0 ? t : 1;
+}
 
 
 int launch_quant(const sbl_quant_item* items, int32_t count, int32_t n, int32_t m, int32_t fmt, int32_t flags,
                  hipStream_t s) {
   const bool kept = (flags & SBL_QW_BETA_KEPT) != 0, mfc = (flags & SBL_QW_MASK_FROM_CODES) != 0;
   const bool one_launch = (flags & (SBL_QW_BETA_KEPT | SBL_QW_MASK_FROM_CODES | SBL_QW_TWO_PASS)) == 0;
-  const uint32_t polls = (flags & SBL_QW_NO_WAIT) ? 0u : kResidentPolls;
+  const uint32_t wait_ticks = (flags & SBL_QW_NO_WAIT) ? 0u : kResidentWaitUs * ticks_per_us();
   for (int i0 = 0; i0 < count; i0 += sbl::kMaxQDesc) {
     sbl::QBatch b;
     b.count = count - i0 < sbl::kMaxQDesc ? count - i0 : sbl::kMaxQDesc;
@@ -166,7 +185,7 @@ int launch_quant(const sbl_quant_item* items, int32_t count, int32_t n, int32_t 
     }
     if (one_launch && outputs) {
       hipError_t err = hipSuccess;
-      if (sbl::launch_resident(b, n, m, polls, s, &err)) {
+      if (sbl::launch_resident(b, n, m, wait_ticks, s, &err)) {
         const int st = launch_status(err);
         if (st != SBL_OK) return st;
         continue;

@@ -126,11 +126,11 @@ hipError_t launch_absmean_final(QBatch& batch, hipStream_t s);
 // One launch for the whole weight preparation of a batch that fits on the
 // chip at once (returns false, launching nothing, when it does not or the
 // pattern drops more than two of a group): every thread keeps its masters in
-// registers while the partial sums of its matrix are completed.  max_polls
+// registers while the partial sums of its matrix are completed.  max_ticks
 // bounds the wait for other workgroups' partial sums; the missing ones are
 // then computed directly (0: at once).  Fills batch.start and sets d.nb to
 // the one-launch partition.
-bool launch_resident(QBatch& batch, int n, int m, uint32_t max_polls, hipStream_t s, hipError_t* err);
+bool launch_resident(QBatch& batch, int n, int m, uint32_t max_ticks, hipStream_t s, hipError_t* err);
 // mask_from_codes: the mask keeps the n largest |code| per group (ties to the
 // lower index) instead of the n largest master magnitudes.
 hipError_t launch_mask_pack(QBatch& batch, int n, int m, hipStream_t s, bool dry = false, int64_t* grid = nullptr,
