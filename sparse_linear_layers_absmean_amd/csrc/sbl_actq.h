@@ -32,19 +32,41 @@ __device__ __forceinline__ Step make_step(float gamma) {
   return Step{s, 1.0f / s};
 }
 
-// q of one value, as a byte (two's complement)
-__device__ __forceinline__ uint32_t q_byte(float v, const Step& st) {
-  const float y = v * st.r;
-  float n = rintf(y);
-  const float f = y - floorf(y);                   // exact: |y| <= 128
-  if (fabsf(f - 0.5f) <= 0x1p-15f) n = rintf(v / st.s);
+__device__ __forceinline__ uint32_t clamp_byte(float n) {
   n = fminf(fmaxf(n, -127.0f), 127.0f);
   return (uint32_t)((int32_t)n) & 0xFFu;
 }
 
-// four values -> four bytes, little-endian
+// Rounded quotient of one value: rint(x * r), and whether it lies within
+// 2^-15 of a half-integer (then only the IEEE quotient decides).
+__device__ __forceinline__ float q_fast(float v, const Step& st, bool& near) {
+  const float y = v * st.r;
+  const float f = y - floorf(y);                   // exact: |y| <= 128
+  near = near || fabsf(f - 0.5f) <= 0x1p-15f;
+  return rintf(y);
+}
+
+// q of one value, as a byte (two's complement)
+__device__ __forceinline__ uint32_t q_byte(float v, const Step& st) {
+  bool near = false;
+  float n = q_fast(v, st, near);
+  if (near) n = rintf(v / st.s);
+  return clamp_byte(n);
+}
+
+// four values -> four bytes, little-endian.  The exact quotients are formed
+// only when some lane of the wave has a value near a rounding boundary (one
+// uniform branch per four values).
 __device__ __forceinline__ uint32_t q_word(float4 v, const Step& st) {
-  return q_byte(v.x, st) | (q_byte(v.y, st) << 8) | (q_byte(v.z, st) << 16) | (q_byte(v.w, st) << 24);
+  bool nx = false, ny = false, nz = false, nw = false;
+  float a = q_fast(v.x, st, nx), b = q_fast(v.y, st, ny), c = q_fast(v.z, st, nz), d = q_fast(v.w, st, nw);
+  if (__any(nx || ny || nz || nw)) {
+    a = nx ? rintf(v.x / st.s) : a;
+    b = ny ? rintf(v.y / st.s) : b;
+    c = nz ? rintf(v.z / st.s) : c;
+    d = nw ? rintf(v.w / st.s) : d;
+  }
+  return clamp_byte(a) | (clamp_byte(b) << 8) | (clamp_byte(c) << 16) | (clamp_byte(d) << 24);
 }
 
 __device__ __forceinline__ float absmax4(float4 v) {
