@@ -3,14 +3,19 @@
 
 Headline (`value`): decode of a 70B-class transformer block (hidden 8192,
 FFN 28672: q, k, v, o 8192x8192, gate, up 28672x8192, down 8192x28672), one
-token, 6:8 N:M packed ternary weights.  A step is the block's decode pass:
+token, 6:8 Sparse-BitLinear weights.  The codes (ternary, masked 6:8) are
+stored 2 bits per weight (DENSE2): on MI355X, whose matrix cores have no 6:8
+mode, that is both the smaller storage (the N:M codes + bitmap take 2.5 bits
+per weight) and the cheaper decode; the same step with the N:M storage is
+measured beside it (`headline_nm68`).  A step is the block's decode pass:
 for each of its 4 inputs (q/k/v share one, o, gate/up share one, down)
 `sbl_linear_acts_batch` quantizes the token (per-token absmax int8) and runs
 the ternary x int8 products with the fp32 rescale, one fused GEMV launch per
 input.  The weights were prepared before the timed region by
 `sbl_quant_weights_batch` (exact absmean beta, 6:8 mask from the BF16
 masters, ternary codes, packing), as a decoder prepares them once at load.
-`value` is the packed weight bytes (codes + metadata) streamed per second.
+`value` is the packed weight bytes (codes, and metadata for N:M) streamed per
+second.
 Steps rotate over distinct copies of the packed weights (>= 560 MB), so the
 256 MB Infinity Cache cannot serve a step from the previous one; one HIP graph
 holds a pass over all copies (as a model's decode graph holds all its
@@ -68,7 +73,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--block", default="70b", choices=sorted(BLOCKS), help="headline decode block")
-    p.add_argument("--fmt", default="nm68", choices=sorted(FORMATS))
+    p.add_argument("--fmt", default="dense2", choices=sorted(FORMATS),
+                   help="headline format (the other N:M one is measured beside it)")
     p.add_argument("--m-tok", type=int, default=1)
     p.add_argument("--sections", default=",".join(SECTIONS),
                    help="comma list of parts to run (default: all): " + ",".join(SECTIONS))
@@ -951,10 +957,20 @@ def main():
         line["measured_library"] = references(torch, dev, tm)
     head = None
     if "headline" in sections:
-        # last, so that the timed steps end a profiled run
+        # the same step with the weights in the other storage format, then
+        # the headline itself last, so that its timed steps end a profiled run
+        alt = "nm68" if args.fmt == "dense2" else "dense2"
+        other = bench_decode_step(torch, np, sbl, dev, tm, argparse.Namespace(**{**vars(args), "fmt": alt}))
+        line["headline_" + alt] = {"format": alt, "value": round(other["gbps"], 1), "unit": "GB/s",
+                                    "ms_per_step": round(other["step_ms"], 5),
+                                    "frac_of_hbm_peak": round(other["gbps"] / HBM_PEAK_GBPS, 4),
+                                    "packed_weight_bytes_per_step": other["wbytes"], "roofline": other["roofline"]}
         head = bench_decode_step(torch, np, sbl, dev, tm, args)
     cpu = cpu_baseline(np, args, args.cpu_seconds) if "cpu" in sections else None
-    desc = f"Decode GEMV, M={args.m_tok} token(s), {BLOCKS[args.block][3]}, {args.fmt} packed ternary weights"
+    fmt_desc = {"dense2": "6:8-masked ternary codes packed 2 bits per weight (DENSE2)",
+                "nm68": "6:8 N:M: kept ternary codes 2 bits each + 8-bit bitmap per 8 weights",
+                "nm24": "2:4 N:M: kept ternary codes 2 bits each + 4-bit bitmap per 4 weights"}[args.fmt]
+    desc = f"Decode GEMV, M={args.m_tok} token(s), {BLOCKS[args.block][3]}, {fmt_desc}"
     out = {
         "metric": METRIC,
         "value": round(head["gbps"], 1) if head else None,
