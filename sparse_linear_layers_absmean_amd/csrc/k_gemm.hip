@@ -4,9 +4,9 @@
 // is a dense contraction, so it runs on gfx950 int8 MFMA
 // (v_mfma_i32_32x32x32_i8, 32 rows x 32 tokens x 32 k per instruction).
 //
-// Tiling: a workgroup of 4 waves owns 32*KRT*4 weight rows x 32*KCT tokens;
-// wave w owns KRT row tiles (32 rows each) x all KCT token tiles, so every
-// weight operand is decoded exactly once per workgroup.  The k loop advances
+// Tiling: a workgroup of 4*WT waves owns 32*KRT*4 weight rows x 32*KCT*WT
+// tokens; wave w owns KRT row tiles (32 rows each) x KCT token tiles, so every
+// weight operand is decoded WT times per workgroup (once for N:M).  The k loop advances
 // 128 k per step (four 32-k MFMA sub-steps); the MFMA's k order is free as
 // long as A and B agree, so lane half g of a row takes the row's 64-weight
 // block 2*step + g whole, with one load per row tile per step, and uses only
@@ -147,17 +147,21 @@ __device__ __forceinline__ v4i decode_w(const WRaw<KIND>& a, int j, const NmLut&
   }
 }
 
-// KRT 32-row tiles and KCT 32-token tiles per wave; 4 waves along the rows.
-// The 256 x 256 tile (16 accumulator tiles per wave) needs every register of
-// a SIMD; the smaller ones are held to half of them, so that two waves share
-// each SIMD and one's latencies hide behind the other's matrix work
-// (256 x 128 tiles, 6144 int8 inputs: +10% at 2048 tokens).
-template <int KIND, int KRT, int KCT>
-__global__ __launch_bounds__(kThreads, KRT * KCT >= 16 ? 1 : 2) void gemm_kernel(const LinBatch batch) {
+// KRT 32-row tiles and KCT 32-token tiles per wave; 4 waves along the rows
+// and WT along the tokens (wave w: rows of w % 4, token tiles of w / 4).
+// A wave with 16 accumulator tiles needs every register of a SIMD; the
+// others are held to half of them, so that two waves share each SIMD and one's
+// latencies hide behind the other's matrix work (256 x 128 tiles: +10% at
+// 2048 tokens; 256 x 256 DENSE2 as 8 waves of 64 x 128: +2% at 2048 and +6%
+// at 4096 tokens against 4 waves of 64 x 256).
+template <int KIND, int KRT, int KCT, int WT>
+__global__ __launch_bounds__(kThreads * WT, KRT * KCT * WT >= 16 ? 1 : 2) void gemm_kernel(const LinBatch batch) {
   constexpr int kRT = KRT, kCT = KCT;
+  constexpr int kThr = kThreads * WT;               // 4 waves along the rows x WT along the tokens
   constexpr int kBM = 4 * 32 * kRT;                 // weight rows per workgroup
-  constexpr int kBN = 32 * kCT;                     // tokens per workgroup (every wave sees all)
-  constexpr int kStPasses = kBN * kBK / (16 * kThreads);   // 16-byte staging loads per thread
+  constexpr int kBN = 32 * kCT * WT;                // tokens per workgroup
+  constexpr int kTokPass = kThr / 8;                // tokens staged per pass (8 threads per token row)
+  constexpr int kStPasses = kBN * kBK / (16 * kThr);   // 16-byte staging loads per thread
   __shared__ NmLut lut;
   __shared__ __attribute__((aligned(16))) uint8_t btile[2][kBN * kBK];
   if (KIND != kDense2) build_lut<KIND>(lut);
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(kThreads, KRT * KCT >= 16 ? 1 : 2) void gemm_kernel
   const int nks = (int)((K + kBK - 1) / kBK);      // steps; the last may be half (K % 128 == 64)
   const int nkb = (int)(K / 64);                    // 64-weight blocks per row
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = (tid >> 6) & 3, wt = tid >> 8, lane = tid & 63;
   const int li = lane & 31, g = lane >> 5;
   __shared__ int32_t qsum_lds[kBN];
 
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(kThreads, KRT * KCT >= 16 ? 1 : 2) void gemm_kernel
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(d.xq, (int64_t)d.m_tok * K);
   int voff_b[kStPasses];
 #pragma unroll
-  for (int p = 0; p < kStPasses; ++p) voff_b[p] = (int)((t0 + st_tok + 32 * p) * K + 16 * st_chunk);
+  for (int p = 0; p < kStPasses; ++p) voff_b[p] = (int)((t0 + st_tok + kTokPass * p) * K + 16 * st_chunk);
   auto load_b = [&](int ks, u32x4* r) {
     const bool ok = kBK * ks + 16 * st_chunk < K;   // false: second half of a last half step
 #pragma unroll
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(kThreads, KRT * KCT >= 16 ? 1 : 2) void gemm_kernel
   auto store_b = [&](int buf, const u32x4* r, bool real) {
 #pragma unroll
     for (int p = 0; p < kStPasses; ++p) {
-      *reinterpret_cast<u32x4*>(&btile[buf][bt_off(st_tok + 32 * p, st_chunk)]) = r[p];
+      *reinterpret_cast<u32x4*>(&btile[buf][bt_off(st_tok + kTokPass * p, st_chunk)]) = r[p];
       if (KIND == kDense2) {                        // branchless: a branch here costs the
         int q = 0;                                  // loop its exact load wait counts
 #pragma unroll
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(kThreads, KRT * KCT >= 16 ? 1 : 2) void gemm_kernel
     for (int j = 0; j < 4; ++j) {                   // 32-k MFMA sub-steps: lane half g takes
       v4i b[kCT];                                   // k = 128 ks + 64 g + 16 j .. +15
 #pragma unroll
-      for (int ct = 0; ct < kCT; ++ct) b[ct] = lds_ld16(bt + bt_off(32 * ct + li, 4 * g + j));
+      for (int ct = 0; ct < kCT; ++ct) b[ct] = lds_ld16(bt + bt_off(32 * (wt * kCT + ct) + li, 4 * g + j));
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
         const v4i a = decode_w<KIND>(wr[slot][rt], j, lut);
@@ -309,19 +313,19 @@ __global__ __launch_bounds__(kThreads, KRT * KCT >= 16 ? 1 : 2) void gemm_kernel
       v += __shfl_xor(v, 1, 64);
       v += __shfl_xor(v, 2, 64);
       v += __shfl_xor(v, 4, 64);
-      if (st_chunk == 0) qsum_lds[st_tok + 32 * p] = v;
+      if (st_chunk == 0) qsum_lds[st_tok + kTokPass * p] = v;
     }
     __syncthreads();
   }
   // epilogue: lane (li, g) holds C[8*(v/4) + 4g + v%4][li] of each 32x32 tile
 #pragma unroll
   for (int ct = 0; ct < kCT; ++ct) {
-    const int64_t t = t0 + 32 * ct + li;
+    const int64_t t = t0 + 32 * (wt * kCT + ct) + li;
     if (t >= d.m_tok) continue;
     const float s = out_scale(d.beta, d.gamma, t);
     float* yrow = d.y + t * d.n_out;
     int32_t* arow = d.acc ? d.acc + t * d.n_out : nullptr;
-    const int32_t corr = KIND == kDense2 ? qsum_lds[32 * ct + li] : 0;
+    const int32_t corr = KIND == kDense2 ? qsum_lds[32 * (wt * kCT + ct) + li] : 0;
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
 #pragma unroll
@@ -389,9 +393,9 @@ bool gemm_fits(const LinearArgs& a, int kind) {
 
 namespace {
 
-template <int KRT, int KCT>
+template <int KRT, int KCT, int WT = 1>
 hipError_t launch_shape(const LinearArgs* items, int count, int kind, hipStream_t s) {
-  constexpr int kBM = 4 * 32 * KRT, kBN = 32 * KCT;
+  constexpr int kBM = 4 * 32 * KRT, kBN = 32 * KCT * WT;
   LinBatch b = {};
   int blocks = 0;
   for (int i = 0; i < count; ++i) {
@@ -403,10 +407,9 @@ hipError_t launch_shape(const LinearArgs* items, int count, int kind, hipStream_
   b.start[count] = blocks;
   b.count = count;
   if (blocks == 0) return hipSuccess;
-  const dim3 grid((unsigned)blocks), block(kThreads);
-  if (kind == kDense2) hipLaunchKernelGGL((gemm_kernel<kDense2, KRT, KCT>), grid, block, 0, s, b);
-  else if (kind == kNm68) hipLaunchKernelGGL((gemm_kernel<kNm68, KRT, KCT>), grid, block, 0, s, b);
-  else hipLaunchKernelGGL((gemm_kernel<kNm24, KRT, KCT>), grid, block, 0, s, b);
+  const dim3 grid((unsigned)blocks), block(kThreads * WT);
+  if (kind == kDense2) hipLaunchKernelGGL((gemm_kernel<kDense2, KRT, KCT, WT>), grid, block, 0, s, b);
+  else hipLaunchKernelGGL((gemm_kernel<kNm68, KRT, KCT, WT>), grid, block, 0, s, b);
   return hipGetLastError();
 }
 
@@ -415,7 +418,11 @@ hipError_t launch_shape(const LinearArgs* items, int count, int kind, hipStream_
 hipError_t launch_gemm_group(const LinearArgs* items, int count, int kind, hipStream_t s) {
   if (kind == kNm24) return launch_gemm24_group(items, count, s);
   switch (pick_shape(items, count)) {
-    case 0: return launch_shape<2, 8>(items, count, kind, s);
+    // 256 x 256: DENSE2 as 8 waves (4 along the rows x 2 along the tokens,
+    // 64 x 128 each, two waves per SIMD; each row's cheap decode done by two
+    // waves), N:M as 4 waves of 64 x 256 (one per SIMD; its decode done once)
+    case 0: return kind == kDense2 ? launch_shape<2, 4, 2>(items, count, kind, s)
+                                   : launch_shape<2, 8, 1>(items, count, kind, s);
     case 1: return launch_shape<2, 4>(items, count, kind, s);
     case 2: return launch_shape<1, 8>(items, count, kind, s);
     default: return launch_shape<1, 4>(items, count, kind, s);
