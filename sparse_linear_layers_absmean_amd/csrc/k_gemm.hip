@@ -62,9 +62,13 @@ __device__ __forceinline__ v4i lds_ld16(const uint8_t* p) {
 }
 
 // byte offset of 16-byte chunk c (0..7) of token row r in an LDS activation
-// tile of 128-byte rows: XOR-swizzled by r so that 8 consecutive rows reading
-// the same chunk hit 8 distinct 16-byte bank groups.
-__device__ __forceinline__ int bt_off(int r, int c) { return r * kBK + 16 * (c ^ (r & 7)); }
+// tile of 128-byte rows.  gfx950's LDS serves a 16-byte read for 16 lanes per
+// cycle from 64 banks (256 bytes): rows r and r+1 lie in the two halves of a
+// bank row, and the chunk is XOR-swizzled by (r/2) % 8, so 16 consecutive
+// rows reading the same chunk hit 16 distinct 16-byte bank groups.  (A swizzle
+// by r % 8 leaves rows r and r+8 on the same banks: a 2-way conflict on every
+// read.)
+__device__ __forceinline__ int bt_off(int r, int c) { return r * kBK + 16 * (c ^ ((r >> 1) & 7)); }
 
 // Buffer resources: loads past the end of a buffer return zeros, so tokens
 // past m_tok need neither branches nor clamping.  Weights are stored

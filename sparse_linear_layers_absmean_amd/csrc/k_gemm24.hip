@@ -48,8 +48,9 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, ui
 }
 
 // byte offset of 16-byte chunk c (0..7) of token row r in an LDS activation
-// tile of 128-byte rows, XOR-swizzled by r
-__device__ __forceinline__ int bt_off(int r, int c) { return r * kBK + 16 * (c ^ (r & 7)); }
+// tile of 128-byte rows, XOR-swizzled by (r/2) % 8: 16 consecutive rows
+// reading one chunk hit 16 distinct 16-byte groups of gfx950's 64 banks
+__device__ __forceinline__ int bt_off(int r, int c) { return r * kBK + 16 * (c ^ ((r >> 1) & 7)); }
 
 __device__ __forceinline__ int32_t lds_ld4(const uint8_t* p, int i) {
   return reinterpret_cast<const int32_t*>(p)[i];
@@ -109,9 +110,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm24_kernel(const LinBatch batc
 
   // activations: instruction q (= wave + 4p) of a step fills LDS rows 8q ..
   // 8q+7 (1 KB); its lane l lands at row 8q + l/8, 16-byte slot l%8, and
-  // fetches chunk (l%8) ^ (l/8) of that token's 128 bytes (bt_off's swizzle)
+  // fetches chunk (l%8) ^ ((row/2) % 8) of that token's 128 bytes (bt_off's
+  // swizzle; (row/2) % 8 = 4 (q % 2) + l/16, and q % 2 = wave % 2)
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(d.xq, (int64_t)d.m_tok * K);
-  const int dchunk = (lane & 7) ^ (lane >> 3);
+  const int dchunk = (lane & 7) ^ (((wave & 1) << 2) | (lane >> 4));
   uint32_t voff_b[kDma];
 #pragma unroll
   for (int p = 0; p < kDma; ++p)
