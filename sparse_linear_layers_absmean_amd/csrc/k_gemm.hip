@@ -33,6 +33,8 @@
 // All integer work is exact; results are bit-identical to the GEMV path.
 #include "sbl_decode.h"
 
+#include <type_traits>
+
 namespace sbl {
 
 namespace {
@@ -184,7 +186,8 @@ __global__ __launch_bounds__(kThreads * WT, KRT * KCT * WT >= 16 ? 1 : 2) void g
 
   const int tid = threadIdx.x, wave = (tid >> 6) & 3, wt = tid >> 8, lane = tid & 63;
   const int li = lane & 31, g = lane >> 5;
-  __shared__ int32_t qsum_lds[kBN];
+  __shared__ __attribute__((aligned(16))) int32_t qsum_lds[kBN];
+  __shared__ __attribute__((aligned(16))) float scale_lds[kBN];
 
   // activation staging: thread -> token (tid >> 3) + 32p, 16-byte chunk tid & 7
   // (eight tokens' whole 128-byte rows per load instruction)
@@ -287,7 +290,7 @@ __global__ __launch_bounds__(kThreads * WT, KRT * KCT * WT >= 16 ? 1 : 2) void g
         const v4i a = decode_w<KIND>(wr[slot][rt], j, lut);
 #pragma unroll
         for (int ct = 0; ct < kCT; ++ct)
-          acc[rt][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[ct], acc[rt][ct], 0, 0, 0);
+          acc[rt][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[ct], a, acc[rt][ct], 0, 0, 0);
       }
     }
     // weights of step ks + kDepth reuse the slot just consumed
@@ -319,44 +322,56 @@ __global__ __launch_bounds__(kThreads * WT, KRT * KCT * WT >= 16 ? 1 : 2) void g
       v += __shfl_xor(v, 4, 64);
       if (st_chunk == 0) qsum_lds[st_tok + kTokPass * p] = v;
     }
-    __syncthreads();
   }
-  // epilogue: lane (li, g) holds C[8*(v/4) + 4g + v%4][li] of each 32x32 tile
+  // output scale per token of the tile
+  for (int i = tid; i < kBN; i += kThr) scale_lds[i] = t0 + i < d.m_tok ? out_scale(d.beta, d.gamma, t0 + i) : 0.0f;
+  __syncthreads();
+  // epilogue: the MFMAs take the activations as A and the weights as B, so
+  // lane (li, g) holds C[token 8*(v/4) + 4g + v%4][row li] of each 32 x 32
+  // tile.  For each v the 32 lanes of a half write 32 consecutive rows of one
+  // token's output: 128 contiguous bytes, whole cache lines.  (Rows as A put 4
+  // rows of 32 tokens in each lane: every 16-byte store touched 32 lines.)
+  // Buffer stores: the token offset is wave-uniform (scalar offset); rows past
+  // n_out get an offset past the buffer and tokens past m_tok land past it, so
+  // both are dropped without branches (the host keeps m_tok*n_out*4 + the last
+  // tile's overhang below 2^31 bytes).
+  const uint32_t tokb = (uint32_t)d.n_out * 4u;      // bytes per token row of y
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(d.y, d.m_tok * (int64_t)tokb);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(d.acc, d.acc ? d.m_tok * (int64_t)tokb : 0);
+  const int wts = __builtin_amdgcn_readfirstlane(wt);
+  uint32_t vo[kRT];
 #pragma unroll
-  for (int ct = 0; ct < kCT; ++ct) {
-    const int64_t t = t0 + 32 * (wt * kCT + ct) + li;
-    if (t >= d.m_tok) continue;
-    const float s = out_scale(d.beta, d.gamma, t);
-    float* yrow = d.y + t * d.n_out;
-    int32_t* arow = d.acc ? d.acc + t * d.n_out : nullptr;
-    const int32_t corr = KIND == kDense2 ? qsum_lds[32 * (wt * kCT + ct) + li] : 0;
+  for (int rt = 0; rt < kRT; ++rt) {
+    const int64_t row = n0 + 32 * kRT * wave + 32 * rt + li;
+    vo[rt] = row < d.n_out ? (uint32_t)row * 4u + (uint32_t)(4 * g) * tokb : kFar;
+  }
+  auto store_all = [&](auto with_acc) {
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) {
+    for (int ct = 0; ct < kCT; ++ct) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t row = n0 + 32 * kRT * wave + 32 * rt + 8 * q + 4 * g;
-        int32_t a4[4];
-        float y4[4];
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int tl4 = 32 * (wt * kCT + ct) + 8 * v4 + 4 * g;   // this lane's 4 tokens: tl4 .. tl4+3
+        const float4 sc4 = *reinterpret_cast<const float4*>(&scale_lds[tl4]);
+        int4 cq4 = make_int4(0, 0, 0, 0);
+        if (KIND == kDense2) cq4 = *reinterpret_cast<const int4*>(&qsum_lds[tl4]);
+        const float scj[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+        const int32_t cqj[4] = {cq4.x, cq4.y, cq4.z, cq4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          a4[j] = acc[rt][ct][4 * q + j] - corr;
-          y4[j] = (float)a4[j] * s;
-        }
-        if (row + 3 < d.n_out && ((t * d.n_out + row) & 3) == 0) {
-          *reinterpret_cast<float4*>(yrow + row) = make_float4(y4[0], y4[1], y4[2], y4[3]);
-          if (arow) *reinterpret_cast<int4*>(arow + row) = make_int4(a4[0], a4[1], a4[2], a4[3]);
-        } else {
+          const int v = 4 * v4 + j;
+          const uint32_t so = (uint32_t)(t0 + 32 * (wts * kCT + ct) + 8 * v4 + j) * tokb;   // wave-uniform
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (row + j < d.n_out) {
-              yrow[row + j] = y4[j];
-              if (arow) arow[row + j] = a4[j];
-            }
+          for (int rt = 0; rt < kRT; ++rt) {
+            const int32_t a = acc[rt][ct][v] - cqj[j];
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((float)a * scj[j]), ry, vo[rt], so, 0);
+            if constexpr (decltype(with_acc)::value) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)a, ra, vo[rt], so, 0);
           }
         }
       }
     }
-  }
+  };
+  if (d.acc) store_all(std::true_type{});
+  else store_all(std::false_type{});
 }
 
 // Tile shapes (weight rows x tokens), workgroups that fit on one CU at once,
@@ -392,7 +407,7 @@ bool gemm_fits(const LinearArgs& a, int kind) {
   const int64_t lim = (int64_t)1 << 31;
   const int64_t row_bytes = kind == kDense2 ? a.k / 4 : (kind == kNm68 ? 3 * a.k / 16 : a.k / 8);
   return (a.m_tok + 256) * a.k < lim && (a.n_out + 256) * row_bytes < lim &&
-         (a.n_out + 256) * (a.k / 8) < lim;
+         (a.n_out + 256) * (a.k / 8) < lim && (a.m_tok + 256) * a.n_out * 4 < lim;
 }
 
 namespace {
