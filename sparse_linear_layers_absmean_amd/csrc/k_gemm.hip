@@ -374,15 +374,20 @@ __global__ __launch_bounds__(kThreads * WT, KRT * KCT * WT >= 16 ? 1 : 2) void g
   else store_all(std::false_type{});
 }
 
-// Tile shapes (weight rows x tokens), workgroups that fit on one CU at once,
-// and the measured time of one such round relative to one 256 x 256 tile.
-// A launch costs whole rounds of 256 CUs: small tiles fill the chip when a
-// product has few large tiles (tile quantization), large tiles reuse operands.
-struct TileShape { int rows, toks, slots; double round_cost; };
-constexpr TileShape kShapes[] = {{256, 256, 1, 1.0}, {256, 128, 1, 0.63}, {128, 256, 1, 0.70},
-                                 {128, 128, 3, 0.90}};
+// Tile shapes (weight rows x tokens), workgroups that fit on one CU at once
+// (occupancy of the kernel: 256 x 256 takes a whole CU), and the measured
+// time of one full round of such workgroups per 128-k step, relative to a
+// round of 256 x 256 tiles, for DENSE2 and for N:M 6:8 (fitted, as the median
+// over the eight launches of the 3B-class block at 2048 tokens and the
+// 13B-class block at 4096).  A launch costs whole rounds: small tiles fill the
+// chip when a product has few large tiles (tile quantization), large tiles
+// reuse operands.
+struct TileShape { int rows, toks, slots; double cost[2]; };
+constexpr TileShape kShapes[] = {{256, 256, 1, {1.0, 1.0}}, {256, 128, 2, {0.775, 0.947}},
+                                 {128, 256, 2, {0.951, 0.829}}, {128, 128, 2, {0.526, 0.569}}};
 
-int pick_shape(const LinearArgs* items, int count) {
+int pick_shape(const LinearArgs* items, int count, int kind) {
+  const int ci = kind == kDense2 ? 0 : 1;
   int best = 0;
   double best_t = 1e300;
   for (int si = 0; si < 4; ++si) {
@@ -395,7 +400,7 @@ int pick_shape(const LinearArgs* items, int count) {
     }
     const int64_t per_round = 256 * (int64_t)sh.slots;
     const double rounds = (double)((tiles + per_round - 1) / per_round);
-    const double t = rounds * sh.round_cost * ((double)ksteps / (double)tiles);
+    const double t = rounds * sh.cost[ci] * ((double)ksteps / (double)tiles);
     if (t < best_t * 0.999) { best_t = t; best = si; }
   }
   return best;
@@ -436,7 +441,7 @@ hipError_t launch_shape(const LinearArgs* items, int count, int kind, hipStream_
 
 hipError_t launch_gemm_group(const LinearArgs* items, int count, int kind, hipStream_t s) {
   if (kind == kNm24) return launch_gemm24_group(items, count, s);
-  switch (pick_shape(items, count)) {
+  switch (pick_shape(items, count, kind)) {
     // 256 x 256: DENSE2 as 8 waves (4 along the rows x 2 along the tokens,
     // 64 x 128 each, two waves per SIMD; each row's cheap decode done by two
     // waves), N:M as 4 waves of 64 x 256 (one per SIMD; its decode done once)
