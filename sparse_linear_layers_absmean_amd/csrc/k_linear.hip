@@ -223,7 +223,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, ui
 // k-block kb = 4*sb + lane/16: super-block sb covers 256 weights of every row.
 // XLM: how the token rows reach LDS: 0 not at all (read from memory per
 // k-block), 1 through registers, issued first (m_tok*k <= kXLdsMax), 2 by
-// LDS-direct loads (m_tok*k <= kXBigMax; the region is rounded up to 1 KB).
+// LDS-direct loads (m_tok*k <= kXBigMax, k a multiple of 1024).
 template <int KIND, int XLM, int D, bool XF>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L) {
   constexpr bool XL = XLM != 0;
@@ -267,12 +267,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
     pl.nfull = nkb / 4;
   }
   // LDS: [token rows m_tok*k (XL)][64 zero bytes][reduction ks*tb*4*64 ints]
+  // LDS token rows are padded by 16 bytes (row t at t*(k+16)): the 16 lanes
+  // that read one k-block of 16 tokens then hit 16 distinct bank groups
+  // (with rows k bytes apart, k a multiple of 256, they all hit the same
+  // banks).  Byte o of the m_tok x k token rows sits at lds_x(o).
   const uint32_t xbytes = XL ? (uint32_t)(d.m_tok * d.k) : 0u;
-  const uint32_t zero_off = xbytes;
-  const uint32_t xreg = XLM == 2 ? (xbytes + 1023u) & ~1023u : xbytes;
-  int32_t* red = reinterpret_cast<int32_t*>(smem + xreg + 64);
+  const uint32_t xpitch = (uint32_t)d.k + 16u;
+  const uint32_t zero_off = XL ? (uint32_t)d.m_tok * xpitch : 0u;
+  auto lds_x = [&](uint32_t o) { return o + 16u * (o / (uint32_t)d.k); };
+  int32_t* red = reinterpret_cast<int32_t*>(smem + zero_off + 64);
   const bool r_ok = r < d.m_tok;
-  const uint32_t ox = r_ok ? (uint32_t)(r * d.k) : (XL ? zero_off : kFar);
+  const uint32_t ox = r_ok ? (XL ? (uint32_t)r * xpitch : (uint32_t)(r * d.k)) : (XL ? zero_off : kFar);
 
   // XL: the activation loads go out first, so that they return ahead of the
   // weight stages; each thread stages up to kXPer 16-byte pieces.
@@ -303,11 +308,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
     if (threadIdx.x < 16) qs[threadIdx.x] = 0;
   } else if constexpr (XLM == 2) {
     // piece i of thread t = bytes (t + i*blockDim)*16 .. +15; a wave's
-    // instruction fills one 1 KB block of LDS (zeros past xbytes), and only
-    // blocks inside the rounded region xreg are issued
+    // instruction fills 1 KB of one token row in LDS (k is a multiple of 1024
+    // in this mode)
     for (int i = 0; i < nxl; ++i) {
       const uint32_t blk = (uint32_t)(wave * 64 + i * (int)blockDim.x) * 16u;   // wave-uniform
-      if (blk < xreg) dma16(rs.x, smem + blk, (threadIdx.x + i * blockDim.x) * 16u);
+      if (blk < xbytes) dma16(rs.x, smem + lds_x(blk), (threadIdx.x + i * blockDim.x) * 16u);
     }
     if (threadIdx.x < 16) qs[threadIdx.x] = 0;
   }
@@ -347,7 +352,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
         u32x4 v;
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = actq::q_word(xf4[i][j], st);
-        *reinterpret_cast<u32x4*>(smem + o) = v;
+        *reinterpret_cast<u32x4*>(smem + lds_x(o)) = v;
         if (publish) *reinterpret_cast<u32x4*>(d.xq_out + o) = v;
         int q = 0;
 #pragma unroll
@@ -365,7 +370,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
     for (int i = 0; i < nxl; ++i) {
       const uint32_t o = (threadIdx.x + i * blockDim.x) * 16u;
       if (o < xbytes) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(smem + o);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(smem + lds_x(o));
         int q = 0;
 #pragma unroll
         for (int w = 0; w < 4; ++w) q = __builtin_amdgcn_sdot4((int)v[w], 0x01010101, q, false);
@@ -380,7 +385,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
     for (int i = 0; i < kXPer; ++i) {
       const uint32_t o = (threadIdx.x + i * blockDim.x) * 16u;
       if (i < nxl && o < xbytes) {
-        *reinterpret_cast<u32x4*>(smem + o) = xv[i];
+        *reinterpret_cast<u32x4*>(smem + lds_x(o)) = xv[i];
         int q = 0;
 #pragma unroll
         for (int w = 0; w < 4; ++w) q = __builtin_amdgcn_sdot4((int)xv[i][w], 0x01010101, q, false);
@@ -598,7 +603,9 @@ struct GemvShape {
 GemvShape gemv_shape(const LinDesc* items, int count) {
   int tiles = 0, max_nsb = 1;
   int64_t max_x = 0, weights = 0;
+  bool k1024 = true;
   for (int i = 0; i < count; ++i) {
+    k1024 = k1024 && items[i].k % 1024 == 0;
     tiles += (int)((items[i].n_out + 15) / 16);
     const int nsb = (items[i].k / 64 + 3) / 4;
     max_nsb = nsb > max_nsb ? nsb : max_nsb;
@@ -610,7 +617,7 @@ GemvShape gemv_shape(const LinDesc* items, int count) {
   // LDS-direct staging pays for its full-size workgroups and its staging pass
   // only on long weight streams (70B-class widths: +23-30% at 8-16 tokens;
   // 3B-class launches: 6-10% slower)
-  g.xlm = max_x <= kXLdsMax ? 1 : (max_x <= kXBigMax && weights >= kXBigMinWeights ? 2 : 0);
+  g.xlm = max_x <= kXLdsMax ? 1 : (max_x <= kXBigMax && weights >= kXBigMinWeights && k1024 ? 2 : 0);
   // the LDS-direct mode runs one 16-wave workgroup per CU; it keeps twice
   // the waves (measured: 5-9% faster than 2048 at 8 tokens, 70B widths)
   const int target = g.xlm == 2 ? 2 * kResidentWaves : kResidentWaves;
@@ -642,11 +649,11 @@ hipError_t launch_gemv_group(int kind, const LinDesc* items, int count, hipStrea
                              int8_t* xq_out = nullptr, float* gamma_out = nullptr) {
   GemvLaunch L = {};
   int tiles = 0;
-  int64_t max_x = 0;
+  int64_t max_xp = 0;                              // token rows in LDS, padded: m_tok * (k + 16)
   for (int i = 0; i < count; ++i) {
     tiles += (int)((items[i].n_out + 15) / 16);
-    const int64_t xb = (int64_t)items[i].m_tok * items[i].k;
-    max_x = xb > max_x ? xb : max_x;
+    const int64_t xp = (int64_t)items[i].m_tok * (items[i].k + 16);
+    max_xp = xp > max_xp ? xp : max_xp;
   }
   if (tiles == 0) return hipSuccess;
   const GemvShape g = gemv_shape(items, count);
@@ -664,7 +671,7 @@ hipError_t launch_gemv_group(int kind, const LinDesc* items, int count, hipStrea
   }
   L.b.start[count] = blocks;
   L.b.count = count;
-  const size_t xreg = g.xlm == 2 ? ((size_t)max_x + 1023) & ~(size_t)1023 : (g.xlm == 1 ? (size_t)max_x : 0);
+  const size_t xreg = g.xlm != 0 ? (size_t)max_xp : 0;
   const size_t lds = xreg + 64 + (g.ks > 1 ? (size_t)g.ks * g.tb * 4 * 64 * sizeof(int32_t) : 0);
   const dim3 grid((unsigned)blocks), block(64 * g.ks * g.tb);
   const bool xf_on = xf != nullptr;
