@@ -26,8 +26,9 @@ tokens, 6:8 / DENSE2 on the dense int8 MFMA, 2:4 on the sparse MFMA; 13B-class
 block, 4096 tokens), the 13B training-step path (per-step weight preparation
 + forward GEMMs), the weight-preparation sweep, the whole path on a 0.7B-class
 block, the GEMV table over every decode configuration, the backward, the group
-scales, library reference rates, and the CPU oracle on a bounded sample of
-the headline workload.
+scales, library reference rates, the chip's measured streaming-read and int8
+MFMA peaks (each roofline is also given as a fraction of the measured peak of
+its bound), and the CPU oracle on a bounded sample of the headline workload.
 
 Printed: one JSON line.  `--sections` selects parts (for profiler runs);
 `--record-traffic` turns two rocprofv3 counter runs into profiles/traffic.json.
@@ -63,7 +64,7 @@ BLOCKS = {
     "13b": ("b13", 5120, 13824, "13B-class block (hidden 5120, FFN 13824)"),
     "70b": ("b70", 8192, 28672, "70B-class block (hidden 8192, FFN 28672)"),
 }
-SECTIONS = ("headline", "gemv", "prefill", "train13b", "weight_prep", "step0p7b", "backward",
+SECTIONS = ("peaks", "headline", "gemv", "prefill", "train13b", "weight_prep", "step0p7b", "backward",
             "group_scales", "references", "cpu")
 
 
@@ -792,6 +793,69 @@ def bench_group_scales(torch, np, sbl, dev, tm, rpg=128, kg=320, n=6, m=8):
 
 # --------------------------------------------------------------------------- library references
 
+def measured_peaks(torch, dev, tm):
+    """What plain kernels reach on this GPU (libsbl_probe.so, outside the path), HIP
+    events around 10 runs each: a streaming read of 1 GB (nontemporal 16-byte loads,
+    8 in flight per thread; best of 2048-16384 workgroups of 256 threads) and
+    back-to-back independent int8 32x32x32 MFMAs (2048 workgroups of 4 waves)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_linear_layers_absmean_amd", "libsbl_probe.so"))
+    lib.sbl_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_void_p]
+    lib.sbl_probe_mfma_i8.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        tm.start()
+        for _ in range(10):
+            fn()
+        return tm.stop_ms() / 10
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed (HIP error {rc})")
+
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    best, best_grid = 0.0, 0
+    for grid in (2048, 4096, 8192, 16384):
+        ms = timed(lambda: check(lib.sbl_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, st)))
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        if gbps > best:
+            best, best_grid = gbps, grid
+    del buf
+    grid, iters = 2048, 2000
+    sink = torch.zeros(grid * 256, dtype=torch.int32, device=dev)
+    ms = timed(lambda: check(lib.sbl_probe_mfma_i8(sink.data_ptr(), grid, iters, st)))
+    tops = grid * 4 * 4 * iters * 65536 / (ms * 1e-3) / 1e12
+    del sink
+    torch.cuda.empty_cache()
+    return {"stream_read_GBps": round(best, 1), "stream_read_workgroups": best_grid,
+            "stream_read_frac_of_peak": round(best / HBM_PEAK_GBPS, 4),
+            "mfma_i8_TOPS": round(tops, 1), "mfma_i8_frac_of_peak": round(tops / INT8_PEAK_TOPS, 4)}
+
+
+def annotate_measured(line, peaks):
+    """Each roofline also as a fraction of the measured peak of its bound."""
+    def add(r):
+        if not r:
+            return
+        if r.get("bound") == "hbm" and r.get("unit") == "GB/s":
+            r["frac_of_measured"] = round(r["achieved"] / peaks["stream_read_GBps"], 4)
+        elif r.get("bound") == "mfma" and r.get("peak") == INT8_PEAK_TOPS:
+            r["frac_of_measured"] = round(r["achieved"] / peaks["mfma_i8_TOPS"], 4)
+    add(line.get("roofline"))
+    for k, v in line.items():
+        if k.startswith("headline_") and isinstance(v, dict):
+            add(v.get("roofline"))
+    for p in line.get("prefill") or []:
+        add(p.get("roofline"))
+
+
 def references(torch, dev, tm):
     """Measured library rates for reference (not part of the path), HIP events around 10
     runs each: torch's fp32 sum over 2 GB (bytes read), a 1 GB device copy (read +
@@ -932,6 +996,9 @@ def main():
     t0 = time.time()
     line = {}
     masters = {}
+    peaks = measured_peaks(torch, dev, tm) if "peaks" in sections else None
+    if peaks:
+        line["measured_peaks"] = peaks
     pre_blocks = {c.split(":")[0] for c in args.prefill_cases.split(",")} if "prefill" in sections else set()
     if "backward" in sections or "3b" in pre_blocks:
         masters["3b"] = synth_masters("3b", mats_of("3b"))
@@ -996,6 +1063,8 @@ def main():
         "frac_of_hbm_peak": round(head["gbps"] / HBM_PEAK_GBPS, 4) if head else None,
     }
     out.update(line)
+    if peaks:
+        annotate_measured(out, peaks)
     out["cpu_baseline"] = cpu
     out["bench_s"] = round(time.time() - t0, 1)
     out["device"] = torch.cuda.get_device_name(0)

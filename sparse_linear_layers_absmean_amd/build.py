@@ -1,4 +1,5 @@
-"""Build libsbl.so (all HIP sources + the C ABI) in-tree for gfx950 with hipcc."""
+"""Build libsbl.so (all HIP sources + the C ABI) in-tree for gfx950 with hipcc, and the
+benchmark's peak probes (libsbl_probe.so)."""
 
 from __future__ import annotations
 
@@ -12,6 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsbl.so")
+PROBE_LIB = os.path.join(PKG, "libsbl_probe.so")
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",
@@ -67,6 +69,10 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    # the benchmark's peak probes: a library of their own, outside the path
+    tmp = PROBE_LIB + ".tmp"
+    _run([hipcc(), *HIP_FLAGS, os.path.join(PKG, "probe", "peaks.hip"), "-o", tmp], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

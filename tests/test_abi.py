@@ -403,3 +403,13 @@ def test_quant_weights_batch_noalloc_validation(lib):
     assert call([item(n_out=1 << 17, k=1 << 17, mask_bits=None, packed=None, meta=None)] * (fits + 1)) == 6
     small = lib.sbl_workspace_bytes(1 << 15, 1 << 16)            # 2^31 weights
     assert limit // small >= 73
+
+
+def test_peak_probe_library_exports_its_two_calls():
+    # the benchmark's peak probes live in a library of their own (not the path's ABI)
+    probe = os.path.join(ROOT, "sparse_linear_layers_absmean_amd", "libsbl_probe.so")
+    if not os.path.exists(probe):
+        pytest.fail("libsbl_probe.so is not built (run __graft_entry__.build())")
+    out = subprocess.run(["nm", "-D", "--defined-only", probe], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (sbl_[a-z0-9_]+)", out))
+    assert exported == {"sbl_probe_stream_read", "sbl_probe_mfma_i8"}
