@@ -13,12 +13,15 @@
 // Both are contractions on the BF16 matrix cores (v_mfma_f32_32x32x16_bf16,
 // fp32 accumulation) with exact products: C is {-1, 0, 1}, and x_hat (24
 // significant bits) is split exactly into three BF16 parts, so dW takes
-// three MFMA per step.  One 128 x 128 output tile per workgroup of 4 waves
-// (each 64 x 64: 2 x 2 MFMA tiles), 64 of the contracted index per LDS stage.
+// three MFMA per step.  Output tiles of 128 x 128 per 4 waves (each wave
+// 64 x 64: 2 x 2 MFMA tiles), 64 of the contracted index per LDS stage; the
+// stage's global loads are issued one stage ahead into registers, and the LDS
+// hand-offs use barriers that leave them in flight.
 //   dX: i = token, j = feature, l = output channel; A = dY rows, B = C decoded
 //       from the packed weights (DENSE2 or N:M + bitmap, panel-major).
 //   dW: i = output channel, j = feature, l = token; A = dY^T, B = x_hat.
 #include "sbl_internal.h"
+
 
 namespace sbl {
 
@@ -33,6 +36,11 @@ constexpr int kStep = 64;         // contracted indices per LDS stage
 constexpr int kRow = kStep + 8;   // LDS row length in bf16 (144 bytes: 16-byte aligned, bank-spread)
 
 constexpr uint16_t kOne = 0x3F80u, kMinusOne = 0xBF80u;   // BF16 1.0, -1.0
+// token tiles per dX workgroup and channel tiles per dW workgroup (measured on
+// the 3B-class block at 2048 tokens: dX 2.11 / 1.78 / 2.93 ms for 1 / 2 / 4;
+// dW 2.77 / 3.11 ms for 1 / 2: the larger LDS footprint halves the resident
+// workgroups)
+constexpr int kDxTW = 2, kDwNW = 1;
 
 __device__ __forceinline__ bf16x8 lds_vec(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
@@ -58,8 +66,30 @@ __device__ __forceinline__ void mma_stage(const uint16_t* A_s, const uint16_t* B
   }
 }
 
-// 16 ternary codes of row `row`, weights 16 qq .. 16 qq + 15 of 64-weight block kb,
-// as u = c + 1 in 2-bit fields (field e = weight 16 qq + e)
+// dW's stage: the same A operands against the three parts of x_hat (A read
+// once per sub-step)
+__device__ __forceinline__ void mma_stage3(const uint16_t* A_s, const uint16_t (*B_s)[kTile * kRow],
+                                           f32x16 (&acc)[2][2], int wi, int wj, int li, int g) {
+#pragma unroll
+  for (int s = 0; s < kStep / 16; ++s) {
+    bf16x8 a[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) a[t] = lds_vec(A_s + (64 * wi + 32 * t + li) * kRow + 16 * s + 8 * g);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      bf16x8 b[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) b[t] = lds_vec(B_s[p] + (64 * wj + 32 * t + li) * kRow + 16 * s + 8 * g);
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj)
+          acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ti], b[tj], acc[ti][tj], 0, 0, 0);
+    }
+  }
+}
+
+// the packed weights of the product (either format, panel-major)
 struct PackedW {
   const uint8_t* packed;
   const uint8_t* meta;
@@ -67,14 +97,23 @@ struct PackedW {
   int32_t nkb, fmt, n, m;
 };
 
-__device__ __forceinline__ uint32_t quarter_fields(const PackedW& W, int64_t row, int kb, int qq) {
+// Raw words of one (row, quarter): loaded a stage ahead, decoded when the
+// stage is staged (quarter_load / quarter_fields), so that no load result is
+// consumed in the stage that issues it.
+struct QRaw {
+  uint32_t w;              // DENSE2: the quarter's word
+  uint32_t m0, m1;         // N:M: the block's bitmap
+  uint32_t h[3];           // N:M: three code halfwords from the quarter's first code on
+};
+
+// a quarter outside the matrix: u = 1 (code 0) everywhere, in both formats
+__device__ __forceinline__ QRaw quarter_zero() { return QRaw{0x55555555u, 0u, 0u, {0u, 0u, 0u}}; }
+
+__device__ __forceinline__ QRaw quarter_load(const PackedW& W, int64_t row, int kb, int qq) {
+  QRaw r = quarter_zero();
   if (W.fmt == 0) {
-    // DENSE2 block word qq holds weights 16 qq .. +15: weight 16 qq + e at bit 8 (e % 4) + 2 (e / 4)
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(W.packed + panel_offset(W.n_out, W.nkb, 16, row, kb) + 4 * qq);
-    uint32_t f = 0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) f |= ((w >> (8 * (e & 3) + 2 * (e >> 2))) & 3u) << (2 * e);
-    return f;
+    r.w = *reinterpret_cast<const uint32_t*>(W.packed + panel_offset(W.n_out, W.nkb, 16, row, kb) + 4 * qq);
+    return r;
   }
   // N:M: the kept weights of the block, in ascending order, hold consecutive
   // 2-bit codes; exactly n per group of m, so the quarter's first kept weight
@@ -83,12 +122,27 @@ __device__ __forceinline__ uint32_t quarter_fields(const PackedW& W, int64_t row
   const int bb = 16 * W.n / W.m;                           // code bytes per block (even)
   const uint16_t* cp = reinterpret_cast<const uint16_t*>(W.packed + panel_offset(W.n_out, W.nkb, bb, row, kb));
   const uint2 mv = *reinterpret_cast<const uint2*>(W.meta + panel_offset(W.n_out, W.nkb, 8, row, kb));
-  const uint32_t keep = (uint32_t)(((uint64_t)mv.x | ((uint64_t)mv.y << 32)) >> (16 * qq)) & 0xFFFFu;
-  const int s0 = 32 * qq * W.n / W.m, h0 = s0 >> 4;
-  uint64_t win = 0;
+  r.m0 = mv.x;
+  r.m1 = mv.y;
+  const int h0 = (32 * qq * W.n / W.m) >> 4;
 #pragma unroll
-  for (int j = 0; j < 3; ++j)
-    if (h0 + j < bb / 2) win |= (uint64_t)cp[h0 + j] << (16 * j);
+  for (int j = 0; j < 3; ++j) r.h[j] = h0 + j < bb / 2 ? cp[h0 + j] : 0u;
+  return r;
+}
+
+// 16 ternary codes of the quarter (weights 16 qq .. 16 qq + 15 of its
+// 64-weight block) as u = c + 1 in 2-bit fields (field e = weight 16 qq + e)
+__device__ __forceinline__ uint32_t quarter_fields(const PackedW& W, const QRaw& r, int qq) {
+  if (W.fmt == 0) {
+    // DENSE2 block word qq holds weights 16 qq .. +15: weight 16 qq + e at bit 8 (e % 4) + 2 (e / 4)
+    uint32_t f = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) f |= ((r.w >> (8 * (e & 3) + 2 * (e >> 2))) & 3u) << (2 * e);
+    return f;
+  }
+  const uint32_t keep = (uint32_t)(((uint64_t)r.m0 | ((uint64_t)r.m1 << 32)) >> (16 * qq)) & 0xFFFFu;
+  const int s0 = 32 * qq * W.n / W.m;
+  uint64_t win = (uint64_t)r.h[0] | ((uint64_t)r.h[1] << 16) | ((uint64_t)r.h[2] << 32);
   win >>= s0 & 15;                                         // bit 0: the quarter's first code
   uint32_t f = 0;
   int idx = 0;
@@ -104,43 +158,96 @@ __device__ __forceinline__ uint32_t quarter_fields(const PackedW& W, int64_t row
   return f;
 }
 
-__global__ __launch_bounds__(kBT) void backward_dx_kernel(const uint16_t* __restrict__ dy, int64_t m_tok, int64_t n_out,
-                                                          int64_t k, PackedW W, const float* __restrict__ beta,
-                                                          const float* __restrict__ x, const float* __restrict__ gamma,
-                                                          float* __restrict__ dx) {
-  __shared__ __attribute__((aligned(16))) uint16_t A_s[kTile * kRow];
+// Workgroup barrier for the LDS hand-offs.  Unlike __syncthreads() it does
+// not wait for outstanding global loads (vmcnt), so the next stage's
+// prefetch stays in flight across it; the "memory" clobber keeps LDS
+// accesses on their side.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// BF16 bits of the code c = u - 1 for a 2-bit field u: 1.0, 0 or -1.0
+__device__ __forceinline__ uint32_t code_bf16(uint32_t u) {
+  return u == 1u ? 0u : (uint32_t)kOne | (u == 0u ? 0x8000u : 0u);
+}
+
+// two 16-bit elements, element j of a and of b, as one dword (a's low)
+__device__ __forceinline__ uint32_t pair16(uint32_t a, uint32_t b, int j) {
+  return __builtin_amdgcn_perm(b, a, (j & 1) ? 0x07060302u : 0x05040100u);
+}
+
+// dX tile: 128 TW tokens x 128 features per workgroup of 4 TW waves (each
+// 64 x 64).  The transposed ternary B tile of a stage is decoded once per
+// workgroup and feeds all TW token tiles: the decode, not the MFMAs, is the
+// VALU-heavy part (with 128 tokens: 36 VALU instructions per MFMA).
+template <int TW>
+__global__ __launch_bounds__(kBT * TW) void backward_dx_kernel(const uint16_t* __restrict__ dy, int64_t m_tok,
+                                                               int64_t n_out, int64_t k, PackedW W,
+                                                               const float* __restrict__ beta,
+                                                               const float* __restrict__ x,
+                                                               const float* __restrict__ gamma,
+                                                               float* __restrict__ dx) {
+  constexpr int kThr = kBT * TW, kTT = kTile * TW;
+  constexpr int kItems = (kTile / 16 * kStep + kThr - 1) / kThr;   // (channel, quarter) items per thread
+  constexpr int kVecs = kTile / 16 * 8 * 16 / kThr;                // B vectors written per thread
+  __shared__ __attribute__((aligned(16))) uint16_t A_s[kTT * kRow];
   __shared__ __attribute__((aligned(16))) uint16_t B_s[kTile * kRow];
+  __shared__ __attribute__((aligned(16))) uint32_t F_s[kTile / 16][kStep];   // 2-bit fields per (quarter, channel)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 31, g = lane >> 5;
   const int wi = wave >> 1, wj = wave & 1;
-  const int64_t t0 = (int64_t)blockIdx.y * kTile, k0 = (int64_t)blockIdx.x * kTile;
+  const int64_t t0 = (int64_t)blockIdx.y * kTT, k0 = (int64_t)blockIdx.x * kTile;
   f32x16 acc[2][2] = {};
-  for (int64_t n0 = 0; n0 < n_out; n0 += kStep) {
-    __syncthreads();                                       // the previous stage has been read
-    {  // A: dY[t0 + r][n0 .. n0 + 63], four 16-byte pieces per thread (n_out % 8 == 0)
-      const int r = tid >> 1, h = tid & 1;
-      const int64_t t = t0 + r;
+  // A: dY[t0 + r][n0 .. n0 + 63], four 16-byte pieces per thread (n_out % 8 == 0);
+  // B: (channel, quarter) items tid, tid + kThr, ...  Each stage's global
+  // loads are issued one stage ahead, into registers.
+  const int ar = tid >> 1, ah = tid & 1;
+  u32x4 ra[4];
+  QRaw rb[kItems];
+  auto load_stage = [&](int64_t n0) {
+    const int64_t t = t0 + ar;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t nn = n0 + 32 * h + 8 * v;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (t < m_tok && nn < n_out) val = *reinterpret_cast<const u32x4*>(dy + t * n_out + nn);
-        *reinterpret_cast<u32x4*>(A_s + r * kRow + 32 * h + 8 * v) = val;
-      }
+    for (int v = 0; v < 4; ++v) {
+      const int64_t nn = n0 + 32 * ah + 8 * v;
+      ra[v] = u32x4{0u, 0u, 0u, 0u};
+      if (t < m_tok && nn < n_out) ra[v] = *reinterpret_cast<const u32x4*>(dy + t * n_out + nn);
     }
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {  // B: C[n0 + nl][k0 + 64 bb + 16 qq + e] -> B_s[64 bb + 16 qq + e][nl]
-      const int nl = 32 * half + (tid >> 3), bb = (tid >> 2) & 1, qq = tid & 3;
+    for (int h = 0; h < kItems; ++h) {
+      const int idx = tid + kThr * h, nl = idx & 63, q = idx >> 6;   // q: features k0 + 16 q .. +15
       const int64_t row = n0 + nl;
-      const int kb = (int)(k0 / 64) + bb;
-      uint32_t f = 0x55555555u;                            // u = 1 everywhere: code 0
-      if (row < n_out && kb < W.nkb) f = quarter_fields(W, row, kb, qq);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t u = (f >> (2 * e)) & 3u;
-        B_s[(64 * bb + 16 * qq + e) * kRow + nl] = u == 2u ? kOne : (u == 0u ? kMinusOne : (uint16_t)0);
-      }
+      const int kb = (int)(k0 / 64) + (q >> 2);
+      rb[h] = idx < kTile / 16 * kStep && row < n_out && kb < W.nkb ? quarter_load(W, row, kb, q & 3)
+                                                                     : quarter_zero();
     }
-    __syncthreads();
+  };
+  load_stage(0);
+  for (int64_t n0 = 0; n0 < n_out; n0 += kStep) {
+    lds_barrier();                                         // the previous stage has been read
+#pragma unroll
+    for (int v = 0; v < 4; ++v) *reinterpret_cast<u32x4*>(A_s + ar * kRow + 32 * ah + 8 * v) = ra[v];
+    // B: C[n0 + nl][k0 + 16 q + e] -> B_s[16 q + e][nl], in two passes so
+    // that every LDS write is a whole 16-byte vector: first the 2-bit fields
+    // of each (output channel, 16-feature quarter) go to F_s, then each
+    // vector (8 channels rg of one feature e) is gathered from F_s.  (One
+    // 2-byte write per value put a wave's 64 writes on 4 banks.)
+#pragma unroll
+    for (int h = 0; h < kItems; ++h) {
+      const int idx = tid + kThr * h, nl = idx & 63, q = idx >> 6;
+      if (idx < kTile / 16 * kStep) F_s[q][nl] = quarter_fields(W, rb[h], q & 3);
+    }
+    if (n0 + kStep < n_out) load_stage(n0 + kStep);
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < kVecs; ++i) {
+      const int w = tid + kThr * i, rg = w & 7, e = (w >> 3) & 15, q = w >> 7;
+      const u32x4 f0 = *reinterpret_cast<const u32x4*>(&F_s[q][8 * rg]);
+      const u32x4 f1 = *reinterpret_cast<const u32x4*>(&F_s[q][8 * rg + 4]);
+      const uint32_t fw[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
+      u32x4 d;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        d[j] = code_bf16((fw[2 * j] >> (2 * e)) & 3u) | (code_bf16((fw[2 * j + 1] >> (2 * e)) & 3u) << 16);
+      *reinterpret_cast<u32x4*>(B_s + (16 * q + e) * kRow + 8 * rg) = d;
+    }
+    lds_barrier();
     mma_stage(A_s, B_s, acc, wi, wj, li, g);
   }
   // epilogue: lane (li, g) holds D[8 (v / 4) + 4 g + v % 4][li] of each 32 x 32 tile
@@ -173,50 +280,82 @@ __device__ __forceinline__ void split3(float xh, uint16_t& h1, uint16_t& h2, uin
   h3 = (uint16_t)(__float_as_uint(r2) >> 16);
 }
 
-__global__ __launch_bounds__(kBT) void backward_dw_kernel(const uint16_t* __restrict__ dy, int64_t m_tok, int64_t n_out,
-                                                          int64_t k, const int8_t* __restrict__ xq,
-                                                          const float* __restrict__ gamma, float* __restrict__ dw) {
-  __shared__ __attribute__((aligned(16))) uint16_t A_s[kTile * kRow];
+// dW tile: 128 NW output channels x 128 features per workgroup of 4 NW waves
+// (each 64 x 64).  The three BF16 parts of a stage's x_hat tile are computed
+// once per workgroup and feed all NW channel tiles (the split, repeated for
+// every channel tile, is the VALU-heavy part).
+template <int NW>
+__global__ __launch_bounds__(kBT * NW) void backward_dw_kernel(const uint16_t* __restrict__ dy, int64_t m_tok,
+                                                               int64_t n_out, int64_t k,
+                                                               const int8_t* __restrict__ xq,
+                                                               const float* __restrict__ gamma,
+                                                               float* __restrict__ dw) {
+  constexpr int kThr = kBT * NW, kTN = kTile * NW;
+  constexpr int kJ = 8 / NW;                               // x_hat columns per thread
+  __shared__ __attribute__((aligned(16))) uint16_t A_s[kTN * kRow];
   __shared__ __attribute__((aligned(16))) uint16_t B_s[3][kTile * kRow];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 31, g = lane >> 5;
   const int wi = wave >> 1, wj = wave & 1;
-  const int64_t n0 = (int64_t)blockIdx.y * kTile, k0 = (int64_t)blockIdx.x * kTile;
+  const int64_t n0 = (int64_t)blockIdx.y * kTN, k0 = (int64_t)blockIdx.x * kTile;
   f32x16 acc[2][2] = {};
-  const int r = tid >> 2, c32 = 32 * (tid & 3);            // staging: token row r of the stage, 32 columns
+  // staging (both operands transposed: the stage's 64 tokens are the MFMA's
+  // contracted index): thread = tokens t0 + 4 tq .. +3 x 8 columns, transposed
+  // in registers and written as 8-byte vectors (4 tokens of one column), so
+  // that 16 lanes fill 128 contiguous bytes of one LDS row.  (One 2-byte write
+  // per value put a wave's writes on a few banks.)  x_hat: thread = 4 tokens x
+  // kJ columns (8 cb + kJ jh ..).
+  const int tq = tid & 15, cb = tid >> 4;                  // token quad, 8-column block of dY
+  const int xb = (tid >> 4) & 15, jh = tid >> 8;           // x_hat: 8-column block, its part jh
+  // each stage's global loads are issued one stage ahead, into registers
+  u32x4 va[4];                                             // dY[t0 + 4 tq + tt][n0 + 8 cb .. +7]
+  uint32_t qv[4][kJ / 4];                                  // xq[t0 + 4 tq + tt][k0 + 8 xb + kJ jh .. +kJ-1]
+  float ge[4];                                             // gamma_eff of those tokens
+  auto load_stage = [&](int64_t t0) {
+    const int64_t nn = n0 + 8 * cb;
+    const int64_t kk = k0 + 8 * xb + kJ * jh;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int64_t t = t0 + 4 * tq + tt;
+      va[tt] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int w = 0; w < kJ / 4; ++w) qv[tt][w] = 0u;
+      ge[tt] = 0.0f;
+      if (t < m_tok && nn < n_out) va[tt] = *reinterpret_cast<const u32x4*>(dy + t * n_out + nn);
+      if (t < m_tok && kk < k) {
+#pragma unroll
+        for (int w = 0; w < kJ / 4; ++w) qv[tt][w] = reinterpret_cast<const uint32_t*>(xq + t * k + kk)[w];
+        ge[tt] = fmaxf(gamma[t], 1e-5f);
+      }
+    }
+  };
+  load_stage(0);
   for (int64_t t0 = 0; t0 < m_tok; t0 += kStep) {
-    __syncthreads();
-    const int64_t t = t0 + r;
+    lds_barrier();
+    // A: dY[t0 + 4 tq + tt][n0 + 8 cb + j] -> A_s[8 cb + j][4 tq + tt]
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {  // A: dY[t][n0 + c32 + 8v .. +7] -> A_s[c32 + 8v + e][r]
-      const int64_t nn = n0 + c32 + 8 * v;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (t < m_tok && nn < n_out) val = *reinterpret_cast<const u32x4*>(dy + t * n_out + nn);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) A_s[(c32 + 8 * v + e) * kRow + r] = (uint16_t)(val[e >> 1] >> (16 * (e & 1)));
+    for (int j = 0; j < 8; ++j) {
+      const uint2 d = make_uint2(pair16(va[0][j >> 1], va[1][j >> 1], j), pair16(va[2][j >> 1], va[3][j >> 1], j));
+      *reinterpret_cast<uint2*>(A_s + (8 * cb + j) * kRow + 4 * tq) = d;
     }
+    // B: x_hat[t0 + 4 tq + tt][k0 + c] in three parts -> B_s[p][c][4 tq + tt], c = 8 xb + kJ jh + j
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {  // B: x_hat[t][k0 + c32 + 16v .. +15] in three parts -> B_s[p][..][r]
-      const int c = c32 + 16 * v;
-      u32x4 qv = {0u, 0u, 0u, 0u};
-      float ge = 0.0f;
-      if (t < m_tok && k0 + c < k) {
-        qv = *reinterpret_cast<const u32x4*>(xq + t * k + k0 + c);
-        ge = fmaxf(gamma[t], 1e-5f);
-      }
+    for (int j = 0; j < kJ; ++j) {
+      uint16_t h[3][4];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int qe = (int)(int8_t)(qv[e >> 2] >> (8 * (e & 3)));
-        const float xh = (ge * (float)qe) * (1.0f / 128.0f);
-        uint16_t h1, h2, h3;
-        split3(xh, h1, h2, h3);
-        B_s[0][(c + e) * kRow + r] = h1;
-        B_s[1][(c + e) * kRow + r] = h2;
-        B_s[2][(c + e) * kRow + r] = h3;
+      for (int tt = 0; tt < 4; ++tt) {
+        const int qe = (int)(int8_t)(qv[tt][j >> 2] >> (8 * (j & 3)));
+        const float xh = (ge[tt] * (float)qe) * (1.0f / 128.0f);
+        split3(xh, h[0][tt], h[1][tt], h[2][tt]);
       }
+      const int c = 8 * xb + kJ * jh + j;
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        *reinterpret_cast<uint2*>(B_s[p] + c * kRow + 4 * tq) =
+            make_uint2((uint32_t)h[p][0] | ((uint32_t)h[p][1] << 16), (uint32_t)h[p][2] | ((uint32_t)h[p][3] << 16));
     }
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < 3; ++p) mma_stage(A_s, B_s[p], acc, wi, wj, li, g);
+    if (t0 + kStep < m_tok) load_stage(t0 + kStep);
+    lds_barrier();
+    mma_stage3(A_s, B_s, acc, wi, wj, li, g);
   }
 #pragma unroll
   for (int ti = 0; ti < 2; ++ti)
@@ -233,18 +372,20 @@ __global__ __launch_bounds__(kBT) void backward_dw_kernel(const uint16_t* __rest
 }  // namespace
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
-  const dim3 block(kBT);
   if (a.dx) {
     PackedW W{a.packed, a.meta, a.n_out, (int32_t)(a.k / 64), a.fmt, a.n, a.m};
-    const dim3 grid((unsigned)((a.k + kTile - 1) / kTile), (unsigned)((a.m_tok + kTile - 1) / kTile));
-    hipLaunchKernelGGL(backward_dx_kernel, grid, block, 0, s, a.dy, a.m_tok, a.n_out, a.k, W, a.beta, a.x, a.gamma,
-                       a.dx);
+    constexpr int kTW = kDxTW;
+    const dim3 grid((unsigned)((a.k + kTile - 1) / kTile), (unsigned)((a.m_tok + kTile * kTW - 1) / (kTile * kTW)));
+    hipLaunchKernelGGL((backward_dx_kernel<kTW>), grid, dim3(kBT * kTW), 0, s, a.dy, a.m_tok, a.n_out, a.k, W, a.beta,
+                       a.x, a.gamma, a.dx);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (a.dw) {
-    const dim3 grid((unsigned)((a.k + kTile - 1) / kTile), (unsigned)((a.n_out + kTile - 1) / kTile));
-    hipLaunchKernelGGL(backward_dw_kernel, grid, block, 0, s, a.dy, a.m_tok, a.n_out, a.k, a.xq, a.gamma, a.dw);
+    constexpr int kNW = kDwNW;
+    const dim3 grid((unsigned)((a.k + kTile - 1) / kTile), (unsigned)((a.n_out + kTile * kNW - 1) / (kTile * kNW)));
+    hipLaunchKernelGGL((backward_dw_kernel<kNW>), grid, dim3(kBT * kNW), 0, s, a.dy, a.m_tok, a.n_out, a.k, a.xq,
+                       a.gamma, a.dw);
   }
   return hipGetLastError();
 }
