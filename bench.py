@@ -107,12 +107,31 @@ def parse():
 # --------------------------------------------------------------------------- traffic records
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = sorted(glob.glob(os.path.join("sparse_linear_layers_absmean_amd", "csrc", "*"), root_dir=ROOT))
+CSRC = os.path.join("sparse_linear_layers_absmean_amd", "csrc")
+# the sources each measured kernel is built from (its file and the headers it
+# includes), plus the header and C ABI that configure every launch: a traffic
+# record holds while these files are unchanged
+_COMMON_SOURCES = ["sbl_internal.h", "sbl_api.hip"]
+KERNEL_SOURCES = {
+    "gemv_kernel": ["k_linear.hip", "sbl_actq.h", "sbl_decode.h"],
+    "quant_acts": ["k_quant_acts.hip", "sbl_actq.h"],
+    "gemm_kernel": ["k_gemm.hip", "k_linear.hip", "sbl_decode.h"],
+    "gemm24_kernel": ["k_gemm24.hip", "k_gemm.hip", "k_linear.hip", "sbl_decode.h"],
+    "absmean_partial_kernel": ["k_beta.hip", "sbl_partial.h", "sbl_beta.h", "sbl_select.h"],
+    "absmean_final_kernel": ["k_beta.hip", "sbl_partial.h", "sbl_beta.h", "sbl_select.h"],
+    "mask_pack_fast_kernel": ["k_maskpack.hip", "sbl_partial.h", "sbl_beta.h", "sbl_select.h"],
+    "resident_kernel": ["k_maskpack.hip", "sbl_partial.h", "sbl_beta.h", "sbl_select.h"],
+}
 
 
-def _sources_sha():
+def _sources_sha(kernels):
+    """SHA-256 of the sources of the comma-separated kernel name prefixes."""
+    files = set(_COMMON_SOURCES)
+    for name in kernels.split(","):
+        files.update(KERNEL_SOURCES[name])
     out = {}
-    for rel in KERNEL_SOURCES:
+    for f in sorted(files):
+        rel = os.path.join(CSRC, f)
         with open(os.path.join(ROOT, rel), "rb") as fh:
             out[rel] = hashlib.sha256(fh.read()).hexdigest()
     return out
@@ -120,12 +139,12 @@ def _sources_sha():
 
 def recorded_traffic(key, field="bytes_per_launch"):
     """HBM bytes per launch (or per step) recorded for `key` in
-    profiles/traffic.json, or None when there is no record or any kernel
-    source has changed since (SHA-256)."""
+    profiles/traffic.json, or None when there is no record or a source of its
+    kernels has changed since (SHA-256)."""
     try:
         with open(TRAFFIC_JSON) as fh:
             rec = json.load(fh)[key]
-        if rec["sources_sha256"] != _sources_sha():
+        if rec["sources_sha256"] != _sources_sha(rec["kernels"]):
             return None
         return rec[field]
     except (OSError, KeyError, ValueError):
@@ -240,7 +259,7 @@ def record_traffic(args):
         "read_bytes_per_launch": round(res["FETCH_SIZE"]["bytes_per_launch"]),
         "write_bytes_per_launch": round(res["WRITE_SIZE"]["bytes_per_launch"]),
         "fetch_factor": round(res["FETCH_SIZE"]["factor"], 4), "write_factor": round(res["WRITE_SIZE"]["factor"], 4),
-        "summary": args.summary, "sources_sha256": _sources_sha()}
+        "summary": args.summary, "sources_sha256": _sources_sha(args.kernel)}
     with open(TRAFFIC_JSON, "w") as fh:
         json.dump(allrec, fh, indent=1, sort_keys=True)
     if args.summary:
