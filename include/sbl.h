@@ -265,7 +265,11 @@ int sbl_quant_acts(const float* x, int64_t m_tok, int64_t k, int8_t* xq, float* 
  *                 RN(fp32(acc) * RN(RN(max(beta,1e-5) * max(gamma,1e-5)) * 2^-7)).
  *   acc           [m_tok][n_out] int32 output (exact sum), or NULL.
  * Decode sizes (m_tok <= 16) run a bandwidth-bound GEMV, larger ones an
- * int8-MFMA GEMM; both give identical bits.  m_tok == 0 is a no-op.
+ * int8-MFMA GEMM; both give identical bits.  Products whose buffers are too
+ * large for those kernels' 32-bit buffer offsets (2 GiB, the last tile's
+ * overhang included, e.g. (m_tok + 256) * n_out * 4 bytes of y for the GEMM)
+ * run a generic kernel instead: the same bits, more slowly.  m_tok == 0 is
+ * a no-op.
  */
 int sbl_linear(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
                const float* beta, const int8_t* xq, const float* gamma,
