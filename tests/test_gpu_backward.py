@@ -96,8 +96,9 @@ def test_backward_outputs_one_at_a_time():
 
 def test_backward_3b_block_matrix_sampled():
     """A 3B-class gate matrix (8640 x 3200) with 2048 tokens, as the benchmark
-    times it: sampled token rows of dX and output rows of dW."""
+    times it: sampled token rows of dX (including both sides of the 128-token
+    wave halves and of the 256-token workgroup tiles) and output rows of dW."""
     rng = np.random.default_rng(93)
-    rows = (np.unique(np.concatenate([[0, 127, 128, 2047], rng.integers(0, 2048, 12)])),
+    rows = (np.unique(np.concatenate([[0, 127, 128, 255, 256, 2047], rng.integers(0, 2048, 12)])),
             np.unique(np.concatenate([[0, 8639], rng.integers(0, 8640, 14)])))
     _run(2048, 8640, 3200, 6, 8, FMT_NM, seed=94, rows=rows, hot=8)
