@@ -853,7 +853,10 @@ def measured_peaks(torch, dev, tm):
     tops = grid * 4 * 4 * iters * 65536 / (ms * 1e-3) / 1e12
     del sink
     torch.cuda.empty_cache()
-    return {"stream_read_GBps": round(best, 1), "stream_read_workgroups": best_grid,
+    khz = ctypes.c_int(0)
+    clock = khz.value / 1000.0 if lib.sbl_probe_clock_khz(ctypes.byref(khz)) == 0 else None
+    return {"peak_engine_clock_MHz": clock,
+            "stream_read_GBps": round(best, 1), "stream_read_workgroups": best_grid,
             "stream_read_frac_of_peak": round(best / HBM_PEAK_GBPS, 4),
             "mfma_i8_TOPS": round(tops, 1), "mfma_i8_frac_of_peak": round(tops / INT8_PEAK_TOPS, 4)}
 
@@ -1087,6 +1090,7 @@ def main():
     out["cpu_baseline"] = cpu
     out["bench_s"] = round(time.time() - t0, 1)
     out["device"] = torch.cuda.get_device_name(0)
+    out["device_arch"] = getattr(torch.cuda.get_device_properties(0), "gcnArchName", None)
     print(json.dumps(out), flush=True)
 
 

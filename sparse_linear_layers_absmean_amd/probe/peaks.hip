@@ -79,4 +79,12 @@ int sbl_probe_mfma_i8(int32_t* sink, int grid, int iters, hipStream_t stream) {
   return (int)hipGetLastError();
 }
 
+// The current device's peak engine clock (kHz), as the runtime reports it.
+int sbl_probe_clock_khz(int* khz) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(khz, hipDeviceAttributeClockRate, dev);
+  return (int)e;
+}
+
 }  // extern "C"

@@ -405,11 +405,11 @@ def test_quant_weights_batch_noalloc_validation(lib):
     assert limit // small >= 73
 
 
-def test_peak_probe_library_exports_its_two_calls():
+def test_peak_probe_library_exports_its_calls():
     # the benchmark's peak probes live in a library of their own (not the path's ABI)
     probe = os.path.join(ROOT, "sparse_linear_layers_absmean_amd", "libsbl_probe.so")
     if not os.path.exists(probe):
         pytest.fail("libsbl_probe.so is not built (run __graft_entry__.build())")
     out = subprocess.run(["nm", "-D", "--defined-only", probe], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (sbl_[a-z0-9_]+)", out))
-    assert exported == {"sbl_probe_stream_read", "sbl_probe_mfma_i8"}
+    assert exported == {"sbl_probe_stream_read", "sbl_probe_mfma_i8", "sbl_probe_clock_khz"}
