@@ -13,15 +13,19 @@
 // the words it loaded (loads are the scarce resource here: the cost of a
 // vector memory instruction grows with the cache lines it touches, not with
 // its bytes).
-//  * activations: each step's token x 128 byte tile is fetched (eight tokens,
-//    whole 128-byte lines, per instruction) into registers kDepth steps
-//    ahead, written to one of two LDS buffers one step ahead of use and read
-//    back as B operands; the 16-byte chunks of a token row are XOR-swizzled
-//    by the token index so that consecutive tokens read distinct banks.
-//  * weights: fetched kDepth-1 steps ahead straight into registers and
-//    decoded into A operands (7 VALU ops per 16 weights; N:M: codes spread
-//    arithmetically, one LDS selector read per 8 weights, v_perm); each A
-//    operand feeds KCT MFMAs.
+//  * activations (the MFMA's A operand): each step's token x 128 byte tile is
+//    fetched (eight tokens, whole 128-byte lines, per instruction) into
+//    registers kDepth steps ahead, written to one of two LDS buffers one step
+//    ahead of use and read back as operands; the 16-byte chunks of a token row
+//    are XOR-swizzled by the token index so that consecutive tokens read
+//    distinct banks.
+//  * weights (the MFMA's B operand): fetched kDepth-1 steps ahead straight
+//    into registers and decoded into operands (7 VALU ops per 16 weights;
+//    N:M: codes spread arithmetically, one LDS selector read per 8 weights,
+//    v_perm); each decoded weight operand feeds KCT MFMAs.
+//  * with the activations as A, each lane's accumulators hold 16 tokens of
+//    one weight row, so the epilogue writes whole 128-byte runs of a token's
+//    output row.
 //  * the per-step workgroup barrier waits only for LDS traffic, never for
 //    the global loads in flight.
 // K need only be a multiple of 64: in a last half step the second half reads
@@ -114,7 +118,7 @@ __device__ __forceinline__ uint32_t spread4(uint32_t x) {
   return __builtin_amdgcn_perm(0u, 0x000100FFu, z);
 }
 
-// A operand (16 weights, k order) of sub-step j: word j of the lane's block.
+// Weight operand (16 weights, k order) of sub-step j: word j of the lane's block.
 template <int KIND>
 __device__ __forceinline__ v4i decode_w(const WRaw<KIND>& a, int j, const NmLut& L) {
   if constexpr (KIND == kDense2) {
