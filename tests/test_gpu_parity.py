@@ -187,7 +187,9 @@ def test_linear_batch_matches_single_calls(fmt, n, m):
     shapes = [(96, 128, 1), (200, 320, 3), (33, 64, 16), (130, 512, 2), (64, 192, 40), (17, 256, 1),
               (300, 640, 5), (48, 128, 8), (80, 384, 1), (16, 64, 1),
               # several items above the decode range: one grouped GEMM launch (2:4: sparse MFMA)
-              (300, 640, 33), (130, 512, 200), (520, 1216, 150)]
+              (300, 640, 33), (130, 512, 200), (520, 1216, 150),
+              # an odd row count: token rows of y are not 16-byte aligned
+              (67, 192, 70)]
     items, refs = [], []
     for n_out, k, m_tok in shapes:
         bits = synth.gaussian_masters(rng, n_out, k)
