@@ -64,8 +64,8 @@ BLOCKS = {
     "13b": ("b13", 5120, 13824, "13B-class block (hidden 5120, FFN 13824)"),
     "70b": ("b70", 8192, 28672, "70B-class block (hidden 8192, FFN 28672)"),
 }
-SECTIONS = ("peaks", "headline", "gemv", "prefill", "train13b", "weight_prep", "step0p7b", "backward",
-            "group_scales", "references", "cpu")
+SECTIONS = ("peaks", "headline", "gemv", "prefill", "act_quant", "train13b", "weight_prep", "step0p7b",
+            "backward", "group_scales", "references", "cpu")
 
 
 def parse():
@@ -442,15 +442,20 @@ def bench_decode_step(torch, np, sbl, dev, tm, args):
 # --------------------------------------------------------------------------- GEMV table
 
 def gemv_sweep(torch, np, sbl, dev, tm):
-    """Packed-weight GB/s of the grouped GEMV (sbl_linear_batch: 4 launches per block) for
-    the decode configurations.  The packed bytes are seeded random valid codes (the GEMV's
+    """Packed-weight GB/s of the GEMV for the decode configurations: grouped (sbl_linear_batch:
+    4 launches per block, matrices sharing an input in one launch) and, for the 3B and 70B
+    blocks at one token, one launch per matrix (7 per block).  The packed bytes are seeded random valid codes (the GEMV's
     time does not depend on their values); blocks rotate over >= 600 MB of distinct
     buffers; each block's 4 launches are one HIP graph."""
-    cases = [("0p7b", 1), ("3b", 1), ("3b", 4), ("3b", 8), ("70b", 1), ("70b", 8)]
+    # (block, tokens, one launch per matrix instead of the grouped launches)
+    cases = [("0p7b", 1, False), ("3b", 1, False), ("3b", 4, False), ("3b", 8, False), ("70b", 1, False),
+             ("70b", 8, False), ("3b", 1, True), ("70b", 1, True)]
     out = []
-    for blk, m_tok in cases:
+    for blk, m_tok, single in cases:
         mats = mats_of(blk)
         for fname, (fmt, n, m) in FORMATS.items():
+            if single and fname == "nm24":
+                continue
             nbytes = [sbl.sbl_packed_bytes(no, k, n, m, fmt) for _, no, k in mats]
             mbytes = [no * k // 8 if fmt == 1 else 0 for _, no, k in mats]
             bb = sum(nbytes) + sum(mbytes)
@@ -474,17 +479,49 @@ def gemv_sweep(torch, np, sbl, dev, tm):
 
             def run(c):
                 for gi, grp in enumerate(GROUPS):
-                    sbl.sbl_linear_batch([dict(pool[c][i], xq=xs[gi], gamma=gam) for i in grp], fmt, n, m)
+                    if single:
+                        for i in grp:
+                            sbl.sbl_linear_batch([dict(pool[c][i], xq=xs[gi], gamma=gam)], fmt, n, m)
+                    else:
+                        sbl.sbl_linear_batch([dict(pool[c][i], xq=xs[gi], gamma=gam) for i in grp], fmt, n, m)
 
             us = timed_steps(torch, tm, run, copies, 8 * copies) * 1e3
             gbps = bb / (us * 1e-6) / 1e9
             hbm = bb + sum(m_tok * mats[g_[0]][2] + 4 * m_tok for g_ in GROUPS) + \
                 sum(4 * m_tok * no for _, no, _k in mats)
-            out.append({"block": blk, "format": fname, "m_tok": m_tok, "weight_bytes": bb,
+            out.append({"block": blk, "format": fname, "m_tok": m_tok,
+                        "launches": f"{len(mats)}, one per matrix" if single else f"{len(GROUPS)}, grouped",
+                        "weight_bytes": bb,
                         "us_per_block": round(us, 2), "weight_GBps": round(gbps, 1),
                         "hbm_GBps": round(hbm / (us * 1e-6) / 1e9, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)})
             del pool, xs
             torch.cuda.empty_cache()
+    return out
+
+
+# --------------------------------------------------------------------------- activation quantization
+
+def bench_act_quant(torch, sbl, dev, tm):
+    """sbl_quant_acts alone (per-token absmax int8 quantization) at the decode and prefill
+    input shapes of the blocks: algorithmic bytes = fp32 read + int8 written (5 B per
+    value) + gamma (4 B per token); N(0,1) inputs drawn on the device; graph replays
+    rotating over >= 560 MB of distinct inputs."""
+    cases = [(1, 8192), (1, 28672), (8, 28672), (16, 28672),
+             (2048, 3200), (2048, 8640), (4096, 5120), (4096, 13824)]
+    out = []
+    g = torch.Generator(device=dev).manual_seed(13)
+    for m_tok, k in cases:
+        copies = rot_copies(m_tok * k * 5, cap=256)
+        pool = [(torch.randn((m_tok, k), generator=g, device=dev),
+                 torch.empty((m_tok, k), dtype=torch.int8, device=dev),
+                 torch.empty(m_tok, device=dev)) for _ in range(copies)]
+        us = timed_steps(torch, tm, lambda c: sbl.sbl_quant_acts(*pool[c]), copies, max(20, 2 * copies)) * 1e3
+        alg = m_tok * k * 5 + 4 * m_tok
+        gbps = alg / (us * 1e-6) / 1e9
+        out.append({"m_tok": m_tok, "k": k, "us_per_call": round(us, 2), "alg_bytes": alg,
+                    "alg_GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+        del pool
+        torch.cuda.empty_cache()
     return out
 
 
@@ -1031,6 +1068,8 @@ def main():
     if "train13b" in sections:
         line["train_step_13b"] = bench_train13b(torch, np, sbl, dev, tm, masters["13b"])
     masters.pop("13b", None)
+    if "act_quant" in sections:
+        line["act_quant"] = bench_act_quant(torch, sbl, dev, tm)
     if "weight_prep" in sections:
         line["weight_prep"] = weight_prep_sweep(torch, np, sbl, dev, tm, args.prep_blocks)
     if "step0p7b" in sections:
