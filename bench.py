@@ -727,7 +727,7 @@ def bench_step0p7b(torch, np, sbl, dev, tm):
 
 def bench_backward(torch, np, sbl, dev, tm, masters3b):
     """Backward of a 3B-class block at 2048 tokens, 6:8 weights: sbl_linear_backward (dX
-    and dW of the 7 matrices) on the BF16 matrix cores.  Algorithmic flops 2*M*N*K per
+    and dW of the 7 matrices) on the BF16 matrix cores, with a caller workspace and without.  Algorithmic flops 2*M*N*K per
     gradient; dW runs three BF16 products per step (x_hat split exactly into three parts)."""
     import synth
     fmt, n, m = FORMATS["nm68"]
@@ -744,32 +744,44 @@ def bench_backward(torch, np, sbl, dev, tm, masters3b):
         items.append((o, x, xq, gamma, dy, torch.empty((m_tok, k), device=dev), torch.empty((no, k), device=dev)))
         del w
 
-    def run(which):
+    # one workspace serves the 7 calls in turn (one stream)
+    ws = sbl.new_backward_workspace(m_tok, max(no for _, no, _k in mats), max(k for _, _n, k in mats), dev)
+
+    def run(which, use_ws):
         for o, x, xq, gamma, dy, dx, dw in items:
             sbl.sbl_linear_backward(dy, o["packed"], o["meta"], fmt, n, m, o["beta"], x, xq, gamma,
                                     dx=dx if which in ("dx", "both") else None,
-                                    dw=dw if which in ("dw", "both") else None)
+                                    dw=dw if which in ("dw", "both") else None,
+                                    workspace=ws if use_ws else None)
 
-    res = {}
-    for which in ("dx", "dw", "both"):
-        for _ in range(2):
-            run(which)
-        torch.cuda.synchronize()
-        tm.start()
-        for _ in range(5):
-            run(which)
-        res[which] = tm.stop_ms() / 5
     flops = sum(2 * m_tok * no * k for _, no, k in mats)
-    tf = {w: (flops * (2 if w == "both" else 1)) / (res[w] * 1e-3) / 1e12 for w in res}
-    del items
-    torch.cuda.empty_cache()
-    return {"workload": "Backward (dX and dW), M=2048 tokens, 3B-class block (hidden 3200, FFN 8640), 6:8 N:M",
-            "kernel": "backward_dx_kernel, backward_dw_kernel (v_mfma_f32_32x32x16_bf16)",
+    out = {}
+    for use_ws in (True, False):
+        res = {}
+        for which in ("dx", "dw", "both"):
+            for _ in range(2):
+                run(which, use_ws)
+            torch.cuda.synchronize()
+            tm.start()
+            for _ in range(5):
+                run(which, use_ws)
+            res[which] = tm.stop_ms() / 5
+        tf = {w: (flops * (2 if w == "both" else 1)) / (res[w] * 1e-3) / 1e12 for w in res}
+        out["workspace" if use_ws else "no_workspace"] = {
             "ms_per_block": {w: round(v, 3) for w, v in res.items()},
             "algorithmic_TFLOPS": {w: round(v, 1) for w, v in tf.items()},
-            "dw_mfma_TFLOPS": round(3 * flops / (res["dw"] * 1e-3) / 1e12, 1),
-            "roofline": {"bound": "mfma", "achieved": round(tf["both"], 1), "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf["both"] / BF16_PEAK_TFLOPS, 4), "traffic": None}}
+            "dw_mfma_TFLOPS": round(3 * flops / (res["dw"] * 1e-3) / 1e12, 1)}
+    del items, ws
+    torch.cuda.empty_cache()
+    main = out["workspace"]
+    tf_both = main["algorithmic_TFLOPS"]["both"]
+    return {"workload": "Backward (dX and dW), M=2048 tokens, 3B-class block (hidden 3200, FFN 8640), 6:8 N:M",
+            "call": "sbl_linear_backward_ws (one caller workspace; sbl_linear_backward without one: no_workspace)",
+            "kernel": "bwd_codes_t/bwd_dy_t/bwd_xhat_t_kernel + bwd_gemm_kernel (v_mfma_f32_32x32x16_bf16); "
+                      "without a workspace backward_dx_kernel, backward_dw_kernel",
+            **main, "no_workspace": out["no_workspace"],
+            "roofline": {"bound": "mfma", "achieved": tf_both, "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf_both / BF16_PEAK_TFLOPS, 4), "traffic": None}}
 
 
 # --------------------------------------------------------------------------- group scales

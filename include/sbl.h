@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SBL_ABI_VERSION 9
+#define SBL_ABI_VERSION 10
 
 typedef enum {
   SBL_OK = 0,
@@ -401,6 +401,30 @@ int sbl_linear_backward(const uint16_t* dy_bf16, int64_t m_tok, int64_t n_out, i
                         const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
                         const float* beta, const float* x, const int8_t* xq, const float* gamma,
                         float* dx, float* dw, sbl_stream stream);
+
+/* Bytes of device scratch that sbl_linear_backward_ws needs at these sizes
+ * (for both outputs), or -1 for sizes sbl_linear_backward rejects.  It holds
+ * the codes transposed as BF16 (k x n_out, n_out rounded up to 64), dy
+ * transposed (n_out x m_tok, both rounded up to 64) and the three BF16 parts
+ * of x_hat transposed (3 x k x m_tok): about 2 k n_out + 2 n_out m_tok +
+ * 6 k m_tok bytes. */
+int64_t sbl_backward_workspace_bytes(int64_t m_tok, int64_t n_out, int64_t k);
+
+/* sbl_linear_backward (the same operation, results within the same bounds;
+ * the same argument checks and status codes) with a caller workspace: the
+ * ternary codes are decoded and the operands transposed once per call into
+ * `workspace`, so that both gradients run as plain BF16 contractions.
+ *   workspace        device memory, 256-byte aligned (SBL_ERR_ALIGN), owned by
+ *                    the caller, of workspace_bytes >=
+ *                    sbl_backward_workspace_bytes(m_tok, n_out, k) bytes
+ *                    (else SBL_ERR_SHAPE); NULL: SBL_ERR_NULL.  Its contents
+ *                    need no initialisation and are scratch after the call;
+ *                    it must not overlap any input or output (SBL_ERR_SHAPE),
+ *                    and calls in flight at the same time need their own. */
+int sbl_linear_backward_ws(const uint16_t* dy_bf16, int64_t m_tok, int64_t n_out, int64_t k,
+                           const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
+                           const float* beta, const float* x, const int8_t* xq, const float* gamma,
+                           float* dx, float* dw, void* workspace, int64_t workspace_bytes, sbl_stream stream);
 
 #ifdef __cplusplus
 }

@@ -5,7 +5,8 @@ declared in include/sbl.h); `sbl` is its thin Python binding.  Importing the
 package does not load the library: `sbl.load()` (or the first call) does.
 """
 
-from .sbl import (SBL_FMT_DENSE2, SBL_FMT_NM, SblError, linear, load, new_workspace, quant_acts,
+from .sbl import (SBL_FMT_DENSE2, SBL_FMT_NM, SblError, linear, load, new_backward_workspace, new_workspace,
+                  quant_acts, sbl_backward_workspace_bytes,
                   quant_weights, sbl_abi_version, sbl_linear, sbl_linear_acts_batch, sbl_linear_backward,
                   sbl_linear_batch, sbl_linear_grouped, sbl_linear_kgrouped, sbl_meta_bytes,
                   sbl_quant_acts_kgrouped, sbl_quant_weights_grouped,
@@ -17,7 +18,8 @@ from .sbl import (SBL_FMT_DENSE2, SBL_FMT_NM, SblError, linear, load, new_worksp
                   sbl_workspace_init)
 
 __all__ = [
-    "SBL_FMT_DENSE2", "SBL_FMT_NM", "SblError", "linear", "load", "new_workspace", "quant_acts",
+    "SBL_FMT_DENSE2", "SBL_FMT_NM", "SblError", "linear", "load", "new_backward_workspace", "new_workspace",
+    "quant_acts", "sbl_backward_workspace_bytes",
     "quant_weights", "sbl_abi_version", "sbl_linear", "sbl_linear_acts_batch", "sbl_linear_backward",
     "sbl_linear_batch", "sbl_linear_grouped", "sbl_linear_kgrouped", "sbl_meta_bytes",
     "sbl_quant_acts_kgrouped", "sbl_quant_weights_grouped",

@@ -369,7 +369,289 @@ __global__ __launch_bounds__(kBT * NW) void backward_dw_kernel(const uint16_t* _
       }
 }
 
+// ---------------------------------------------------------------------------
+// Workspace path.  The kernels above decode the ternary codes (dX) and
+// transpose and split the operands (dW) again for every output tile.  With a
+// caller workspace this is done once per call:
+//   ct  [k][np]     the codes C^T as BF16 (np = n_out rounded up to 64; zeros
+//                   past n_out)
+//   dyt [np][mp]    dY^T (mp = m_tok rounded up to 64; zeros past both ends)
+//   xt  [3][k][mp]  the three BF16 parts of x_hat, transposed (zeros past m_tok)
+// and the two gradients become plain BF16 contractions whose operands both
+// have the contracted index contiguous:
+//   dX[t][kk] = sum_n dy[t][n] ct[kk][n]               (A = dY, B = ct)
+//   dW[n][kk] = sum_p sum_t dyt[n][t] xt[p][kk][t]      (A = dyt, B = xt)
+// ---------------------------------------------------------------------------
+
+// C^T of one tile of 64 output channels x one 64-weight block (grid: np / 64,
+// k / 64).  Rows past n_out decode as code 0.
+__global__ __launch_bounds__(256) void bwd_codes_t_kernel(PackedW W, int64_t np, uint16_t* __restrict__ ct) {
+  __shared__ uint32_t F[4][64];                            // 2-bit fields of (quarter, channel)
+  const int tid = threadIdx.x, nl = tid & 63, q = tid >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * 64, row = n0 + nl;
+  const int kb = (int)blockIdx.y;
+  F[q][nl] = quarter_fields(W, row < W.n_out ? quarter_load(W, row, kb, q) : quarter_zero(), q);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int w = tid + 256 * i, e = w >> 3, rg = w & 7;  // feature 64 kb + e, channels n0 + 8 rg .. +7
+    const int qq = e >> 4, sh = 2 * (e & 15);
+    u32x4 d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      d[j] = code_bf16((F[qq][8 * rg + 2 * j] >> sh) & 3u) | (code_bf16((F[qq][8 * rg + 2 * j + 1] >> sh) & 3u) << 16);
+    *reinterpret_cast<u32x4*>(ct + ((int64_t)kb * 64 + e) * np + n0 + 8 * rg) = d;
+  }
+}
+
+// dY^T of one 64-channel x 64-token tile (grid: np / 64, mp / 64)
+__global__ __launch_bounds__(256) void bwd_dy_t_kernel(const uint16_t* __restrict__ dy, int64_t m_tok, int64_t n_out,
+                                                       int64_t mp, uint16_t* __restrict__ dyt) {
+  __shared__ __attribute__((aligned(16))) uint16_t T[64][kRow];   // [token][channel]
+  const int tid = threadIdx.x;
+  const int64_t n0 = (int64_t)blockIdx.x * 64, t0 = (int64_t)blockIdx.y * 64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int w = tid + 256 * i, t = w >> 3, c = w & 7;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (t0 + t < m_tok && n0 + 8 * c < n_out) v = *reinterpret_cast<const u32x4*>(dy + (t0 + t) * n_out + n0 + 8 * c);
+    *reinterpret_cast<u32x4*>(&T[t][8 * c]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int w = tid + 256 * i, nl = w >> 3, c = w & 7;  // channel n0 + nl, tokens t0 + 8 c .. +7
+    u32x4 d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[j] = (uint32_t)T[8 * c + 2 * j][nl] | ((uint32_t)T[8 * c + 2 * j + 1][nl] << 16);
+    *reinterpret_cast<u32x4*>(dyt + (n0 + nl) * mp + t0 + 8 * c) = d;
+  }
+}
+
+// the three BF16 parts of x_hat, transposed, for one 64-feature x 64-token
+// tile (grid: k / 64, mp / 64)
+__global__ __launch_bounds__(256) void bwd_xhat_t_kernel(const int8_t* __restrict__ xq, const float* __restrict__ gamma,
+                                                         int64_t m_tok, int64_t k, int64_t mp,
+                                                         uint16_t* __restrict__ xt) {
+  __shared__ __attribute__((aligned(16))) uint32_t S[3][64][kStep / 2 + 4];   // [part][token][feature pair]
+  const int tid = threadIdx.x, t = tid >> 2, c = tid & 3;  // token t0 + t, features k0 + 16 c .. +15
+  const int64_t k0 = (int64_t)blockIdx.x * 64, t0 = (int64_t)blockIdx.y * 64;
+  u32x4 qv = {0u, 0u, 0u, 0u};
+  float ge = 0.0f;
+  if (t0 + t < m_tok) {
+    qv = *reinterpret_cast<const u32x4*>(xq + (t0 + t) * k + k0 + 16 * c);
+    ge = fmaxf(gamma[t0 + t], 1e-5f);
+  }
+#pragma unroll
+  for (int e = 0; e < 16; e += 2) {
+    uint16_t h[2][3];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int qe = (int)(int8_t)(qv[(e + u) >> 2] >> (8 * ((e + u) & 3)));
+      split3((ge * (float)qe) * (1.0f / 128.0f), h[u][0], h[u][1], h[u][2]);
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) S[p][t][8 * c + e / 2] = (uint32_t)h[0][p] | ((uint32_t)h[1][p] << 16);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const int w = tid + 256 * i, p = w >> 9, f = (w >> 3) & 63, c8 = w & 7;   // part p, feature k0 + f, tokens t0 + 8 c8 ..
+    const int sh = 16 * (f & 1);
+    u32x4 d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      d[j] = ((S[p][8 * c8 + 2 * j][f >> 1] >> sh) & 0xFFFFu) | (((S[p][8 * c8 + 2 * j + 1][f >> 1] >> sh) & 0xFFFFu) << 16);
+    *reinterpret_cast<u32x4*>(xt + (int64_t)p * k * mp + (k0 + f) * mp + t0 + 8 * c8) = d;
+  }
+}
+
+// Operands of a contraction D[i][j] = sum_p sum_l A[i][l] B[p][j][l]: rows of
+// A are i < ni (pitch lda; l < la_valid, a multiple of 8, else zero), rows of
+// B are j < nj (pitch ldb, parts plane elements apart); the contracted length
+// L is a multiple of 64 and B holds zeros wherever A's l is invalid.
+struct BwdGemm {
+  const uint16_t* a;
+  int64_t ni, lda, la_valid;
+  const uint16_t* b;
+  int64_t nj, ldb, plane;
+  int64_t L;
+  // epilogue: dX (EPI 0) or dW (EPI 1)
+  const float* beta;
+  const float* x;
+  const float* gamma;
+  float* out;
+  int64_t m_tok, k;
+};
+
+// 128 TI x 128 output tiles per workgroup of 4 TI waves (each 64 x 64: 2 x 2
+// MFMA tiles), 64 of the contracted index per LDS stage, the global loads of
+// the next D stages in flight in registers.  NB = 2 LDS buffers: a stage's
+// operands are written to one while the MFMAs read the other (one barrier per
+// stage); NB = 1: one buffer, refilled between two barriers, which halves the
+// LDS and lets two workgroups share a CU.  P parts of B share each A operand.
+// Tile order: the grid is 1-D over gx x gy tiles (gx along j).  Workgroup b
+// runs on XCD b % 8, and each XCD takes a contiguous run of tile numbers;
+// tile numbers walk groups of gm rows of tiles column by column, so that the
+// workgroups an XCD runs at once share both A and B tiles in its L2.
+template <int P, int TI, int EPI, int D, int NB>
+__global__ __launch_bounds__(kBT * TI) void bwd_gemm_kernel(const BwdGemm o, int gx, int gy, int gm) {
+  constexpr int kThr = kBT * TI, kTI = kTile * TI;
+  constexpr int kBPer = kTile * 8 / kThr;                  // B pieces per thread and part
+  __shared__ __attribute__((aligned(16))) uint16_t A_s[NB][kTI * kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t B_s[NB][P][kTile * kRow];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 31, g = lane >> 5;
+  const int wi = wave >> 1, wj = wave & 1;
+  const int nwg = (int)gridDim.x, xcd = (int)blockIdx.x & 7, per = nwg >> 3, rem = nwg & 7;
+  const int t = xcd * per + (xcd < rem ? xcd : rem) + ((int)blockIdx.x >> 3);
+  const int grp = t / (gm * gx), rr = t - grp * gm * gx;
+  const int rows = gy - grp * gm < gm ? gy - grp * gm : gm;
+  const int64_t i0 = (int64_t)(grp * gm + rr % rows) * kTI, j0 = (int64_t)(rr / rows) * kTile;
+  f32x16 acc[2][2] = {};
+  const int ar = tid >> 1, ah = tid & 1;                   // A: row i0 + ar, pieces l = 32 ah + 8 v
+  const bool a_row = i0 + ar < o.ni;
+  const uint16_t* pa = o.a + (a_row ? (i0 + ar) * o.lda : 0) + 32 * ah;
+  const uint16_t* pb[kBPer];
+  bool b_row[kBPer];
+#pragma unroll
+  for (int h = 0; h < kBPer; ++h) {
+    const int w = tid + kThr * h;
+    b_row[h] = j0 + (w >> 3) < o.nj;
+    pb[h] = o.b + (b_row[h] ? (j0 + (w >> 3)) * o.ldb : 0) + 8 * (w & 7);
+  }
+  u32x4 ra[D][4], rb[D][P][kBPer];
+  auto load_stage = [&](int64_t l0, int slot) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      ra[slot][v] = u32x4{0u, 0u, 0u, 0u};
+      if (a_row && l0 + 32 * ah + 8 * v < o.la_valid) ra[slot][v] = *reinterpret_cast<const u32x4*>(pa + l0 + 8 * v);
+    }
+#pragma unroll
+    for (int h = 0; h < kBPer; ++h)
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        rb[slot][p][h] = u32x4{0u, 0u, 0u, 0u};
+        if (b_row[h]) rb[slot][p][h] = *reinterpret_cast<const u32x4*>(pb[h] + p * o.plane + l0);
+      }
+  };
+  auto write_stage = [&](int buf, int slot) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) *reinterpret_cast<u32x4*>(A_s[buf] + ar * kRow + 32 * ah + 8 * v) = ra[slot][v];
+#pragma unroll
+    for (int h = 0; h < kBPer; ++h) {
+      const int w = tid + kThr * h;
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        *reinterpret_cast<u32x4*>(B_s[buf][p] + (w >> 3) * kRow + 8 * (w & 7)) = rb[slot][p][h];
+    }
+  };
+  const int nst = (int)(o.L / kStep);
+  // stage s travels in register set s % D; stage 0 goes to LDS first
+#pragma unroll
+  for (int s = 0; s < D; ++s)
+    if (s < nst) load_stage((int64_t)s * kStep, s);
+  write_stage(0, 0);
+  if (D < nst) load_stage((int64_t)D * kStep, 0);
+  lds_barrier();
+  for (int st0 = 0; st0 < nst; st0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int st = st0 + u;
+      if (st < nst) {
+        const int buf = NB == 2 ? st & 1 : 0;
+        if (NB == 2 && st + 1 < nst) {
+          write_stage(buf ^ 1, (u + 1) % D);               // stage st + 1; its buffer's readers passed the barrier
+          if (st + 1 + D < nst) load_stage((int64_t)(st + 1 + D) * kStep, (u + 1) % D);
+        }
+        if constexpr (P == 1) mma_stage(A_s[buf], B_s[buf][0], acc, wi, wj, li, g);
+        else mma_stage3(A_s[buf], B_s[buf], acc, wi, wj, li, g);
+        lds_barrier();
+        if (NB == 1 && st + 1 < nst) {                     // one buffer: refill it once every wave has read it
+          write_stage(0, (u + 1) % D);
+          if (st + 1 + D < nst) load_stage((int64_t)(st + 1 + D) * kStep, (u + 1) % D);
+          lds_barrier();
+        }
+      }
+    }
+  }
+  // lane (li, g) holds D[8 (v / 4) + 4 g + v % 4][li] of each 32 x 32 tile
+  const float b = EPI == 0 ? fmaxf(o.beta[0], 1e-5f) : 0.0f;
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t i = i0 + 64 * wi + 32 * ti + 8 * (v >> 2) + 4 * g + (v & 3);
+        const int64_t j = j0 + 64 * wj + 32 * tj + li;
+        if (i < o.ni && j < o.nj) {
+          if constexpr (EPI == 0) {                        // i = token, j = feature
+            const float s = fmaxf(o.gamma[i], 1e-5f) * (1.0f / 128.0f);   // exact power-of-two scaling
+            const float r = rintf(o.x[i * o.k + j] / s);                 // the forward's fp32 quotient
+            o.out[i * o.k + j] = fabsf(r) <= 127.0f ? b * acc[ti][tj][v] : 0.0f;
+          } else {                                         // i = output channel, j = feature
+            o.out[i * o.k + j] = acc[ti][tj][v];
+          }
+        }
+      }
+}
+
+// Register stages of loads, LDS buffers, token tiles per dX workgroup and
+// row groups of the tile order.  Measured on the 3B-class gate and down
+// matrices at 2048 tokens: the operands' LDS traffic per MFMA about equals
+// the matrix pipe's time, so what pays is two independent workgroups per CU,
+// whose barrier phases interleave (dW 488-496 us with one buffer against
+// 580-592 us with two, at one workgroup per CU); deeper register stages and
+// the grouped tile order changed dX by less than 2%.
+constexpr int kDxStages = 2, kDwStages = 1, kDxGroup = 4, kDwGroup = 8, kDxBuffers = 1, kDwBuffers = 1, kDxTI = 1;
+
+__host__ __device__ constexpr int64_t round64(int64_t v) { return (v + 63) / 64 * 64; }
+constexpr int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
+
 }  // namespace
+
+int64_t backward_ws_bytes(int64_t m_tok, int64_t n_out, int64_t k) {
+  const int64_t np = round64(n_out), mp = round64(m_tok);
+  return align256(k * np * 2) + align256(np * mp * 2) + align256(3 * k * mp * 2);
+}
+
+hipError_t launch_backward_ws(const BackwardArgs& a, void* ws, hipStream_t s) {
+  const int64_t np = round64(a.n_out), mp = round64(a.m_tok);
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  uint16_t* ct = reinterpret_cast<uint16_t*>(p);
+  uint16_t* dyt = reinterpret_cast<uint16_t*>(p + align256(a.k * np * 2));
+  uint16_t* xt = reinterpret_cast<uint16_t*>(p + align256(a.k * np * 2) + align256(np * mp * 2));
+  if (a.dx) {
+    PackedW W{a.packed, a.meta, a.n_out, (int32_t)(a.k / 64), a.fmt, a.n, a.m};
+    hipLaunchKernelGGL(bwd_codes_t_kernel, dim3((unsigned)(np / 64), (unsigned)(a.k / 64)), dim3(256), 0, s, W, np, ct);
+    BwdGemm o = {};
+    o.a = a.dy; o.ni = a.m_tok; o.lda = a.n_out; o.la_valid = a.n_out;
+    o.b = ct; o.nj = a.k; o.ldb = np; o.plane = 0; o.L = np;
+    o.beta = a.beta; o.x = a.x; o.gamma = a.gamma; o.out = a.dx; o.m_tok = a.m_tok; o.k = a.k;
+    constexpr int kTI = kDxTI;
+    const int gx = (int)((a.k + kTile - 1) / kTile), gy = (int)((a.m_tok + kTile * kTI - 1) / (kTile * kTI));
+    if ((int64_t)gx * gy * kBT * kTI >= ((int64_t)1 << 32)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_gemm_kernel<1, kTI, 0, kDxStages, kDxBuffers>), dim3((unsigned)(gx * gy)), dim3(kBT * kTI), 0, s, o,
+                       gx, gy, kDxGroup);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.dw) {
+    hipLaunchKernelGGL(bwd_dy_t_kernel, dim3((unsigned)(np / 64), (unsigned)(mp / 64)), dim3(256), 0, s, a.dy, a.m_tok,
+                       a.n_out, mp, dyt);
+    hipLaunchKernelGGL(bwd_xhat_t_kernel, dim3((unsigned)(a.k / 64), (unsigned)(mp / 64)), dim3(256), 0, s, a.xq,
+                       a.gamma, a.m_tok, a.k, mp, xt);
+    BwdGemm o = {};
+    o.a = dyt; o.ni = a.n_out; o.lda = mp; o.la_valid = mp;
+    o.b = xt; o.nj = a.k; o.ldb = mp; o.plane = a.k * mp; o.L = mp;
+    o.out = a.dw; o.m_tok = a.m_tok; o.k = a.k;
+    const int gx = (int)((a.k + kTile - 1) / kTile), gy = (int)((a.n_out + kTile - 1) / kTile);
+    if ((int64_t)gx * gy * kBT >= ((int64_t)1 << 32)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_gemm_kernel<3, 1, 1, kDwStages, kDwBuffers>), dim3((unsigned)(gx * gy)), dim3(kBT), 0, s, o, gx, gy,
+                       kDwGroup);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   if (a.dx) {

@@ -497,12 +497,16 @@ int sbl_linear_kgrouped(const uint8_t* packed, const uint8_t* meta, int32_t fmt,
                                                    reinterpret_cast<hipStream_t>(stream)));
 }
 
-int sbl_linear_backward(const uint16_t* dy_bf16, int64_t m_tok, int64_t n_out, int64_t k, const uint8_t* packed,
-                        const uint8_t* meta, int32_t fmt, int32_t n, int32_t m, const float* beta, const float* x,
-                        const int8_t* xq, const float* gamma, float* dx, float* dw, sbl_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// the argument checks of both backward entry points; SBL_OK with `a` filled
+int backward_args(const uint16_t* dy_bf16, int64_t m_tok, int64_t n_out, int64_t k, const uint8_t* packed,
+                  const uint8_t* meta, int32_t fmt, int32_t n, int32_t m, const float* beta, const float* x,
+                  const int8_t* xq, const float* gamma, float* dx, float* dw, sbl::BackwardArgs& a) {
   if (m_tok < 1 || m_tok > kMaxTokens || n_out < 8 || n_out % 8 != 0 || !k_ok(k) || n_out * k > kMaxElems)
     return SBL_ERR_SHAPE;
-  if (!dx && !dw) return SBL_OK;
   if (!dy_bf16 || !gamma) return SBL_ERR_NULL;
   if (dx) {
     if (!packed || !beta || !x) return SBL_ERR_NULL;
@@ -532,7 +536,6 @@ int sbl_linear_backward(const uint16_t* dy_bf16, int64_t m_tok, int64_t n_out, i
         (dw && ranges_overlap(outs[o], outb[o], xq, xqb)))
       return SBL_ERR_SHAPE;
   }
-  sbl::BackwardArgs a;
   a.dy = dy_bf16;
   a.m_tok = m_tok;
   a.n_out = n_out;
@@ -548,7 +551,58 @@ int sbl_linear_backward(const uint16_t* dy_bf16, int64_t m_tok, int64_t n_out, i
   a.gamma = gamma;
   a.dx = dx;
   a.dw = dw;
+  return SBL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sbl_linear_backward(const uint16_t* dy_bf16, int64_t m_tok, int64_t n_out, int64_t k, const uint8_t* packed,
+                        const uint8_t* meta, int32_t fmt, int32_t n, int32_t m, const float* beta, const float* x,
+                        const int8_t* xq, const float* gamma, float* dx, float* dw, sbl_stream stream) {
+  if (!dx && !dw) {
+    if (m_tok < 1 || m_tok > kMaxTokens || n_out < 8 || n_out % 8 != 0 || !k_ok(k) || n_out * k > kMaxElems)
+      return SBL_ERR_SHAPE;
+    return SBL_OK;
+  }
+  sbl::BackwardArgs a;
+  const int st = backward_args(dy_bf16, m_tok, n_out, k, packed, meta, fmt, n, m, beta, x, xq, gamma, dx, dw, a);
+  if (st != SBL_OK) return st;
   return launch_status(sbl::launch_backward(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int64_t sbl_backward_workspace_bytes(int64_t m_tok, int64_t n_out, int64_t k) {
+  if (m_tok < 1 || m_tok > kMaxTokens || n_out < 8 || n_out % 8 != 0 || !k_ok(k) || n_out * k > kMaxElems) return -1;
+  return sbl::backward_ws_bytes(m_tok, n_out, k);
+}
+
+int sbl_linear_backward_ws(const uint16_t* dy_bf16, int64_t m_tok, int64_t n_out, int64_t k, const uint8_t* packed,
+                           const uint8_t* meta, int32_t fmt, int32_t n, int32_t m, const float* beta, const float* x,
+                           const int8_t* xq, const float* gamma, float* dx, float* dw, void* workspace,
+                           int64_t workspace_bytes, sbl_stream stream) {
+  if (!dx && !dw) {
+    if (m_tok < 1 || m_tok > kMaxTokens || n_out < 8 || n_out % 8 != 0 || !k_ok(k) || n_out * k > kMaxElems)
+      return SBL_ERR_SHAPE;
+    return SBL_OK;
+  }
+  sbl::BackwardArgs a;
+  const int st = backward_args(dy_bf16, m_tok, n_out, k, packed, meta, fmt, n, m, beta, x, xq, gamma, dx, dw, a);
+  if (st != SBL_OK) return st;
+  if (!workspace) return SBL_ERR_NULL;
+  if (!aligned(workspace, 256)) return SBL_ERR_ALIGN;
+  const int64_t wb = sbl::backward_ws_bytes(m_tok, n_out, k);
+  if (workspace_bytes < wb) return SBL_ERR_SHAPE;
+  // the workspace must not overlap any input or output
+  const int64_t pb = fmt == SBL_FMT_NM && nm_ok(n, m) ? n_out * (k / m) * n / 4 : n_out * (k / 4);
+  if (ranges_overlap(workspace, wb, dy_bf16, m_tok * n_out * 2) || ranges_overlap(workspace, wb, gamma, m_tok * 4) ||
+      ranges_overlap(workspace, wb, dx, m_tok * k * 4) || ranges_overlap(workspace, wb, dw, n_out * k * 4) ||
+      (dx && (ranges_overlap(workspace, wb, x, m_tok * k * 4) || ranges_overlap(workspace, wb, packed, pb) ||
+              ranges_overlap(workspace, wb, beta, 4) ||
+              (fmt == SBL_FMT_NM && ranges_overlap(workspace, wb, meta, n_out * (k / 8))))) ||
+      (dw && ranges_overlap(workspace, wb, xq, m_tok * k)))
+    return SBL_ERR_SHAPE;
+  return launch_status(sbl::launch_backward_ws(a, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

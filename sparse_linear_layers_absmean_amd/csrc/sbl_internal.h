@@ -221,5 +221,8 @@ struct BackwardArgs {
   float* dw;                      // [n_out][k]
 };
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
+// the same gradients through a caller workspace of backward_ws_bytes bytes
+int64_t backward_ws_bytes(int64_t m_tok, int64_t n_out, int64_t k);
+hipError_t launch_backward_ws(const BackwardArgs& a, void* ws, hipStream_t s);
 
 }  // namespace sbl

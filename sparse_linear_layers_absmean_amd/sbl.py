@@ -24,7 +24,7 @@ SBL_FMT_NM = 1
 # weight-preparation variants and execution choices (sbl_quant_weights_batch_ex flags)
 SBL_QW_DEFAULT, SBL_QW_BETA_KEPT, SBL_QW_MASK_FROM_CODES = 0, 1, 2
 SBL_QW_TWO_PASS, SBL_QW_NO_WAIT = 4, 8
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32
@@ -116,6 +116,11 @@ def load():
     lib.sbl_linear_backward.restype = ctypes.c_int
     lib.sbl_linear_backward.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
                                         _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]
+    lib.sbl_backward_workspace_bytes.restype = ctypes.c_int64
+    lib.sbl_backward_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64]
+    lib.sbl_linear_backward_ws.restype = ctypes.c_int
+    lib.sbl_linear_backward_ws.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                                           _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p]
     if lib.sbl_abi_version() != ABI_VERSION:
         raise RuntimeError("libsbl.so ABI version mismatch: rebuild it")
     _lib = lib
@@ -349,15 +354,35 @@ def sbl_linear_kgrouped(packed, meta, fmt: int, n: int, m: int, beta, rows_per_g
     _check("sbl_linear_kgrouped", st)
 
 
+def sbl_backward_workspace_bytes(m_tok: int, n_out: int, k: int) -> int:
+    return load().sbl_backward_workspace_bytes(m_tok, n_out, k)
+
+
+def new_backward_workspace(m_tok: int, n_out: int, k: int, device="cuda"):
+    """Scratch for sbl_linear_backward(..., workspace=) at these sizes (any contents)."""
+    nbytes = sbl_backward_workspace_bytes(m_tok, n_out, k)
+    if nbytes < 0:
+        raise ValueError("unsupported shape")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def sbl_linear_backward(dy, packed, meta, fmt: int, n: int, m: int, beta, x, xq, gamma, dx=None, dw=None,
-                        stream=None):
+                        workspace=None, stream=None):
     """Backward of the layer (dual straight-through estimator): dy BF16 [m_tok][n_out];
-    dx fp32 [m_tok][k] and/or dw fp32 [n_out][k] outputs (either may be None)."""
+    dx fp32 [m_tok][k] and/or dw fp32 [n_out][k] outputs (either may be None).  With a
+    workspace (uint8, sbl_backward_workspace_bytes(m_tok, n_out, k) bytes) the call goes
+    to sbl_linear_backward_ws."""
     lib = load()
     m_tok, n_out = dy.shape
     k = (xq if xq is not None else x).shape[1]
     pb = lib.sbl_packed_bytes(n_out, k, n, m, fmt) if dx is not None else 0
-    st = lib.sbl_linear_backward(
+    if workspace is not None:
+        wsb = workspace.numel() * workspace.element_size()
+        fn, extra, name = lib.sbl_linear_backward_ws, (_ptr(workspace, None, wsb, "workspace"), wsb), \
+            "sbl_linear_backward_ws"
+    else:
+        fn, extra, name = lib.sbl_linear_backward, (), "sbl_linear_backward"
+    st = fn(
         _ptr(dy, _W16, m_tok * n_out * 2, "dy"), m_tok, n_out, k,
         _ptr(packed, torch.uint8, max(pb, 0), "packed") if dx is not None else None,
         _ptr(meta, torch.uint8, n_out * k // 8, "meta") if dx is not None and fmt == SBL_FMT_NM else None,
@@ -367,8 +392,8 @@ def sbl_linear_backward(dy, packed, meta, fmt: int, n: int, m: int, beta, x, xq,
         _ptr(xq, torch.int8, m_tok * k, "xq") if dw is not None else None,
         _ptr(gamma, torch.float32, m_tok * 4, "gamma"),
         _ptr(dx, torch.float32, m_tok * k * 4, "dx"), _ptr(dw, torch.float32, n_out * k * 4, "dw"),
-        _stream(stream))
-    _check("sbl_linear_backward", st)
+        *extra, _stream(stream))
+    _check(name, st)
 
 
 def sbl_linear_batch(items, fmt: int, n: int, m: int, stream=None):

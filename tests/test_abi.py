@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.sbl_abi_version() == 9
+    assert lib.sbl_abi_version() == 10
     for st in range(7):
         assert len(lib.sbl_status_string(st)) > 0
     assert lib.sbl_last_hip_error() == 0
@@ -306,6 +306,43 @@ def test_backward_validation(lib):
     assert call(dw=A + 7 * F + 64) == 2                    # overlaps dx
     assert call(dx=A + 16) == 2                            # overlaps dy
     assert call(dw=A + 5 * F + 16) == 2                    # overlaps xq
+
+
+def test_backward_workspace_sizes(lib):
+    # codes^T (k x n_out rounded up to 64), dy^T (both rounded up to 64), 3 parts of x_hat^T, 256-byte aligned
+    def ws(t, no, k):
+        np_, mp = -(-no // 64) * 64, -(-t // 64) * 64
+        return sum(-(-b // 256) * 256 for b in (2 * k * np_, 2 * np_ * mp, 6 * k * mp))
+    for t, no, k in [(4, 16, 64), (2048, 8640, 3200), (300, 520, 448), (1, 8, 64)]:
+        assert lib.sbl_backward_workspace_bytes(t, no, k) == ws(t, no, k)
+    assert lib.sbl_backward_workspace_bytes(0, 16, 64) == -1
+    assert lib.sbl_backward_workspace_bytes(4, 12, 64) == -1
+    assert lib.sbl_backward_workspace_bytes(4, 16, 96) == -1
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation runs only on GPU-less hosts")
+def test_backward_ws_validation(lib):
+    f = lib.sbl_linear_backward_ws
+    F = 1 << 40
+    wsb = lib.sbl_backward_workspace_bytes(4, 16, 64)
+
+    def call(dy=A, m_tok=4, n_out=16, k=64, packed=A + F, meta=A + 2 * F, fmt=1, n=6, beta=A + 3 * F,
+             x=A + 4 * F, xq=A + 5 * F, gamma=A + 6 * F, dx=A + 7 * F, dw=A + 8 * F, ws=A + 9 * F, nb=wsb):
+        return f(dy, m_tok, n_out, k, packed, meta, fmt, n, 8, beta, x, xq, gamma, dx, dw, ws, nb, None)
+
+    assert call(dx=None, dw=None) == 0                     # nothing asked: no-op
+    assert call(dx=None, dw=None, ws=None) == 0
+    assert call(m_tok=0) == 2
+    assert call(n_out=12) == 2
+    assert call(dy=None) == 1
+    assert call(ws=None) == 1
+    assert call(ws=A + 9 * F + 16) == 3                    # 256-byte alignment
+    assert call(nb=wsb - 1) == 2                           # too small
+    assert call(ws=A + 7 * F) == 2                         # overlaps dx
+    assert call(ws=A + 5 * F - 256) == 2                   # overlaps xq
+    assert call(ws=A + 8 * F + 256, dx=None) == 2          # overlaps dw
+    assert call(fmt=2) == 4
+    assert call(dw=A + 7 * F + 64) == 2                    # the plain call's checks hold too
 
 
 def test_grouped_workspace_sizes(lib):
