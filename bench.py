@@ -584,9 +584,10 @@ def bench_prefill(torch, np, sbl, dev, tm, masters_by_block, cases):
 
 def bench_train13b(torch, np, sbl, dev, tm, masters13):
     """The training-step path of a 13B-class block: per-step weight preparation from the
-    BF16 masters (exact beta, 6:8 mask with planted near-ties, codes, N:M packing) and
-    the forward products at 4096 tokens (activation quantization + GEMM per input).
-    Graph replays over 2 copies of masters and activations."""
+    BF16 masters (exact beta, 6:8 mask with planted near-ties, codes, N:M packing), the
+    forward products at 4096 tokens (activation quantization + GEMM per input) and the
+    layer's backward (dX and dW of every matrix from a synthetic BF16 dY).  Graph replays
+    over 2 copies of masters and activations."""
     import synth
     fmt, n, m = FORMATS["nm68"]
     mats = mats_of("13b")
@@ -606,6 +607,20 @@ def bench_train13b(torch, np, sbl, dev, tm, masters13):
         acts = [dict(xq=torch.empty((m_tok, x.shape[1]), dtype=torch.int8, device=dev),
                      gamma=torch.empty(m_tok, device=dev)) for x in xs]
         state.append((ms_, xs, outs, wss, acts))
+    # backward buffers, shared by the copies: dY per matrix, dX per input, dW per matrix
+    g = torch.Generator(device=dev).manual_seed(12)
+    dys = [(torch.randn((m_tok, no), generator=g, device=dev) * 0.05).to(torch.bfloat16) for _, no, k in mats]
+    dxs = [torch.empty((m_tok, k), device=dev) for _, no, k in mats]
+    dws = [torch.empty((no, k), device=dev) for _, no, k in mats]
+    bws = sbl.new_backward_workspace(m_tok, max(no for _, no, _k in mats), max(k for _, _n, k in mats), dev)
+    group_of = {i: gi for gi, grp in enumerate(GROUPS) for i in grp}
+
+    def bwd(c):
+        ms_, xs, outs, wss, acts = state[c]
+        for i in range(len(mats)):
+            gi = group_of[i]
+            sbl.sbl_linear_backward(dys[i], outs[i]["packed"], outs[i]["meta"], fmt, n, m, outs[i]["beta"], xs[gi],
+                                    acts[gi]["xq"], acts[gi]["gamma"], dx=dxs[i], dw=dws[i], workspace=bws)
 
     def prep(c):
         ms_, xs, outs, wss, acts = state[c]
@@ -622,20 +637,27 @@ def bench_train13b(torch, np, sbl, dev, tm, masters13):
     step_ms = timed_steps(torch, tm, lambda c: (prep(c), fwd(c)), copies, 10)
     prep_us = timed_steps(torch, tm, prep, copies, 20) * 1e3
     fwd_ms = timed_steps(torch, tm, fwd, copies, 10)
+    full_ms = timed_steps(torch, tm, lambda c: (prep(c), fwd(c), bwd(c)), copies, 4)
+    bwd_ms = timed_steps(torch, tm, bwd, copies, 4)
     weights = sum(no * k for _, no, k in mats)
     prep_alg = sum(2 * no * k + packed_bytes(sbl, no, k, n, m, fmt) for _, no, k in mats)
     ops = 2 * m_tok * weights
-    del state
+    del state, dys, dxs, dws, bws
     torch.cuda.empty_cache()
     return {"workload": f"Training-step path, {BLOCKS['13b'][3]}, 6:8 N:M, M=4096 tokens, "
                         "masters with near-ties planted on the keep boundary",
-            "ms_per_step": round(step_ms, 4), "weight_prep_us": round(prep_us, 1),
+            "ms_per_step": round(step_ms, 4),
+            "with_backward_ms_per_step": round(full_ms, 4), "backward_ms": round(bwd_ms, 4),
+            "backward_TFLOPS": round(2 * ops / (bwd_ms * 1e-3) / 1e12, 1),
+            "backward_frac": round(2 * ops / (bwd_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "weight_prep_us": round(prep_us, 1),
             "weight_prep_GBps": round(prep_alg / (prep_us * 1e-6) / 1e9, 1),
             "weight_prep_frac": round(prep_alg / (prep_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "forward_ms": round(fwd_ms, 4), "forward_int8_TOPS": round(ops / (fwd_ms * 1e-3) / 1e12, 1),
             "forward_frac": round(ops / (fwd_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
             "calls": "sbl_quant_weights_batch (7 matrices), then per input sbl_linear_acts_batch "
-                     "(quant_acts_kernel + gemm_kernel)"}
+                     "(quant_acts_kernel + gemm_kernel); with_backward adds per matrix "
+                     "sbl_linear_backward_ws (dX and dW, one shared workspace)"}
 
 
 # --------------------------------------------------------------------------- weight preparation sweep

@@ -466,6 +466,8 @@ __global__ __launch_bounds__(256) void bwd_xhat_t_kernel(const int8_t* __restric
   }
 }
 
+constexpr uint32_t kFarOff = 0x80000000u;   // a buffer offset past every buffer of this path: reads zeros
+
 // Operands of a contraction D[i][j] = sum_p sum_l A[i][l] B[p][j][l]: rows of
 // A are i < ni (pitch lda; l < la_valid, a multiple of 8, else zero), rows of
 // B are j < nj (pitch ldb, parts plane elements apart); the contracted length
@@ -508,31 +510,38 @@ __global__ __launch_bounds__(kBT * TI) void bwd_gemm_kernel(const BwdGemm o, int
   const int rows = gy - grp * gm < gm ? gy - grp * gm : gm;
   const int64_t i0 = (int64_t)(grp * gm + rr % rows) * kTI, j0 = (int64_t)(rr / rows) * kTile;
   f32x16 acc[2][2] = {};
+  // Buffer loads without branches (a load under a branch makes the compiler
+  // drain every load in flight before using any of them, which serialised
+  // the stages): resources over this tile's rows, so that rows past the end
+  // read zeros; pieces past A's valid l take an offset past every buffer.
   const int ar = tid >> 1, ah = tid & 1;                   // A: row i0 + ar, pieces l = 32 ah + 8 v
-  const bool a_row = i0 + ar < o.ni;
-  const uint16_t* pa = o.a + (a_row ? (i0 + ar) * o.lda : 0) + 32 * ah;
-  const uint16_t* pb[kBPer];
-  bool b_row[kBPer];
+  const int64_t a_rows = o.ni - i0 < kTI ? o.ni - i0 : kTI;
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(o.a + i0 * o.lda, a_rows * o.lda * 2);
+  const uint32_t voa = (uint32_t)(ar * o.lda + 32 * ah) * 2u;
+  const int64_t b_rows = o.nj - j0 < kTile ? o.nj - j0 : kTile;
+  __amdgpu_buffer_rsrc_t rsb[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) rsb[p] = make_rsrc(o.b + p * o.plane + j0 * o.ldb, b_rows * o.ldb * 2);
+  uint32_t vob[kBPer];
 #pragma unroll
   for (int h = 0; h < kBPer; ++h) {
     const int w = tid + kThr * h;
-    b_row[h] = j0 + (w >> 3) < o.nj;
-    pb[h] = o.b + (b_row[h] ? (j0 + (w >> 3)) * o.ldb : 0) + 8 * (w & 7);
+    vob[h] = (uint32_t)((w >> 3) * o.ldb + 8 * (w & 7)) * 2u;
   }
   u32x4 ra[D][4], rb[D][P][kBPer];
   auto load_stage = [&](int64_t l0, int slot) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      ra[slot][v] = u32x4{0u, 0u, 0u, 0u};
-      if (a_row && l0 + 32 * ah + 8 * v < o.la_valid) ra[slot][v] = *reinterpret_cast<const u32x4*>(pa + l0 + 8 * v);
+      const bool ok = l0 + 32 * ah + 8 * v < o.la_valid;
+      ra[slot][v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rsa, ok ? voa + (uint32_t)(l0 + 8 * v) * 2u : kFarOff, 0, 0));
     }
 #pragma unroll
     for (int h = 0; h < kBPer; ++h)
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        rb[slot][p][h] = u32x4{0u, 0u, 0u, 0u};
-        if (b_row[h]) rb[slot][p][h] = *reinterpret_cast<const u32x4*>(pb[h] + p * o.plane + l0);
-      }
+      for (int p = 0; p < P; ++p)
+        rb[slot][p][h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rsb[p], vob[h] + (uint32_t)l0 * 2u, 0, 0));
   };
   auto write_stage = [&](int buf, int slot) {
 #pragma unroll
@@ -546,34 +555,39 @@ __global__ __launch_bounds__(kBT * TI) void bwd_gemm_kernel(const BwdGemm o, int
     }
   };
   const int nst = (int)(o.L / kStep);
-  // stage s travels in register set s % D; stage 0 goes to LDS first
+  // Stage s travels in register set s % D; stage 0 goes to LDS first.  Loads
+  // of stages past the end read zeros or bytes nobody uses (buffer loads stay
+  // in bounds), so the refills need no branch.
 #pragma unroll
-  for (int s = 0; s < D; ++s)
-    if (s < nst) load_stage((int64_t)s * kStep, s);
+  for (int s = 0; s < D; ++s) load_stage((int64_t)s * kStep, s);
   write_stage(0, 0);
-  if (D < nst) load_stage((int64_t)D * kStep, 0);
+  load_stage((int64_t)D * kStep, 0);
   lds_barrier();
-  for (int st0 = 0; st0 < nst; st0 += D) {
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
-      const int st = st0 + u;
-      if (st < nst) {
-        const int buf = NB == 2 ? st & 1 : 0;
-        if (NB == 2 && st + 1 < nst) {
-          write_stage(buf ^ 1, (u + 1) % D);               // stage st + 1; its buffer's readers passed the barrier
-          if (st + 1 + D < nst) load_stage((int64_t)(st + 1 + D) * kStep, (u + 1) % D);
-        }
-        if constexpr (P == 1) mma_stage(A_s[buf], B_s[buf][0], acc, wi, wj, li, g);
-        else mma_stage3(A_s[buf], B_s[buf], acc, wi, wj, li, g);
-        lds_barrier();
-        if (NB == 1 && st + 1 < nst) {                     // one buffer: refill it once every wave has read it
-          write_stage(0, (u + 1) % D);
-          if (st + 1 + D < nst) load_stage((int64_t)(st + 1 + D) * kStep, (u + 1) % D);
-          lds_barrier();
-        }
-      }
+  // one stage: u = st mod D fixes the register set of stage st + 1
+  auto step = [&](int st, int u, bool last) {
+    const int buf = NB == 2 ? st & 1 : 0;
+    if (NB == 2 && !last) {
+      write_stage(buf ^ 1, (u + 1) % D);                   // stage st + 1; its buffer's readers passed the barrier
+      load_stage((int64_t)(st + 1 + D) * kStep, (u + 1) % D);
     }
+    if constexpr (P == 1) mma_stage(A_s[buf], B_s[buf][0], acc, wi, wj, li, g);
+    else mma_stage3(A_s[buf], B_s[buf], acc, wi, wj, li, g);
+    lds_barrier();
+    if (NB == 1 && !last) {                                // one buffer: refill it once every wave has read it
+      write_stage(0, (u + 1) % D);
+      load_stage((int64_t)(st + 1 + D) * kStep, (u + 1) % D);
+      lds_barrier();
+    }
+  };
+  // main loop: every stage has a successor; then the last ones
+  int st0 = 0;
+  for (; st0 + D < nst; st0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) step(st0 + u, u, false);
   }
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (st0 + u < nst) step(st0 + u, u, st0 + u + 1 == nst);
   // lane (li, g) holds D[8 (v / 4) + 4 g + v % 4][li] of each 32 x 32 tile
   const float b = EPI == 0 ? fmaxf(o.beta[0], 1e-5f) : 0.0f;
 #pragma unroll
