@@ -121,6 +121,10 @@ hipError_t launch_quant_acts(const float* x, int64_t m_tok, int64_t k, int8_t* x
                        q4, gamma);
   else if (m_tok < 128)
     hipLaunchKernelGGL((quant_acts_kernel<1024, 8>), dim3((unsigned)m_tok), dim3(1024), 0, s, x4, k / 4, q4, gamma);
+  else if (k <= 256 * 4 * 4)   // register slots sized to the row: fewer registers, more rows resident
+    hipLaunchKernelGGL((quant_acts_kernel<256, 4>), dim3((unsigned)m_tok), dim3(256), 0, s, x4, k / 4, q4, gamma);
+  else if (k <= 256 * 8 * 4)
+    hipLaunchKernelGGL((quant_acts_kernel<256, 8>), dim3((unsigned)m_tok), dim3(256), 0, s, x4, k / 4, q4, gamma);
   else
     hipLaunchKernelGGL((quant_acts_kernel<256, 16>), dim3((unsigned)m_tok), dim3(256), 0, s, x4, k / 4, q4, gamma);
   return hipGetLastError();

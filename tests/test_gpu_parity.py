@@ -132,6 +132,25 @@ def test_quant_acts_edge_rows():
     assert to_np(xq)[0, :8].tolist() == [127, 2, -2, 0, 127, -127, 1, 4]
 
 
+@pytest.mark.parametrize("k", [64, 3200, 4096, 4160, 8192, 8256, 16384, 16448, 28672])
+def test_quant_acts_many_tokens(k):
+    """At 128 tokens and more the quantizer sizes its per-thread register slots
+    by the row (rows up to 4096, 8192 and 16384 values, longer rows in two
+    sweeps): every variant and both sides of each boundary, bit for bit."""
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    m_tok = 130
+    x = synth.gaussian_acts(np.random.default_rng([14, k]), m_tok, k, hot_channels=4)
+    x[1] = 0.0
+    x[2, k - 1] = 50.0                                      # gamma from the row's last value
+    say(f"quant_acts {m_tok} x {k}")
+    xq, gamma = sbl.quant_acts(to_dev(x))
+    torch.cuda.synchronize()
+    q_ref, g_ref = O.quant_acts(x)
+    assert np.array_equal(to_np(gamma), g_ref)
+    assert np.array_equal(to_np(xq), q_ref)
+
+
 @pytest.mark.parametrize("n,m", [(6, 8), (2, 4), (5, 8), (8, 8)])
 def test_pack_standalone(n, m):
     import torch
