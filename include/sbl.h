@@ -420,7 +420,9 @@ int64_t sbl_backward_workspace_bytes(int64_t m_tok, int64_t n_out, int64_t k);
  *                    (else SBL_ERR_SHAPE); NULL: SBL_ERR_NULL.  Its contents
  *                    need no initialisation and are scratch after the call;
  *                    it must not overlap any input or output (SBL_ERR_SHAPE),
- *                    and calls in flight at the same time need their own. */
+ *                    and calls in flight at the same time need their own.
+ * Rows longer than 2^22 values (n_out or m_tok rounded up to 64) take the
+ * kernels of sbl_linear_backward and leave the workspace unused. */
 int sbl_linear_backward_ws(const uint16_t* dy_bf16, int64_t m_tok, int64_t n_out, int64_t k,
                            const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
                            const float* beta, const float* x, const int8_t* xq, const float* gamma,

@@ -632,6 +632,9 @@ int64_t backward_ws_bytes(int64_t m_tok, int64_t n_out, int64_t k) {
 
 hipError_t launch_backward_ws(const BackwardArgs& a, void* ws, hipStream_t s) {
   const int64_t np = round64(a.n_out), mp = round64(a.m_tok);
+  // the contraction's buffer resources span up to 256 rows of np or mp BF16
+  // values (32-bit sizes); beyond that the tile kernels need no workspace
+  if (256 * 2 * (np > mp ? np : mp) >= ((int64_t)1 << 31)) return launch_backward(a, s);
   uint8_t* p = static_cast<uint8_t*>(ws);
   uint16_t* ct = reinterpret_cast<uint16_t*>(p);
   uint16_t* dyt = reinterpret_cast<uint16_t*>(p + align256(a.k * np * 2));
