@@ -449,7 +449,7 @@ def gemv_sweep(torch, np, sbl, dev, tm):
     buffers; each block's 4 launches are one HIP graph."""
     # (block, tokens, one launch per matrix instead of the grouped launches)
     cases = [("0p7b", 1, False), ("3b", 1, False), ("3b", 4, False), ("3b", 8, False), ("70b", 1, False),
-             ("70b", 8, False), ("3b", 1, True), ("70b", 1, True)]
+             ("70b", 8, False), ("70b", 16, False), ("3b", 1, True), ("70b", 1, True)]
     out = []
     for blk, m_tok, single in cases:
         mats = mats_of(blk)

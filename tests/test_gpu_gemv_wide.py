@@ -1,6 +1,8 @@
-"""Decode GEMV on a 70B-class weight stream with 9 and 16 tokens: the launch
-streams 235M weights and stages m_tok x 8192 activation bytes (up to 128 KB)
-in LDS with LDS-direct loads.
+"""Decode GEMV on a 70B-class weight stream with 5-16 tokens: the launch
+streams 235M weights.  The gate/up shape stages m_tok x 8192 activation
+bytes (up to 128 KB) in LDS with LDS-direct loads; the down shape's token
+rows (28672 wide: up to 458 KB) do not fit, and every wave reads its k-blocks
+of them from memory.
 
 The packed weights are random valid codes written straight in the packed
 formats (this test is about the product alone); the oracle unpacks every
@@ -16,7 +18,6 @@ from oracle import sbl_oracle as O
 
 pytestmark = pytest.mark.gpu
 
-N_OUT, K = 28672, 8192
 
 
 def _random_fields(rng, nbytes):
@@ -31,12 +32,13 @@ def _random_bitmap(rng, nbytes):
     return pats[rng.integers(0, len(pats), nbytes)]
 
 
-@pytest.mark.parametrize("m_tok", [16, 9])
+@pytest.mark.parametrize("N_OUT,K,m_tok", [(28672, 8192, 16), (28672, 8192, 9),
+                                            (8192, 28672, 16), (8192, 28672, 9), (8192, 28672, 5)])
 @pytest.mark.parametrize("fmt", [FMT_DENSE2, FMT_NM])
-def test_wide_gemv_every_row(fmt, m_tok):
+def test_wide_gemv_every_row(fmt, N_OUT, K, m_tok):
     import torch
     from sparse_linear_layers_absmean_amd import sbl
-    rng = np.random.default_rng([41, fmt, m_tok])
+    rng = np.random.default_rng([41, fmt, m_tok, K])
     n, m = 6, 8
     if fmt == FMT_DENSE2:
         packed = _random_fields(rng, N_OUT * K // 4)
