@@ -468,6 +468,30 @@ __global__ __launch_bounds__(256) void bwd_xhat_t_kernel(const int8_t* __restric
 
 constexpr uint32_t kFarOff = 0x80000000u;   // a buffer offset past every buffer of this path: reads zeros
 
+// One LDS stage of a WTI x WTJ block of 32 x 32 MFMA tiles per wave, against
+// P parts of B (plane stride ps elements) that share each A operand.
+template <int WTI, int WTJ, int P>
+__device__ __forceinline__ void mma_block(const uint16_t* A_s, const uint16_t* B_s, int ps, f32x16 (&acc)[WTI][WTJ],
+                                          int i_off, int j_off, int li, int g) {
+#pragma unroll
+  for (int s = 0; s < kStep / 16; ++s) {
+    bf16x8 a[WTI];
+#pragma unroll
+    for (int t = 0; t < WTI; ++t) a[t] = lds_vec(A_s + (i_off + 32 * t + li) * kRow + 16 * s + 8 * g);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      bf16x8 b[WTJ];
+#pragma unroll
+      for (int t = 0; t < WTJ; ++t) b[t] = lds_vec(B_s + p * ps + (j_off + 32 * t + li) * kRow + 16 * s + 8 * g);
+#pragma unroll
+      for (int ti = 0; ti < WTI; ++ti)
+#pragma unroll
+        for (int tj = 0; tj < WTJ; ++tj)
+          acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ti], b[tj], acc[ti][tj], 0, 0, 0);
+    }
+  }
+}
+
 // Operands of a contraction D[i][j] = sum_p sum_l A[i][l] B[p][j][l]: rows of
 // A are i < ni (pitch lda; l < la_valid, a multiple of 8, else zero), rows of
 // B are j < nj (pitch ldb, parts plane elements apart); the contracted length
@@ -486,8 +510,9 @@ struct BwdGemm {
   int64_t m_tok, k;
 };
 
-// 128 TI x 128 output tiles per workgroup of 4 TI waves (each 64 x 64: 2 x 2
-// MFMA tiles), 64 of the contracted index per LDS stage, the global loads of
+// 64 TI WTI x 64 WTJ output tiles per workgroup of 4 TI waves (2 TI along i x
+// 2 along j, each a WTI x WTJ block of 32 x 32 MFMA tiles), 64 of the
+// contracted index per LDS stage, the global loads of
 // the next D stages in flight in registers.  NB = 2 LDS buffers: a stage's
 // operands are written to one while the MFMAs read the other (one barrier per
 // stage); NB = 1: one buffer, refilled between two barriers, which halves the
@@ -496,29 +521,36 @@ struct BwdGemm {
 // runs on XCD b % 8, and each XCD takes a contiguous run of tile numbers;
 // tile numbers walk groups of gm rows of tiles column by column, so that the
 // workgroups an XCD runs at once share both A and B tiles in its L2.
-template <int P, int TI, int EPI, int D, int NB>
+template <int P, int TI, int EPI, int D, int NB, int WTI, int WTJ>
 __global__ __launch_bounds__(kBT * TI) void bwd_gemm_kernel(const BwdGemm o, int gx, int gy, int gm) {
-  constexpr int kThr = kBT * TI, kTI = kTile * TI;
-  constexpr int kBPer = kTile * 8 / kThr;                  // B pieces per thread and part
+  constexpr int kThr = kBT * TI, kTI = 64 * TI * WTI, kTJ = 64 * WTJ;
+  constexpr int kAPer = kTI * 8 / kThr;                    // A pieces per thread
+  constexpr int kBPer = kTJ * 8 / kThr;                    // B pieces per thread and part
   __shared__ __attribute__((aligned(16))) uint16_t A_s[NB][kTI * kRow];
-  __shared__ __attribute__((aligned(16))) uint16_t B_s[NB][P][kTile * kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t B_s[NB][P][kTJ * kRow];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 31, g = lane >> 5;
   const int wi = wave >> 1, wj = wave & 1;
   const int nwg = (int)gridDim.x, xcd = (int)blockIdx.x & 7, per = nwg >> 3, rem = nwg & 7;
   const int t = xcd * per + (xcd < rem ? xcd : rem) + ((int)blockIdx.x >> 3);
   const int grp = t / (gm * gx), rr = t - grp * gm * gx;
   const int rows = gy - grp * gm < gm ? gy - grp * gm : gm;
-  const int64_t i0 = (int64_t)(grp * gm + rr % rows) * kTI, j0 = (int64_t)(rr / rows) * kTile;
-  f32x16 acc[2][2] = {};
+  const int64_t i0 = (int64_t)(grp * gm + rr % rows) * kTI, j0 = (int64_t)(rr / rows) * kTJ;
+  f32x16 acc[WTI][WTJ] = {};
   // Buffer loads without branches (a load under a branch makes the compiler
   // drain every load in flight before using any of them, which serialised
   // the stages): resources over this tile's rows, so that rows past the end
   // read zeros; pieces past A's valid l take an offset past every buffer.
-  const int ar = tid >> 1, ah = tid & 1;                   // A: row i0 + ar, pieces l = 32 ah + 8 v
+  // piece w of a tile (A or B) = row w / 8, l = 8 (w % 8) .. +7 of the stage;
+  // thread t holds pieces t, t + kThr, ...
   const int64_t a_rows = o.ni - i0 < kTI ? o.ni - i0 : kTI;
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(o.a + i0 * o.lda, a_rows * o.lda * 2);
-  const uint32_t voa = (uint32_t)(ar * o.lda + 32 * ah) * 2u;
-  const int64_t b_rows = o.nj - j0 < kTile ? o.nj - j0 : kTile;
+  uint32_t voa[kAPer];
+#pragma unroll
+  for (int h = 0; h < kAPer; ++h) {
+    const int w = tid + kThr * h;
+    voa[h] = (uint32_t)((w >> 3) * o.lda + 8 * (w & 7)) * 2u;
+  }
+  const int64_t b_rows = o.nj - j0 < kTJ ? o.nj - j0 : kTJ;
   __amdgpu_buffer_rsrc_t rsb[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) rsb[p] = make_rsrc(o.b + p * o.plane + j0 * o.ldb, b_rows * o.ldb * 2);
@@ -528,13 +560,13 @@ __global__ __launch_bounds__(kBT * TI) void bwd_gemm_kernel(const BwdGemm o, int
     const int w = tid + kThr * h;
     vob[h] = (uint32_t)((w >> 3) * o.ldb + 8 * (w & 7)) * 2u;
   }
-  u32x4 ra[D][4], rb[D][P][kBPer];
+  u32x4 ra[D][kAPer], rb[D][P][kBPer];
   auto load_stage = [&](int64_t l0, int slot) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const bool ok = l0 + 32 * ah + 8 * v < o.la_valid;
-      ra[slot][v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rsa, ok ? voa + (uint32_t)(l0 + 8 * v) * 2u : kFarOff, 0, 0));
+    for (int h = 0; h < kAPer; ++h) {
+      const bool ok = l0 + 8 * ((tid + kThr * h) & 7) < o.la_valid;
+      ra[slot][h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rsa, ok ? voa[h] + (uint32_t)l0 * 2u : kFarOff, 0, 0));
     }
 #pragma unroll
     for (int h = 0; h < kBPer; ++h)
@@ -545,7 +577,10 @@ __global__ __launch_bounds__(kBT * TI) void bwd_gemm_kernel(const BwdGemm o, int
   };
   auto write_stage = [&](int buf, int slot) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) *reinterpret_cast<u32x4*>(A_s[buf] + ar * kRow + 32 * ah + 8 * v) = ra[slot][v];
+    for (int h = 0; h < kAPer; ++h) {
+      const int w = tid + kThr * h;
+      *reinterpret_cast<u32x4*>(A_s[buf] + (w >> 3) * kRow + 8 * (w & 7)) = ra[slot][h];
+    }
 #pragma unroll
     for (int h = 0; h < kBPer; ++h) {
       const int w = tid + kThr * h;
@@ -570,8 +605,7 @@ __global__ __launch_bounds__(kBT * TI) void bwd_gemm_kernel(const BwdGemm o, int
       write_stage(buf ^ 1, (u + 1) % D);                   // stage st + 1; its buffer's readers passed the barrier
       load_stage((int64_t)(st + 1 + D) * kStep, (u + 1) % D);
     }
-    if constexpr (P == 1) mma_stage(A_s[buf], B_s[buf][0], acc, wi, wj, li, g);
-    else mma_stage3(A_s[buf], B_s[buf], acc, wi, wj, li, g);
+    mma_block<WTI, WTJ, P>(A_s[buf], B_s[buf][0], kTJ * kRow, acc, 32 * WTI * wi, 32 * WTJ * wj, li, g);
     lds_barrier();
     if (NB == 1 && !last) {                                // one buffer: refill it once every wave has read it
       write_stage(0, (u + 1) % D);
@@ -591,13 +625,13 @@ __global__ __launch_bounds__(kBT * TI) void bwd_gemm_kernel(const BwdGemm o, int
   // lane (li, g) holds D[8 (v / 4) + 4 g + v % 4][li] of each 32 x 32 tile
   const float b = EPI == 0 ? fmaxf(o.beta[0], 1e-5f) : 0.0f;
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti)
+  for (int ti = 0; ti < WTI; ++ti)
 #pragma unroll
-    for (int tj = 0; tj < 2; ++tj)
+    for (int tj = 0; tj < WTJ; ++tj)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t i = i0 + 64 * wi + 32 * ti + 8 * (v >> 2) + 4 * g + (v & 3);
-        const int64_t j = j0 + 64 * wj + 32 * tj + li;
+        const int64_t i = i0 + 32 * WTI * wi + 32 * ti + 8 * (v >> 2) + 4 * g + (v & 3);
+        const int64_t j = j0 + 32 * WTJ * wj + 32 * tj + li;
         if (i < o.ni && j < o.nj) {
           if constexpr (EPI == 0) {                        // i = token, j = feature
             const float s = fmaxf(o.gamma[i], 1e-5f) * (1.0f / 128.0f);   // exact power-of-two scaling
@@ -610,15 +644,16 @@ __global__ __launch_bounds__(kBT * TI) void bwd_gemm_kernel(const BwdGemm o, int
       }
 }
 
-// Register stages of loads, LDS buffers, token tiles per dX workgroup and
-// row groups of the tile order.  Measured on the 3B-class gate and down
-// matrices at 2048 tokens: the operands' LDS traffic per MFMA about equals
-// the matrix pipe's time, so what pays is two independent workgroups per CU,
-// whose barrier phases interleave (dW 488-496 us with one buffer against
-// 580-592 us with two, at one workgroup per CU); deeper register stages and
-// the grouped tile order changed dX by less than 2%.
+// Register stages of loads, LDS buffers, token tiles per dX workgroup, MFMA
+// tiles per wave and row groups of the tile order.  Measured on the 3B-class
+// gate and down matrices at 2048 tokens (and the 13B-class ones at 4096):
+// what pays is two independent workgroups per CU, whose barrier phases
+// interleave (dW 488-496 us with one buffer against 580-592 us with two, at
+// one workgroup per CU); deeper register stages and the grouped tile order
+// changed dX by less than 2%; 4 x 2 or 2 x 4 MFMA tiles per wave (over 256
+// VGPRs: one workgroup per CU) were 10-50% slower.
 constexpr int kDxStages = 2, kDwStages = 1, kDxGroup = 4, kDwGroup = 8, kDxBuffers = 1, kDwBuffers = 1, kDxTI = 1,
-              kDwTI = 1;
+              kDwTI = 1, kDxWTI = 2, kDxWTJ = 2, kDwWTI = 2, kDwWTJ = 2;
 
 __host__ __device__ constexpr int64_t round64(int64_t v) { return (v + 63) / 64 * 64; }
 constexpr int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
@@ -646,11 +681,11 @@ hipError_t launch_backward_ws(const BackwardArgs& a, void* ws, hipStream_t s) {
     o.a = a.dy; o.ni = a.m_tok; o.lda = a.n_out; o.la_valid = a.n_out;
     o.b = ct; o.nj = a.k; o.ldb = np; o.plane = 0; o.L = np;
     o.beta = a.beta; o.x = a.x; o.gamma = a.gamma; o.out = a.dx; o.m_tok = a.m_tok; o.k = a.k;
-    constexpr int kTI = kDxTI;
-    const int gx = (int)((a.k + kTile - 1) / kTile), gy = (int)((a.m_tok + kTile * kTI - 1) / (kTile * kTI));
+    constexpr int kTI = kDxTI, kRi = 64 * kTI * kDxWTI, kRj = 64 * kDxWTJ;
+    const int gx = (int)((a.k + kRj - 1) / kRj), gy = (int)((a.m_tok + kRi - 1) / kRi);
     if ((int64_t)gx * gy * kBT * kTI >= ((int64_t)1 << 32)) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_gemm_kernel<1, kTI, 0, kDxStages, kDxBuffers>), dim3((unsigned)(gx * gy)), dim3(kBT * kTI), 0, s, o,
-                       gx, gy, kDxGroup);
+    hipLaunchKernelGGL((bwd_gemm_kernel<1, kTI, 0, kDxStages, kDxBuffers, kDxWTI, kDxWTJ>), dim3((unsigned)(gx * gy)),
+                       dim3(kBT * kTI), 0, s, o, gx, gy, kDxGroup);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -663,11 +698,11 @@ hipError_t launch_backward_ws(const BackwardArgs& a, void* ws, hipStream_t s) {
     o.a = dyt; o.ni = a.n_out; o.lda = mp; o.la_valid = mp;
     o.b = xt; o.nj = a.k; o.ldb = mp; o.plane = a.k * mp; o.L = mp;
     o.out = a.dw; o.m_tok = a.m_tok; o.k = a.k;
-    constexpr int kTI = kDwTI;
-    const int gx = (int)((a.k + kTile - 1) / kTile), gy = (int)((a.n_out + kTile * kTI - 1) / (kTile * kTI));
+    constexpr int kTI = kDwTI, kRi = 64 * kTI * kDwWTI, kRj = 64 * kDwWTJ;
+    const int gx = (int)((a.k + kRj - 1) / kRj), gy = (int)((a.n_out + kRi - 1) / kRi);
     if ((int64_t)gx * gy * kBT * kTI >= ((int64_t)1 << 32)) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_gemm_kernel<3, kTI, 1, kDwStages, kDwBuffers>), dim3((unsigned)(gx * gy)), dim3(kBT * kTI), 0, s,
-                       o, gx, gy, kDwGroup);
+    hipLaunchKernelGGL((bwd_gemm_kernel<3, kTI, 1, kDwStages, kDwBuffers, kDwWTI, kDwWTJ>), dim3((unsigned)(gx * gy)),
+                       dim3(kBT * kTI), 0, s, o, gx, gy, kDwGroup);
   }
   return hipGetLastError();
 }
