@@ -869,7 +869,7 @@ def bench_group_scales(torch, np, sbl, dev, tm, rpg=128, kg=320, n=6, m=8):
                                     gq[i][0], gq[i][1], kg, no, ys[i])
 
     for name, fn, what in (("sbl_linear", plain, "per-matrix beta and gamma (one launch per matrix)"),
-                           ("sbl_linear_grouped", grouped, f"beta per {rpg} rows: GEMV + grouped rescale"),
+                           ("sbl_linear_grouped", grouped, f"beta per {rpg} rows, read by the GEMV epilogue"),
                            ("sbl_linear_kgrouped", kgrouped,
                             f"beta per {rpg} rows, gamma per {kg} features: activation quant + product")):
         us = timed_steps(torch, tm, fn, pcopies, max(20, 2 * pcopies)) * 1e3

@@ -341,8 +341,11 @@ int sbl_quant_weights_grouped(const uint16_t* w_bf16, int64_t n_out, int64_t k, 
 /* sbl_linear with one beta per row group:
  *   y[t][r] = RN(fp32(acc[t][r]) * RN(RN(beta_eff[r / rows_per_group] *
  *             gamma_eff[t]) * 2^-7)).
- *   acc        [m_tok][n_out] int32, REQUIRED (written: the exact products).
- * Validation as sbl_linear; rows_per_group < 1 gives SBL_ERR_SHAPE. */
+ *   beta       [ceil(n_out / rows_per_group)] fp32 (sbl_quant_weights_grouped).
+ *   acc        [m_tok][n_out] int32, nullable (the exact products).
+ * The same kernels as sbl_linear, whose epilogues read beta per row.
+ * Validation as sbl_linear; rows_per_group < 1 gives SBL_ERR_SHAPE, and y
+ * and acc must not overlap beta. */
 int sbl_linear_grouped(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
                        const float* beta, int64_t rows_per_group, const int8_t* xq, const float* gamma,
                        int64_t m_tok, int64_t n_out, int64_t k, float* y, int32_t* acc, sbl_stream stream);

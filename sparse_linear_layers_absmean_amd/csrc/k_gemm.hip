@@ -164,7 +164,7 @@ __device__ __forceinline__ v4i decode_w(const WRaw<KIND>& a, int j, const NmLut&
 // latencies hide behind the other's matrix work (256 x 128 tiles: +10% at
 // 2048 tokens; 256 x 256 DENSE2 as 8 waves of 64 x 128: +2% at 2048 and +6%
 // at 4096 tokens against 4 waves of 64 x 256).
-template <int KIND, int KRT, int KCT, int WT>
+template <int KIND, int KRT, int KCT, int WT, bool GRP = false>
 __global__ __launch_bounds__(kThreads * WT, KRT * KCT * WT >= 16 ? 1 : 2) void gemm_kernel(const LinBatch batch) {
   constexpr int kRT = KRT, kCT = KCT;
   constexpr int kThr = kThreads * WT;               // 4 waves along the rows x WT along the tokens
@@ -327,8 +327,10 @@ __global__ __launch_bounds__(kThreads * WT, KRT * KCT * WT >= 16 ? 1 : 2) void g
       if (st_chunk == 0) qsum_lds[st_tok + kTokPass * p] = v;
     }
   }
-  // output scale per token of the tile
-  for (int i = tid; i < kBN; i += kThr) scale_lds[i] = t0 + i < d.m_tok ? out_scale(d.beta, d.gamma, t0 + i) : 0.0f;
+  // output scale per token of the tile; with beta per row group (group
+  // scales) the token's max(gamma, 1e-5), the scale being formed per row
+  for (int i = tid; i < kBN; i += kThr)
+    scale_lds[i] = t0 + i >= d.m_tok ? 0.0f : GRP ? fmaxf(d.gamma[t0 + i], 1e-5f) : out_scale(d.beta, d.gamma, t0 + i);
   __syncthreads();
   // epilogue: the MFMAs take the activations as A and the weights as B, so
   // lane (li, g) holds C[token 8*(v/4) + 4g + v%4][row li] of each 32 x 32
@@ -350,6 +352,15 @@ __global__ __launch_bounds__(kThreads * WT, KRT * KCT * WT >= 16 ? 1 : 2) void g
     vo[rt] = row < d.n_out ? (uint32_t)row * 4u + (uint32_t)(4 * g) * tokb : kFar;
   }
   auto store_all = [&](auto with_acc) {
+    // group scales: max(beta, 1e-5) of each row tile's row (rows past n_out take the last row's)
+    float brow[kRT];
+    if constexpr (GRP) {
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+        const int64_t row = n0 + 32 * kRT * wave + 32 * rt + li;
+        brow[rt] = fmaxf(*row_beta(d.beta, d.beta_rows, row < d.n_out ? row : d.n_out - 1), 1e-5f);
+      }
+    }
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) {
 #pragma unroll
@@ -367,7 +378,9 @@ __global__ __launch_bounds__(kThreads * WT, KRT * KCT * WT >= 16 ? 1 : 2) void g
 #pragma unroll
           for (int rt = 0; rt < kRT; ++rt) {
             const int32_t a = acc[rt][ct][v] - cqj[j];
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((float)a * scj[j]), ry, vo[rt], so, 0);
+            float sc = scj[j];
+            if constexpr (GRP) sc = (brow[rt] * scj[j]) * 0.0078125f;   // RN(RN(beta*gamma)*2^-7)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((float)a * sc), ry, vo[rt], so, 0);
             if constexpr (decltype(with_acc)::value) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)a, ra, vo[rt], so, 0);
           }
         }
@@ -421,7 +434,7 @@ bool gemm_fits(const LinearArgs& a, int kind) {
 
 namespace {
 
-template <int KRT, int KCT, int WT = 1>
+template <int KRT, int KCT, int WT = 1, bool GRP = false>
 hipError_t launch_shape(const LinearArgs* items, int count, int kind, hipStream_t s) {
   constexpr int kBM = 4 * 32 * KRT, kBN = 32 * KCT * WT;
   LinBatch b = {};
@@ -436,8 +449,8 @@ hipError_t launch_shape(const LinearArgs* items, int count, int kind, hipStream_
   b.count = count;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(kThreads * WT);
-  if (kind == kDense2) hipLaunchKernelGGL((gemm_kernel<kDense2, KRT, KCT, WT>), grid, block, 0, s, b);
-  else hipLaunchKernelGGL((gemm_kernel<kNm68, KRT, KCT, WT>), grid, block, 0, s, b);
+  if (kind == kDense2) hipLaunchKernelGGL((gemm_kernel<kDense2, KRT, KCT, WT, GRP>), grid, block, 0, s, b);
+  else hipLaunchKernelGGL((gemm_kernel<kNm68, KRT, KCT, WT, GRP>), grid, block, 0, s, b);
   return hipGetLastError();
 }
 
@@ -445,6 +458,9 @@ hipError_t launch_shape(const LinearArgs* items, int count, int kind, hipStream_
 
 hipError_t launch_gemm_group(const LinearArgs* items, int count, int kind, hipStream_t s) {
   if (kind == kNm24) return launch_gemm24_group(items, count, s);
+  // group scales (beta per row block): one tile shape, with the epilogue that
+  // reads beta per row
+  if (items[0].beta_rows > 0) return launch_shape<1, 4, 1, true>(items, count, kind, s);
   switch (pick_shape(items, count, kind)) {
     // 256 x 256: DENSE2 as 8 waves (4 along the rows x 2 along the tokens,
     // 64 x 128 each, two waves per SIMD; each row's cheap decode done by two

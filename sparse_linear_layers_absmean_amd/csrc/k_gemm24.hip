@@ -82,7 +82,7 @@ __device__ __forceinline__ int sparse_index(uint32_t x) {
 }
 
 // 4 waves along the rows; KRT 16-row tiles and KCT 16-token tiles per wave.
-template <int KRT, int KCT>
+template <int KRT, int KCT, bool GRP = false>
 __global__ __launch_bounds__(kThreads, 2) void gemm24_kernel(const LinBatch batch) {
   constexpr int kBM = 4 * 16 * KRT;                 // weight rows per workgroup
   constexpr int kBN = 16 * KCT;                     // tokens per workgroup (every wave sees all)
@@ -239,7 +239,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm24_kernel(const LinBatch batc
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         a4[j] = acc[rt][ct][j];
-        y4[j] = (float)a4[j] * s;
+        if constexpr (GRP) {   // group scales: beta of each row (rows past n_out take the last row's)
+          const int64_t rj = row + j < d.n_out ? row + j : d.n_out - 1;
+          y4[j] = (float)a4[j] * out_scale_g(row_beta(d.beta, d.beta_rows, rj), d.gamma[t]);
+        } else {
+          y4[j] = (float)a4[j] * s;
+        }
       }
       if (row + 3 < d.n_out && ((t * d.n_out + row) & 3) == 0) {
         *reinterpret_cast<float4*>(yrow + row) = make_float4(y4[0], y4[1], y4[2], y4[3]);
@@ -257,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm24_kernel(const LinBatch batc
   }
 }
 
-template <int KRT, int KCT>
+template <int KRT, int KCT, bool GRP = false>
 hipError_t launch24(const LinearArgs* items, int count, hipStream_t s) {
   constexpr int kBM = 4 * 16 * KRT, kBN = 16 * KCT;
   LinBatch b = {};
@@ -271,13 +276,14 @@ hipError_t launch24(const LinearArgs* items, int count, hipStream_t s) {
   b.start[count] = blocks;
   b.count = count;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm24_kernel<KRT, KCT>), dim3((unsigned)blocks), dim3(kThreads), 0, s, b);
+  hipLaunchKernelGGL((gemm24_kernel<KRT, KCT, GRP>), dim3((unsigned)blocks), dim3(kThreads), 0, s, b);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm24_group(const LinearArgs* items, int count, hipStream_t s) {
+  if (items[0].beta_rows > 0) return launch24<4, 8, true>(items, count, s);   // group scales
   return launch24<4, 8>(items, count, s);
 }
 

@@ -9,10 +9,10 @@
 //    group g's rows exactly (sbl_partial.h) into slot w of the group's
 //    workspace region; every group uses the partition of a full group.
 //  * group_final_kernel: one workgroup per group rounds the exact mean once
-//    (sbl_beta.h) into beta[g].
-//  * The mask/pack kernel then reads beta per row group (QDesc.beta_rows).
-//  * rescale_grouped_kernel: the products' epilogue with beta per row group,
-//    from the int32 products.
+//    (sbl_beta.h) into beta[g]; a group whose masters fit one absmean
+//    workgroup is rounded by that workgroup instead (no second launch).
+//  * The mask/pack kernel then reads beta per row group (QDesc.beta_rows), and
+//    the products' epilogues do too (LinearArgs.beta_rows).
 #include "sbl_partial.h"
 
 namespace sbl {
@@ -23,7 +23,7 @@ using namespace part;
 
 __global__ __launch_bounds__(kAbsThreads) void group_partial_kernel(const u32x4* __restrict__ w, int64_t n_out,
                                                                     int64_t k, int64_t rpg, GroupPlan plan,
-                                                                    uint64_t* ws) {
+                                                                    uint64_t* ws, float* beta) {
   const int64_t g = blockIdx.y, wg = blockIdx.x;
   const int64_t r0 = g * rpg;
   const int64_t rows = n_out - r0 < rpg ? n_out - r0 : rpg;
@@ -48,6 +48,21 @@ __global__ __launch_bounds__(kAbsThreads) void group_partial_kernel(const u32x4*
     for (int u = 0; u < 8; ++u) consume(v[u], acc0, acc1, bins, rare);
   }
   publish_partial(ws + g * plan.region, plan.nb, wg, acc0, acc1, rare, bins);
+  if (plan.nb == 1) {
+    // the group's only partial sum is this workgroup's: round the exact mean
+    // here (thread 0's workspace stores are visible to the workgroup after
+    // the barrier)
+    __syncthreads();
+    QDesc d = {};
+    d.w = w + r0 * k / 8;
+    d.nvec = nvec;
+    d.count = rows * k;
+    d.nb = 1;
+    d.vpt = plan.vpt;
+    d.ws = ws + g * plan.region;
+    d.beta = beta + g;
+    (void)beta::workgroup_beta(d, true);
+  }
 }
 
 __global__ __launch_bounds__(kAbsThreads) void group_final_kernel(const u32x4* w, int64_t n_out, int64_t k,
@@ -64,17 +79,6 @@ __global__ __launch_bounds__(kAbsThreads) void group_final_kernel(const u32x4* w
   d.ws = ws + g * plan.region;
   d.beta = beta + g;
   (void)beta::workgroup_beta(d, true);
-}
-
-__global__ void rescale_grouped_kernel(const int32_t* __restrict__ acc, const float* __restrict__ beta, int64_t rpg,
-                                       const float* __restrict__ gamma, int64_t m_tok, int64_t n_out,
-                                       float* __restrict__ y) {
-  const int64_t total = m_tok * n_out, stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const int64_t t = i / n_out, r = i - t * n_out;
-    const float s = (fmaxf(beta[r / rpg], 1e-5f) * fmaxf(gamma[t], 1e-5f)) * (1.0f / 128.0f);
-    y[i] = (float)acc[i] * s;
-  }
 }
 
 // Activation groups along k: workgroup (j, t) quantizes features
@@ -251,19 +255,11 @@ hipError_t launch_grouped_beta(const uint16_t* w, int64_t n_out, int64_t k, int6
   const int64_t rpg = rows_per_group < n_out ? rows_per_group : n_out;
   const u32x4* wv = reinterpret_cast<const u32x4*>(w);
   hipLaunchKernelGGL(group_partial_kernel, dim3((unsigned)plan.nb, (unsigned)plan.groups), dim3(kAbsThreads), 0, s,
-                     wv, n_out, k, rpg, plan, ws);
-  hipLaunchKernelGGL(group_final_kernel, dim3((unsigned)plan.groups), dim3(kAbsThreads), 0, s, wv, n_out, k, rpg,
-                     plan, ws, beta);
-  return hipGetLastError();
-}
-
-hipError_t launch_rescale_grouped(const int32_t* acc, const float* beta, int64_t rows_per_group, const float* gamma,
-                                  int64_t m_tok, int64_t n_out, float* y, hipStream_t s) {
-  const int64_t total = m_tok * n_out;
-  int64_t blocks = (total + 255) / 256;
-  blocks = blocks < 1 ? 1 : (blocks > 65536 ? 65536 : blocks);
-  hipLaunchKernelGGL(rescale_grouped_kernel, dim3((unsigned)blocks), dim3(256), 0, s, acc, beta, rows_per_group, gamma,
-                     m_tok, n_out, y);
+                     wv, n_out, k, rpg, plan, ws, beta);
+  // groups of one absmean workgroup were finalized by it
+  if (plan.nb > 1)
+    hipLaunchKernelGGL(group_final_kernel, dim3((unsigned)plan.groups), dim3(kAbsThreads), 0, s, wv, n_out, k, rpg,
+                       plan, ws, beta);
   return hipGetLastError();
 }
 

@@ -460,7 +460,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
     }
   }
   if (t >= d.m_tok || row0 >= d.n_out) return;
-  const float sc = XF ? out_scale_g(d.beta, __uint_as_float(gbits[t])) : out_scale(d.beta, d.gamma, t);
+  const float gt = XF ? __uint_as_float(gbits[t]) : d.gamma[t];
+  const float sc = out_scale_g(d.beta, gt);
   const int32_t qt = XL ? qs[t] : 0;
   const int64_t rbase = row0 + 4 * g;
   float* yrow = d.y + (int64_t)t * d.n_out;
@@ -470,7 +471,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvLaunch L
     const int64_t row = rbase + v;
     if ((ks == 1 || v % ks == slice) && row < d.n_out) {
       const int32_t a = c[v] - qt;
-      yrow[row] = (float)a * sc;
+      const float sr = d.beta_rows > 0 ? out_scale_g(row_beta(d.beta, d.beta_rows, row), gt) : sc;
+      yrow[row] = (float)a * sr;
       if (arow) arow[row] = a;
     }
   }
@@ -518,7 +520,8 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(const uint8_t* __re
                                                              const float* __restrict__ gamma,
                                                              int64_t m_tok, int64_t n_out, int64_t k,
                                                              float* __restrict__ y,
-                                                             int32_t* __restrict__ acc_out) {
+                                                             int32_t* __restrict__ acc_out,
+                                                             int32_t beta_rows) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row0 = (int64_t)blockIdx.x * 64 + wave * 16;
   const int64_t tok0 = (int64_t)blockIdx.y * 16;
@@ -549,13 +552,12 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(const uint8_t* __re
   qs += __shfl_xor(qs, 16, 64);
   qs += __shfl_xor(qs, 32, 64);
   if (!tok_ok) return;
-  const float s = out_scale(beta, gamma, t);
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int64_t row = row0 + 4 * g + v;            // C[4*(lane/16)+v][lane%16]
     if (row < n_out) {
       const int32_t a = c[v] - (FMT == 0 ? qs : 0);
-      y[t * n_out + row] = (float)a * s;
+      y[t * n_out + row] = (float)a * out_scale_g(row_beta(beta, beta_rows, row), gamma[t]);
       if (acc_out) acc_out[t * n_out + row] = a;
     }
   }
@@ -686,11 +688,11 @@ hipError_t launch_gemv_group(int kind, const LinDesc* items, int count, hipStrea
 hipError_t launch_linear_generic(const LinearArgs& a, int fmt, int n, int m, hipStream_t s) {
   const dim3 grid((unsigned)((a.n_out + 63) / 64), (unsigned)((a.m_tok + 15) / 16)), block(256);
   if (fmt == 0)
-    hipLaunchKernelGGL((linear_generic_kernel<0, 8>), grid, block, 0, s, a.packed, a.meta, n, a.beta, a.xq, a.gamma, a.m_tok, a.n_out, a.k, a.y, a.acc);
+    hipLaunchKernelGGL((linear_generic_kernel<0, 8>), grid, block, 0, s, a.packed, a.meta, n, a.beta, a.xq, a.gamma, a.m_tok, a.n_out, a.k, a.y, a.acc, (int32_t)a.beta_rows);
   else if (m == 8)
-    hipLaunchKernelGGL((linear_generic_kernel<1, 8>), grid, block, 0, s, a.packed, a.meta, n, a.beta, a.xq, a.gamma, a.m_tok, a.n_out, a.k, a.y, a.acc);
+    hipLaunchKernelGGL((linear_generic_kernel<1, 8>), grid, block, 0, s, a.packed, a.meta, n, a.beta, a.xq, a.gamma, a.m_tok, a.n_out, a.k, a.y, a.acc, (int32_t)a.beta_rows);
   else
-    hipLaunchKernelGGL((linear_generic_kernel<1, 4>), grid, block, 0, s, a.packed, a.meta, n, a.beta, a.xq, a.gamma, a.m_tok, a.n_out, a.k, a.y, a.acc);
+    hipLaunchKernelGGL((linear_generic_kernel<1, 4>), grid, block, 0, s, a.packed, a.meta, n, a.beta, a.xq, a.gamma, a.m_tok, a.n_out, a.k, a.y, a.acc, (int32_t)a.beta_rows);
   return hipGetLastError();
 }
 

@@ -459,13 +459,14 @@ int sbl_linear_grouped(const uint8_t* packed, const uint8_t* meta, int32_t fmt, 
   const sbl_linear_item it{packed, meta, beta, xq, gamma, m_tok, n_out, k, y, acc};
   const int st = check_linear(it, fmt, n, m);
   if (st != SBL_OK || m_tok == 0 || n_out == 0) return st;
-  if (!acc) return SBL_ERR_NULL;
-  if (ranges_overlap(y, m_tok * n_out * 4, acc, m_tok * n_out * 4)) return SBL_ERR_SHAPE;
-  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const sbl::LinearArgs a = to_args(it, fmt);
-  const int st2 = launch_status(sbl::launch_linear_batch(&a, 1, fmt, n, m, s));
-  if (st2 != SBL_OK) return st2;
-  return launch_status(sbl::launch_rescale_grouped(acc, beta, rows_per_group, gamma, m_tok, n_out, y, s));
+  const int64_t groups = (n_out + rows_per_group - 1) / rows_per_group;
+  if (ranges_overlap(y, m_tok * n_out * 4, beta, 4 * groups) ||
+      (acc && (ranges_overlap(acc, m_tok * n_out * 4, beta, 4 * groups) ||
+               ranges_overlap(y, m_tok * n_out * 4, acc, m_tok * n_out * 4))))
+    return SBL_ERR_SHAPE;
+  sbl::LinearArgs a = to_args(it, fmt);
+  a.beta_rows = rows_per_group < n_out ? rows_per_group : 0;   // the products' epilogues read beta per row
+  return launch_status(sbl::launch_linear_batch(&a, 1, fmt, n, m, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int sbl_quant_acts_kgrouped(const float* x, int64_t m_tok, int64_t k, int64_t kg, int8_t* xq, float* gamma,

@@ -33,6 +33,12 @@ __device__ __forceinline__ float out_scale(const float* beta, const float* gamma
   return out_scale_g(beta, gamma[t]);
 }
 
+// beta of output row `row` (< n_out): one per matrix (beta_rows = 0) or one
+// per block of beta_rows consecutive rows (group scales)
+__device__ __forceinline__ const float* row_beta(const float* beta, int32_t beta_rows, int64_t row) {
+  return beta_rows > 0 ? beta + (uint32_t)row / (uint32_t)beta_rows : beta;
+}
+
 // LDS lookup tables of the N:M decode
 struct NmLut {
   uint32_t spread[256];   // byte of 4 codes (2 bits each) -> 4 int8 c = u - 1
@@ -76,6 +82,7 @@ struct LinDesc {
   int32_t k;
   int32_t m_tok;
   int32_t tiles_n;        // GEMM: row tiles of this matrix
+  int32_t beta_rows;      // > 0: beta per block of beta_rows output rows (group scales)
   // GEMV with the activation quantization fused in: fp32 input, and the
   // quantized activations and scales to publish (nullable; written once)
   const float* x;
@@ -88,6 +95,7 @@ inline LinDesc to_desc(const LinearArgs& a) {
   d.packed = a.packed; d.meta = a.meta; d.xq = a.xq; d.gamma = a.gamma; d.beta = a.beta;
   d.y = a.y; d.acc = a.acc; d.n_out = a.n_out; d.k = (int32_t)a.k; d.m_tok = (int32_t)a.m_tok;
   d.tiles_n = 0;
+  d.beta_rows = (int32_t)a.beta_rows;
   d.x = nullptr; d.xq_out = nullptr; d.gamma_out = nullptr;
   return d;
 }

@@ -153,6 +153,7 @@ struct LinearArgs {
   int64_t m_tok, n_out, k;
   float* y;
   int32_t* acc;
+  int64_t beta_rows = 0;          // > 0: beta per block of beta_rows output rows, beta[row / beta_rows]
 };
 
 // token counts up to this run the grouped GEMV; larger ones the GEMM
@@ -195,9 +196,6 @@ inline GroupPlan group_plan(int64_t n_out, int64_t k, int64_t rows_per_group) {
 // beta[g] for every group (partial sums, then one finalizing workgroup per group)
 hipError_t launch_grouped_beta(const uint16_t* w, int64_t n_out, int64_t k, int64_t rows_per_group, float* beta,
                                uint64_t* ws, hipStream_t s);
-// y[t][r] = fp32(acc[t][r]) * RN(RN(beta_eff[r / rows_per_group] * gamma_eff[t]) * 2^-7)
-hipError_t launch_rescale_grouped(const int32_t* acc, const float* beta, int64_t rows_per_group, const float* gamma,
-                                  int64_t m_tok, int64_t n_out, float* y, hipStream_t s);
 
 // Activation groups along k (kg features per gamma; kg % 64 == 0, k % kg == 0)
 hipError_t launch_quant_acts_kgrouped(const float* x, int64_t m_tok, int64_t k, int64_t kg, int8_t* xq, float* gamma,

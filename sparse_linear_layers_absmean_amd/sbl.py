@@ -315,7 +315,7 @@ def sbl_quant_weights_grouped(w_bf16, n: int, m: int, rows_per_group: int, beta,
 
 
 def sbl_linear_grouped(packed, meta, fmt: int, n: int, m: int, beta, rows_per_group: int, xq, gamma, n_out: int, y,
-                       acc, stream=None):
+                       acc=None, stream=None):
     lib = load()
     m_tok, k = xq.shape
     groups = -(-n_out // rows_per_group) if rows_per_group > 0 else 1

@@ -379,8 +379,9 @@ def test_grouped_validation(lib):
         return fl(A + 2 * F, A + 3 * F, fmt, 6, 8, A + F, rpg, A + 7 * F, A + 8 * F, 2, 16, 64, y, acc, None)
 
     assert lin(rpg=0) == 2
-    assert lin(acc=None) == 1
     assert lin(acc=A + 6 * F + 4) == 2                      # acc overlaps y
+    assert lin(y=A + F + 8) == 2                            # y overlaps beta (4 groups)
+    assert lin(acc=A + F + 12) == 2                         # acc overlaps beta
     assert lin(fmt=3) == 4
 
 

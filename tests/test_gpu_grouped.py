@@ -68,6 +68,41 @@ def test_grouped_rare_values(rpg):
     _run(bits, x, 6, 8, FMT_NM, rpg, "rare mixture")
 
 
+@pytest.mark.parametrize("fmt,n,m", [(FMT_DENSE2, 6, 8), (FMT_NM, 6, 8), (FMT_NM, 2, 4), (FMT_NM, 5, 8)])
+@pytest.mark.parametrize("n_out,k,rpg,t", [(300, 640, 1, 40), (520, 1216, 24, 300), (136, 320, 100, 5),
+                                           (1100, 512, 257, 17)])
+@pytest.mark.parametrize("with_acc", [True, False])
+def test_grouped_products_every_path(n_out, k, rpg, t, fmt, n, m, with_acc):
+    """beta per row group read by each product kernel's epilogue: the GEMV
+    (<= 16 tokens), the int8 MFMA GEMM (DENSE2, 6:8), the 2:4 sparse-MFMA GEMM
+    and the generic kernel (5:8), over ragged row and token tiles, with and
+    without the int32 output."""
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    rng = np.random.default_rng([99, n_out, k, rpg, t, fmt, n, m])
+    bits = synth.gaussian_masters(rng, n_out, k, outlier_frac=0.01)
+    x = synth.gaussian_acts(rng, t, k, hot_channels=2)
+    say(f"grouped products {n_out}x{k} rows_per_group={rpg} t={t} {n}:{m} fmt={fmt} acc={with_acc}")
+    groups = -(-n_out // rpg)
+    beta = torch.empty(groups, device="cuda")
+    packed = torch.empty(sbl.sbl_packed_bytes(n_out, k, n, m, fmt), dtype=torch.uint8, device="cuda")
+    meta = torch.empty((n_out, k // 8), dtype=torch.uint8, device="cuda") if fmt == FMT_NM else None
+    ws = torch.empty(sbl.sbl_workspace_bytes_grouped(n_out, k, rpg), dtype=torch.uint8, device="cuda")
+    sbl.sbl_quant_weights_grouped(to_dev(bits), n, m, rpg, beta, ws, fmt=fmt, packed=packed, meta=meta)
+    xq, gamma = sbl.quant_acts(to_dev(x.astype(np.float32)))
+    y = torch.full((t, n_out), float("nan"), dtype=torch.float32, device="cuda")
+    acc = torch.empty((t, n_out), dtype=torch.int32, device="cuda") if with_acc else None
+    sbl.sbl_linear_grouped(packed, meta, fmt, n, m, beta, rpg, xq, gamma, n_out, y, acc)
+    torch.cuda.synchronize()
+    betas, keep, c = O.quant_weights_grouped(bits, n, m, rpg)
+    assert np.array_equal(to_np(beta), betas)
+    q, g = O.quant_acts(x)
+    acc_ref = O.contract(c, q)
+    if with_acc:
+        assert np.array_equal(to_np(acc), acc_ref)
+    check_y(to_np(y), O.rescale_grouped(acc_ref, betas, rpg, g), acc_ref)
+
+
 def test_grouped_large_groups_decode_and_prefill():
     """Groups spanning many absmean workgroups; GEMV (4 tokens) and GEMM (40 tokens) products."""
     rng = np.random.default_rng(97)
