@@ -862,16 +862,26 @@ def bench_group_scales(torch, np, sbl, dev, tm, rpg=128, kg=320, n=6, m=8):
             sbl.sbl_linear_grouped(pool[c][i]["packed"], pool[c][i]["meta"], fmt, n, m, betas[i], rpg,
                                    acts[i][0], acts[i][1], no, ys[i], accs[i])
 
+    for i in range(len(mats)):
+        sbl.sbl_quant_acts_kgrouped(xs[i], kg, gq[i][0], gq[i][1])
+
     def kgrouped(c):
+        for i, (_, no, k) in enumerate(mats):
+            sbl.sbl_linear_kgrouped(pool[c][i]["packed"], pool[c][i]["meta"], fmt, n, m, betas[i], rpg,
+                                    gq[i][0], gq[i][1], kg, no, ys[i])
+
+    def kgrouped_q(c):
         for i, (_, no, k) in enumerate(mats):
             sbl.sbl_quant_acts_kgrouped(xs[i], kg, gq[i][0], gq[i][1])
             sbl.sbl_linear_kgrouped(pool[c][i]["packed"], pool[c][i]["meta"], fmt, n, m, betas[i], rpg,
                                     gq[i][0], gq[i][1], kg, no, ys[i])
 
+    # every product row times the products alone on activations quantized beforehand
     for name, fn, what in (("sbl_linear", plain, "per-matrix beta and gamma (one launch per matrix)"),
                            ("sbl_linear_grouped", grouped, f"beta per {rpg} rows, read by the GEMV epilogue"),
-                           ("sbl_linear_kgrouped", kgrouped,
-                            f"beta per {rpg} rows, gamma per {kg} features: activation quant + product")):
+                           ("sbl_linear_kgrouped", kgrouped, f"beta per {rpg} rows, gamma per {kg} features"),
+                           ("sbl_quant_acts_kgrouped + sbl_linear_kgrouped", kgrouped_q,
+                            f"the same with the activation quantization per matrix in the step")):
         us = timed_steps(torch, tm, fn, pcopies, max(20, 2 * pcopies)) * 1e3
         gbps = wbytes / (us * 1e-6) / 1e9
         out["products"].append({"call": name, "scales": what, "us_per_block": round(us, 1),

@@ -106,17 +106,20 @@ __global__ __launch_bounds__(256) void quant_acts_kgrouped_kernel(const float* _
   if (threadIdx.x == 0) gamma[t * groups + j] = g;
 }
 
-// Products with activation groups: one single-wave workgroup per (output row,
-// token).  A pass covers 16 k-blocks (4 panels): lanes 4c .. 4c+3 take
-// k-block c, 16 consecutive weights each, and the 4 lanes' int32 sums make
-// that k-block's exact product, kept in LDS.  Then lane j adds up the
-// k-blocks of feature block j (an exact int32 sum) and rescales it with beta
-// of the row's group and gamma[t][j] (the two roundings of the per-matrix
+// Products with activation groups: workgroups of kKgRows waves, one output
+// row per wave, of one token (fewer, larger workgroups than one wave each:
+// a launch over a whole matrix has tens of thousands of rows).  A pass covers
+// 16 k-blocks (4 panels): lanes 4c .. 4c+3 take k-block c, 16 consecutive
+// weights each, and the 4 lanes' int32 sums make that k-block's exact
+// product, kept in the wave's LDS slice.  Then lane j adds up the k-blocks
+// of feature block j (an exact int32 sum) and rescales it with beta of the
+// row's group and gamma[t][j] (the two roundings of the per-matrix
 // epilogue), and the blocks' fp32 results are added in ascending j.
 //
 // Weights go in as u = c + 1 in {0, 1, 2} (pruned positions u = 1), so that
 // sum c x = sum u x - sum x, both as v_dot4_i32_i8 over bytes.
 constexpr int kKgPasses = 2;       // passes whose loads are issued together
+constexpr int kKgRows = 4;         // waves (rows) per workgroup
 
 struct KgLoad {
   u32x4 x;           // the 16 int8 activations
@@ -126,9 +129,10 @@ struct KgLoad {
 
 // Every load is independent of the others (no address depends on loaded data).
 __device__ __forceinline__ KgLoad kg_issue(const uint8_t* packed, const uint8_t* meta, const int8_t* xr,
-                                           int64_t n_out, int nkb, int fmt, int n, int m, int64_t row, int kb, int q) {
+                                           int64_t n_out, int nkb, int fmt, int n, int m, int64_t row, int kb, int q,
+                                           int kb_end) {
   KgLoad L = {u32x4{0u, 0u, 0u, 0u}, 0u, 0ull};
-  if (kb < nkb) {
+  if (kb < kb_end) {
     L.x = *reinterpret_cast<const u32x4*>(xr + 64 * (int64_t)kb + 16 * q);
     if (fmt == 0) {
       L.w = *reinterpret_cast<const uint32_t*>(packed + panel_offset(n_out, nkb, 16, row, kb) + 4 * q);
@@ -175,22 +179,23 @@ __device__ __forceinline__ void kg_decode(const KgLoad& L, int fmt, int n, int m
   }
 }
 
-__global__ __launch_bounds__(64) void linear_kgrouped_kernel(const uint8_t* __restrict__ packed,
-                                                             const uint8_t* __restrict__ meta, int fmt, int n, int m,
-                                                             const float* __restrict__ beta, int64_t rpg,
-                                                             const int8_t* __restrict__ xq,
-                                                             const float* __restrict__ gamma, int64_t kg,
-                                                             int64_t n_out, int64_t k, float* __restrict__ y) {
-  extern __shared__ int32_t kbsum[];                       // [nkb] k-block sums, then [groups] fp32 terms
-  const int lane = threadIdx.x, c = lane >> 2, q = lane & 3;
-  const int64_t row = blockIdx.x, t = blockIdx.y;
+__global__ __launch_bounds__(64 * kKgRows) void linear_kgrouped_kernel(
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ meta, int fmt, int n, int m,
+    const float* __restrict__ beta, int64_t rpg, const int8_t* __restrict__ xq, const float* __restrict__ gamma,
+    int64_t kg, int64_t n_out, int64_t k, float* __restrict__ y) {
+  extern __shared__ int32_t kg_lds[];                      // per wave: [nkb] k-block sums, then [groups] fp32 terms
+  const int lane = threadIdx.x & 63, c = lane >> 2, q = lane & 3, wave = threadIdx.x >> 6;
+  const int64_t row_w = (int64_t)blockIdx.x * kKgRows + wave, t = blockIdx.y;
+  const int64_t row = row_w < n_out ? row_w : n_out - 1;   // a row past n_out repeats the last and stores nothing
   const int nkb = (int)(k / 64);
   const int groups = (int)(k / kg), bpg = (int)(kg / 64);
+  int32_t* kbsum = kg_lds + wave * (nkb + groups);
   const int8_t* xr = xq + t * k;
   for (int kb0 = 0; kb0 < nkb; kb0 += 16 * kKgPasses) {
     KgLoad L[kKgPasses];
 #pragma unroll
-    for (int v = 0; v < kKgPasses; ++v) L[v] = kg_issue(packed, meta, xr, n_out, nkb, fmt, n, m, row, kb0 + 16 * v + c, q);
+    for (int v = 0; v < kKgPasses; ++v)
+      L[v] = kg_issue(packed, meta, xr, n_out, nkb, fmt, n, m, row, kb0 + 16 * v + c, q, nkb);
 #pragma unroll
     for (int v = 0; v < kKgPasses; ++v) {
       const int kb = kb0 + 16 * v + c;
@@ -227,7 +232,7 @@ __global__ __launch_bounds__(64) void linear_kgrouped_kernel(const uint8_t* __re
     __syncthreads();
     for (int j = 0; j < groups; ++j) yacc = yacc + term[j];
   }
-  if (lane == 0) y[t * n_out + row] = yacc;
+  if (lane == 0 && row_w < n_out) y[t * n_out + row_w] = yacc;
 }
 
 }  // namespace
@@ -242,10 +247,11 @@ hipError_t launch_quant_acts_kgrouped(const float* x, int64_t m_tok, int64_t k, 
 hipError_t launch_linear_kgrouped(const uint8_t* packed, const uint8_t* meta, int fmt, int n, int m, const float* beta,
                                   int64_t rows_per_group, const int8_t* xq, const float* gamma, int64_t kg,
                                   int64_t m_tok, int64_t n_out, int64_t k, float* y, hipStream_t s) {
-  // LDS: k/64 int32 block sums and k/kg fp32 terms, at most 2 * 2048 words
-  const size_t lds = (size_t)(k / 64 + k / kg) * 4;
-  hipLaunchKernelGGL(linear_kgrouped_kernel, dim3((unsigned)n_out, (unsigned)m_tok), dim3(64), lds, s, packed, meta,
-                     fmt, n, m, beta, rows_per_group, xq, gamma, kg, n_out, k, y);
+  // LDS per wave: k/64 int32 block sums and k/kg fp32 terms (at most 2 * 2048 words)
+  const size_t lds = (size_t)kKgRows * (k / 64 + k / kg) * 4;
+  hipLaunchKernelGGL(linear_kgrouped_kernel, dim3((unsigned)((n_out + kKgRows - 1) / kKgRows), (unsigned)m_tok),
+                     dim3(64 * kKgRows), lds, s, packed, meta, fmt, n, m, beta, rows_per_group, xq, gamma, kg, n_out,
+                     k, y);
   return hipGetLastError();
 }
 
