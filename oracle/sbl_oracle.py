@@ -48,6 +48,10 @@ beta per block of consecutive output rows instead of one per matrix.
 Activation groups (`quant_acts_kgrouped`, `linear_kgrouped`): one gamma per
 token and block of kg features; each block's product is rescaled on its own
 and the blocks' fp32 results are added in ascending block order.
+Block scales (`quant_weights_blocked`): one absmean beta per block of
+consecutive output rows x consecutive features (the weight groups of the same
+section taken along k as well); `linear_kgrouped` then takes one beta per row
+group and feature block, the feature blocks being those of the activations.
 
 Backward (dual straight-through estimator; readings listed with the
 function `backward`): the scales are constants, the incoming gradient is
@@ -450,6 +454,30 @@ def quant_weights_grouped(bits: np.ndarray, n: int, m: int, rows_per_group: int)
     return np.array(betas, np.float32), keep, codes
 
 
+def quant_weights_blocked(bits: np.ndarray, n: int, m: int, rows_per_group: int, cols_per_group: int):
+    """(betas fp32 [Gr][Gk], keep bool, codes int8): quant-then-mask with one beta per
+    block of rows_per_group consecutive rows (the last block may be shorter) and
+    cols_per_group consecutive features (a multiple of m dividing k).  Each block's beta
+    is the method's exact absmean over the block's masters, and the block's codes use it;
+    the mask does not depend on beta."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    n_out, k = bits.shape
+    if rows_per_group < 1 or cols_per_group < 1 or k % cols_per_group or cols_per_group % m:
+        raise ValueError("rows_per_group >= 1 and cols_per_group a multiple of m dividing k")
+    keep = nm_keep(bits, n, m)
+    row_starts = range(0, n_out, rows_per_group)
+    col_starts = range(0, k, cols_per_group)
+    betas = np.zeros((len(row_starts), len(col_starts)), np.float32)
+    codes = np.zeros(bits.shape, np.int8)
+    for gi, r0 in enumerate(row_starts):
+        for gj, c0 in enumerate(col_starts):
+            blk = (slice(r0, min(n_out, r0 + rows_per_group)), slice(c0, c0 + cols_per_group))
+            betas[gi, gj] = absmean_beta(bits[blk])
+            codes[blk] = ternarize(bits[blk], betas[gi, gj])
+    codes = (codes * keep).astype(np.int8)
+    return betas, keep, codes
+
+
 def rescale_grouped(acc: np.ndarray, betas: np.ndarray, rows_per_group: int, gamma: np.ndarray) -> np.ndarray:
     """y[t, r] = RN(fp32(acc) * RN(RN(beta_eff[r // rows_per_group] * gamma_eff[t]) * 2^-7))."""
     acc = np.asarray(acc)
@@ -478,16 +506,21 @@ def quant_acts_kgrouped(x: np.ndarray, kg: int):
 def linear_kgrouped(codes: np.ndarray, q: np.ndarray, betas: np.ndarray, rows_per_group: int,
                     gamma: np.ndarray, kg: int):
     """(acc int32 [m_tok][n_out][G], y fp32): per feature block j the exact
-    product acc_j, rescaled with beta of the row's group and gamma[t, j] (the two
+    product acc_j, rescaled with beta of the row's group (betas [Gr]) or of the
+    row's group and block j (betas [Gr][G], block scales) and gamma[t, j] (the two
     roundings of rescale), and the blocks' fp32 results added in ascending j."""
     c = np.asarray(codes, dtype=np.int8)
     qq = np.asarray(q, dtype=np.int8)
+    b = np.asarray(betas, dtype=np.float32)
     n_out, k = c.shape
     groups = k // kg
+    if b.ndim == 2 and b.shape[1] != groups:
+        raise ValueError("block scales need one beta per feature block of the activations")
     acc = np.stack([contract(c[:, j * kg:(j + 1) * kg], qq[:, j * kg:(j + 1) * kg]) for j in range(groups)], axis=2)
     y = np.zeros((qq.shape[0], n_out), np.float32)
     for j in range(groups):
-        y = (y + rescale_grouped(acc[:, :, j], betas, rows_per_group, np.asarray(gamma)[:, j])).astype(np.float32)
+        bj = b if b.ndim == 1 else b[:, j]
+        y = (y + rescale_grouped(acc[:, :, j], bj, rows_per_group, np.asarray(gamma)[:, j])).astype(np.float32)
     return acc, y
 
 

@@ -135,3 +135,83 @@ def test_kgroups_sum_in_block_order():
                 term = np.float32(float(Fraction(int(acc[t, r, j])) * s))
                 tot = np.float32(tot + term)
             assert y[t, r] == tot
+
+
+# ---- block scales: one beta per block of rows x features ----
+
+def test_blocks_spanning_k_are_the_row_groups():
+    rng = np.random.default_rng(407)
+    bits = synth.gaussian_masters(rng, 30, 256, outlier_frac=0.02)
+    for rpg in (1, 7, 30):
+        b2, keep2, c2 = O.quant_weights_blocked(bits, 6, 8, rpg, 256)
+        b1, keep1, c1 = O.quant_weights_grouped(bits, 6, 8, rpg)
+        assert b2.shape == (len(b1), 1) and np.array_equal(b2[:, 0], b1)
+        assert np.array_equal(keep2, keep1) and np.array_equal(c2, c1)
+
+
+@pytest.mark.parametrize("rpg,cpg,n,m", [(1, 64, 6, 8), (5, 128, 2, 4), (16, 192, 6, 8), (40, 64, 5, 8)])
+def test_each_block_is_the_method_on_its_submatrix(rpg, cpg, n, m):
+    """Every block's beta, mask and codes equal the per-matrix method run on the
+    block's masters alone (m divides cpg, so the mask's groups never straddle a
+    block edge)."""
+    rng = np.random.default_rng([408, rpg, cpg, n, m])
+    bits = synth.gaussian_masters(rng, 37, 384, outlier_frac=0.02)
+    betas, keep, codes = O.quant_weights_blocked(bits, n, m, rpg, cpg)
+    assert betas.shape == (-(-37 // rpg), 384 // cpg)
+    for gi, r0 in enumerate(range(0, 37, rpg)):
+        for gj, c0 in enumerate(range(0, 384, cpg)):
+            blk = (slice(r0, min(37, r0 + rpg)), slice(c0, c0 + cpg))
+            b, k1, c1 = O.quant_weights(bits[blk], n, m)
+            assert betas[gi, gj] == b
+            assert np.array_equal(keep[blk], k1) and np.array_equal(codes[blk], c1)
+
+
+def test_blocks_closed_form_and_locality():
+    """Constant-magnitude blocks have beta = that magnitude; changing one
+    block's masters changes only that block's beta and codes."""
+    mags = np.array([[0.015625, 0.25], [0.0078125, 2.0]], np.float32)
+    w = np.zeros((4, 128), np.float32)
+    for gi in range(2):
+        for gj in range(2):
+            w[2 * gi:2 * gi + 2, 64 * gj:64 * gj + 64] = mags[gi, gj]
+    w[:, ::2] *= -1
+    betas, keep, codes = O.quant_weights_blocked(synth.f32_to_bf16_bits(w), 6, 8, 2, 64)
+    assert np.array_equal(betas, mags)
+    assert np.all(np.abs(codes[keep]) == 1) and np.all(codes[~keep] == 0)
+    rng = np.random.default_rng(409)
+    bits = synth.gaussian_masters(rng, 8, 256)
+    b0, _, c0 = O.quant_weights_blocked(bits, 6, 8, 4, 128)
+    bits2 = bits.copy()
+    bits2[4:8, 128:] = synth.gaussian_masters(rng, 4, 128, sigma=0.5)
+    b1, _, c1 = O.quant_weights_blocked(bits2, 6, 8, 4, 128)
+    changed = b0 != b1
+    assert changed[1, 1] and changed.sum() == 1
+    assert np.array_equal(c0[:4], c1[:4]) and np.array_equal(c0[4:, :128], c1[4:, :128])
+
+
+def test_block_scales_in_the_product():
+    """With one beta per (row group, feature block): a beta table constant along
+    the feature blocks gives the row-group product; otherwise every block's
+    term uses its own beta (Fraction-exact terms, fp32 sum in block order)."""
+    rng = np.random.default_rng(410)
+    bits = synth.gaussian_masters(rng, 9, 192)
+    x = synth.gaussian_acts(rng, 2, 192, hot_channels=1)
+    q, g = O.quant_acts_kgrouped(x, 64)
+    rb, keep, codes = O.quant_weights_grouped(bits, 6, 8, 4)
+    acc1, y1 = O.linear_kgrouped(codes, q, rb, 4, g, 64)
+    acc2, y2 = O.linear_kgrouped(codes, q, np.repeat(rb[:, None], 3, axis=1), 4, g, 64)
+    assert np.array_equal(acc1, acc2) and np.array_equal(y1, y2)
+    betas, keep, codes = O.quant_weights_blocked(bits, 6, 8, 4, 64)
+    acc, y = O.linear_kgrouped(codes, q, betas, 4, g, 64)
+    assert np.array_equal(acc.sum(axis=2), O.contract(codes, q))
+    for t in range(2):
+        for r in range(9):
+            tot = np.float32(0)
+            for j in range(3):
+                b = Fraction(float(max(np.float32(betas[r // 4, j]), np.float32(1e-5))))
+                gj = Fraction(float(max(np.float32(g[t, j]), np.float32(1e-5))))
+                s = Fraction(float(np.float32(float(b * gj)))) / 128
+                tot = np.float32(tot + np.float32(float(Fraction(int(acc[t, r, j])) * s)))
+            assert y[t, r] == tot
+    with pytest.raises(ValueError):
+        O.linear_kgrouped(codes, q, betas[:, :2], 4, g, 64)
