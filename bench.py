@@ -810,8 +810,9 @@ def bench_backward(torch, np, sbl, dev, tm, masters3b):
 
 def bench_group_scales(torch, np, sbl, dev, tm, rpg=128, kg=320, n=6, m=8):
     """Group scales on a 3B-class block, 6:8 N:M, M = 1: weight preparation with beta per
-    block of rows (rows_per_group 1 and rpg), and the decode products with beta per row
-    group and with gamma per block of kg features, beside the per-matrix sbl_linear.  Each
+    block of rows (rows_per_group 1 and rpg) and per block of rpg rows x kg features, and
+    the decode products with beta per row group, with gamma per block of kg features and
+    with both per block, beside the per-matrix sbl_linear.  Each
     block's calls are one HIP graph; every block uses distinct buffers (>= 600 MB)."""
     fmt = 1
     mats = mats_of("3b")
@@ -826,6 +827,22 @@ def bench_group_scales(torch, np, sbl, dev, tm, rpg=128, kg=320, n=6, m=8):
     outs = [[dict(packed=torch.empty(pb[i], dtype=torch.uint8, device=dev),
                   meta=torch.empty((no, k // 8), dtype=torch.uint8, device=dev)) for i, (_, no, k) in enumerate(mats)]
             for _ in range(copies)]
+    # block scales: beta per rpg rows x kg features
+    bbetas = [torch.empty((-(-no // rpg), k // kg), device=dev) for _, no, k in mats]
+    bwss = [torch.empty(sbl.sbl_workspace_bytes_blocked(no, k, rpg, kg), dtype=torch.uint8, device=dev)
+            for _, no, k in mats]
+
+    def prep_blocked(c):
+        for i, (_, no, k) in enumerate(mats):
+            sbl.sbl_quant_weights_blocked(masters[c][i], n, m, rpg, kg, bbetas[i], bwss[i], fmt=fmt,
+                                          packed=outs[c][i]["packed"], meta=outs[c][i]["meta"])
+    us = timed_steps(torch, tm, prep_blocked, copies, max(10, 2 * copies)) * 1e3
+    bouts = [{k2: v.clone() for k2, v in o.items()} for o in outs[0]]     # codes with the block betas
+    gbps = (2 * bw + wbytes) / (us * 1e-6) / 1e9
+    out["weight_prep"].append({"rows_per_group": rpg, "cols_per_group": kg,
+                               "groups": sum(-(-no // rpg) * (k // kg) for _, no, k in mats),
+                               "us_per_block": round(us, 1), "alg_GBps": round(gbps, 1),
+                               "frac": round(gbps / HBM_PEAK_GBPS, 4)})
     for r in (1, rpg):
         betas = [torch.empty(-(-no // r), device=dev) for _, no, k in mats]
         wss = [torch.empty(sbl.sbl_workspace_bytes_grouped(no, k, r), dtype=torch.uint8, device=dev)
@@ -844,6 +861,7 @@ def bench_group_scales(torch, np, sbl, dev, tm, rpg=128, kg=320, n=6, m=8):
     torch.cuda.empty_cache()
     pcopies = rot_copies(wbytes, 600e6)
     pool = [[{k2: v.clone() for k2, v in o.items()} for o in outs[0]] for _ in range(pcopies)]
+    bpool = [[{k2: v.clone() for k2, v in o.items()} for o in bouts] for _ in range(pcopies)]
     beta1 = [b[:1].contiguous() for b in betas]
     xs = [torch.randn((1, k), generator=g, device=dev) for _, no, k in mats]
     acts = [sbl.quant_acts(x) for x in xs]
@@ -870,6 +888,11 @@ def bench_group_scales(torch, np, sbl, dev, tm, rpg=128, kg=320, n=6, m=8):
             sbl.sbl_linear_kgrouped(pool[c][i]["packed"], pool[c][i]["meta"], fmt, n, m, betas[i], rpg,
                                     gq[i][0], gq[i][1], kg, no, ys[i])
 
+    def blocked(c):
+        for i, (_, no, k) in enumerate(mats):
+            sbl.sbl_linear_blocked(bpool[c][i]["packed"], bpool[c][i]["meta"], fmt, n, m, bbetas[i], rpg,
+                                   gq[i][0], gq[i][1], kg, no, ys[i])
+
     def kgrouped_q(c):
         for i, (_, no, k) in enumerate(mats):
             sbl.sbl_quant_acts_kgrouped(xs[i], kg, gq[i][0], gq[i][1])
@@ -880,13 +903,14 @@ def bench_group_scales(torch, np, sbl, dev, tm, rpg=128, kg=320, n=6, m=8):
     for name, fn, what in (("sbl_linear", plain, "per-matrix beta and gamma (one launch per matrix)"),
                            ("sbl_linear_grouped", grouped, f"beta per {rpg} rows, read by the GEMV epilogue"),
                            ("sbl_linear_kgrouped", kgrouped, f"beta per {rpg} rows, gamma per {kg} features"),
+                           ("sbl_linear_blocked", blocked, f"beta per {rpg} rows x {kg} features, gamma per {kg} features"),
                            ("sbl_quant_acts_kgrouped + sbl_linear_kgrouped", kgrouped_q,
                             f"the same with the activation quantization per matrix in the step")):
         us = timed_steps(torch, tm, fn, pcopies, max(20, 2 * pcopies)) * 1e3
         gbps = wbytes / (us * 1e-6) / 1e9
         out["products"].append({"call": name, "scales": what, "us_per_block": round(us, 1),
                                 "weight_GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)})
-    del pool, outs
+    del pool, bpool, outs, bouts
     torch.cuda.empty_cache()
     return out
 

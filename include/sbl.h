@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SBL_ABI_VERSION 10
+#define SBL_ABI_VERSION 11
 
 typedef enum {
   SBL_OK = 0,
@@ -371,6 +371,36 @@ int sbl_quant_acts_kgrouped(const float* x, int64_t m_tok, int64_t k, int64_t kg
 int sbl_linear_kgrouped(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
                         const float* beta, int64_t rows_per_group, const int8_t* xq, const float* gamma, int64_t kg,
                         int64_t m_tok, int64_t n_out, int64_t k, float* y, sbl_stream stream);
+
+/* Block scales (the same article and section, the weight groups taken
+ * along k as well): one beta per block of rows_per_group consecutive output
+ * rows x cols_per_group consecutive features (cols_per_group a multiple of 64
+ * dividing k; rows_per_group >= 1, the last row block may be shorter; at
+ * most 65535 row blocks and 65535 column blocks).
+ *   beta[gr][gc] = RN_fp32 of the exact mean of |w| over block (gr, gc); the
+ *   codes of the block use max(beta[gr][gc], 1e-5).  The mask does not
+ *   depend on beta.
+ *   beta       [ceil(n_out / rows_per_group)][k / cols_per_group] fp32 output.
+ *   workspace  sbl_workspace_bytes_blocked(n_out, k, rows_per_group,
+ *              cols_per_group) bytes (-1: invalid shape).
+ * Everything else as sbl_quant_weights_grouped; cols_per_group = k is
+ * sbl_quant_weights_grouped. */
+int64_t sbl_workspace_bytes_blocked(int64_t n_out, int64_t k, int64_t rows_per_group, int64_t cols_per_group);
+int sbl_quant_weights_blocked(const uint16_t* w_bf16, int64_t n_out, int64_t k, int32_t n, int32_t m,
+                              int64_t rows_per_group, int64_t cols_per_group, float* beta, uint8_t* mask_bits,
+                              int8_t* codes, int32_t fmt, uint8_t* packed, uint8_t* meta,
+                              void* workspace, int64_t workspace_bytes, sbl_stream stream);
+
+/* Products with block scales: as sbl_linear_kgrouped, with beta
+ * [ceil(n_out / rows_per_group)][k / kg] from sbl_quant_weights_blocked with
+ * cols_per_group = kg, so that every feature block j of the activations is
+ * one column block of the weights:
+ *   y[t][r] = sum over j, ascending, in fp32, of RN(fp32(acc_j[t][r]) *
+ *             RN(RN(beta_eff[r / rows_per_group][j] * gamma_eff[t][j]) * 2^-7)).
+ * beta must not overlap y. */
+int sbl_linear_blocked(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
+                       const float* beta, int64_t rows_per_group, const int8_t* xq, const float* gamma, int64_t kg,
+                       int64_t m_tok, int64_t n_out, int64_t k, float* y, sbl_stream stream);
 
 /* Backward of the layer under the dual straight-through estimator
  * (Sparse-BitNet summaries: Spanish section 2, "Estrategia de Entrenamiento",

@@ -9,8 +9,8 @@ from .sbl import (SBL_FMT_DENSE2, SBL_FMT_NM, SblError, linear, load, new_backwa
                   quant_acts, sbl_backward_workspace_bytes,
                   quant_weights, sbl_abi_version, sbl_linear, sbl_linear_acts_batch, sbl_linear_backward,
                   sbl_linear_batch, sbl_linear_grouped, sbl_linear_kgrouped, sbl_meta_bytes,
-                  sbl_quant_acts_kgrouped, sbl_quant_weights_grouped,
-                  sbl_workspace_bytes_grouped,
+                  sbl_linear_blocked, sbl_quant_acts_kgrouped, sbl_quant_weights_blocked,
+                  sbl_quant_weights_grouped, sbl_workspace_bytes_blocked, sbl_workspace_bytes_grouped,
                   sbl_pack,
                   sbl_packed_bytes, sbl_quant_acts, sbl_quant_weights, sbl_quant_weights_batch,
                   sbl_quant_weights_batch_noalloc,
@@ -22,8 +22,8 @@ __all__ = [
     "quant_acts", "sbl_backward_workspace_bytes",
     "quant_weights", "sbl_abi_version", "sbl_linear", "sbl_linear_acts_batch", "sbl_linear_backward",
     "sbl_linear_batch", "sbl_linear_grouped", "sbl_linear_kgrouped", "sbl_meta_bytes",
-    "sbl_quant_acts_kgrouped", "sbl_quant_weights_grouped",
-    "sbl_workspace_bytes_grouped",
+    "sbl_linear_blocked", "sbl_quant_acts_kgrouped", "sbl_quant_weights_blocked",
+    "sbl_quant_weights_grouped", "sbl_workspace_bytes_blocked", "sbl_workspace_bytes_grouped",
     "sbl_pack",
     "sbl_packed_bytes", "sbl_quant_acts", "sbl_quant_weights", "sbl_quant_weights_batch",
     "sbl_quant_weights_batch_noalloc",

@@ -1,18 +1,21 @@
 // Group scales (BitNet.cpp article, "Cuantizacion y normalizacion de grupos":
 // the quantization parameters are computed per group of weights rather than
 // per matrix, so groups need no communication).  A group is a block of
-// rows_per_group consecutive output rows; each has its own exact absmean
+// rows_per_group consecutive output rows x cols_per_group consecutive
+// features (cols_per_group = k: whole rows); each has its own exact absmean
 // beta (the method's "Ternary Quantization" scale, restricted to the group),
-// and its rows' codes and outputs use it.
+// and its weights' codes and products use it.
 //
-//  * group_partial_kernel: workgroup (w, g) adds the magnitudes of slice w of
-//    group g's rows exactly (sbl_partial.h) into slot w of the group's
-//    workspace region; every group uses the partition of a full group.
+//  * group_partial_kernel: workgroup (w, gr, gc) adds the magnitudes of
+//    slice w of group (gr, gc) exactly (sbl_partial.h) into slot w of the
+//    group's workspace region; every group uses the partition of a full group.
 //  * group_final_kernel: one workgroup per group rounds the exact mean once
 //    (sbl_beta.h) into beta[g]; a group whose masters fit one absmean
 //    workgroup is rounded by that workgroup instead (no second launch).
-//  * The mask/pack kernel then reads beta per row group (QDesc.beta_rows), and
-//    the products' epilogues do too (LinearArgs.beta_rows).
+//  * The mask/pack kernel then reads beta per chunk's group (QDesc.beta_rows,
+//    beta_kblocks), and the products' epilogues read it per row
+//    (LinearArgs.beta_rows) or per row and feature block (the
+//    activation-group product).
 #include "sbl_partial.h"
 
 namespace sbl {
@@ -22,30 +25,50 @@ namespace {
 using namespace part;
 
 __global__ __launch_bounds__(kAbsThreads) void group_partial_kernel(const u32x4* __restrict__ w, int64_t n_out,
-                                                                    int64_t k, int64_t rpg, GroupPlan plan,
-                                                                    uint64_t* ws, float* beta) {
-  const int64_t g = blockIdx.y, wg = blockIdx.x;
-  const int64_t r0 = g * rpg;
+                                                                    int64_t k, int64_t rpg, int64_t cpg,
+                                                                    GroupPlan plan, uint64_t* ws, float* beta) {
+  const int64_t gr = blockIdx.y, gc = blockIdx.z, wg = blockIdx.x;
+  const int64_t g = gr * plan.gk + gc;
+  const int64_t r0 = gr * rpg;
   const int64_t rows = n_out - r0 < rpg ? n_out - r0 : rpg;
-  const int64_t nvec = rows * k / 8;                      // this group's 16-byte vectors
+  const int64_t nvec = rows * cpg / 8;                    // this group's 16-byte vectors
   const int vpt = (int)plan.vpt;
   const int64_t first = wg * kAbsThreads * vpt;
   int64_t span = nvec - first;
   span = span < 0 ? 0 : (span > (int64_t)kAbsThreads * vpt ? (int64_t)kAbsThreads * vpt : span);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + r0 * k / 8 + (span > 0 ? first : 0), span * 16);
   __shared__ unsigned long long bins[256];
   bins[threadIdx.x] = 0;
   __syncthreads();
   double acc0 = 0.0, acc1 = 0.0;
   uint32_t rare = 0;
-  for (int j = 0; j < vpt; j += 8) {
-    u32x4 v[8];
+  if (cpg == k) {
+    // whole rows: the group's vectors are contiguous (one buffer over the slice)
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + r0 * k / 8 + (span > 0 ? first : 0), span * 16);
+    for (int j = 0; j < vpt; j += 8) {
+      u32x4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rw, (threadIdx.x + (j + u) * kAbsThreads) * 16, 0, 0));
+      for (int u = 0; u < 8; ++u)
+        v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rw, (threadIdx.x + (j + u) * kAbsThreads) * 16, 0, 0));
 #pragma unroll
-    for (int u = 0; u < 8; ++u) consume(v[u], acc0, acc1, bins, rare);
+      for (int u = 0; u < 8; ++u) consume(v[u], acc0, acc1, bins, rare);
+    }
+  } else {
+    // a block of columns: vector i of the slice is vector i % vpr of the
+    // group's row i / vpr (vpr vectors per row); past the slice: zeros
+    const uint32_t vpr = (uint32_t)(cpg / 8);
+    const u32x4* base = w + r0 * (k / 8) + gc * vpr;
+    for (int j = 0; j < vpt; j += 8) {
+      u32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t i = (uint32_t)threadIdx.x + (uint32_t)(j + u) * kAbsThreads;
+        const uint32_t gi = (uint32_t)first + i;
+        v[u] = i < (uint32_t)span ? base[(int64_t)(gi / vpr) * (k / 8) + gi % vpr] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) consume(v[u], acc0, acc1, bins, rare);
+    }
   }
   publish_partial(ws + g * plan.region, plan.nb, wg, acc0, acc1, rare, bins);
   if (plan.nb == 1) {
@@ -56,7 +79,7 @@ __global__ __launch_bounds__(kAbsThreads) void group_partial_kernel(const u32x4*
     QDesc d = {};
     d.w = w + r0 * k / 8;
     d.nvec = nvec;
-    d.count = rows * k;
+    d.count = rows * cpg;
     d.nb = 1;
     d.vpt = plan.vpt;
     d.ws = ws + g * plan.region;
@@ -66,14 +89,15 @@ __global__ __launch_bounds__(kAbsThreads) void group_partial_kernel(const u32x4*
 }
 
 __global__ __launch_bounds__(kAbsThreads) void group_final_kernel(const u32x4* w, int64_t n_out, int64_t k,
-                                                                  int64_t rpg, GroupPlan plan, uint64_t* ws,
-                                                                  float* beta) {
+                                                                  int64_t rpg, int64_t cpg, GroupPlan plan,
+                                                                  uint64_t* ws, float* beta) {
   const int64_t g = blockIdx.x;
-  const int64_t rows = n_out - g * rpg < rpg ? n_out - g * rpg : rpg;
+  const int64_t r0 = g / plan.gk * rpg;
+  const int64_t rows = n_out - r0 < rpg ? n_out - r0 : rpg;
   QDesc d = {};
   d.w = w;
-  d.nvec = rows * k / 8;
-  d.count = rows * k;
+  d.nvec = rows * cpg / 8;
+  d.count = rows * cpg;
   d.nb = plan.nb;
   d.vpt = plan.vpt;
   d.ws = ws + g * plan.region;
@@ -181,8 +205,8 @@ __device__ __forceinline__ void kg_decode(const KgLoad& L, int fmt, int n, int m
 
 __global__ __launch_bounds__(64 * kKgRows) void linear_kgrouped_kernel(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ meta, int fmt, int n, int m,
-    const float* __restrict__ beta, int64_t rpg, const int8_t* __restrict__ xq, const float* __restrict__ gamma,
-    int64_t kg, int64_t n_out, int64_t k, float* __restrict__ y) {
+    const float* __restrict__ beta, int64_t rpg, int per_block, const int8_t* __restrict__ xq,
+    const float* __restrict__ gamma, int64_t kg, int64_t n_out, int64_t k, float* __restrict__ y) {
   extern __shared__ int32_t kg_lds[];                      // per wave: [nkb] k-block sums, then [groups] fp32 terms
   const int lane = threadIdx.x & 63, c = lane >> 2, q = lane & 3, wave = threadIdx.x >> 6;
   const int64_t row_w = (int64_t)blockIdx.x * kKgRows + wave, t = blockIdx.y;
@@ -215,11 +239,13 @@ __global__ __launch_bounds__(64 * kKgRows) void linear_kgrouped_kernel(
   }
   __syncthreads();
   float* term = reinterpret_cast<float*>(kbsum + nkb);
-  const float b = fmaxf(beta[row / rpg], 1e-5f);
+  // beta of the row's group, or (block scales) of the row's group and feature block j
+  const float* brow = per_block ? beta + row / rpg * groups : beta + row / rpg;
   float tj = 0.0f;
   for (int j = lane; j < groups; j += 64) {
     int s = 0;
     for (int i = 0; i < bpg; ++i) s += kbsum[j * bpg + i];
+    const float b = fmaxf(brow[per_block ? j : 0], 1e-5f);
     const float sc = (b * fmaxf(gamma[t * groups + j], 1e-5f)) * (1.0f / 128.0f);
     tj = (float)s * sc;
     term[j] = tj;
@@ -245,27 +271,27 @@ hipError_t launch_quant_acts_kgrouped(const float* x, int64_t m_tok, int64_t k, 
 }
 
 hipError_t launch_linear_kgrouped(const uint8_t* packed, const uint8_t* meta, int fmt, int n, int m, const float* beta,
-                                  int64_t rows_per_group, const int8_t* xq, const float* gamma, int64_t kg,
-                                  int64_t m_tok, int64_t n_out, int64_t k, float* y, hipStream_t s) {
+                                  int64_t rows_per_group, bool beta_per_block, const int8_t* xq, const float* gamma,
+                                  int64_t kg, int64_t m_tok, int64_t n_out, int64_t k, float* y, hipStream_t s) {
   // LDS per wave: k/64 int32 block sums and k/kg fp32 terms (at most 2 * 2048 words)
   const size_t lds = (size_t)kKgRows * (k / 64 + k / kg) * 4;
   hipLaunchKernelGGL(linear_kgrouped_kernel, dim3((unsigned)((n_out + kKgRows - 1) / kKgRows), (unsigned)m_tok),
-                     dim3(64 * kKgRows), lds, s, packed, meta, fmt, n, m, beta, rows_per_group, xq, gamma, kg, n_out,
-                     k, y);
+                     dim3(64 * kKgRows), lds, s, packed, meta, fmt, n, m, beta, rows_per_group, beta_per_block ? 1 : 0,
+                     xq, gamma, kg, n_out, k, y);
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_beta(const uint16_t* w, int64_t n_out, int64_t k, int64_t rows_per_group, float* beta,
-                               uint64_t* ws, hipStream_t s) {
-  const GroupPlan plan = group_plan(n_out, k, rows_per_group);
+hipError_t launch_grouped_beta(const uint16_t* w, int64_t n_out, int64_t k, int64_t rows_per_group,
+                               int64_t cols_per_group, float* beta, uint64_t* ws, hipStream_t s) {
+  const GroupPlan plan = group_plan(n_out, k, rows_per_group, cols_per_group);
   const int64_t rpg = rows_per_group < n_out ? rows_per_group : n_out;
   const u32x4* wv = reinterpret_cast<const u32x4*>(w);
-  hipLaunchKernelGGL(group_partial_kernel, dim3((unsigned)plan.nb, (unsigned)plan.groups), dim3(kAbsThreads), 0, s,
-                     wv, n_out, k, rpg, plan, ws, beta);
+  hipLaunchKernelGGL(group_partial_kernel, dim3((unsigned)plan.nb, (unsigned)plan.gr, (unsigned)plan.gk),
+                     dim3(kAbsThreads), 0, s, wv, n_out, k, rpg, cols_per_group, plan, ws, beta);
   // groups of one absmean workgroup were finalized by it
   if (plan.nb > 1)
     hipLaunchKernelGGL(group_final_kernel, dim3((unsigned)plan.groups), dim3(kAbsThreads), 0, s, wv, n_out, k, rpg,
-                       plan, ws, beta);
+                       cols_per_group, plan, ws, beta);
   return hipGetLastError();
 }
 

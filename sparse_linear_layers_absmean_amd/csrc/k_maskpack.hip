@@ -325,9 +325,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     const int64_t c = cg + threadIdx.x;
     if (c < nchunks) {
-      // group scales (beta complete before the launch): the beta of this chunk's row group
+      // group scales (beta complete before the launch): the beta of this chunk's group
       const uint32_t tc =
-          d.beta_rows > 0 ? (__float_as_uint(fmaxf(d.beta[c / d.nkb / d.beta_rows], 1e-5f) * 0.5f) >> 16) * kOnes : t2;
+          d.beta_rows > 0 ? (__float_as_uint(fmaxf(d.beta[chunk_beta_index(d, c)], 1e-5f) * 0.5f) >> 16) * kOnes : t2;
       mask_pack_chunk<M, DROP, FMT, CODES>(dw, c, d, tc);
     }
   }
@@ -665,8 +665,8 @@ __global__ __launch_bounds__(kThreads) void mask_pack_kernel(const QBatch batch,
     load_chunk(d.w, c0, cnt, stage, dw);
     const int64_t c = c0 + threadIdx.x;
     if (c >= nchunks) return;
-    if (d.beta_rows > 0)                             // group scales: the beta of this chunk's row group
-      thr_mag = (int)(__float_as_uint(fmaxf(d.beta[c / d.nkb / d.beta_rows], 1e-5f) * 0.5f) >> 16);
+    if (d.beta_rows > 0)                             // group scales: the beta of this chunk's group
+      thr_mag = (int)(__float_as_uint(fmaxf(d.beta[chunk_beta_index(d, c)], 1e-5f) * 0.5f) >> 16);
     ChunkOut o = {};
 #pragma unroll
     for (int g = 0; g < 64 / M; ++g) {

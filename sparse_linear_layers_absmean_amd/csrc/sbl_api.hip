@@ -125,6 +125,7 @@ sbl::QDesc to_qdesc(const sbl_quant_item& it, int32_t fmt) {
   d.ws = reinterpret_cast<uint64_t*>(it.workspace);
   d.ws_words = it.workspace_bytes / 8;
   d.beta_rows = 0;
+  d.beta_kblocks = 0;
   d.mask = it.mask_bits;
   d.codes = it.codes;
   d.packed = it.packed;
@@ -413,26 +414,31 @@ int sbl_linear_batch(const sbl_linear_item* items, int32_t count, int32_t fmt, i
   return launch_status(sbl::launch_linear_batch(args, count, fmt, n, m, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int64_t sbl_workspace_bytes_grouped(int64_t n_out, int64_t k, int64_t rows_per_group) {
-  if (n_out < 1 || !k_ok(k) || n_out * k > kMaxElems || rows_per_group < 1) return -1;
-  const sbl::GroupPlan p = sbl::group_plan(n_out, k, rows_per_group);
-  if (p.groups > 65535) return -1;                   // one grid row per group
+}  // extern "C"
+
+namespace {
+
+// group scales: rows_per_group rows x cols_per_group features per beta
+int64_t workspace_bytes_groups(int64_t n_out, int64_t k, int64_t rpg, int64_t cpg) {
+  if (n_out < 1 || !k_ok(k) || n_out * k > kMaxElems || rpg < 1 || cpg < 64 || cpg % 64 != 0 || k % cpg != 0)
+    return -1;
+  const sbl::GroupPlan p = sbl::group_plan(n_out, k, rpg, cpg);
+  if (p.gr > 65535 || p.gk > 65535) return -1;       // grid rows and layers of the partial-sum launch
   return (8 * p.groups * p.region + 4095) / 4096 * 4096;
 }
 
-int sbl_quant_weights_grouped(const uint16_t* w_bf16, int64_t n_out, int64_t k, int32_t n, int32_t m,
-                              int64_t rows_per_group, float* beta, uint8_t* mask_bits, int8_t* codes, int32_t fmt,
-                              uint8_t* packed, uint8_t* meta, void* workspace, int64_t workspace_bytes,
-                              sbl_stream stream) {
-  if (rows_per_group < 1) return SBL_ERR_SHAPE;
+int quant_weights_groups(const uint16_t* w_bf16, int64_t n_out, int64_t k, int32_t n, int32_t m, int64_t rpg,
+                         int64_t cpg, float* beta, uint8_t* mask_bits, int8_t* codes, int32_t fmt, uint8_t* packed,
+                         uint8_t* meta, void* workspace, int64_t workspace_bytes, sbl_stream stream) {
+  if (rpg < 1 || cpg < 64 || cpg % 64 != 0 || k % cpg != 0) return SBL_ERR_SHAPE;
   // the per-matrix checks (their workspace size aside), then the group workspace's size
   const sbl_quant_item it{w_bf16, n_out, k, beta, mask_bits, codes, packed, meta, workspace, INT64_MAX};
   int st = check_quant(it, n, m, fmt);
   if (st != SBL_OK) return st;
-  const int64_t need = sbl_workspace_bytes_grouped(n_out, k, rows_per_group);
-  if (need < 0) return SBL_ERR_SHAPE;                // more than 65535 groups
+  const int64_t need = workspace_bytes_groups(n_out, k, rpg, cpg);
+  if (need < 0) return SBL_ERR_SHAPE;                // more than 65535 row or column groups
   if (workspace_bytes < need) return SBL_ERR_WORKSPACE;
-  const int64_t groups = (n_out + rows_per_group - 1) / rows_per_group;
+  const int64_t groups = (n_out + rpg - 1) / rpg * (k / cpg);
   const int64_t mask_b = n_out * (k / 8);
   const int64_t packed_b = fmt == SBL_FMT_DENSE2 ? n_out * (k / 4) : n_out * (k / m) * n / 4;
   if (ranges_overlap(beta, 4 * groups, mask_bits, mask_b) || ranges_overlap(beta, 4 * groups, codes, n_out * k) ||
@@ -441,15 +447,61 @@ int sbl_quant_weights_grouped(const uint16_t* w_bf16, int64_t n_out, int64_t k, 
       ranges_overlap(beta, 4 * groups, workspace, workspace_bytes))
     return SBL_ERR_SHAPE;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  st = launch_status(sbl::launch_grouped_beta(w_bf16, n_out, k, rows_per_group, beta,
+  st = launch_status(sbl::launch_grouped_beta(w_bf16, n_out, k, rpg, cpg, beta,
                                               reinterpret_cast<uint64_t*>(workspace), s));
   if (st != SBL_OK || (!mask_bits && !codes && !packed)) return st;
   sbl::QBatch b;
   b.count = 1;
   b.beta_ready = 1;
   b.d[0] = to_qdesc(it, fmt);
-  b.d[0].beta_rows = rows_per_group;
+  b.d[0].beta_rows = rpg;
+  b.d[0].beta_kblocks = cpg == k ? 0 : (int32_t)(cpg / 64);
   return launch_status(sbl::launch_mask_pack(b, n, m, s));
+}
+
+int linear_kgroups(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m, const float* beta,
+                   int64_t rpg, bool per_block, const int8_t* xq, const float* gamma, int64_t kg, int64_t m_tok,
+                   int64_t n_out, int64_t k, float* y, sbl_stream stream) {
+  if (rpg < 1 || kg < 64 || kg % 64 != 0 || k % kg != 0 || m_tok > 65535) return SBL_ERR_SHAPE;
+  const sbl_linear_item it{packed, meta, beta, xq, gamma, m_tok, n_out, k, y, nullptr};
+  const int st = check_linear(it, fmt, n, m);
+  if (st != SBL_OK || m_tok == 0 || n_out == 0) return st;
+  const int64_t betas = (n_out + rpg - 1) / rpg * (per_block ? k / kg : 1);
+  if (ranges_overlap(y, m_tok * n_out * 4, gamma, m_tok * (k / kg) * 4) ||
+      ranges_overlap(y, m_tok * n_out * 4, beta, 4 * betas))
+    return SBL_ERR_SHAPE;
+  return launch_status(sbl::launch_linear_kgrouped(packed, fmt == SBL_FMT_NM ? meta : nullptr, fmt, n, m, beta, rpg,
+                                                   per_block, xq, gamma, kg, m_tok, n_out, k, y,
+                                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t sbl_workspace_bytes_grouped(int64_t n_out, int64_t k, int64_t rows_per_group) {
+  return workspace_bytes_groups(n_out, k, rows_per_group, k);
+}
+
+int sbl_quant_weights_grouped(const uint16_t* w_bf16, int64_t n_out, int64_t k, int32_t n, int32_t m,
+                              int64_t rows_per_group, float* beta, uint8_t* mask_bits, int8_t* codes, int32_t fmt,
+                              uint8_t* packed, uint8_t* meta, void* workspace, int64_t workspace_bytes,
+                              sbl_stream stream) {
+  if (!k_ok(k)) return SBL_ERR_SHAPE;
+  return quant_weights_groups(w_bf16, n_out, k, n, m, rows_per_group, k, beta, mask_bits, codes, fmt, packed, meta,
+                              workspace, workspace_bytes, stream);
+}
+
+int64_t sbl_workspace_bytes_blocked(int64_t n_out, int64_t k, int64_t rows_per_group, int64_t cols_per_group) {
+  return workspace_bytes_groups(n_out, k, rows_per_group, cols_per_group);
+}
+
+int sbl_quant_weights_blocked(const uint16_t* w_bf16, int64_t n_out, int64_t k, int32_t n, int32_t m,
+                              int64_t rows_per_group, int64_t cols_per_group, float* beta, uint8_t* mask_bits,
+                              int8_t* codes, int32_t fmt, uint8_t* packed, uint8_t* meta, void* workspace,
+                              int64_t workspace_bytes, sbl_stream stream) {
+  return quant_weights_groups(w_bf16, n_out, k, n, m, rows_per_group, cols_per_group, beta, mask_bits, codes, fmt,
+                              packed, meta, workspace, workspace_bytes, stream);
 }
 
 int sbl_linear_grouped(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
@@ -486,16 +538,15 @@ int sbl_quant_acts_kgrouped(const float* x, int64_t m_tok, int64_t k, int64_t kg
 int sbl_linear_kgrouped(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
                         const float* beta, int64_t rows_per_group, const int8_t* xq, const float* gamma, int64_t kg,
                         int64_t m_tok, int64_t n_out, int64_t k, float* y, sbl_stream stream) {
-  if (rows_per_group < 1 || kg < 64 || kg % 64 != 0 || k % kg != 0 || m_tok > 65535) return SBL_ERR_SHAPE;
-  const sbl_linear_item it{packed, meta, beta, xq, gamma, m_tok, n_out, k, y, nullptr};
-  const int st = check_linear(it, fmt, n, m);
-  if (st != SBL_OK || m_tok == 0 || n_out == 0) return st;
-  if (ranges_overlap(y, m_tok * n_out * 4, gamma, m_tok * (k / kg) * 4) ||
-      ranges_overlap(y, m_tok * n_out * 4, beta, 4 * ((n_out + rows_per_group - 1) / rows_per_group)))
-    return SBL_ERR_SHAPE;
-  return launch_status(sbl::launch_linear_kgrouped(packed, fmt == SBL_FMT_NM ? meta : nullptr, fmt, n, m, beta,
-                                                   rows_per_group, xq, gamma, kg, m_tok, n_out, k, y,
-                                                   reinterpret_cast<hipStream_t>(stream)));
+  return linear_kgroups(packed, meta, fmt, n, m, beta, rows_per_group, false, xq, gamma, kg, m_tok, n_out, k, y,
+                        stream);
+}
+
+int sbl_linear_blocked(const uint8_t* packed, const uint8_t* meta, int32_t fmt, int32_t n, int32_t m,
+                       const float* beta, int64_t rows_per_group, const int8_t* xq, const float* gamma, int64_t kg,
+                       int64_t m_tok, int64_t n_out, int64_t k, float* y, sbl_stream stream) {
+  return linear_kgroups(packed, meta, fmt, n, m, beta, rows_per_group, true, xq, gamma, kg, m_tok, n_out, k, y,
+                        stream);
 }
 
 }  // extern "C"

@@ -103,7 +103,16 @@ struct QDesc {
   int64_t n_out;          // rows; k / 64 blocks per row (panel layout of packed, meta)
   int32_t nkb;
   int32_t fmt;            // format of `packed`
+  int32_t beta_kblocks;   // group scales: 0 one beta per row group; > 0 per row group and block of
+                          // beta_kblocks k-blocks, beta[(row / beta_rows) * (nkb / beta_kblocks) + kb / beta_kblocks]
 };
+
+// group scales: index of the beta of chunk c (64 weights: row c / nkb, k-block c % nkb)
+__host__ __device__ __forceinline__ int64_t chunk_beta_index(const QDesc& d, int64_t c) {
+  const int64_t row = c / d.nkb;
+  if (d.beta_kblocks <= 0) return row / d.beta_rows;
+  return (row / d.beta_rows) * (d.nkb / d.beta_kblocks) + (c - row * d.nkb) / d.beta_kblocks;
+}
 constexpr int kMaxQDesc = 8;
 struct QBatch {
   QDesc d[kMaxQDesc];
@@ -183,26 +192,32 @@ bool gemm_fits(const LinearArgs& a, int kind);
 hipError_t launch_gemm24_group(const LinearArgs* items, int count, hipStream_t s);
 
 // Group scales (k_grouped.hip): one exact absmean beta per block of
-// rows_per_group output rows.  Workspace: one region per group of
-// grouped_region_words(..) words (the absmean slot layout of one group).
+// rows_per_group output rows x cols_per_group features (cols_per_group = k:
+// row groups).  Groups are numbered row group first: g = gr * gk + gc.
+// Workspace: one region of `region` words per group (the absmean slot
+// layout of one group).
 struct GroupPlan {
   int64_t groups, nb, vpt, region;   // region: words per group
+  int64_t gr, gk;                    // row groups, column groups (groups = gr * gk)
 };
-inline GroupPlan group_plan(int64_t n_out, int64_t k, int64_t rows_per_group) {
+inline GroupPlan group_plan(int64_t n_out, int64_t k, int64_t rows_per_group, int64_t cols_per_group) {
   const int64_t rpg = rows_per_group < n_out ? rows_per_group : n_out;
-  const AbsmeanPlan p = absmean_plan(rpg * k);
-  return GroupPlan{(n_out + rpg - 1) / rpg, p.nb, p.vpt, ws_limb_base(p.nb) + kWsLimbWords * p.nb};
+  const AbsmeanPlan p = absmean_plan(rpg * cols_per_group);
+  const int64_t gr = (n_out + rpg - 1) / rpg, gk = k / cols_per_group;
+  return GroupPlan{gr * gk, p.nb, p.vpt, ws_limb_base(p.nb) + kWsLimbWords * p.nb, gr, gk};
 }
-// beta[g] for every group (partial sums, then one finalizing workgroup per group)
-hipError_t launch_grouped_beta(const uint16_t* w, int64_t n_out, int64_t k, int64_t rows_per_group, float* beta,
-                               uint64_t* ws, hipStream_t s);
+// beta[g] for every group (partial sums, then one finalizing workgroup per
+// group, or the partial-sum workgroup itself when one holds the group)
+hipError_t launch_grouped_beta(const uint16_t* w, int64_t n_out, int64_t k, int64_t rows_per_group,
+                               int64_t cols_per_group, float* beta, uint64_t* ws, hipStream_t s);
 
 // Activation groups along k (kg features per gamma; kg % 64 == 0, k % kg == 0)
 hipError_t launch_quant_acts_kgrouped(const float* x, int64_t m_tok, int64_t k, int64_t kg, int8_t* xq, float* gamma,
                                       hipStream_t s);
+// beta_per_block: beta [row groups][k / kg] (block scales) instead of [row groups]
 hipError_t launch_linear_kgrouped(const uint8_t* packed, const uint8_t* meta, int fmt, int n, int m, const float* beta,
-                                  int64_t rows_per_group, const int8_t* xq, const float* gamma, int64_t kg,
-                                  int64_t m_tok, int64_t n_out, int64_t k, float* y, hipStream_t s);
+                                  int64_t rows_per_group, bool beta_per_block, const int8_t* xq, const float* gamma,
+                                  int64_t kg, int64_t m_tok, int64_t n_out, int64_t k, float* y, hipStream_t s);
 
 // Backward of the layer (k_backward.hip): dx and/or dw (each nullable).
 struct BackwardArgs {

@@ -24,7 +24,7 @@ SBL_FMT_NM = 1
 # weight-preparation variants and execution choices (sbl_quant_weights_batch_ex flags)
 SBL_QW_DEFAULT, SBL_QW_BETA_KEPT, SBL_QW_MASK_FROM_CODES = 0, 1, 2
 SBL_QW_TWO_PASS, SBL_QW_NO_WAIT = 4, 8
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32
@@ -110,6 +110,14 @@ def load():
                                        _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]
     lib.sbl_quant_acts_kgrouped.restype = ctypes.c_int
     lib.sbl_quant_acts_kgrouped.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]
+    lib.sbl_workspace_bytes_blocked.restype = _c_i64
+    lib.sbl_workspace_bytes_blocked.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64]
+    lib.sbl_quant_weights_blocked.restype = ctypes.c_int
+    lib.sbl_quant_weights_blocked.argtypes = [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_p,
+                                              _c_i32, _c_p, _c_p, _c_p, _c_i64, _c_p]
+    lib.sbl_linear_blocked.restype = ctypes.c_int
+    lib.sbl_linear_blocked.argtypes = [_c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_i64, _c_p, _c_p, _c_i64,
+                                       _c_i64, _c_i64, _c_i64, _c_p, _c_p]
     lib.sbl_linear_kgrouped.restype = ctypes.c_int
     lib.sbl_linear_kgrouped.argtypes = [_c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_i64, _c_p, _c_p, _c_i64,
                                         _c_i64, _c_i64, _c_i64, _c_p, _c_p]
@@ -327,6 +335,47 @@ def sbl_linear_grouped(packed, meta, fmt: int, n: int, m: int, beta, rows_per_gr
                                 m_tok, n_out, k, _ptr(y, torch.float32, m_tok * n_out * 4, "y"),
                                 _ptr(acc, torch.int32, m_tok * n_out * 4, "acc"), _stream(stream))
     _check("sbl_linear_grouped", st)
+
+
+def sbl_workspace_bytes_blocked(n_out: int, k: int, rows_per_group: int, cols_per_group: int) -> int:
+    return load().sbl_workspace_bytes_blocked(n_out, k, rows_per_group, cols_per_group)
+
+
+def sbl_quant_weights_blocked(w_bf16, n: int, m: int, rows_per_group: int, cols_per_group: int, beta, workspace,
+                              mask_bits=None, codes=None, fmt: int = SBL_FMT_DENSE2, packed=None, meta=None,
+                              stream=None):
+    """Block scales: beta fp32 [ceil(n_out / rows_per_group)][k // cols_per_group]."""
+    lib = load()
+    n_out, k = w_bf16.shape
+    gr = -(-n_out // rows_per_group) if rows_per_group > 0 else 1
+    gk = k // cols_per_group if cols_per_group > 0 else 1
+    pb = lib.sbl_packed_bytes(n_out, k, n, m, fmt) if packed is not None else 0
+    wsb = lib.sbl_workspace_bytes_blocked(n_out, k, rows_per_group, cols_per_group)
+    st = lib.sbl_quant_weights_blocked(
+        _ptr(w_bf16, _W16, n_out * k * 2, "w_bf16"), n_out, k, n, m, rows_per_group, cols_per_group,
+        _ptr(beta, torch.float32, 4 * gr * gk, "beta"),
+        _ptr(mask_bits, torch.uint8, n_out * k // 8, "mask_bits"), _ptr(codes, torch.int8, n_out * k, "codes"),
+        fmt, _ptr(packed, torch.uint8, max(pb, 0), "packed"),
+        _ptr(meta, torch.uint8, n_out * k // 8, "meta") if fmt == SBL_FMT_NM else None,
+        _ptr(workspace, None, max(wsb, 0), "workspace"), _nbytes(workspace), _stream(stream))
+    _check("sbl_quant_weights_blocked", st)
+
+
+def sbl_linear_blocked(packed, meta, fmt: int, n: int, m: int, beta, rows_per_group: int, xq, gamma, kg: int,
+                       n_out: int, y, stream=None):
+    """Products with block scales: beta [ceil(n_out / rows_per_group)][k // kg]."""
+    lib = load()
+    m_tok, k = xq.shape
+    gr = -(-n_out // rows_per_group) if rows_per_group > 0 else 1
+    gk = k // kg if kg > 0 else 1
+    pb = lib.sbl_packed_bytes(n_out, k, n, m, fmt) if n_out > 0 else 0
+    st = lib.sbl_linear_blocked(_ptr(packed, torch.uint8, max(pb, 0), "packed"),
+                                _ptr(meta, torch.uint8, n_out * k // 8, "meta") if fmt == SBL_FMT_NM else None,
+                                fmt, n, m, _ptr(beta, torch.float32, 4 * gr * gk, "beta"), rows_per_group,
+                                _ptr(xq, torch.int8, m_tok * k, "xq"),
+                                _ptr(gamma, torch.float32, m_tok * gk * 4, "gamma"), kg, m_tok, n_out, k,
+                                _ptr(y, torch.float32, m_tok * n_out * 4, "y"), _stream(stream))
+    _check("sbl_linear_blocked", st)
 
 
 def sbl_quant_acts_kgrouped(x, kg: int, xq, gamma, stream=None):

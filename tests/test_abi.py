@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.sbl_abi_version() == 10
+    assert lib.sbl_abi_version() == 11
     for st in range(7):
         assert len(lib.sbl_status_string(st)) > 0
     assert lib.sbl_last_hip_error() == 0
@@ -383,6 +383,35 @@ def test_grouped_validation(lib):
     assert lin(y=A + F + 8) == 2                            # y overlaps beta (4 groups)
     assert lin(acc=A + F + 12) == 2                         # acc overlaps beta
     assert lin(fmt=3) == 4
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation runs only on GPU-less hosts")
+def test_blocked_validation(lib):
+    F = 1 << 40
+    wsb = lib.sbl_workspace_bytes_blocked
+    assert wsb(16, 256, 4, 64) > 0
+    assert wsb(16, 256, 4, 96) == -1                        # not a multiple of 64
+    assert wsb(16, 256, 4, 192) == -1                       # does not divide k
+    assert wsb(16, 256, 0, 64) == -1
+    assert wsb(16, 256, 4, 256) == lib.sbl_workspace_bytes_grouped(16, 256, 4)
+    ws = wsb(16, 256, 4, 64)
+    fq = lib.sbl_quant_weights_blocked
+
+    def q(rpg=4, cpg=64, beta=A + F, workspace=A + 4 * F, wsb_=ws):
+        return fq(A, 16, 256, 6, 8, rpg, cpg, beta, None, None, 1, A + 2 * F, A + 3 * F, workspace, wsb_, None)
+
+    assert q(cpg=96) == 2
+    assert q(rpg=0) == 2
+    assert q(wsb_=ws - 8) == 6
+    assert q(beta=None) == 1
+    assert q(beta=A + 2 * F + 48) == 2                      # beta (4 x 4 blocks) overlaps packed
+    fl = lib.sbl_linear_blocked
+
+    def lin(kg=64, y=A + 6 * F, beta=A + F):
+        return fl(A + 2 * F, A + 3 * F, 1, 6, 8, beta, 4, A + 7 * F, A + 8 * F, kg, 2, 16, 256, y, None)
+
+    assert lin(kg=96) == 2
+    assert lin(y=A + F + 48) == 2                           # y overlaps beta (4 x 4)
 
 
 @pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation runs only on GPU-less hosts")

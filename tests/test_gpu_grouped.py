@@ -175,3 +175,79 @@ def test_group_scales_at_benchmark_shapes(idx, rpg):
     betas, keep, codes = O.quant_weights_grouped(bits, 6, 8, rpg)
     _, y_ref = O.linear_kgrouped(codes, q, betas, rpg, g, kg)
     assert np.array_equal(to_np(y), y_ref)
+
+
+# ---- block scales: one beta per block of rows x features ----
+
+def _run_blocked(bits, x, n, m, fmt, rpg, cpg, label):
+    """sbl_quant_weights_blocked (twice, one workspace) and sbl_linear_blocked
+    against the oracle: beta, mask, codes, packed bytes and metadata bit for
+    bit; y bit for bit (the same fp32 operations in the same order)."""
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    n_out, k = bits.shape
+    gr, gk = -(-n_out // rpg), k // cpg
+    say(f"block scales {label} {n_out}x{k} rows_per_group={rpg} cols_per_group={cpg} {n}:{m} fmt={fmt}")
+    beta = torch.full((gr, gk), -1.0, device="cuda")
+    mask = torch.empty((n_out, k // 8), dtype=torch.uint8, device="cuda")
+    codes = torch.empty((n_out, k), dtype=torch.int8, device="cuda")
+    packed = torch.empty(sbl.sbl_packed_bytes(n_out, k, n, m, fmt), dtype=torch.uint8, device="cuda")
+    meta = torch.empty((n_out, k // 8), dtype=torch.uint8, device="cuda") if fmt == FMT_NM else None
+    ws = torch.full((sbl.sbl_workspace_bytes_blocked(n_out, k, rpg, cpg),), 0xFF, dtype=torch.uint8, device="cuda")
+    w = to_dev(bits)
+    for _ in range(2):
+        sbl.sbl_quant_weights_blocked(w, n, m, rpg, cpg, beta, ws, mask_bits=mask, codes=codes, fmt=fmt,
+                                      packed=packed, meta=meta)
+    t = x.shape[0]
+    xq = torch.empty((t, k), dtype=torch.int8, device="cuda")
+    gamma = torch.empty((t, gk), dtype=torch.float32, device="cuda")
+    sbl.sbl_quant_acts_kgrouped(to_dev(x.astype(np.float32)), cpg, xq, gamma)
+    y = torch.full((t, n_out), float("nan"), dtype=torch.float32, device="cuda")
+    sbl.sbl_linear_blocked(packed, meta, fmt, n, m, beta, rpg, xq, gamma, cpg, n_out, y)
+    torch.cuda.synchronize()
+    betas, keep, c = O.quant_weights_blocked(bits, n, m, rpg, cpg)
+    assert np.array_equal(to_np(beta), betas)
+    assert np.array_equal(to_np(mask), O.pack_bitmap(keep))
+    assert np.array_equal(to_np(codes), c)
+    if fmt == FMT_DENSE2:
+        assert np.array_equal(packed_rows(to_np(packed), n_out, k, fmt, n, m), O.pack_dense2(c))
+    else:
+        if (k * n // m) % 4 == 0:
+            assert np.array_equal(packed_rows(to_np(packed), n_out, k, fmt, n, m), O.pack_nm(c, keep, n, m))
+        assert np.array_equal(meta_rows(to_np(meta), n_out, k), O.pack_bitmap(keep))
+    q, g = O.quant_acts_kgrouped(x, cpg)
+    assert np.array_equal(to_np(xq), q) and np.array_equal(to_np(gamma), g)
+    _, y_ref = O.linear_kgrouped(c, q, betas, rpg, g, cpg)
+    assert np.array_equal(to_np(y), y_ref)
+
+
+@pytest.mark.parametrize("fmt,n,m", [(FMT_NM, 6, 8), (FMT_DENSE2, 6, 8), (FMT_NM, 2, 4), (FMT_NM, 5, 8)])
+@pytest.mark.parametrize("n_out,k,rpg,cpg,t", [(64, 256, 1, 64, 2), (130, 1536, 16, 512, 3), (100, 640, 1000, 128, 1),
+                                               (300, 2048, 128, 256, 5), (37, 4096, 37, 4096, 2)])
+def test_block_scales_match_oracle(n_out, k, rpg, cpg, t, fmt, n, m):
+    """Blocks held by one absmean workgroup and blocks split over several (300 x
+    2048 with 128 x 256 blocks: 32768 values each), a ragged last row block, and
+    blocks spanning k (the row-group case)."""
+    rng = np.random.default_rng([99, n_out, k, rpg, cpg, fmt, n, m])
+    bits = synth.gaussian_masters(rng, n_out, k, outlier_frac=0.01)
+    x = synth.gaussian_acts(rng, t, k, hot_channels=2)
+    _run_blocked(bits, x, n, m, fmt, rpg, cpg, "gaussian")
+
+
+@pytest.mark.parametrize("rpg,cpg", [(1, 64), (7, 128), (260, 256)])
+def test_block_scales_rare_values(rpg, cpg):
+    """Zeros, subnormals, tiny and large magnitudes: exact out-of-window sums per block."""
+    rng = np.random.default_rng([100, rpg, cpg])
+    bits = synth.rare_mixture(rng, 260, 512)
+    x = synth.gaussian_acts(rng, 2, 512)
+    _run_blocked(bits, x, 6, 8, FMT_NM, rpg, cpg, "rare mixture")
+
+
+@pytest.mark.parametrize("idx", [4, 6])
+def test_block_scales_at_benchmark_shapes(idx):
+    """A 3B-class gate (8640 x 3200) or down (3200 x 8640) matrix of the decode
+    workload, 6:8 N:M, M = 1, beta per 128 rows x 320 features."""
+    name, n_out, k = synth.block_shapes(3200, 8640)[idx]
+    bits = synth.workload_masters("b3", idx, n_out, k)
+    x = synth.workload_acts("b3", idx, 1, k)
+    _run_blocked(bits, x, 6, 8, FMT_NM, 128, 320, f"3B {name}")
