@@ -10,8 +10,11 @@
 //    slice w of group (gr, gc) exactly (sbl_partial.h) into slot w of the
 //    group's workspace region; every group uses the partition of a full group.
 //  * group_final_kernel: one workgroup per group rounds the exact mean once
-//    (sbl_beta.h) into beta[g]; a group whose masters fit one absmean
-//    workgroup is rounded by that workgroup instead (no second launch).
+//    (sbl_beta.h) into beta[g].
+//  * group_wave_kernel: groups of at most 2048 16-byte vectors (one absmean
+//    workgroup's worth) instead take one wave each, 4 per workgroup, which
+//    sums them exactly in registers and rounds beta[g] itself: one launch,
+//    no workspace traffic, no workgroup-wide reductions.
 //  * The mask/pack kernel then reads beta per chunk's group (QDesc.beta_rows,
 //    beta_kblocks), and the products' epilogues read it per row
 //    (LinearArgs.beta_rows) or per row and feature block (the
@@ -26,7 +29,7 @@ using namespace part;
 
 __global__ __launch_bounds__(kAbsThreads) void group_partial_kernel(const u32x4* __restrict__ w, int64_t n_out,
                                                                     int64_t k, int64_t rpg, int64_t cpg,
-                                                                    GroupPlan plan, uint64_t* ws, float* beta) {
+                                                                    GroupPlan plan, uint64_t* ws) {
   const int64_t gr = blockIdx.y, gc = blockIdx.z, wg = blockIdx.x;
   const int64_t g = gr * plan.gk + gc;
   const int64_t r0 = gr * rpg;
@@ -71,21 +74,67 @@ __global__ __launch_bounds__(kAbsThreads) void group_partial_kernel(const u32x4*
     }
   }
   publish_partial(ws + g * plan.region, plan.nb, wg, acc0, acc1, rare, bins);
-  if (plan.nb == 1) {
-    // the group's only partial sum is this workgroup's: round the exact mean
-    // here (thread 0's workspace stores are visible to the workgroup after
-    // the barrier)
-    __syncthreads();
-    QDesc d = {};
-    d.w = w + r0 * k / 8;
-    d.nvec = nvec;
-    d.count = rows * cpg;
-    d.nb = 1;
-    d.vpt = plan.vpt;
-    d.ws = ws + g * plan.region;
-    d.beta = beta + g;
-    (void)beta::workgroup_beta(d, true);
+}
+
+// One wave per group of at most kWaveGroupVecs vectors: every lane adds at
+// most 32 vectors (256 values, far below the 2^14 of the fast-window bound)
+// into its fp64 sums and the wave's own exponent bins; lane 0 then forms the
+// exact total (fast-window units of 2^-38, and the bins as a multi-word
+// integer in units of 2^-133 when the wave met out-of-window values) and
+// rounds the quotient once, as the workspace path's finalize does.
+constexpr int kWaveGroups = 4;                 // waves (groups) per workgroup
+constexpr int64_t kWaveGroupVecs = 2048;
+
+__global__ __launch_bounds__(64 * kWaveGroups) void group_wave_kernel(const u32x4* __restrict__ w, int64_t n_out,
+                                                                      int64_t k, int64_t rpg, int64_t cpg,
+                                                                      GroupPlan plan, float* __restrict__ beta) {
+  __shared__ unsigned long long bins_all[kWaveGroups][256];
+  __shared__ uint32_t limbs_all[kWaveGroups][beta::kLimbs + 2];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  unsigned long long* bins = bins_all[wave];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bins[lane + 64 * i] = 0;
+  __syncthreads();
+  const int64_t g = (int64_t)blockIdx.x * kWaveGroups + wave;
+  const bool live = g < plan.groups;                 // waves past the last group only join the barriers
+  const int64_t gr = live ? g / plan.gk : 0, gc = live ? g % plan.gk : 0;
+  const int64_t r0 = gr * rpg;
+  const int64_t rows = n_out - r0 < rpg ? n_out - r0 : rpg;
+  const uint32_t nvec = live ? (uint32_t)(rows * cpg / 8) : 0u;
+  const uint32_t vpr = (uint32_t)(cpg / 8);          // vectors per row of the group
+  const u32x4* base = w + r0 * (k / 8) + gc * vpr;
+  double acc0 = 0.0, acc1 = 0.0;
+  uint32_t rare = 0;
+  for (uint32_t j0 = 0; j0 < nvec; j0 += 64 * 8) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t i = j0 + (uint32_t)lane + 64u * u;
+      v[u] = i < nvec ? base[(int64_t)(i / vpr) * (k / 8) + i % vpr] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) consume(v[u], acc0, acc1, bins, rare);
   }
+  // both sums are exact multiples of 2^-38 below 2^15
+  unsigned long long units = (unsigned long long)(acc0 * 0x1p38) + (unsigned long long)(acc1 * 0x1p38);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) units += __shfl_xor(units, off, 64);
+  const bool wave_rare = __ballot(rare != 0) != 0;
+  __syncthreads();                                   // the wave's bin atomics are done
+  if (!live || lane != 0) return;
+  const uint64_t count = (uint64_t)(rows * cpg);
+  float b;
+  if (!wave_rare) {
+    b = beta::round_quotient_fast((uint32_t)units, units >> 32, count);
+  } else {
+    uint32_t* limbs = limbs_all[wave];
+    for (int i = 0; i < beta::kLimbs + 2; ++i) limbs[i] = 0;
+    for (int e = 0; e < 256; ++e) beta::add_shifted(limbs, bins[e], max(e, 1) - 1);   // significand * 2^(max(e,1)-134)
+    beta::add_shifted(limbs, (uint32_t)units, 95);                                   // 2^-38 = 2^95 * 2^-133
+    beta::add_shifted(limbs, units >> 32, 95 + 32);
+    b = beta::round_quotient(limbs, count);
+  }
+  beta[g] = b;
 }
 
 __global__ __launch_bounds__(kAbsThreads) void group_final_kernel(const u32x4* w, int64_t n_out, int64_t k,
@@ -286,12 +335,15 @@ hipError_t launch_grouped_beta(const uint16_t* w, int64_t n_out, int64_t k, int6
   const GroupPlan plan = group_plan(n_out, k, rows_per_group, cols_per_group);
   const int64_t rpg = rows_per_group < n_out ? rows_per_group : n_out;
   const u32x4* wv = reinterpret_cast<const u32x4*>(w);
+  if ((rpg * cols_per_group) / 8 <= kWaveGroupVecs) {     // small groups: one wave each, one launch
+    hipLaunchKernelGGL(group_wave_kernel, dim3((unsigned)((plan.groups + kWaveGroups - 1) / kWaveGroups)),
+                       dim3(64 * kWaveGroups), 0, s, wv, n_out, k, rpg, cols_per_group, plan, beta);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(group_partial_kernel, dim3((unsigned)plan.nb, (unsigned)plan.gr, (unsigned)plan.gk),
-                     dim3(kAbsThreads), 0, s, wv, n_out, k, rpg, cols_per_group, plan, ws, beta);
-  // groups of one absmean workgroup were finalized by it
-  if (plan.nb > 1)
-    hipLaunchKernelGGL(group_final_kernel, dim3((unsigned)plan.groups), dim3(kAbsThreads), 0, s, wv, n_out, k, rpg,
-                       cols_per_group, plan, ws, beta);
+                     dim3(kAbsThreads), 0, s, wv, n_out, k, rpg, cols_per_group, plan, ws);
+  hipLaunchKernelGGL(group_final_kernel, dim3((unsigned)plan.groups), dim3(kAbsThreads), 0, s, wv, n_out, k, rpg,
+                     cols_per_group, plan, ws, beta);
   return hipGetLastError();
 }
 
