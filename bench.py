@@ -583,14 +583,15 @@ def bench_prefill(torch, np, sbl, dev, tm, masters_by_block, cases):
 
 # --------------------------------------------------------------------------- 13B training-step path
 
-def bench_train13b(torch, np, sbl, dev, tm, masters13):
+def bench_train13b(torch, np, sbl, dev, tm, masters13, fname="nm68"):
     """The training-step path of a 13B-class block: per-step weight preparation from the
-    BF16 masters (exact beta, 6:8 mask with planted near-ties, codes, N:M packing), the
-    forward products at 4096 tokens (activation quantization + GEMM per input) and the
-    layer's backward (dX and dW of every matrix from a synthetic BF16 dY).  Graph replays
-    over 2 copies of masters and activations."""
+    BF16 masters (exact beta, 6:8 mask with planted near-ties, codes, packing in the
+    storage `fname`: N:M codes + bitmap, or DENSE2), the forward products at 4096 tokens
+    (activation quantization + GEMM per input) and the layer's backward (dX and dW of
+    every matrix from a synthetic BF16 dY).  Graph replays over 2 copies of masters and
+    activations."""
     import synth
-    fmt, n, m = FORMATS["nm68"]
+    fmt, n, m = FORMATS[fname]
     mats = mats_of("13b")
     m_tok = 4096
     copies = 2
@@ -645,7 +646,8 @@ def bench_train13b(torch, np, sbl, dev, tm, masters13):
     ops = 2 * m_tok * weights
     del state, dys, dxs, dws, bws
     torch.cuda.empty_cache()
-    return {"workload": f"Training-step path, {BLOCKS['13b'][3]}, 6:8 N:M, M=4096 tokens, "
+    storage = "N:M codes + bitmap" if fname == "nm68" else "DENSE2 (2 bits per weight)"
+    return {"workload": f"Training-step path, {BLOCKS['13b'][3]}, 6:8 stored {storage}, M=4096 tokens, "
                         "masters with near-ties planted on the keep boundary",
             "ms_per_step": round(step_ms, 4),
             "with_backward_ms_per_step": round(full_ms, 4), "backward_ms": round(bwd_ms, 4),
@@ -1136,6 +1138,7 @@ def main():
         line["prefill"] = bench_prefill(torch, np, sbl, dev, tm, masters, args.prefill_cases)
     if "train13b" in sections:
         line["train_step_13b"] = bench_train13b(torch, np, sbl, dev, tm, masters["13b"])
+        line["train_step_13b_dense2"] = bench_train13b(torch, np, sbl, dev, tm, masters["13b"], "dense2")
     masters.pop("13b", None)
     if "act_quant" in sections:
         line["act_quant"] = bench_act_quant(torch, sbl, dev, tm)
