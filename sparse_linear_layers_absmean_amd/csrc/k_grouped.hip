@@ -214,9 +214,13 @@ __device__ __forceinline__ KgLoad kg_issue(const uint8_t* packed, const uint8_t*
       L.keep = (uint64_t)mv.x | ((uint64_t)mv.y << 32);
       const int bb = 16 * n / m;                          // code bytes of a block
       const uint8_t* cp = packed + panel_offset(n_out, nkb, bb, row, kb);
+      if (bb % 4 == 0) {                                   // 6:8, 2:4, ...: block offsets are dword-aligned
+        if (4 * q < bb) L.w = *reinterpret_cast<const uint32_t*>(cp + 4 * q);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * q + i < bb) L.w |= (uint32_t)cp[4 * q + i] << (8 * i);
+        for (int i = 0; i < 4; ++i)
+          if (4 * q + i < bb) L.w |= (uint32_t)cp[4 * q + i] << (8 * i);
+      }
     }
   }
   return L;
