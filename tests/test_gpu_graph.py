@@ -98,3 +98,79 @@ def test_step_graph_replays_match_eager(fmt, n, m, m_tok):
         if rep == 1:                                # an eager step between replays
             step()
             torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("m_tok", [3, 40])
+def test_group_scale_graph_replays_match_eager(m_tok):
+    """Group scales in a graph: beta per row (one wave per group), beta per
+    block of rows x features (partial sums through the workspace), the
+    products with beta per row (GEMV or GEMM epilogue) and with beta per
+    block and gamma per feature block; every replay equals the eager step."""
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    rng = np.random.default_rng([42, m_tok])
+    n_out, k, rpg, bk_rows, kg = 300, 1024, 1, 128, 256
+    bits = synth.gaussian_masters(rng, n_out, k, outlier_frac=0.01)
+    x_np = synth.gaussian_acts(rng, m_tok, k, hot_channels=2)
+    w, x = to_dev(bits), to_dev(x_np)
+    pb = sbl.sbl_packed_bytes(n_out, k, 6, 8, FMT_NM)
+    gr, gk = -(-n_out // bk_rows), k // kg
+    buf = dict(
+        beta_r=torch.empty(n_out, device="cuda"), packed_r=torch.empty(pb, dtype=torch.uint8, device="cuda"),
+        meta_r=torch.empty((n_out, k // 8), dtype=torch.uint8, device="cuda"),
+        beta_b=torch.empty((gr, gk), device="cuda"), packed_b=torch.empty(pb, dtype=torch.uint8, device="cuda"),
+        meta_b=torch.empty((n_out, k // 8), dtype=torch.uint8, device="cuda"),
+        xq=torch.empty((m_tok, k), dtype=torch.int8, device="cuda"), gamma=torch.empty(m_tok, device="cuda"),
+        xqk=torch.empty((m_tok, k), dtype=torch.int8, device="cuda"), gammak=torch.empty((m_tok, gk), device="cuda"),
+        y_r=torch.empty((m_tok, n_out), device="cuda"), y_b=torch.empty((m_tok, n_out), device="cuda"))
+    ws_r = torch.empty(sbl.sbl_workspace_bytes_grouped(n_out, k, rpg), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(sbl.sbl_workspace_bytes_blocked(n_out, k, bk_rows, kg), dtype=torch.uint8, device="cuda")
+
+    def step():
+        sbl.sbl_quant_weights_grouped(w, 6, 8, rpg, buf["beta_r"], ws_r, fmt=FMT_NM, packed=buf["packed_r"],
+                                      meta=buf["meta_r"])
+        sbl.sbl_quant_weights_blocked(w, 6, 8, bk_rows, kg, buf["beta_b"], ws_b, fmt=FMT_NM, packed=buf["packed_b"],
+                                      meta=buf["meta_b"])
+        sbl.sbl_quant_acts(x, buf["xq"], buf["gamma"])
+        sbl.sbl_linear_grouped(buf["packed_r"], buf["meta_r"], FMT_NM, 6, 8, buf["beta_r"], rpg, buf["xq"],
+                               buf["gamma"], n_out, buf["y_r"])
+        sbl.sbl_quant_acts_kgrouped(x, kg, buf["xqk"], buf["gammak"])
+        sbl.sbl_linear_blocked(buf["packed_b"], buf["meta_b"], FMT_NM, 6, 8, buf["beta_b"], bk_rows, buf["xqk"],
+                               buf["gammak"], kg, n_out, buf["y_b"])
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return {key: to_np(v).copy() for key, v in buf.items()}
+
+    say(f"group-scale graph eager m_tok={m_tok}")
+    step()
+    eager = snapshot()
+    betas, keep, codes = O.quant_weights_grouped(bits, 6, 8, rpg)
+    assert np.array_equal(eager["beta_r"], betas)
+    q, g = O.quant_acts(x_np)
+    acc = O.contract(codes, q)
+    check_y(eager["y_r"], O.rescale_grouped(acc, betas, rpg, g), acc)
+    bb, keepb, codesb = O.quant_weights_blocked(bits, 6, 8, bk_rows, kg)
+    assert np.array_equal(eager["beta_b"], bb)
+    qk, gk_ref = O.quant_acts_kgrouped(x_np, kg)
+    _, yb = O.linear_kgrouped(codesb, qk, bb, bk_rows, gk_ref, kg)
+    assert np.array_equal(eager["y_b"], yb)
+
+    graph = torch.cuda.CUDAGraph()
+    for v in buf.values():
+        v.zero_()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        for v in buf.values():                      # eager work between replays
+            v.zero_()
+        torch.cuda.synchronize()
+        say(f"group-scale graph replay {rep}")
+        graph.replay()
+        got = snapshot()
+        for key, want in eager.items():
+            assert np.array_equal(got[key].view(np.uint8), want.view(np.uint8)), (rep, key)
+        if rep == 1:
+            step()
+            torch.cuda.synchronize()
