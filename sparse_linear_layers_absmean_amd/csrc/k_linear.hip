@@ -78,6 +78,12 @@ struct PanelLane {
   int nfull;                    // full panels
 };
 
+// The weights are streamed once per call: nontemporal cache policy (bit "nt"
+// of the buffer instruction).  Measured against the default policy on every
+// block of the decode table: 0.7B 17.9 -> 15.8 us, 3B 23.7 -> 21.4 us, 70B
+// 58.4 -> 55.4 us at one token (DENSE2), and 3-12% at 4-16 tokens and for N:M.
+constexpr int kWNt = 2;
+
 template <int KIND>
 __device__ __forceinline__ void load_w(WStage& s, const Rsrc& rs, const PanelLane& pl, int p, int g, bool kok) {
   constexpr uint32_t bw = kBlockBytes<KIND>;
@@ -85,15 +91,15 @@ __device__ __forceinline__ void load_w(WStage& s, const Rsrc& rs, const PanelLan
   const uint32_t ow = kok ? (uint32_t)p * pl.pb_w + (full ? pl.full_w : pl.last_w) + (uint32_t)g * bw : kFar;
   const uint32_t om = kok ? (uint32_t)p * pl.pb_m + (full ? pl.full_m : pl.last_m) + (uint32_t)g * 8u : kFar;
   if constexpr (KIND == kDense2) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs.w, ow, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs.w, ow, 0, kWNt);
     s.a[0] = v[0]; s.a[1] = v[1]; s.a[2] = v[2]; s.a[3] = v[3];
   } else if constexpr (KIND == kNm68) {
-    const auto c = __builtin_amdgcn_raw_buffer_load_b96(rs.w, ow, 0, 0);
-    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rs.m, om, 0, 0);
+    const auto c = __builtin_amdgcn_raw_buffer_load_b96(rs.w, ow, 0, kWNt);
+    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rs.m, om, 0, kWNt);
     s.a[0] = c[0]; s.a[1] = c[1]; s.a[2] = c[2]; s.a[3] = m[0]; s.a[4] = m[1];
   } else {
-    const auto c = __builtin_amdgcn_raw_buffer_load_b64(rs.w, ow, 0, 0);
-    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rs.m, om, 0, 0);
+    const auto c = __builtin_amdgcn_raw_buffer_load_b64(rs.w, ow, 0, kWNt);
+    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rs.m, om, 0, kWNt);
     s.a[0] = c[0]; s.a[1] = c[1]; s.a[2] = m[0]; s.a[3] = m[1];
   }
 }
