@@ -41,6 +41,7 @@ constexpr int kMaxWaves = 16;          // waves per workgroup, at most
 // quantization); measured against 1536-4096: best or within 2% everywhere,
 // 70B block -4%, 3B block -13% to -18% with the quantization fused.
 constexpr int kResidentWaves = 2048;
+constexpr int kSmallLaunchWaves = 1536;
 constexpr int kXLdsMax = 32 * 1024;    // token rows staged through registers into LDS up to this many bytes
 constexpr int kXBigMax = 128 * 1024;   // ... and by LDS-direct loads up to this many (one workgroup per CU)
 constexpr int kBigLdsAttr = 150 * 1024;  // dynamic LDS the LDS-direct mode may request
@@ -628,7 +629,12 @@ GemvShape gemv_shape(const LinDesc* items, int count) {
   g.xlm = max_x <= kXLdsMax ? 1 : (max_x <= kXBigMax && weights >= kXBigMinWeights && k1024 ? 2 : 0);
   // the LDS-direct mode runs one 16-wave workgroup per CU; it keeps twice
   // the waves (measured: 5-9% faster than 2048 at 8 tokens, 70B widths)
-  const int target = g.xlm == 2 ? 2 * kResidentWaves : kResidentWaves;
+  // launches streaming fewer than 2^26 weights (3B-class blocks) do better
+  // with fewer waves still (measured: 3B block 21.4 -> 20.2 us at one token,
+  // 24.0 -> 22.6 at 4, 27.6 -> 26.2 at 8; the 70B-class launches, all at
+  // least 2^26 weights, were 2-5% slower with 1536)
+  const int base = weights < (int64_t(1) << 26) ? kSmallLaunchWaves : kResidentWaves;
+  const int target = g.xlm == 2 ? 2 * base : base;
   g.ks = tiles > 0 ? target / tiles : 1;
   g.ks = g.ks < 1 ? 1 : (g.ks > kMaxWaves ? kMaxWaves : g.ks);
   g.ks = g.ks > max_nsb ? max_nsb : g.ks;
