@@ -579,14 +579,21 @@ int kind_of(int fmt, int n, int m) {
 
 // D = weight stages in flight per wave: the wave's whole k range when it is
 // short, else 4 (with the panel-major layout the waves of a launch sweep the
-// matrix together, and a shallower ring keeps the sweep's front compact)
+// matrix together, and a shallower ring keeps the sweep's front compact).
+// DENSE2 launches of at least 2^26 weights (70B-class) take 6: with the
+// nontemporal weight loads the deeper ring measured 1-2% faster there (and
+// slower for N:M, whose decode holds more registers, and for smaller
+// launches).
 template <int KIND>
-void launch_gemv(const GemvLaunch& L, int xlm, bool xf, int spw, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+void launch_gemv(const GemvLaunch& L, int xlm, bool xf, int spw, bool deep, dim3 grid, dim3 block, size_t lds,
+                 hipStream_t s) {
   if (xf) {
     if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, 1, 2, true>), grid, block, lds, s, L);
+    else if (KIND == kDense2 && deep) hipLaunchKernelGGL((gemv_kernel<kDense2, 1, 6, true>), grid, block, lds, s, L);
     else hipLaunchKernelGGL((gemv_kernel<KIND, 1, 4, true>), grid, block, lds, s, L);
   } else if (xlm == 1) {
     if (spw <= 2) hipLaunchKernelGGL((gemv_kernel<KIND, 1, 2, false>), grid, block, lds, s, L);
+    else if (KIND == kDense2 && deep) hipLaunchKernelGGL((gemv_kernel<kDense2, 1, 6, false>), grid, block, lds, s, L);
     else hipLaunchKernelGGL((gemv_kernel<KIND, 1, 4, false>), grid, block, lds, s, L);
   } else if (xlm == 2) {
     // more dynamic LDS than the default limit: raised once per kernel
@@ -608,6 +615,7 @@ void launch_gemv(const GemvLaunch& L, int xlm, bool xf, int spw, dim3 grid, dim3
 struct GemvShape {
   int ks, tb, spw;
   int xlm;    // token-row staging: 0 none, 1 registers, 2 LDS-direct (gemv_kernel's XLM)
+  bool big;   // at least 2^26 weights in the launch
 };
 GemvShape gemv_shape(const LinDesc* items, int count) {
   int tiles = 0, max_nsb = 1;
@@ -633,7 +641,8 @@ GemvShape gemv_shape(const LinDesc* items, int count) {
   // with fewer waves still (measured: 3B block 21.4 -> 20.2 us at one token,
   // 24.0 -> 22.6 at 4, 27.6 -> 26.2 at 8; the 70B-class launches, all at
   // least 2^26 weights, were 2-5% slower with 1536)
-  const int base = weights < (int64_t(1) << 26) ? kSmallLaunchWaves : kResidentWaves;
+  g.big = weights >= (int64_t(1) << 26);
+  const int base = g.big ? kResidentWaves : kSmallLaunchWaves;
   const int target = g.xlm == 2 ? 2 * base : base;
   g.ks = tiles > 0 ? target / tiles : 1;
   g.ks = g.ks < 1 ? 1 : (g.ks > kMaxWaves ? kMaxWaves : g.ks);
@@ -689,9 +698,9 @@ hipError_t launch_gemv_group(int kind, const LinDesc* items, int count, hipStrea
   const size_t lds = xreg + 64 + (g.ks > 1 ? (size_t)g.ks * g.tb * 4 * 64 * sizeof(int32_t) : 0);
   const dim3 grid((unsigned)blocks), block(64 * g.ks * g.tb);
   const bool xf_on = xf != nullptr;
-  if (kind == kDense2) launch_gemv<kDense2>(L, g.xlm, xf_on, g.spw, grid, block, lds, s);
-  else if (kind == kNm68) launch_gemv<kNm68>(L, g.xlm, xf_on, g.spw, grid, block, lds, s);
-  else launch_gemv<kNm24>(L, g.xlm, xf_on, g.spw, grid, block, lds, s);
+  if (kind == kDense2) launch_gemv<kDense2>(L, g.xlm, xf_on, g.spw, g.big, grid, block, lds, s);
+  else if (kind == kNm68) launch_gemv<kNm68>(L, g.xlm, xf_on, g.spw, g.big, grid, block, lds, s);
+  else launch_gemv<kNm24>(L, g.xlm, xf_on, g.spw, g.big, grid, block, lds, s);
   return hipGetLastError();
 }
 
