@@ -151,6 +151,26 @@ def test_quant_acts_many_tokens(k):
     assert np.array_equal(to_np(xq), q_ref)
 
 
+@pytest.mark.parametrize("k", [16384, 16448, 28672, 32704, 32768])
+def test_quant_acts_split_rows(k):
+    """Decode-sized tokens of 16384-32768 values are split over 8 workgroups,
+    each quantizing its part of the row from registers: both ends of that
+    range, parts that do not start on a 1024-piece boundary, the row maximum
+    in the last part."""
+    import torch
+    from sparse_linear_layers_absmean_amd import sbl
+    m_tok = 3
+    x = synth.gaussian_acts(np.random.default_rng([15, k]), m_tok, k, hot_channels=4)
+    x[1] = 0.0
+    x[2, k - 1] = -50.0
+    say(f"quant_acts split {m_tok} x {k}")
+    xq, gamma = sbl.quant_acts(to_dev(x))
+    torch.cuda.synchronize()
+    q_ref, g_ref = O.quant_acts(x)
+    assert np.array_equal(to_np(gamma), g_ref)
+    assert np.array_equal(to_np(xq), q_ref)
+
+
 @pytest.mark.parametrize("n,m", [(6, 8), (2, 4), (5, 8), (8, 8)])
 def test_pack_standalone(n, m):
     import torch
