@@ -1,0 +1,162 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case swaps one oracle function for a deliberately wrong variant (a
+dropped term, a wrong sign, index or rounding rule, a transposed operand, a
+changed byte layout), runs the pins that cover that step, and requires at
+least one of them to fail.  The mistakes are planted in the oracle, on the
+CPU; nothing here touches the HIP library.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import test_oracle_acts_linear as A
+import test_oracle_scales as S
+import test_oracle_weights as W
+from oracle import sbl_oracle as O
+
+
+def _ties_to_higher_index(orig):
+    def top_n_keep(mag, n, m):
+        mag = np.asarray(mag)
+        n_out, k = mag.shape
+        a = mag.reshape(n_out, k // m, m)
+        idx = np.arange(m)
+        higher = idx[None, :] > idx[:, None]              # the mistake: i > j wins ties
+        rank = (a[..., None, :] > a[..., :, None]).sum(-1) + \
+            ((a[..., None, :] == a[..., :, None]) & higher).sum(-1)
+        return (rank < n).reshape(n_out, k)
+    return top_n_keep
+
+
+def _mask_from_codes(orig):
+    return lambda bits, n, m, order=O.QUANT_THEN_MASK: orig(bits, n, m, O.MASK_FROM_CODES)
+
+
+def _absmean_doubled(orig):
+    return lambda bits, keep=None: orig(bits, keep) * 2
+
+
+def _mean_of_signed_w(orig):
+    def absmean_exact(bits, keep=None):
+        w = O.bf16_to_f32(np.asarray(bits, np.uint16).ravel()).astype(np.float64)
+        if keep is not None:
+            w = w[np.asarray(keep, bool).ravel()]
+        return Fraction(float(w.mean()))                   # the mistake: no |.|
+    return absmean_exact
+
+
+def _round_half_away(orig):
+    def ternarize(bits, beta):
+        w = O.bf16_to_f32(bits).astype(np.float64)
+        r = w / np.float64(O.beta_eff(beta))
+        return np.clip(np.sign(r) * np.floor(np.abs(r) + 0.5), -1, 1).astype(np.int8)
+    return ternarize
+
+
+def _no_beta_floor(orig):
+    def ternarize(bits, beta):
+        w = O.bf16_to_f32(bits).astype(np.float64)
+        return np.clip(np.rint(w / np.float64(beta)), -1, 1).astype(np.int8)
+    return ternarize
+
+
+def _quant_acts_variant(signed_max=False, qb=128, lo=-127):
+    def make(orig):
+        def quant_acts(x):
+            x = np.asarray(x, np.float32)
+            gamma = (x.max(axis=1) if signed_max else np.abs(x).max(axis=1)).astype(np.float32)
+            s = (np.maximum(gamma, np.float32(1e-5)) / np.float32(qb)).astype(np.float32)
+            t = (x / s[:, None]).astype(np.float32)
+            return np.clip(np.rint(t), lo, 127).astype(np.int8), gamma
+        return quant_acts
+    return make
+
+
+def _contract_drops_last_k(orig):
+    return lambda codes, q: orig(np.asarray(codes)[:, :-1], np.asarray(q)[:, :-1])
+
+
+def _contract_transposed(orig):
+    return lambda codes, q: orig(codes, q).T
+
+
+def _rescale_without_2_pow_minus_7(orig):
+    return lambda acc, beta, gamma: (orig(acc, beta, gamma) * np.float32(128)).astype(np.float32)
+
+
+def _rescale_without_gamma_floor(orig):
+    def rescale(acc, beta, gamma):
+        s = ((O.beta_eff(beta) * np.asarray(gamma, np.float32)).astype(np.float32) / np.float32(128))
+        return (np.asarray(acc).astype(np.float32) * s.astype(np.float32)[:, None]).astype(np.float32)
+    return rescale
+
+
+def _bitmap_msb_first(orig):
+    def pack_bitmap(keep):
+        kp = np.asarray(keep, bool)
+        n_out, k = kp.shape
+        return np.packbits(kp.reshape(n_out, k // 8, 8), axis=-1, bitorder="big").reshape(n_out, k // 8)
+    return pack_bitmap
+
+
+def _dense2_twos_complement(orig):
+    def pack_dense2(codes):
+        c = np.asarray(codes, np.int8)
+        n_out, k = c.shape
+        u = (c.astype(np.int16) & 3).astype(np.uint8)       # the mistake: u = c mod 4, not c + 1
+        out = np.zeros((n_out, k // 4), np.uint8)
+        for kk in range(16):
+            out[:, 4 * np.arange(k // 16) + kk % 4] |= (u[:, kk::16] << (2 * (kk // 4))).astype(np.uint8)
+        return out
+    return pack_dense2
+
+
+MUTANTS = [
+    ("mask ties to the higher index", "top_n_keep", _ties_to_higher_index,
+     [W.test_mask_ties_prefer_lower_index, lambda: W.test_mask_matches_subset_enumeration(8)]),
+    ("mask chosen from the codes, not the masters", "quant_weights", _mask_from_codes,
+     [W.test_mask_is_from_master_not_codes, A.test_worked_example_end_to_end]),
+    ("absmean off by a factor 2 (exponent offset)", "absmean_exact", _absmean_doubled,
+     [S.test_absmean_equals_fraction_sum, W.test_ternarize_tie_at_half_beta_goes_to_zero]),
+    ("mean of w instead of |w|", "absmean_exact", _mean_of_signed_w,
+     [S.test_beta_gaussian_half_normal_mean, A.test_worked_example_end_to_end]),
+    ("RoundClip rounds half away from zero", "ternarize", _round_half_away,
+     [W.test_ternarize_tie_at_half_beta_goes_to_zero]),
+    ("RoundClip divides by beta without the 1e-5 floor", "ternarize", _no_beta_floor,
+     [W.test_ternarize_matches_fraction_roundclip, W.test_ternarize_beta_below_the_floor]),
+    ("gamma = max x instead of max |x|", "quant_acts", _quant_acts_variant(signed_max=True),
+     [A.test_quant_acts_against_exact_rationals, A.test_worked_example_end_to_end]),
+    ("activation scale Qb = 127", "quant_acts", _quant_acts_variant(qb=127),
+     [A.test_quant_acts_ties_and_clamp, A.test_quant_acts_against_exact_rationals]),
+    ("activations clipped to -128", "quant_acts", _quant_acts_variant(lo=-128),
+     [A.test_quant_acts_ties_and_clamp]),
+    ("contraction drops the last k", "contract", _contract_drops_last_k,
+     [A.test_contract_matches_python_ints_non_square]),
+    ("contraction result transposed", "contract", _contract_transposed,
+     [A.test_contract_matches_python_ints_non_square, A.test_worked_example_end_to_end]),
+    ("rescale without the 2^-7", "rescale", _rescale_without_2_pow_minus_7,
+     [A.test_rescale_against_float64_and_zero, A.test_forward_equals_dequantized_float_matmul]),
+    ("rescale without the gamma floor", "rescale", _rescale_without_gamma_floor,
+     [A.test_rescale_against_float64_and_zero]),
+    ("bitmap bits most significant first", "pack_bitmap", _bitmap_msb_first,
+     [W.test_pack_round_trips, A.test_worked_example_end_to_end]),
+    ("DENSE2 stores c mod 4 instead of c + 1", "pack_dense2", _dense2_twos_complement,
+     [W.test_pack_round_trips, A.test_worked_example_end_to_end]),
+]
+
+
+@pytest.mark.parametrize("name,attr,make,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(monkeypatch, name, attr, make, pins):
+    for pin in pins:                                   # the pins hold for the oracle as it is
+        pin()
+    monkeypatch.setattr(O, attr, make(getattr(O, attr)))
+    failed = []
+    for pin in pins:
+        try:
+            pin()
+        except Exception:                              # an assertion, or a shape or value error
+            failed.append(getattr(pin, "__name__", "pin"))
+    assert failed, f"no pin caught: {name}"

@@ -44,6 +44,16 @@ def test_ternarize_tie_at_half_beta_goes_to_zero():
     assert O.ternarize(bits, beta).tolist() == [0, 0, 1, -1] * 4
 
 
+def test_ternarize_beta_below_the_floor():
+    # beta below 1e-5 is replaced by 1e-5: |w| ~ 4e-6 lies above beta/2 = 1e-6
+    # but below 1e-5/2, so it quantizes to 0; |w| ~ 6e-6 goes to sign(w)
+    bits = f32_to_bf16_bits(np.array([4e-6, -4e-6, 6e-6, -6e-6], np.float32))
+    beta = np.float32(2e-6)
+    got = O.ternarize(bits, beta)
+    assert got.tolist() == [0, 0, 1, -1]
+    assert got.tolist() == [_roundclip_fraction(float(v), beta) for v in O.bf16_to_f32(bits)]
+
+
 def test_ternarize_is_monotone_and_ternary():
     rng = np.random.default_rng(9)
     bits = f32_to_bf16_bits(rng.standard_normal(10000).astype(np.float32))
