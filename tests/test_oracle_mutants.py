@@ -13,6 +13,8 @@ import numpy as np
 import pytest
 
 import test_oracle_acts_linear as A
+import test_oracle_backward as B
+import test_oracle_grouped as G
 import test_oracle_scales as S
 import test_oracle_weights as W
 from oracle import sbl_oracle as O
@@ -114,6 +116,77 @@ def _dense2_twos_complement(orig):
     return pack_dense2
 
 
+def _rational_toward_zero(orig):
+    def rational_to_f32(num, den):
+        v = orig(num, den)
+        if np.isfinite(v) and Fraction(float(v)) > Fraction(num, den):
+            v = np.nextafter(v, np.float32(0))              # the mistake: truncation
+        return np.float32(v)
+    return rational_to_f32
+
+
+def _nm_fields_reversed(orig):
+    def pack_nm(codes, keep, n, m):
+        b = orig(codes, keep, n, m)
+        out = np.zeros_like(b)
+        for s in range(4):                                  # kept codes in descending order
+            out |= (((b >> (2 * s)) & 3) << (2 * (3 - s))).astype(np.uint8)
+        return out
+    return pack_nm
+
+
+def _clip_pass_off_by_one(orig):
+    def clip_pass(x, gamma):
+        x = np.asarray(x, np.float32)
+        s = (np.maximum(np.asarray(gamma, np.float32), np.float32(1e-5)) / np.float32(128)).astype(np.float32)
+        t = np.rint((x / s[:, None]).astype(np.float32))
+        return (np.abs(t) <= 128).astype(np.float64)
+    return clip_pass
+
+
+def _backward_without_clip(orig):
+    return lambda codes, beta, x, q, gamma, dy_bits, clip=True: orig(codes, beta, x, q, gamma, dy_bits, clip=False)
+
+
+def _dw_only_through_nonzero_codes(orig):
+    def backward(codes, beta, x, q, gamma, dy_bits, clip=True):
+        r = orig(codes, beta, x, q, gamma, dy_bits, clip)
+        r["dw"] = r["dw"] * (np.asarray(codes) != 0)
+        return r
+    return backward
+
+
+def _dequant_without_2_pow_minus_7(orig):
+    return lambda q, gamma: (orig(q, gamma) * np.float32(128)).astype(np.float32)
+
+
+def _row_groups_one_too_large(orig):
+    return lambda bits, n, m, rows_per_group: orig(bits, n, m, rows_per_group + 1)
+
+
+def _row_group_scales_reversed(orig):
+    return lambda acc, betas, rows_per_group, gamma: orig(acc, np.asarray(betas)[::-1], rows_per_group, gamma)
+
+
+def _one_gamma_per_token(orig):
+    def quant_acts_kgrouped(x, kg):
+        q, g = O.quant_acts(x)
+        return q, np.repeat(g[:, None], np.asarray(x).shape[1] // kg, axis=1)
+    return quant_acts_kgrouped
+
+
+def _blocks_added_descending(orig):
+    def linear_kgrouped(codes, q, betas, rows_per_group, gamma, kg):
+        def rev(a):                                          # feature blocks in reverse order
+            a = np.asarray(a)
+            return a.reshape(a.shape[0], -1, kg)[:, ::-1].reshape(a.shape)
+        b = np.asarray(betas)
+        acc, y = orig(rev(codes), rev(q), b if b.ndim == 1 else b[:, ::-1], rows_per_group,
+                      np.asarray(gamma)[:, ::-1], kg)
+        return acc[:, :, ::-1], y
+    return linear_kgrouped
+
+
 MUTANTS = [
     ("mask ties to the higher index", "top_n_keep", _ties_to_higher_index,
      [W.test_mask_ties_prefer_lower_index, lambda: W.test_mask_matches_subset_enumeration(8)]),
@@ -145,6 +218,26 @@ MUTANTS = [
      [W.test_pack_round_trips, A.test_worked_example_end_to_end]),
     ("DENSE2 stores c mod 4 instead of c + 1", "pack_dense2", _dense2_twos_complement,
      [W.test_pack_round_trips, A.test_worked_example_end_to_end]),
+    ("fp32 rounding of beta toward zero", "rational_to_f32", _rational_toward_zero,
+     [S.test_rational_to_f32_matches_neighbour_search, S.test_rational_to_f32_midpoints_go_to_even]),
+    ("N:M codes stored in descending k", "pack_nm", _nm_fields_reversed,
+     [W.test_pack_round_trips, A.test_worked_example_end_to_end]),
+    ("activation clip test off by one", "clip_pass", _clip_pass_off_by_one,
+     [B.test_clip_pass_crafted]),
+    ("dX without the quantizer's clip mask", "backward", _backward_without_clip,
+     [B.test_brute_force_fractions, B.test_single_token_single_output]),
+    ("dW only through nonzero codes", "backward", _dw_only_through_nonzero_codes,
+     [B.test_mask_ste_reaches_pruned_masters, B.test_brute_force_fractions]),
+    ("x_hat without the 2^-7", "dequant_acts", _dequant_without_2_pow_minus_7,
+     [B.test_dequant_is_the_scaled_code]),
+    ("row groups one row too large", "quant_weights_grouped", _row_groups_one_too_large,
+     [lambda: G.test_each_group_is_the_method_on_its_rows(3), G.test_closed_form_constant_rows]),
+    ("row-group scales applied in reverse", "rescale_grouped", _row_group_scales_reversed,
+     [G.test_rescale_grouped_two_roundings]),
+    ("one gamma per token instead of per feature block", "quant_acts_kgrouped", _one_gamma_per_token,
+     [G.test_kgroups_blocks_are_independent_quantizations]),
+    ("feature blocks added in descending order", "linear_kgrouped", _blocks_added_descending,
+     [G.test_kgroups_sum_in_block_order]),
 ]
 
 
