@@ -12,6 +12,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
+import test_oracle_ablations as AB
 import test_oracle_acts_linear as A
 import test_oracle_backward as B
 import test_oracle_grouped as G
@@ -187,6 +188,15 @@ def _blocks_added_descending(orig):
     return linear_kgrouped
 
 
+def _mask_then_quant_beta_over_all(orig):
+    def quant_weights(bits, n, m, order=O.QUANT_THEN_MASK):
+        if order == O.MASK_THEN_QUANT:                     # the mistake: beta over every master
+            beta, keep, _ = orig(bits, n, m, O.QUANT_THEN_MASK)
+            return beta, keep, (O.ternarize(bits, beta) * keep).astype(np.int8)
+        return orig(bits, n, m, order)
+    return quant_weights
+
+
 MUTANTS = [
     ("mask ties to the higher index", "top_n_keep", _ties_to_higher_index,
      [W.test_mask_ties_prefer_lower_index, lambda: W.test_mask_matches_subset_enumeration(8)]),
@@ -238,6 +248,10 @@ MUTANTS = [
      [G.test_kgroups_blocks_are_independent_quantizations]),
     ("feature blocks added in descending order", "linear_kgrouped", _blocks_added_descending,
      [G.test_kgroups_sum_in_block_order]),
+    ("panels two blocks wide instead of four", "PANEL_BLOCKS", lambda orig: 2,
+     [W.test_panel_order_hand_example, W.test_panel_order_per_byte_and_inverse]),
+    ("mask-then-quant ablation with beta over every master", "quant_weights", _mask_then_quant_beta_over_all,
+     [AB.test_hand_example_three_orders, lambda: AB.test_mask_then_quant_brute_force(6, 8)]),
 ]
 
 
