@@ -197,6 +197,19 @@ def _mask_then_quant_beta_over_all(orig):
     return quant_weights
 
 
+def _block_beta_over_whole_rows(orig):
+    def quant_weights_blocked(bits, n, m, rows_per_group, cols_per_group):
+        betas, keep, _ = orig(bits, n, m, rows_per_group, cols_per_group)
+        rows, _, _ = O.quant_weights_grouped(bits, n, m, rows_per_group)   # the mistake: beta over the row block
+        betas = np.repeat(np.asarray(rows, np.float32)[:, None], betas.shape[1], axis=1)
+        codes = np.zeros(np.shape(bits), np.int8)
+        for gi in range(betas.shape[0]):
+            sl = slice(gi * rows_per_group, (gi + 1) * rows_per_group)
+            codes[sl] = O.ternarize(np.asarray(bits)[sl], betas[gi, 0])
+        return betas, keep, (codes * keep).astype(np.int8)
+    return quant_weights_blocked
+
+
 MUTANTS = [
     ("mask ties to the higher index", "top_n_keep", _ties_to_higher_index,
      [W.test_mask_ties_prefer_lower_index, lambda: W.test_mask_matches_subset_enumeration(8)]),
@@ -252,6 +265,8 @@ MUTANTS = [
      [W.test_panel_order_hand_example, W.test_panel_order_per_byte_and_inverse]),
     ("mask-then-quant ablation with beta over every master", "quant_weights", _mask_then_quant_beta_over_all,
      [AB.test_hand_example_three_orders, lambda: AB.test_mask_then_quant_brute_force(6, 8)]),
+    ("block scales taken over whole row blocks", "quant_weights_blocked", _block_beta_over_whole_rows,
+     [lambda: G.test_each_block_is_the_method_on_its_submatrix(16, 192, 6, 8), G.test_blocks_closed_form_and_locality]),
 ]
 
 
